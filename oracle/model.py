@@ -1,0 +1,454 @@
+"""Plain CPU oracle of the looped transformer's hot path (test infrastructure only).
+
+Pages cited (titles as printed on each page):
+  [DYN]  "Dynamic-L Inference" (tinyloop docs, architecture)
+  [BENCH] "Benchmark Comparison" (tinyloop docs, measured benchmarks)
+  [CLI]  "CLI Reference" (tinyloop docs, framework)
+  [VSG]  "Benchmark Comparison" (tinyloop docs, vs generic runtimes)
+  [CDB]  "Depth-adaptive Inference of Looped Language Models via Continuous Depth
+         Batching" (summary page)
+
+What is computed (readings of open points are listed in the design doc's table of
+readings; the short form is repeated where a function depends on one):
+  * pipeline embed -> pre blocks -> shared loop block (stack) x L -> post blocks ->
+    head, [VSG] "Where Generic Runtimes Lose On Looped Checkpoints";
+  * L is a call argument, never part of the weights, [DYN] "The Core Idea";
+  * pre-norm blocks, one K/V cache per block application ([CLI], environment
+    variable table, TINYLOOP_KV_H_MODE: the norm output feeds attn_qkv and the
+    runtime keeps per-layer K/V buffers);
+  * cached decode is the default and must agree with the uncached path ([CLI]
+    "Current Behavior" and "Debugging The Reference Path");
+  * symmetric per-group min-max INT4 without calibration ([BENCH] section 7),
+    groups of 128 along K ([BENCH] section 5, 16 groups at K = 2048), two's
+    complement nibbles in [-7, 7], even element in the low nibble ([CLI],
+    TINYLOOP_KV_INT4);
+  * FP16 body = the INT4 body dequantised once to fp16 ([CLI],
+    TINYLOOP_EXPERIMENTAL_FP16_BODY);
+  * per-token depth is clamped so it never rises within a generation ([CLI]
+    "generate", --early-exit-patience);
+  * greedy decoding is temperature 0 ([CLI] "generate", --temperature);
+  * lanes of a batch run at their own depth ([DYN] "L-Aware Batching"), tokens
+    leave the batch after their last loop iteration ([CDB] summary bullets).
+
+Parity pins (tests/test_oracle_*.py): every function here is pinned by a closed
+form, an invariant, a brute force or an independent library routine; none is
+"parity unpinned" except absolute output values of the synthetic models, for
+which the pages print no numbers.
+"""
+from __future__ import annotations
+
+import math
+from dataclasses import dataclass, field
+
+import numpy as np
+
+__all__ = [
+    "rmsnorm", "rope_angles", "apply_rope", "silu", "causal_attention",
+    "quantize_w4g128", "pack_nibbles", "unpack_nibbles", "dequant_w4g128", "fp16_body",
+    "OracleModel", "Lane", "prefill", "decode_step", "forward_batch", "forward_ragged",
+    "greedy_argmax", "clamp_depths", "active_lists", "bf16_bits_to_float",
+]
+
+
+# ---------------------------------------------------------------------------
+# elementary steps
+
+
+def rmsnorm(h: np.ndarray, g: np.ndarray, eps: float) -> np.ndarray:
+    """x = h / sqrt(mean(h^2) + eps) * g over the last axis.
+
+    Placement before QKV and before the MLP: [CLI] TINYLOOP_KV_H_MODE names the
+    "pre-QKV" norm output as the input of attn_qkv.
+    """
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return h / np.sqrt(ms + eps) * g
+
+
+def rope_angles(positions: np.ndarray, head_dim: int, base: float, dt=np.float64):
+    """cos and sin of p * theta_i, theta_i = base^(-2i/head_dim), i < head_dim/2.
+
+    Rotary position embedding with base 10000 (model definition of the workloads);
+    the rotate-half pairing (i, i + head_dim/2) is a reading, see the design doc.
+    """
+    half = head_dim // 2
+    i = np.arange(half, dtype=np.float64)
+    theta = base ** (-2.0 * i / head_dim)
+    ang = np.asarray(positions, dtype=np.float64)[:, None] * theta[None, :]
+    return np.cos(ang).astype(dt), np.sin(ang).astype(dt)
+
+
+def apply_rope(x: np.ndarray, cos: np.ndarray, sin: np.ndarray) -> np.ndarray:
+    """x: [T, H, dh]; rotate each pair (x_i, x_{i+dh/2}) by its angle at the row's position."""
+    half = x.shape[-1] // 2
+    x1, x2 = x[..., :half], x[..., half:]
+    c, s = cos[:, None, :], sin[:, None, :]
+    return np.concatenate([x1 * c - x2 * s, x2 * c + x1 * s], axis=-1)
+
+
+def silu(z: np.ndarray) -> np.ndarray:
+    return z / (1.0 + np.exp(-z))
+
+
+def causal_attention(q: np.ndarray, k_all: np.ndarray, v_all: np.ndarray, q_pos: np.ndarray) -> np.ndarray:
+    """Softmax attention of queries at positions q_pos over keys 0..q_pos (inclusive).
+
+    q: [T, H, dh]; k_all, v_all: [S, H, dh] hold positions 0..S-1 of one lane in one
+    cache slot.  Scale 1/sqrt(dh), max subtraction, no bias, one K/V head per query
+    head.  Returns [T, H*dh].
+    """
+    T, H, dh = q.shape
+    S = k_all.shape[0]
+    scores = np.einsum("thd,shd->hts", q, k_all) / math.sqrt(dh)
+    mask = np.arange(S)[None, :] > np.asarray(q_pos)[:, None]          # [T, S]
+    scores = np.where(mask[None, :, :], -np.inf, scores)
+    scores = scores - scores.max(axis=-1, keepdims=True)
+    p = np.exp(scores)
+    p = p / p.sum(axis=-1, keepdims=True)
+    o = np.einsum("hts,shd->thd", p, v_all)
+    return o.reshape(T, H * dh)
+
+
+# ---------------------------------------------------------------------------
+# INT4 group quantisation ([BENCH] sections 5 and 7; [CLI] TINYLOOP_KV_INT4)
+
+GROUP = 128
+
+
+def quantize_w4g128(w32: np.ndarray):
+    """Symmetric per-group min-max INT4 of fp32 weights [N, K], groups of 128 along K.
+
+    s = fp16(max|w| / 7) with the division in fp32, q = clamp(rint(w / s), -7, 7)
+    with round-half-to-even and the division in fp32; a group whose fp16 scale is 0
+    gets q = 0.  The fp32 arithmetic is the precision in which the GPU library takes
+    the same integer decisions.  Returns (q int8 [N, K], s float16 [N, K/128]).
+    """
+    w32 = np.asarray(w32, dtype=np.float32)
+    N, K = w32.shape
+    assert K % GROUP == 0
+    g = w32.reshape(N, K // GROUP, GROUP)
+    amax = np.abs(g).max(axis=2)
+    s16 = (amax / np.float32(7.0)).astype(np.float16)
+    s32 = s16.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(s32 > 0, np.rint(g / np.where(s32 > 0, s32, np.float32(1))), np.float32(0))
+    q = np.clip(r, -7, 7).astype(np.int8).reshape(N, K)
+    return q, s16
+
+
+def pack_nibbles(q: np.ndarray) -> np.ndarray:
+    """Two's complement nibbles, element 2i in the low nibble of byte i, 2i+1 in the high."""
+    q = np.asarray(q, dtype=np.int8)
+    lo = q[..., 0::2].astype(np.uint8) & 0xF
+    hi = q[..., 1::2].astype(np.uint8) & 0xF
+    return (lo | (hi << 4)).astype(np.uint8)
+
+
+def unpack_nibbles(packed: np.ndarray) -> np.ndarray:
+    """Inverse of pack_nibbles: every nibble n maps to n if n < 8 else n - 16."""
+    packed = np.asarray(packed, dtype=np.uint8)
+    lo = (packed & 0xF).astype(np.int16)
+    hi = (packed >> 4).astype(np.int16)
+    lo = np.where(lo >= 8, lo - 16, lo)
+    hi = np.where(hi >= 8, hi - 16, hi)
+    out = np.empty(packed.shape[:-1] + (packed.shape[-1] * 2,), dtype=np.int8)
+    out[..., 0::2] = lo
+    out[..., 1::2] = hi
+    return out
+
+
+def dequant_w4g128(q: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """w[n, k] = q[n, k] * s[n, k // 128]; exact in fp32 (a 4-bit integer times an fp16)."""
+    N, K = q.shape
+    s = np.repeat(s16.astype(np.float32), GROUP, axis=1)
+    return q.astype(np.float32) * s
+
+
+def fp16_body(q: np.ndarray, s16: np.ndarray) -> np.ndarray:
+    """FP16 body: fp16(q * s), the dequantised cache built once at load ([CLI] FP16_BODY)."""
+    return dequant_w4g128(q, s16).astype(np.float16)
+
+
+def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
+    return (np.asarray(bits, dtype=np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# model
+
+
+BLOCK_MATS = ("wqkv", "wo", "wgate", "wup", "wdown")
+
+
+def _stored_to_float(a: np.ndarray, kind: str, dt) -> np.ndarray:
+    if kind == "bf16":
+        return bf16_bits_to_float(a).astype(dt)
+    return np.asarray(a).astype(dt)
+
+
+@dataclass
+class OracleModel:
+    """Weights of one looped model converted to the oracle's float type ``dt``.
+
+    blocks are ordered pre blocks, loop-stack layers, post blocks.  For an INT4 loop
+    block the oracle quantises the fp32 draws itself (quantize_w4g128) and keeps q
+    and s for the bit-exact comparison; an FP16-body loop block is fp16(q*s) of the
+    same q and s.
+    """
+    spec: object
+    dt: type
+    embed: np.ndarray
+    head: np.ndarray
+    final_norm: np.ndarray
+    blocks: list
+    w4: dict = field(default_factory=dict)   # (block, name) -> (q int8, s fp16)
+    embed_kind: str = "f32"
+
+    @classmethod
+    def from_weights(cls, w, dt=np.float64):
+        spec = w.spec
+        bkind = spec.boundary_dtype
+        blocks, w4 = [], {}
+        for b, blk in enumerate(w.blocks):
+            kind = spec.block_kind(b)
+            out = {"norm1": blk["norm1"].astype(dt), "norm2": blk["norm2"].astype(dt)}
+            for name in BLOCK_MATS:
+                a = blk[name]
+                if kind == "loop" and spec.loop_dtype in ("w4g128", "f16body"):
+                    q, s = quantize_w4g128(a)
+                    w4[(b, name)] = (q, s)
+                    mat = dequant_w4g128(q, s) if spec.loop_dtype == "w4g128" else fp16_body(q, s)
+                    out[name] = mat.astype(dt)
+                else:
+                    k = spec.loop_dtype if kind == "loop" else bkind
+                    out[name] = _stored_to_float(a, k, dt)
+            blocks.append(out)
+        return cls(spec=spec, dt=dt, embed=w.embed, head=_stored_to_float(w.head, bkind, dt),
+                   final_norm=w.final_norm.astype(dt), blocks=blocks, w4=w4, embed_kind=bkind)
+
+    # -- pieces of the pipeline
+
+    def embed_rows(self, tokens: np.ndarray) -> np.ndarray:
+        return _stored_to_float(self.embed[np.asarray(tokens)], self.embed_kind, self.dt)
+
+    def block(self, b: int, h: np.ndarray, pos: np.ndarray, past_k: np.ndarray, past_v: np.ndarray):
+        """One pre-norm block on rows h at positions pos of ONE lane.
+
+        past_k/past_v hold the lane's earlier positions in this block application's
+        own cache slot ([CLI] TINYLOOP_KV_H_MODE: per-layer K/V buffers).  Returns the
+        new residual rows and the k, v rows to append to that slot.
+        """
+        sp, W = self.spec, self.blocks[b]
+        H, dh, d = sp.n_heads, sp.head_dim, sp.d_model
+        T = h.shape[0]
+        x = rmsnorm(h, W["norm1"], sp.rms_eps)
+        qkv = x @ W["wqkv"].T
+        q = qkv[:, :d].reshape(T, H, dh)
+        k = qkv[:, d:2 * d].reshape(T, H, dh)
+        v = qkv[:, 2 * d:].reshape(T, H, dh)
+        cos, sin = rope_angles(pos, dh, sp.rope_base, self.dt)
+        q = apply_rope(q, cos, sin)
+        k = apply_rope(k, cos, sin)
+        k_all = np.concatenate([past_k, k], axis=0)
+        v_all = np.concatenate([past_v, v], axis=0)
+        o = causal_attention(q, k_all, v_all, pos)
+        h = h + o @ W["wo"].T
+        x2 = rmsnorm(h, W["norm2"], sp.rms_eps)
+        u = silu(x2 @ W["wgate"].T) * (x2 @ W["wup"].T)
+        h = h + u @ W["wdown"].T
+        return h, k, v
+
+    def logits(self, h: np.ndarray) -> np.ndarray:
+        """Final RMSNorm then the head projection (head readable at any state: [CLI] logit margin)."""
+        return rmsnorm(h, self.final_norm, self.spec.rms_eps) @ self.head.T
+
+    def empty_kv(self):
+        sp = self.spec
+        z = np.zeros((0, sp.n_heads, sp.head_dim), dtype=self.dt)
+        return z, z
+
+    def slots(self, L: int):
+        """Block applications in pipeline order for depth L: (block index, cache-slot key)."""
+        sp = self.spec
+        seq = [(b, ("pre", b)) for b in range(sp.n_pre)]
+        for j in range(1, L + 1):
+            seq += [(sp.n_pre + l, ("loop", j, l)) for l in range(sp.n_loop)]
+        seq += [(sp.n_pre + sp.n_loop + b, ("post", b)) for b in range(sp.n_post)]
+        return seq
+
+
+def greedy_argmax(logits: np.ndarray) -> np.ndarray:
+    """Greedy token ([CLI] temperature 0): argmax over fp32 logits, lowest index on ties.
+
+    The comparison is taken in fp32, the precision in which the GPU library takes it.
+    """
+    l32 = np.asarray(logits, dtype=np.float32)
+    return np.argmax(l32, axis=-1).astype(np.int32)   # numpy returns the first maximum
+
+
+# ---------------------------------------------------------------------------
+# lanes: prefill, cached decode, monotone depth
+
+
+@dataclass
+class Lane:
+    """One generation: its tokens, per-slot K/V caches, current length and depth ceiling."""
+    tokens: list
+    kv: dict
+    ceiling: int
+    pending: int = -1
+    hidden_last: np.ndarray | None = None
+
+
+def prefill(m: OracleModel, tokens, L: int, want_logits: str = "last"):
+    """Full causal forward of one sequence at depth L, filling every slot's cache.
+
+    Returns (lane, hidden [T, d], logits).  want_logits: "last" -> [V] at the last
+    position, "all" -> [T, V], "none" -> None.  The lane's pending token is the
+    greedy token at the last position; its depth ceiling is L.
+    """
+    assert L >= 1
+    tokens = np.asarray(tokens, dtype=np.int64)
+    T = len(tokens)
+    pos = np.arange(T)
+    h = m.embed_rows(tokens)
+    kv = {}
+    for b, key in m.slots(L):
+        pk, pv = m.empty_kv()
+        h, k, v = m.block(b, h, pos, pk, pv)
+        kv[key] = (k, v)
+    lane = Lane(tokens=list(map(int, tokens)), kv=kv, ceiling=L, hidden_last=h[-1].copy())
+    logits = None
+    if want_logits == "all":
+        logits = m.logits(h)
+        lane.pending = int(greedy_argmax(logits[-1]))
+    elif want_logits == "last":
+        logits = m.logits(h[-1:])[0]
+        lane.pending = int(greedy_argmax(logits))
+    return lane, h, logits
+
+
+def decode_step(m: OracleModel, lane: Lane, L_req: int, token: int | None = None):
+    """One cached decode step of one lane.
+
+    The effective depth is min(L_req, ceiling) and becomes the new ceiling, so depth
+    never rises within a generation ([CLI] --early-exit-patience).  Every slot used
+    at this depth already holds all earlier positions of the lane.  ``token``
+    defaults to the lane's pending greedy token.  Returns (hidden [d], logits [V],
+    next token, effective depth).
+    """
+    assert L_req >= 1
+    L = min(int(L_req), lane.ceiling)
+    tok = lane.pending if token is None else int(token)
+    p = len(lane.tokens)
+    pos = np.array([p])
+    h = m.embed_rows(np.array([tok]))
+    for b, key in m.slots(L):
+        pk, pv = lane.kv[key]
+        assert pk.shape[0] == p, "cache slot misses earlier positions"
+        h, k, v = m.block(b, h, pos, pk, pv)
+        lane.kv[key] = (np.concatenate([pk, k]), np.concatenate([pv, v]))
+    lane.tokens.append(tok)
+    lane.ceiling = L
+    logits = m.logits(h)[0]
+    nxt = int(greedy_argmax(logits))
+    lane.pending = nxt
+    lane.hidden_last = h[0].copy()
+    return h[0], logits, nxt, L
+
+
+def clamp_depths(requests, first_ceiling: int) -> np.ndarray:
+    """Non-increasing depths: L_i = min(request_i, L_{i-1}), L_0 = first_ceiling ([CLI])."""
+    out, c = [], int(first_ceiling)
+    for r in requests:
+        c = min(int(r), c)
+        out.append(c)
+    return np.asarray(out, dtype=np.int32)
+
+
+# ---------------------------------------------------------------------------
+# batches at iteration granularity ([DYN] L-Aware Batching; [CDB] summary)
+
+
+def active_lists(depths: np.ndarray, max_L: int | None = None):
+    """active_1 = all rows; active_{j+1} = [r in active_j, in order, if depth[r] > j]."""
+    depths = np.asarray(depths)
+    if max_L is None:
+        max_L = int(depths.max()) if len(depths) else 0
+    lists = []
+    cur = list(range(len(depths)))
+    for j in range(1, max_L + 1):
+        lists.append(np.asarray(cur, dtype=np.int32))
+        cur = [r for r in cur if depths[r] > j]
+    return lists
+
+
+def forward_batch(m: OracleModel, seqs, Ls, want_logits: str = "last"):
+    """Several sequences in one pass, scheduled one loop iteration at a time.
+
+    Rows of all sequences go through each block application together; at iteration
+    j only rows whose sequence depth is >= j are active (rows leave after their last
+    iteration).  Attention stays within a sequence and its own cache slot.  Returns
+    (hidden rows in input order [sum T, d], per-sequence last logits or None,
+    active row lists per iteration).
+    """
+    sp = m.spec
+    seqs = [np.asarray(s, dtype=np.int64) for s in seqs]
+    lens = [len(s) for s in seqs]
+    starts = np.cumsum([0] + lens)
+    row_seq = np.concatenate([np.full(n, i) for i, n in enumerate(lens)])
+    row_pos = np.concatenate([np.arange(n) for n in lens])
+    row_L = np.asarray(Ls)[row_seq]
+    h = m.embed_rows(np.concatenate(seqs))
+
+    def apply(b, rows):
+        sub = h[rows]
+        out = np.empty_like(sub)
+        for i in np.unique(row_seq[rows]):
+            sel = np.nonzero(row_seq[rows] == i)[0]
+            pk, pv = m.empty_kv()
+            out[sel], _, _ = m.block(b, sub[sel], row_pos[rows][sel], pk, pv)
+        h[rows] = out
+
+    all_rows = np.arange(len(row_seq))
+    for b in range(sp.n_pre):
+        apply(b, all_rows)
+    lists = active_lists(row_L)
+    for act in lists:
+        for l in range(sp.n_loop):
+            apply(sp.n_pre + l, act)
+    for b in range(sp.n_post):
+        apply(sp.n_pre + sp.n_loop + b, all_rows)
+    logits = None
+    if want_logits == "last":
+        logits = m.logits(h[starts[1:] - 1])
+    return h, logits, lists
+
+
+def forward_ragged(m: OracleModel, tokens, depth_per_pos, want_logits: str = "all"):
+    """One sequence whose position p runs depth_per_pos[p] loop iterations.
+
+    With non-increasing depths the rows active at iteration j are a prefix of the
+    sequence, so iteration j is a causal pass over that prefix in slot j.  This is
+    the uncached counterpart of prompt prefill followed by cached steps at clamped
+    per-token depths.  Returns (hidden [T, d], logits [T, V] or None).
+    """
+    sp = m.spec
+    tokens = np.asarray(tokens, dtype=np.int64)
+    dep = np.asarray(depth_per_pos)
+    assert np.all(np.diff(dep) <= 0) and dep.min() >= 1
+    T = len(tokens)
+    pos = np.arange(T)
+    h = m.embed_rows(tokens)
+    for b in range(sp.n_pre):
+        pk, pv = m.empty_kv()
+        h, _, _ = m.block(b, h, pos, pk, pv)
+    for j in range(1, int(dep.max()) + 1):
+        n = int(np.sum(dep >= j))
+        for l in range(sp.n_loop):
+            pk, pv = m.empty_kv()
+            h[:n], _, _ = m.block(sp.n_pre + l, h[:n], pos[:n], pk, pv)
+    for b in range(sp.n_post):
+        pk, pv = m.empty_kv()
+        h, _, _ = m.block(sp.n_pre + sp.n_loop + b, h, pos, pk, pv)
+    logits = m.logits(h) if want_logits == "all" else None
+    return h, logits

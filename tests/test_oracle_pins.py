@@ -1,0 +1,400 @@
+"""Pins of the CPU oracle against closed forms, invariants, brute force and
+independent library routines (torch CPU ops).  None of these re-types the oracle's
+own formulas: each compares against something the mathematics or another library
+fixes.  CPU only.
+"""
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+import torch.nn.functional as F
+
+import oracle
+import synth
+
+
+# ---------------------------------------------------------------------------
+# RMSNorm: closed forms
+
+
+def test_rmsnorm_hand_value():
+    h = np.array([[3.0, 4.0]])
+    out = oracle.rmsnorm(h, np.ones(2), 0.0)
+    # mean square 12.5 -> divide by sqrt(12.5)
+    assert np.allclose(out, [[3 / math.sqrt(12.5), 4 / math.sqrt(12.5)]], rtol=0, atol=1e-15)
+    out = oracle.rmsnorm(h, np.array([2.0, -1.0]), 0.0)
+    assert np.allclose(out, [[6 / math.sqrt(12.5), -4 / math.sqrt(12.5)]], rtol=0, atol=1e-15)
+
+
+def test_rmsnorm_rms_identity():
+    rng = np.random.default_rng(1)
+    h = rng.standard_normal((7, 33)) * 0.01
+    eps = 1e-5
+    out = oracle.rmsnorm(h, np.ones(33), eps)
+    ms = np.mean(h * h, axis=1)
+    rms_out = np.sqrt(np.mean(out * out, axis=1))
+    assert np.allclose(rms_out, np.sqrt(ms / (ms + eps)), rtol=1e-13)
+    ref = F.rms_norm(torch.from_numpy(h), (33,), torch.ones(33, dtype=torch.float64), eps).numpy()
+    assert np.allclose(out, ref, rtol=1e-13, atol=0)
+
+
+# ---------------------------------------------------------------------------
+# RoPE: textbook rotations and invariants
+
+
+def test_rope_dh2_is_plane_rotation():
+    # head_dim 2: theta_0 = base^0 = 1, so position p rotates (x, y) by p radians
+    x = np.array([[[0.3, -1.2]]] * 4)              # [T=4, H=1, 2]
+    pos = np.arange(4)
+    c, s = oracle.rope_angles(pos, 2, 10000.0)
+    out = oracle.apply_rope(x, c, s)
+    for p in range(4):
+        R = np.array([[math.cos(p), -math.sin(p)], [math.sin(p), math.cos(p)]])
+        assert np.allclose(out[p, 0], R @ x[p, 0], atol=1e-15)
+
+
+def test_rope_dh4_frequencies():
+    # head_dim 4, base 10000: pairs (0,2) turn at 1 rad/pos, (1,3) at 10000^(-1/2) = 0.01 rad/pos
+    x = np.array([[[1.0, 2.0, 3.0, 4.0]]])
+    p = 5
+    c, s = oracle.rope_angles(np.array([p]), 4, 10000.0)
+    out = oracle.apply_rope(x, c, s)[0, 0]
+    a0, a1 = 5.0, 0.05
+    assert np.allclose(out[[0, 2]], [1 * math.cos(a0) - 3 * math.sin(a0), 3 * math.cos(a0) + 1 * math.sin(a0)])
+    assert np.allclose(out[[1, 3]], [2 * math.cos(a1) - 4 * math.sin(a1), 4 * math.cos(a1) + 2 * math.sin(a1)])
+
+
+def test_rope_invariants():
+    rng = np.random.default_rng(2)
+    dh = 16
+    q = rng.standard_normal((1, 3, dh))
+    k = rng.standard_normal((1, 3, dh))
+    c0, s0 = oracle.rope_angles(np.array([0]), dh, 10000.0)
+    assert np.array_equal(oracle.apply_rope(q, c0, s0), q)          # identity at p = 0
+    for p in (1, 7, 300):
+        c, s = oracle.rope_angles(np.array([p]), dh, 10000.0)
+        r = oracle.apply_rope(q, c, s)
+        assert np.allclose(np.linalg.norm(r, axis=-1), np.linalg.norm(q, axis=-1), rtol=1e-14)
+    # scores depend only on the position difference
+    def score(pq, pk, shift):
+        cq, sq = oracle.rope_angles(np.array([pq + shift]), dh, 10000.0)
+        ck, sk = oracle.rope_angles(np.array([pk + shift]), dh, 10000.0)
+        return np.sum(oracle.apply_rope(q, cq, sq) * oracle.apply_rope(k, ck, sk), axis=-1)
+    assert np.allclose(score(9, 4, 0), score(9, 4, 123), rtol=1e-11, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# attention: torch's SDPA (an independent library routine) and special cases
+
+
+def _sdpa(q, k, v, mask):
+    # q [T,H,dh] -> [H,T,dh]
+    tq = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))
+    tk = torch.from_numpy(np.ascontiguousarray(k.transpose(1, 0, 2)))
+    tv = torch.from_numpy(np.ascontiguousarray(v.transpose(1, 0, 2)))
+    o = F.scaled_dot_product_attention(tq, tk, tv, attn_mask=torch.from_numpy(mask))
+    return o.numpy().transpose(1, 0, 2).reshape(q.shape[0], -1)
+
+
+def test_attention_matches_sdpa_causal_and_with_past():
+    rng = np.random.default_rng(3)
+    T, H, dh, past = 9, 3, 8, 5
+    q = rng.standard_normal((T, H, dh))
+    k = rng.standard_normal((past + T, H, dh))
+    v = rng.standard_normal((past + T, H, dh))
+    pos = np.arange(past, past + T)
+    out = oracle.causal_attention(q, k, v, pos)
+    allowed = np.arange(past + T)[None, :] <= pos[:, None]
+    assert np.allclose(out, _sdpa(q, k, v, allowed), rtol=1e-12, atol=1e-13)
+    # no past: standard causal mask
+    out0 = oracle.causal_attention(q, k[:T], v[:T], np.arange(T))
+    tq = torch.from_numpy(np.ascontiguousarray(q.transpose(1, 0, 2)))
+    tk = torch.from_numpy(np.ascontiguousarray(k[:T].transpose(1, 0, 2)))
+    tv = torch.from_numpy(np.ascontiguousarray(v[:T].transpose(1, 0, 2)))
+    ref = F.scaled_dot_product_attention(tq, tk, tv, is_causal=True).numpy().transpose(1, 0, 2).reshape(T, -1)
+    assert np.allclose(out0, ref, rtol=1e-12, atol=1e-13)
+
+
+def test_attention_special_cases():
+    rng = np.random.default_rng(4)
+    H, dh = 2, 4
+    v = rng.standard_normal((6, H, dh))
+    k = rng.standard_normal((6, H, dh))
+    # a single key: output is that value exactly
+    q = rng.standard_normal((1, H, dh))
+    assert np.array_equal(oracle.causal_attention(q, k[:1], v[:1], np.array([0])), v[0].reshape(1, -1))
+    # zero query: uniform weights -> running means of the values
+    out = oracle.causal_attention(np.zeros((6, H, dh)), k, v, np.arange(6))
+    means = np.cumsum(v, axis=0) / np.arange(1, 7)[:, None, None]
+    assert np.allclose(out, means.reshape(6, -1), rtol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# INT4: definitions, fixtures and exhaustive checks
+
+
+def _read_lines(path):
+    with open(path) as f:
+        return [ln.split("#")[0].strip() for ln in f if ln.split("#")[0].strip()]
+
+
+def test_nibble_table_matches_golden(golden_dir):
+    rows = _read_lines(os.path.join(golden_dir, "int4_nibbles.txt"))
+    table = {int(a, 16): int(b) for a, b in (r.split() for r in rows)}
+    assert len(table) == 16
+    for byte in range(256):
+        got = oracle.unpack_nibbles(np.array([[byte]], dtype=np.uint8))[0]
+        assert got[0] == table[byte & 0xF] and got[1] == table[byte >> 4]
+
+
+def test_pack_example_matches_golden(golden_dir):
+    rows = _read_lines(os.path.join(golden_dir, "int4_pack_example.txt"))
+    q = np.array([[int(t) for t in rows[0].split()]], dtype=np.int8)
+    want = np.array([[int(t, 16) for t in rows[1].split()]], dtype=np.uint8)
+    assert np.array_equal(oracle.pack_nibbles(q), want)
+    assert np.array_equal(oracle.unpack_nibbles(want), q)
+
+
+def test_pack_unpack_exhaustive_pairs():
+    vals = np.arange(-8, 8, dtype=np.int8)
+    a, b = np.meshgrid(vals, vals, indexing="ij")
+    q = np.stack([a.ravel(), b.ravel()], axis=1).reshape(1, -1)
+    assert np.array_equal(oracle.unpack_nibbles(oracle.pack_nibbles(q)), q)
+
+
+def test_dequant_exact_for_all_nibbles_and_all_finite_fp16_scales():
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    s = bits.view(np.float16)
+    s = s[np.isfinite(s)]                                     # 63,488 finite scales
+    assert s.size == 63488
+    q = np.arange(-8, 8, dtype=np.int8)
+    # one row per nibble value, one group per scale
+    Q = np.repeat(q[:, None], s.size * 128, axis=1)[:, ::128].repeat(128, axis=1)
+    S = np.broadcast_to(s[None, :], (16, s.size))
+    w = oracle.dequant_w4g128(Q, S)
+    exact = q.astype(np.float64)[:, None] * s.astype(np.float64)[None, :]
+    assert np.array_equal(w[:, ::128].astype(np.float64), exact)
+
+
+def test_quantizer_hand_example(golden_dir):
+    rows = _read_lines(os.path.join(golden_dir, "int4_quant_example.txt"))
+    scale_bits = int(rows[0].split()[1], 16)
+    w = np.zeros((1, 128), np.float32)
+    want = np.zeros(128, np.int8)
+    for r in rows[1:]:
+        i, x, qq = r.split()
+        w[0, int(i)] = np.float32(float(x))
+        want[int(i)] = int(qq)
+    q, s = oracle.quantize_w4g128(w)
+    assert s.view(np.uint16)[0, 0] == scale_bits
+    assert np.array_equal(q[0], want)
+
+
+def test_quantizer_properties():
+    w = synth.normal(7, 99, (64, 512), 0.02)
+    w[3, :128] = 0.0                                        # an all-zero group
+    q, s = oracle.quantize_w4g128(w)
+    assert q.min() >= -7 and q.max() <= 7
+    assert np.all(q[3, :128] == 0) and s[3, 0] == 0
+    sf = np.repeat(s.astype(np.float64), 128, axis=1)
+    err = np.abs(w.astype(np.float64) - q * sf)
+    # rounding to the nearest level: error at most half a step (plus fp32 division slack)
+    assert np.all(err <= sf * 0.5 * (1 + 1e-6) + 1e-12)
+    # the largest-magnitude element of every non-zero group lands on +-7
+    g = np.abs(q.reshape(64, 4, 128)).max(axis=2)
+    assert np.all(g[s > 0] == 7)
+
+
+# ---------------------------------------------------------------------------
+# argmax, depth clamp and active lists: brute force
+
+
+def test_argmax_ties_lowest_index():
+    x = np.array([[0.5, 2.0, 2.0, -1.0], [3.0, 3.0, 3.0, 3.0], [-5.0, -4.0, -4.5, -4.0]])
+    assert list(oracle.greedy_argmax(x)) == [1, 0, 1]
+    rng = np.random.default_rng(5)
+    y = rng.integers(0, 4, size=(50, 33)).astype(np.float32)
+    for r in range(50):
+        best = max(y[r])
+        assert oracle.greedy_argmax(y[r]) == min(i for i in range(33) if y[r, i] == best)
+
+
+def test_clamp_depths_brute_force():
+    rng = np.random.default_rng(6)
+    for _ in range(20):
+        req = rng.integers(1, 33, size=40)
+        L0 = int(rng.integers(1, 33))
+        out = oracle.clamp_depths(req, L0)
+        for i in range(40):
+            assert out[i] == min([L0] + list(req[: i + 1]))
+        assert np.all(np.diff(out) <= 0)
+
+
+def test_active_lists_brute_force():
+    rng = np.random.default_rng(7)
+    d = rng.choice([2, 4, 8, 16, 32], size=64)
+    lists = oracle.active_lists(d)
+    assert len(lists) == 32
+    for j, act in enumerate(lists, start=1):
+        assert list(act) == [r for r in range(64) if d[r] >= j]
+        assert len(act) == int(np.sum(d >= j))
+
+
+# ---------------------------------------------------------------------------
+# whole-model properties on the tiny fp32 model
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    spec = synth.SPECS[1]
+    w = synth.make_weights(spec, seed=0)
+    return w, oracle.OracleModel.from_weights(w)
+
+
+def _torch_block(Wb, h, pos, spec):
+    """Independent transcription with torch CPU routines: F.rms_norm, F.linear,
+    complex-number rotation for RoPE, F.scaled_dot_product_attention, F.silu."""
+    d, H, dh = spec.d_model, spec.n_heads, spec.head_dim
+    T = h.shape[0]
+    t = lambda a: torch.from_numpy(np.asarray(a, dtype=np.float64))
+    x = F.rms_norm(h, (d,), t(Wb["norm1"]), spec.rms_eps)
+    qkv = F.linear(x, t(Wb["wqkv"]))
+    q, k, v = qkv.split(d, dim=1)
+    half = dh // 2
+    inv = spec.rope_base ** (-torch.arange(half, dtype=torch.float64) * 2 / dh)
+    rot = torch.polar(torch.ones(T, half, dtype=torch.float64), torch.outer(t(pos), inv))
+
+    def rope(z):
+        z = z.reshape(T, H, dh)
+        c = torch.complex(z[..., :half], z[..., half:]) * rot[:, None, :]
+        return torch.cat([c.real, c.imag], dim=-1)
+
+    q, k, v = rope(q).transpose(0, 1), rope(k).transpose(0, 1), v.reshape(T, H, dh).transpose(0, 1)
+    o = F.scaled_dot_product_attention(q, k, v, is_causal=True).transpose(0, 1).reshape(T, d)
+    h = h + F.linear(o, t(Wb["wo"]))
+    x2 = F.rms_norm(h, (d,), t(Wb["norm2"]), spec.rms_eps)
+    return h + F.linear(F.silu(F.linear(x2, t(Wb["wgate"]))) * F.linear(x2, t(Wb["wup"])), t(Wb["wdown"]))
+
+
+@pytest.mark.parametrize("L", [1, 3])
+def test_model_matches_torch_transcription(tiny, L):
+    w, m = tiny
+    spec = w.spec
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 16, spec.vocab)
+    lane, hid, logits = oracle.prefill(m, toks, L, want_logits="all")
+    h = torch.from_numpy(w.embed[toks].astype(np.float64))
+    pos = np.arange(16)
+    h = _torch_block(w.blocks[0], h, pos, spec)
+    for _ in range(L):
+        h = _torch_block(w.blocks[1], h, pos, spec)
+    ref_logits = F.linear(F.rms_norm(h, (spec.d_model,), torch.ones(spec.d_model, dtype=torch.float64),
+                                     spec.rms_eps), torch.from_numpy(w.head.astype(np.float64)))
+    assert np.allclose(hid, h.numpy(), rtol=1e-12, atol=1e-13)
+    assert np.allclose(logits, ref_logits.numpy(), rtol=1e-11, atol=1e-13)
+
+
+def test_loop_equals_unrolled_stack(tiny):
+    """L iterations of the shared block == L explicit applications of copies of it."""
+    w, m = tiny
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 16, 256)
+    _, h_loop, _ = oracle.prefill(m, toks, 4, want_logits="none")
+    import copy
+    spec2 = copy.copy(w.spec)
+    spec2.n_loop = 4
+    m2 = copy.copy(m)
+    m2.spec = spec2
+    m2.blocks = [m.blocks[0]] + [m.blocks[1]] * 4
+    _, h_unrolled, _ = oracle.prefill(m2, toks, 1, want_logits="none")
+    assert np.array_equal(h_loop, h_unrolled)
+
+
+def test_causality(tiny):
+    w, m = tiny
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 16, 256)
+    _, h0, _ = oracle.prefill(m, toks, 3, want_logits="none")
+    for p in (5, 11):
+        t2 = toks.copy()
+        t2[p] = (t2[p] + 17) % 256
+        t2[-1] = (t2[-1] + 3) % 256
+        _, h1, _ = oracle.prefill(m, t2, 3, want_logits="none")
+        assert np.allclose(h1[:p], h0[:p], rtol=0, atol=1e-14)
+        assert not np.allclose(h1[p], h0[p])
+
+
+def test_mixed_batch_equals_each_lane_alone(tiny):
+    w, m = tiny
+    rng = np.random.default_rng(8)
+    seqs = [synth.tokens(0, 3000 + i, n, 256) for i, n in enumerate([5, 9, 3, 12])]
+    Ls = [4, 1, 7, 2]
+    h, logits, lists = oracle.forward_batch(m, seqs, Ls)
+    off = 0
+    for i, s in enumerate(seqs):
+        _, hi, li = oracle.prefill(m, s, Ls[i])
+        assert np.allclose(h[off:off + len(s)], hi, rtol=1e-13, atol=1e-14)
+        assert np.allclose(logits[i], li, rtol=1e-12, atol=1e-13)
+        off += len(s)
+    assert len(lists) == 7
+
+
+def test_cached_decode_equals_uncached_forward(tiny):
+    """The cached path agrees with re-running the whole extended sequence."""
+    w, m = tiny
+    toks = list(synth.tokens(0, synth.STREAM_TOKENS, 16, 256))
+    lane, _, _ = oracle.prefill(m, toks, 4)
+    seq = list(toks)
+    for step in range(5):
+        tok = lane.pending
+        h, logits, nxt, L = oracle.decode_step(m, lane, 4)
+        seq.append(tok)
+        _, h_full, lg_full = oracle.prefill(m, seq, 4, want_logits="last")
+        assert L == 4
+        assert np.allclose(h, h_full[-1], rtol=1e-11, atol=1e-13)
+        assert np.allclose(logits, lg_full, rtol=1e-10, atol=1e-12)
+        assert nxt == oracle.greedy_argmax(lg_full)
+
+
+def test_monotone_depth_cached_equals_ragged(tiny):
+    w, m = tiny
+    toks = list(synth.tokens(0, synth.STREAM_TOKENS, 16, 256))
+    L1 = 6
+    req = [9, 5, 5, 7, 3, 4, 1, 2]
+    deps = oracle.clamp_depths(req, L1)
+    lane, _, _ = oracle.prefill(m, toks, L1)
+    seq = list(toks)
+    hs = []
+    for r in req:
+        seq.append(lane.pending)
+        h, _, _, L = oracle.decode_step(m, lane, r)
+        hs.append(h)
+    assert list(deps) == [6, 5, 5, 5, 3, 3, 1, 1]
+    h_rag, lg = oracle.forward_ragged(m, seq, [L1] * 16 + list(deps))
+    assert np.allclose(np.array(hs), h_rag[16:], rtol=1e-11, atol=1e-13)
+
+
+def test_fp32_vs_fp64_conditioning_tiny(tiny):
+    """Intrinsic sensitivity of the synthetic model: the oracle in fp32 vs fp64."""
+    w, m64 = tiny
+    m32 = oracle.OracleModel.from_weights(w, dt=np.float32)
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 16, 256)
+    for L in (4, 32):
+        _, h64, _ = oracle.prefill(m64, toks, L, want_logits="none")
+        _, h32, _ = oracle.prefill(m32, toks, L, want_logits="none")
+        rel = np.linalg.norm(h32 - h64) / np.linalg.norm(h64)
+        assert rel < 1e-5, (L, rel)
+
+
+@pytest.mark.slow
+def test_fp32_vs_fp64_conditioning_int4_model():
+    """Same check on the 2048-wide INT4-loop model at L = 8 and 32 (32 tokens)."""
+    spec = synth.SPECS[2]
+    w = synth.make_weights(spec, 0)
+    m64 = oracle.OracleModel.from_weights(w)
+    m32 = oracle.OracleModel.from_weights(w, dt=np.float32)
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 32, spec.vocab)
+    for L in (8, 32):
+        _, h64, _ = oracle.prefill(m64, toks, L, want_logits="none")
+        _, h32, _ = oracle.prefill(m32, toks, L, want_logits="none")
+        rel = np.linalg.norm(h32 - h64) / np.linalg.norm(h64)
+        assert rel < 1e-4, (L, rel)
