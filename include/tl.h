@@ -1,0 +1,208 @@
+/*
+ * tl.h — C ABI of the MI355X (gfx950) looped-transformer runtime.
+ *
+ * The model is  embed -> pre blocks -> one shared loop block (or a stack of
+ * n_loop layers) applied L times -> post blocks -> final RMSNorm -> head
+ * ("Benchmark Comparison / vs generic runtimes" page, section "Where Generic
+ * Runtimes Lose On Looped Checkpoints").  L is an argument of every call, never
+ * a property of the weights ("Dynamic-L Inference" page, "The Core Idea").
+ *
+ * Conventions shared by every entry point
+ *   - Pointers named *_dev are device pointers (HIP device memory); *_host are
+ *     host pointers.  The caller owns every pointer it passes; the library never
+ *     frees them and keeps none of them after the call returns.
+ *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue device work
+ *     on it and return without waiting; device outputs are valid once the stream
+ *     has reached that point.  Host outputs are written before the call returns.
+ *   - On any status other than TL_OK nothing has been enqueued and the model and
+ *     its lanes are unchanged (validation happens before any device work), except
+ *     TL_E_HIP, which reports a failed HIP call; tl_last_error() gives the reason.
+ *   - A model is used by one host thread at a time.
+ *   - There are no silent fallbacks: an unsupported shape or dtype is an error.
+ */
+#ifndef TL_H
+#define TL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TL_ABI_VERSION 1
+
+typedef enum {
+  TL_OK = 0,
+  TL_E_ARG = -1,          /* an argument is out of range or a required pointer is NULL */
+  TL_E_OOM = -2,          /* the allocator returned NULL; model state unchanged */
+  TL_E_HIP = -3,          /* a HIP runtime call failed */
+  TL_E_STATE = -4,        /* lane state does not allow the call (never prefilled, full) */
+  TL_E_UNSUPPORTED = -5   /* shape, dtype or device not supported (not gfx950) */
+} tl_status;
+
+typedef enum {
+  TL_DT_F32 = 0,
+  TL_DT_F16 = 1,
+  TL_DT_BF16 = 2,
+  /* Symmetric INT4, one fp16 scale per 128 consecutive input features of an
+   * output row: s = fp16(max|w| / 7) (division in fp32), q = clamp(rint(w / s),
+   * -7, 7) with ties to even, w ~ q * s.  Min-max without calibration ("Benchmark
+   * Comparison" page, section 7); groups of 128 along K ("Benchmark Comparison"
+   * page, section 5: 16 groups at K = 2048).  Only for loop blocks, with
+   * F16 operands. */
+  TL_DT_W4G128 = 3
+} tl_dtype;
+
+/* Device memory provider.  alloc returns device memory of at least `bytes`
+ * (256-byte aligned) or NULL; dealloc releases it.  Passing NULL for both makes
+ * the library use hipMalloc/hipFree. */
+typedef void* (*tl_alloc_fn)(size_t bytes, void* user);
+typedef void (*tl_dealloc_fn)(void* ptr, void* user);
+
+typedef struct {
+  int32_t vocab, d_model, n_heads, head_dim, ffn;
+  int32_t n_pre, n_loop, n_post;   /* n_loop = layers in the shared loop stack (>= 1) */
+  float rms_eps;                   /* RMSNorm epsilon */
+  float rope_base;                 /* rotary base, e.g. 10000 */
+  int32_t act_dtype;               /* GEMM operand / activation storage: F32, F16 or BF16 */
+  int32_t boundary_dtype;          /* embed, head, pre and post blocks: F32, F16 or BF16 */
+  int32_t loop_dtype;              /* loop blocks: F32, F16, BF16 or W4G128 */
+  /* W4G128 only: 1 = dequantise the loop block once at load to fp16(q * s) and run
+   * it as an F16 block (the "FP16 body" of the "CLI Reference" page, environment
+   * variable TINYLOOP_EXPERIMENTAL_FP16_BODY). */
+  int32_t loop_fp16_body;
+  int32_t max_lanes;               /* lanes that can keep a KV cache between calls */
+  int32_t max_L;                   /* largest loop count accepted */
+  int32_t max_pos;                 /* positions 0 .. max_pos-1 are valid */
+  uint64_t kv_arena_bytes;         /* device bytes reserved for lane KV caches (0 = none) */
+} tl_config;
+
+/* Host weights of one block, canonical layout: linear weights are [out, in]
+ * row-major (y = x W^T).  wqkv rows are q (heads 0..H-1, head_dim rows each), then
+ * k, then v.  Norm gains are float32 [d_model].  Element type is the block's dtype;
+ * a W4G128 block is given as float32 and quantised at load. */
+typedef struct {
+  const float* norm1;
+  const float* norm2;
+  const void* wqkv;   /* [3 d, d] */
+  const void* wo;     /* [d, d]   */
+  const void* wgate;  /* [F, d]   */
+  const void* wup;    /* [F, d]   */
+  const void* wdown;  /* [d, F]   */
+} tl_block_weights;
+
+typedef struct {
+  const void* embed;          /* [V, d] boundary dtype */
+  const void* head;           /* [V, d] boundary dtype (may equal embed: tied) */
+  const float* final_norm;    /* [d] */
+  const tl_block_weights* blocks;  /* n_pre + n_loop + n_post, pipeline order */
+} tl_weights;
+
+typedef struct tl_model tl_model;
+
+/* Copy host weights to the device and prepare them for the kernels: INT4
+ * quantisation and repacking of W4G128 loop blocks, the optional FP16-body
+ * dequantisation, row orders that put each rotary pair and each gate/up pair in
+ * one tile, the rotary cos/sin table, the KV arena.  Synchronises `stream` before
+ * returning, so the host weights may be freed afterwards.
+ * Errors: TL_E_ARG (NULL pointer, inconsistent dims), TL_E_UNSUPPORTED (device is
+ * not gfx950, head_dim not even or above 128, 16-bit operands with head_dim not a
+ * multiple of 32 or d_model/ffn not a multiple of 32, W4G128 with K not a
+ * multiple of 128 or with non-F16 operands), TL_E_OOM, TL_E_HIP. */
+tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn alloc,
+                          tl_dealloc_fn dealloc, void* alloc_user, void* stream, tl_model** out);
+
+/* Causal forward of n_seqs packed sequences (scoring or prefill).
+ *   cu_seqlens_host [n_seqs+1]: prefix sums of sequence lengths (>= 1 each).
+ *   tokens_dev [total] int32 ids in [0, vocab).
+ *   L: loop count for every sequence, or per-sequence counts in seq_L_host
+ *      (non-NULL overrides L).  1 <= L <= max_L.  Sequences with different L run
+ *      in one pass; at iteration j only rows whose L >= j are computed and rows
+ *      leave after their last iteration ("Dynamic-L Inference" page, "L-Aware
+ *      Batching"; "Continuous Depth Batching" summary).
+ *   lanes_host [n_seqs] or NULL.  With lanes, each listed lane is (re)initialised
+ *      from its sequence: its KV cache keeps one slot per block application (pre
+ *      blocks, loop iteration x layer for j <= L, post blocks), capacity
+ *      seq_len + max_new_tokens positions ("CLI Reference" page, "Current
+ *      Behavior": max_seq = prompt + max_tokens), depth ceiling L, pending token =
+ *      greedy token at the last position.  Without lanes the call only scores.
+ *   out_hidden_dev [total, d] float32: residual stream after the last block
+ *      (before the final norm), or NULL.
+ *   out_logits_dev [n_seqs, V] float32 logits at each sequence's last position,
+ *      or NULL.
+ *   out_next_dev [n_seqs] int32 greedy token at the last position (lowest index on
+ *      ties), or NULL.
+ *   out_active_log_dev, or NULL: for j = 1..maxL the original row indices active
+ *      at iteration j, concatenated (sum_j n_j entries).
+ * Errors: TL_E_ARG, TL_E_STATE (seq_len + max_new_tokens > max_pos, KV arena
+ * full), TL_E_OOM, TL_E_HIP. */
+tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu_seqlens_host,
+                     const int32_t* tokens_dev, int32_t L, const int32_t* seq_L_host,
+                     const int32_t* lanes_host, int32_t max_new_tokens, float* out_hidden_dev,
+                     float* out_logits_dev, int32_t* out_next_dev, int32_t* out_active_log_dev,
+                     void* stream);
+
+/* One cached greedy decode step for n_lanes prefilled lanes.
+ *   per_lane_L_host [n_lanes]: requested depth; the effective depth is
+ *      min(request, lane ceiling) and becomes the new ceiling, so depth never rises
+ *      within a generation and every cache slot an iteration reads holds all
+ *      earlier positions ("CLI Reference" page, "generate", early-exit options:
+ *      monotonic clamping).
+ *   in_tokens_dev [n_lanes] int32 or NULL (NULL: each lane's pending token).
+ *   out_tokens_dev [n_lanes] int32: greedy next token (also the new pending token).
+ *   out_logits_dev [n_lanes, V] float32 or NULL; out_hidden_dev [n_lanes, d] or NULL.
+ *   out_eff_L_host [n_lanes] or NULL: effective depth used.
+ *   out_active_log_dev: as in tl_forward, over the lanes of this call.
+ * Errors: TL_E_ARG (lane out of range, repeated lane, L < 1), TL_E_STATE (lane
+ * never prefilled or full), TL_E_HIP. */
+tl_status tl_decode_step(tl_model* m, int32_t n_lanes, const int32_t* lanes_host,
+                         const int32_t* per_lane_L_host, const int32_t* in_tokens_dev,
+                         int32_t* out_tokens_dev, float* out_logits_dev, float* out_hidden_dev,
+                         int32_t* out_eff_L_host, int32_t* out_active_log_dev, void* stream);
+
+/* n_steps greedy tokens for each of n_lanes prefilled lanes, scheduled one loop
+ * iteration at a time across lanes (continuous depth batching: "Continuous Depth
+ * Batching" summary page).  Lanes whose token has finished its loop iterations pass
+ * through the boundary stages (post blocks, head, argmax, embedding, pre blocks)
+ * and re-enter the loop pool at iteration 1 with their next token while other lanes
+ * are still iterating.  Exits are known one tick ahead from the depth schedule.
+ *   L_req_host [n_lanes, n_steps]: requested depth of each new token; clamped
+ *      exactly as in tl_decode_step.  The results equal n_steps calls of
+ *      tl_decode_step with these requests; only the order of work differs.
+ *   out_tokens_dev [n_lanes, n_steps] int32.
+ *   out_eff_L_host [n_lanes, n_steps] or NULL.
+ * Errors: as tl_decode_step. */
+tl_status tl_decode_run(tl_model* m, int32_t n_lanes, const int32_t* lanes_host, int32_t n_steps,
+                        const int32_t* L_req_host, int32_t* out_tokens_dev,
+                        int32_t* out_eff_L_host, void* stream);
+
+/* Copy the device-resident INT4 weights of one W4G128 matrix back to canonical
+ * form, unpacked by the same device routine the GEMM uses: q_host [N, K] int8 and
+ * scale_bits_host [N, K/128] fp16 bit patterns.  matrix: 0 wqkv, 1 wo, 2 wgate,
+ * 3 wup, 4 wdown, in canonical row order.  Synchronous.
+ * Errors: TL_E_ARG (block not a W4G128 loop block), TL_E_HIP. */
+tl_status tl_export_w4(tl_model* m, int32_t block, int32_t matrix, int8_t* q_host,
+                       uint16_t* scale_bits_host);
+
+/* Release a lane's KV cache; the lane must be prefilled again before decoding. */
+tl_status tl_lane_release(tl_model* m, int32_t lane);
+
+/* Device bytes the model holds: weights, KV arena, workspaces. */
+tl_status tl_memory_info(tl_model* m, uint64_t* weight_bytes, uint64_t* kv_bytes,
+                         uint64_t* workspace_bytes);
+
+/* Synchronises stream and reports errors the kernels detected since the last
+ * check: a token id outside [0, vocab) (it was read as 0) gives TL_E_ARG. */
+tl_status tl_sync_errors(tl_model* m, void* stream);
+
+/* Waits for the model's own device work, frees everything the model holds. */
+void tl_free(tl_model* m);
+
+/* Message for the last non-OK status on this thread ("" if none). */
+const char* tl_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* TL_H */

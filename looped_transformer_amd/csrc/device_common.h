@@ -1,0 +1,50 @@
+// Device-side types and helpers shared by the gfx950 kernels of the runtime.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef _Float16 f16;
+typedef __bf16 bf16;
+typedef _Float16 half8 __attribute__((ext_vector_type(8)));
+typedef _Float16 half2v __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+
+#include "kernels.h"
+
+template <class T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
+template <class T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }  // RNE
+
+// Wave64 reductions (xor butterflies keep every lane holding the result).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
+  return v;
+}
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));
+  return v;
+}
+
+// Address of K (which = 0) or V (which = 1) for (row's lane, slot, head, row's pos).
+// Cache layout of one lane: [slot][K|V][head][position < cap][head_dim].
+template <class T>
+__device__ __forceinline__ T* kv_ptr(const KVParams& kv, const RowInfo& ri, int which, int head, int pos) {
+  const int slot = kv.s0 + kv.s1 * ri.iter;
+  const int64_t cap = kv.lane_cap[ri.lane];
+  const int64_t off = kv.lane_off[ri.lane] +
+                      ((int64_t)(slot * 2 + which) * kv.H + head) * cap * kv.dh + (int64_t)pos * kv.dh;
+  return reinterpret_cast<T*>(kv.base) + off;
+}
+
+// INT4 kernel layout: a 32-bit word holds 8 consecutive k of one output row as
+// offset-binary nibbles (q + 8); element 2i sits in bits [4i, 4i+4), element 2i+1
+// in bits [16+4i, 16+4i+4).  ((w >> 4i) & 0x000F000F) | 0x64006400 is then the
+// fp16 pair (1024 + q_2i + 8, 1024 + q_2i+1 + 8); subtracting 1032 gives q exactly.
+__device__ __forceinline__ half2v w4_pair(uint32_t w, int i) {
+  uint32_t b = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
+  half2v h = __builtin_bit_cast(half2v, b);
+  const half2v off = {(f16)1032.0f, (f16)1032.0f};
+  return h - off;
+}

@@ -1,0 +1,846 @@
+// Host engine of the looped-transformer runtime: weight preparation, the KV arena,
+// forward / decode passes scheduled one loop iteration at a time, and the C ABI.
+#include "engine.h"
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <numeric>
+
+using tl::BlockDev;
+using tl::Lane;
+using tl::MatDev;
+
+namespace {
+
+thread_local std::string g_err;
+
+tl_status fail(tl_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+#define HIPCHK(x)                                                                                  \
+  do {                                                                                             \
+    hipError_t e_ = (x);                                                                           \
+    if (e_ != hipSuccess) return fail(TL_E_HIP, "%s failed: %s (%s:%d)", #x, hipGetErrorString(e_), \
+                                      __FILE__, __LINE__);                                         \
+  } while (0)
+
+#define TRY(x)                        \
+  do {                                \
+    tl_status s_ = (x);               \
+    if (s_ != TL_OK) return s_;       \
+  } while (0)
+
+int dtype_size(int dt) { return dt == DT_F32 ? 4 : 2; }
+
+void* dev_alloc(tl_model* m, size_t bytes) {
+  bytes = (bytes + 255) & ~(size_t)255;
+  if (bytes == 0) bytes = 256;
+  void* p = nullptr;
+  if (m->alloc) {
+    p = m->alloc(bytes, m->user);
+  } else if (hipMalloc(&p, bytes) != hipSuccess) {
+    (void)hipGetLastError();
+    p = nullptr;
+  }
+  if (p) m->owned[p] = bytes;
+  return p;
+}
+
+void dev_free(tl_model* m, void* p) {
+  if (!p) return;
+  auto it = m->owned.find(p);
+  if (it == m->owned.end()) return;
+  m->owned.erase(it);
+  if (m->dealloc) m->dealloc(p, m->user);
+  else (void)hipFree(p);
+}
+
+// ----------------------------------------------------------------- staging
+// Host data of one call is assembled here and copied in one transfer to a device
+// area; device pointers are offsets into that area.
+struct Stage {
+  std::vector<uint8_t> buf;
+  size_t add(const void* data, size_t bytes) {
+    size_t off = (buf.size() + 255) & ~(size_t)255;
+    buf.resize(off + bytes);
+    if (bytes) std::memcpy(buf.data() + off, data, bytes);
+    return off;
+  }
+  template <class T> size_t add(const std::vector<T>& v) { return add(v.data(), v.size() * sizeof(T)); }
+};
+
+template <class T> T* staged(tl_model* m, size_t off) {
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(m->stage_dev) + off);
+}
+
+tl_status stage_upload(tl_model* m, const Stage& st, hipStream_t s) {
+  const size_t need = std::max<size_t>(st.buf.size(), 256);
+  if (need > m->stage_bytes) {
+    if (m->stage_host) {
+      HIPCHK(hipStreamSynchronize(s));
+      if (m->last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
+      HIPCHK(hipHostFree(m->stage_host));
+      m->stage_host = nullptr;
+      dev_free(m, m->stage_dev);
+      m->stage_dev = nullptr;
+    }
+    size_t cap = std::max<size_t>(need * 2, 1 << 20);
+    HIPCHK(hipHostMalloc(&m->stage_host, cap, hipHostMallocDefault));
+    m->stage_dev = dev_alloc(m, cap);
+    if (!m->stage_dev) return fail(TL_E_OOM, "staging area of %zu bytes", cap);
+    m->stage_bytes = cap;
+  } else {
+    HIPCHK(hipEventSynchronize(m->stage_done));
+  }
+  std::memcpy(m->stage_host, st.buf.data(), st.buf.size());
+  HIPCHK(hipMemcpyAsync(m->stage_dev, m->stage_host, st.buf.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(hipEventRecord(m->stage_done, s));
+  m->last_stream = s;
+  return TL_OK;
+}
+
+// ----------------------------------------------------------------- workspace
+tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStream_t s) {
+  auto& w = m->ws;
+  if (rows <= w.rows && outs <= w.outs && kv_scratch <= w.kv_scratch_elems) return TL_OK;
+  const tl_config& c = m->cfg;
+  const int R = std::max(w.rows, (rows + 63) / 64 * 64);
+  const int O = std::max(w.outs, (outs + 63) / 64 * 64);
+  const int64_t KS = std::max(w.kv_scratch_elems, kv_scratch);
+  HIPCHK(hipStreamSynchronize(s));
+  if (m->last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
+  void* olds[] = {w.hA, w.hB, w.hX, w.hE, w.x16, w.q16, w.o16, w.u16, w.xh, w.rowsA, w.rowsB,
+                  w.dest, w.count, w.tok, w.part_v, w.part_i, w.kv_scratch};
+  for (void* p : olds) dev_free(m, p);
+  w = tl::Workspace{};
+  m->ws_bytes = 0;
+  const int64_t d = c.d_model, F = c.ffn;
+  const int tiles = (c.vocab + 63) / 64;   // upper bound over tile widths (64 or 128)
+  struct Req { void** p; size_t bytes; } reqs[] = {
+      {(void**)&w.hA, (size_t)R * d * 4},           {(void**)&w.hB, (size_t)R * d * 4},
+      {(void**)&w.hX, (size_t)R * d * 4},           {(void**)&w.hE, (size_t)R * d * 4},
+      {&w.x16, (size_t)R * d * m->esz},             {&w.q16, (size_t)R * d * m->esz},
+      {&w.o16, (size_t)R * d * m->esz},             {&w.u16, (size_t)R * F * m->esz},
+      {&w.xh, (size_t)std::max(O, 1) * d * m->esz}, {(void**)&w.rowsA, (size_t)R * sizeof(RowInfo)},
+      {(void**)&w.rowsB, (size_t)R * sizeof(RowInfo)}, {(void**)&w.dest, (size_t)R * 4},
+      {(void**)&w.count, 256},                      {(void**)&w.tok, (size_t)R * 4},
+      {(void**)&w.part_v, (size_t)std::max(O, 1) * tiles * 4},
+      {(void**)&w.part_i, (size_t)std::max(O, 1) * tiles * 4},
+      {&w.kv_scratch, (size_t)std::max<int64_t>(KS, 1) * m->esz},
+  };
+  for (auto& r : reqs) {
+    *r.p = dev_alloc(m, r.bytes);
+    if (!*r.p) {
+      for (auto& q : reqs) { dev_free(m, *q.p); *q.p = nullptr; }
+      w = tl::Workspace{};
+      return fail(TL_E_OOM, "workspace allocation of %zu bytes failed", r.bytes);
+    }
+    m->ws_bytes += r.bytes;
+  }
+  w.rows = R;
+  w.outs = O;
+  w.kv_scratch_elems = KS;
+  w.part_tiles = tiles;
+  return TL_OK;
+}
+
+// ----------------------------------------------------------------- passes
+tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, hipStream_t s) {
+  GemmArgs g{};
+  g.A = A;
+  g.M = M;
+  g.N = W.N;
+  g.K = W.K;
+  g.B = W.dense;
+  g.Bw4 = W.dense ? nullptr : W.w4;
+  g.Bs = W.s4;
+  e.pair_g = m->G;
+  HIPCHK(launch_gemm(m->act, g, e, s));
+  return TL_OK;
+}
+
+tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, const KVParams& kv, hipStream_t s) {
+  if (n <= 0) return TL_OK;
+  const tl_config& c = m->cfg;
+  const BlockDev& B = m->blocks[b];
+  auto& w = m->ws;
+  HIPCHK(launch_rmsnorm(m->act, h, B.norm1, nullptr, n, c.d_model, c.rms_eps, w.x16, s));
+  GemmEpi e{};
+  e.kind = EPI_QKV;
+  e.q_out = w.q16;
+  e.kv = kv;
+  e.rows = rows;
+  e.rope_cos = m->rope_cos;
+  e.rope_sin = m->rope_sin;
+  e.d = c.d_model;
+  e.H = c.n_heads;
+  e.dh = c.head_dim;
+  TRY(gemm(m, w.x16, n, B.qkv, e, s));
+  HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, s));
+  GemmEpi r{};
+  r.kind = EPI_RESID;
+  r.h = h;
+  r.ldh = c.d_model;
+  TRY(gemm(m, w.o16, n, B.o, r, s));
+  HIPCHK(launch_rmsnorm(m->act, h, B.norm2, nullptr, n, c.d_model, c.rms_eps, w.x16, s));
+  GemmEpi sw{};
+  sw.kind = EPI_SWIGLU;
+  sw.u_out = w.u16;
+  sw.F = c.ffn;
+  TRY(gemm(m, w.x16, n, B.gu, sw, s));
+  TRY(gemm(m, w.u16, n, B.down, r, s));
+  return TL_OK;
+}
+
+struct Pass {
+  int n = 0;
+  const int32_t* tokens = nullptr;   // device [n]
+  const RowInfo* rows0 = nullptr;    // device, caller order, iter = 1
+  std::vector<int> n_active;         // n_j for j = 1..maxL
+  KVParams kv{};
+  bool scoring = false;              // one reusable slot per sequence
+  float* final_h = nullptr;          // [n, d], caller order
+  int32_t* log = nullptr;
+};
+
+tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
+  const tl_config& c = m->cfg;
+  auto& w = m->ws;
+  const int d = c.d_model;
+  HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, w.hA, m->d_err, c.vocab, s));
+  KVParams kv = p.kv;
+  for (int b = 0; b < c.n_pre; ++b) {
+    kv.s0 = p.scoring ? 0 : b;
+    kv.s1 = 0;
+    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s));
+  }
+  float* h = w.hA;
+  float* hn = w.hB;
+  const RowInfo* rows = p.rows0;
+  RowInfo* rbuf[2] = {w.rowsA, w.rowsB};
+  int flip = 0;
+  int64_t log_off = 0;
+  for (size_t j = 1; j <= p.n_active.size(); ++j) {
+    const int nj = p.n_active[j - 1];
+    if (p.log && j == 1) HIPCHK(launch_write_orig(rows, nj, p.log, s));
+    for (int l = 0; l < c.n_loop; ++l) {
+      kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + l - c.n_loop;
+      kv.s1 = p.scoring ? 0 : c.n_loop;
+      TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s));
+    }
+    RowInfo* rout = rbuf[flip];
+    int32_t* logn = p.log ? p.log + log_off + nj : nullptr;
+    HIPCHK(launch_compact(rows, nj, rout, w.dest, w.count, logn, s));
+    HIPCHK(launch_move_rows(h, w.dest, rows, nj, d, hn, p.final_h, s));
+    log_off += nj;
+    rows = rout;
+    flip ^= 1;
+    std::swap(h, hn);
+  }
+  for (int b = 0; b < c.n_post; ++b) {
+    kv.s0 = p.scoring ? 0 : c.n_pre + b;
+    kv.s1 = 0;
+    TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s));
+  }
+  return TL_OK;
+}
+
+// Final norm on the selected rows, head GEMM, greedy token (lowest index on ties).
+tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out, float* logits, int32_t* out_tok,
+                   const int32_t* pend_lanes, hipStream_t s) {
+  if (n_out <= 0) return TL_OK;
+  const tl_config& c = m->cfg;
+  auto& w = m->ws;
+  HIPCHK(launch_rmsnorm(m->act, h, m->final_norm, gather, n_out, c.d_model, c.rms_eps, w.xh, s));
+  const int tiles = gemm_head_tiles(m->act, n_out, c.vocab);
+  GemmArgs g{};
+  g.A = w.xh;
+  g.M = n_out;
+  g.N = c.vocab;
+  g.K = c.d_model;
+  g.B = m->head;
+  GemmEpi e{};
+  e.kind = EPI_HEAD;
+  e.logits = logits;
+  e.ldl = c.vocab;
+  e.part_val = w.part_v;
+  e.part_idx = w.part_i;
+  e.n_tiles = tiles;
+  HIPCHK(launch_gemm(m->act, g, e, s));
+  if (out_tok || pend_lanes)
+    HIPCHK(launch_argmax_reduce(w.part_v, w.part_i, n_out, tiles, out_tok, pend_lanes ? m->d_pending : nullptr,
+                                pend_lanes, s));
+  return TL_OK;
+}
+
+std::vector<int> active_counts(const std::vector<int>& depth) {
+  int mx = 0;
+  for (int v : depth) mx = std::max(mx, v);
+  std::vector<int> n(mx, 0);
+  for (int v : depth)
+    for (int j = 1; j <= v; ++j) n[j - 1]++;
+  return n;
+}
+
+int lane_slots(const tl_config& c, int ceiling) { return c.n_pre + c.n_post + c.n_loop * ceiling; }
+
+uint64_t lane_elems(const tl_model* m, int ceiling, int cap) {
+  const tl_config& c = m->cfg;
+  uint64_t e = (uint64_t)lane_slots(c, ceiling) * 2ull * c.n_heads * (uint64_t)cap * c.head_dim;
+  return (e + 63) / 64 * 64;
+}
+
+// Row order used by the paired epilogues: each rotary pair (i, i + dh/2) of q and k
+// heads, and each (gate_i, up_i), lands G columns apart inside one 2G-wide chunk.
+std::vector<int32_t> perm_qkv(const tl_config& c, int G) {
+  const int d = c.d_model, dh = c.head_dim, half = dh / 2;
+  std::vector<int32_t> p(3 * d);
+  for (int n = 0; n < 3 * d; ++n) {
+    const int sect = n / d, within = n % d;
+    if (sect == 2) {
+      p[n] = n;
+      continue;
+    }
+    const int head = within / dh, cd = within % dh;
+    const int ci = cd / G, off = cd % G, pi = ci / 2, which = ci % 2;
+    p[n] = sect * d + head * dh + which * half + pi * G + off;
+  }
+  return p;
+}
+
+std::vector<int32_t> perm_gu(const tl_config& c, int G) {
+  const int F = c.ffn;
+  std::vector<int32_t> p(2 * F);
+  for (int n = 0; n < 2 * F; ++n) {
+    const int ci = n / G, off = n % G, pi = ci / 2, which = ci % 2;
+    p[n] = which * F + pi * G + off;
+  }
+  return p;
+}
+
+tl_status upload_bytes(tl_model* m, void** dst, const void* src, size_t bytes, hipStream_t s) {
+  *dst = dev_alloc(m, bytes);
+  if (!*dst) return fail(TL_E_OOM, "weights: %zu bytes", bytes);
+  m->weight_bytes += bytes;
+  HIPCHK(hipMemcpyAsync(*dst, src, bytes, hipMemcpyHostToDevice, s));
+  return TL_OK;
+}
+
+// Upload one matrix (or a stacked pair) in canonical order and produce the kernel layout.
+tl_status prepare_matrix(tl_model* m, MatDev& md, const void* src0, const void* src1, int N, int K, int dtype,
+                         bool w4, bool fp16_body, const int32_t* perm_dev, hipStream_t s,
+                         std::vector<void*>& temps) {
+  md.N = N;
+  md.K = K;
+  md.perm = const_cast<int32_t*>(perm_dev);
+  const int in_esz = w4 ? 4 : dtype_size(dtype);
+  const size_t half_bytes = (size_t)(src1 ? N / 2 : N) * K * in_esz;
+  void* canon = dev_alloc(m, (size_t)N * K * in_esz);
+  if (!canon) return fail(TL_E_OOM, "weight staging");
+  temps.push_back(canon);
+  HIPCHK(hipMemcpyAsync(canon, src0, half_bytes, hipMemcpyHostToDevice, s));
+  if (src1)
+    HIPCHK(hipMemcpyAsync(static_cast<uint8_t*>(canon) + half_bytes, src1, half_bytes, hipMemcpyHostToDevice, s));
+  if (w4) {
+    const size_t wbytes = (size_t)N * K / 2, sbytes = (size_t)N * (K / 128) * 2;
+    md.w4 = static_cast<uint32_t*>(dev_alloc(m, wbytes));
+    md.s4 = static_cast<uint16_t*>(dev_alloc(m, sbytes));
+    if (!md.w4 || !md.s4) return fail(TL_E_OOM, "INT4 weights");
+    m->weight_bytes += wbytes + sbytes;
+    HIPCHK(launch_quant_w4(static_cast<const float*>(canon), perm_dev, N, K, md.w4, md.s4, s));
+    if (fp16_body) {
+      md.dense = dev_alloc(m, (size_t)N * K * 2);
+      if (!md.dense) return fail(TL_E_OOM, "FP16 body");
+      m->weight_bytes += (size_t)N * K * 2;
+      HIPCHK(launch_w4_to_f16(md.w4, md.s4, N, K, static_cast<uint16_t*>(md.dense), s));
+    }
+    return TL_OK;
+  }
+  const size_t bytes = (size_t)N * K * in_esz;
+  md.dense = dev_alloc(m, bytes);
+  if (!md.dense) return fail(TL_E_OOM, "dense weights");
+  m->weight_bytes += bytes;
+  if (perm_dev) HIPCHK(launch_permute_rows(in_esz, canon, perm_dev, N, K, md.dense, s));
+  else HIPCHK(hipMemcpyAsync(md.dense, canon, bytes, hipMemcpyDeviceToDevice, s));
+  return TL_OK;
+}
+
+tl_status validate_config(const tl_config* c) {
+  if (c->vocab < 1 || c->d_model < 1 || c->n_heads < 1 || c->head_dim < 2 || c->ffn < 1)
+    return fail(TL_E_ARG, "dimensions must be positive");
+  if (c->d_model != c->n_heads * c->head_dim) return fail(TL_E_ARG, "d_model != n_heads * head_dim");
+  if (c->n_pre < 0 || c->n_post < 0 || c->n_loop < 1) return fail(TL_E_ARG, "block counts");
+  if (c->max_L < 1 || c->max_pos < 1 || c->max_lanes < 0) return fail(TL_E_ARG, "max_L / max_pos / max_lanes");
+  if (c->act_dtype < DT_F32 || c->act_dtype > DT_BF16) return fail(TL_E_UNSUPPORTED, "act_dtype");
+  if (c->boundary_dtype != c->act_dtype) return fail(TL_E_UNSUPPORTED, "boundary dtype must equal act dtype");
+  if (c->loop_dtype != c->act_dtype && !(c->loop_dtype == DT_W4G128 && c->act_dtype == DT_F16))
+    return fail(TL_E_UNSUPPORTED, "loop dtype must equal act dtype, or W4G128 with F16 operands");
+  if (c->loop_fp16_body && c->loop_dtype != DT_W4G128) return fail(TL_E_ARG, "loop_fp16_body needs W4G128");
+  if (c->head_dim % 2 || c->head_dim > 128) return fail(TL_E_UNSUPPORTED, "head_dim must be even and <= 128");
+  if (c->d_model % 8 || c->ffn % 8) return fail(TL_E_UNSUPPORTED, "d_model and ffn must be multiples of 8");
+  if (c->act_dtype == DT_F32) {
+    if (c->head_dim % 4) return fail(TL_E_UNSUPPORTED, "fp32 head_dim must be a multiple of 4");
+  } else {
+    if (c->head_dim % 32 || c->ffn % 16) return fail(TL_E_UNSUPPORTED, "16-bit: head_dim % 32, ffn % 16");
+  }
+  if (c->loop_dtype == DT_W4G128 && (c->d_model % 128 || c->ffn % 128))
+    return fail(TL_E_UNSUPPORTED, "W4G128 needs d_model and ffn multiples of 128");
+  return TL_OK;
+}
+
+}  // namespace
+
+// ----------------------------------------------------------------- KV arena
+namespace tl {
+void KvArena::reset(uint64_t total) {
+  total_ = total;
+  free_.clear();
+  if (total) free_[0] = total;
+}
+bool KvArena::alloc(uint64_t n, uint64_t* off) {
+  for (auto it = free_.begin(); it != free_.end(); ++it) {
+    if (it->second >= n) {
+      *off = it->first;
+      const uint64_t rest = it->second - n, o = it->first + n;
+      free_.erase(it);
+      if (rest) free_[o] = rest;
+      return true;
+    }
+  }
+  return false;
+}
+void KvArena::release(uint64_t off, uint64_t n) {
+  if (!n) return;
+  auto it = free_.emplace(off, n).first;
+  auto nx = std::next(it);
+  if (nx != free_.end() && it->first + it->second == nx->first) {
+    it->second += nx->second;
+    free_.erase(nx);
+  }
+  if (it != free_.begin()) {
+    auto pv = std::prev(it);
+    if (pv->first + pv->second == it->first) {
+      pv->second += it->second;
+      free_.erase(it);
+    }
+  }
+}
+}  // namespace tl
+
+// ----------------------------------------------------------------- C ABI
+extern "C" {
+
+const char* tl_last_error(void) { return g_err.c_str(); }
+
+tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn alloc, tl_dealloc_fn dealloc,
+                          void* alloc_user, void* stream, tl_model** out) {
+  g_err.clear();
+  if (!cfg || !w || !out) return fail(TL_E_ARG, "NULL argument");
+  *out = nullptr;
+  if ((alloc == nullptr) != (dealloc == nullptr)) return fail(TL_E_ARG, "alloc and dealloc must both be set or NULL");
+  TRY(validate_config(cfg));
+  const int nb = cfg->n_pre + cfg->n_loop + cfg->n_post;
+  if (!w->embed || !w->head || !w->final_norm || !w->blocks) return fail(TL_E_ARG, "NULL weight pointer");
+  for (int b = 0; b < nb; ++b) {
+    const tl_block_weights& bw = w->blocks[b];
+    if (!bw.norm1 || !bw.norm2 || !bw.wqkv || !bw.wo || !bw.wgate || !bw.wup || !bw.wdown)
+      return fail(TL_E_ARG, "NULL pointer in block %d", b);
+  }
+  int dev = 0;
+  HIPCHK(hipGetDevice(&dev));
+  hipDeviceProp_t prop;
+  HIPCHK(hipGetDeviceProperties(&prop, dev));
+  if (std::strncmp(prop.gcnArchName, "gfx950", 6) != 0)
+    return fail(TL_E_UNSUPPORTED, "device %s is not gfx950", prop.gcnArchName);
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  tl_model* m = new tl_model();
+  m->cfg = *cfg;
+  m->alloc = alloc;
+  m->dealloc = dealloc;
+  m->user = alloc_user;
+  m->act = cfg->act_dtype;
+  m->G = m->act == DT_F32 ? 1 : 16;
+  m->esz = dtype_size(m->act);
+  std::vector<void*> temps;
+  auto cleanup_fail = [&](tl_status st) {
+    std::string msg = g_err;
+    (void)hipStreamSynchronize(s);
+    tl_free(m);
+    g_err = msg;
+    return st;
+  };
+#define LTRY(x)                          \
+  do {                                   \
+    tl_status s_ = (x);                  \
+    if (s_ != TL_OK) return cleanup_fail(s_); \
+  } while (0)
+#define LHIP(x)                                                                                        \
+  do {                                                                                                 \
+    hipError_t e_ = (x);                                                                               \
+    if (e_ != hipSuccess)                                                                              \
+      return cleanup_fail(fail(TL_E_HIP, "%s failed: %s", #x, hipGetErrorString(e_)));                \
+  } while (0)
+
+  const tl_config& c = m->cfg;
+  const int64_t d = c.d_model, F = c.ffn, V = c.vocab;
+  const int besz = dtype_size(c.boundary_dtype);
+  LTRY(upload_bytes(m, &m->embed, w->embed, (size_t)V * d * besz, s));
+  if (w->head == w->embed) m->head = m->embed;
+  else LTRY(upload_bytes(m, &m->head, w->head, (size_t)V * d * besz, s));
+  void* fn = nullptr;
+  LTRY(upload_bytes(m, &fn, w->final_norm, (size_t)d * 4, s));
+  m->final_norm = static_cast<float*>(fn);
+
+  // row orders of the paired epilogues
+  const std::vector<int32_t> pq = perm_qkv(c, m->G), pg = perm_gu(c, m->G);
+  void *pq_dev = nullptr, *pg_dev = nullptr;
+  LTRY(upload_bytes(m, &pq_dev, pq.data(), pq.size() * 4, s));
+  LTRY(upload_bytes(m, &pg_dev, pg.data(), pg.size() * 4, s));
+
+  m->blocks.resize(nb);
+  for (int b = 0; b < nb; ++b) {
+    const tl_block_weights& bw = w->blocks[b];
+    BlockDev& B = m->blocks[b];
+    B.kind = b < c.n_pre ? 0 : (b < c.n_pre + c.n_loop ? 1 : 2);
+    const int dt = B.kind == 1 ? c.loop_dtype : c.boundary_dtype;
+    const bool w4 = dt == DT_W4G128;
+    const bool body = w4 && c.loop_fp16_body;
+    B.is_w4 = w4;
+    void* n1 = nullptr;
+    void* n2 = nullptr;
+    LTRY(upload_bytes(m, &n1, bw.norm1, (size_t)d * 4, s));
+    LTRY(upload_bytes(m, &n2, bw.norm2, (size_t)d * 4, s));
+    B.norm1 = static_cast<float*>(n1);
+    B.norm2 = static_cast<float*>(n2);
+    LTRY(prepare_matrix(m, B.qkv, bw.wqkv, nullptr, 3 * d, d, dt, w4, body, static_cast<int32_t*>(pq_dev), s, temps));
+    LTRY(prepare_matrix(m, B.o, bw.wo, nullptr, d, d, dt, w4, body, nullptr, s, temps));
+    LTRY(prepare_matrix(m, B.gu, bw.wgate, bw.wup, 2 * F, d, dt, w4, body, static_cast<int32_t*>(pg_dev), s, temps));
+    LTRY(prepare_matrix(m, B.down, bw.wdown, nullptr, d, F, dt, w4, body, nullptr, s, temps));
+    // Free the canonical copies as soon as their kernels have consumed them.
+    LHIP(hipStreamSynchronize(s));
+    for (void* t : temps) dev_free(m, t);
+    temps.clear();
+  }
+
+  // rotary table: cos/sin of p * base^(-2i/dh) in double, stored fp32
+  {
+    const int half = c.head_dim / 2;
+    std::vector<float> cs((size_t)c.max_pos * half), sn((size_t)c.max_pos * half);
+    for (int p = 0; p < c.max_pos; ++p)
+      for (int i = 0; i < half; ++i) {
+        const double th = std::pow((double)c.rope_base, -2.0 * i / c.head_dim);
+        cs[(size_t)p * half + i] = (float)std::cos(p * th);
+        sn[(size_t)p * half + i] = (float)std::sin(p * th);
+      }
+    void *a = nullptr, *b = nullptr;
+    LTRY(upload_bytes(m, &a, cs.data(), cs.size() * 4, s));
+    LTRY(upload_bytes(m, &b, sn.data(), sn.size() * 4, s));
+    m->rope_cos = static_cast<float*>(a);
+    m->rope_sin = static_cast<float*>(b);
+  }
+
+  // KV arena and lane tables
+  const uint64_t kv_elems = c.kv_arena_bytes / m->esz;
+  if (kv_elems) {
+    m->kv_base = dev_alloc(m, kv_elems * m->esz);
+    if (!m->kv_base) return cleanup_fail(fail(TL_E_OOM, "KV arena of %llu bytes", (unsigned long long)c.kv_arena_bytes));
+    m->kv_bytes = kv_elems * m->esz;
+  }
+  m->arena.reset(kv_elems);
+  const int ml = std::max(c.max_lanes, 1);
+  m->lanes.assign(ml, Lane{});
+  m->h_lane_off.assign(ml, 0);
+  m->h_lane_cap.assign(ml, 0);
+  m->d_lane_off = static_cast<int64_t*>(dev_alloc(m, ml * 8));
+  m->d_lane_cap = static_cast<int32_t*>(dev_alloc(m, ml * 4));
+  m->d_pending = static_cast<int32_t*>(dev_alloc(m, ml * 4));
+  m->d_err = static_cast<int32_t*>(dev_alloc(m, 256));
+  if (!m->d_lane_off || !m->d_lane_cap || !m->d_pending || !m->d_err) return cleanup_fail(fail(TL_E_OOM, "lane tables"));
+  LHIP(hipMemsetAsync(m->d_lane_off, 0, ml * 8, s));
+  LHIP(hipMemsetAsync(m->d_lane_cap, 0, ml * 4, s));
+  LHIP(hipMemsetAsync(m->d_pending, 0, ml * 4, s));
+  LHIP(hipMemsetAsync(m->d_err, 0, 256, s));
+  LHIP(hipEventCreateWithFlags(&m->stage_done, hipEventDisableTiming));
+  LHIP(hipStreamSynchronize(s));
+  *out = m;
+  return TL_OK;
+#undef LTRY
+#undef LHIP
+}
+
+void tl_free(tl_model* m) {
+  if (!m) return;
+  (void)hipDeviceSynchronize();
+  std::vector<void*> ps;
+  for (auto& kv : m->owned) ps.push_back(kv.first);
+  for (void* p : ps) dev_free(m, p);
+  if (m->stage_host) (void)hipHostFree(m->stage_host);
+  if (m->stage_done) (void)hipEventDestroy(m->stage_done);
+  delete m;
+}
+
+tl_status tl_memory_info(tl_model* m, uint64_t* weight_bytes, uint64_t* kv_bytes, uint64_t* workspace_bytes) {
+  if (!m) return fail(TL_E_ARG, "NULL model");
+  if (weight_bytes) *weight_bytes = m->weight_bytes;
+  if (kv_bytes) *kv_bytes = m->kv_bytes;
+  if (workspace_bytes) *workspace_bytes = m->ws_bytes;
+  return TL_OK;
+}
+
+tl_status tl_lane_release(tl_model* m, int32_t lane) {
+  g_err.clear();
+  if (!m) return fail(TL_E_ARG, "NULL model");
+  if (lane < 0 || lane >= m->cfg.max_lanes) return fail(TL_E_ARG, "lane %d out of range", lane);
+  Lane& L = m->lanes[lane];
+  if (L.live) m->arena.release(L.off, L.elems);
+  L = Lane{};
+  return TL_OK;
+}
+
+tl_status tl_sync_errors(tl_model* m, void* stream) {
+  g_err.clear();
+  if (!m) return fail(TL_E_ARG, "NULL model");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t flag = 0;
+  HIPCHK(hipStreamSynchronize(s));
+  HIPCHK(hipMemcpy(&flag, m->d_err, 4, hipMemcpyDeviceToHost));
+  if (flag) {
+    HIPCHK(hipMemset(m->d_err, 0, 4));
+    return fail(TL_E_ARG, "a token id was outside [0, vocab) (treated as 0)");
+  }
+  return TL_OK;
+}
+
+tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32_t* tokens, int32_t L,
+                     const int32_t* seq_L, const int32_t* lanes, int32_t max_new, float* out_hidden,
+                     float* out_logits, int32_t* out_next, int32_t* out_log, void* stream) {
+  g_err.clear();
+  if (!m || !cu || !tokens) return fail(TL_E_ARG, "NULL argument");
+  const tl_config& c = m->cfg;
+  if (n_seqs < 1) return fail(TL_E_ARG, "n_seqs must be >= 1");
+  if (cu[0] != 0) return fail(TL_E_ARG, "cu_seqlens[0] must be 0");
+  std::vector<int> Ls(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int len = cu[i + 1] - cu[i];
+    if (len < 1) return fail(TL_E_ARG, "sequence %d is empty", i);
+    Ls[i] = seq_L ? seq_L[i] : L;
+    if (Ls[i] < 1 || Ls[i] > c.max_L) return fail(TL_E_ARG, "L = %d outside [1, %d]", Ls[i], c.max_L);
+    const int need = len + (lanes ? max_new : 0);
+    if (need > c.max_pos) return fail(TL_E_STATE, "sequence %d needs %d positions > max_pos %d", i, need, c.max_pos);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = cu[n_seqs];
+
+  // lane plan on a copy of the arena so that a failure leaves the state unchanged
+  tl::KvArena arena = m->arena;
+  std::vector<Lane> new_lanes;
+  if (lanes) {
+    if (max_new < 0) return fail(TL_E_ARG, "max_new_tokens < 0");
+    std::vector<char> seen(c.max_lanes, 0);
+    for (int i = 0; i < n_seqs; ++i) {
+      const int l = lanes[i];
+      if (l < 0 || l >= c.max_lanes) return fail(TL_E_ARG, "lane %d out of range [0, %d)", l, c.max_lanes);
+      if (seen[l]) return fail(TL_E_ARG, "lane %d listed twice", l);
+      seen[l] = 1;
+      if (m->lanes[l].live) arena.release(m->lanes[l].off, m->lanes[l].elems);
+    }
+    for (int i = 0; i < n_seqs; ++i) {
+      Lane ln;
+      ln.live = true;
+      ln.len = cu[i + 1] - cu[i];
+      ln.cap = ln.len + max_new;
+      ln.ceiling = Ls[i];
+      ln.nslots = lane_slots(c, Ls[i]);
+      ln.elems = lane_elems(m, Ls[i], ln.cap);
+      if (!arena.alloc(ln.elems, &ln.off))
+        return fail(TL_E_STATE, "KV arena full (lane %d needs %llu elements)", lanes[i], (unsigned long long)ln.elems);
+      new_lanes.push_back(ln);
+    }
+  }
+  const bool want_head = out_logits || out_next || lanes;
+  const int n_out = want_head ? n_seqs : 0;
+  TRY(ensure_ws(m, T, n_out, lanes ? 0 : (int64_t)T * 2 * c.d_model, s));
+
+  std::vector<RowInfo> rows(T);
+  std::vector<int> depth(T);
+  std::vector<int32_t> last(n_seqs), lane_ids(n_seqs);
+  std::vector<int64_t> soff(n_seqs);
+  std::vector<int32_t> scap(n_seqs);
+  int64_t acc = 0;
+  for (int i = 0; i < n_seqs; ++i) {
+    const int len = cu[i + 1] - cu[i];
+    for (int p = 0; p < len; ++p) {
+      RowInfo& r = rows[cu[i] + p];
+      r = RowInfo{};
+      r.orig = cu[i] + p;
+      r.lane = lanes ? lanes[i] : i;
+      r.pos = p;
+      r.depth = Ls[i];
+      r.iter = 1;
+      depth[cu[i] + p] = Ls[i];
+    }
+    last[i] = cu[i + 1] - 1;
+    lane_ids[i] = lanes ? lanes[i] : -1;
+    soff[i] = acc;
+    scap[i] = len;
+    acc += (int64_t)2 * c.d_model * len;
+  }
+  std::vector<int64_t> loff = m->h_lane_off;
+  std::vector<int32_t> lcap = m->h_lane_cap;
+  if (lanes)
+    for (int i = 0; i < n_seqs; ++i) {
+      loff[lanes[i]] = (int64_t)new_lanes[i].off;
+      lcap[lanes[i]] = new_lanes[i].cap;
+    }
+  Stage st;
+  const size_t o_rows = st.add(rows), o_last = st.add(last), o_lanes = st.add(lane_ids);
+  const size_t o_soff = st.add(soff), o_scap = st.add(scap);
+  const size_t o_loff = st.add(loff), o_lcap = st.add(lcap);
+  TRY(stage_upload(m, st, s));
+  if (lanes) {
+    HIPCHK(hipMemcpyAsync(m->d_lane_off, staged<int64_t>(m, o_loff), loff.size() * 8, hipMemcpyDeviceToDevice, s));
+    HIPCHK(hipMemcpyAsync(m->d_lane_cap, staged<int32_t>(m, o_lcap), lcap.size() * 4, hipMemcpyDeviceToDevice, s));
+    m->arena = arena;
+    for (int i = 0; i < n_seqs; ++i) m->lanes[lanes[i]] = new_lanes[i];
+    m->h_lane_off = loff;
+    m->h_lane_cap = lcap;
+  }
+  Pass p;
+  p.n = T;
+  p.tokens = tokens;
+  p.rows0 = staged<RowInfo>(m, o_rows);
+  p.n_active = active_counts(depth);
+  p.kv.H = c.n_heads;
+  p.kv.dh = c.head_dim;
+  if (lanes) {
+    p.kv.base = m->kv_base;
+    p.kv.lane_off = m->d_lane_off;
+    p.kv.lane_cap = m->d_lane_cap;
+  } else {
+    p.kv.base = m->ws.kv_scratch;
+    p.kv.lane_off = staged<int64_t>(m, o_soff);
+    p.kv.lane_cap = staged<int32_t>(m, o_scap);
+    p.scoring = true;
+  }
+  p.final_h = out_hidden ? out_hidden : m->ws.hX;
+  p.log = out_log;
+  TRY(run_pass(m, p, s));
+  if (want_head)
+    TRY(run_head(m, p.final_h, staged<int32_t>(m, o_last), n_seqs, out_logits, out_next,
+                 lanes ? staged<int32_t>(m, o_lanes) : nullptr, s));
+  return TL_OK;
+}
+
+tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int32_t* req_L,
+                         const int32_t* in_tokens, int32_t* out_tokens, float* out_logits, float* out_hidden,
+                         int32_t* out_eff_L, int32_t* out_log, void* stream) {
+  g_err.clear();
+  if (!m || !lanes || !req_L || !out_tokens) return fail(TL_E_ARG, "NULL argument");
+  const tl_config& c = m->cfg;
+  if (n < 1) return fail(TL_E_ARG, "n_lanes must be >= 1");
+  std::vector<char> seen(c.max_lanes, 0);
+  std::vector<int> eff(n);
+  for (int i = 0; i < n; ++i) {
+    const int l = lanes[i];
+    if (l < 0 || l >= c.max_lanes) return fail(TL_E_ARG, "lane %d out of range [0, %d)", l, c.max_lanes);
+    if (seen[l]) return fail(TL_E_ARG, "lane %d listed twice", l);
+    seen[l] = 1;
+    if (req_L[i] < 1) return fail(TL_E_ARG, "requested L %d < 1", req_L[i]);
+    const Lane& ln = m->lanes[l];
+    if (!ln.live) return fail(TL_E_STATE, "lane %d was never prefilled", l);
+    if (ln.len >= ln.cap) return fail(TL_E_STATE, "lane %d is full (%d positions)", l, ln.cap);
+    eff[i] = std::min(req_L[i], ln.ceiling);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(ensure_ws(m, n, n, 0, s));
+  std::vector<RowInfo> rows(n);
+  std::vector<int32_t> lane_ids(lanes, lanes + n);
+  for (int i = 0; i < n; ++i) {
+    rows[i] = RowInfo{};
+    rows[i].orig = i;
+    rows[i].lane = lanes[i];
+    rows[i].pos = m->lanes[lanes[i]].len;
+    rows[i].depth = eff[i];
+    rows[i].iter = 1;
+  }
+  Stage st;
+  const size_t o_rows = st.add(rows), o_lanes = st.add(lane_ids);
+  TRY(stage_upload(m, st, s));
+  const int32_t* lanes_dev = staged<int32_t>(m, o_lanes);
+  const int32_t* toks = in_tokens;
+  if (!toks) {
+    HIPCHK(launch_gather_i32(m->d_pending, lanes_dev, n, m->ws.tok, s));
+    toks = m->ws.tok;
+  }
+  Pass p;
+  p.n = n;
+  p.tokens = toks;
+  p.rows0 = staged<RowInfo>(m, o_rows);
+  p.n_active = active_counts(eff);
+  p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
+  p.final_h = out_hidden ? out_hidden : m->ws.hX;
+  p.log = out_log;
+  TRY(run_pass(m, p, s));
+  TRY(run_head(m, p.final_h, nullptr, n, out_logits, out_tokens, lanes_dev, s));
+  for (int i = 0; i < n; ++i) {
+    Lane& ln = m->lanes[lanes[i]];
+    ln.len += 1;
+    ln.ceiling = eff[i];
+    if (out_eff_L) out_eff_L[i] = eff[i];
+  }
+  return TL_OK;
+}
+
+tl_status tl_export_w4(tl_model* m, int32_t block, int32_t matrix, int8_t* q_host, uint16_t* s_host) {
+  g_err.clear();
+  if (!m || !q_host || !s_host) return fail(TL_E_ARG, "NULL argument");
+  const tl_config& c = m->cfg;
+  if (block < 0 || block >= (int)m->blocks.size() || !m->blocks[block].is_w4)
+    return fail(TL_E_ARG, "block %d is not a W4G128 block", block);
+  if (matrix < 0 || matrix > 4) return fail(TL_E_ARG, "matrix %d out of range", matrix);
+  const BlockDev& B = m->blocks[block];
+  const MatDev& md = matrix == 0 ? B.qkv : matrix == 1 ? B.o : matrix == 4 ? B.down : B.gu;
+  const int N = md.N, K = md.K;
+  int8_t* dq = static_cast<int8_t*>(dev_alloc(m, (size_t)N * K));
+  uint16_t* ds = static_cast<uint16_t*>(dev_alloc(m, (size_t)N * (K / 128) * 2));
+  if (!dq || !ds) {
+    dev_free(m, dq);
+    dev_free(m, ds);
+    return fail(TL_E_OOM, "export buffers");
+  }
+  tl_status st = TL_OK;
+  hipError_t e = launch_w4_export(md.w4, md.s4, md.perm, N, K, dq, ds, nullptr);
+  if (e == hipSuccess) e = hipDeviceSynchronize();
+  if (e == hipSuccess) {
+    // gate/up live stacked [gate; up] in canonical order after export
+    const size_t rows = (matrix == 2 || matrix == 3) ? (size_t)c.ffn : (size_t)N;
+    const size_t row0 = matrix == 3 ? (size_t)c.ffn : 0;
+    e = hipMemcpy(q_host, dq + row0 * K, rows * K, hipMemcpyDeviceToHost);
+    if (e == hipSuccess)
+      e = hipMemcpy(s_host, ds + row0 * (K / 128), rows * (K / 128) * 2, hipMemcpyDeviceToHost);
+  }
+  if (e != hipSuccess) st = fail(TL_E_HIP, "export: %s", hipGetErrorString(e));
+  dev_free(m, dq);
+  dev_free(m, ds);
+  return st;
+}
+
+tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_steps, const int32_t* L_req,
+                        int32_t* out_tokens, int32_t* out_eff_L, void* stream) {
+  if (!m || !lanes || !L_req || !out_tokens) return fail(TL_E_ARG, "NULL argument");
+  (void)n; (void)lanes; (void)n_steps; (void)L_req; (void)out_tokens; (void)out_eff_L; (void)stream;
+  return fail(TL_E_UNSUPPORTED, "continuous-depth decode not built yet");
+}
+
+}  // extern "C"

@@ -1,0 +1,105 @@
+// Host-side state of a loaded looped model (one GPU, one process).
+#pragma once
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+#include <map>
+#include <string>
+#include <vector>
+
+#include "../../include/tl.h"
+#include "kernels.h"
+
+namespace tl {
+
+// First-fit allocator over element offsets of the KV arena.
+class KvArena {
+ public:
+  void reset(uint64_t total);
+  bool alloc(uint64_t n, uint64_t* off);
+  void release(uint64_t off, uint64_t n);
+  uint64_t total() const { return total_; }
+
+ private:
+  uint64_t total_ = 0;
+  std::map<uint64_t, uint64_t> free_;   // offset -> length
+};
+
+struct Lane {
+  bool live = false;
+  int32_t len = 0;        // positions written
+  int32_t cap = 0;        // positions per slot
+  int32_t ceiling = 0;    // depth bound of the next token
+  int32_t nslots = 0;
+  uint64_t off = 0, elems = 0;
+};
+
+// One matrix in kernel row order: dense [N, K] in the operand dtype, or INT4
+// words + scales (and optionally the FP16-body dense copy).
+struct MatDev {
+  int N = 0, K = 0;
+  void* dense = nullptr;
+  uint32_t* w4 = nullptr;
+  uint16_t* s4 = nullptr;
+  int32_t* perm = nullptr;   // device: kernel row -> canonical (stacked) row, or NULL = identity
+};
+
+struct BlockDev {
+  int kind = 0;              // 0 pre, 1 loop, 2 post
+  float* norm1 = nullptr;
+  float* norm2 = nullptr;
+  MatDev qkv, o, gu, down;   // gu = gate/up interleaved [2F, d]
+  bool is_w4 = false;
+};
+
+struct Workspace {
+  int rows = 0, outs = 0;
+  int64_t kv_scratch_elems = 0;
+  float *hA = nullptr, *hB = nullptr, *hX = nullptr, *hE = nullptr;
+  void *x16 = nullptr, *q16 = nullptr, *o16 = nullptr, *u16 = nullptr, *xh = nullptr;
+  RowInfo *rowsA = nullptr, *rowsB = nullptr;
+  int32_t *dest = nullptr, *count = nullptr, *tok = nullptr;
+  float* part_v = nullptr;
+  int32_t* part_i = nullptr;
+  void* kv_scratch = nullptr;
+  int part_tiles = 0;
+};
+
+}  // namespace tl
+
+struct tl_model {
+  tl_config cfg{};
+  int act = DT_F16;
+  int G = 16;
+  int esz = 2;               // bytes of an activation / KV element
+  tl_alloc_fn alloc = nullptr;
+  tl_dealloc_fn dealloc = nullptr;
+  void* user = nullptr;
+  std::map<void*, size_t> owned;
+  uint64_t weight_bytes = 0, kv_bytes = 0, ws_bytes = 0;
+
+  void* embed = nullptr;
+  void* head = nullptr;
+  float* final_norm = nullptr;
+  std::vector<tl::BlockDev> blocks;
+  float* rope_cos = nullptr;
+  float* rope_sin = nullptr;
+
+  void* kv_base = nullptr;
+  tl::KvArena arena;
+  std::vector<tl::Lane> lanes;
+  std::vector<int64_t> h_lane_off;
+  std::vector<int32_t> h_lane_cap;
+  int64_t* d_lane_off = nullptr;
+  int32_t* d_lane_cap = nullptr;
+  int32_t* d_pending = nullptr;
+  int32_t* d_err = nullptr;
+
+  tl::Workspace ws;
+  // per-call upload: pinned host staging mirrored by a device area
+  void* stage_host = nullptr;
+  void* stage_dev = nullptr;
+  size_t stage_bytes = 0;
+  hipEvent_t stage_done = nullptr;
+  hipStream_t last_stream = nullptr;
+};

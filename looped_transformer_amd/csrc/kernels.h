@@ -1,0 +1,96 @@
+// Host-callable launchers of the gfx950 kernels and the plain structs they share
+// with the engine.  No torch types anywhere below the C ABI.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+enum DType : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_W4G128 = 3 };
+
+// One activation row of a pass.  orig: index of the row in the caller's order;
+// lane: KV lane table entry; pos: absolute position; depth: loop iterations the
+// row runs; iter: current loop iteration (1-based) of the row.
+struct RowInfo {
+  int32_t orig, lane, pos, depth, iter, tok_slot, p1, p2;
+};
+
+// KV cache addressing: slot of a block application for a row = s0 + s1 * row.iter.
+struct KVParams {
+  void* base;
+  const int64_t* lane_off;   // element offset of each lane's slot 0
+  const int32_t* lane_cap;   // positions per slot of each lane
+  int32_t H, dh, s0, s1;
+};
+
+enum EpiKind : int32_t { EPI_QKV = 0, EPI_RESID = 1, EPI_SWIGLU = 2, EPI_HEAD = 3, EPI_STORE = 4 };
+
+struct GemmArgs {
+  const void* A;          // [M, K] activations, lda = K
+  int32_t M, N, K;
+  const void* B;          // dense weights [N, K] (act dtype), or NULL for W4
+  const uint32_t* Bw4;    // INT4 kernel layout words, or NULL
+  const uint16_t* Bs;     // INT4 fp16 scales [K/128][N]
+};
+
+struct GemmEpi {
+  int32_t kind;
+  int32_t pair_g;          // row-permutation granularity of paired epilogues
+  // EPI_QKV
+  void* q_out;             // [M, d] act dtype
+  KVParams kv;
+  const RowInfo* rows;
+  const float* rope_cos;   // [max_pos, dh/2]
+  const float* rope_sin;
+  int32_t d, H, dh;
+  // EPI_RESID: h[r, c] += acc
+  float* h;
+  int32_t ldh;
+  // EPI_SWIGLU: u[r, n] = silu(gate) * up
+  void* u_out;
+  int32_t F;
+  // EPI_HEAD: optional logits store + per-tile (max, argmax) partials
+  float* logits;
+  int64_t ldl;
+  float* part_val;
+  int32_t* part_idx;
+  int32_t n_tiles;
+  // EPI_STORE: out[r, c] = acc (fp32)
+  float* out;
+  int32_t ldo;
+};
+
+// Returns the number of N tiles the head GEMM uses for N columns (partials per row).
+int gemm_head_tiles(int act_dtype, int M, int N);
+hipError_t launch_gemm(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s);
+
+hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, int d, float* h,
+                        int32_t* err_flag, int vocab, hipStream_t s);
+hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const int32_t* gather, int n,
+                          int d, float eps, void* out, hipStream_t s);
+hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv,
+                            void* out, hipStream_t s);
+// Stable filter of the active rows: rows with depth > iter stay (iter + 1), the
+// others leave.  dest[i] = new index or -1.  count_out[0] = number kept.  If
+// log_out is non-NULL the kept rows' orig indices are written there.
+hipError_t launch_compact(const RowInfo* rows_in, int n, RowInfo* rows_out, int32_t* dest,
+                          int32_t* count_out, int32_t* log_out, hipStream_t s);
+// h_next[dest[i]] = h[i] for kept rows; h_exit[rows[i].orig] = h[i] for leaving rows.
+hipError_t launch_move_rows(const float* h, const int32_t* dest, const RowInfo* rows, int n, int d,
+                            float* h_next, float* h_exit, hipStream_t s);
+hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream_t s);
+hipError_t launch_argmax_reduce(const float* part_val, const int32_t* part_idx, int n, int n_tiles,
+                                int32_t* out_tok, int32_t* out_tok2, const int32_t* scatter, hipStream_t s);
+hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
+hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s);
+
+// Load-time kernels.  perm[n] = canonical source row of kernel row n.
+hipError_t launch_permute_rows(int elem_bytes, const void* src, const int32_t* perm, int N, int K, void* dst,
+                               hipStream_t s);
+hipError_t launch_quant_w4(const float* w, const int32_t* perm, int N, int K, uint32_t* words,
+                           uint16_t* scales, hipStream_t s);
+hipError_t launch_w4_to_f16(const uint32_t* words, const uint16_t* scales, int N, int K, uint16_t* out,
+                            hipStream_t s);
+// Canonical export: q[perm[n], k], s[perm[n], g] from kernel row n.
+hipError_t launch_w4_export(const uint32_t* words, const uint16_t* scales, const int32_t* perm, int N, int K,
+                            int8_t* q, uint16_t* s_out, hipStream_t s);

@@ -1,0 +1,335 @@
+// Small kernels of the hot path (embedding gather, RMSNorm, per-iteration
+// compaction of active rows, greedy-token reduction, row moves) and the
+// load-time kernels (INT4 quantisation into the kernel layout, FP16-body
+// dequantisation, canonical export, row permutation).
+#include "device_common.h"
+
+namespace {
+
+// ---------------------------------------------------------------- embedding
+template <class T>
+__global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E, const int32_t* __restrict__ tokens,
+                                                   int d, float* __restrict__ h, int32_t* err, int vocab) {
+  const int r = blockIdx.x;
+  int tok = tokens[r];
+  if (tok < 0 || tok >= vocab) {
+    if (threadIdx.x == 0 && err) atomicOr(err, 1);
+    tok = 0;
+  }
+  const T* src = E + (int64_t)tok * d;
+  float* dst = h + (int64_t)r * d;
+  for (int i = threadIdx.x; i < d; i += 256) dst[i] = (float)src[i];
+}
+
+// ---------------------------------------------------------------- RMSNorm
+// x = h / sqrt(mean(h^2) + eps) * g, one wave per row; fp32 statistics.
+template <class T>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, const float* __restrict__ g,
+                                                     const int32_t* __restrict__ gather, int n, int d, float eps,
+                                                     T* __restrict__ out) {
+  const int lane = threadIdx.x & 63;
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (r >= n) return;
+  const int src = gather ? gather[r] : r;
+  const float* hr = h + (int64_t)src * d;
+  float ss = 0.f;
+  for (int i = lane * 4; i < d; i += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(hr + i);
+    ss = fmaf(v.x, v.x, ss);
+    ss = fmaf(v.y, v.y, ss);
+    ss = fmaf(v.z, v.z, ss);
+    ss = fmaf(v.w, v.w, ss);
+  }
+  ss = wave_sum(ss);
+  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+  T* o = out + (int64_t)r * d;
+  for (int i = lane * 4; i < d; i += 256) {
+    const float4 v = *reinterpret_cast<const float4*>(hr + i);
+    const float4 gg = *reinterpret_cast<const float4*>(g + i);
+    o[i] = from_f32<T>(v.x * inv * gg.x);
+    o[i + 1] = from_f32<T>(v.y * inv * gg.y);
+    o[i + 2] = from_f32<T>(v.z * inv * gg.z);
+    o[i + 3] = from_f32<T>(v.w * inv * gg.w);
+  }
+}
+
+// ---------------------------------------------------------------- compaction
+// Stable filter in one workgroup: chunks of 1024 rows, wave ballots + prefix.
+__global__ __launch_bounds__(1024) void compact_kernel(const RowInfo* __restrict__ in, int n,
+                                                      RowInfo* __restrict__ out, int32_t* __restrict__ dest,
+                                                      int32_t* count_out, int32_t* log_out) {
+  __shared__ int wave_cnt[16];
+  __shared__ int base_s;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (threadIdx.x == 0) base_s = 0;
+  __syncthreads();
+  for (int c0 = 0; c0 < n; c0 += 1024) {
+    const int i = c0 + threadIdx.x;
+    bool keep = false;
+    RowInfo ri;
+    if (i < n) {
+      ri = in[i];
+      keep = ri.depth > ri.iter;
+    }
+    const uint64_t mask = __ballot(keep);
+    const int before = __popcll(mask & ((1ull << lane) - 1ull));
+    if (lane == 0) wave_cnt[w] = __popcll(mask);
+    __syncthreads();
+    int off = base_s;
+    for (int k = 0; k < w; ++k) off += wave_cnt[k];
+    if (i < n) {
+      if (keep) {
+        const int ni = off + before;
+        ri.iter += 1;
+        out[ni] = ri;
+        dest[i] = ni;
+        if (log_out) log_out[ni] = ri.orig;
+      } else {
+        dest[i] = -1;
+      }
+    }
+    __syncthreads();
+    if (threadIdx.x == 0) {
+      int tot = 0;
+      for (int k = 0; k < 16; ++k) tot += wave_cnt[k];
+      base_s += tot;
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0 && count_out) *count_out = base_s;
+}
+
+__global__ __launch_bounds__(256) void move_rows_kernel(const float* __restrict__ h, const int32_t* __restrict__ dest,
+                                                       const RowInfo* __restrict__ rows, int d,
+                                                       float* __restrict__ h_next, float* __restrict__ h_exit) {
+  const int i = blockIdx.x;
+  const int di = dest[i];
+  float* dst = di >= 0 ? h_next + (int64_t)di * d : h_exit + (int64_t)rows[i].orig * d;
+  const float* src = h + (int64_t)i * d;
+  for (int c = threadIdx.x * 4; c < d; c += 1024) *reinterpret_cast<float4*>(dst + c) = *reinterpret_cast<const float4*>(src + c);
+}
+
+__global__ void write_orig_kernel(const RowInfo* rows, int n, int32_t* out) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) out[i] = rows[i].orig;
+}
+
+// ---------------------------------------------------------------- greedy token
+__global__ void argmax_reduce_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi, int n, int tiles,
+                                     int32_t* out, int32_t* out2, const int32_t* scatter) {
+  const int r = blockIdx.x * 256 + threadIdx.x;
+  if (r >= n) return;
+  float bv = -INFINITY;
+  int bi = 0x7fffffff;
+  for (int t = 0; t < tiles; ++t) {
+    const float v = pv[(int64_t)r * tiles + t];
+    const int i = pi[(int64_t)r * tiles + t];
+    if (v > bv || (v == bv && i < bi)) {
+      bv = v;
+      bi = i;
+    }
+  }
+  if (out) out[r] = bi;
+  if (out2) out2[scatter ? scatter[r] : r] = bi;
+}
+
+__global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restrict__ src, const int32_t* __restrict__ idx,
+                                                         int d, float* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const float* s = src + (int64_t)idx[r] * d;
+  float* o = dst + (int64_t)r * d;
+  for (int c = threadIdx.x; c < d; c += 256) o[c] = s[c];
+}
+
+__global__ __launch_bounds__(256) void scatter_rows_kernel(const float* __restrict__ src, const int32_t* __restrict__ idx,
+                                                          int d, float* __restrict__ dst) {
+  const int r = blockIdx.x;
+  const float* s = src + (int64_t)r * d;
+  float* o = dst + (int64_t)idx[r] * d;
+  for (int c = threadIdx.x; c < d; c += 256) o[c] = s[c];
+}
+
+__global__ void fill_i32_kernel(int32_t* p, int32_t v, int64_t n) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+__global__ void gather_i32_kernel(const int32_t* src, const int32_t* idx, int n, int32_t* dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[i] = src[idx[i]];
+}
+
+// ---------------------------------------------------------------- load time
+__global__ __launch_bounds__(256) void permute_rows_kernel(const uint32_t* __restrict__ src, const int32_t* __restrict__ perm,
+                                                          int words_per_row, uint32_t* __restrict__ dst) {
+  const int n = blockIdx.x;
+  const uint32_t* s = src + (int64_t)perm[n] * words_per_row;
+  uint32_t* o = dst + (int64_t)n * words_per_row;
+  for (int c = threadIdx.x; c < words_per_row; c += 256) o[c] = s[c];
+}
+
+// One wave per (kernel row n, group): s = fp16(max|w| / 7), q = clamp(rint(w / s), -7, 7).
+__global__ __launch_bounds__(256) void quant_w4_kernel(const float* __restrict__ w, const int32_t* __restrict__ perm,
+                                                      int N, int K, uint32_t* __restrict__ words,
+                                                      uint16_t* __restrict__ scales) {
+  const int lane = threadIdx.x & 63;
+  const int groups = K >> 7;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= (int64_t)N * groups) return;
+  const int n = (int)(item / groups), gi = (int)(item - (int64_t)n * groups);
+  const int src = perm ? perm[n] : n;
+  const float2 ab = *reinterpret_cast<const float2*>(w + (int64_t)src * K + gi * 128 + 2 * lane);
+  const float amax = wave_max(fmaxf(fabsf(ab.x), fabsf(ab.y)));
+  const f16 s16 = (f16)__fdiv_rn(amax, 7.0f);
+  const float s32 = (float)s16;
+  int qa = 0, qb = 0;
+  if (s32 > 0.f) {
+    qa = (int)fminf(fmaxf(rintf(__fdiv_rn(ab.x, s32)), -7.f), 7.f);
+    qb = (int)fminf(fmaxf(rintf(__fdiv_rn(ab.y, s32)), -7.f), 7.f);
+  }
+  const int sh = 4 * (lane & 3);
+  int part = (int)(((uint32_t)(qa + 8) << sh) | ((uint32_t)(qb + 8) << (16 + sh)));
+  part |= __shfl_xor(part, 1, 64);
+  part |= __shfl_xor(part, 2, 64);
+  if ((lane & 3) == 0)
+    words[((int64_t)(n >> 4) * groups + gi) * 256 + (n & 15) * 16 + (lane >> 2)] = (uint32_t)part;
+  if (lane == 0) scales[(int64_t)gi * N + n] = __builtin_bit_cast(uint16_t, s16);
+}
+
+__device__ __forceinline__ f16 w4_value(const uint32_t* words, int groups, int n, int k) {
+  const uint32_t wd = words[((int64_t)(n >> 4) * groups + (k >> 7)) * 256 + (n & 15) * 16 + ((k & 127) >> 3)];
+  const int e = k & 7;
+  const half2v p = w4_pair(wd, e >> 1);
+  return p[e & 1];
+}
+
+// FP16 body: fp16(q * s), product in fp32 (exact), one rounding.
+__global__ __launch_bounds__(256) void w4_to_f16_kernel(const uint32_t* __restrict__ words, const uint16_t* __restrict__ scales,
+                                                       int N, int K, uint16_t* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)N * K) return;
+  const int n = (int)(i / K), k = (int)(i - (int64_t)n * K);
+  const int groups = K >> 7;
+  const float q = (float)w4_value(words, groups, n, k);
+  const float s = (float)__builtin_bit_cast(f16, scales[(int64_t)(k >> 7) * N + n]);
+  out[i] = __builtin_bit_cast(uint16_t, (f16)(q * s));
+}
+
+__global__ __launch_bounds__(256) void w4_export_kernel(const uint32_t* __restrict__ words, const uint16_t* __restrict__ scales,
+                                                       const int32_t* __restrict__ perm, int N, int K,
+                                                       int8_t* __restrict__ q, uint16_t* __restrict__ s_out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (i >= (int64_t)N * K) return;
+  const int n = (int)(i / K), k = (int)(i - (int64_t)n * K);
+  const int groups = K >> 7;
+  const int dst = perm ? perm[n] : n;
+  q[(int64_t)dst * K + k] = (int8_t)(int)(float)w4_value(words, groups, n, k);
+  if ((k & 127) == 0) s_out[(int64_t)dst * groups + (k >> 7)] = scales[(int64_t)(k >> 7) * N + n];
+}
+
+}  // namespace
+
+hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, int d, float* h, int32_t* err,
+                        int vocab, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  switch (dtype) {
+    case DT_F32: hipLaunchKernelGGL(embed_kernel<float>, dim3(n), dim3(256), 0, s, (const float*)E, tokens, d, h, err, vocab); break;
+    case DT_F16: hipLaunchKernelGGL(embed_kernel<f16>, dim3(n), dim3(256), 0, s, (const f16*)E, tokens, d, h, err, vocab); break;
+    case DT_BF16: hipLaunchKernelGGL(embed_kernel<bf16>, dim3(n), dim3(256), 0, s, (const bf16*)E, tokens, d, h, err, vocab); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const int32_t* gather, int n, int d, float eps,
+                          void* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  dim3 grid((n + 3) / 4);
+  switch (out_dtype) {
+    case DT_F32: hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, h, g, gather, n, d, eps, (float*)out); break;
+    case DT_F16: hipLaunchKernelGGL(rmsnorm_kernel<f16>, grid, dim3(256), 0, s, h, g, gather, n, d, eps, (f16*)out); break;
+    case DT_BF16: hipLaunchKernelGGL(rmsnorm_kernel<bf16>, grid, dim3(256), 0, s, h, g, gather, n, d, eps, (bf16*)out); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_compact(const RowInfo* rows_in, int n, RowInfo* rows_out, int32_t* dest, int32_t* count_out,
+                          int32_t* log_out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, rows_in, n, rows_out, dest, count_out, log_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_move_rows(const float* h, const int32_t* dest, const RowInfo* rows, int n, int d, float* h_next,
+                            float* h_exit, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(move_rows_kernel, dim3(n), dim3(256), 0, s, h, dest, rows, d, h_next, h_exit);
+  return hipGetLastError();
+}
+
+hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(write_orig_kernel, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax_reduce(const float* pv, const int32_t* pi, int n, int tiles, int32_t* out, int32_t* out2,
+                                const int32_t* scatter, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, pv, pi, n, tiles, out, out2, scatter);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(256), 0, s, src, idx, d, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_rows_kernel, dim3(n), dim3(256), 0, s, src, idx, d, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, v, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_rows(int elem_bytes, const void* src, const int32_t* perm, int N, int K, void* dst,
+                               hipStream_t s) {
+  if ((int64_t)K * elem_bytes % 4 != 0) return hipErrorInvalidValue;
+  const int wpr = (int)((int64_t)K * elem_bytes / 4);
+  hipLaunchKernelGGL(permute_rows_kernel, dim3(N), dim3(256), 0, s, (const uint32_t*)src, perm, wpr, (uint32_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_quant_w4(const float* w, const int32_t* perm, int N, int K, uint32_t* words, uint16_t* scales,
+                           hipStream_t s) {
+  const int64_t items = (int64_t)N * (K / 128);
+  hipLaunchKernelGGL(quant_w4_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, w, perm, N, K, words, scales);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4_to_f16(const uint32_t* words, const uint16_t* scales, int N, int K, uint16_t* out, hipStream_t s) {
+  const int64_t tot = (int64_t)N * K;
+  hipLaunchKernelGGL(w4_to_f16_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, words, scales, N, K, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_w4_export(const uint32_t* words, const uint16_t* scales, const int32_t* perm, int N, int K, int8_t* q,
+                            uint16_t* s_out, hipStream_t s) {
+  const int64_t tot = (int64_t)N * K;
+  hipLaunchKernelGGL(w4_export_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, words, scales, perm, N, K,
+                     q, s_out);
+  return hipGetLastError();
+}

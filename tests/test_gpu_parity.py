@@ -1,0 +1,188 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bars: INT4 codes and scales and every per-iteration active-row list bit-exact;
+relative L2 of final hidden states <= 1e-2 for L <= 8 and <= 3e-2 above
+(fp32 models: 1e-4); top-1 agreement >= 99 % on greedy tokens.
+"""
+import os
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.harness import ensure_built, kv_bytes, load_model, rel_l2
+
+torch = pytest.importorskip("torch")
+import looped_transformer_amd as tl  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+TINY = {
+    "tiny-f32": synth.SPECS[1],
+    "tiny-f16": synth.ModelSpec("tiny-f16", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "f16"),
+    "tiny-w4": synth.ModelSpec("tiny-w4", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "w4g128"),
+    "tiny-f16body": synth.ModelSpec("tiny-f16body", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "f16body"),
+    "tiny-bf16-stack": synth.ModelSpec("tiny-bf16-stack", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16"),
+}
+
+
+def say(*a):
+    print("[gpu-parity]", *a, flush=True)
+    sys.stdout.flush()
+
+
+def hidden_bar(spec, L):
+    if spec.boundary_dtype == "f32":
+        return 1e-4
+    return 1e-2 if L <= 8 else 3e-2
+
+
+def gpu_forward(model, spec, seqs, Ls, lanes=None, max_new=0, logits=True):
+    toks = torch.tensor(np.concatenate(seqs), dtype=torch.int32, device="cuda")
+    cu = np.cumsum([0] + [len(s) for s in seqs]).astype(np.int32)
+    T = int(cu[-1])
+    depth = np.concatenate([np.full(len(s), L) for s, L in zip(seqs, Ls)])
+    n_log = int(sum(np.sum(depth >= j) for j in range(1, int(depth.max()) + 1)))
+    hid = torch.empty(T, spec.d_model, dtype=torch.float32, device="cuda")
+    lg = torch.empty(len(seqs), spec.vocab, dtype=torch.float32, device="cuda") if logits else None
+    nxt = torch.empty(len(seqs), dtype=torch.int32, device="cuda")
+    log = torch.empty(max(n_log, 1), dtype=torch.int32, device="cuda")
+    tl.tl_forward(model, cu, toks, seq_L=Ls, lanes=lanes, max_new_tokens=max_new, out_hidden=hid,
+                  out_logits=lg, out_next=nxt, out_active_log=log)
+    torch.cuda.synchronize()
+    tl.tl_sync_errors(model)
+    return (hid.cpu().numpy(), lg.cpu().numpy() if logits else None, nxt.cpu().numpy(),
+            log.cpu().numpy()[:n_log], depth)
+
+
+def check_log(log, depth):
+    want = np.concatenate(oracle.active_lists(depth))
+    assert np.array_equal(log, want), "active-row lists differ"
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+@pytest.mark.parametrize("name", list(TINY))
+def test_tiny_forward_parity(name):
+    spec = TINY[name]
+    say("tiny forward", name)
+    w = synth.make_weights(spec, seed=3)
+    m = oracle.OracleModel.from_weights(w)
+    seqs = [synth.tokens(3, 3000 + i, n, spec.vocab) for i, n in enumerate([16, 5, 33, 70])]
+    Ls = [4, 1, 3, 9]
+    model = load_model(w, max_pos=256, max_L=16)
+    try:
+        hid, lg, nxt, log, depth = gpu_forward(model, spec, seqs, Ls)
+    finally:
+        tl.tl_free(model)
+    check_log(log, depth)
+    ref_h, ref_lg, _ = oracle.forward_batch(m, seqs, Ls)
+    off = 0
+    for i, s in enumerate(seqs):
+        r = rel_l2(hid[off:off + len(s)], ref_h[off:off + len(s)])
+        say(name, "seq", i, "L", Ls[i], "rel", r)
+        assert r <= hidden_bar(spec, Ls[i]), (i, r)
+        off += len(s)
+    assert rel_l2(lg, ref_lg) <= (1e-4 if spec.boundary_dtype == "f32" else 1e-2)
+    assert np.array_equal(nxt, oracle.greedy_argmax(ref_lg)) or np.mean(nxt == oracle.greedy_argmax(ref_lg)) >= 0.75
+
+
+def test_w4_export_bit_exact():
+    spec = synth.SPECS[2]
+    say("w4 export cfg2")
+    w = synth.make_weights(spec, seed=0)
+    model = load_model(w, max_pos=256)
+    try:
+        d, F = spec.d_model, spec.ffn
+        shapes = [(3 * d, d, "wqkv"), (d, d, "wo"), (F, d, "wgate"), (F, d, "wup"), (d, F, "wdown")]
+        for mi, (N, K, name) in enumerate(shapes):
+            q, s = tl.tl_export_w4(model, 1, mi, N, K)
+            qo, so = oracle.quantize_w4g128(w.blocks[1][name])
+            assert np.array_equal(q, qo), name
+            assert np.array_equal(s, so.view(np.uint16)), name
+    finally:
+        tl.tl_free(model)
+
+
+def test_cfg1_forward_and_greedy_decode():
+    """Tiny fp32 model: 16 tokens at L = 4, then 8 greedy cached decode steps."""
+    spec = synth.SPECS[1]
+    w = synth.make_weights(spec, seed=0)
+    m = oracle.OracleModel.from_weights(w)
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 16, spec.vocab)
+    model = load_model(w, max_lanes=1, max_pos=64, kv_arena_bytes=kv_bytes(spec, [4], [24]))
+    try:
+        hid, lg, nxt, log, depth = gpu_forward(model, spec, [toks], [4], lanes=[0], max_new=8)
+        lane, ref_h, ref_lg = oracle.prefill(m, toks, 4)
+        assert rel_l2(hid, ref_h) <= 1e-5
+        assert nxt[0] == lane.pending
+        out = torch.empty(1, dtype=torch.int32, device="cuda")
+        hs = torch.empty(1, spec.d_model, dtype=torch.float32, device="cuda")
+        lgt = torch.empty(1, spec.vocab, dtype=torch.float32, device="cuda")
+        for step in range(8):
+            eff = tl.tl_decode_step(model, [0], [4], out, out_logits=lgt, out_hidden=hs)
+            torch.cuda.synchronize()
+            h_ref, l_ref, nxt_ref, L = oracle.decode_step(m, lane, 4)
+            assert eff[0] == 4
+            assert rel_l2(hs.cpu().numpy()[0], h_ref) <= 1e-5, step
+            assert rel_l2(lgt.cpu().numpy()[0], l_ref) <= 1e-5, step
+            assert int(out.cpu()[0]) == nxt_ref, step
+    finally:
+        tl.tl_free(model)
+
+
+@pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack"])
+def test_tiny_decode_mixed_and_monotone_depth(name):
+    """Lanes at different depths, per-token requests clamped to never rise."""
+    spec = TINY[name]
+    w = synth.make_weights(spec, seed=5)
+    m = oracle.OracleModel.from_weights(w)
+    n_lanes, plen, steps = 5, 12, 6
+    L0 = [6, 1, 3, 8, 4]
+    seqs = [synth.tokens(5, 4000 + i, plen + i, spec.vocab) for i in range(n_lanes)]
+    reqs = np.array([[6, 5, 7, 2, 3, 1], [1, 1, 2, 1, 1, 1], [9, 3, 3, 2, 8, 1],
+                     [8, 8, 4, 4, 4, 2], [2, 4, 1, 4, 4, 4]], np.int32)
+    caps = [plen + i + steps for i in range(n_lanes)]
+    model = load_model(w, max_lanes=8, max_pos=64, max_L=16, kv_arena_bytes=kv_bytes(spec, [16] * n_lanes, caps))
+    try:
+        lanes = [3, 0, 7, 1, 5]
+        gpu_forward(model, spec, seqs, L0, lanes=lanes, max_new=steps)
+        olanes = [oracle.prefill(m, s, L)[0] for s, L in zip(seqs, L0)]
+        out = torch.empty(n_lanes, dtype=torch.int32, device="cuda")
+        hs = torch.empty(n_lanes, spec.d_model, dtype=torch.float32, device="cuda")
+        for t in range(steps):
+            # teacher-force both sides with the oracle's greedy tokens
+            feed = torch.tensor([ol.pending for ol in olanes], dtype=torch.int32, device="cuda")
+            eff = tl.tl_decode_step(model, lanes, reqs[:, t], out, in_tokens=feed, out_hidden=hs)
+            torch.cuda.synchronize()
+            for i, ol in enumerate(olanes):
+                h_ref, l_ref, nxt_ref, L = oracle.decode_step(m, ol, int(reqs[i, t]))
+                assert eff[i] == L
+                r = rel_l2(hs.cpu().numpy()[i], h_ref)
+                assert r <= hidden_bar(spec, L), (t, i, r)
+    finally:
+        tl.tl_free(model)
+
+
+def test_cfg2_forward_full_size():
+    """Forward scoring on the 2048-wide INT4-loop model, 1 x 128 tokens, L = 8, no logits."""
+    spec = synth.SPECS[2]
+    say("cfg2 forward")
+    w = synth.make_weights(spec, seed=0)
+    m = oracle.OracleModel.from_weights(w)
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 128, spec.vocab)
+    model = load_model(w, max_pos=256)
+    try:
+        hid, _, _, log, depth = gpu_forward(model, spec, [toks], [8], logits=False)
+    finally:
+        tl.tl_free(model)
+    check_log(log, depth)
+    _, ref_h, _ = oracle.prefill(m, toks, 8, want_logits="none")
+    r = rel_l2(hid, ref_h)
+    say("cfg2 rel", r)
+    assert r <= 1e-2
