@@ -1,0 +1,193 @@
+#!/usr/bin/env python3
+"""Benchmark of the looped transformer's hot path on one MI355X.
+
+Step: one forward scoring pass of the 2048-wide model with an INT4 shared loop
+block (vocab 50304, 16 heads x 128, SwiGLU 5632, 1 pre block, 1 x 128 tokens,
+L = 8, no logits) with inputs resident in HBM.  Reported value: token-loop
+iterations per second (128 tokens x 8 iterations per step); ms_per_step is the
+milliseconds per seq-128 L = 8 forward.  Secondary field: greedy cached decode
+tok/s at L = 8 on the FP16-body model (32 lanes, 32-token prompts).
+
+Prints one JSON line.  Synthetic seeded weights and token ids (no checkpoint).
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16/bf16 MFMA
+PEAK_HBM_GBS = 8000.0
+PAGES_H100_INT4_MS = 30.48     # the pages' H100 INT4 forward at seq 128, loops 8 (context)
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
+    return ap.parse_args()
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def traffic_for(kernel_class: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source is unchanged."""
+    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % kernel_class)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = open(os.path.join(ROOT, "looped_transformer_amd", "csrc", "gemm.hip"), "rb").read()
+    if rec.get("gemm_source_sha256") != hashlib.sha256(src).hexdigest():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def cpu_baseline(seconds: float):
+    import numpy as np
+    import oracle
+    import synth
+    from threadpoolctl import threadpool_info
+    spec = synth.SPECS[2]
+    w = synth.make_weights(spec, 0)
+    m = oracle.OracleModel.from_weights(w)
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 128, spec.vocab)
+    runs, t0 = 0, time.perf_counter()
+    while True:
+        oracle.prefill(m, toks, 8, want_logits="none")
+        runs += 1
+        el = time.perf_counter() - t0
+        if el >= seconds or runs >= 50:
+            break
+    threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    return {"value": round(1024 * runs / el, 1), "unit": "token-loop iterations/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": "%d full forwards of the same workload (1x128 tokens, L=8) by the fp64 numpy oracle, %.1f s"
+                      % (runs, el)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (lanes would be sharded across "
+              "GPUs with replicated weights; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+    import looped_transformer_amd as tl
+    import synth
+    from tests.harness import ensure_built, kv_bytes, load_model
+
+    ensure_built()
+    spec = synth.SPECS[2]
+    log("generating weights")
+    w = synth.make_weights(spec, 0)
+    model = load_model(w, max_pos=256)
+    toks = torch.tensor(synth.tokens(0, synth.STREAM_TOKENS, 128, spec.vocab), dtype=torch.int32, device="cuda")
+    cu = np.array([0, 128], np.int32)
+    hid = torch.empty(128, spec.d_model, dtype=torch.float32, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def step():
+        tl.tl_forward(model, cu, toks, L=8, out_hidden=hid, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    log("timed region: %d steps" % args.steps)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    ms = el / args.steps * 1e3
+    value = 128 * 8 / (ms / 1e3)
+    if args.profile_only:
+        log("ms/step %.4f" % ms)
+        return
+
+    # per-kernel-class HIP-event timing over a second timed region of the same steps
+    tl.tl_timing_enable(model, True)
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    cls = tl.tl_timing_read(model)
+    tl.tl_timing_enable(model, False)
+    M, d, F = 128, spec.d_model, spec.ffn
+    flops = {"gemm_qkv_loop": 2 * M * 3 * d * d, "gemm_o_loop": 2 * M * d * d,
+             "gemm_gu_loop": 2 * M * 2 * F * d, "gemm_down_loop": 2 * M * d * F}
+    dom = max(flops, key=lambda k: cls[k][0])
+    tot_ms, n = cls[dom]
+    avg_s = tot_ms / n / 1e3
+    achieved = flops[dom] / avg_s / 1e12
+    roofline = {"bound": "mfma", "kernel": dom, "achieved": round(achieved, 2), "peak": PEAK_F16_TFLOPS,
+                "unit": "TFLOP/s", "frac": round(achieved / PEAK_F16_TFLOPS, 4), "traffic": traffic_for(dom),
+                "avg_launch_us": round(avg_s * 1e6, 2), "launches": n,
+                "algorithmic_flops_per_launch": flops[dom]}
+    breakdown = {k: round(v[0] / args.steps * 1e3, 2) for k, v in cls.items() if v[1]}
+    tl.tl_free(model)
+    del model
+
+    out = {"metric": "token-loop iterations/sec + ms per seq128 L=8 forward; decode tok/s at L=8",
+           "value": round(value, 1), "unit": "token-loop iterations/s", "n_gpus": 1, "steps": args.steps,
+           "warmup": args.warmup, "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak",
+           "vs_baseline": round(PAGES_H100_INT4_MS / ms, 2), "dtype": "f16", "data": "synthetic",
+           "config": {"workload": "forward scoring, INT4 (W4G128) shared loop block, d_model 2048, 16x128 heads, "
+                                  "SwiGLU 5632, vocab 50304, 1 pre block, batch 1, seq_len 128, L=8, no logits",
+                      "batch": 1, "seq_len": 128, "L": 8, "parallelism": "single GPU"},
+           "roofline": roofline, "us_per_step_by_kernel_class": breakdown,
+           "baseline_note": "vs_baseline = the pages' H100 INT4 forward (30.48 ms, same workload) / ms_per_step; "
+                            "another machine's number, context only"}
+
+    if not args.no_decode:
+        out["decode_L8"] = decode_bench(tl, torch, np, synth, kv_bytes, load_model)
+    if not args.no_cpu_baseline:
+        log("cpu baseline")
+        out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
+    """32 lanes, 32-token prompts, greedy cached decode at L = 8 on the FP16-body model."""
+    spec = synth.SPECS[3]
+    log("decode: FP16-body model")
+    w = synth.make_weights(spec, 0)
+    n, plen, new = 32, 32, 32
+    model = load_model(w, max_lanes=n, max_pos=plen + new, kv_arena_bytes=kv_bytes(spec, [8] * n, [plen + new] * n))
+    prompts = synth.tokens(0, synth.STREAM_PROMPT_TOKENS, n * plen, spec.vocab)
+    toks = torch.tensor(prompts, dtype=torch.int32, device="cuda")
+    cu = np.arange(0, n * plen + 1, plen, dtype=np.int32)
+    lanes = np.arange(n, dtype=np.int32)
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    Ls = np.full(n, 8, np.int32)
+    times = []
+    for rep in range(3):
+        tl.tl_forward(model, cu, toks, L=8, lanes=lanes, max_new_tokens=new)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(new - 1):
+            tl.tl_decode_step(model, lanes, Ls, out)
+        torch.cuda.synchronize()
+        times.append(time.perf_counter() - t0)
+    tl.tl_free(model)
+    best = min(times)
+    return {"tok_per_s": round(n * (new - 1) / best, 1), "ms_per_step": round(best / (new - 1) * 1e3, 4),
+            "config": "FP16-body loop block, 32 lanes, 32-token prompts, 31 cached greedy steps at L=8 "
+                      "(first token comes from the prefill)"}
+
+
+if __name__ == "__main__":
+    main()

@@ -170,12 +170,16 @@ tl_status tl_decode_step(tl_model* m, int32_t n_lanes, const int32_t* lanes_host
  *   L_req_host [n_lanes, n_steps]: requested depth of each new token; clamped
  *      exactly as in tl_decode_step.  The results equal n_steps calls of
  *      tl_decode_step with these requests; only the order of work differs.
- *   out_tokens_dev [n_lanes, n_steps] int32.
+ *   in_tokens_dev [n_lanes, n_steps] int32 or NULL: token fed at each step (NULL:
+ *      the lane's pending greedy token, i.e. free-running greedy decoding).
+ *   out_tokens_dev [n_lanes, n_steps] int32: greedy token of each step.
+ *   out_hidden_dev [n_lanes, n_steps, d] float32 or NULL: residual after the last
+ *      block for each step.
  *   out_eff_L_host [n_lanes, n_steps] or NULL.
  * Errors: as tl_decode_step. */
 tl_status tl_decode_run(tl_model* m, int32_t n_lanes, const int32_t* lanes_host, int32_t n_steps,
-                        const int32_t* L_req_host, int32_t* out_tokens_dev,
-                        int32_t* out_eff_L_host, void* stream);
+                        const int32_t* L_req_host, const int32_t* in_tokens_dev, int32_t* out_tokens_dev,
+                        float* out_hidden_dev, int32_t* out_eff_L_host, void* stream);
 
 /* Copy the device-resident INT4 weights of one W4G128 matrix back to canonical
  * form, unpacked by the same device routine the GEMM uses: q_host [N, K] int8 and
@@ -195,6 +199,28 @@ tl_status tl_memory_info(tl_model* m, uint64_t* weight_bytes, uint64_t* kv_bytes
 /* Synchronises stream and reports errors the kernels detected since the last
  * check: a token id outside [0, vocab) (it was read as 0) gives TL_E_ARG. */
 tl_status tl_sync_errors(tl_model* m, void* stream);
+
+/* Measurement: with timing on, the library records a pair of HIP events on the
+ * call's stream around every launch of the kernel classes below and sums their
+ * elapsed times.  tl_timing_read waits for the recorded events, writes the total
+ * milliseconds and launch counts of each class (arrays of TL_TIMING_CLASSES) and
+ * resets the sums.  Classes: */
+#define TL_T_GEMM_QKV_LOOP 0
+#define TL_T_GEMM_O_LOOP 1
+#define TL_T_GEMM_GU_LOOP 2      /* gate/up with the SwiGLU epilogue */
+#define TL_T_GEMM_DOWN_LOOP 3
+#define TL_T_GEMM_QKV_BOUNDARY 4 /* pre and post blocks */
+#define TL_T_GEMM_O_BOUNDARY 5
+#define TL_T_GEMM_GU_BOUNDARY 6
+#define TL_T_GEMM_DOWN_BOUNDARY 7
+#define TL_T_ATTENTION 8
+#define TL_T_RMSNORM 9
+#define TL_T_HEAD 10             /* head GEMM and greedy-token reduction */
+#define TL_T_COMPACT 11          /* active-row compaction and row moves */
+#define TL_T_EMBED 12
+#define TL_TIMING_CLASSES 13
+tl_status tl_timing_enable(tl_model* m, int32_t on);
+tl_status tl_timing_read(tl_model* m, double* total_ms, int64_t* launches);
 
 /* Waits for the model's own device work, frees everything the model holds. */
 void tl_free(tl_model* m);

@@ -69,11 +69,13 @@ def lib():
                             ctypes.POINTER(_P)],
         "tl_forward": [_P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P],
         "tl_decode_step": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
-        "tl_decode_run": [_P, _I, _P, _I, _P, _P, _P, _P],
+        "tl_decode_run": [_P, _I, _P, _I, _P, _P, _P, _P, _P, _P],
         "tl_export_w4": [_P, _I, _I, _P, _P],
         "tl_lane_release": [_P, _I],
         "tl_memory_info": [_P, _P, _P, _P],
         "tl_sync_errors": [_P, _P],
+        "tl_timing_enable": [_P, _I],
+        "tl_timing_read": [_P, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -214,14 +216,14 @@ def tl_decode_step(model, lanes, per_lane_L, out_tokens, in_tokens=None, out_log
     return eff
 
 
-def tl_decode_run(model, lanes, L_req, out_tokens, stream=None):
+def tl_decode_run(model, lanes, L_req, out_tokens, in_tokens=None, out_hidden=None, stream=None):
     """L_req: [n_lanes, n_steps]; returns the effective depths [n_lanes, n_steps]."""
     ln = _i32(lanes)
     req = _i32(L_req)
     n, steps = req.shape
     eff = np.zeros((n, steps), np.int32)
-    _check(lib().tl_decode_run(model.handle, n, _ptr(ln), steps, _ptr(req), _ptr(out_tokens), _ptr(eff),
-                               _stream(stream)))
+    _check(lib().tl_decode_run(model.handle, n, _ptr(ln), steps, _ptr(req), _ptr(in_tokens), _ptr(out_tokens),
+                               _ptr(out_hidden), _ptr(eff), _stream(stream)))
     return eff
 
 
@@ -244,6 +246,23 @@ def tl_memory_info(model):
 
 def tl_sync_errors(model, stream=None):
     _check(lib().tl_sync_errors(model.handle, _stream(stream)))
+
+
+TIMING_CLASSES = ("gemm_qkv_loop", "gemm_o_loop", "gemm_gu_loop", "gemm_down_loop", "gemm_qkv_boundary",
+                  "gemm_o_boundary", "gemm_gu_boundary", "gemm_down_boundary", "attention", "rmsnorm", "head",
+                  "compact", "embed")
+
+
+def tl_timing_enable(model, on: bool = True):
+    _check(lib().tl_timing_enable(model.handle, 1 if on else 0))
+
+
+def tl_timing_read(model):
+    """{class name: (total ms, launches)} since the last read."""
+    ms = np.zeros(len(TIMING_CLASSES), np.float64)
+    n = np.zeros(len(TIMING_CLASSES), np.int64)
+    _check(lib().tl_timing_read(model.handle, _ptr(ms), _ptr(n)))
+    return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(TIMING_CLASSES)}
 
 
 def tl_free(model):

@@ -110,6 +110,7 @@ tl_status stage_upload(tl_model* m, const Stage& st, hipStream_t s) {
 }
 
 // ----------------------------------------------------------------- workspace
+constexpr int64_t kSplitFloats = 8ll << 20;   // 32 MB of split-K partials
 tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStream_t s) {
   auto& w = m->ws;
   if (rows <= w.rows && outs <= w.outs && kv_scratch <= w.kv_scratch_elems) return TL_OK;
@@ -120,7 +121,7 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
   HIPCHK(hipStreamSynchronize(s));
   if (m->last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
   void* olds[] = {w.hA, w.hB, w.hX, w.hE, w.x16, w.q16, w.o16, w.u16, w.xh, w.rowsA, w.rowsB,
-                  w.dest, w.count, w.tok, w.part_v, w.part_i, w.kv_scratch};
+                  w.dest, w.count, w.tok, w.tok2, w.part_v, w.part_i, w.kv_scratch, w.splitk};
   for (void* p : olds) dev_free(m, p);
   w = tl::Workspace{};
   m->ws_bytes = 0;
@@ -134,9 +135,11 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
       {&w.xh, (size_t)std::max(O, 1) * d * m->esz}, {(void**)&w.rowsA, (size_t)R * sizeof(RowInfo)},
       {(void**)&w.rowsB, (size_t)R * sizeof(RowInfo)}, {(void**)&w.dest, (size_t)R * 4},
       {(void**)&w.count, 256},                      {(void**)&w.tok, (size_t)R * 4},
+      {(void**)&w.tok2, (size_t)R * 4},
       {(void**)&w.part_v, (size_t)std::max(O, 1) * tiles * 4},
       {(void**)&w.part_i, (size_t)std::max(O, 1) * tiles * 4},
       {&w.kv_scratch, (size_t)std::max<int64_t>(KS, 1) * m->esz},
+      {(void**)&w.splitk, (size_t)kSplitFloats * 4},
   };
   for (auto& r : reqs) {
     *r.p = dev_alloc(m, r.bytes);
@@ -154,6 +157,52 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
   return TL_OK;
 }
 
+// ----------------------------------------------------------------- timing
+tl_status flush_timing(tl_model* m) {
+  if (m->ev_used == 0) return TL_OK;
+  HIPCHK(hipEventSynchronize(m->ev_pool[m->ev_used - 1]));
+  for (size_t i = 0; i < m->ev_class.size(); ++i) {
+    float ms = 0.f;
+    HIPCHK(hipEventElapsedTime(&ms, m->ev_pool[2 * i], m->ev_pool[2 * i + 1]));
+    m->t_ms[m->ev_class[i]] += ms;
+    m->t_n[m->ev_class[i]] += 1;
+  }
+  m->ev_used = 0;
+  m->ev_class.clear();
+  return TL_OK;
+}
+
+tl_status tbegin(tl_model* m, hipStream_t s) {
+  if (!m->timing) return TL_OK;
+  if (m->ev_used + 2 > m->ev_pool.size()) {
+    if (m->ev_pool.size() >= 16384) {
+      TRY(flush_timing(m));
+    } else {
+      for (int i = 0; i < 512; ++i) {
+        hipEvent_t e;
+        HIPCHK(hipEventCreate(&e));
+        m->ev_pool.push_back(e);
+      }
+    }
+  }
+  HIPCHK(hipEventRecord(m->ev_pool[m->ev_used++], s));
+  return TL_OK;
+}
+
+tl_status tend(tl_model* m, int cls, hipStream_t s) {
+  if (!m->timing) return TL_OK;
+  HIPCHK(hipEventRecord(m->ev_pool[m->ev_used++], s));
+  m->ev_class.push_back(cls);
+  return TL_OK;
+}
+
+#define TIMED(cls, stmt)      \
+  do {                        \
+    TRY(tbegin(m, s));        \
+    stmt;                     \
+    TRY(tend(m, (cls), s));   \
+  } while (0)
+
 // ----------------------------------------------------------------- passes
 tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, hipStream_t s) {
   GemmArgs g{};
@@ -164,6 +213,8 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
   g.B = W.dense;
   g.Bw4 = W.dense ? nullptr : W.w4;
   g.Bs = W.s4;
+  g.partial = m->ws.splitk;
+  g.partial_cap = kSplitFloats;
   e.pair_g = m->G;
   HIPCHK(launch_gemm(m->act, g, e, s));
   return TL_OK;
@@ -174,7 +225,8 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   const tl_config& c = m->cfg;
   const BlockDev& B = m->blocks[b];
   auto& w = m->ws;
-  HIPCHK(launch_rmsnorm(m->act, h, B.norm1, nullptr, n, c.d_model, c.rms_eps, w.x16, s));
+  const int tb = B.kind == 1 ? TL_T_GEMM_QKV_LOOP : TL_T_GEMM_QKV_BOUNDARY;
+  TIMED(TL_T_RMSNORM, HIPCHK(launch_rmsnorm(m->act, h, B.norm1, nullptr, n, c.d_model, c.rms_eps, w.x16, s)));
   GemmEpi e{};
   e.kind = EPI_QKV;
   e.q_out = w.q16;
@@ -185,20 +237,20 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   e.d = c.d_model;
   e.H = c.n_heads;
   e.dh = c.head_dim;
-  TRY(gemm(m, w.x16, n, B.qkv, e, s));
-  HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, s));
+  TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s)));
+  TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, s)));
   GemmEpi r{};
   r.kind = EPI_RESID;
   r.h = h;
   r.ldh = c.d_model;
-  TRY(gemm(m, w.o16, n, B.o, r, s));
-  HIPCHK(launch_rmsnorm(m->act, h, B.norm2, nullptr, n, c.d_model, c.rms_eps, w.x16, s));
+  TIMED(tb + 1, TRY(gemm(m, w.o16, n, B.o, r, s)));
+  TIMED(TL_T_RMSNORM, HIPCHK(launch_rmsnorm(m->act, h, B.norm2, nullptr, n, c.d_model, c.rms_eps, w.x16, s)));
   GemmEpi sw{};
   sw.kind = EPI_SWIGLU;
   sw.u_out = w.u16;
   sw.F = c.ffn;
-  TRY(gemm(m, w.x16, n, B.gu, sw, s));
-  TRY(gemm(m, w.u16, n, B.down, r, s));
+  TIMED(tb + 2, TRY(gemm(m, w.x16, n, B.gu, sw, s)));
+  TIMED(tb + 3, TRY(gemm(m, w.u16, n, B.down, r, s)));
   return TL_OK;
 }
 
@@ -217,7 +269,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   const tl_config& c = m->cfg;
   auto& w = m->ws;
   const int d = c.d_model;
-  HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, w.hA, m->d_err, c.vocab, s));
+  TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, w.hA, m->d_err, c.vocab, s)));
   KVParams kv = p.kv;
   for (int b = 0; b < c.n_pre; ++b) {
     kv.s0 = p.scoring ? 0 : b;
@@ -240,8 +292,8 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     }
     RowInfo* rout = rbuf[flip];
     int32_t* logn = p.log ? p.log + log_off + nj : nullptr;
-    HIPCHK(launch_compact(rows, nj, rout, w.dest, w.count, logn, s));
-    HIPCHK(launch_move_rows(h, w.dest, rows, nj, d, hn, p.final_h, s));
+    TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rows, nj, rout, w.dest, w.count, logn, s));
+                        HIPCHK(launch_move_rows(h, w.dest, rows, nj, d, hn, p.final_h, s)));
     log_off += nj;
     rows = rout;
     flip ^= 1;
@@ -261,6 +313,7 @@ tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out
   if (n_out <= 0) return TL_OK;
   const tl_config& c = m->cfg;
   auto& w = m->ws;
+  TRY(tbegin(m, s));
   HIPCHK(launch_rmsnorm(m->act, h, m->final_norm, gather, n_out, c.d_model, c.rms_eps, w.xh, s));
   const int tiles = gemm_head_tiles(m->act, n_out, c.vocab);
   GemmArgs g{};
@@ -280,6 +333,7 @@ tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out
   if (out_tok || pend_lanes)
     HIPCHK(launch_argmax_reduce(w.part_v, w.part_i, n_out, tiles, out_tok, pend_lanes ? m->d_pending : nullptr,
                                 pend_lanes, s));
+  TRY(tend(m, TL_T_HEAD, s));
   return TL_OK;
 }
 
@@ -587,6 +641,7 @@ void tl_free(tl_model* m) {
   for (void* p : ps) dev_free(m, p);
   if (m->stage_host) (void)hipHostFree(m->stage_host);
   if (m->stage_done) (void)hipEventDestroy(m->stage_done);
+  for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   delete m;
 }
 
@@ -836,11 +891,195 @@ tl_status tl_export_w4(tl_model* m, int32_t block, int32_t matrix, int8_t* q_hos
   return st;
 }
 
+tl_status tl_timing_enable(tl_model* m, int32_t on) {
+  g_err.clear();
+  if (!m) return fail(TL_E_ARG, "NULL model");
+  TRY(flush_timing(m));
+  m->timing = on != 0;
+  return TL_OK;
+}
+
+tl_status tl_timing_read(tl_model* m, double* total_ms, int64_t* launches) {
+  g_err.clear();
+  if (!m || !total_ms || !launches) return fail(TL_E_ARG, "NULL argument");
+  TRY(flush_timing(m));
+  for (int i = 0; i < TL_TIMING_CLASSES; ++i) {
+    total_ms[i] = m->t_ms[i];
+    launches[i] = m->t_n[i];
+    m->t_ms[i] = 0.0;
+    m->t_n[i] = 0;
+  }
+  return TL_OK;
+}
+
+// Continuous depth batching ("Continuous Depth Batching" summary page): work is
+// scheduled one loop iteration at a time.  A pool holds one in-flight token per
+// lane, each at its own iteration; every tick applies the loop stack once to the
+// whole pool, compacts out the tokens that just ran their last iteration, and
+// sends those through the boundary stages (post blocks, final norm, head, greedy
+// token) while the others keep iterating.  A lane whose token left re-enters at
+// the next tick with its next token (embedding, pre blocks, iteration 1).  The
+// depth of every token is known when it enters (clamped request), so the whole
+// schedule, including every exit, is computed on the host first, uploaded in one
+// transfer and enqueued without waiting on the device.
 tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_steps, const int32_t* L_req,
-                        int32_t* out_tokens, int32_t* out_eff_L, void* stream) {
+                        const int32_t* in_tokens, int32_t* out_tokens, float* out_hidden, int32_t* out_eff_L,
+                        void* stream) {
+  g_err.clear();
   if (!m || !lanes || !L_req || !out_tokens) return fail(TL_E_ARG, "NULL argument");
-  (void)n; (void)lanes; (void)n_steps; (void)L_req; (void)out_tokens; (void)out_eff_L; (void)stream;
-  return fail(TL_E_UNSUPPORTED, "continuous-depth decode not built yet");
+  const tl_config& c = m->cfg;
+  if (n < 1 || n_steps < 1) return fail(TL_E_ARG, "n_lanes and n_steps must be >= 1");
+  std::vector<char> seen(c.max_lanes, 0);
+  for (int i = 0; i < n; ++i) {
+    const int l = lanes[i];
+    if (l < 0 || l >= c.max_lanes) return fail(TL_E_ARG, "lane %d out of range [0, %d)", l, c.max_lanes);
+    if (seen[l]) return fail(TL_E_ARG, "lane %d listed twice", l);
+    seen[l] = 1;
+    const Lane& ln = m->lanes[l];
+    if (!ln.live) return fail(TL_E_STATE, "lane %d was never prefilled", l);
+    if (ln.len + n_steps > ln.cap) return fail(TL_E_STATE, "lane %d has room for %d more positions", l, ln.cap - ln.len);
+    for (int t = 0; t < n_steps; ++t)
+      if (L_req[(int64_t)i * n_steps + t] < 1) return fail(TL_E_ARG, "requested L < 1 (lane %d step %d)", l, t);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(ensure_ws(m, n, n, 0, s));
+
+  // ---- host simulation of the schedule
+  struct Item { int i, j, L, pos; };
+  struct Tick {
+    int n_enter = 0, n_pool = 0, n_keep = 0, n_exit = 0;
+    size_t o_erows = 0, o_elanes = 0, o_etok = 0, o_xrows = 0, o_xidx = 0, o_xlanes = 0, o_xout = 0;
+  };
+  std::vector<int> t(n, 0), ceil_(n), len(n);
+  std::vector<int32_t> eff((size_t)n * n_steps, 0);
+  for (int i = 0; i < n; ++i) {
+    ceil_[i] = m->lanes[lanes[i]].ceiling;
+    len[i] = m->lanes[lanes[i]].len;
+  }
+  std::vector<Item> pool;
+  std::vector<int> enter(n);
+  std::iota(enter.begin(), enter.end(), 0);
+  std::vector<Tick> ticks;
+  Stage st;
+  while (!enter.empty() || !pool.empty()) {
+    Tick tk;
+    std::vector<RowInfo> er;
+    std::vector<int32_t> el, etok;
+    for (int i : enter) {
+      etok.push_back(i * n_steps + t[i]);
+      const int L = std::min(L_req[(int64_t)i * n_steps + t[i]], ceil_[i]);
+      ceil_[i] = L;
+      eff[(size_t)i * n_steps + t[i]] = L;
+      RowInfo r{};
+      r.orig = i;
+      r.lane = lanes[i];
+      r.pos = len[i] + t[i];
+      r.depth = L;
+      r.iter = 1;
+      er.push_back(r);
+      el.push_back(lanes[i]);
+      pool.push_back(Item{i, 1, L, r.pos});
+    }
+    tk.n_enter = (int)er.size();
+    if (tk.n_enter) {
+      tk.o_erows = st.add(er);
+      tk.o_elanes = st.add(el);
+      tk.o_etok = st.add(etok);
+    }
+    tk.n_pool = (int)pool.size();
+    std::vector<Item> keep, exits;
+    for (Item it : pool) {
+      if (it.L > it.j) {
+        it.j += 1;
+        keep.push_back(it);
+      } else {
+        exits.push_back(it);
+      }
+    }
+    tk.n_keep = (int)keep.size();
+    tk.n_exit = (int)exits.size();
+    std::vector<RowInfo> xr;
+    std::vector<int32_t> xi, xl, xo;
+    enter.clear();
+    for (const Item& it : exits) {
+      RowInfo r{};
+      r.orig = it.i;
+      r.lane = lanes[it.i];
+      r.pos = it.pos;
+      r.depth = it.L;
+      r.iter = it.j;
+      xr.push_back(r);
+      xi.push_back(it.i);
+      xl.push_back(lanes[it.i]);
+      xo.push_back(it.i * n_steps + t[it.i]);
+      t[it.i] += 1;
+      if (t[it.i] < n_steps) enter.push_back(it.i);
+    }
+    if (tk.n_exit) {
+      tk.o_xrows = st.add(xr);
+      tk.o_xidx = st.add(xi);
+      tk.o_xlanes = st.add(xl);
+      tk.o_xout = st.add(xo);
+    }
+    pool.swap(keep);
+    ticks.push_back(tk);
+  }
+  TRY(stage_upload(m, st, s));
+
+  // ---- enqueue every tick
+  auto& w = m->ws;
+  const int d = c.d_model;
+  KVParams kv{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
+  float* hcur = w.hA;
+  float* hnxt = w.hB;
+  RowInfo* rcur = w.rowsA;
+  RowInfo* rnxt = w.rowsB;
+  int npool = 0;
+  for (const Tick& tk : ticks) {
+    if (tk.n_enter) {
+      const RowInfo* er = staged<RowInfo>(m, tk.o_erows);
+      float* hin = hcur + (int64_t)npool * d;
+      if (in_tokens) HIPCHK(launch_gather_i32(in_tokens, staged<int32_t>(m, tk.o_etok), tk.n_enter, w.tok, s));
+      else HIPCHK(launch_gather_i32(m->d_pending, staged<int32_t>(m, tk.o_elanes), tk.n_enter, w.tok, s));
+      TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, w.tok, tk.n_enter, d, hin, m->d_err, c.vocab, s)));
+      for (int b = 0; b < c.n_pre; ++b) {
+        kv.s0 = b;
+        kv.s1 = 0;
+        TRY(run_block(m, b, hin, er, tk.n_enter, kv, s));
+      }
+      HIPCHK(hipMemcpyAsync(rcur + npool, er, sizeof(RowInfo) * tk.n_enter, hipMemcpyDeviceToDevice, s));
+      npool += tk.n_enter;
+    }
+    for (int l = 0; l < c.n_loop; ++l) {
+      kv.s0 = c.n_pre + c.n_post + l - c.n_loop;
+      kv.s1 = c.n_loop;
+      TRY(run_block(m, c.n_pre + l, hcur, rcur, npool, kv, s));
+    }
+    TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rcur, npool, rnxt, w.dest, w.count, nullptr, s));
+                        HIPCHK(launch_move_rows(hcur, w.dest, rcur, npool, d, hnxt, w.hX, s)));
+    std::swap(hcur, hnxt);
+    std::swap(rcur, rnxt);
+    npool = tk.n_keep;
+    if (tk.n_exit) {
+      const RowInfo* xr = staged<RowInfo>(m, tk.o_xrows);
+      HIPCHK(launch_gather_rows(w.hX, staged<int32_t>(m, tk.o_xidx), tk.n_exit, d, w.hE, s));
+      for (int b = 0; b < c.n_post; ++b) {
+        kv.s0 = c.n_pre + b;
+        kv.s1 = 0;
+        TRY(run_block(m, c.n_pre + c.n_loop + b, w.hE, xr, tk.n_exit, kv, s));
+      }
+      TRY(run_head(m, w.hE, nullptr, tk.n_exit, nullptr, w.tok2, staged<int32_t>(m, tk.o_xlanes), s));
+      HIPCHK(launch_scatter_i32(w.tok2, staged<int32_t>(m, tk.o_xout), tk.n_exit, out_tokens, s));
+      if (out_hidden) HIPCHK(launch_scatter_rows(w.hE, staged<int32_t>(m, tk.o_xout), tk.n_exit, d, out_hidden, s));
+    }
+  }
+  for (int i = 0; i < n; ++i) {
+    Lane& ln = m->lanes[lanes[i]];
+    ln.len += n_steps;
+    ln.ceiling = ceil_[i];
+  }
+  if (out_eff_L) std::memcpy(out_eff_L, eff.data(), eff.size() * 4);
+  return TL_OK;
 }
 
 }  // extern "C"

@@ -58,11 +58,12 @@ struct Workspace {
   float *hA = nullptr, *hB = nullptr, *hX = nullptr, *hE = nullptr;
   void *x16 = nullptr, *q16 = nullptr, *o16 = nullptr, *u16 = nullptr, *xh = nullptr;
   RowInfo *rowsA = nullptr, *rowsB = nullptr;
-  int32_t *dest = nullptr, *count = nullptr, *tok = nullptr;
+  int32_t *dest = nullptr, *count = nullptr, *tok = nullptr, *tok2 = nullptr;
   float* part_v = nullptr;
   int32_t* part_i = nullptr;
   void* kv_scratch = nullptr;
   int part_tiles = 0;
+  float* splitk = nullptr;          // split-K partial tiles
 };
 
 }  // namespace tl
@@ -102,4 +103,11 @@ struct tl_model {
   size_t stage_bytes = 0;
   hipEvent_t stage_done = nullptr;
   hipStream_t last_stream = nullptr;
+  // kernel-class timing (measurement only)
+  bool timing = false;
+  std::vector<hipEvent_t> ev_pool;
+  size_t ev_used = 0;
+  std::vector<int> ev_class;           // class of each recorded (start, stop) pair
+  double t_ms[TL_TIMING_CLASSES] = {};
+  int64_t t_n[TL_TIMING_CLASSES] = {};
 };

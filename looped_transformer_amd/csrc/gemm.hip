@@ -16,6 +16,8 @@
 //   STORE  : fp32 store.
 #include "device_common.h"
 
+#include <algorithm>
+
 namespace {
 
 template <class AT> struct Mfma;
@@ -88,13 +90,22 @@ __device__ __forceinline__ void best_merge(float& v, int& i, float v2, int i2) {
   }
 }
 
+// Workgroup of 4 waves (2 x 2) computes a BM x BN tile over the K range of its
+// split (blockIdx.z).  Per 64-wide K stage: global -> registers (issued one stage
+// ahead, so the loads of stage s+1 are in flight during the MFMAs of stage s),
+// registers -> LDS, then each wave runs (BM/32) x (BN/32) 16x16x32 MFMAs per
+// 32-wide k step.  With several splits, every workgroup stores its fp32 partial
+// tile; the last one to arrive (per-tile counter) adds the partials in split
+// order, so the result does not depend on arrival order, and runs the epilogue.
 template <class AT, bool W4, int BM, int BN, int KIND>
-__global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, GemmEpi e) {
+__global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e, int kchunk) {
   constexpr int BK = 64;
   constexpr int LDK = BK + 8;   // padded LDS row, elements
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 16, TN = WTN / 16;
-  static_assert(TM >= 1 && TN >= 2 && (TN % 2) == 0, "tile");
+  constexpr int AC = BM * (BK / 8) / 256;                 // 16-byte A chunks per thread
+  constexpr int BC = W4 ? 1 : BN * (BK / 8) / 256;        // 16-byte B chunks per thread
+  static_assert(TM >= 1 && TN >= 2 && (TN % 2) == 0 && AC >= 1 && BC >= 1, "tile");
   typedef typename Mfma<AT>::frag frag;
 
   __shared__ __attribute__((aligned(16))) AT As[BM * LDK];
@@ -105,7 +116,10 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, GemmEpi e) {
   const int wm = wave >> 1, wn = wave & 1;
   const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN;
   const int M = g.M, N = g.N, K = g.K;
+  const int S = gridDim.z, z = blockIdx.z;
+  const int kb = z * kchunk, ke = min(K, kb + kchunk);
   const AT* A = reinterpret_cast<const AT*>(g.A);
+  const int groups = K >> 7;
 
   floatx4 acc[TM][TN];
   floatx4 tmp[TM][TN];
@@ -117,64 +131,82 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, GemmEpi e) {
       tmp[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-  const int groups = K / 128;
-  for (int k0 = 0; k0 < K; k0 += BK) {
-    // A tile: BM x BK in 16-byte chunks (8 elements); rows >= M and k >= K read as 0.
-    constexpr int ACH = BM * (BK / 8);
+  uint4 ra[AC], rb[BC];
+  uint16_t rs = 0;
+  auto gload = [&](int k0) {
 #pragma unroll
-    for (int c = tid; c < ACH; c += 256) {
-      const int r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+    for (int i = 0; i < AC; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
       const int gr = m0 + r, gk = k0 + kc;
-      uint4 v = {0u, 0u, 0u, 0u};
-      if (gr < M && gk < K) v = *reinterpret_cast<const uint4*>(A + (int64_t)gr * K + gk);
-      *reinterpret_cast<uint4*>(&As[r * LDK + kc]) = v;
+      ra[i] = uint4{0u, 0u, 0u, 0u};
+      if (gr < M && gk < ke) ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)gr * K + gk);
     }
     if constexpr (W4) {
-      // Half a 128-wide group per stage: 32 bytes (64 k) of each of BN rows.
       const int gidx = k0 >> 7, hsel = (k0 >> 6) & 1;
-      constexpr int BCH = BN * 2;
-#pragma unroll
-      for (int c = tid; c < BCH; c += 256) {
+      const int c = tid;
+      rb[0] = uint4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};   // q = 0
+      if (c < BN * 2) {
         const int nb = c >> 5, within = c & 31, row = within >> 1, qq = within & 1;
         const int gn = n0 + nb * 16 + row;
-        uint4 w = {0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};   // q = 0
         if (gn < N) {
           const int64_t blk = (int64_t)((n0 >> 4) + nb) * groups + gidx;
-          w = *reinterpret_cast<const uint4*>(g.Bw4 + blk * 256 + row * 16 + hsel * 8 + qq * 4);
+          rb[0] = *reinterpret_cast<const uint4*>(g.Bw4 + blk * 256 + row * 16 + hsel * 8 + qq * 4);
         }
-        const uint32_t ws[4] = {w.x, w.y, w.z, w.w};
+      }
+      if (hsel == 0 && tid < BN) {
+        const int gn = n0 + tid;
+        rs = gn < N ? g.Bs[(int64_t)gidx * N + gn] : (uint16_t)0;
+      }
+    } else {
+      const AT* B = reinterpret_cast<const AT*>(g.B);
+#pragma unroll
+      for (int i = 0; i < BC; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
+        const int gn = n0 + r, gk = k0 + kc;
+        rb[i] = uint4{0u, 0u, 0u, 0u};
+        if (gn < N && gk < ke) rb[i] = *reinterpret_cast<const uint4*>(B + (int64_t)gn * K + gk);
+      }
+    }
+  };
+  auto lstore = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
+      *reinterpret_cast<uint4*>(&As[r * LDK + kc]) = ra[i];
+    }
+    if constexpr (W4) {
+      const int c = tid;
+      if (c < BN * 2) {
+        const int nb = c >> 5, within = c & 31, row = within >> 1, qq = within & 1;
+        const uint32_t ws[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
         f16* dst = reinterpret_cast<f16*>(&Bs[(nb * 16 + row) * LDK + qq * 32]);
 #pragma unroll
         for (int wi = 0; wi < 4; ++wi) {
           half8 h;
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            half2v t = w4_pair(ws[wi], p);
+            const half2v t = w4_pair(ws[wi], p);
             h[2 * p] = t[0];
             h[2 * p + 1] = t[1];
           }
           *reinterpret_cast<half8*>(dst + wi * 8) = h;
         }
       }
-      if (hsel == 0 && tid < BN) {
-        const int gn = n0 + tid;
-        uint16_t sb = gn < N ? g.Bs[(int64_t)gidx * N + gn] : (uint16_t)0;
-        Ss[tid] = (float)__builtin_bit_cast(f16, sb);
-      }
+      if (((k0 >> 6) & 1) == 0 && tid < BN) Ss[tid] = (float)__builtin_bit_cast(f16, rs);
     } else {
-      const AT* B = reinterpret_cast<const AT*>(g.B);
-      constexpr int BCH = BN * (BK / 8);
 #pragma unroll
-      for (int c = tid; c < BCH; c += 256) {
-        const int r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-        const int gn = n0 + r, gk = k0 + kc;
-        uint4 v = {0u, 0u, 0u, 0u};
-        if (gn < N && gk < K) v = *reinterpret_cast<const uint4*>(B + (int64_t)gn * K + gk);
-        *reinterpret_cast<uint4*>(&Bs[r * LDK + kc]) = v;
+      for (int i = 0; i < BC; ++i) {
+        const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
+        *reinterpret_cast<uint4*>(&Bs[r * LDK + kc]) = rb[i];
       }
     }
-    __syncthreads();
+  };
 
+  if (kb < ke) gload(kb);
+  for (int k0 = kb; k0 < ke; k0 += BK) {
+    lstore(k0);
+    __syncthreads();
+    if (k0 + BK < ke) gload(k0 + BK);
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       frag a[TM], b[TN];
@@ -192,13 +224,13 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, GemmEpi e) {
         }
     }
     if constexpr (W4) {
-      if (((k0 >> 6) & 1) == 1 || k0 + BK >= K) {   // end of a 128-wide group: apply its scale
+      if (((k0 >> 6) & 1) == 1) {   // end of a 128-wide group: apply its scale
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          const float s = Ss[wn * WTN + j * 16 + (lane & 15)];
+          const float sc = Ss[wn * WTN + j * 16 + (lane & 15)];
 #pragma unroll
           for (int i = 0; i < TM; ++i) {
-            acc[i][j] += s * tmp[i][j];
+            acc[i][j] += sc * tmp[i][j];
             tmp[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
           }
         }
@@ -207,8 +239,28 @@ __global__ __launch_bounds__(256) void gemm_mfma_kernel(GemmArgs g, GemmEpi e) {
     __syncthreads();
   }
 
-  // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + r of each 16x16 tile
   const int lc = lane & 15, lr = 4 * (lane >> 4);
+  if (S > 1) {
+    // split-K: store this split's fp32 partial tile; splitk_epilogue_kernel adds
+    // the splits in order and runs the epilogue (the kernel boundary makes the
+    // partials visible across XCDs without any cache maintenance here)
+    float* part = g.partial + (int64_t)z * M * N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * WTM + i * 16 + lr + r;
+        if (row >= M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int col = n0 + wn * WTN + j * 16 + lc;
+          if (col < N) part[(int64_t)row * N + col] = acc[i][j][r];
+        }
+      }
+    return;
+  }
+
+  // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + r of each 16x16 tile
   if constexpr (KIND == EPI_HEAD) {
     __shared__ float red_v[BM][2];
     __shared__ int red_i[BM][2];
@@ -358,43 +410,117 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, GemmEpi e) {
   }
 }
 
+// Sum of the split-K partials in split order, then the epilogue.  Paired
+// epilogues get one thread per (row, pair): columns c and c + G with c in an even
+// G-chunk; the others one thread per (row, column).
+template <class AT, int KIND>
+__global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEpi e, int S) {
+  const int M = g.M, N = g.N;
+  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if constexpr (paired(KIND)) {
+    const int G = e.pair_g;
+    const int64_t per_row = N / 2;
+    if (idx >= (int64_t)M * per_row) return;
+    const int row = (int)(idx / per_row);
+    const int p = (int)(idx - (int64_t)row * per_row);
+    const int c = (p / G) * 2 * G + (p % G);
+    float v0 = 0.f, v1 = 0.f;
+    for (int z = 0; z < S; ++z) {
+      const float* pr = g.partial + ((int64_t)z * M + row) * N;
+      v0 += pr[c];
+      v1 += pr[c + G];
+    }
+    epi_pair<AT, KIND>(e, row, c, v0, v1);
+  } else {
+    if (idx >= (int64_t)M * N) return;
+    const int row = (int)(idx / N);
+    const int c = (int)(idx - (int64_t)row * N);
+    float v = 0.f;
+    for (int z = 0; z < S; ++z) v += g.partial[((int64_t)z * M + row) * N + c];
+    epi_one<KIND>(e, row, c, v);
+  }
+}
+
 struct TileCfg {
-  int bm, bn;
+  int bm, bn, splits, kchunk;
 };
 
-TileCfg pick_tile(int act_dtype, int M) {
-  if (act_dtype == DT_F32) return {64, 64};
-  if (M <= 32) return {32, 128};
-  if (M <= 64) return {64, 128};
-  return {128, 128};
+constexpr int kCUs = 256;
+
+// Tile and split choice: enough workgroups to cover the 256 CUs about twice,
+// splitting K (in whole 128-wide groups) only when the tiles alone cannot.
+TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
+  if (act_dtype == DT_F32) return {64, 64, 1, g.K};
+  TileCfg t{g.M <= 32 ? 32 : (g.M <= 64 ? 64 : 128), 128, 1, g.K};
+  const int64_t mt = (g.M + t.bm - 1) / t.bm;
+  if (mt * ((g.N + 127) / 128) < kCUs) t.bn = 64;
+  if (kind == EPI_HEAD) t.bn = 128;
+  const int64_t tiles = mt * ((g.N + t.bn - 1) / t.bn);
+  const int unit = 128;
+  const int64_t units = (g.K + unit - 1) / unit;
+  if (kind != EPI_HEAD && tiles < 2 * kCUs && g.partial && units > 1 && (g.N % 32) == 0) {
+    int64_t want = (2 * kCUs + tiles - 1) / tiles;
+    want = std::min<int64_t>(want, 16);
+    want = std::min<int64_t>(want, units);
+    while (want > 1 && want * g.M * g.N > g.partial_cap) --want;
+    if (want > 1) {
+      const int64_t per = (units + want - 1) / want;     // units per split
+      t.kchunk = (int)(per * unit);
+      t.splits = (int)((units + per - 1) / per);
+    }
+  }
+  return t;
 }
 
 template <class AT, bool W4, int BM, int BN>
-hipError_t launch_mfma_bm(const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
-  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM);
+hipError_t launch_mfma_t(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, hipStream_t s) {
+  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, t.splits);
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_QKV>), grid, dim3(256), 0, s, g, e); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_RESID>), grid, dim3(256), 0, s, g, e); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e); break;
-    case EPI_HEAD: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_HEAD>), grid, dim3(256), 0, s, g, e); break;
-    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_STORE>), grid, dim3(256), 0, s, g, e); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_HEAD: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_HEAD>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
     default: return hipErrorInvalidValue;
+  }
+  if (t.splits > 1) {
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const bool pr = e.kind == EPI_QKV || e.kind == EPI_SWIGLU;
+    const int64_t items = (int64_t)g.M * (pr ? g.N / 2 : g.N);
+    dim3 rg((unsigned)((items + 255) / 256));
+    switch (e.kind) {
+      case EPI_QKV: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_QKV>), rg, dim3(256), 0, s, g, e, t.splits); break;
+      case EPI_RESID: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_RESID>), rg, dim3(256), 0, s, g, e, t.splits); break;
+      case EPI_SWIGLU: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_SWIGLU>), rg, dim3(256), 0, s, g, e, t.splits); break;
+      case EPI_STORE: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_STORE>), rg, dim3(256), 0, s, g, e, t.splits); break;
+      default: return hipErrorInvalidValue;
+    }
   }
   return hipGetLastError();
 }
 
 template <class AT, bool W4>
 hipError_t launch_mfma(const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
-  const TileCfg t = pick_tile(DT_F16, g.M);
-  if (t.bm == 32) return launch_mfma_bm<AT, W4, 32, 128>(g, e, s);
-  if (t.bm == 64) return launch_mfma_bm<AT, W4, 64, 128>(g, e, s);
-  return launch_mfma_bm<AT, W4, 128, 128>(g, e, s);
+  const TileCfg t = pick_tile(DT_F16, g, e.kind);
+  if (t.bn == 64) {
+    if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 64>(g, e, t, s);
+    if (t.bm == 64) return launch_mfma_t<AT, W4, 64, 64>(g, e, t, s);
+    return launch_mfma_t<AT, W4, 128, 64>(g, e, t, s);
+  }
+  if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 128>(g, e, t, s);
+  if (t.bm == 64) return launch_mfma_t<AT, W4, 64, 128>(g, e, t, s);
+  return launch_mfma_t<AT, W4, 128, 128>(g, e, t, s);
 }
 
 }  // namespace
 
 int gemm_head_tiles(int act_dtype, int M, int N) {
-  const TileCfg t = pick_tile(act_dtype, M);
+  GemmArgs g{};
+  g.M = M;
+  g.N = N;
+  g.K = 128;
+  const TileCfg t = pick_tile(act_dtype, g, EPI_HEAD);
   return (N + t.bn - 1) / t.bn;
 }
 

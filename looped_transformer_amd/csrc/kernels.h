@@ -29,6 +29,9 @@ struct GemmArgs {
   const void* B;          // dense weights [N, K] (act dtype), or NULL for W4
   const uint32_t* Bw4;    // INT4 kernel layout words, or NULL
   const uint16_t* Bs;     // INT4 fp16 scales [K/128][N]
+  // split-K workspace: fp32 partial tiles [splits][M][N]
+  float* partial;
+  int64_t partial_cap;    // floats
 };
 
 struct GemmEpi {
@@ -82,6 +85,7 @@ hipError_t launch_argmax_reduce(const float* part_val, const int32_t* part_idx, 
 hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
+hipError_t launch_scatter_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s);
 hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s);
 
 // Load-time kernels.  perm[n] = canonical source row of kernel row n.

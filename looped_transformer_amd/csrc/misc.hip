@@ -159,6 +159,11 @@ __global__ void gather_i32_kernel(const int32_t* src, const int32_t* idx, int n,
   if (i < n) dst[i] = src[idx[i]];
 }
 
+__global__ void scatter_i32_kernel(const int32_t* src, const int32_t* idx, int n, int32_t* dst) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) dst[idx[i]] = src[i];
+}
+
 // ---------------------------------------------------------------- load time
 __global__ __launch_bounds__(256) void permute_rows_kernel(const uint32_t* __restrict__ src, const int32_t* __restrict__ perm,
                                                           int words_per_row, uint32_t* __restrict__ dst) {
@@ -302,6 +307,12 @@ hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
 hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(gather_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_scatter_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(scatter_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
   return hipGetLastError();
 }
 
