@@ -89,7 +89,194 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   }
 }
 
+// ----------------------------------------------------------------------------
+// Tiled causal attention for runs of consecutive query rows of one sequence.
+// Workgroup = (64-row tile, head); wave w owns query rows 16w .. 16w+15.  Keys and
+// values stream through LDS in blocks of 64 positions.  S = Q K^T and O += P V run
+// on 16x16x32 MFMA (QK^T in the cache type, PV in fp16 with V converted on its way
+// into LDS), with a running row max / sum in fp32 (online softmax).  The score
+// tile leaves the MFMA in column-per-lane layout, so P goes through LDS to become
+// the row-per-lane A operand of PV.
+template <class T> struct QkMfma;
+template <> struct QkMfma<f16> {
+  typedef half8 frag;
+  static __device__ __forceinline__ floatx4 run(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+};
+template <> struct QkMfma<bf16> {
+  typedef bf16x8 frag;
+  static __device__ __forceinline__ floatx4 run(frag a, frag b, floatx4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+};
+
+template <class T, int DH>
+__global__ __launch_bounds__(256) void attn_tiled_kernel(const T* __restrict__ q, const AttnTile* __restrict__ tiles,
+                                                        KVParams kv, T* __restrict__ out, int d, float scale) {
+  constexpr int KB = 64;
+  constexpr int LDK = DH + 8;
+  constexpr int LDV = KB + 8;
+  constexpr int KS = DH / 32;
+  constexpr int OT = DH / 16;
+  typedef typename QkMfma<T>::frag qfrag;
+  __shared__ __attribute__((aligned(16))) T Ks[KB * LDK];
+  __shared__ __attribute__((aligned(16))) f16 Vt[DH * LDV];
+  __shared__ __attribute__((aligned(16))) f16 Ps[4][16 * LDV];
+
+  const AttnTile tile = tiles[blockIdx.x];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int slot = kv.s0 + kv.s1 * tile.iter;
+  const int64_t cap = kv.lane_cap[tile.lane];
+  const T* Kg = reinterpret_cast<const T*>(kv.base) + kv.lane_off[tile.lane] + ((int64_t)(slot * 2) * kv.H + h) * cap * DH;
+  const T* Vg = Kg + (int64_t)kv.H * cap * DH;
+
+  const int qr = 16 * w + l16;
+  qfrag qa[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    qfrag v = {};
+    if (qr < tile.nrows)
+      v = *reinterpret_cast<const qfrag*>(q + (int64_t)(tile.row0 + qr) * d + h * DH + ks * 32 + 8 * g4);
+    qa[ks] = v;
+  }
+  floatx4 o[OT];
+#pragma unroll
+  for (int t = 0; t < OT; ++t) o[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+  }
+  const int qpos0 = tile.pos0 + 16 * w + 4 * g4;
+  const int kend = tile.pos0 + tile.nrows;
+
+  for (int k0 = 0; k0 < kend; k0 += KB) {
+    __syncthreads();
+    for (int c = tid; c < KB * DH / 8; c += 256) {
+      const int key = c / (DH / 8), dc = (c % (DH / 8)) * 8;
+      const int kp = k0 + key;
+      uint4 kvv = {0u, 0u, 0u, 0u}, vvv = {0u, 0u, 0u, 0u};
+      if (kp < kend) {
+        kvv = *reinterpret_cast<const uint4*>(Kg + (int64_t)kp * DH + dc);
+        vvv = *reinterpret_cast<const uint4*>(Vg + (int64_t)kp * DH + dc);
+      }
+      *reinterpret_cast<uint4*>(&Ks[key * LDK + dc]) = kvv;
+      const T* ve = reinterpret_cast<const T*>(&vvv);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) Vt[(dc + e) * LDV + key] = (f16)(float)ve[e];
+    }
+    __syncthreads();
+
+    floatx4 sacc[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      sacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const qfrag b = *reinterpret_cast<const qfrag*>(&Ks[(16 * n + l16) * LDK + ks * 32 + 8 * g4]);
+        sacc[n] = QkMfma<T>::run(qa[ks], b, sacc[n]);
+      }
+    }
+    float mx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx[r] = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kp = k0 + 16 * n + l16;
+        float v = sacc[n][r] * scale;
+        if (kp > qpos0 + r || kp >= kend) v = -INFINITY;
+        sacc[n][r] = v;
+        mx[r] = fmaxf(mx[r], v);
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], off, 64));
+    }
+    float corr[4], rs[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mn = fmaxf(mrow[r], mx[r]);
+      corr[r] = expf(mrow[r] - mn);
+      mrow[r] = mn;
+      rs[r] = 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = expf(sacc[n][r] - mrow[r]);
+        rs[r] += p;
+        Ps[w][(4 * g4 + r) * LDV + 16 * n + l16] = (f16)p;
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) rs[r] += __shfl_xor(rs[r], off, 64);
+      lrow[r] = lrow[r] * corr[r] + rs[r];
+    }
+#pragma unroll
+    for (int t = 0; t < OT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[t][r] *= corr[r];
+    __syncthreads();   // P tiles written
+#pragma unroll
+    for (int kk = 0; kk < KB; kk += 32) {
+      const half8 a = *reinterpret_cast<const half8*>(&Ps[w][l16 * LDV + kk + 8 * g4]);
+#pragma unroll
+      for (int t = 0; t < OT; ++t) {
+        const half8 b = *reinterpret_cast<const half8*>(&Vt[(16 * t + l16) * LDV + kk + 8 * g4]);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, o[t], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rl = 16 * w + 4 * g4 + r;
+    if (rl >= tile.nrows) continue;
+    const float inv = 1.0f / lrow[r];
+    T* op = out + (int64_t)(tile.row0 + rl) * d + h * DH + l16;
+#pragma unroll
+    for (int t = 0; t < OT; ++t) op[16 * t] = from_f32<T>(o[t][r] * inv);
+  }
+}
+
 }  // namespace
+
+bool attn_tiled_supported(int dtype, int head_dim) {
+  return (dtype == DT_F16 || dtype == DT_BF16) && (head_dim == 64 || head_dim == 96 || head_dim == 128);
+}
+
+hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tiles, int n_tiles, const KVParams& kv,
+                                  void* out, hipStream_t s) {
+  if (n_tiles <= 0) return hipSuccess;
+  const int d = kv.H * kv.dh;
+  const float scale = 1.0f / sqrtf((float)kv.dh);
+  dim3 grid(n_tiles, kv.H);
+#define TL_ATTN_CASE(T, DHV)                                                                                   \
+  if (kv.dh == DHV) {                                                                                          \
+    hipLaunchKernelGGL((attn_tiled_kernel<T, DHV>), grid, dim3(256), 0, s, (const T*)q, tiles, kv, (T*)out, d, \
+                       scale);                                                                                 \
+    return hipGetLastError();                                                                                  \
+  }
+  if (dtype == DT_F16) {
+    TL_ATTN_CASE(f16, 64)
+    TL_ATTN_CASE(f16, 96)
+    TL_ATTN_CASE(f16, 128)
+  } else if (dtype == DT_BF16) {
+    TL_ATTN_CASE(bf16, 64)
+    TL_ATTN_CASE(bf16, 96)
+    TL_ATTN_CASE(bf16, 128)
+  }
+#undef TL_ATTN_CASE
+  return hipErrorInvalidValue;
+}
 
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
                             hipStream_t s) {

@@ -220,7 +220,8 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
   return TL_OK;
 }
 
-tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, const KVParams& kv, hipStream_t s) {
+tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, const KVParams& kv, hipStream_t s,
+                    const AttnTile* tiles = nullptr, int n_tiles = 0) {
   if (n <= 0) return TL_OK;
   const tl_config& c = m->cfg;
   const BlockDev& B = m->blocks[b];
@@ -238,7 +239,8 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   e.H = c.n_heads;
   e.dh = c.head_dim;
   TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s)));
-  TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, s)));
+  if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, kv, w.o16, s)));
+  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, s)));
   GemmEpi r{};
   r.kind = EPI_RESID;
   r.h = h;
@@ -263,18 +265,28 @@ struct Pass {
   bool scoring = false;              // one reusable slot per sequence
   float* final_h = nullptr;          // [n, d], caller order
   int32_t* log = nullptr;
+  // tiled attention (prefill / scoring): tile lists per iteration (index j-1);
+  // iteration 1's list covers every row in caller order (pre and post blocks too)
+  std::vector<const AttnTile*> tiles;
+  std::vector<int> n_tiles;
 };
 
+// Pre blocks on all rows; loop iteration j on the n_j rows still active, each
+// application writing its own cache slot; rows leave (compaction) only after an
+// iteration that is the last one of some row; post blocks on all rows.
 tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   const tl_config& c = m->cfg;
   auto& w = m->ws;
   const int d = c.d_model;
+  const bool tiled = !p.tiles.empty();
   TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, w.hA, m->d_err, c.vocab, s)));
   KVParams kv = p.kv;
+  kv.s1 = 0;
+  const AttnTile* t0 = tiled ? p.tiles[0] : nullptr;
+  const int nt0 = tiled ? p.n_tiles[0] : 0;
   for (int b = 0; b < c.n_pre; ++b) {
     kv.s0 = p.scoring ? 0 : b;
-    kv.s1 = 0;
-    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s));
+    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0));
   }
   float* h = w.hA;
   float* hn = w.hB;
@@ -282,29 +294,56 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   RowInfo* rbuf[2] = {w.rowsA, w.rowsB};
   int flip = 0;
   int64_t log_off = 0;
-  for (size_t j = 1; j <= p.n_active.size(); ++j) {
+  bool moved = true;
+  const int Lmax = (int)p.n_active.size();
+  for (int j = 1; j <= Lmax; ++j) {
     const int nj = p.n_active[j - 1];
-    if (p.log && j == 1) HIPCHK(launch_write_orig(rows, nj, p.log, s));
+    if (p.log && moved) HIPCHK(launch_write_orig(rows, nj, p.log + log_off, s));
     for (int l = 0; l < c.n_loop; ++l) {
-      kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + l - c.n_loop;
-      kv.s1 = p.scoring ? 0 : c.n_loop;
-      TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s));
+      kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + (j - 1) * c.n_loop + l;
+      TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr, tiled ? p.n_tiles[j - 1] : 0));
     }
-    RowInfo* rout = rbuf[flip];
-    int32_t* logn = p.log ? p.log + log_off + nj : nullptr;
-    TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rows, nj, rout, w.dest, w.count, logn, s));
-                        HIPCHK(launch_move_rows(h, w.dest, rows, nj, d, hn, p.final_h, s)));
+    const int next = j < Lmax ? p.n_active[j] : 0;
+    moved = next < nj;
+    if (moved) {
+      RowInfo* rout = rbuf[flip];
+      int32_t* logn = p.log ? p.log + log_off + nj : nullptr;
+      TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rows, nj, j, rout, w.dest, w.count, logn, s));
+                          HIPCHK(launch_move_rows(h, w.dest, rows, nj, d, hn, p.final_h, s)));
+      rows = rout;
+      flip ^= 1;
+      std::swap(h, hn);
+      moved = false;   // the compaction already logged iteration j + 1
+    } else {
+      moved = true;    // rows unchanged: log iteration j + 1 from the same list
+    }
     log_off += nj;
-    rows = rout;
-    flip ^= 1;
-    std::swap(h, hn);
   }
   for (int b = 0; b < c.n_post; ++b) {
     kv.s0 = p.scoring ? 0 : c.n_pre + b;
-    kv.s1 = 0;
-    TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s));
+    TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s, t0, nt0));
   }
   return TL_OK;
+}
+
+// Attention tiles of one iteration: sequences still active, in caller order, each
+// cut into runs of at most 64 consecutive rows.
+void add_tiles(std::vector<AttnTile>& out, const std::vector<int>& seq_len, const std::vector<int>& seq_lane,
+               const std::vector<int>& Ls, int j) {
+  int row = 0;
+  for (size_t sq = 0; sq < seq_len.size(); ++sq) {
+    if (Ls[sq] < j) continue;
+    for (int p0 = 0; p0 < seq_len[sq]; p0 += 64) {
+      AttnTile t{};
+      t.row0 = row + p0;
+      t.nrows = std::min(64, seq_len[sq] - p0);
+      t.pos0 = p0;
+      t.lane = seq_lane[sq];
+      t.iter = j;
+      out.push_back(t);
+    }
+    row += seq_len[sq];
+  }
 }
 
 // Final norm on the selected rows, head GEMM, greedy token (lowest index on ties).
@@ -758,7 +797,23 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
       loff[lanes[i]] = (int64_t)new_lanes[i].off;
       lcap[lanes[i]] = new_lanes[i].cap;
     }
+  // attention tiles for each distinct active set (prefill / scoring passes)
+  const bool tiled = attn_tiled_supported(m->act, c.head_dim);
+  std::vector<int> slen(n_seqs), slane(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    slen[i] = cu[i + 1] - cu[i];
+    slane[i] = lanes ? lanes[i] : i;
+  }
+  const std::vector<int> n_act = active_counts(depth);
+  std::vector<std::vector<AttnTile>> tile_lists;
+  if (tiled)
+    for (size_t j = 1; j <= n_act.size(); ++j) {
+      tile_lists.emplace_back();
+      add_tiles(tile_lists.back(), slen, slane, Ls, (int)j);
+    }
   Stage st;
+  std::vector<size_t> o_tiles;
+  for (auto& tlst : tile_lists) o_tiles.push_back(st.add(tlst));
   const size_t o_rows = st.add(rows), o_last = st.add(last), o_lanes = st.add(lane_ids);
   const size_t o_soff = st.add(soff), o_scap = st.add(scap);
   const size_t o_loff = st.add(loff), o_lcap = st.add(lcap);
@@ -775,7 +830,11 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   p.n = T;
   p.tokens = tokens;
   p.rows0 = staged<RowInfo>(m, o_rows);
-  p.n_active = active_counts(depth);
+  p.n_active = n_act;
+  for (size_t k = 0; k < tile_lists.size(); ++k) {
+    p.tiles.push_back(staged<AttnTile>(m, o_tiles[k]));
+    p.n_tiles.push_back((int)tile_lists[k].size());
+  }
   p.kv.H = c.n_heads;
   p.kv.dh = c.head_dim;
   if (lanes) {
@@ -1055,7 +1114,7 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
       kv.s1 = c.n_loop;
       TRY(run_block(m, c.n_pre + l, hcur, rcur, npool, kv, s));
     }
-    TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rcur, npool, rnxt, w.dest, w.count, nullptr, s));
+    TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rcur, npool, 0, rnxt, w.dest, w.count, nullptr, s));
                         HIPCHK(launch_move_rows(hcur, w.dest, rcur, npool, d, hnxt, w.hX, s)));
     std::swap(hcur, hnxt);
     std::swap(rcur, rnxt);

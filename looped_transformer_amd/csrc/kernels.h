@@ -71,10 +71,21 @@ hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const i
                           int d, float eps, void* out, hipStream_t s);
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv,
                             void* out, hipStream_t s);
-// Stable filter of the active rows: rows with depth > iter stay (iter + 1), the
-// others leave.  dest[i] = new index or -1.  count_out[0] = number kept.  If
-// log_out is non-NULL the kept rows' orig indices are written there.
-hipError_t launch_compact(const RowInfo* rows_in, int n, RowInfo* rows_out, int32_t* dest,
+// A run of up to 64 consecutive rows of one sequence (positions pos0 .. pos0+nrows-1)
+// that attend to positions 0 .. pos0+nrows-1 of their lane's slot.
+struct AttnTile {
+  int32_t row0, nrows, pos0, lane, iter, p0, p1, p2;
+};
+// Tiled causal attention (MFMA) for prefill / scoring passes; 16-bit types and
+// head_dim in {64, 96, 128} only (attn_tiled_supported).
+bool attn_tiled_supported(int dtype, int head_dim);
+hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tiles, int n_tiles, const KVParams& kv,
+                                  void* out, hipStream_t s);
+// Stable filter of the active rows after iteration it (it = 0: each row's own
+// iter): rows with depth > it stay (their iter becomes it + 1), the others leave.
+// dest[i] = new index or -1.  count_out[0] = number kept.  If log_out is non-NULL
+// the kept rows' orig indices are written there.
+hipError_t launch_compact(const RowInfo* rows_in, int n, int it, RowInfo* rows_out, int32_t* dest,
                           int32_t* count_out, int32_t* log_out, hipStream_t s);
 // h_next[dest[i]] = h[i] for kept rows; h_exit[rows[i].orig] = h[i] for leaving rows.
 hipError_t launch_move_rows(const float* h, const int32_t* dest, const RowInfo* rows, int n, int d,

@@ -55,7 +55,7 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 
 // ---------------------------------------------------------------- compaction
 // Stable filter in one workgroup: chunks of 1024 rows, wave ballots + prefix.
-__global__ __launch_bounds__(1024) void compact_kernel(const RowInfo* __restrict__ in, int n,
+__global__ __launch_bounds__(1024) void compact_kernel(const RowInfo* __restrict__ in, int n, int it,
                                                       RowInfo* __restrict__ out, int32_t* __restrict__ dest,
                                                       int32_t* count_out, int32_t* log_out) {
   __shared__ int wave_cnt[16];
@@ -69,6 +69,7 @@ __global__ __launch_bounds__(1024) void compact_kernel(const RowInfo* __restrict
     RowInfo ri;
     if (i < n) {
       ri = in[i];
+      if (it > 0) ri.iter = it;
       keep = ri.depth > ri.iter;
     }
     const uint64_t mask = __ballot(keep);
@@ -259,10 +260,10 @@ hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const i
   return hipGetLastError();
 }
 
-hipError_t launch_compact(const RowInfo* rows_in, int n, RowInfo* rows_out, int32_t* dest, int32_t* count_out,
+hipError_t launch_compact(const RowInfo* rows_in, int n, int it, RowInfo* rows_out, int32_t* dest, int32_t* count_out,
                           int32_t* log_out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, rows_in, n, rows_out, dest, count_out, log_out);
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, rows_in, n, it, rows_out, dest, count_out, log_out);
   return hipGetLastError();
 }
 
