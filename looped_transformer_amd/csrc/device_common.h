@@ -15,6 +15,15 @@ typedef float floatx4 __attribute__((ext_vector_type(4)));
 template <class T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
 template <class T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }  // RNE
 
+// Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
+// for every outstanding global load of the thread, which would drain the
+// register prefetch of the next K stage at each stage boundary.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 // Wave64 reductions (xor butterflies keep every lane holding the result).
 __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll

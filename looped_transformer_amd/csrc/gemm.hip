@@ -17,8 +17,18 @@
 #include "device_common.h"
 
 #include <algorithm>
+#include <type_traits>
 
 namespace {
+
+// Compile-time loop: f(std::integral_constant<int, I>) for I = 0 .. N-1.
+template <int I, int N, class F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
 
 template <class AT> struct Mfma;
 template <> struct Mfma<f16> {
@@ -91,26 +101,29 @@ __device__ __forceinline__ void best_merge(float& v, int& i, float v2, int i2) {
 }
 
 // Workgroup of 4 waves (2 x 2) computes a BM x BN tile over the K range of its
-// split (blockIdx.z).  Per 64-wide K stage: global -> registers (issued one stage
-// ahead, so the loads of stage s+1 are in flight during the MFMAs of stage s),
-// registers -> LDS, then each wave runs (BM/32) x (BN/32) 16x16x32 MFMAs per
-// 32-wide k step.  With several splits, every workgroup stores its fp32 partial
-// tile; the last one to arrive (per-tile counter) adds the partials in split
-// order, so the result does not depend on arrival order, and runs the epilogue.
-template <class AT, bool W4, int BM, int BN, int KIND>
+// split (blockIdx.z).  Per BK-wide K stage: global -> registers, issued D-1 stages
+// ahead into a ring of D register sets (so D-1 stages of loads are in flight while
+// a stage computes), registers -> LDS, then each wave runs (BM/32) x (BN/32)
+// 16x16x32 MFMAs per 32-wide k step.  INT4 stages cover whole 128-wide groups; each group's MFMA sum
+// is scaled when the group ends.  With several splits each workgroup stores an
+// fp32 partial tile and splitk_epilogue_kernel finishes the tile.
+template <class AT, bool W4, int BM, int BN, int BK, int D, int KIND>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e, int kchunk) {
-  constexpr int BK = 64;
   constexpr int LDK = BK + 8;   // padded LDS row, elements
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 16, TN = WTN / 16;
-  constexpr int AC = BM * (BK / 8) / 256;                 // 16-byte A chunks per thread
-  constexpr int BC = W4 ? 1 : BN * (BK / 8) / 256;        // 16-byte B chunks per thread
-  static_assert(TM >= 1 && TN >= 2 && (TN % 2) == 0 && AC >= 1 && BC >= 1, "tile");
+  constexpr int AC = BM * (BK / 8) / 256;                             // 16-byte A chunks per thread
+  constexpr int BCH = W4 ? BN * (BK / 32) : BN * (BK / 8);            // 16-byte B chunks per stage
+  constexpr int BC = (BCH + 255) / 256;                               // per thread
+  constexpr int GPS = BK / 128;                                       // INT4 groups per stage
+  static_assert(TM >= 1 && TN >= 2 && (TN % 2) == 0 && AC >= 1, "tile");
+  static_assert(!W4 || (BK % 128) == 0, "INT4 stages hold whole groups");
+  static_assert(D >= 2, "the ring holds the stage being stored plus D-1 prefetched ones");
   typedef typename Mfma<AT>::frag frag;
 
   __shared__ __attribute__((aligned(16))) AT As[BM * LDK];
   __shared__ __attribute__((aligned(16))) AT Bs[BN * LDK];
-  __shared__ float Ss[W4 ? BN : 1];
+  __shared__ float Ss[W4 ? GPS : 1][W4 ? BN : 1];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -131,82 +144,108 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       tmp[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
     }
 
-  uint4 ra[AC], rb[BC];
-  uint16_t rs = 0;
-  auto gload = [&](int k0) {
+  // Register ring.  Every load is issued unconditionally from an address clamped
+  // into the operand (branch-free code lets the compiler wait for exactly the
+  // oldest stage); chunks outside the tile are zeroed when they go to LDS.
+  uint4 ra_[D][AC], rb_[D][BC];
+  uint16_t rs_[D][W4 ? GPS : 1];
+  uint32_t okA_[D], okB_[D];
+  auto gload = [&](uint4 (&ra)[AC], uint4 (&rb)[BC], uint16_t (&rs)[W4 ? GPS : 1], uint32_t& okA, uint32_t& okB,
+                   int k0) {
+    okA = 0;
+    okB = 0;
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
+      const int c = tid + 256 * i, r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
       const int gr = m0 + r, gk = k0 + kc;
-      ra[i] = uint4{0u, 0u, 0u, 0u};
-      if (gr < M && gk < ke) ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)gr * K + gk);
+      okA |= (gr < M && gk < ke) ? (1u << i) : 0u;
+      const int grc = min(gr, M - 1), gkc = min(gk, K - 8);
+      ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)grc * K + gkc);
     }
     if constexpr (W4) {
-      const int gidx = k0 >> 7, hsel = (k0 >> 6) & 1;
-      const int c = tid;
-      rb[0] = uint4{0x88888888u, 0x88888888u, 0x88888888u, 0x88888888u};   // q = 0
-      if (c < BN * 2) {
-        const int nb = c >> 5, within = c & 31, row = within >> 1, qq = within & 1;
-        const int gn = n0 + nb * 16 + row;
-        if (gn < N) {
-          const int64_t blk = (int64_t)((n0 >> 4) + nb) * groups + gidx;
-          rb[0] = *reinterpret_cast<const uint4*>(g.Bw4 + blk * 256 + row * 16 + hsel * 8 + qq * 4);
-        }
+      // chunk c: group go of the stage, row of the tile, 16-byte quarter of the
+      // row's 64 bytes; 64 consecutive chunks are one contiguous 1 KB block
+#pragma unroll
+      for (int i = 0; i < BC; ++i) {
+        const int c = min(tid + 256 * i, BCH - 1);
+        const int go = c / (BN * 4), rem = c % (BN * 4), row = rem >> 2, qw = rem & 3;
+        const int gn = n0 + row;
+        okB |= (tid + 256 * i < BCH && gn < N && k0 + go * 128 < ke) ? (1u << i) : 0u;
+        const int gnc = min(gn, N - 1), gic = min((k0 >> 7) + go, groups - 1);
+        const int64_t blk = (int64_t)(gnc >> 4) * groups + gic;
+        rb[i] = *reinterpret_cast<const uint4*>(g.Bw4 + blk * 256 + (gnc & 15) * 16 + qw * 4);
       }
-      if (hsel == 0 && tid < BN) {
-        const int gn = n0 + tid;
-        rs = gn < N ? g.Bs[(int64_t)gidx * N + gn] : (uint16_t)0;
+#pragma unroll
+      for (int go = 0; go < GPS; ++go) {
+        const int gn = n0 + (tid < BN ? tid : 0);
+        const bool ok = tid < BN && gn < N && k0 + go * 128 < ke;
+        const int gnc = min(gn, N - 1), gic = min((k0 >> 7) + go, groups - 1);
+        rs[go] = g.Bs[(int64_t)gic * N + gnc];
+        okB |= ok ? (1u << (16 + go)) : 0u;
       }
     } else {
       const AT* B = reinterpret_cast<const AT*>(g.B);
 #pragma unroll
       for (int i = 0; i < BC; ++i) {
-        const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
+        const int c = min(tid + 256 * i, BCH - 1), r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
         const int gn = n0 + r, gk = k0 + kc;
-        rb[i] = uint4{0u, 0u, 0u, 0u};
-        if (gn < N && gk < ke) rb[i] = *reinterpret_cast<const uint4*>(B + (int64_t)gn * K + gk);
+        okB |= (tid + 256 * i < BCH && gn < N && gk < ke) ? (1u << i) : 0u;
+        const int gnc = min(gn, N - 1), gkc = min(gk, K - 8);
+        rb[i] = *reinterpret_cast<const uint4*>(B + (int64_t)gnc * K + gkc);
       }
     }
   };
-  auto lstore = [&](int k0) {
+  auto lstore = [&](const uint4 (&ra)[AC], const uint4 (&rb)[BC], const uint16_t (&rs)[W4 ? GPS : 1], uint32_t okA,
+                    uint32_t okB) {
+    // keep the masking here: without this the compiler may move it next to the
+    // loads and wait for the data as soon as it is requested
+    asm volatile("" : "+v"(okA), "+v"(okB));
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
-      const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
-      *reinterpret_cast<uint4*>(&As[r * LDK + kc]) = ra[i];
+      const int c = tid + 256 * i, r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+      const uint32_t mk = 0u - ((okA >> i) & 1u);
+      *reinterpret_cast<uint4*>(&As[r * LDK + kc]) = uint4{ra[i].x & mk, ra[i].y & mk, ra[i].z & mk, ra[i].w & mk};
     }
     if constexpr (W4) {
-      const int c = tid;
-      if (c < BN * 2) {
-        const int nb = c >> 5, within = c & 31, row = within >> 1, qq = within & 1;
-        const uint32_t ws[4] = {rb[0].x, rb[0].y, rb[0].z, rb[0].w};
-        f16* dst = reinterpret_cast<f16*>(&Bs[(nb * 16 + row) * LDK + qq * 32]);
 #pragma unroll
-        for (int wi = 0; wi < 4; ++wi) {
-          half8 h;
+      for (int i = 0; i < BC; ++i) {
+        const int c = tid + 256 * i;
+        if (c < BCH) {
+          const int go = c / (BN * 4), rem = c % (BN * 4), row = rem >> 2, qw = rem & 3;
+          // outside the tile: nibbles 8, i.e. q = 0
+          const uint32_t mk = 0u - ((okB >> i) & 1u), q0 = 0x88888888u & ~mk;
+          const uint32_t ws[4] = {(rb[i].x & mk) | q0, (rb[i].y & mk) | q0, (rb[i].z & mk) | q0, (rb[i].w & mk) | q0};
+          f16* dst = reinterpret_cast<f16*>(&Bs[row * LDK + go * 128 + qw * 32]);
 #pragma unroll
-          for (int p = 0; p < 4; ++p) {
-            const half2v t = w4_pair(ws[wi], p);
-            h[2 * p] = t[0];
-            h[2 * p + 1] = t[1];
+          for (int wi = 0; wi < 4; ++wi) {
+            half8 h;
+#pragma unroll
+            for (int p = 0; p < 4; ++p) {
+              const half2v t = w4_pair(ws[wi], p);
+              h[2 * p] = t[0];
+              h[2 * p + 1] = t[1];
+            }
+            *reinterpret_cast<half8*>(dst + wi * 8) = h;
           }
-          *reinterpret_cast<half8*>(dst + wi * 8) = h;
         }
       }
-      if (((k0 >> 6) & 1) == 0 && tid < BN) Ss[tid] = (float)__builtin_bit_cast(f16, rs);
+      if (tid < BN) {
+#pragma unroll
+        for (int go = 0; go < GPS; ++go)
+          Ss[go][tid] = ((okB >> (16 + go)) & 1u) ? (float)__builtin_bit_cast(f16, rs[go]) : 0.f;
+      }
     } else {
 #pragma unroll
       for (int i = 0; i < BC; ++i) {
-        const int c = tid + 256 * i, r = c >> 3, kc = (c & 7) * 8;
-        *reinterpret_cast<uint4*>(&Bs[r * LDK + kc]) = rb[i];
+        const int c = tid + 256 * i, r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+        const uint32_t mk = 0u - ((okB >> i) & 1u);
+        if (c < BCH)
+          *reinterpret_cast<uint4*>(&Bs[r * LDK + kc]) = uint4{rb[i].x & mk, rb[i].y & mk, rb[i].z & mk, rb[i].w & mk};
       }
     }
   };
 
-  if (kb < ke) gload(kb);
-  for (int k0 = kb; k0 < ke; k0 += BK) {
-    lstore(k0);
-    __syncthreads();
-    if (k0 + BK < ke) gload(k0 + BK);
+  auto compute = [&]() {
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
       frag a[TM], b[TN];
@@ -222,21 +261,38 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
           if constexpr (W4) tmp[i][j] = Mfma<AT>::run(a[i], b[j], tmp[i][j]);
           else acc[i][j] = Mfma<AT>::run(a[i], b[j], acc[i][j]);
         }
-    }
-    if constexpr (W4) {
-      if (((k0 >> 6) & 1) == 1) {   // end of a 128-wide group: apply its scale
+      if constexpr (W4) {
+        if ((kk & 127) == 96) {   // end of a 128-wide group: apply its scale
 #pragma unroll
-        for (int j = 0; j < TN; ++j) {
-          const float sc = Ss[wn * WTN + j * 16 + (lane & 15)];
+          for (int j = 0; j < TN; ++j) {
+            const float sc = Ss[kk >> 7][wn * WTN + j * 16 + (lane & 15)];
 #pragma unroll
-          for (int i = 0; i < TM; ++i) {
-            acc[i][j] += sc * tmp[i][j];
-            tmp[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+            for (int i = 0; i < TM; ++i) {
+              acc[i][j] += sc * tmp[i][j];
+              tmp[i][j] = floatx4{0.f, 0.f, 0.f, 0.f};
+            }
           }
         }
       }
     }
-    __syncthreads();
+  };
+
+  // Stage count padded to a multiple of D so that the loop body is straight-line
+  // (every prefetch issued unconditionally; padded stages load clamped addresses
+  // and are masked to zero), which lets the compiler wait for just the oldest stage.
+  const int nst = ((ke - kb + BK - 1) / BK + D - 1) / D * D;
+#pragma unroll
+  for (int u = 0; u < D - 1; ++u) gload(ra_[u], rb_[u], rs_[u], okA_[u], okB_[u], kb + u * BK);
+  for (int s0 = 0; s0 < nst; s0 += D) {
+    static_for<0, D>([&](auto uc) {
+      constexpr int u = decltype(uc)::value;
+      constexpr int nx = (u + D - 1) % D;
+      lstore(ra_[u], rb_[u], rs_[u], okA_[u], okB_[u]);
+      lds_barrier();
+      gload(ra_[nx], rb_[nx], rs_[nx], okA_[nx], okB_[nx], kb + (s0 + u + D - 1) * BK);
+      compute();
+      lds_barrier();
+    });
   }
 
   const int lc = lane & 15, lr = 4 * (lane >> 4);
@@ -442,45 +498,55 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
 }
 
 struct TileCfg {
-  int bm, bn, splits, kchunk;
+  int bm, bn, splits, kchunk, bk, depth;
 };
 
 constexpr int kCUs = 256;
 
-// Tile and split choice: enough workgroups to cover the 256 CUs about twice,
-// splitting K (in whole 128-wide groups) only when the tiles alone cannot.
+// Tile and split choice, from a sweep of the 2048-wide model's shapes on MI355X:
+// for M <= 128 the kernels are bound by per-workgroup latency, so small tiles
+// (BM 32/64 x BN 64, BK 128, two-stage ring) and a split of K that brings the
+// workgroup count to roughly 320 work best; larger M uses 128 x 128 tiles and
+// splits K only when the tiles cannot cover the 256 CUs.
 TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
-  if (act_dtype == DT_F32) return {64, 64, 1, g.K};
-  TileCfg t{g.M <= 32 ? 32 : (g.M <= 64 ? 64 : 128), 128, 1, g.K};
-  const int64_t mt = (g.M + t.bm - 1) / t.bm;
-  if (mt * ((g.N + 127) / 128) < kCUs) t.bn = 64;
-  if (kind == EPI_HEAD) t.bn = 128;
-  const int64_t tiles = mt * ((g.N + t.bn - 1) / t.bn);
-  const int unit = 128;
-  const int64_t units = (g.K + unit - 1) / unit;
-  if (kind != EPI_HEAD && tiles < 2 * kCUs && g.partial && units > 1 && (g.N % 32) == 0) {
-    int64_t want = (2 * kCUs + tiles - 1) / tiles;
-    want = std::min<int64_t>(want, 16);
-    want = std::min<int64_t>(want, units);
+  if (act_dtype == DT_F32) return {64, 64, 1, g.K, 16, 2};
+  TileCfg t{};
+  t.depth = 2;
+  t.splits = 1;
+  t.kchunk = g.K;
+  if (g.M <= 128 && kind != EPI_HEAD) {
+    t.bm = g.M <= 32 ? 32 : 64;
+    t.bn = 64;
+    t.bk = 128;
+  } else {
+    t.bm = g.M <= 32 ? 32 : ((g.M <= 64 || g.Bw4) ? 64 : 128);   // INT4 128 x 128 would spill
+    t.bn = 128;
+    t.bk = g.Bw4 ? 128 : 64;
+  }
+  const int64_t tiles = (int64_t)((g.M + t.bm - 1) / t.bm) * ((g.N + t.bn - 1) / t.bn);
+  const int64_t units = g.K / 128;   // splits cut K at 128-wide group boundaries
+  const int64_t target = g.M <= 128 ? 320 : 2 * kCUs;
+  if (kind != EPI_HEAD && g.partial && (g.N % 32) == 0 && (g.K % 128) == 0 && tiles < target && units >= 4) {
+    int64_t want = std::min<int64_t>(target / tiles, units / 2);
     while (want > 1 && want * g.M * g.N > g.partial_cap) --want;
     if (want > 1) {
-      const int64_t per = (units + want - 1) / want;     // units per split
-      t.kchunk = (int)(per * unit);
+      const int64_t per = (units + want - 1) / want;
+      t.kchunk = (int)(per * 128);
       t.splits = (int)((units + per - 1) / per);
     }
   }
   return t;
 }
 
-template <class AT, bool W4, int BM, int BN>
+template <class AT, bool W4, int BM, int BN, int BK, int D>
 hipError_t launch_mfma_t(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, hipStream_t s) {
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, t.splits);
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_HEAD: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_HEAD>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_HEAD: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_HEAD>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
     default: return hipErrorInvalidValue;
   }
   if (t.splits > 1) {
@@ -504,13 +570,13 @@ template <class AT, bool W4>
 hipError_t launch_mfma(const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
   const TileCfg t = pick_tile(DT_F16, g, e.kind);
   if (t.bn == 64) {
-    if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 64>(g, e, t, s);
-    if (t.bm == 64) return launch_mfma_t<AT, W4, 64, 64>(g, e, t, s);
-    return launch_mfma_t<AT, W4, 128, 64>(g, e, t, s);
+    if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 64, 128, 2>(g, e, t, s);
+    return launch_mfma_t<AT, W4, 64, 64, 128, 2>(g, e, t, s);
   }
-  if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 128>(g, e, t, s);
-  if (t.bm == 64) return launch_mfma_t<AT, W4, 64, 128>(g, e, t, s);
-  return launch_mfma_t<AT, W4, 128, 128>(g, e, t, s);
+  if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 128, 128, 2>(g, e, t, s);
+  if (t.bm == 64) return launch_mfma_t<AT, W4, 64, 128, 128, 2>(g, e, t, s);
+  if constexpr (W4) return hipErrorInvalidValue;
+  else return launch_mfma_t<AT, W4, 128, 128, 64, 2>(g, e, t, s);
 }
 
 }  // namespace

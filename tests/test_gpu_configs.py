@@ -126,11 +126,16 @@ def _oracle_lane(m, prompt, forced_row, L, steps):
 
 
 def _check_decode(m, prompts, forced, lane_L, sample, H, T, nxt, plg, steps):
+    """Hidden-state rel-L2 per lane; greedy top-1 agreement pooled over every sampled
+    token (prefill token + decode steps).  With ~1e-3 logit error a near-tie flips
+    a token ~0.3 % of the time, so the 99 % bar needs several hundred tokens to be
+    a measurement rather than a coin toss."""
     agree, total = 0, 0
     for k, i in enumerate(sample):
         h_ref, lg_ref, last_ref = _oracle_lane(m, prompts[i], forced[i], int(lane_L[i]), steps)
         r = rel_l2(H[:, k], h_ref)
-        say("  lane", i, "L", lane_L[i], "decode hidden rel", r)
+        if k < 6 or r > 5e-3:
+            say("  lane", i, "L", lane_L[i], "decode hidden rel", r)
         assert r <= bar(int(lane_L[i]))
         assert rel_l2(plg[k], last_ref) <= bar(int(lane_L[i]))
         top = oracle.greedy_argmax(lg_ref)
@@ -150,7 +155,7 @@ def test_cfg3_batched_decode_L8(d2048):
     forced = synth.tokens(0, 1100, n * steps, spec.vocab).reshape(n, steps)
     lane_L = np.full(n, 8, np.int32)
     model = load_model(w, max_lanes=n, max_pos=plen + steps, kv_arena_bytes=kv_bytes(spec, lane_L, [plen + steps] * n))
-    sample = [0, 9, 17, 31]
+    sample = list(range(n))          # top-1 is pooled over all 32 x 32 greedy tokens
     try:
         H, T, nxt, plg = _decode_lanes(model, spec, prompts, lane_L, forced, steps, sample)
     finally:
@@ -168,7 +173,7 @@ def test_cfg4_L_aware_int4_decode(d2048):
     forced = synth.tokens(0, 1100, n * steps, spec.vocab).reshape(n, steps)
     lane_L = synth.lane_loops(0, n)
     model = load_model(w, max_lanes=n, max_pos=plen + steps, kv_arena_bytes=kv_bytes(spec, lane_L, [plen + steps] * n))
-    sample = [int(np.nonzero(lane_L == L)[0][0]) for L in (2, 4, 8, 16, 32)]
+    sample = [int(i) for L in (2, 4, 8, 16, 32) for i in np.nonzero(lane_L == L)[0][:4]]
     try:
         H, T, nxt, plg = _decode_lanes(model, spec, prompts, lane_L, forced, steps, sample)
     finally:
