@@ -65,7 +65,11 @@ typedef struct {
   int32_t n_pre, n_loop, n_post;   /* n_loop = layers in the shared loop stack (>= 1) */
   float rms_eps;                   /* RMSNorm epsilon */
   float rope_base;                 /* rotary base, e.g. 10000 */
-  int32_t act_dtype;               /* GEMM operand / activation storage: F32, F16 or BF16 */
+  int32_t act_dtype;               /* GEMM operands, activations and KV cache: F32, F16 or BF16 */
+  /* Storage type of the weights the caller passes.  Each must equal act_dtype,
+   * except BF16 weights with F16 operands (converted once at load, exact for
+   * |w| >= 2^-14; the embedding table is read in its stored type) and W4G128
+   * loop blocks with F16 operands. */
   int32_t boundary_dtype;          /* embed, head, pre and post blocks: F32, F16 or BF16 */
   int32_t loop_dtype;              /* loop blocks: F32, F16, BF16 or W4G128 */
   /* W4G128 only: 1 = dequantise the loop block once at load to fp16(q * s) and run
@@ -163,23 +167,30 @@ tl_status tl_decode_step(tl_model* m, int32_t n_lanes, const int32_t* lanes_host
 
 /* n_steps greedy tokens for each of n_lanes prefilled lanes, scheduled one loop
  * iteration at a time across lanes (continuous depth batching: "Continuous Depth
- * Batching" summary page).  Lanes whose token has finished its loop iterations pass
- * through the boundary stages (post blocks, head, argmax, embedding, pre blocks)
- * and re-enter the loop pool at iteration 1 with their next token while other lanes
- * are still iterating.  Exits are known one tick ahead from the depth schedule.
+ * Batching" summary page).  A pool holds one in-flight token per lane, each at its
+ * own iteration; every tick applies the loop stack once to the whole pool and
+ * compacts out tokens that ran their last iteration.  Those wait in a boundary
+ * queue; the boundary stages (post blocks, head, greedy token, embedding, pre
+ * blocks) run on the whole queue once it holds boundary_min lanes, or when the
+ * pool has nothing left to iterate, and the lanes re-enter the pool at iteration 1
+ * with their next token.  Exits are known one tick ahead from the depth schedule,
+ * so the host plans every tick before enqueuing any work.
  *   L_req_host [n_lanes, n_steps]: requested depth of each new token; clamped
  *      exactly as in tl_decode_step.  The results equal n_steps calls of
- *      tl_decode_step with these requests; only the order of work differs.
+ *      tl_decode_step with these requests (up to fp32 summation order: batches of
+ *      different sizes may split K differently); only the order of work differs.
  *   in_tokens_dev [n_lanes, n_steps] int32 or NULL: token fed at each step (NULL:
  *      the lane's pending greedy token, i.e. free-running greedy decoding).
  *   out_tokens_dev [n_lanes, n_steps] int32: greedy token of each step.
  *   out_hidden_dev [n_lanes, n_steps, d] float32 or NULL: residual after the last
  *      block for each step.
  *   out_eff_L_host [n_lanes, n_steps] or NULL.
+ *   boundary_min: boundary-queue size that triggers the boundary stages (<= 1:
+ *      every tick).
  * Errors: as tl_decode_step. */
 tl_status tl_decode_run(tl_model* m, int32_t n_lanes, const int32_t* lanes_host, int32_t n_steps,
                         const int32_t* L_req_host, const int32_t* in_tokens_dev, int32_t* out_tokens_dev,
-                        float* out_hidden_dev, int32_t* out_eff_L_host, void* stream);
+                        float* out_hidden_dev, int32_t* out_eff_L_host, int32_t boundary_min, void* stream);
 
 /* Copy the device-resident INT4 weights of one W4G128 matrix back to canonical
  * form, unpacked by the same device routine the GEMM uses: q_host [N, K] int8 and

@@ -69,7 +69,7 @@ def lib():
                             ctypes.POINTER(_P)],
         "tl_forward": [_P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P],
         "tl_decode_step": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
-        "tl_decode_run": [_P, _I, _P, _I, _P, _P, _P, _P, _P, _P],
+        "tl_decode_run": [_P, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P],
         "tl_export_w4": [_P, _I, _I, _P, _P],
         "tl_lane_release": [_P, _I],
         "tl_memory_info": [_P, _P, _P, _P],
@@ -216,14 +216,14 @@ def tl_decode_step(model, lanes, per_lane_L, out_tokens, in_tokens=None, out_log
     return eff
 
 
-def tl_decode_run(model, lanes, L_req, out_tokens, in_tokens=None, out_hidden=None, stream=None):
+def tl_decode_run(model, lanes, L_req, out_tokens, in_tokens=None, out_hidden=None, boundary_min=1, stream=None):
     """L_req: [n_lanes, n_steps]; returns the effective depths [n_lanes, n_steps]."""
     ln = _i32(lanes)
     req = _i32(L_req)
     n, steps = req.shape
     eff = np.zeros((n, steps), np.int32)
     _check(lib().tl_decode_run(model.handle, n, _ptr(ln), steps, _ptr(req), _ptr(in_tokens), _ptr(out_tokens),
-                               _ptr(out_hidden), _ptr(eff), _stream(stream)))
+                               _ptr(out_hidden), _ptr(eff), int(boundary_min), _stream(stream)))
     return eff
 
 

@@ -433,6 +433,8 @@ tl_status upload_bytes(tl_model* m, void** dst, const void* src, size_t bytes, h
 tl_status prepare_matrix(tl_model* m, MatDev& md, const void* src0, const void* src1, int N, int K, int dtype,
                          bool w4, bool fp16_body, const int32_t* perm_dev, hipStream_t s,
                          std::vector<void*>& temps) {
+  // dtype: storage type given by the caller; dense matrices end in the operand type
+  // (m->act), converting bf16 -> fp16 on the way when the two differ.
   md.N = N;
   md.K = K;
   md.perm = const_cast<int32_t*>(perm_dev);
@@ -459,11 +461,14 @@ tl_status prepare_matrix(tl_model* m, MatDev& md, const void* src0, const void* 
     }
     return TL_OK;
   }
-  const size_t bytes = (size_t)N * K * in_esz;
+  const size_t bytes = (size_t)N * K * m->esz;
   md.dense = dev_alloc(m, bytes);
   if (!md.dense) return fail(TL_E_OOM, "dense weights");
   m->weight_bytes += bytes;
-  if (perm_dev) HIPCHK(launch_permute_rows(in_esz, canon, perm_dev, N, K, md.dense, s));
+  if (dtype == DT_BF16 && m->act == DT_F16)
+    HIPCHK(launch_permute_bf16_to_f16(static_cast<const uint16_t*>(canon), perm_dev, N, K,
+                                      static_cast<uint16_t*>(md.dense), s));
+  else if (perm_dev) HIPCHK(launch_permute_rows(in_esz, canon, perm_dev, N, K, md.dense, s));
   else HIPCHK(hipMemcpyAsync(md.dense, canon, bytes, hipMemcpyDeviceToDevice, s));
   return TL_OK;
 }
@@ -475,9 +480,15 @@ tl_status validate_config(const tl_config* c) {
   if (c->n_pre < 0 || c->n_post < 0 || c->n_loop < 1) return fail(TL_E_ARG, "block counts");
   if (c->max_L < 1 || c->max_pos < 1 || c->max_lanes < 0) return fail(TL_E_ARG, "max_L / max_pos / max_lanes");
   if (c->act_dtype < DT_F32 || c->act_dtype > DT_BF16) return fail(TL_E_UNSUPPORTED, "act_dtype");
-  if (c->boundary_dtype != c->act_dtype) return fail(TL_E_UNSUPPORTED, "boundary dtype must equal act dtype");
-  if (c->loop_dtype != c->act_dtype && !(c->loop_dtype == DT_W4G128 && c->act_dtype == DT_F16))
-    return fail(TL_E_UNSUPPORTED, "loop dtype must equal act dtype, or W4G128 with F16 operands");
+  // weights are stored in the operand type, or as bf16 with fp16 operands (converted
+  // at load), or (loop blocks) as W4G128 with fp16 operands
+  auto storable = [&](int dt) {
+    return dt == c->act_dtype || (dt == DT_BF16 && c->act_dtype == DT_F16);
+  };
+  if (!storable(c->boundary_dtype)) return fail(TL_E_UNSUPPORTED, "boundary dtype incompatible with act dtype");
+  if (!storable(c->loop_dtype) && !(c->loop_dtype == DT_W4G128 && c->act_dtype == DT_F16))
+    return fail(TL_E_UNSUPPORTED, "loop dtype must match act dtype (bf16 storage allowed with F16 operands), "
+                                  "or W4G128 with F16 operands");
   if (c->loop_fp16_body && c->loop_dtype != DT_W4G128) return fail(TL_E_ARG, "loop_fp16_body needs W4G128");
   if (c->head_dim % 2 || c->head_dim > 128) return fail(TL_E_UNSUPPORTED, "head_dim must be even and <= 128");
   if (c->d_model % 8 || c->ffn % 8) return fail(TL_E_UNSUPPORTED, "d_model and ffn must be multiples of 8");
@@ -589,8 +600,23 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   const int64_t d = c.d_model, F = c.ffn, V = c.vocab;
   const int besz = dtype_size(c.boundary_dtype);
   LTRY(upload_bytes(m, &m->embed, w->embed, (size_t)V * d * besz, s));
-  if (w->head == w->embed) m->head = m->embed;
-  else LTRY(upload_bytes(m, &m->head, w->head, (size_t)V * d * besz, s));
+  if (c.boundary_dtype != m->act) {
+    // head in the operand type (bf16 storage -> fp16); the embedding gather reads
+    // the stored type directly
+    void* hs = nullptr;
+    LTRY(upload_bytes(m, &hs, w->head, (size_t)V * d * besz, s));
+    m->head = dev_alloc(m, (size_t)V * d * m->esz);
+    if (!m->head) return cleanup_fail(fail(TL_E_OOM, "head"));
+    m->weight_bytes += (size_t)V * d * m->esz - (size_t)V * d * besz;
+    LHIP(launch_permute_bf16_to_f16(static_cast<const uint16_t*>(hs), nullptr, (int)V, (int)d,
+                                    static_cast<uint16_t*>(m->head), s));
+    LHIP(hipStreamSynchronize(s));
+    dev_free(m, hs);
+  } else if (w->head == w->embed) {
+    m->head = m->embed;
+  } else {
+    LTRY(upload_bytes(m, &m->head, w->head, (size_t)V * d * besz, s));
+  }
   void* fn = nullptr;
   LTRY(upload_bytes(m, &fn, w->final_norm, (size_t)d * 4, s));
   m->final_norm = static_cast<float*>(fn);
@@ -974,16 +1000,17 @@ tl_status tl_timing_read(tl_model* m, double* total_ms, int64_t* launches) {
 // Continuous depth batching ("Continuous Depth Batching" summary page): work is
 // scheduled one loop iteration at a time.  A pool holds one in-flight token per
 // lane, each at its own iteration; every tick applies the loop stack once to the
-// whole pool, compacts out the tokens that just ran their last iteration, and
-// sends those through the boundary stages (post blocks, final norm, head, greedy
-// token) while the others keep iterating.  A lane whose token left re-enters at
-// the next tick with its next token (embedding, pre blocks, iteration 1).  The
-// depth of every token is known when it enters (clamped request), so the whole
-// schedule, including every exit, is computed on the host first, uploaded in one
-// transfer and enqueued without waiting on the device.
+// whole pool and compacts out the tokens that just ran their last iteration.
+// Those wait in the boundary queue; the boundary stages (post blocks, final norm,
+// head, greedy token; then embedding and pre blocks of the lane's next token) run
+// on the whole queue once it holds boundary_min lanes or the pool is empty, and
+// the lanes re-enter the pool at iteration 1.  The depth of every token is known
+// when it enters (clamped request), so the whole schedule, including every exit,
+// is computed on the host first, uploaded in one transfer and enqueued without
+// waiting on the device.
 tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_steps, const int32_t* L_req,
                         const int32_t* in_tokens, int32_t* out_tokens, float* out_hidden, int32_t* out_eff_L,
-                        void* stream) {
+                        int32_t boundary_min, void* stream) {
   g_err.clear();
   if (!m || !lanes || !L_req || !out_tokens) return fail(TL_E_ARG, "NULL argument");
   const tl_config& c = m->cfg;
@@ -1006,8 +1033,8 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
   // ---- host simulation of the schedule
   struct Item { int i, j, L, pos; };
   struct Tick {
-    int n_enter = 0, n_pool = 0, n_keep = 0, n_exit = 0;
-    size_t o_erows = 0, o_elanes = 0, o_etok = 0, o_xrows = 0, o_xidx = 0, o_xlanes = 0, o_xout = 0;
+    int n_exit = 0, n_enter = 0, n_pool = 0, n_keep = 0;
+    size_t o_xrows = 0, o_xidx = 0, o_xlanes = 0, o_xout = 0, o_erows = 0, o_elanes = 0, o_etok = 0;
   };
   std::vector<int> t(n, 0), ceil_(n), len(n);
   std::vector<int32_t> eff((size_t)n * n_steps, 0);
@@ -1015,77 +1042,82 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
     ceil_[i] = m->lanes[lanes[i]].ceiling;
     len[i] = m->lanes[lanes[i]].len;
   }
-  std::vector<Item> pool;
+  std::vector<Item> pool, waiting;
   std::vector<int> enter(n);
   std::iota(enter.begin(), enter.end(), 0);
   std::vector<Tick> ticks;
   Stage st;
-  while (!enter.empty() || !pool.empty()) {
+  const int bmin = std::max(1, boundary_min);
+  bool first = true;
+  while (first || !pool.empty() || !waiting.empty()) {
     Tick tk;
-    std::vector<RowInfo> er;
-    std::vector<int32_t> el, etok;
-    for (int i : enter) {
-      etok.push_back(i * n_steps + t[i]);
-      const int L = std::min(L_req[(int64_t)i * n_steps + t[i]], ceil_[i]);
-      ceil_[i] = L;
-      eff[(size_t)i * n_steps + t[i]] = L;
-      RowInfo r{};
-      r.orig = i;
-      r.lane = lanes[i];
-      r.pos = len[i] + t[i];
-      r.depth = L;
-      r.iter = 1;
-      er.push_back(r);
-      el.push_back(lanes[i]);
-      pool.push_back(Item{i, 1, L, r.pos});
+    if (!first && !waiting.empty() && ((int)waiting.size() >= bmin || pool.empty())) {
+      // boundary stages for every waiting lane; lanes with steps left re-enter
+      std::vector<RowInfo> xr;
+      std::vector<int32_t> xi, xl, xo;
+      for (const Item& it : waiting) {
+        RowInfo r{};
+        r.orig = it.i;
+        r.lane = lanes[it.i];
+        r.pos = it.pos;
+        r.depth = it.L;
+        r.iter = it.j;
+        xr.push_back(r);
+        xi.push_back(it.i);
+        xl.push_back(lanes[it.i]);
+        xo.push_back(it.i * n_steps + t[it.i]);
+        t[it.i] += 1;
+        if (t[it.i] < n_steps) enter.push_back(it.i);
+      }
+      tk.n_exit = (int)xr.size();
+      tk.o_xrows = st.add(xr);
+      tk.o_xidx = st.add(xi);
+      tk.o_xlanes = st.add(xl);
+      tk.o_xout = st.add(xo);
+      waiting.clear();
     }
-    tk.n_enter = (int)er.size();
-    if (tk.n_enter) {
+    first = false;
+    if (!enter.empty()) {
+      std::vector<RowInfo> er;
+      std::vector<int32_t> el, etok;
+      for (int i : enter) {
+        const int L = std::min(L_req[(int64_t)i * n_steps + t[i]], ceil_[i]);
+        ceil_[i] = L;
+        eff[(size_t)i * n_steps + t[i]] = L;
+        RowInfo r{};
+        r.orig = i;
+        r.lane = lanes[i];
+        r.pos = len[i] + t[i];
+        r.depth = L;
+        r.iter = 1;
+        er.push_back(r);
+        el.push_back(lanes[i]);
+        etok.push_back(i * n_steps + t[i]);
+        pool.push_back(Item{i, 1, L, r.pos});
+      }
+      tk.n_enter = (int)er.size();
       tk.o_erows = st.add(er);
       tk.o_elanes = st.add(el);
       tk.o_etok = st.add(etok);
+      enter.clear();
     }
     tk.n_pool = (int)pool.size();
-    std::vector<Item> keep, exits;
+    std::vector<Item> keep;
     for (Item it : pool) {
       if (it.L > it.j) {
         it.j += 1;
         keep.push_back(it);
       } else {
-        exits.push_back(it);
+        waiting.push_back(it);
       }
     }
     tk.n_keep = (int)keep.size();
-    tk.n_exit = (int)exits.size();
-    std::vector<RowInfo> xr;
-    std::vector<int32_t> xi, xl, xo;
-    enter.clear();
-    for (const Item& it : exits) {
-      RowInfo r{};
-      r.orig = it.i;
-      r.lane = lanes[it.i];
-      r.pos = it.pos;
-      r.depth = it.L;
-      r.iter = it.j;
-      xr.push_back(r);
-      xi.push_back(it.i);
-      xl.push_back(lanes[it.i]);
-      xo.push_back(it.i * n_steps + t[it.i]);
-      t[it.i] += 1;
-      if (t[it.i] < n_steps) enter.push_back(it.i);
-    }
-    if (tk.n_exit) {
-      tk.o_xrows = st.add(xr);
-      tk.o_xidx = st.add(xi);
-      tk.o_xlanes = st.add(xl);
-      tk.o_xout = st.add(xo);
-    }
     pool.swap(keep);
     ticks.push_back(tk);
   }
   TRY(stage_upload(m, st, s));
 
-  // ---- enqueue every tick
+  // ---- enqueue every tick: boundary batch, entering lanes, one loop-stack pass
   auto& w = m->ws;
   const int d = c.d_model;
   KVParams kv{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
@@ -1095,41 +1127,43 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
   RowInfo* rnxt = w.rowsB;
   int npool = 0;
   for (const Tick& tk : ticks) {
+    if (tk.n_exit) {
+      const RowInfo* xr = staged<RowInfo>(m, tk.o_xrows);
+      HIPCHK(launch_gather_rows(w.hX, staged<int32_t>(m, tk.o_xidx), tk.n_exit, d, w.hE, s));
+      kv.s1 = 0;
+      for (int b = 0; b < c.n_post; ++b) {
+        kv.s0 = c.n_pre + b;
+        TRY(run_block(m, c.n_pre + c.n_loop + b, w.hE, xr, tk.n_exit, kv, s));
+      }
+      TRY(run_head(m, w.hE, nullptr, tk.n_exit, nullptr, w.tok2, staged<int32_t>(m, tk.o_xlanes), s));
+      HIPCHK(launch_scatter_i32(w.tok2, staged<int32_t>(m, tk.o_xout), tk.n_exit, out_tokens, s));
+      if (out_hidden) HIPCHK(launch_scatter_rows(w.hE, staged<int32_t>(m, tk.o_xout), tk.n_exit, d, out_hidden, s));
+    }
     if (tk.n_enter) {
       const RowInfo* er = staged<RowInfo>(m, tk.o_erows);
       float* hin = hcur + (int64_t)npool * d;
       if (in_tokens) HIPCHK(launch_gather_i32(in_tokens, staged<int32_t>(m, tk.o_etok), tk.n_enter, w.tok, s));
       else HIPCHK(launch_gather_i32(m->d_pending, staged<int32_t>(m, tk.o_elanes), tk.n_enter, w.tok, s));
       TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, w.tok, tk.n_enter, d, hin, m->d_err, c.vocab, s)));
+      kv.s1 = 0;
       for (int b = 0; b < c.n_pre; ++b) {
         kv.s0 = b;
-        kv.s1 = 0;
         TRY(run_block(m, b, hin, er, tk.n_enter, kv, s));
       }
       HIPCHK(hipMemcpyAsync(rcur + npool, er, sizeof(RowInfo) * tk.n_enter, hipMemcpyDeviceToDevice, s));
       npool += tk.n_enter;
     }
-    for (int l = 0; l < c.n_loop; ++l) {
-      kv.s0 = c.n_pre + c.n_post + l - c.n_loop;
-      kv.s1 = c.n_loop;
-      TRY(run_block(m, c.n_pre + l, hcur, rcur, npool, kv, s));
-    }
-    TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rcur, npool, 0, rnxt, w.dest, w.count, nullptr, s));
-                        HIPCHK(launch_move_rows(hcur, w.dest, rcur, npool, d, hnxt, w.hX, s)));
-    std::swap(hcur, hnxt);
-    std::swap(rcur, rnxt);
-    npool = tk.n_keep;
-    if (tk.n_exit) {
-      const RowInfo* xr = staged<RowInfo>(m, tk.o_xrows);
-      HIPCHK(launch_gather_rows(w.hX, staged<int32_t>(m, tk.o_xidx), tk.n_exit, d, w.hE, s));
-      for (int b = 0; b < c.n_post; ++b) {
-        kv.s0 = c.n_pre + b;
-        kv.s1 = 0;
-        TRY(run_block(m, c.n_pre + c.n_loop + b, w.hE, xr, tk.n_exit, kv, s));
+    if (tk.n_pool) {
+      for (int l = 0; l < c.n_loop; ++l) {
+        kv.s0 = c.n_pre + c.n_post + l - c.n_loop;
+        kv.s1 = c.n_loop;
+        TRY(run_block(m, c.n_pre + l, hcur, rcur, npool, kv, s));
       }
-      TRY(run_head(m, w.hE, nullptr, tk.n_exit, nullptr, w.tok2, staged<int32_t>(m, tk.o_xlanes), s));
-      HIPCHK(launch_scatter_i32(w.tok2, staged<int32_t>(m, tk.o_xout), tk.n_exit, out_tokens, s));
-      if (out_hidden) HIPCHK(launch_scatter_rows(w.hE, staged<int32_t>(m, tk.o_xout), tk.n_exit, d, out_hidden, s));
+      TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rcur, npool, 0, rnxt, w.dest, w.count, nullptr, s));
+                          HIPCHK(launch_move_rows(hcur, w.dest, rcur, npool, d, hnxt, w.hX, s)));
+      std::swap(hcur, hnxt);
+      std::swap(rcur, rnxt);
+      npool = tk.n_keep;
     }
   }
   for (int i = 0; i < n; ++i) {

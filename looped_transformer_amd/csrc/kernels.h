@@ -102,6 +102,9 @@ hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int3
 // Load-time kernels.  perm[n] = canonical source row of kernel row n.
 hipError_t launch_permute_rows(int elem_bytes, const void* src, const int32_t* perm, int N, int K, void* dst,
                                hipStream_t s);
+// Row permutation with bf16 -> fp16 conversion (RNE; exact for |w| >= 2^-14).
+hipError_t launch_permute_bf16_to_f16(const uint16_t* src, const int32_t* perm, int N, int K, uint16_t* dst,
+                                      hipStream_t s);
 hipError_t launch_quant_w4(const float* w, const int32_t* perm, int N, int K, uint32_t* words,
                            uint16_t* scales, hipStream_t s);
 hipError_t launch_w4_to_f16(const uint32_t* words, const uint16_t* scales, int N, int K, uint16_t* out,

@@ -174,6 +174,18 @@ __global__ __launch_bounds__(256) void permute_rows_kernel(const uint32_t* __res
   for (int c = threadIdx.x; c < words_per_row; c += 256) o[c] = s[c];
 }
 
+__global__ __launch_bounds__(256) void permute_bf16_to_f16_kernel(const uint16_t* __restrict__ src,
+                                                                 const int32_t* __restrict__ perm, int K,
+                                                                 uint16_t* __restrict__ dst) {
+  const int n = blockIdx.x;
+  const uint16_t* sr = src + (int64_t)(perm ? perm[n] : n) * K;
+  uint16_t* o = dst + (int64_t)n * K;
+  for (int c = threadIdx.x; c < K; c += 256) {
+    const float v = (float)__builtin_bit_cast(bf16, sr[c]);
+    o[c] = __builtin_bit_cast(uint16_t, (f16)v);
+  }
+}
+
 // One wave per (kernel row n, group): s = fp16(max|w| / 7), q = clamp(rint(w / s), -7, 7).
 __global__ __launch_bounds__(256) void quant_w4_kernel(const float* __restrict__ w, const int32_t* __restrict__ perm,
                                                       int N, int K, uint32_t* __restrict__ words,
@@ -322,6 +334,12 @@ hipError_t launch_permute_rows(int elem_bytes, const void* src, const int32_t* p
   if ((int64_t)K * elem_bytes % 4 != 0) return hipErrorInvalidValue;
   const int wpr = (int)((int64_t)K * elem_bytes / 4);
   hipLaunchKernelGGL(permute_rows_kernel, dim3(N), dim3(256), 0, s, (const uint32_t*)src, perm, wpr, (uint32_t*)dst);
+  return hipGetLastError();
+}
+
+hipError_t launch_permute_bf16_to_f16(const uint16_t* src, const int32_t* perm, int N, int K, uint16_t* dst,
+                                      hipStream_t s) {
+  hipLaunchKernelGGL(permute_bf16_to_f16_kernel, dim3(N), dim3(256), 0, s, src, perm, K, dst);
   return hipGetLastError();
 }
 

@@ -134,6 +134,7 @@ class ModelSpec:
     rms_eps: float = 1e-5
     rope_base: float = 10000.0
     std: float = 0.02
+    act: str = ""        # GEMM operand type on the GPU path ("" = boundary_dtype)
 
     @property
     def n_blocks(self) -> int:
@@ -149,7 +150,7 @@ class ModelSpec:
     @property
     def act_dtype(self) -> str:
         """Element type of the GEMM operands on the GPU path."""
-        return self.boundary_dtype
+        return self.act or self.boundary_dtype
 
     def block_params(self) -> int:
         d, f = self.d_model, self.ffn
@@ -161,7 +162,7 @@ SPECS = {
     2: ModelSpec("d2048-int4loop", 50304, 2048, 16, 128, 5632, 1, 1, 0, "f16", "w4g128"),
     3: ModelSpec("d2048-fp16body", 50304, 2048, 16, 128, 5632, 1, 1, 0, "f16", "f16body"),
     4: ModelSpec("d2048-int4loop", 50304, 2048, 16, 128, 5632, 1, 1, 0, "f16", "w4g128"),
-    5: ModelSpec("d5280-bf16-stack4", 65536, 5280, 55, 96, 17920, 2, 4, 2, "bf16", "bf16"),
+    5: ModelSpec("d5280-bf16-stack4", 65536, 5280, 55, 96, 17920, 2, 4, 2, "bf16", "bf16", act="f16"),
 }
 
 

@@ -29,7 +29,8 @@ def make_config(spec: synth.ModelSpec, max_lanes: int = 0, max_L: int = 32, max_
     c.vocab, c.d_model, c.n_heads, c.head_dim, c.ffn = spec.vocab, spec.d_model, spec.n_heads, spec.head_dim, spec.ffn
     c.n_pre, c.n_loop, c.n_post = spec.n_pre, spec.n_loop, spec.n_post
     c.rms_eps, c.rope_base = spec.rms_eps, spec.rope_base
-    c.act_dtype = c.boundary_dtype = DT[spec.boundary_dtype]
+    c.boundary_dtype = DT[spec.boundary_dtype]
+    c.act_dtype = DT[spec.act_dtype]
     if spec.loop_dtype in ("w4g128", "f16body"):
         c.loop_dtype = tl.TL_DT_W4G128
         c.loop_fp16_body = 1 if spec.loop_dtype == "f16body" else 0
@@ -46,7 +47,7 @@ def kv_bytes(spec: synth.ModelSpec, ceilings, caps) -> int:
         slots = spec.n_pre + spec.n_post + spec.n_loop * int(L)
         e = slots * 2 * spec.d_model * int(cap)
         tot += (e + 63) // 64 * 64
-    return tot * ESZ[spec.boundary_dtype] + (1 << 20)
+    return tot * ESZ[spec.act_dtype] + (1 << 20)
 
 
 def load_model(w: synth.Weights, **cfg_kw) -> tl.Model:

@@ -181,8 +181,8 @@ def test_cfg4_L_aware_int4_decode(d2048):
     _check_decode(m, prompts, forced, lane_L, sample, H, T, nxt, plg, steps)
 
 
-@pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack"])
-def test_continuous_depth_equals_lockstep_and_oracle(name):
+@pytest.mark.parametrize("name,bmin", [("tiny-w4", 1), ("tiny-bf16-stack", 1), ("tiny-bf16-stack", 4)])
+def test_continuous_depth_equals_lockstep_and_oracle(name, bmin):
     """tl_decode_run (scheduled per loop iteration) vs tl_decode_step per token vs the oracle."""
     from tests.test_gpu_parity import TINY
     spec = TINY[name]
@@ -205,7 +205,7 @@ def test_continuous_depth_equals_lockstep_and_oracle(name):
             tl.tl_forward(model, cu, toks, seq_L=L1, lanes=lanes, max_new_tokens=steps)
         run_tok = torch.empty(n, steps, dtype=torch.int32, device="cuda")
         run_h = torch.empty(n, steps, spec.d_model, dtype=torch.float32, device="cuda")
-        eff_run = tl.tl_decode_run(model, A, reqs, run_tok, out_hidden=run_h)
+        eff_run = tl.tl_decode_run(model, A, reqs, run_tok, out_hidden=run_h, boundary_min=bmin)
         out = torch.empty(n, dtype=torch.int32, device="cuda")
         hs = torch.empty(n, spec.d_model, dtype=torch.float32, device="cuda")
         step_tok, step_h, eff_step = [], [], []
