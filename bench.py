@@ -99,7 +99,9 @@ def main():
     toks = torch.tensor(synth.tokens(0, synth.STREAM_TOKENS, 128, spec.vocab), dtype=torch.int32, device="cuda")
     cu = np.array([0, 128], np.int32)
     hid = torch.empty(128, spec.d_model, dtype=torch.float32, device="cuda")
-    stream = torch.cuda.current_stream()
+    torch.cuda.synchronize()
+    # a dedicated stream: repeated identical scoring calls replay a captured HIP graph
+    stream = torch.cuda.Stream()
 
     def step():
         tl.tl_forward(model, cu, toks, L=8, out_hidden=hid, stream=stream)
@@ -111,6 +113,7 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
+    stream.synchronize()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms = el / args.steps * 1e3
@@ -120,9 +123,11 @@ def main():
         return
 
     # per-kernel-class HIP-event timing over a second timed region of the same steps
+    # (eager launches: event pairs are recorded on the forward's stream)
     tl.tl_timing_enable(model, True)
     for _ in range(args.steps):
         step()
+    stream.synchronize()
     torch.cuda.synchronize()
     cls = tl.tl_timing_read(model)
     tl.tl_timing_enable(model, False)

@@ -80,7 +80,16 @@ struct Stage {
 };
 
 template <class T> T* staged(tl_model* m, size_t off) {
-  return reinterpret_cast<T*>(static_cast<uint8_t*>(m->stage_dev) + off);
+  void* base = m->stage_override ? m->stage_override : m->stage_dev;
+  return reinterpret_cast<T*>(static_cast<uint8_t*>(base) + off);
+}
+
+void drop_graphs(tl_model* m) {
+  for (auto& g : m->graphs) {
+    if (g.exec) (void)hipGraphExecDestroy(g.exec);
+    dev_free(m, g.stage);
+  }
+  m->graphs.clear();
 }
 
 tl_status stage_upload(tl_model* m, const Stage& st, hipStream_t s) {
@@ -120,6 +129,7 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
   const int64_t KS = std::max(w.kv_scratch_elems, kv_scratch);
   HIPCHK(hipStreamSynchronize(s));
   if (m->last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
+  drop_graphs(m);
   void* olds[] = {w.hA, w.hB, w.hX, w.hE, w.x16, w.q16, w.o16, w.u16, w.xh, w.rowsA, w.rowsB,
                   w.dest, w.count, w.tok, w.tok2, w.part_v, w.part_i, w.kv_scratch, w.splitk};
   for (void* p : olds) dev_free(m, p);
@@ -220,14 +230,20 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
   return TL_OK;
 }
 
+// One pre-norm block on n rows.  x_ready: the caller's previous block already left
+// this block's normalised input in ws.x16.  next_norm: gain of the norm that
+// follows on the same rows (the next block's first norm), fused into the down
+// projection's residual update when possible (then ws.x16 holds its output).
 tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, const KVParams& kv, hipStream_t s,
-                    const AttnTile* tiles = nullptr, int n_tiles = 0) {
+                    const AttnTile* tiles = nullptr, int n_tiles = 0, bool x_ready = false,
+                    const float* next_norm = nullptr) {
   if (n <= 0) return TL_OK;
   const tl_config& c = m->cfg;
   const BlockDev& B = m->blocks[b];
   auto& w = m->ws;
   const int tb = B.kind == 1 ? TL_T_GEMM_QKV_LOOP : TL_T_GEMM_QKV_BOUNDARY;
-  TIMED(TL_T_RMSNORM, HIPCHK(launch_rmsnorm(m->act, h, B.norm1, nullptr, n, c.d_model, c.rms_eps, w.x16, s)));
+  if (!x_ready)
+    TIMED(TL_T_RMSNORM, HIPCHK(launch_rmsnorm(m->act, h, B.norm1, nullptr, n, c.d_model, c.rms_eps, w.x16, s)));
   GemmEpi e{};
   e.kind = EPI_QKV;
   e.q_out = w.q16;
@@ -245,13 +261,16 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   r.kind = EPI_RESID;
   r.h = h;
   r.ldh = c.d_model;
+  r.norm_g = B.norm2;
+  r.norm_out = w.x16;
+  r.norm_eps = c.rms_eps;
   TIMED(tb + 1, TRY(gemm(m, w.o16, n, B.o, r, s)));
-  TIMED(TL_T_RMSNORM, HIPCHK(launch_rmsnorm(m->act, h, B.norm2, nullptr, n, c.d_model, c.rms_eps, w.x16, s)));
   GemmEpi sw{};
   sw.kind = EPI_SWIGLU;
   sw.u_out = w.u16;
   sw.F = c.ffn;
   TIMED(tb + 2, TRY(gemm(m, w.x16, n, B.gu, sw, s)));
+  r.norm_g = next_norm;
   TIMED(tb + 3, TRY(gemm(m, w.u16, n, B.down, r, s)));
   return TL_OK;
 }
@@ -284,9 +303,15 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   kv.s1 = 0;
   const AttnTile* t0 = tiled ? p.tiles[0] : nullptr;
   const int nt0 = tiled ? p.n_tiles[0] : 0;
+  const int Lmax = (int)p.n_active.size();
+  // norm gain of the first block after pre block b / loop layer l on the same rows
+  auto loop_first = [&]() { return m->blocks[c.n_pre].norm1; };
+  bool x_ready = false;
   for (int b = 0; b < c.n_pre; ++b) {
     kv.s0 = p.scoring ? 0 : b;
-    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0));
+    const float* nn = b + 1 < c.n_pre ? m->blocks[b + 1].norm1 : (Lmax > 0 ? loop_first() : nullptr);
+    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn));
+    x_ready = nn != nullptr;
   }
   float* h = w.hA;
   float* hn = w.hB;
@@ -295,16 +320,19 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   int flip = 0;
   int64_t log_off = 0;
   bool moved = true;
-  const int Lmax = (int)p.n_active.size();
   for (int j = 1; j <= Lmax; ++j) {
     const int nj = p.n_active[j - 1];
     if (p.log && moved) HIPCHK(launch_write_orig(rows, nj, p.log + log_off, s));
+    const int next = j < Lmax ? p.n_active[j] : 0;
+    const bool leaving = next < nj;
     for (int l = 0; l < c.n_loop; ++l) {
       kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + (j - 1) * c.n_loop + l;
-      TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr, tiled ? p.n_tiles[j - 1] : 0));
+      const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1 : (leaving ? nullptr : loop_first());
+      TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
+                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn));
+      x_ready = nn != nullptr;
     }
-    const int next = j < Lmax ? p.n_active[j] : 0;
-    moved = next < nj;
+    moved = leaving;
     if (moved) {
       RowInfo* rout = rbuf[flip];
       int32_t* logn = p.log ? p.log + log_off + nj : nullptr;
@@ -319,9 +347,12 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     }
     log_off += nj;
   }
+  x_ready = false;
   for (int b = 0; b < c.n_post; ++b) {
     kv.s0 = p.scoring ? 0 : c.n_pre + b;
-    TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s, t0, nt0));
+    const float* nn = b + 1 < c.n_post ? m->blocks[c.n_pre + c.n_loop + b + 1].norm1 : nullptr;
+    TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn));
+    x_ready = nn != nullptr;
   }
   return TL_OK;
 }
@@ -701,6 +732,7 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
 void tl_free(tl_model* m) {
   if (!m) return;
   (void)hipDeviceSynchronize();
+  drop_graphs(m);
   std::vector<void*> ps;
   for (auto& kv : m->owned) ps.push_back(kv.first);
   for (void* p : ps) dev_free(m, p);
@@ -792,6 +824,23 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   const int n_out = want_head ? n_seqs : 0;
   TRY(ensure_ws(m, T, n_out, lanes ? 0 : (int64_t)T * 2 * c.d_model, s));
 
+  // scoring passes on a stream are replayed from a captured graph when repeated
+  const bool graphable = !lanes && s != nullptr && !m->timing;
+  std::vector<int64_t> key;
+  if (graphable) {
+    key = {n_seqs, (int64_t)(intptr_t)tokens, (int64_t)(intptr_t)out_hidden, (int64_t)(intptr_t)out_logits,
+           (int64_t)(intptr_t)out_next, (int64_t)(intptr_t)out_log, (int64_t)(intptr_t)s};
+    for (int i = 0; i <= n_seqs; ++i) key.push_back(cu[i]);
+    for (int i = 0; i < n_seqs; ++i) key.push_back(Ls[i]);
+    for (auto& g : m->graphs) {
+      if (g.key == key) {
+        g.last_use = ++m->graph_clock;
+        HIPCHK(hipGraphLaunch(g.exec, s));
+        return TL_OK;
+      }
+    }
+  }
+
   std::vector<RowInfo> rows(T);
   std::vector<int> depth(T);
   std::vector<int32_t> last(n_seqs), lane_ids(n_seqs);
@@ -843,7 +892,26 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   const size_t o_rows = st.add(rows), o_last = st.add(last), o_lanes = st.add(lane_ids);
   const size_t o_soff = st.add(soff), o_scap = st.add(scap);
   const size_t o_loff = st.add(loff), o_lcap = st.add(lcap);
-  TRY(stage_upload(m, st, s));
+  tl::GraphEntry ge;
+  if (graphable) {
+    // descriptors in a buffer the graph owns, then capture the pass
+    ge.stage = dev_alloc(m, st.buf.size());
+    if (!ge.stage) return fail(TL_E_OOM, "graph descriptors");
+    hipError_t e1 = hipMemcpy(ge.stage, st.buf.data(), st.buf.size(), hipMemcpyHostToDevice);
+    if (e1 != hipSuccess) {
+      dev_free(m, ge.stage);
+      return fail(TL_E_HIP, "graph descriptors: %s", hipGetErrorString(e1));
+    }
+    m->stage_override = ge.stage;
+    e1 = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
+    if (e1 != hipSuccess) {
+      m->stage_override = nullptr;
+      dev_free(m, ge.stage);
+      return fail(TL_E_HIP, "stream capture: %s", hipGetErrorString(e1));
+    }
+  } else {
+    TRY(stage_upload(m, st, s));
+  }
   if (lanes) {
     HIPCHK(hipMemcpyAsync(m->d_lane_off, staged<int64_t>(m, o_loff), loff.size() * 8, hipMemcpyDeviceToDevice, s));
     HIPCHK(hipMemcpyAsync(m->d_lane_cap, staged<int32_t>(m, o_lcap), lcap.size() * 4, hipMemcpyDeviceToDevice, s));
@@ -875,11 +943,37 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   }
   p.final_h = out_hidden ? out_hidden : m->ws.hX;
   p.log = out_log;
-  TRY(run_pass(m, p, s));
-  if (want_head)
-    TRY(run_head(m, p.final_h, staged<int32_t>(m, o_last), n_seqs, out_logits, out_next,
-                 lanes ? staged<int32_t>(m, o_lanes) : nullptr, s));
-  return TL_OK;
+  tl_status stt = run_pass(m, p, s);
+  if (stt == TL_OK && want_head)
+    stt = run_head(m, p.final_h, staged<int32_t>(m, o_last), n_seqs, out_logits, out_next,
+                   lanes ? staged<int32_t>(m, o_lanes) : nullptr, s);
+  if (graphable) {
+    m->stage_override = nullptr;
+    hipGraph_t graph = nullptr;
+    const hipError_t e2 = hipStreamEndCapture(s, &graph);
+    hipError_t e3 = hipSuccess;
+    if (stt == TL_OK && e2 == hipSuccess) e3 = hipGraphInstantiate(&ge.exec, graph, nullptr, nullptr, 0);
+    if (graph) (void)hipGraphDestroy(graph);
+    if (stt != TL_OK || e2 != hipSuccess || e3 != hipSuccess) {
+      if (ge.exec) (void)hipGraphExecDestroy(ge.exec);
+      dev_free(m, ge.stage);
+      if (stt != TL_OK) return stt;
+      return fail(TL_E_HIP, "graph capture: %s", hipGetErrorString(e2 != hipSuccess ? e2 : e3));
+    }
+    HIPCHK(hipGraphLaunch(ge.exec, s));
+    ge.key = key;
+    ge.last_use = ++m->graph_clock;
+    if (m->graphs.size() >= 4) {
+      auto old = std::min_element(m->graphs.begin(), m->graphs.end(),
+                                  [](const tl::GraphEntry& a, const tl::GraphEntry& b) { return a.last_use < b.last_use; });
+      HIPCHK(hipStreamSynchronize(s));
+      (void)hipGraphExecDestroy(old->exec);
+      dev_free(m, old->stage);
+      m->graphs.erase(old);
+    }
+    m->graphs.push_back(ge);
+  }
+  return stt;
 }
 
 tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int32_t* req_L,

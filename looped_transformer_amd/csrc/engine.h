@@ -52,6 +52,15 @@ struct BlockDev {
   bool is_w4 = false;
 };
 
+// A captured scoring pass, replayed when tl_forward is called again with the same
+// arguments (same pointers, lengths and depths) on the same stream.
+struct GraphEntry {
+  std::vector<int64_t> key;
+  hipGraphExec_t exec = nullptr;
+  void* stage = nullptr;     // device copy of the call's descriptors (owned)
+  uint64_t last_use = 0;
+};
+
 struct Workspace {
   int rows = 0, outs = 0;
   int64_t kv_scratch_elems = 0;
@@ -103,6 +112,10 @@ struct tl_model {
   size_t stage_bytes = 0;
   hipEvent_t stage_done = nullptr;
   hipStream_t last_stream = nullptr;
+  // captured scoring passes; a workspace reallocation invalidates them
+  std::vector<tl::GraphEntry> graphs;
+  uint64_t graph_clock = 0;
+  void* stage_override = nullptr;      // descriptor base while capturing a graph
   // kernel-class timing (measurement only)
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;

@@ -497,6 +497,54 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
   }
 }
 
+// Split-K residual reduction fused with the next RMSNorm: one workgroup per row
+// adds the splits in order onto the fp32 residual, then normalises the new row
+// (fp32 statistics) into the next GEMM's operand type.
+template <class AT, int NPT>
+__global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, GemmEpi e, int S) {
+  constexpr int SMAX = 8;
+  const int row = blockIdx.x, N = g.N, M = g.M;
+  float* hr = e.h + (int64_t)row * e.ldh;
+  // every split's value is requested before any is used (branch-free, clamped
+  // indices), then the splits are added in order onto the residual
+  float p[SMAX][NPT];
+#pragma unroll
+  for (int z = 0; z < SMAX; ++z)
+#pragma unroll
+    for (int u = 0; u < NPT; ++u) {
+      const int c = min(threadIdx.x + 256 * u, N - 1);
+      p[z][u] = g.partial[((int64_t)min(z, S - 1) * M + row) * N + c];
+    }
+  float v[NPT];
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int c = threadIdx.x + 256 * u;
+    float a = 0.f;
+#pragma unroll
+    for (int z = 0; z < SMAX; ++z)
+      if (z < S) a += p[z][u];
+    v[u] = 0.f;
+    if (c < N) {
+      v[u] = hr[c] + a;
+      hr[c] = v[u];
+      ss = fmaf(v[u], v[u], ss);
+    }
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  const float tot = red[0] + red[1] + red[2] + red[3];
+  const float inv = 1.0f / sqrtf(tot / (float)N + e.norm_eps);
+  AT* o = reinterpret_cast<AT*>(e.norm_out) + (int64_t)row * N;
+#pragma unroll
+  for (int u = 0; u < NPT; ++u) {
+    const int c = threadIdx.x + 256 * u;
+    if (c < N) o[c] = from_f32<AT>(v[u] * inv * e.norm_g[c]);
+  }
+}
+
 struct TileCfg {
   int bm, bn, splits, kchunk, bk, depth;
 };
@@ -527,7 +575,7 @@ TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
   const int64_t units = g.K / 128;   // splits cut K at 128-wide group boundaries
   const int64_t target = g.M <= 128 ? 320 : 2 * kCUs;
   if (kind != EPI_HEAD && g.partial && (g.N % 32) == 0 && (g.K % 128) == 0 && tiles < target && units >= 4) {
-    int64_t want = std::min<int64_t>(target / tiles, units / 2);
+    int64_t want = std::min<int64_t>(std::min<int64_t>(target / tiles, units / 2), 8);
     while (want > 1 && want * g.M * g.N > g.partial_cap) --want;
     if (want > 1) {
       const int64_t per = (units + want - 1) / want;
@@ -548,6 +596,15 @@ hipError_t launch_mfma_t(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, 
     case EPI_HEAD: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_HEAD>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
     case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
     default: return hipErrorInvalidValue;
+  }
+  if (t.splits > 1 && e.kind == EPI_RESID && e.norm_g) {
+    hipError_t err = hipGetLastError();
+    if (err != hipSuccess) return err;
+    const int npt = (g.N + 255) / 256;
+    if (npt <= 8) hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, 8>), dim3(g.M), dim3(256), 0, s, g, e, t.splits);
+    else if (npt <= 24) hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, 24>), dim3(g.M), dim3(256), 0, s, g, e, t.splits);
+    else return hipErrorInvalidValue;   // unreachable: launch_gemm only fuses rows of <= 24 * 256
+    return hipGetLastError();
   }
   if (t.splits > 1) {
     hipError_t err = hipGetLastError();
@@ -590,8 +647,22 @@ int gemm_head_tiles(int act_dtype, int M, int N) {
   return (N + t.bn - 1) / t.bn;
 }
 
+static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s);
+
+// Residual GEMM with a following RMSNorm: fused into the split-K reduction when K
+// is split, else the epilogue adds into h and a separate RMSNorm kernel runs.
 hipError_t launch_gemm(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  hipError_t err = launch_gemm_core(act_dtype, g, e, s);
+  if (err != hipSuccess || e.kind != EPI_RESID || !e.norm_g) return err;
+  if (act_dtype != DT_F32 && (g.N + 255) / 256 <= 24) {
+    const TileCfg t = pick_tile(act_dtype, g, e.kind);
+    if (t.splits > 1) return hipSuccess;   // normalised by the fused reduction
+  }
+  return launch_rmsnorm(act_dtype, e.h, e.norm_g, nullptr, g.M, g.N, e.norm_eps, e.norm_out, s);
+}
+
+static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
   if (act_dtype == DT_F32) {
     dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
     switch (e.kind) {

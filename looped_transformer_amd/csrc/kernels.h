@@ -44,9 +44,13 @@ struct GemmEpi {
   const float* rope_cos;   // [max_pos, dh/2]
   const float* rope_sin;
   int32_t d, H, dh;
-  // EPI_RESID: h[r, c] += acc
+  // EPI_RESID: h[r, c] += acc; then, if norm_g is set, norm_out = RMSNorm(h) * norm_g
+  // in the operand type (the next GEMM's input), fused with the split-K reduction
   float* h;
   int32_t ldh;
+  const float* norm_g;
+  void* norm_out;
+  float norm_eps;
   // EPI_SWIGLU: u[r, n] = silu(gate) * up
   void* u_out;
   int32_t F;

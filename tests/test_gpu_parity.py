@@ -186,3 +186,39 @@ def test_cfg2_forward_full_size():
     r = rel_l2(hid, ref_h)
     say("cfg2 rel", r)
     assert r <= 1e-2
+
+
+@pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack"])
+def test_graph_replay_matches_eager(name):
+    """Repeated scoring calls on a stream replay a captured graph; every replay,
+    with eager work and synchronisations between them, equals the eager pass."""
+    spec = TINY[name]
+    w = synth.make_weights(spec, seed=21)
+    seqs = [synth.tokens(21, 6000 + i, n, spec.vocab) for i, n in enumerate([40, 7, 66])]
+    Ls = [3, 1, 5]
+    model = load_model(w, max_pos=128, max_L=8)
+    try:
+        toks = torch.tensor(np.concatenate(seqs), dtype=torch.int32, device="cuda")
+        cu = np.cumsum([0] + [len(s) for s in seqs]).astype(np.int32)
+        T = int(cu[-1])
+        ref = torch.empty(T, spec.d_model, dtype=torch.float32, device="cuda")
+        ref_next = torch.empty(3, dtype=torch.int32, device="cuda")
+        tl.tl_forward(model, cu, toks, seq_L=Ls, out_hidden=ref, out_next=ref_next, stream=0)   # eager
+        torch.cuda.synchronize()
+        side = torch.cuda.Stream()
+        hid = torch.empty(T, spec.d_model, dtype=torch.float32, device="cuda")
+        nxt = torch.empty(3, dtype=torch.int32, device="cuda")
+        other = torch.empty(T, spec.d_model, dtype=torch.float32, device="cuda")
+        for rep in range(4):
+            hid.fill_(float("nan"))
+            nxt.fill_(-1)
+            torch.cuda.synchronize()
+            tl.tl_forward(model, cu, toks, seq_L=Ls, out_hidden=hid, out_next=nxt, stream=side)
+            side.synchronize()
+            assert torch.equal(hid, ref), rep
+            assert torch.equal(nxt, ref_next), rep
+            # eager work on the same model between replays
+            tl.tl_forward(model, cu, toks, seq_L=[1, 1, 1], out_hidden=other, stream=0)
+            torch.cuda.synchronize()
+    finally:
+        tl.tl_free(model)
