@@ -36,6 +36,9 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
+    ap.add_argument("--eager", action="store_true", help="launch kernels one by one (no graph replay)")
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the steps, copy 256 MiB once with a plain device copy (counter calibration)")
     return ap.parse_args()
 
 
@@ -101,7 +104,7 @@ def main():
     hid = torch.empty(128, spec.d_model, dtype=torch.float32, device="cuda")
     torch.cuda.synchronize()
     # a dedicated stream: repeated identical scoring calls replay a captured HIP graph
-    stream = torch.cuda.Stream()
+    stream = 0 if args.eager else torch.cuda.Stream()
 
     def step():
         tl.tl_forward(model, cu, toks, L=8, out_hidden=hid, stream=stream)
@@ -113,13 +116,19 @@ def main():
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
-    stream.synchronize()
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
     ms = el / args.steps * 1e3
     value = 128 * 8 / (ms / 1e3)
     if args.profile_only:
         log("ms/step %.4f" % ms)
+        if args.calibrate_copy:
+            src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+            dst = torch.empty_like(src)
+            torch.cuda.synchronize()
+            dst.copy_(src)
+            torch.cuda.synchronize()
+            log("copied %d bytes" % (src.numel() * 4))
         return
 
     # per-kernel-class HIP-event timing over a second timed region of the same steps
@@ -127,7 +136,6 @@ def main():
     tl.tl_timing_enable(model, True)
     for _ in range(args.steps):
         step()
-    stream.synchronize()
     torch.cuda.synchronize()
     cls = tl.tl_timing_read(model)
     tl.tl_timing_enable(model, False)
