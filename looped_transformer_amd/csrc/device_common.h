@@ -9,6 +9,8 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef _Float16 half2v __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+// native 16-byte vector (HIP's uint4 is a struct whose copies can block register promotion)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 #include "kernels.h"
 
@@ -51,6 +53,17 @@ __device__ __forceinline__ T* kv_ptr(const KVParams& kv, const RowInfo& ri, int 
 // offset-binary nibbles (q + 8); element 2i sits in bits [4i, 4i+4), element 2i+1
 // in bits [16+4i, 16+4i+4).  ((w >> 4i) & 0x000F000F) | 0x64006400 is then the
 // fp16 pair (1024 + q_2i + 8, 1024 + q_2i+1 + 8); subtracting 1032 gives q exactly.
+//
+// Words are ordered as 32x32x16 MFMA B fragments: one 2 KB block per (32 output
+// rows, 128-wide group), made of two 1 KB halves; half hb holds, for each lane
+// L = (n mod 32) + 32 h, four words t = 0..3 covering k steps j = 4 hb + t, i.e.
+// k = 16 j + 8 h + (0..7) of the group.  A wave thus reads a fragment set for four
+// k steps as one contiguous 1 KB load.  Needs N a multiple of 32.
+__host__ __device__ __forceinline__ int64_t w4_word_offset(int n, int k8, int groups) {
+  const int gi = k8 >> 4, kk = k8 & 15, j = kk >> 1, h = kk & 1;
+  const int lane = (n & 31) + 32 * h;
+  return ((((int64_t)(n >> 5) * groups + gi) * 2 + (j >> 2)) * 64 + lane) * 4 + (j & 3);
+}
 __device__ __forceinline__ half2v w4_pair(uint32_t w, int i) {
   uint32_t b = ((w >> (4 * i)) & 0x000F000Fu) | 0x64006400u;
   half2v h = __builtin_bit_cast(half2v, b);

@@ -163,17 +163,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)grc * K + gkc);
     }
     if constexpr (W4) {
-      // chunk c: group go of the stage, row of the tile, 16-byte quarter of the
-      // row's 64 bytes; 64 consecutive chunks are one contiguous 1 KB block
+      // chunk c: group go of the stage, 32-row block of the tile, half hb of the
+      // 2 KB fragment block, lane (row mod 32, k half h): 64 consecutive chunks are
+      // one contiguous 1 KB half (four words: k steps 4 hb .. 4 hb + 3)
 #pragma unroll
       for (int i = 0; i < BC; ++i) {
         const int c = min(tid + 256 * i, BCH - 1);
-        const int go = c / (BN * 4), rem = c % (BN * 4), row = rem >> 2, qw = rem & 3;
+        const int go = c / (BN * 4), rem = c % (BN * 4);
+        const int row = (rem >> 7) * 32 + (rem & 31), hb = (rem >> 6) & 1, h = (rem >> 5) & 1;
         const int gn = n0 + row;
         okB |= (tid + 256 * i < BCH && gn < N && k0 + go * 128 < ke) ? (1u << i) : 0u;
         const int gnc = min(gn, N - 1), gic = min((k0 >> 7) + go, groups - 1);
-        const int64_t blk = (int64_t)(gnc >> 4) * groups + gic;
-        rb[i] = *reinterpret_cast<const uint4*>(g.Bw4 + blk * 256 + (gnc & 15) * 16 + qw * 4);
+        rb[i] = *reinterpret_cast<const uint4*>(g.Bw4 + w4_word_offset(gnc, gic * 16 + 8 * hb + h, groups));
       }
 #pragma unroll
       for (int go = 0; go < GPS; ++go) {
@@ -211,11 +212,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       for (int i = 0; i < BC; ++i) {
         const int c = tid + 256 * i;
         if (c < BCH) {
-          const int go = c / (BN * 4), rem = c % (BN * 4), row = rem >> 2, qw = rem & 3;
+          const int go = c / (BN * 4), rem = c % (BN * 4);
+          const int row = (rem >> 7) * 32 + (rem & 31), hb = (rem >> 6) & 1, hk = (rem >> 5) & 1;
           // outside the tile: nibbles 8, i.e. q = 0
           const uint32_t mk = 0u - ((okB >> i) & 1u), q0 = 0x88888888u & ~mk;
           const uint32_t ws[4] = {(rb[i].x & mk) | q0, (rb[i].y & mk) | q0, (rb[i].z & mk) | q0, (rb[i].w & mk) | q0};
-          f16* dst = reinterpret_cast<f16*>(&Bs[row * LDK + go * 128 + qw * 32]);
+          // word wi: k = 16 (4 hb + wi) + 8 hk + (0..7) of the group
+          f16* dst = reinterpret_cast<f16*>(&Bs[row * LDK + go * 128 + 64 * hb + 8 * hk]);
 #pragma unroll
           for (int wi = 0; wi < 4; ++wi) {
             half8 h;
@@ -225,7 +228,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
               h[2 * p] = t[0];
               h[2 * p + 1] = t[1];
             }
-            *reinterpret_cast<half8*>(dst + wi * 8) = h;
+            *reinterpret_cast<half8*>(dst + wi * 16) = h;
           }
         }
       }
@@ -383,6 +386,192 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   }
 }
 
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+
+__device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_f16(a, b, c, 0, 0, 0);
+}
+
+// Small-M GEMM with INT4 weights (M <= BM <= 64 rows per workgroup).
+//
+// At decode sizes the product is bound by fixed costs and by how often each CU
+// re-reads the activations, so one workgroup takes every row of the pass and a
+// BN = 128 * WNB column tile, and K is split across workgroups (blockIdx.z) to
+// fill the CUs.  Per 128-wide K stage:
+//  * A (BM x 128 fp16) goes global -> registers -> LDS once per workgroup, rows of
+//    16 chunks of 16 bytes with the chunk slot XOR-ed by (row mod 16), so both the
+//    row-wise stores and the 32-row fragment reads hit 16 distinct slots;
+//  * each of the four waves owns all BM rows and WNB 32-column blocks; its INT4
+//    fragments come straight from global memory in MFMA order (two coalesced
+//    1 KB loads per 32 columns) and are expanded to exact fp16 integers in
+//    registers, so every weight is expanded once per workgroup;
+//  * 32x32x16 MFMAs form the group's sum in a fresh accumulator, which is then
+//    multiplied by the column's fp32 scale and added: sum_k x_k q_k s exactly as
+//    in the per-group definition.  A fragments of the next k step are read from
+//    LDS while the current step's MFMAs run.
+// Global loads run D-1 stages ahead in a register ring (straight-line loop,
+// clamped addresses; stages past the split's end are given scale 0).  LDS is
+// double-buffered, one barrier per stage.
+template <int BM, int WNB, int D, int KIND>
+__global__ __launch_bounds__(256) void gemm_skinny_w4_kernel(GemmArgs g, GemmEpi e, int kchunk) {
+  constexpr int RBW = BM / 32;           // 32-row blocks (every wave covers all rows)
+  constexpr int WN = 32 * WNB;
+  constexpr int BN = 4 * WN;
+  constexpr int AC = BM / 16;            // 16-byte A chunks per thread per stage
+  static_assert(RBW >= 1 && D >= 2, "tile");
+  __shared__ u32x4 As[2][BM * 16];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int m0 = blockIdx.y * BM, n0 = blockIdx.x * BN, wn0 = n0 + wave * WN, wr0 = 0;
+  const int M = g.M, N = g.N, K = g.K, groups = K >> 7;
+  const int S = gridDim.z, z = blockIdx.z;
+  const int kb = z * kchunk, ke = min(K, kb + kchunk);
+  const int nreal = (ke - kb) >> 7;
+  const int nst = (nreal + D - 1) / D * D;
+  const f16* A = reinterpret_cast<const f16*>(g.A);
+
+  floatx16 acc[RBW][WNB];
+#pragma unroll
+  for (int i = 0; i < RBW; ++i)
+#pragma unroll
+    for (int j = 0; j < WNB; ++j)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.f;
+
+  u32x4 ra[D][AC];
+  u32x4 rw[D][WNB][2];
+  uint16_t rs[D][WNB];
+
+  auto gload = [&](auto uc, int st) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+    const int gi = (kb >> 7) + min(st, nreal - 1);
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int c = tid + 256 * i, r = c >> 4, ch = c & 15;
+      const int gr = min(m0 + r, M - 1);
+      ra[u][i] = *reinterpret_cast<const u32x4*>(A + (int64_t)gr * K + gi * 128 + ch * 8);
+    }
+#pragma unroll
+    for (int cb = 0; cb < WNB; ++cb) {
+      const int nb = min((wn0 >> 5) + cb, (N >> 5) - 1);
+      const uint32_t* wp = g.Bw4 + ((int64_t)nb * groups + gi) * 512 + lane * 4;
+      rw[u][cb][0] = *reinterpret_cast<const u32x4*>(wp);
+      rw[u][cb][1] = *reinterpret_cast<const u32x4*>(wp + 256);
+      rs[u][cb] = g.Bs[(int64_t)gi * N + min(wn0 + cb * 32 + (lane & 31), N - 1)];
+    }
+  };
+  auto lstore = [&](auto uc, int buf) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int c = tid + 256 * i, r = c >> 4, ch = c & 15;
+      As[buf][r * 16 + (ch ^ (r & 15))] = ra[u][i];
+    }
+  };
+  auto read_a = [&](half8 (&a)[RBW], int buf, int j) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < RBW; ++i) {
+      const int r = wr0 + 32 * i + (lane & 31), ch = 2 * j + (lane >> 5);
+      a[i] = __builtin_bit_cast(half8, As[buf][r * 16 + (ch ^ (r & 15))]);
+    }
+  };
+  auto compute = [&](auto uc, int buf, bool valid) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+    floatx16 tmp[RBW][WNB];
+    half8 a[2][RBW];
+    read_a(a[0], buf, 0);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j < 7) read_a(a[(j + 1) & 1], buf, j + 1);
+      half8 b[WNB];
+#pragma unroll
+      for (int cb = 0; cb < WNB; ++cb) {
+        const u32x4 q4 = rw[u][cb][j >> 2];
+        const uint32_t w = q4[j & 3];
+#pragma unroll
+        for (int p = 0; p < 4; ++p) {
+          const half2v t = w4_pair(w, p);
+          b[cb][2 * p] = t[0];
+          b[cb][2 * p + 1] = t[1];
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < RBW; ++i)
+#pragma unroll
+        for (int cb = 0; cb < WNB; ++cb) {
+          if (j == 0) {
+            floatx16 zero;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+            tmp[i][cb] = mfma32(a[0][i], b[cb], zero);
+          } else {
+            tmp[i][cb] = mfma32(a[j & 1][i], b[cb], tmp[i][cb]);
+          }
+        }
+    }
+#pragma unroll
+    for (int cb = 0; cb < WNB; ++cb) {
+      const float sc = valid ? (float)__builtin_bit_cast(f16, rs[u][cb]) : 0.f;
+#pragma unroll
+      for (int i = 0; i < RBW; ++i) acc[i][cb] += sc * tmp[i][cb];
+    }
+  };
+
+  static_for<0, D - 1>([&](auto uc) __attribute__((always_inline)) { gload(uc, decltype(uc)::value); });
+  for (int s0 = 0; s0 < nst; s0 += D) {
+    static_for<0, D>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      const int st = s0 + u;
+      lstore(uc, st & 1);
+      lds_barrier();
+      gload(std::integral_constant<int, (u + D - 1) % D>{}, st + D - 1);
+      // keep the prefetch here: otherwise it is sunk past this stage's MFMAs to
+      // where its registers are next used, and nothing overlaps the load latency
+      asm volatile("" ::: "memory");
+      __builtin_amdgcn_sched_barrier(0);
+      compute(uc, st & 1, st < nreal);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+  }
+
+  // C layout of a 32x32 tile: lane holds column (lane & 31), rows
+  // 8 (r / 4) + 4 (lane / 32) + (r mod 4) for r = 0 .. 15
+  const int lc = lane & 31, lh = lane >> 5;
+  if (S > 1) {
+    float* part = g.partial + (int64_t)z * M * N;
+#pragma unroll
+    for (int i = 0; i < RBW; ++i)
+#pragma unroll
+      for (int cb = 0; cb < WNB; ++cb) {
+        const int col = wn0 + 32 * cb + lc;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int row = m0 + wr0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+          if (row < M && col < N) part[(int64_t)row * N + col] = acc[i][cb][r];
+        }
+      }
+    return;
+  }
+#pragma unroll
+  for (int i = 0; i < RBW; ++i)
+#pragma unroll
+    for (int cb = 0; cb < WNB; ++cb) {
+      const int col = wn0 + 32 * cb + lc;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int row = m0 + wr0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const float v = acc[i][cb][r];
+        if constexpr (paired(KIND)) {
+          // pair (c, c + 16) of a 32-column chunk: the partner sits 16 lanes away
+          const float v1 = __shfl_xor(v, 16, 64);
+          if (lc < 16 && row < M && col < N) epi_pair<f16, KIND>(e, row, col, v, v1);
+        } else {
+          if (row < M && col < N) epi_one<KIND>(e, row, col, v);
+        }
+      }
+    }
+}
+
 // fp32 operands: a plain LDS-tiled SIMT kernel (64 x 64 tile, 4 x 4 per thread).
 // Paired epilogues use adjacent column pairs (row-permutation granularity 1).
 template <int KIND>
@@ -499,7 +688,8 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
 
 // Split-K residual reduction fused with the next RMSNorm: one workgroup per row
 // adds the splits in order onto the fp32 residual, then normalises the new row
-// (fp32 statistics) into the next GEMM's operand type.
+// (fp32 statistics) into the next GEMM's operand type.  The first SMAX splits are
+// loaded together (branch-free); any further ones follow in order.
 template <class AT, int NPT>
 __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, GemmEpi e, int S) {
   constexpr int SMAX = 8;
@@ -524,6 +714,7 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
 #pragma unroll
     for (int z = 0; z < SMAX; ++z)
       if (z < S) a += p[z][u];
+    for (int z = SMAX; z < S; ++z) a += g.partial[((int64_t)z * M + row) * N + min(c, N - 1)];
     v[u] = 0.f;
     if (c < N) {
       v[u] = hr[c] + a;
@@ -586,8 +777,35 @@ TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
   return t;
 }
 
+// Finish a split-K product: the residual GEMM with a following RMSNorm sums the
+// splits in one kernel per row and normalises (fused, *norm_done = true); the
+// others sum per element and run their epilogue.
+template <class AT>
+hipError_t finish_splits(const GemmArgs& g, const GemmEpi& e, int splits, hipStream_t s, bool* norm_done) {
+  hipError_t err = hipGetLastError();
+  if (err != hipSuccess) return err;
+  const int npt = (g.N + 255) / 256;
+  if (e.kind == EPI_RESID && e.norm_g && npt <= 24) {
+    if (npt <= 8) hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, 8>), dim3(g.M), dim3(256), 0, s, g, e, splits);
+    else hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, 24>), dim3(g.M), dim3(256), 0, s, g, e, splits);
+    *norm_done = true;
+    return hipGetLastError();
+  }
+  const bool pr = paired(e.kind);
+  const int64_t items = (int64_t)g.M * (pr ? g.N / 2 : g.N);
+  dim3 rg((unsigned)((items + 255) / 256));
+  switch (e.kind) {
+    case EPI_QKV: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_QKV>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_RESID: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_RESID>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_SWIGLU>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_STORE: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_STORE>), rg, dim3(256), 0, s, g, e, splits); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <class AT, bool W4, int BM, int BN, int BK, int D>
-hipError_t launch_mfma_t(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, hipStream_t s) {
+hipError_t launch_mfma_t(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, hipStream_t s, bool* norm_done) {
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, t.splits);
   switch (e.kind) {
     case EPI_QKV: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
@@ -597,43 +815,85 @@ hipError_t launch_mfma_t(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, 
     case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
     default: return hipErrorInvalidValue;
   }
-  if (t.splits > 1 && e.kind == EPI_RESID && e.norm_g) {
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const int npt = (g.N + 255) / 256;
-    if (npt <= 8) hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, 8>), dim3(g.M), dim3(256), 0, s, g, e, t.splits);
-    else if (npt <= 24) hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, 24>), dim3(g.M), dim3(256), 0, s, g, e, t.splits);
-    else return hipErrorInvalidValue;   // unreachable: launch_gemm only fuses rows of <= 24 * 256
-    return hipGetLastError();
-  }
-  if (t.splits > 1) {
-    hipError_t err = hipGetLastError();
-    if (err != hipSuccess) return err;
-    const bool pr = e.kind == EPI_QKV || e.kind == EPI_SWIGLU;
-    const int64_t items = (int64_t)g.M * (pr ? g.N / 2 : g.N);
-    dim3 rg((unsigned)((items + 255) / 256));
-    switch (e.kind) {
-      case EPI_QKV: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_QKV>), rg, dim3(256), 0, s, g, e, t.splits); break;
-      case EPI_RESID: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_RESID>), rg, dim3(256), 0, s, g, e, t.splits); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_SWIGLU>), rg, dim3(256), 0, s, g, e, t.splits); break;
-      case EPI_STORE: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_STORE>), rg, dim3(256), 0, s, g, e, t.splits); break;
-      default: return hipErrorInvalidValue;
-    }
-  }
+  if (t.splits > 1) return finish_splits<AT>(g, e, t.splits, s, norm_done);
   return hipGetLastError();
 }
 
 template <class AT, bool W4>
-hipError_t launch_mfma(const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
+hipError_t launch_mfma(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool* norm_done) {
   const TileCfg t = pick_tile(DT_F16, g, e.kind);
   if (t.bn == 64) {
-    if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 64, 128, 2>(g, e, t, s);
-    return launch_mfma_t<AT, W4, 64, 64, 128, 2>(g, e, t, s);
+    if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 64, 128, 2>(g, e, t, s, norm_done);
+    return launch_mfma_t<AT, W4, 64, 64, 128, 2>(g, e, t, s, norm_done);
   }
-  if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 128, 128, 2>(g, e, t, s);
-  if (t.bm == 64) return launch_mfma_t<AT, W4, 64, 128, 128, 2>(g, e, t, s);
+  if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 128, 128, 2>(g, e, t, s, norm_done);
+  if (t.bm == 64) return launch_mfma_t<AT, W4, 64, 128, 128, 2>(g, e, t, s, norm_done);
   if constexpr (W4) return hipErrorInvalidValue;
-  else return launch_mfma_t<AT, W4, 128, 128, 64, 2>(g, e, t, s);
+  else return launch_mfma_t<AT, W4, 128, 128, 64, 2>(g, e, t, s, norm_done);
+}
+
+// ---- small-M INT4 path
+struct SkinnyCfg {
+  int bm, wnb, splits, kchunk, depth;   // bm == 0: not applicable
+};
+
+// Tile and split choice for the small-M INT4 kernel, fitted to a sweep of the
+// 2048-wide model's shapes at 32 and 64 rows on MI355X: two 32-column blocks per
+// wave when one-block tiles would number 32..63 (else one), K split so that
+// about 192 workgroups run, a third ring stage for K >= 4096.  For 33..64 rows
+// and N >= 8192 the LDS-tiled kernel measured faster and is kept.
+SkinnyCfg pick_skinny(const GemmArgs& g, int kind) {
+  SkinnyCfg t{0, 1, 1, 0, 2};
+  if (!g.Bw4 || g.M > 64 || kind == EPI_HEAD || (g.K % 128) != 0 || (g.N % 32) != 0) return t;
+  if (g.M > 32 && g.N >= 8192) return t;
+  const int bm = g.M <= 32 ? 32 : 64;
+  const int units = g.K / 128;
+  const int64_t rows = (g.M + bm - 1) / bm;
+  const int64_t tiles1 = (int64_t)((g.N + 127) / 128) * rows;
+  const int wnb = (tiles1 >= 32 && tiles1 < 64) ? 2 : 1;
+  const int64_t tiles = (int64_t)((g.N + 128 * wnb - 1) / (128 * wnb)) * rows;
+  int sp = (int)std::min<int64_t>(16, std::max<int64_t>(1, (192 + tiles / 2) / tiles));
+  sp = std::min(sp, units);
+  int per = (units + sp - 1) / sp;
+  sp = (units + per - 1) / per;
+  while (sp > 1 && (!g.partial || (int64_t)sp * g.M * g.N > g.partial_cap)) {
+    ++per;
+    sp = (units + per - 1) / per;
+  }
+  t.bm = bm;
+  t.wnb = wnb;
+  t.splits = sp;
+  t.kchunk = per * 128;
+  t.depth = g.K >= 4096 ? 3 : 2;
+  return t;
+}
+
+template <int BM, int WNB, int D>
+hipError_t launch_skinny_t(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg& t, hipStream_t s, bool* norm_done) {
+  constexpr int BN = 4 * 32 * WNB;
+  dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, t.splits);
+  switch (e.kind) {
+    case EPI_QKV: hipLaunchKernelGGL((gemm_skinny_w4_kernel<BM, WNB, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny_w4_kernel<BM, WNB, D, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_skinny_w4_kernel<BM, WNB, D, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny_w4_kernel<BM, WNB, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    default: return hipErrorInvalidValue;
+  }
+  if (t.splits > 1) return finish_splits<f16>(g, e, t.splits, s, norm_done);
+  return hipGetLastError();
+}
+
+template <int D>
+hipError_t launch_skinny_d(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg& t, hipStream_t s, bool* norm_done) {
+  if (t.bm == 32) return t.wnb == 1 ? launch_skinny_t<32, 1, D>(g, e, t, s, norm_done) : launch_skinny_t<32, 2, D>(g, e, t, s, norm_done);
+  if (t.bm == 64) return t.wnb == 1 ? launch_skinny_t<64, 1, D>(g, e, t, s, norm_done) : launch_skinny_t<64, 2, D>(g, e, t, s, norm_done);
+  return hipErrorInvalidValue;
+}
+
+hipError_t launch_skinny(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg& t, hipStream_t s, bool* norm_done) {
+  if (t.depth == 2) return launch_skinny_d<2>(g, e, t, s, norm_done);
+  if (t.depth == 3) return launch_skinny_d<3>(g, e, t, s, norm_done);
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -647,22 +907,21 @@ int gemm_head_tiles(int act_dtype, int M, int N) {
   return (N + t.bn - 1) / t.bn;
 }
 
-static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s);
+static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s,
+                                   bool* norm_done);
 
 // Residual GEMM with a following RMSNorm: fused into the split-K reduction when K
 // is split, else the epilogue adds into h and a separate RMSNorm kernel runs.
 hipError_t launch_gemm(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
-  hipError_t err = launch_gemm_core(act_dtype, g, e, s);
-  if (err != hipSuccess || e.kind != EPI_RESID || !e.norm_g) return err;
-  if (act_dtype != DT_F32 && (g.N + 255) / 256 <= 24) {
-    const TileCfg t = pick_tile(act_dtype, g, e.kind);
-    if (t.splits > 1) return hipSuccess;   // normalised by the fused reduction
-  }
+  bool norm_done = false;
+  hipError_t err = launch_gemm_core(act_dtype, g, e, s, &norm_done);
+  if (err != hipSuccess || e.kind != EPI_RESID || !e.norm_g || norm_done) return err;
   return launch_rmsnorm(act_dtype, e.h, e.norm_g, nullptr, g.M, g.N, e.norm_eps, e.norm_out, s);
 }
 
-static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
+static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s,
+                                   bool* norm_done) {
   if (act_dtype == DT_F32) {
     dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
     switch (e.kind) {
@@ -676,12 +935,18 @@ static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmE
     return hipGetLastError();
   }
   if (act_dtype == DT_F16) {
-    if (g.Bw4) return launch_mfma<f16, true>(g, e, s);
-    return launch_mfma<f16, false>(g, e, s);
+    if (g.Bw4) {
+      if (e.pair_g == 16) {
+        const SkinnyCfg t = pick_skinny(g, e.kind);
+        if (t.bm) return launch_skinny(g, e, t, s, norm_done);
+      }
+      return launch_mfma<f16, true>(g, e, s, norm_done);
+    }
+    return launch_mfma<f16, false>(g, e, s, norm_done);
   }
   if (act_dtype == DT_BF16) {
     if (g.Bw4) return hipErrorInvalidValue;
-    return launch_mfma<bf16, false>(g, e, s);
+    return launch_mfma<bf16, false>(g, e, s, norm_done);
   }
   return hipErrorInvalidValue;
 }

@@ -210,12 +210,12 @@ __global__ __launch_bounds__(256) void quant_w4_kernel(const float* __restrict__
   part |= __shfl_xor(part, 1, 64);
   part |= __shfl_xor(part, 2, 64);
   if ((lane & 3) == 0)
-    words[((int64_t)(n >> 4) * groups + gi) * 256 + (n & 15) * 16 + (lane >> 2)] = (uint32_t)part;
+    words[w4_word_offset(n, gi * 16 + (lane >> 2), groups)] = (uint32_t)part;
   if (lane == 0) scales[(int64_t)gi * N + n] = __builtin_bit_cast(uint16_t, s16);
 }
 
 __device__ __forceinline__ f16 w4_value(const uint32_t* words, int groups, int n, int k) {
-  const uint32_t wd = words[((int64_t)(n >> 4) * groups + (k >> 7)) * 256 + (n & 15) * 16 + ((k & 127) >> 3)];
+  const uint32_t wd = words[w4_word_offset(n, k >> 3, groups)];
   const int e = k & 7;
   const half2v p = w4_pair(wd, e >> 1);
   return p[e & 1];

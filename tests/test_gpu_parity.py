@@ -25,6 +25,9 @@ TINY = {
     "tiny-w4": synth.ModelSpec("tiny-w4", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "w4g128"),
     "tiny-f16body": synth.ModelSpec("tiny-f16body", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "f16body"),
     "tiny-bf16-stack": synth.ModelSpec("tiny-bf16-stack", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16"),
+    # INT4, 16 K groups in the down projection: at decode sizes its K is split 16
+    # ways, more than the fused residual + norm reduction loads at once
+    "tiny-w4-wide": synth.ModelSpec("tiny-w4-wide", 256, 256, 4, 64, 2048, 1, 1, 0, "f16", "w4g128"),
 }
 
 
@@ -136,7 +139,7 @@ def test_cfg1_forward_and_greedy_decode():
         tl.tl_free(model)
 
 
-@pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack"])
+@pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack", "tiny-w4-wide"])
 def test_tiny_decode_mixed_and_monotone_depth(name):
     """Lanes at different depths, per-token requests clamped to never rise."""
     spec = TINY[name]
