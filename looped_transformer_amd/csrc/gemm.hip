@@ -688,38 +688,46 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
 
 // Split-K residual reduction fused with the next RMSNorm: one workgroup per row
 // adds the splits in order onto the fp32 residual, then normalises the new row
-// (fp32 statistics) into the next GEMM's operand type.  The first SMAX splits are
-// loaded together (branch-free); any further ones follow in order.
-template <class AT, int NPT>
+// (fp32 statistics) into the next GEMM's operand type.  Each thread owns VPT
+// groups of 4 consecutive columns (16-byte loads); with SN > 0 the SN splits are
+// all requested before any is used, with SN == 0 a loop adds any number.
+template <class AT, int VPT, int SN>
 __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, GemmEpi e, int S) {
-  constexpr int SMAX = 8;
   const int row = blockIdx.x, N = g.N, M = g.M;
   float* hr = e.h + (int64_t)row * e.ldh;
-  // every split's value is requested before any is used (branch-free, clamped
-  // indices), then the splits are added in order onto the residual
-  float p[SMAX][NPT];
+  const floatx4* P = reinterpret_cast<const floatx4*>(g.partial);
+  const int64_t zs = (int64_t)M * N / 4, rs = (int64_t)row * N / 4;
+  floatx4 acc[VPT];
 #pragma unroll
-  for (int z = 0; z < SMAX; ++z)
+  for (int u = 0; u < VPT; ++u) acc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  if constexpr (SN > 0) {
+    floatx4 p[SN][VPT];
 #pragma unroll
-    for (int u = 0; u < NPT; ++u) {
-      const int c = min(threadIdx.x + 256 * u, N - 1);
-      p[z][u] = g.partial[((int64_t)min(z, S - 1) * M + row) * N + c];
-    }
-  float v[NPT];
+    for (int z = 0; z < SN; ++z)
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) p[z][u] = P[z * zs + rs + min((int)threadIdx.x + 256 * u, N / 4 - 1)];
+#pragma unroll
+    for (int z = 0; z < SN; ++z)
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        acc[u] += p[z][u];
+      }
+  } else {
+    for (int z = 0; z < S; ++z)
+#pragma unroll
+      for (int u = 0; u < VPT; ++u) {
+        acc[u] += P[z * zs + rs + min((int)threadIdx.x + 256 * u, N / 4 - 1)];
+      }
+  }
   float ss = 0.f;
 #pragma unroll
-  for (int u = 0; u < NPT; ++u) {
-    const int c = threadIdx.x + 256 * u;
-    float a = 0.f;
-#pragma unroll
-    for (int z = 0; z < SMAX; ++z)
-      if (z < S) a += p[z][u];
-    for (int z = SMAX; z < S; ++z) a += g.partial[((int64_t)z * M + row) * N + min(c, N - 1)];
-    v[u] = 0.f;
-    if (c < N) {
-      v[u] = hr[c] + a;
-      hr[c] = v[u];
-      ss = fmaf(v[u], v[u], ss);
+  for (int u = 0; u < VPT; ++u) {
+    const int c4 = (int)threadIdx.x + 256 * u;
+    if (c4 * 4 < N) {
+      const floatx4 hv = *reinterpret_cast<const floatx4*>(hr + 4 * c4) + acc[u];
+      *reinterpret_cast<floatx4*>(hr + 4 * c4) = hv;
+      acc[u] = hv;
+      ss = fmaf(hv[0], hv[0], fmaf(hv[1], hv[1], fmaf(hv[2], hv[2], fmaf(hv[3], hv[3], ss))));
     }
   }
   __shared__ float red[4];
@@ -730,9 +738,13 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
   const float inv = 1.0f / sqrtf(tot / (float)N + e.norm_eps);
   AT* o = reinterpret_cast<AT*>(e.norm_out) + (int64_t)row * N;
 #pragma unroll
-  for (int u = 0; u < NPT; ++u) {
-    const int c = threadIdx.x + 256 * u;
-    if (c < N) o[c] = from_f32<AT>(v[u] * inv * e.norm_g[c]);
+  for (int u = 0; u < VPT; ++u) {
+    const int c4 = (int)threadIdx.x + 256 * u;
+    if (c4 * 4 < N) {
+      const floatx4 gg = *reinterpret_cast<const floatx4*>(e.norm_g + 4 * c4);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) o[4 * c4 + q] = from_f32<AT>(acc[u][q] * inv * gg[q]);
+    }
   }
 }
 
@@ -784,10 +796,21 @@ template <class AT>
 hipError_t finish_splits(const GemmArgs& g, const GemmEpi& e, int splits, hipStream_t s, bool* norm_done) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
-  const int npt = (g.N + 255) / 256;
-  if (e.kind == EPI_RESID && e.norm_g && npt <= 24) {
-    if (npt <= 8) hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, 8>), dim3(g.M), dim3(256), 0, s, g, e, splits);
-    else hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, 24>), dim3(g.M), dim3(256), 0, s, g, e, splits);
+  const int vpt = (g.N / 4 + 255) / 256;
+  if (e.kind == EPI_RESID && e.norm_g && (g.N % 4) == 0 && (e.ldh % 4) == 0 && vpt <= 6) {
+#define TL_RN(VPT_)                                                                                                \
+  switch (splits) {                                                                                               \
+    case 2: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 2>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 3: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 3>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 4: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 4>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 5: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 5>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 6: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 6>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 8: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 8>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    default: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 0>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+  }
+    if (vpt <= 2) { TL_RN(2) }
+    else { TL_RN(6) }
+#undef TL_RN
     *norm_done = true;
     return hipGetLastError();
   }
