@@ -91,12 +91,14 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
 
 // ----------------------------------------------------------------------------
 // Tiled causal attention for runs of consecutive query rows of one sequence.
-// Workgroup = (64-row tile, head); wave w owns query rows 16w .. 16w+15.  Keys and
-// values stream through LDS in blocks of 64 positions.  S = Q K^T and O += P V run
-// on 16x16x32 MFMA (QK^T in the cache type, PV in fp16 with V converted on its way
-// into LDS), with a running row max / sum in fp32 (online softmax).  The score
-// tile leaves the MFMA in column-per-lane layout, so P goes through LDS to become
-// the row-per-lane A operand of PV.
+// Workgroup = (tile of kAttnTileRows rows, head); wave w owns query rows
+// 16w .. 16w+15.  Keys and values stream through LDS in blocks of 64 positions;
+// the next block's K/V are loaded into registers while the current block
+// computes (LDS-only barriers, so the loads stay in flight).  S = Q K^T and
+// O += P V run on 16x16x32 MFMA (QK^T in the cache type, PV in fp16 with V
+// converted on its way into LDS), with a running row max / sum in fp32 (online
+// softmax).  The score tile leaves the MFMA in column-per-lane layout, so P goes
+// through LDS to become the row-per-lane A operand of PV.
 template <class T> struct QkMfma;
 template <> struct QkMfma<f16> {
   typedef half8 frag;
@@ -111,18 +113,26 @@ template <> struct QkMfma<bf16> {
   }
 };
 
+constexpr int kAttnTileRows = 32;
+constexpr int kAttnWaves = kAttnTileRows / 16;
+
 template <class T, int DH>
-__global__ __launch_bounds__(256) void attn_tiled_kernel(const T* __restrict__ q, const AttnTile* __restrict__ tiles,
-                                                        KVParams kv, T* __restrict__ out, int d, float scale) {
+__global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __restrict__ q,
+                                                                     const AttnTile* __restrict__ tiles, KVParams kv,
+                                                                     T* __restrict__ out, int d, float scale) {
+  constexpr int NW = kAttnWaves, NT = 64 * NW;
   constexpr int KB = 64;
   constexpr int LDK = DH + 8;
   constexpr int LDV = KB + 8;
   constexpr int KS = DH / 32;
   constexpr int OT = DH / 16;
+  constexpr int CH = KB * DH / 8;   // 16-byte chunks of one K (or V) block
+  constexpr int CPT = CH / NT;      // per thread
+  static_assert(CH % NT == 0, "block split");
   typedef typename QkMfma<T>::frag qfrag;
   __shared__ __attribute__((aligned(16))) T Ks[KB * LDK];
   __shared__ __attribute__((aligned(16))) f16 Vt[DH * LDV];
-  __shared__ __attribute__((aligned(16))) f16 Ps[4][16 * LDV];
+  __shared__ __attribute__((aligned(16))) f16 Ps[NW][16 * LDV];
 
   const AttnTile tile = tiles[blockIdx.x];
   const int h = blockIdx.y;
@@ -132,15 +142,28 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(const T* __restrict__ q
   const int64_t cap = kv.lane_cap[tile.lane];
   const T* Kg = reinterpret_cast<const T*>(kv.base) + kv.lane_off[tile.lane] + ((int64_t)(slot * 2) * kv.H + h) * cap * DH;
   const T* Vg = Kg + (int64_t)kv.H * cap * DH;
+  const int kend = tile.pos0 + tile.nrows;
+
+  // K/V block k0 -> registers; positions past the end are clamped to the last
+  // valid one (their scores are masked, so P = 0 multiplies finite values)
+  u32x4 rk[CPT], rv[CPT];
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + NT * i, key = c / (DH / 8), dc = (c % (DH / 8)) * 8;
+      const int kp = min(k0 + key, kend - 1);
+      rk[i] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)kp * DH + dc);
+      rv[i] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)kp * DH + dc);
+    }
+  };
+  load(0);
 
   const int qr = 16 * w + l16;
   qfrag qa[KS];
 #pragma unroll
   for (int ks = 0; ks < KS; ++ks) {
-    qfrag v = {};
-    if (qr < tile.nrows)
-      v = *reinterpret_cast<const qfrag*>(q + (int64_t)(tile.row0 + qr) * d + h * DH + ks * 32 + 8 * g4);
-    qa[ks] = v;
+    const int qrc = min(qr, tile.nrows - 1);
+    qa[ks] = *reinterpret_cast<const qfrag*>(q + (int64_t)(tile.row0 + qrc) * d + h * DH + ks * 32 + 8 * g4);
   }
   floatx4 o[OT];
 #pragma unroll
@@ -152,24 +175,20 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(const T* __restrict__ q
     lrow[r] = 0.f;
   }
   const int qpos0 = tile.pos0 + 16 * w + 4 * g4;
-  const int kend = tile.pos0 + tile.nrows;
 
   for (int k0 = 0; k0 < kend; k0 += KB) {
-    __syncthreads();
-    for (int c = tid; c < KB * DH / 8; c += 256) {
-      const int key = c / (DH / 8), dc = (c % (DH / 8)) * 8;
-      const int kp = k0 + key;
-      uint4 kvv = {0u, 0u, 0u, 0u}, vvv = {0u, 0u, 0u, 0u};
-      if (kp < kend) {
-        kvv = *reinterpret_cast<const uint4*>(Kg + (int64_t)kp * DH + dc);
-        vvv = *reinterpret_cast<const uint4*>(Vg + (int64_t)kp * DH + dc);
-      }
-      *reinterpret_cast<uint4*>(&Ks[key * LDK + dc]) = kvv;
-      const T* ve = reinterpret_cast<const T*>(&vvv);
+    lds_barrier();   // every wave is done reading the previous block
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + NT * i, key = c / (DH / 8), dc = (c % (DH / 8)) * 8;
+      *reinterpret_cast<u32x4*>(&Ks[key * LDK + dc]) = rk[i];
+      const T* ve = reinterpret_cast<const T*>(&rv[i]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) Vt[(dc + e) * LDV + key] = (f16)(float)ve[e];
     }
-    __syncthreads();
+    lds_barrier();
+    if (k0 + KB < kend) load(k0 + KB);
+    asm volatile("" ::: "memory");   // keep the prefetch ahead of this block's math
 
     floatx4 sacc[4];
 #pragma unroll
@@ -202,8 +221,10 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(const T* __restrict__ q
     float corr[4], rs[4];
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
+      // a row with no key yet in this block keeps m = -inf; exp(-inf - -inf)
+      // would be NaN, so its correction is 1 and its probabilities 0
       const float mn = fmaxf(mrow[r], mx[r]);
-      corr[r] = expf(mrow[r] - mn);
+      corr[r] = mn == -INFINITY ? 1.f : expf(mrow[r] - mn);
       mrow[r] = mn;
       rs[r] = 0.f;
     }
@@ -211,7 +232,7 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(const T* __restrict__ q
     for (int n = 0; n < 4; ++n)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const float p = expf(sacc[n][r] - mrow[r]);
+        const float p = sacc[n][r] == -INFINITY ? 0.f : expf(sacc[n][r] - mrow[r]);
         rs[r] += p;
         Ps[w][(4 * g4 + r) * LDV + 16 * n + l16] = (f16)p;
       }
@@ -225,7 +246,10 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(const T* __restrict__ q
     for (int t = 0; t < OT; ++t)
 #pragma unroll
       for (int r = 0; r < 4; ++r) o[t][r] *= corr[r];
-    __syncthreads();   // P tiles written
+    // P tile of this wave written by this wave only: a wave-level LDS barrier
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
 #pragma unroll
     for (int kk = 0; kk < KB; kk += 32) {
       const half8 a = *reinterpret_cast<const half8*>(&Ps[w][l16 * LDV + kk + 8 * g4]);
@@ -249,6 +273,8 @@ __global__ __launch_bounds__(256) void attn_tiled_kernel(const T* __restrict__ q
 
 }  // namespace
 
+int attn_tile_rows() { return kAttnTileRows; }
+
 bool attn_tiled_supported(int dtype, int head_dim) {
   return (dtype == DT_F16 || dtype == DT_BF16) && (head_dim == 64 || head_dim == 96 || head_dim == 128);
 }
@@ -261,7 +287,7 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
   dim3 grid(n_tiles, kv.H);
 #define TL_ATTN_CASE(T, DHV)                                                                                   \
   if (kv.dh == DHV) {                                                                                          \
-    hipLaunchKernelGGL((attn_tiled_kernel<T, DHV>), grid, dim3(256), 0, s, (const T*)q, tiles, kv, (T*)out, d, \
+    hipLaunchKernelGGL((attn_tiled_kernel<T, DHV>), grid, dim3(kAttnWaves * 64), 0, s, (const T*)q, tiles, kv, (T*)out, d, \
                        scale);                                                                                 \
     return hipGetLastError();                                                                                  \
   }

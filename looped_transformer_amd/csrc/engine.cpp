@@ -358,16 +358,17 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
 }
 
 // Attention tiles of one iteration: sequences still active, in caller order, each
-// cut into runs of at most 64 consecutive rows.
+// cut into runs of at most attn_tile_rows() consecutive rows.
 void add_tiles(std::vector<AttnTile>& out, const std::vector<int>& seq_len, const std::vector<int>& seq_lane,
                const std::vector<int>& Ls, int j) {
+  const int tr = attn_tile_rows();
   int row = 0;
   for (size_t sq = 0; sq < seq_len.size(); ++sq) {
     if (Ls[sq] < j) continue;
-    for (int p0 = 0; p0 < seq_len[sq]; p0 += 64) {
+    for (int p0 = 0; p0 < seq_len[sq]; p0 += tr) {
       AttnTile t{};
       t.row0 = row + p0;
-      t.nrows = std::min(64, seq_len[sq] - p0);
+      t.nrows = std::min(tr, seq_len[sq] - p0);
       t.pos0 = p0;
       t.lane = seq_lane[sq];
       t.iter = j;

@@ -75,14 +75,16 @@ hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const i
                           int d, float eps, void* out, hipStream_t s);
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv,
                             void* out, hipStream_t s);
-// A run of up to 64 consecutive rows of one sequence (positions pos0 .. pos0+nrows-1)
+// A run of up to attn_tile_rows() consecutive rows of one sequence (positions pos0 .. pos0+nrows-1)
 // that attend to positions 0 .. pos0+nrows-1 of their lane's slot.
 struct AttnTile {
   int32_t row0, nrows, pos0, lane, iter, p0, p1, p2;
 };
 // Tiled causal attention (MFMA) for prefill / scoring passes; 16-bit types and
-// head_dim in {64, 96, 128} only (attn_tiled_supported).
+// head_dim in {64, 96, 128} only (attn_tiled_supported).  A tile holds at most
+// attn_tile_rows() consecutive rows.
 bool attn_tiled_supported(int dtype, int head_dim);
+int attn_tile_rows();
 hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tiles, int n_tiles, const KVParams& kv,
                                   void* out, hipStream_t s);
 // Stable filter of the active rows after iteration it (it = 0: each row's own
