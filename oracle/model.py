@@ -47,6 +47,7 @@ __all__ = [
     "quantize_w4g128", "pack_nibbles", "unpack_nibbles", "dequant_w4g128", "fp16_body",
     "OracleModel", "Lane", "prefill", "decode_step", "forward_batch", "forward_ragged",
     "greedy_argmax", "clamp_depths", "active_lists", "bf16_bits_to_float",
+    "EarlyExit", "probe_iteration", "relative_delta", "logit_margin", "decode_step_ee",
 ]
 
 
@@ -354,6 +355,102 @@ def decode_step(m: OracleModel, lane: Lane, L_req: int, token: int | None = None
     lane.pending = nxt
     lane.hidden_last = h[0].copy()
     return h[0], logits, nxt, L
+
+
+# ---------------------------------------------------------------------------
+# confidence-based early exit of cached decode ([CLI] "generate": the options
+# --early-exit-patience, --early-exit-min-L, --early-exit-tau,
+# --early-exit-peek-every and --early-exit-logit-margin)
+
+
+@dataclass
+class EarlyExit:
+    """Early-exit rule of one decode call.
+
+    patience: consecutive stable probes that end the token's loop (0 disables);
+    min_L: first loop iteration that is probed; peek_every: probe every this many
+    iterations from min_L on; tau: hidden-state rule, stable when the relative L2
+    change of the residual over one iteration is below tau; logit_margin > 0
+    switches to the logit rule, stable when top-1 minus top-2 of the full head
+    projection at the current state exceeds it.
+    """
+    patience: int
+    min_L: int = 2
+    tau: float = 1e-3
+    peek_every: int = 1
+    logit_margin: float = 0.0
+
+
+def probe_iteration(ee: EarlyExit, j: int, L: int) -> bool:
+    """Iteration j of a token running at most L iterations is probed.
+
+    Probes start at min_L and repeat every peek_every iterations; a probe after the
+    last iteration (j = L) could not shorten the loop and is not taken.
+    """
+    return ee.patience > 0 and j < L and j >= ee.min_L and (j - ee.min_L) % ee.peek_every == 0
+
+
+def relative_delta(h_prev: np.ndarray, h: np.ndarray) -> float:
+    """||h - h_prev||_2 / ||h||_2 of one token's residual across one loop iteration."""
+    return float(np.linalg.norm(h - h_prev) / np.linalg.norm(h))
+
+
+def logit_margin(logits: np.ndarray) -> float:
+    """Top-1 minus top-2 logit (the two largest values of the row; equal values give 0)."""
+    top = np.sort(np.asarray(logits, dtype=np.float64).ravel())[-2:]
+    return float(top[1] - top[0])
+
+
+def decode_step_ee(m: OracleModel, lane: Lane, L_req: int, ee: EarlyExit, token: int | None = None):
+    """decode_step with the early-exit rule applied after every probed iteration.
+
+    The token starts with depth L = min(L_req, ceiling).  After probed iteration j
+    the rule looks at the state h_j; a stable probe extends the streak, an unstable
+    one resets it; when the streak reaches patience the loop stops at j (its later
+    cache slots are not written) and j becomes the effective depth and the lane's
+    new ceiling (monotone clamping keeps the cache consistent for later tokens).
+    Returns (hidden [d], logits [V], next token, effective depth).
+    """
+    assert L_req >= 1
+    L = min(int(L_req), lane.ceiling)
+    tok = lane.pending if token is None else int(token)
+    p = len(lane.tokens)
+    pos = np.array([p])
+    sp = m.spec
+    h = m.embed_rows(np.array([tok]))
+
+    def run(b, key, h):
+        pk, pv = lane.kv[key]
+        assert pk.shape[0] == p, "cache slot misses earlier positions"
+        h, k, v = m.block(b, h, pos, pk, pv)
+        lane.kv[key] = (np.concatenate([pk, k]), np.concatenate([pv, v]))
+        return h
+
+    for b in range(sp.n_pre):
+        h = run(b, ("pre", b), h)
+    eff, streak = L, 0
+    for j in range(1, L + 1):
+        h_prev = h
+        for l in range(sp.n_loop):
+            h = run(sp.n_pre + l, ("loop", j, l), h)
+        if probe_iteration(ee, j, L):
+            if ee.logit_margin > 0:
+                stable = logit_margin(m.logits(h)[0]) > ee.logit_margin
+            else:
+                stable = relative_delta(h_prev[0], h[0]) < ee.tau
+            streak = streak + 1 if stable else 0
+            if streak >= ee.patience:
+                eff = j
+                break
+    for b in range(sp.n_post):
+        h = run(sp.n_pre + sp.n_loop + b, ("post", b), h)
+    lane.tokens.append(tok)
+    lane.ceiling = eff
+    logits = m.logits(h)[0]
+    nxt = int(greedy_argmax(logits))
+    lane.pending = nxt
+    lane.hidden_last = h[0].copy()
+    return h[0], logits, nxt, eff
 
 
 def clamp_depths(requests, first_ceiling: int) -> np.ndarray:

@@ -398,3 +398,94 @@ def test_fp32_vs_fp64_conditioning_int4_model():
         _, h32, _ = oracle.prefill(m32, toks, L, want_logits="none")
         rel = np.linalg.norm(h32 - h64) / np.linalg.norm(h64)
         assert rel < 1e-4, (L, rel)
+
+
+# ---------------------------------------------------------------------------
+# early exit ([CLI] "generate": --early-exit-* options)
+
+
+def test_ee_relative_delta_and_margin_hand_values():
+    # ||(0, 0, 12)|| / ||(3, 4, 12)|| = 12 / 13
+    assert abs(oracle.relative_delta(np.array([3.0, 4.0, 0.0]), np.array([3.0, 4.0, 12.0])) - 12.0 / 13.0) < 1e-15
+    assert oracle.logit_margin(np.array([0.5, 2.0, -1.0])) == 1.5
+    assert oracle.logit_margin(np.array([1.0, 5.0, 2.0, 5.0])) == 0.0   # tied top-1
+
+
+def test_ee_probe_schedule_brute_force():
+    ee = oracle.EarlyExit(patience=1, min_L=3, peek_every=2)
+    assert [j for j in range(1, 11) if oracle.probe_iteration(ee, j, 10)] == [3, 5, 7, 9]
+    assert [j for j in range(1, 10) if oracle.probe_iteration(ee, j, 9)] == [3, 5, 7]   # never at j = L
+    assert not any(oracle.probe_iteration(oracle.EarlyExit(patience=0), j, 10) for j in range(1, 11))
+
+
+def _tiny_lane(seed=11, plen=9, L=6):
+    spec = synth.SPECS[1]
+    w = synth.make_weights(spec, seed)
+    m = oracle.OracleModel.from_weights(w)
+    toks = synth.tokens(seed, 77, plen, spec.vocab)
+    return m, (lambda: oracle.prefill(m, toks, L)[0])
+
+
+def _same_lane(a, b):
+    assert a.tokens == b.tokens and a.ceiling == b.ceiling and a.pending == b.pending
+    assert set(a.kv) == set(b.kv)
+    for k in a.kv:
+        assert np.array_equal(a.kv[k][0], b.kv[k][0]) and np.array_equal(a.kv[k][1], b.kv[k][1])
+
+
+def test_ee_disabled_equals_plain_decode():
+    m, fresh = _tiny_lane()
+    a, b = fresh(), fresh()
+    for t, L in enumerate([6, 5, 6, 3]):
+        ha, la, na, Ea = oracle.decode_step(m, a, L)
+        hb, lb, nb, Eb = oracle.decode_step_ee(m, b, L, oracle.EarlyExit(patience=0, tau=1e9))
+        assert np.array_equal(ha, hb) and np.array_equal(la, lb) and na == nb and Ea == Eb
+        _same_lane(a, b)
+
+
+@pytest.mark.parametrize("patience,min_L,peek,exit_at", [(1, 2, 1, 2), (2, 2, 1, 3), (2, 2, 2, 4), (1, 5, 1, 5)])
+def test_ee_always_stable_equals_decode_at_exit_depth(patience, min_L, peek, exit_at):
+    """tau = inf: every probe is stable, so the loop stops at the patience-th probe,
+    which must equal plain cached decode requested at that depth."""
+    m, fresh = _tiny_lane()
+    a, b = fresh(), fresh()
+    ee = oracle.EarlyExit(patience=patience, min_L=min_L, tau=np.inf, peek_every=peek)
+    hb, lb, nb, Eb = oracle.decode_step_ee(m, b, 6, ee)
+    ha, la, na, Ea = oracle.decode_step(m, a, exit_at)
+    assert Eb == exit_at == Ea
+    assert np.array_equal(ha, hb) and np.array_equal(la, lb) and na == nb
+    _same_lane(a, b)
+    # the lowered ceiling holds for the next token
+    hb2, _, _, Eb2 = oracle.decode_step_ee(m, b, 6, oracle.EarlyExit(patience=0))
+    ha2, _, _, Ea2 = oracle.decode_step(m, a, 6)
+    assert Eb2 == Ea2 == exit_at and np.array_equal(ha2, hb2)
+
+
+def test_ee_never_stable_runs_full_depth():
+    m, fresh = _tiny_lane()
+    a, b = fresh(), fresh()
+    hb, _, _, Eb = oracle.decode_step_ee(m, b, 6, oracle.EarlyExit(patience=1, min_L=1, tau=0.0))
+    ha, _, _, Ea = oracle.decode_step(m, a, 6)
+    assert Eb == Ea == 6 and np.array_equal(ha, hb)
+    hb, _, _, Eb = oracle.decode_step_ee(m, b, 6, oracle.EarlyExit(patience=1, min_L=1, logit_margin=1e300))
+    ha, _, _, Ea = oracle.decode_step(m, a, 6)
+    assert Eb == Ea == 6 and np.array_equal(ha, hb)
+
+
+def test_ee_logit_rule_tiny_margin_exits_at_first_probe():
+    m, fresh = _tiny_lane()
+    a, b = fresh(), fresh()
+    hb, lb, _, Eb = oracle.decode_step_ee(m, b, 6, oracle.EarlyExit(patience=1, min_L=3, logit_margin=1e-300))
+    ha, la, _, Ea = oracle.decode_step(m, a, 3)
+    assert Eb == Ea == 3 and np.array_equal(ha, hb) and np.array_equal(la, lb)
+
+
+def test_ee_streak_resets_on_unstable_probe(monkeypatch):
+    """Scripted probe outcomes: stable, unstable, stable, stable with patience 2 ->
+    the loop ends at the fourth probe, not the second."""
+    m, fresh = _tiny_lane(L=8)
+    script = iter([0.0, 1.0, 0.0, 0.0, 0.0, 0.0])
+    monkeypatch.setattr(oracle.model, "relative_delta", lambda hp, h: next(script))
+    b = fresh()
+    _, _, _, E = oracle.decode_step_ee(m, b, 8, oracle.EarlyExit(patience=2, min_L=2, tau=0.5))
+    assert E == 5   # probes at 2 (stable), 3 (unstable), 4, 5 (stable, stable)
