@@ -165,6 +165,43 @@ tl_status tl_decode_step(tl_model* m, int32_t n_lanes, const int32_t* lanes_host
                          int32_t* out_tokens_dev, float* out_logits_dev, float* out_hidden_dev,
                          int32_t* out_eff_L_host, int32_t* out_active_log_dev, void* stream);
 
+/* Early-exit rule of a decode call ("CLI Reference" page, "generate": the
+ * --early-exit-patience, --early-exit-min-L, --early-exit-tau,
+ * --early-exit-peek-every and --early-exit-logit-margin options).  A token is
+ * probed after loop iterations j >= min_L with (j - min_L) divisible by
+ * peek_every, never after its last iteration.  A probe is stable when the
+ * relative L2 change of the token's residual over iteration j,
+ * ||h_j - h_(j-1)|| / ||h_j||, is below tau, or, with logit_margin > 0, when
+ * top-1 minus top-2 of the head logits at h_j (final norm, head projection)
+ * exceeds logit_margin.  patience consecutive stable probes end the token's loop
+ * at j; an unstable probe resets the count; patience 0 disables the rule. */
+typedef struct tl_early_exit {
+  int32_t patience;
+  int32_t min_L;
+  int32_t peek_every;
+  float tau;
+  float logit_margin;
+} tl_early_exit;
+
+/* tl_decode_step with the early-exit rule decided on the device.  Each token
+ * starts at depth min(request, lane ceiling).  After a probed iteration a kernel
+ * marks the tokens whose streak reached patience as finished there: their
+ * residual at that point is the step's hidden state (and feeds the head), their
+ * later cache slots of this position are not written, and they are carried but
+ * ignored until the planned compaction drops them.  Nothing in the loop waits for
+ * the host; once every token has finished, the remaining iterations' kernels
+ * return at once.  The effective depth becomes the lane's ceiling (monotonic
+ * clamping).  The call waits for the stream once, at the end, to return
+ * out_eff_L_host.
+ *   ee: the rule; patience >= 0, min_L >= 1, peek_every >= 1, tau >= 0,
+ *       logit_margin >= 0.  Other arguments as tl_decode_step (no active-row log).
+ * Errors: as tl_decode_step; TL_E_ARG for a NULL or invalid rule. */
+tl_status tl_decode_step_ee(tl_model* m, int32_t n_lanes, const int32_t* lanes_host,
+                            const int32_t* per_lane_L_host, const tl_early_exit* ee,
+                            const int32_t* in_tokens_dev, int32_t* out_tokens_dev,
+                            float* out_logits_dev, float* out_hidden_dev, int32_t* out_eff_L_host,
+                            void* stream);
+
 /* n_steps greedy tokens for each of n_lanes prefilled lanes, scheduled one loop
  * iteration at a time across lanes (continuous depth batching: "Continuous Depth
  * Batching" summary page).  A pool holds one in-flight token per lane, each at its

@@ -48,6 +48,11 @@ class tl_weights(ctypes.Structure):
                 ("blocks", ctypes.POINTER(tl_block_weights))]
 
 
+class tl_early_exit(ctypes.Structure):
+    _fields_ = [("patience", ctypes.c_int32), ("min_L", ctypes.c_int32), ("peek_every", ctypes.c_int32),
+                ("tau", ctypes.c_float), ("logit_margin", ctypes.c_float)]
+
+
 ALLOC_FN = ctypes.CFUNCTYPE(ctypes.c_void_p, ctypes.c_size_t, ctypes.c_void_p)
 DEALLOC_FN = ctypes.CFUNCTYPE(None, ctypes.c_void_p, ctypes.c_void_p)
 
@@ -69,6 +74,7 @@ def lib():
                             ctypes.POINTER(_P)],
         "tl_forward": [_P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P],
         "tl_decode_step": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+        "tl_decode_step_ee": [_P, _I, _P, _P, ctypes.POINTER(tl_early_exit), _P, _P, _P, _P, _P, _P],
         "tl_decode_run": [_P, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P],
         "tl_export_w4": [_P, _I, _I, _P, _P],
         "tl_lane_release": [_P, _I],
@@ -213,6 +219,19 @@ def tl_decode_step(model, lanes, per_lane_L, out_tokens, in_tokens=None, out_log
     _check(lib().tl_decode_step(model.handle, len(ln), _ptr(ln), _ptr(pl), _ptr(in_tokens), _ptr(out_tokens),
                                 _ptr(out_logits), _ptr(out_hidden), _ptr(eff), _ptr(out_active_log),
                                 _stream(stream)))
+    return eff
+
+
+def tl_decode_step_ee(model, lanes, per_lane_L, out_tokens, patience, min_L=2, tau=1e-3, peek_every=1,
+                      logit_margin=0.0, in_tokens=None, out_logits=None, out_hidden=None, stream=None):
+    """Decode step with the device-side early-exit rule; returns the effective depths."""
+    ln = _i32(lanes)
+    pl = _i32(per_lane_L)
+    eff = np.zeros(len(ln), np.int32)
+    rule = tl_early_exit(int(patience), int(min_L), int(peek_every), float(tau), float(logit_margin))
+    _check(lib().tl_decode_step_ee(model.handle, len(ln), _ptr(ln), _ptr(pl), ctypes.byref(rule), _ptr(in_tokens),
+                                   _ptr(out_tokens), _ptr(out_logits), _ptr(out_hidden), _ptr(eff),
+                                   _stream(stream)))
     return eff
 
 

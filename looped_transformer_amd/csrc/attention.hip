@@ -41,7 +41,8 @@ __device__ __forceinline__ float dot_row(const float* __restrict__ q, const T* _
 template <class T>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, const RowInfo* __restrict__ rows,
                                                        int n, KVParams kv, T* __restrict__ out, int d,
-                                                       float scale) {
+                                                       float scale, const int32_t* live) {
+  if (live && *live <= 0) return;
   __shared__ float qs[4][128];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = kv.H, dh = kv.dh;
@@ -49,6 +50,10 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   if (item >= n * H) return;            // whole wave leaves together
   const int r = item / H, h = item - (item / H) * H;
   const RowInfo ri = rows[r];
+  if (ri.done) {   // finished by early exit: carried only, its state no longer matters
+    for (int i = lane; i < dh; i += 64) out[(int64_t)r * d + h * dh + i] = from_f32<T>(0.f);
+    return;
+  }
   const T* Kp = kv_ptr<T>(kv, ri, 0, h, 0);
   const T* Vp = kv_ptr<T>(kv, ri, 1, h, 0);
   float* qw = qs[wv];
@@ -305,7 +310,7 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
 }
 
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
-                            hipStream_t s) {
+                            const int32_t* live, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   const int d = kv.H * kv.dh;
   const float scale = 1.0f / sqrtf((float)kv.dh);
@@ -313,14 +318,14 @@ hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n
   switch (dtype) {
     case DT_F32:
       hipLaunchKernelGGL(attn_rows_kernel<float>, grid, dim3(256), 0, s, (const float*)q, rows, n, kv, (float*)out, d,
-                         scale);
+                         scale, live);
       break;
     case DT_F16:
-      hipLaunchKernelGGL(attn_rows_kernel<f16>, grid, dim3(256), 0, s, (const f16*)q, rows, n, kv, (f16*)out, d, scale);
+      hipLaunchKernelGGL(attn_rows_kernel<f16>, grid, dim3(256), 0, s, (const f16*)q, rows, n, kv, (f16*)out, d, scale, live);
       break;
     case DT_BF16:
       hipLaunchKernelGGL(attn_rows_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)q, rows, n, kv, (bf16*)out, d,
-                         scale);
+                         scale, live);
       break;
     default:
       return hipErrorInvalidValue;

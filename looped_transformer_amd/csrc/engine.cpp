@@ -225,6 +225,7 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
   g.Bs = W.s4;
   g.partial = m->ws.splitk;
   g.partial_cap = kSplitFloats;
+  g.live = m->gate_live;
   e.pair_g = m->G;
   HIPCHK(launch_gemm(m->act, g, e, s));
   return TL_OK;
@@ -256,7 +257,7 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   e.dh = c.head_dim;
   TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s)));
   if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, kv, w.o16, s)));
-  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, s)));
+  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, m->gate_live, s)));
   GemmEpi r{};
   r.kind = EPI_RESID;
   r.h = h;
@@ -288,12 +289,27 @@ struct Pass {
   // iteration 1's list covers every row in caller order (pre and post blocks too)
   std::vector<const AttnTile*> tiles;
   std::vector<int> n_tiles;
+  // early exit (decode steps): rule, or NULL
+  const tl_early_exit* ee = nullptr;
 };
+
+tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out, float* logits, int32_t* out_tok,
+                   const int32_t* pend_lanes, hipStream_t s);
+
+// Iteration j is probed by the early-exit rule (never the last one: it could not
+// shorten the loop).
+bool ee_probed(const tl_early_exit* ee, int j, int Lmax) {
+  return ee && ee->patience > 0 && j < Lmax && j >= ee->min_L && (j - ee->min_L) % ee->peek_every == 0;
+}
 
 // Pre blocks on all rows; loop iteration j on the n_j rows still active, each
 // application writing its own cache slot; rows leave (compaction) only after an
 // iteration that is the last one of some row; post blocks on all rows.
 tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
+  struct GateReset {
+    tl_model* m;
+    ~GateReset() { m->gate_live = nullptr; }
+  } gate_reset{m};
   const tl_config& c = m->cfg;
   auto& w = m->ws;
   const int d = c.d_model;
@@ -320,23 +336,43 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   int flip = 0;
   int64_t log_off = 0;
   bool moved = true;
+  if (p.ee) {
+    m->gate_live = m->ee_live;
+    // the probe marks rows in the loop's row list: keep the caller-order list the
+    // post blocks use untouched
+    HIPCHK(hipMemcpyAsync(rbuf[1], rows, (size_t)p.n * sizeof(RowInfo), hipMemcpyDeviceToDevice, s));
+    rows = rbuf[1];
+  }
   for (int j = 1; j <= Lmax; ++j) {
     const int nj = p.n_active[j - 1];
     if (p.log && moved) HIPCHK(launch_write_orig(rows, nj, p.log + log_off, s));
     const int next = j < Lmax ? p.n_active[j] : 0;
     const bool leaving = next < nj;
+    const bool probe = ee_probed(p.ee, j, Lmax);
+    const bool by_margin = probe && p.ee->logit_margin > 0.f;
+    if (probe && !by_margin) HIPCHK(hipMemcpyAsync(m->ee_hprev, h, (size_t)nj * d * 4, hipMemcpyDeviceToDevice, s));
     for (int l = 0; l < c.n_loop; ++l) {
       kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + (j - 1) * c.n_loop + l;
-      const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1 : (leaving ? nullptr : loop_first());
+      // a probe may finish rows, so the next iteration normalises its own input
+      const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1
+                                         : ((leaving || probe) ? nullptr : loop_first());
       TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
                     tiled ? p.n_tiles[j - 1] : 0, x_ready, nn));
       x_ready = nn != nullptr;
+    }
+    if (probe) {
+      if (by_margin) {
+        TRY(run_head(m, h, nullptr, nj, m->ee_logits, nullptr, nullptr, s));
+        HIPCHK(launch_top2_margin(m->ee_logits, nj, c.vocab, m->ee_margin, s));
+      }
+      HIPCHK(launch_ee_probe(const_cast<RowInfo*>(rows), nj, j, h, m->ee_hprev, by_margin ? m->ee_margin : nullptr,
+                             p.ee->tau, p.ee->logit_margin, p.ee->patience, d, p.final_h, m->ee_eff, m->ee_live, s));
     }
     moved = leaving;
     if (moved) {
       RowInfo* rout = rbuf[flip];
       int32_t* logn = p.log ? p.log + log_off + nj : nullptr;
-      TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rows, nj, j, rout, w.dest, w.count, logn, s));
+      TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rows, nj, j, rout, w.dest, w.count, logn, p.ee ? m->ee_live : nullptr, s));
                           HIPCHK(launch_move_rows(h, w.dest, rows, nj, d, hn, p.final_h, s)));
       rows = rout;
       flip ^= 1;
@@ -347,6 +383,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     }
     log_off += nj;
   }
+  m->gate_live = nullptr;
   x_ready = false;
   for (int b = 0; b < c.n_post; ++b) {
     kv.s0 = p.scoring ? 0 : c.n_pre + b;
@@ -738,6 +775,7 @@ void tl_free(tl_model* m) {
   for (auto& kv : m->owned) ps.push_back(kv.first);
   for (void* p : ps) dev_free(m, p);
   if (m->stage_host) (void)hipHostFree(m->stage_host);
+  if (m->ee_eff_host) (void)hipHostFree(m->ee_eff_host);
   if (m->stage_done) (void)hipEventDestroy(m->stage_done);
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   delete m;
@@ -1037,6 +1075,104 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
   return TL_OK;
 }
 
+// Early-exit buffers for n rows (logits only for the logit-margin rule).
+tl_status ensure_ee(tl_model* m, int n, bool logits, hipStream_t s) {
+  const tl_config& c = m->cfg;
+  if (n > m->ee_rows) {
+    HIPCHK(hipStreamSynchronize(s));
+    dev_free(m, m->ee_eff);
+    dev_free(m, m->ee_hprev);
+    dev_free(m, m->ee_margin);
+    if (!m->ee_live) m->ee_live = static_cast<int32_t*>(dev_alloc(m, 256));
+    const int R = (n + 63) / 64 * 64;
+    m->ee_eff = static_cast<int32_t*>(dev_alloc(m, (size_t)R * 4));
+    m->ee_hprev = static_cast<float*>(dev_alloc(m, (size_t)R * c.d_model * 4));
+    m->ee_margin = static_cast<float*>(dev_alloc(m, (size_t)R * 4));
+    if (m->ee_eff_host) HIPCHK(hipHostFree(m->ee_eff_host));
+    m->ee_eff_host = nullptr;
+    HIPCHK(hipHostMalloc((void**)&m->ee_eff_host, (size_t)R * 4, hipHostMallocDefault));
+    m->ee_rows = (m->ee_live && m->ee_eff && m->ee_hprev && m->ee_margin) ? R : 0;
+    if (!m->ee_rows) return fail(TL_E_OOM, "early-exit buffers for %d rows", n);
+  }
+  if (logits && n > m->ee_logit_rows) {
+    HIPCHK(hipStreamSynchronize(s));
+    dev_free(m, m->ee_logits);
+    const int R = (n + 63) / 64 * 64;
+    m->ee_logits = static_cast<float*>(dev_alloc(m, (size_t)R * c.vocab * 4));
+    m->ee_logit_rows = m->ee_logits ? R : 0;
+    if (!m->ee_logits) return fail(TL_E_OOM, "early-exit logits for %d rows", n);
+  }
+  return TL_OK;
+}
+
+tl_status tl_decode_step_ee(tl_model* m, int32_t n, const int32_t* lanes, const int32_t* req_L,
+                            const tl_early_exit* ee, const int32_t* in_tokens, int32_t* out_tokens,
+                            float* out_logits, float* out_hidden, int32_t* out_eff_L, void* stream) {
+  g_err.clear();
+  if (!m || !lanes || !req_L || !out_tokens || !ee) return fail(TL_E_ARG, "NULL argument");
+  if (ee->patience < 0 || ee->min_L < 1 || ee->peek_every < 1 || !(ee->tau >= 0.f) || !(ee->logit_margin >= 0.f))
+    return fail(TL_E_ARG, "early-exit rule: patience >= 0, min_L >= 1, peek_every >= 1, tau >= 0, logit_margin >= 0");
+  const tl_config& c = m->cfg;
+  if (n < 1) return fail(TL_E_ARG, "n_lanes must be >= 1");
+  std::vector<char> seen(c.max_lanes, 0);
+  std::vector<int> eff(n);
+  for (int i = 0; i < n; ++i) {
+    const int l = lanes[i];
+    if (l < 0 || l >= c.max_lanes) return fail(TL_E_ARG, "lane %d out of range [0, %d)", l, c.max_lanes);
+    if (seen[l]) return fail(TL_E_ARG, "lane %d listed twice", l);
+    seen[l] = 1;
+    if (req_L[i] < 1) return fail(TL_E_ARG, "requested L %d < 1", req_L[i]);
+    const Lane& ln = m->lanes[l];
+    if (!ln.live) return fail(TL_E_STATE, "lane %d was never prefilled", l);
+    if (ln.len >= ln.cap) return fail(TL_E_STATE, "lane %d is full (%d positions)", l, ln.cap);
+    eff[i] = std::min(req_L[i], ln.ceiling);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(ensure_ws(m, n, n, 0, s));
+  TRY(ensure_ee(m, n, ee->logit_margin > 0.f, s));
+  std::vector<RowInfo> rows(n);
+  std::vector<int32_t> lane_ids(lanes, lanes + n), eff32(eff.begin(), eff.end()), live0(1, n);
+  for (int i = 0; i < n; ++i) {
+    rows[i] = RowInfo{};
+    rows[i].orig = i;
+    rows[i].lane = lanes[i];
+    rows[i].pos = m->lanes[lanes[i]].len;
+    rows[i].depth = eff[i];
+    rows[i].iter = 1;
+  }
+  Stage st;
+  const size_t o_rows = st.add(rows), o_lanes = st.add(lane_ids), o_eff = st.add(eff32), o_live = st.add(live0);
+  TRY(stage_upload(m, st, s));
+  HIPCHK(hipMemcpyAsync(m->ee_eff, staged<int32_t>(m, o_eff), (size_t)n * 4, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(m->ee_live, staged<int32_t>(m, o_live), 4, hipMemcpyDeviceToDevice, s));
+  const int32_t* lanes_dev = staged<int32_t>(m, o_lanes);
+  const int32_t* toks = in_tokens;
+  if (!toks) {
+    HIPCHK(launch_gather_i32(m->d_pending, lanes_dev, n, m->ws.tok, s));
+    toks = m->ws.tok;
+  }
+  Pass p;
+  p.n = n;
+  p.tokens = toks;
+  p.rows0 = staged<RowInfo>(m, o_rows);
+  p.n_active = active_counts(eff);
+  p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
+  p.final_h = out_hidden ? out_hidden : m->ws.hX;
+  p.ee = ee;
+  TRY(run_pass(m, p, s));
+  TRY(run_head(m, p.final_h, nullptr, n, out_logits, out_tokens, lanes_dev, s));
+  HIPCHK(hipMemcpyAsync(m->ee_eff_host, m->ee_eff, (size_t)n * 4, hipMemcpyDeviceToHost, s));
+  HIPCHK(hipStreamSynchronize(s));
+  for (int i = 0; i < n; ++i) {
+    Lane& ln = m->lanes[lanes[i]];
+    const int e = m->ee_eff_host[i];
+    ln.len += 1;
+    ln.ceiling = e;
+    if (out_eff_L) out_eff_L[i] = e;
+  }
+  return TL_OK;
+}
+
 tl_status tl_export_w4(tl_model* m, int32_t block, int32_t matrix, int8_t* q_host, uint16_t* s_host) {
   g_err.clear();
   if (!m || !q_host || !s_host) return fail(TL_E_ARG, "NULL argument");
@@ -1254,7 +1390,7 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
         kv.s1 = c.n_loop;
         TRY(run_block(m, c.n_pre + l, hcur, rcur, npool, kv, s));
       }
-      TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rcur, npool, 0, rnxt, w.dest, w.count, nullptr, s));
+      TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rcur, npool, 0, rnxt, w.dest, w.count, nullptr, nullptr, s));
                           HIPCHK(launch_move_rows(hcur, w.dest, rcur, npool, d, hnxt, w.hX, s)));
       std::swap(hcur, hnxt);
       std::swap(rcur, rnxt);

@@ -116,6 +116,15 @@ struct tl_model {
   std::vector<tl::GraphEntry> graphs;
   uint64_t graph_clock = 0;
   void* stage_override = nullptr;      // descriptor base while capturing a graph
+  // early exit of decode steps (allocated on first use)
+  const int32_t* gate_live = nullptr;  // set while the loop of an early-exit step runs
+  int32_t* ee_live = nullptr;          // rows still running
+  int32_t* ee_eff = nullptr;           // [ee_rows] effective depth by caller order
+  float* ee_hprev = nullptr;           // [ee_rows, d] residual before a probed iteration
+  float* ee_margin = nullptr;          // [ee_rows]
+  float* ee_logits = nullptr;          // [ee_logit_rows, V]
+  int32_t* ee_eff_host = nullptr;      // pinned mirror of ee_eff
+  int ee_rows = 0, ee_logit_rows = 0;
   // kernel-class timing (measurement only)
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;

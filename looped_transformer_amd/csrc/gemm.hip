@@ -53,6 +53,7 @@ __device__ __forceinline__ void epi_pair(const GemmEpi& e, int r, int c, float v
     const int head = cc / dh;
     const int cd = cc - head * dh;
     const RowInfo ri = e.rows[r];
+    if (ri.done) return;   // finished by early exit: its later cache slots stay unwritten
     if (sect == 2) {
       AT* vp = kv_ptr<AT>(e.kv, ri, 1, head, ri.pos);
       vp[cd] = from_f32<AT>(v0);
@@ -109,6 +110,7 @@ __device__ __forceinline__ void best_merge(float& v, int& i, float v2, int i2) {
 // fp32 partial tile and splitk_epilogue_kernel finishes the tile.
 template <class AT, bool W4, int BM, int BN, int BK, int D, int KIND>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e, int kchunk) {
+  if (g.live && *g.live <= 0) return;
   constexpr int LDK = BK + 8;   // padded LDS row, elements
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -414,6 +416,7 @@ __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
 // double-buffered, one barrier per stage.
 template <int BM, int WNB, int D, int KIND>
 __global__ __launch_bounds__(256) void gemm_skinny_w4_kernel(GemmArgs g, GemmEpi e, int kchunk) {
+  if (g.live && *g.live <= 0) return;
   constexpr int RBW = BM / 32;           // 32-row blocks (every wave covers all rows)
   constexpr int WN = 32 * WNB;
   constexpr int BN = 4 * WN;
@@ -576,6 +579,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_w4_kernel(GemmArgs g, GemmEpi
 // Paired epilogues use adjacent column pairs (row-permutation granularity 1).
 template <int KIND>
 __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, GemmEpi e) {
+  if (g.live && *g.live <= 0) return;
   constexpr int BM = 64, BN = 64, BK = 16;
   __shared__ float As[BK][BM + 4];
   __shared__ float Bs[BK][BN + 4];
@@ -660,6 +664,7 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, GemmEpi e) {
 // G-chunk; the others one thread per (row, column).
 template <class AT, int KIND>
 __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEpi e, int S) {
+  if (g.live && *g.live <= 0) return;
   const int M = g.M, N = g.N;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if constexpr (paired(KIND)) {
@@ -693,6 +698,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
 // all requested before any is used, with SN == 0 a loop adds any number.
 template <class AT, int VPT, int SN>
 __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, GemmEpi e, int S) {
+  if (g.live && *g.live <= 0) return;
   const int row = blockIdx.x, N = g.N, M = g.M;
   float* hr = e.h + (int64_t)row * e.ldh;
   const floatx4* P = reinterpret_cast<const floatx4*>(g.partial);

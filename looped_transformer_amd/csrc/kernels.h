@@ -8,9 +8,12 @@ enum DType : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_W4G128 = 3 };
 
 // One activation row of a pass.  orig: index of the row in the caller's order;
 // lane: KV lane table entry; pos: absolute position; depth: loop iterations the
-// row runs; iter: current loop iteration (1-based) of the row.
+// row runs; iter: current loop iteration (1-based) of the row.  done / streak:
+// early exit of a decode step (done: the row finished at an earlier probe and is
+// only carried until the planned compaction drops it; streak: consecutive
+// stable probes so far); both 0 elsewhere.
 struct RowInfo {
-  int32_t orig, lane, pos, depth, iter, tok_slot, p1, p2;
+  int32_t orig, lane, pos, depth, iter, tok_slot, done, streak;
 };
 
 // KV cache addressing: slot of a block application for a row = s0 + s1 * row.iter.
@@ -32,6 +35,9 @@ struct GemmArgs {
   // split-K workspace: fp32 partial tiles [splits][M][N]
   float* partial;
   int64_t partial_cap;    // floats
+  // device count of rows still running (early exit), or NULL: when it reads 0 the
+  // kernels return at once
+  const int32_t* live;
 };
 
 struct GemmEpi {
@@ -73,8 +79,9 @@ hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, 
                         int32_t* err_flag, int vocab, hipStream_t s);
 hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const int32_t* gather, int n,
                           int d, float eps, void* out, hipStream_t s);
+// live: as GemmArgs::live (NULL: always run).  Rows marked done get a zero output.
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv,
-                            void* out, hipStream_t s);
+                            void* out, const int32_t* live, hipStream_t s);
 // A run of up to attn_tile_rows() consecutive rows of one sequence (positions pos0 .. pos0+nrows-1)
 // that attend to positions 0 .. pos0+nrows-1 of their lane's slot.
 struct AttnTile {
@@ -90,13 +97,25 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
 // Stable filter of the active rows after iteration it (it = 0: each row's own
 // iter): rows with depth > it stay (their iter becomes it + 1), the others leave.
 // dest[i] = new index or -1.  count_out[0] = number kept.  If log_out is non-NULL
-// the kept rows' orig indices are written there.
+// the kept rows' orig indices are written there; if running_out is non-NULL it
+// receives the number of kept rows not marked done.
 hipError_t launch_compact(const RowInfo* rows_in, int n, int it, RowInfo* rows_out, int32_t* dest,
-                          int32_t* count_out, int32_t* log_out, hipStream_t s);
-// h_next[dest[i]] = h[i] for kept rows; h_exit[rows[i].orig] = h[i] for leaving rows.
+                          int32_t* count_out, int32_t* log_out, int32_t* running_out, hipStream_t s);
+// h_next[dest[i]] = h[i] for kept rows; h_exit[rows[i].orig] = h[i] for leaving rows
+// (not for rows marked done: their exit state was stored when they finished).
 hipError_t launch_move_rows(const float* h, const int32_t* dest, const RowInfo* rows, int n, int d,
                             float* h_next, float* h_exit, hipStream_t s);
 hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream_t s);
+// Early-exit probe after loop iteration it on n rows (one wave per row): rows not
+// done are stable when margin[i] > margin_thr (margin != NULL) or when
+// ||h_i - h_prev_i|| / ||h_i|| < tau; streak counts consecutive stable probes and
+// resets otherwise; at streak >= patience the row is marked done, its state goes to
+// h_exit[orig], eff_depth[orig] = it and *live is decremented.
+hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, const float* h_prev,
+                           const float* margin, float tau, float margin_thr, int patience, int d,
+                           float* h_exit, int32_t* eff_depth, int32_t* live, hipStream_t s);
+// margin[i] = largest minus second largest of logits row i (equal values give 0).
+hipError_t launch_top2_margin(const float* logits, int n, int V, float* margin, hipStream_t s);
 hipError_t launch_argmax_reduce(const float* part_val, const int32_t* part_idx, int n, int n_tiles,
                                 int32_t* out_tok, int32_t* out_tok2, const int32_t* scatter, hipStream_t s);
 hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);

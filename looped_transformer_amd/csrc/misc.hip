@@ -57,11 +57,14 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
 // Stable filter in one workgroup: chunks of 1024 rows, wave ballots + prefix.
 __global__ __launch_bounds__(1024) void compact_kernel(const RowInfo* __restrict__ in, int n, int it,
                                                       RowInfo* __restrict__ out, int32_t* __restrict__ dest,
-                                                      int32_t* count_out, int32_t* log_out) {
-  __shared__ int wave_cnt[16];
-  __shared__ int base_s;
+                                                      int32_t* count_out, int32_t* log_out, int32_t* running_out) {
+  __shared__ int wave_cnt[16], wave_run[16];
+  __shared__ int base_s, run_s;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  if (threadIdx.x == 0) base_s = 0;
+  if (threadIdx.x == 0) {
+    base_s = 0;
+    run_s = 0;
+  }
   __syncthreads();
   for (int c0 = 0; c0 < n; c0 += 1024) {
     const int i = c0 + threadIdx.x;
@@ -73,8 +76,12 @@ __global__ __launch_bounds__(1024) void compact_kernel(const RowInfo* __restrict
       keep = ri.depth > ri.iter;
     }
     const uint64_t mask = __ballot(keep);
+    const uint64_t run_mask = __ballot(keep && !ri.done);
     const int before = __popcll(mask & ((1ull << lane) - 1ull));
-    if (lane == 0) wave_cnt[w] = __popcll(mask);
+    if (lane == 0) {
+      wave_cnt[w] = __popcll(mask);
+      wave_run[w] = __popcll(run_mask);
+    }
     __syncthreads();
     int off = base_s;
     for (int k = 0; k < w; ++k) off += wave_cnt[k];
@@ -91,13 +98,18 @@ __global__ __launch_bounds__(1024) void compact_kernel(const RowInfo* __restrict
     }
     __syncthreads();
     if (threadIdx.x == 0) {
-      int tot = 0;
-      for (int k = 0; k < 16; ++k) tot += wave_cnt[k];
+      int tot = 0, run = 0;
+      for (int k = 0; k < 16; ++k) {
+        tot += wave_cnt[k];
+        run += wave_run[k];
+      }
       base_s += tot;
+      run_s += run;
     }
     __syncthreads();
   }
   if (threadIdx.x == 0 && count_out) *count_out = base_s;
+  if (threadIdx.x == 0 && running_out) *running_out = run_s;
 }
 
 __global__ __launch_bounds__(256) void move_rows_kernel(const float* __restrict__ h, const int32_t* __restrict__ dest,
@@ -105,6 +117,7 @@ __global__ __launch_bounds__(256) void move_rows_kernel(const float* __restrict_
                                                        float* __restrict__ h_next, float* __restrict__ h_exit) {
   const int i = blockIdx.x;
   const int di = dest[i];
+  if (di < 0 && rows[i].done) return;   // exit state already stored by the early-exit probe
   float* dst = di >= 0 ? h_next + (int64_t)di * d : h_exit + (int64_t)rows[i].orig * d;
   const float* src = h + (int64_t)i * d;
   for (int c = threadIdx.x * 4; c < d; c += 1024) *reinterpret_cast<float4*>(dst + c) = *reinterpret_cast<const float4*>(src + c);
@@ -113,6 +126,77 @@ __global__ __launch_bounds__(256) void move_rows_kernel(const float* __restrict_
 __global__ void write_orig_kernel(const RowInfo* rows, int n, int32_t* out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) out[i] = rows[i].orig;
+}
+
+// ---------------------------------------------------------------- early exit
+// One wave per row: relative L2 change (or a precomputed logit margin) decides a
+// stable probe; patience consecutive stable probes finish the row.
+__global__ __launch_bounds__(256) void ee_probe_kernel(RowInfo* __restrict__ rows, int n, int it,
+                                                      const float* __restrict__ h, const float* __restrict__ h_prev,
+                                                      const float* __restrict__ margin, float tau, float margin_thr,
+                                                      int patience, int d, float* __restrict__ h_exit,
+                                                      int32_t* __restrict__ eff_depth, int32_t* live) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= n) return;
+  RowInfo ri = rows[r];
+  if (ri.done) return;
+  const float* hr = h + (int64_t)r * d;
+  bool stable;
+  if (margin) {
+    stable = margin[r] > margin_thr;
+  } else {
+    const float* pr = h_prev + (int64_t)r * d;
+    float dd = 0.f, hh = 0.f;
+    for (int c = lane; c < d; c += 64) {
+      const float a = hr[c], b = a - pr[c];
+      dd = fmaf(b, b, dd);
+      hh = fmaf(a, a, hh);
+    }
+    dd = wave_sum(dd);
+    hh = wave_sum(hh);
+    stable = sqrtf(dd) < tau * sqrtf(hh);
+  }
+  const int streak = stable ? ri.streak + 1 : 0;
+  const bool fin = streak >= patience;
+  if (fin) {
+    float* dst = h_exit + (int64_t)ri.orig * d;
+    for (int c = lane; c < d; c += 64) dst[c] = hr[c];
+  }
+  if (lane == 0) {
+    rows[r].streak = streak;
+    if (fin) {
+      rows[r].done = 1;
+      eff_depth[ri.orig] = it;
+      atomicSub(live, 1);
+    }
+  }
+}
+
+// One wave per row: the two largest logits (lane-local pairs merged across the wave).
+__global__ __launch_bounds__(256) void top2_margin_kernel(const float* __restrict__ logits, int n, int V,
+                                                         float* __restrict__ margin) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= n) return;
+  const float* lr = logits + (int64_t)r * V;
+  float a = -INFINITY, b = -INFINITY;   // a >= b
+  for (int c = lane; c < V; c += 64) {
+    const float v = lr[c];
+    if (v > a) {
+      b = a;
+      a = v;
+    } else if (v > b) {
+      b = v;
+    }
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) {
+    const float a2 = __shfl_xor(a, o, 64), b2 = __shfl_xor(b, o, 64);
+    const float na = fmaxf(a, a2);
+    const float nb = a >= a2 ? fmaxf(b, a2) : fmaxf(b2, a);
+    a = na;
+    b = nb;
+  }
+  if (lane == 0) margin[r] = a - b;
 }
 
 // ---------------------------------------------------------------- greedy token
@@ -273,9 +357,9 @@ hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const i
 }
 
 hipError_t launch_compact(const RowInfo* rows_in, int n, int it, RowInfo* rows_out, int32_t* dest, int32_t* count_out,
-                          int32_t* log_out, hipStream_t s) {
+                          int32_t* log_out, int32_t* running_out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, rows_in, n, it, rows_out, dest, count_out, log_out);
+  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, rows_in, n, it, rows_out, dest, count_out, log_out, running_out);
   return hipGetLastError();
 }
 
@@ -289,6 +373,21 @@ hipError_t launch_move_rows(const float* h, const int32_t* dest, const RowInfo* 
 hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(write_orig_kernel, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, const float* h_prev, const float* margin,
+                           float tau, float margin_thr, int patience, int d, float* h_exit, int32_t* eff_depth,
+                           int32_t* live, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(ee_probe_kernel, dim3((n + 3) / 4), dim3(256), 0, s, rows, n, it, h, h_prev, margin, tau,
+                     margin_thr, patience, d, h_exit, eff_depth, live);
+  return hipGetLastError();
+}
+
+hipError_t launch_top2_margin(const float* logits, int n, int V, float* margin, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(top2_margin_kernel, dim3((n + 3) / 4), dim3(256), 0, s, logits, n, V, margin);
   return hipGetLastError();
 }
 

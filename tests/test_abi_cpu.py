@@ -38,6 +38,7 @@ def test_null_arguments_rejected(L):
     assert L.tl_forward(None, 1, None, None, 1, None, None, 0, None, None, None, None, None) == tl.TL_E_ARG
     assert L.tl_decode_step(None, 1, None, None, None, None, None, None, None, None, None) == tl.TL_E_ARG
     assert L.tl_decode_run(None, 1, None, 1, None, None, None, None, None, 1, None) == tl.TL_E_ARG
+    assert L.tl_decode_step_ee(None, 1, None, None, None, None, None, None, None, None, None) == tl.TL_E_ARG
     assert L.tl_lane_release(None, 0) == tl.TL_E_ARG
 
 
