@@ -174,7 +174,8 @@ def main():
 
 
 def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
-    """32 lanes, 32-token prompts, greedy cached decode at L = 8 on the FP16-body model."""
+    """32 lanes, 32-token prompts, greedy cached decode at L = 8 on the FP16-body model;
+    the same run with the device-side early-exit rule at three settings."""
     spec = synth.SPECS[3]
     log("decode: FP16-body model")
     w = synth.make_weights(spec, 0)
@@ -186,20 +187,38 @@ def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
     lanes = np.arange(n, dtype=np.int32)
     out = torch.empty(n, dtype=torch.int32, device="cuda")
     Ls = np.full(n, 8, np.int32)
-    times = []
-    for rep in range(3):
-        tl.tl_forward(model, cu, toks, L=8, lanes=lanes, max_new_tokens=new)
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(new - 1):
-            tl.tl_decode_step(model, lanes, Ls, out)
-        torch.cuda.synchronize()
-        times.append(time.perf_counter() - t0)
+
+    def run(step):
+        times, depth = [], 0
+        for rep in range(3):
+            tl.tl_forward(model, cu, toks, L=8, lanes=lanes, max_new_tokens=new)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            tot = 0
+            for _ in range(new - 1):
+                tot += int(np.sum(step()))
+            torch.cuda.synchronize()
+            times.append(time.perf_counter() - t0)
+            depth = tot / (n * (new - 1))
+        best = min(times)
+        return {"tok_per_s": round(n * (new - 1) / best, 1), "ms_per_step": round(best / (new - 1) * 1e3, 4),
+                "mean_depth": round(depth, 3)}
+
+    res = run(lambda: tl.tl_decode_step(model, lanes, Ls, out))
+    res["config"] = ("FP16-body loop block, 32 lanes, 32-token prompts, 31 cached greedy steps at L=8 "
+                     "(first token comes from the prefill)")
+    ee = {
+        # relative-L2 rule that never fires: the cost of probing every iteration from 2 on
+        "hidden_rule_never_fires": dict(patience=1, min_L=2, tau=0.0),
+        # the pages' logit-margin setting (margin 3, patience 1, peek every 2, min L 4)
+        "margin3_patience1_peek2_minL4": dict(patience=1, min_L=4, peek_every=2, logit_margin=3.0),
+        # every token finishes at iteration 4: iterations 5..8 run gated kernels only
+        "all_finish_at_4": dict(patience=1, min_L=4, tau=1e30),
+    }
+    res["early_exit"] = {k: run(lambda kw=kw: tl.tl_decode_step_ee(model, lanes, Ls, out, **kw))
+                         for k, kw in ee.items()}
     tl.tl_free(model)
-    best = min(times)
-    return {"tok_per_s": round(n * (new - 1) / best, 1), "ms_per_step": round(best / (new - 1) * 1e3, 4),
-            "config": "FP16-body loop block, 32 lanes, 32-token prompts, 31 cached greedy steps at L=8 "
-                      "(first token comes from the prefill)"}
+    return res
 
 
 if __name__ == "__main__":

@@ -42,7 +42,6 @@ template <class T>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, const RowInfo* __restrict__ rows,
                                                        int n, KVParams kv, T* __restrict__ out, int d,
                                                        float scale, const int32_t* live) {
-  if (live && *live <= 0) return;
   __shared__ float qs[4][128];
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
   const int H = kv.H, dh = kv.dh;
@@ -50,6 +49,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   if (item >= n * H) return;            // whole wave leaves together
   const int r = item / H, h = item - (item / H) * H;
   const RowInfo ri = rows[r];
+  if (gate_closed(live)) return;
   if (ri.done) {   // finished by early exit: carried only, its state no longer matters
     for (int i = lane; i < dh; i += 64) out[(int64_t)r * d + h * dh + i] = from_f32<T>(0.f);
     return;

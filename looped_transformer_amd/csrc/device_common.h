@@ -70,3 +70,13 @@ __device__ __forceinline__ half2v w4_pair(uint32_t w, int i) {
   const half2v off = {(f16)1032.0f, (f16)1032.0f};
   return h - off;
 }
+
+// Early-exit gate: true when the pass has no live row left (every row finished).
+// Kernels read it once their first loads are in flight, so its latency overlaps
+// theirs instead of delaying every other argument load; the barrier keeps those
+// loads from being sunk below the test.  A wave that returns here with loads in
+// flight is fine: the end of the program waits for them.
+__device__ __forceinline__ bool gate_closed(const int32_t* live) {
+  asm volatile("" ::: "memory");
+  return live && *live <= 0;
+}

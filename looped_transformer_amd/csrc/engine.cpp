@@ -255,6 +255,7 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   e.d = c.d_model;
   e.H = c.n_heads;
   e.dh = c.head_dim;
+  e.skip_done = m->gate_live != nullptr;
   TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s)));
   if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, kv, w.o16, s)));
   else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, m->gate_live, s)));
@@ -353,9 +354,9 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     if (probe && !by_margin) HIPCHK(hipMemcpyAsync(m->ee_hprev, h, (size_t)nj * d * 4, hipMemcpyDeviceToDevice, s));
     for (int l = 0; l < c.n_loop; ++l) {
       kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + (j - 1) * c.n_loop + l;
-      // a probe may finish rows, so the next iteration normalises its own input
-      const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1
-                                         : ((leaving || probe) ? nullptr : loop_first());
+      // (a probe leaves the next iteration's normalised input alone: the logit
+      // probe normalises into its own buffer, rows it finishes are only carried)
+      const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1 : (leaving ? nullptr : loop_first());
       TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
                     tiled ? p.n_tiles[j - 1] : 0, x_ready, nn));
       x_ready = nn != nullptr;

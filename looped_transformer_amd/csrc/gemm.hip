@@ -53,7 +53,7 @@ __device__ __forceinline__ void epi_pair(const GemmEpi& e, int r, int c, float v
     const int head = cc / dh;
     const int cd = cc - head * dh;
     const RowInfo ri = e.rows[r];
-    if (ri.done) return;   // finished by early exit: its later cache slots stay unwritten
+    if (e.skip_done && ri.done) return;   // finished by early exit: its later cache slots stay unwritten
     if (sect == 2) {
       AT* vp = kv_ptr<AT>(e.kv, ri, 1, head, ri.pos);
       vp[cd] = from_f32<AT>(v0);
@@ -110,7 +110,6 @@ __device__ __forceinline__ void best_merge(float& v, int& i, float v2, int i2) {
 // fp32 partial tile and splitk_epilogue_kernel finishes the tile.
 template <class AT, bool W4, int BM, int BN, int BK, int D, int KIND>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e, int kchunk) {
-  if (g.live && *g.live <= 0) return;
   constexpr int LDK = BK + 8;   // padded LDS row, elements
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -288,6 +287,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   const int nst = ((ke - kb + BK - 1) / BK + D - 1) / D * D;
 #pragma unroll
   for (int u = 0; u < D - 1; ++u) gload(ra_[u], rb_[u], rs_[u], okA_[u], okB_[u], kb + u * BK);
+  if (gate_closed(g.live)) return;
   for (int s0 = 0; s0 < nst; s0 += D) {
     static_for<0, D>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
@@ -416,7 +416,6 @@ __device__ __forceinline__ floatx16 mfma32(half8 a, half8 b, floatx16 c) {
 // double-buffered, one barrier per stage.
 template <int BM, int WNB, int D, int KIND>
 __global__ __launch_bounds__(256) void gemm_skinny_w4_kernel(GemmArgs g, GemmEpi e, int kchunk) {
-  if (g.live && *g.live <= 0) return;
   constexpr int RBW = BM / 32;           // 32-row blocks (every wave covers all rows)
   constexpr int WN = 32 * WNB;
   constexpr int BN = 4 * WN;
@@ -521,6 +520,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_w4_kernel(GemmArgs g, GemmEpi
   };
 
   static_for<0, D - 1>([&](auto uc) __attribute__((always_inline)) { gload(uc, decltype(uc)::value); });
+  if (gate_closed(g.live)) return;
   for (int s0 = 0; s0 < nst; s0 += D) {
     static_for<0, D>([&](auto uc) __attribute__((always_inline)) {
       constexpr int u = decltype(uc)::value;
@@ -664,7 +664,6 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, GemmEpi e) {
 // G-chunk; the others one thread per (row, column).
 template <class AT, int KIND>
 __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEpi e, int S) {
-  if (g.live && *g.live <= 0) return;
   const int M = g.M, N = g.N;
   const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if constexpr (paired(KIND)) {
@@ -680,6 +679,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
       v0 += pr[c];
       v1 += pr[c + G];
     }
+    if (gate_closed(g.live)) return;
     epi_pair<AT, KIND>(e, row, c, v0, v1);
   } else {
     if (idx >= (int64_t)M * N) return;
@@ -687,6 +687,7 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
     const int c = (int)(idx - (int64_t)row * N);
     float v = 0.f;
     for (int z = 0; z < S; ++z) v += g.partial[((int64_t)z * M + row) * N + c];
+    if (gate_closed(g.live)) return;
     epi_one<KIND>(e, row, c, v);
   }
 }
@@ -698,7 +699,6 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
 // all requested before any is used, with SN == 0 a loop adds any number.
 template <class AT, int VPT, int SN>
 __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, GemmEpi e, int S) {
-  if (g.live && *g.live <= 0) return;
   const int row = blockIdx.x, N = g.N, M = g.M;
   float* hr = e.h + (int64_t)row * e.ldh;
   const floatx4* P = reinterpret_cast<const floatx4*>(g.partial);
@@ -712,6 +712,7 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
     for (int z = 0; z < SN; ++z)
 #pragma unroll
       for (int u = 0; u < VPT; ++u) p[z][u] = P[z * zs + rs + min((int)threadIdx.x + 256 * u, N / 4 - 1)];
+    if (gate_closed(g.live)) return;
 #pragma unroll
     for (int z = 0; z < SN; ++z)
 #pragma unroll
@@ -719,6 +720,7 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
         acc[u] += p[z][u];
       }
   } else {
+    if (gate_closed(g.live)) return;
     for (int z = 0; z < S; ++z)
 #pragma unroll
       for (int u = 0; u < VPT; ++u) {

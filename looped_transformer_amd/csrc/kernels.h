@@ -50,6 +50,7 @@ struct GemmEpi {
   const float* rope_cos;   // [max_pos, dh/2]
   const float* rope_sin;
   int32_t d, H, dh;
+  int32_t skip_done;       // rows marked done (finished by early exit) write nothing
   // EPI_RESID: h[r, c] += acc; then, if norm_g is set, norm_out = RMSNorm(h) * norm_g
   // in the operand type (the next GEMM's input), fused with the split-K reduction
   float* h;
