@@ -4,93 +4,143 @@
 // positions).  Row r at position p attends to positions 0..p of its slot; scale
 // 1/sqrt(head_dim); one K/V head per query head.
 //
-// One wave per (row, head).  Keys are streamed in chunks of 64 (one key per lane
-// for the score), with a running max / sum (online softmax); the value sum keeps
-// two head dimensions per lane.  Serves prefill (rows of one sequence share the
-// slot) and decode (one row per lane) alike.
+// Rows (decode, or prefill where the tiled kernel does not apply): one workgroup
+// per (row, head), its four waves taking every fourth block of positions
+// (split over the keys, merged through LDS at the end).  Inside a wave a group of
+// lanes holds one key row, 16 bytes per lane, so each load instruction reads
+// several whole K (and V) rows; the K and V of a block are requested together.
+// The lanes that form a key's score also hold that key's V slice, so P V needs no
+// data exchange until the final merge.  Online softmax in fp32.  The tiled kernel
+// below serves prefill runs of consecutive rows.
 #include "device_common.h"
 
 namespace {
 
-template <class T> struct Vec8;
-template <> struct Vec8<f16> { typedef half8 type; };
-template <> struct Vec8<bf16> { typedef bf16x8 type; };
+template <class T> struct Row16;   // 16 bytes of a K/V row
+template <> struct Row16<f16> { typedef half8 type; };
+template <> struct Row16<bf16> { typedef bf16x8 type; };
+template <> struct Row16<float> { typedef floatx4 type; };
 
-template <class T>
-__device__ __forceinline__ float dot_row(const float* __restrict__ q, const T* __restrict__ k, int dh) {
-  float acc = 0.f;
-  if constexpr (sizeof(T) == 2) {
-    typedef typename Vec8<T>::type v8;
-    for (int i = 0; i < dh; i += 8) {
-      const v8 kv = *reinterpret_cast<const v8*>(k + i);
-#pragma unroll
-      for (int u = 0; u < 8; ++u) acc = fmaf(q[i + u], (float)kv[u], acc);
-    }
-  } else {
-    for (int i = 0; i < dh; i += 4) {
-      const float4 kv = *reinterpret_cast<const float4*>(k + i);
-      acc = fmaf(q[i], kv.x, acc);
-      acc = fmaf(q[i + 1], kv.y, acc);
-      acc = fmaf(q[i + 2], kv.z, acc);
-      acc = fmaf(q[i + 3], kv.w, acc);
-    }
-  }
-  return acc;
-}
-
-template <class T>
+// LPK lanes per key (a power of two >= head_dim / elements-per-16-bytes; lanes
+// past the row hold zeros), 64 / LPK keys per load instruction, U loads per lane
+// per block of P = (64 / LPK) * U positions.
+template <class T, int LPK>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, const RowInfo* __restrict__ rows,
-                                                       int n, KVParams kv, T* __restrict__ out, int d,
-                                                       float scale, const int32_t* live) {
-  __shared__ float qs[4][128];
-  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+                                                       KVParams kv, T* __restrict__ out, int d, float scale,
+                                                       const int32_t* live) {
+  typedef typename Row16<T>::type R16;
+  constexpr int EPL = 16 / (int)sizeof(T);   // elements per lane of a key row
+  constexpr int KPI = 64 / LPK;              // keys per load instruction
+  constexpr int U = LPK < 16 ? LPK : 16;
+  constexpr int P = KPI * U;                 // positions per block
   const int H = kv.H, dh = kv.dh;
-  const int item = blockIdx.x * 4 + wv;
-  if (item >= n * H) return;            // whole wave leaves together
-  const int r = item / H, h = item - (item / H) * H;
+  const int r = blockIdx.x / H, h = blockIdx.x - r * H;
+  const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+  const int g = lane / LPK, k = lane % LPK;   // key in the instruction, 16-byte chunk of the row
+  const bool kin = k * EPL < dh;
   const RowInfo ri = rows[r];
   if (gate_closed(live)) return;
+  T* op = out + (int64_t)r * d + h * dh;
   if (ri.done) {   // finished by early exit: carried only, its state no longer matters
-    for (int i = lane; i < dh; i += 64) out[(int64_t)r * d + h * dh + i] = from_f32<T>(0.f);
+    if (tid < 64 && kin) {
+      R16 z;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) z[e] = from_f32<T>(0.f);
+      if (g == 0) *reinterpret_cast<R16*>(op + k * EPL) = z;
+    }
     return;
   }
   const T* Kp = kv_ptr<T>(kv, ri, 0, h, 0);
   const T* Vp = kv_ptr<T>(kv, ri, 1, h, 0);
-  float* qw = qs[wv];
-  for (int i = lane; i < dh; i += 64) qw[i] = (float)q[(int64_t)r * d + h * dh + i] * scale;
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-
+  float qv[EPL];
+  {
+    R16 x{};
+    if (kin) x = *reinterpret_cast<const R16*>(q + (int64_t)r * d + h * dh + k * EPL);
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] = (float)x[e] * scale;
+  }
   const int npos = ri.pos + 1;
-  const bool own = 2 * lane < dh;
-  float m = -INFINITY, l = 0.f, o0 = 0.f, o1 = 0.f;
-  for (int t0 = 0; t0 < npos; t0 += 64) {
-    const int t = t0 + lane;
-    float s = -INFINITY;
-    if (t < npos) s = dot_row<T>(qw, Kp + (int64_t)t * dh, dh);
-    const float mn = fmaxf(m, wave_max(s));
-    const float p = (t < npos) ? expf(s - mn) : 0.f;
-    const float corr = expf(m - mn);
-    l = l * corr + wave_sum(p);
-    o0 *= corr;
-    o1 *= corr;
-    const int cnt = min(64, npos - t0);
-    for (int u = 0; u < cnt; ++u) {
-      const float pu = __shfl(p, u, 64);
-      if (own) {
-        const T* vr = Vp + (int64_t)(t0 + u) * dh + 2 * lane;
-        o0 = fmaf(pu, (float)vr[0], o0);
-        o1 = fmaf(pu, (float)vr[1], o1);
+  const int nblk = (npos + P - 1) / P;
+  float m = -INFINITY, l = 0.f, o[EPL];
+#pragma unroll
+  for (int e = 0; e < EPL; ++e) o[e] = 0.f;
+  for (int b = wv; b < nblk; b += 4) {
+    const int t0 = b * P;
+    R16 kr[U], vr[U];
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const int tc = min(t0 + u * KPI + g, npos - 1);   // clamped: masked below, V weighted by 0
+      kr[u] = R16{};
+      vr[u] = R16{};
+      if (kin) {
+        kr[u] = *reinterpret_cast<const R16*>(Kp + (int64_t)tc * dh + k * EPL);
+        vr[u] = *reinterpret_cast<const R16*>(Vp + (int64_t)tc * dh + k * EPL);
       }
     }
+    float sc[U], cm = -INFINITY;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      float a = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) a = fmaf(qv[e], (float)kr[u][e], a);
+#pragma unroll
+      for (int x = 1; x < LPK; x <<= 1) a += __shfl_xor(a, x, 64);
+      sc[u] = (t0 + u * KPI + g < npos) ? a : -INFINITY;
+      cm = fmaxf(cm, sc[u]);
+    }
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) cm = fmaxf(cm, __shfl_xor(cm, x, 64));
+    const float mn = fmaxf(m, cm);
+    const float corr = expf(m - mn);
+    float ls = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[e] *= corr;
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const float pu = expf(sc[u] - mn);
+      ls += pu;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[e] = fmaf(pu, (float)vr[u][e], o[e]);
+    }
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) ls += __shfl_xor(ls, x, 64);
+    l = l * corr + ls;
     m = mn;
   }
-  if (own) {
-    const float inv = 1.0f / l;
-    T* op = out + (int64_t)r * d + h * dh + 2 * lane;
-    op[0] = from_f32<T>(o0 * inv);
-    op[1] = from_f32<T>(o1 * inv);
+  // this wave's output: add the key groups' partial sums
+#pragma unroll
+  for (int e = 0; e < EPL; ++e)
+#pragma unroll
+    for (int x = LPK; x < 64; x <<= 1) o[e] += __shfl_xor(o[e], x, 64);
+  __shared__ float wm[4], wl[4];
+  __shared__ float wo[4][128];
+  if (lane == 0) {
+    wm[wv] = m;
+    wl[wv] = l;
+  }
+  if (g == 0 && kin) {
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) wo[wv][k * EPL + e] = o[e];
+  }
+  __syncthreads();
+  if (wv == 0 && g == 0 && kin) {
+    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));   // wave 0 always saw position 0
+    float f[4], L = 0.f;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      f[w] = expf(wm[w] - M);   // 0 for a wave without positions (m = -inf)
+      L += wl[w] * f[w];
+    }
+    const float inv = 1.0f / L;
+    R16 res;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) {
+      float acc = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) acc += wo[w][k * EPL + e] * f[w];
+      res[e] = from_f32<T>(acc * inv);
+    }
+    *reinterpret_cast<R16*>(op + k * EPL) = res;
   }
 }
 
@@ -309,26 +359,35 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
   return hipErrorInvalidValue;
 }
 
+template <class T, int LPK>
+void attn_rows_launch(const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out, const int32_t* live,
+                      hipStream_t s) {
+  const int d = kv.H * kv.dh;
+  const float scale = 1.0f / sqrtf((float)kv.dh);
+  hipLaunchKernelGGL((attn_rows_kernel<T, LPK>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out, d,
+                     scale, live);
+}
+
+template <class T>
+hipError_t attn_rows_dispatch(const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
+                              const int32_t* live, hipStream_t s) {
+  const int chunks = kv.dh * (int)sizeof(T) / 16;   // 16-byte chunks of a row (head_dim is checked at load)
+  if (chunks <= 4) attn_rows_launch<T, 4>(q, rows, n, kv, out, live, s);
+  else if (chunks <= 8) attn_rows_launch<T, 8>(q, rows, n, kv, out, live, s);
+  else if (chunks <= 16) attn_rows_launch<T, 16>(q, rows, n, kv, out, live, s);
+  else if (chunks <= 32) attn_rows_launch<T, 32>(q, rows, n, kv, out, live, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
                             const int32_t* live, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  const int d = kv.H * kv.dh;
-  const float scale = 1.0f / sqrtf((float)kv.dh);
-  dim3 grid((n * kv.H + 3) / 4);
+  if (kv.dh > 128 || (kv.dh * 4) % 16 != 0) return hipErrorInvalidValue;
   switch (dtype) {
-    case DT_F32:
-      hipLaunchKernelGGL(attn_rows_kernel<float>, grid, dim3(256), 0, s, (const float*)q, rows, n, kv, (float*)out, d,
-                         scale, live);
-      break;
-    case DT_F16:
-      hipLaunchKernelGGL(attn_rows_kernel<f16>, grid, dim3(256), 0, s, (const f16*)q, rows, n, kv, (f16*)out, d, scale, live);
-      break;
-    case DT_BF16:
-      hipLaunchKernelGGL(attn_rows_kernel<bf16>, grid, dim3(256), 0, s, (const bf16*)q, rows, n, kv, (bf16*)out, d,
-                         scale, live);
-      break;
-    default:
-      return hipErrorInvalidValue;
+    case DT_F32: return attn_rows_dispatch<float>(q, rows, n, kv, out, live, s);
+    case DT_F16: return attn_rows_dispatch<f16>(q, rows, n, kv, out, live, s);
+    case DT_BF16: return attn_rows_dispatch<bf16>(q, rows, n, kv, out, live, s);
+    default: return hipErrorInvalidValue;
   }
-  return hipGetLastError();
 }

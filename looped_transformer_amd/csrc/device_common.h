@@ -80,3 +80,25 @@ __device__ __forceinline__ bool gate_closed(const int32_t* live) {
   asm volatile("" ::: "memory");
   return live && *live <= 0;
 }
+
+// Greedy-token reduction with the runner-up value: (v, i) is the largest value
+// with the lowest index on ties, v2 the largest of the others (a repeated maximum
+// gives v2 = v).  The result does not depend on the order of pushes and merges.
+__device__ __forceinline__ void best2_push(float& v, int& i, float& v2, float nv, int ni) {
+  if (nv > v || (nv == v && ni < i)) {
+    v2 = v;
+    v = nv;
+    i = ni;
+  } else {
+    v2 = fmaxf(v2, nv);
+  }
+}
+__device__ __forceinline__ void best2_merge(float& v, int& i, float& v2, float ov, int oi, float ov2) {
+  if (ov > v || (ov == v && oi < i)) {
+    v2 = fmaxf(ov2, v);
+    v = ov;
+    i = oi;
+  } else {
+    v2 = fmaxf(v2, ov);
+  }
+}

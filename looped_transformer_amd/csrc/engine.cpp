@@ -131,7 +131,7 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
   if (m->last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
   drop_graphs(m);
   void* olds[] = {w.hA, w.hB, w.hX, w.hE, w.x16, w.q16, w.o16, w.u16, w.xh, w.rowsA, w.rowsB,
-                  w.dest, w.count, w.tok, w.tok2, w.part_v, w.part_i, w.kv_scratch, w.splitk};
+                  w.dest, w.count, w.tok, w.tok2, w.part_v, w.part_i, w.part_v2, w.kv_scratch, w.splitk};
   for (void* p : olds) dev_free(m, p);
   w = tl::Workspace{};
   m->ws_bytes = 0;
@@ -148,6 +148,7 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
       {(void**)&w.tok2, (size_t)R * 4},
       {(void**)&w.part_v, (size_t)std::max(O, 1) * tiles * 4},
       {(void**)&w.part_i, (size_t)std::max(O, 1) * tiles * 4},
+      {(void**)&w.part_v2, (size_t)std::max(O, 1) * tiles * 4},
       {&w.kv_scratch, (size_t)std::max<int64_t>(KS, 1) * m->esz},
       {(void**)&w.splitk, (size_t)kSplitFloats * 4},
   };
@@ -295,7 +296,7 @@ struct Pass {
 };
 
 tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out, float* logits, int32_t* out_tok,
-                   const int32_t* pend_lanes, hipStream_t s);
+                   const int32_t* pend_lanes, hipStream_t s, float* margin = nullptr);
 
 // Iteration j is probed by the early-exit rule (never the last one: it could not
 // shorten the loop).
@@ -363,8 +364,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     }
     if (probe) {
       if (by_margin) {
-        TRY(run_head(m, h, nullptr, nj, m->ee_logits, nullptr, nullptr, s));
-        HIPCHK(launch_top2_margin(m->ee_logits, nj, c.vocab, m->ee_margin, s));
+        TRY(run_head(m, h, nullptr, nj, nullptr, nullptr, nullptr, s, m->ee_margin));
       }
       HIPCHK(launch_ee_probe(const_cast<RowInfo*>(rows), nj, j, h, m->ee_hprev, by_margin ? m->ee_margin : nullptr,
                              p.ee->tau, p.ee->logit_margin, p.ee->patience, d, p.final_h, m->ee_eff, m->ee_live, s));
@@ -416,9 +416,10 @@ void add_tiles(std::vector<AttnTile>& out, const std::vector<int>& seq_len, cons
   }
 }
 
-// Final norm on the selected rows, head GEMM, greedy token (lowest index on ties).
+// Final norm on the selected rows, head GEMM, greedy token (lowest index on ties)
+// and, with margin != NULL, the top-1 minus top-2 logit margin of each row.
 tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out, float* logits, int32_t* out_tok,
-                   const int32_t* pend_lanes, hipStream_t s) {
+                   const int32_t* pend_lanes, hipStream_t s, float* margin) {
   if (n_out <= 0) return TL_OK;
   const tl_config& c = m->cfg;
   auto& w = m->ws;
@@ -438,10 +439,11 @@ tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out
   e.part_val = w.part_v;
   e.part_idx = w.part_i;
   e.n_tiles = tiles;
+  e.part_val2 = margin ? w.part_v2 : nullptr;
   HIPCHK(launch_gemm(m->act, g, e, s));
-  if (out_tok || pend_lanes)
-    HIPCHK(launch_argmax_reduce(w.part_v, w.part_i, n_out, tiles, out_tok, pend_lanes ? m->d_pending : nullptr,
-                                pend_lanes, s));
+  if (out_tok || pend_lanes || margin)
+    HIPCHK(launch_argmax_reduce(w.part_v, w.part_i, e.part_val2, n_out, tiles, out_tok,
+                                pend_lanes ? m->d_pending : nullptr, pend_lanes, margin, s));
   TRY(tend(m, TL_T_HEAD, s));
   return TL_OK;
 }
@@ -1076,8 +1078,8 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
   return TL_OK;
 }
 
-// Early-exit buffers for n rows (logits only for the logit-margin rule).
-tl_status ensure_ee(tl_model* m, int n, bool logits, hipStream_t s) {
+// Early-exit buffers for n rows.
+tl_status ensure_ee(tl_model* m, int n, hipStream_t s) {
   const tl_config& c = m->cfg;
   if (n > m->ee_rows) {
     HIPCHK(hipStreamSynchronize(s));
@@ -1094,14 +1096,6 @@ tl_status ensure_ee(tl_model* m, int n, bool logits, hipStream_t s) {
     HIPCHK(hipHostMalloc((void**)&m->ee_eff_host, (size_t)R * 4, hipHostMallocDefault));
     m->ee_rows = (m->ee_live && m->ee_eff && m->ee_hprev && m->ee_margin) ? R : 0;
     if (!m->ee_rows) return fail(TL_E_OOM, "early-exit buffers for %d rows", n);
-  }
-  if (logits && n > m->ee_logit_rows) {
-    HIPCHK(hipStreamSynchronize(s));
-    dev_free(m, m->ee_logits);
-    const int R = (n + 63) / 64 * 64;
-    m->ee_logits = static_cast<float*>(dev_alloc(m, (size_t)R * c.vocab * 4));
-    m->ee_logit_rows = m->ee_logits ? R : 0;
-    if (!m->ee_logits) return fail(TL_E_OOM, "early-exit logits for %d rows", n);
   }
   return TL_OK;
 }
@@ -1130,7 +1124,7 @@ tl_status tl_decode_step_ee(tl_model* m, int32_t n, const int32_t* lanes, const 
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
   TRY(ensure_ws(m, n, n, 0, s));
-  TRY(ensure_ee(m, n, ee->logit_margin > 0.f, s));
+  TRY(ensure_ee(m, n, s));
   std::vector<RowInfo> rows(n);
   std::vector<int32_t> lane_ids(lanes, lanes + n), eff32(eff.begin(), eff.end()), live0(1, n);
   for (int i = 0; i < n; ++i) {

@@ -70,6 +70,7 @@ struct Workspace {
   int32_t *dest = nullptr, *count = nullptr, *tok = nullptr, *tok2 = nullptr;
   float* part_v = nullptr;
   int32_t* part_i = nullptr;
+  float* part_v2 = nullptr;         // runner-up value per head tile (logit-margin probe)
   void* kv_scratch = nullptr;
   int part_tiles = 0;
   float* splitk = nullptr;          // split-K partial tiles
@@ -122,9 +123,8 @@ struct tl_model {
   int32_t* ee_eff = nullptr;           // [ee_rows] effective depth by caller order
   float* ee_hprev = nullptr;           // [ee_rows, d] residual before a probed iteration
   float* ee_margin = nullptr;          // [ee_rows]
-  float* ee_logits = nullptr;          // [ee_logit_rows, V]
   int32_t* ee_eff_host = nullptr;      // pinned mirror of ee_eff
-  int ee_rows = 0, ee_logit_rows = 0;
+  int ee_rows = 0;
   // kernel-class timing (measurement only)
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;

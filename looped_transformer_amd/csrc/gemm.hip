@@ -93,14 +93,6 @@ __device__ __forceinline__ void epi_one(const GemmEpi& e, int r, int c, float v)
 
 constexpr bool paired(int kind) { return kind == EPI_QKV || kind == EPI_SWIGLU; }
 
-// (value, index) ordering for the greedy token: larger value wins, ties -> lower index.
-__device__ __forceinline__ void best_merge(float& v, int& i, float v2, int i2) {
-  if (v2 > v || (v2 == v && i2 < i)) {
-    v = v2;
-    i = i2;
-  }
-}
-
 // Workgroup of 4 waves (2 x 2) computes a BM x BN tile over the K range of its
 // split (blockIdx.z).  Per BK-wide K stage: global -> registers, issued D-1 stages
 // ahead into a ring of D register sets (so D-1 stages of loads are in flight while
@@ -323,7 +315,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
 
   // ---- epilogue: lane holds column (lane & 15), rows 4*(lane >> 4) + r of each 16x16 tile
   if constexpr (KIND == EPI_HEAD) {
-    __shared__ float red_v[BM][2];
+    __shared__ float red_v[BM][2], red_v2[BM][2];
     __shared__ int red_i[BM][2];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -331,7 +323,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       for (int r = 0; r < 4; ++r) {
         const int lrow_t = wm * WTM + i * 16 + lr + r;
         const int row = m0 + lrow_t;
-        float bv = -INFINITY;
+        float bv = -INFINITY, b2 = -INFINITY;
         int bi = 0x7fffffff;
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
@@ -339,17 +331,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
           if (col < N) {
             const float v = acc[i][j][r];
             if (row < M) epi_one<KIND>(e, row, col, v);
-            best_merge(bv, bi, v, col);
+            best2_push(bv, bi, b2, v, col);
           }
         }
 #pragma unroll
         for (int o = 1; o < 16; o <<= 1) {
-          const float ov = __shfl_xor(bv, o, 64);
+          const float ov = __shfl_xor(bv, o, 64), ov2 = __shfl_xor(b2, o, 64);
           const int oi = __shfl_xor(bi, o, 64);
-          best_merge(bv, bi, ov, oi);
+          best2_merge(bv, bi, b2, ov, oi, ov2);
         }
         if (lc == 0) {
           red_v[lrow_t][wn] = bv;
+          red_v2[lrow_t][wn] = b2;
           red_i[lrow_t][wn] = bi;
         }
       }
@@ -357,11 +350,12 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
     for (int t = tid; t < BM; t += 256) {
       const int row = m0 + t;
       if (row < M) {
-        float bv = red_v[t][0];
+        float bv = red_v[t][0], b2 = red_v2[t][0];
         int bi = red_i[t][0];
-        best_merge(bv, bi, red_v[t][1], red_i[t][1]);
+        best2_merge(bv, bi, b2, red_v[t][1], red_i[t][1], red_v2[t][1]);
         e.part_val[(int64_t)row * e.n_tiles + blockIdx.x] = bv;
         e.part_idx[(int64_t)row * e.n_tiles + blockIdx.x] = bi;
+        if (e.part_val2) e.part_val2[(int64_t)row * e.n_tiles + blockIdx.x] = b2;
       }
     }
   } else {
@@ -616,25 +610,26 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, GemmEpi e) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = m0 + ty * 4 + i;
-      float bv = -INFINITY;
+      float bv = -INFINITY, b2 = -INFINITY;
       int bi = 0x7fffffff;
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
         const int col = n0 + tx * 4 + j;
         if (col < N) {
           if (row < M) epi_one<KIND>(e, row, col, acc[i][j]);
-          best_merge(bv, bi, acc[i][j], col);
+          best2_push(bv, bi, b2, acc[i][j], col);
         }
       }
 #pragma unroll
       for (int o = 1; o < 16; o <<= 1) {
-        const float ov = __shfl_xor(bv, o, 64);
+        const float ov = __shfl_xor(bv, o, 64), ov2 = __shfl_xor(b2, o, 64);
         const int oi = __shfl_xor(bi, o, 64);
-        best_merge(bv, bi, ov, oi);
+        best2_merge(bv, bi, b2, ov, oi, ov2);
       }
       if (tx == 0 && row < M) {
         e.part_val[(int64_t)row * e.n_tiles + blockIdx.x] = bv;
         e.part_idx[(int64_t)row * e.n_tiles + blockIdx.x] = bi;
+        if (e.part_val2) e.part_val2[(int64_t)row * e.n_tiles + blockIdx.x] = b2;
       }
     }
     return;

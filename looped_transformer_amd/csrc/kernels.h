@@ -66,6 +66,7 @@ struct GemmEpi {
   int64_t ldl;
   float* part_val;
   int32_t* part_idx;
+  float* part_val2;        // optional: runner-up value of each tile (logit margin)
   int32_t n_tiles;
   // EPI_STORE: out[r, c] = acc (fp32)
   float* out;
@@ -107,7 +108,7 @@ hipError_t launch_compact(const RowInfo* rows_in, int n, int it, RowInfo* rows_o
 hipError_t launch_move_rows(const float* h, const int32_t* dest, const RowInfo* rows, int n, int d,
                             float* h_next, float* h_exit, hipStream_t s);
 hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream_t s);
-// Early-exit probe after loop iteration it on n rows (one wave per row): rows not
+// Early-exit probe after loop iteration it on n rows (one workgroup per row): rows not
 // done are stable when margin[i] > margin_thr (margin != NULL) or when
 // ||h_i - h_prev_i|| / ||h_i|| < tau; streak counts consecutive stable probes and
 // resets otherwise; at streak >= patience the row is marked done, its state goes to
@@ -115,10 +116,12 @@ hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream
 hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, const float* h_prev,
                            const float* margin, float tau, float margin_thr, int patience, int d,
                            float* h_exit, int32_t* eff_depth, int32_t* live, hipStream_t s);
-// margin[i] = largest minus second largest of logits row i (equal values give 0).
-hipError_t launch_top2_margin(const float* logits, int n, int V, float* margin, hipStream_t s);
-hipError_t launch_argmax_reduce(const float* part_val, const int32_t* part_idx, int n, int n_tiles,
-                                int32_t* out_tok, int32_t* out_tok2, const int32_t* scatter, hipStream_t s);
+// Per row i of the head GEMM's tile partials (pv/pi: best value and index of each
+// of the tiles, pv2: the tile's runner-up value or NULL): greedy token to out[i]
+// and out2[scatter[i]] (either may be NULL; scatter NULL = identity), and, when
+// margin != NULL, margin[i] = top-1 minus top-2 logit (a repeated maximum gives 0).
+hipError_t launch_argmax_reduce(const float* pv, const int32_t* pi, const float* pv2, int n, int tiles, int32_t* out,
+                                int32_t* out2, const int32_t* scatter, float* margin, hipStream_t s);
 hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);

@@ -129,40 +129,66 @@ __global__ void write_orig_kernel(const RowInfo* rows, int n, int32_t* out) {
 }
 
 // ---------------------------------------------------------------- early exit
-// One wave per row: relative L2 change (or a precomputed logit margin) decides a
-// stable probe; patience consecutive stable probes finish the row.
-__global__ __launch_bounds__(256) void ee_probe_kernel(RowInfo* __restrict__ rows, int n, int it,
+// One workgroup per row: relative L2 change (or a precomputed logit margin)
+// decides a stable probe; patience consecutive stable probes finish the row, whose
+// state is copied out as its exit state.
+__global__ __launch_bounds__(256) void ee_probe_kernel(RowInfo* __restrict__ rows, int it,
                                                       const float* __restrict__ h, const float* __restrict__ h_prev,
                                                       const float* __restrict__ margin, float tau, float margin_thr,
                                                       int patience, int d, float* __restrict__ h_exit,
                                                       int32_t* __restrict__ eff_depth, int32_t* live) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= n) return;
-  RowInfo ri = rows[r];
-  if (ri.done) return;
+  const int r = blockIdx.x, tid = threadIdx.x;
+  const RowInfo ri = rows[r];
+  if (ri.done) return;   // uniform over the workgroup
   const float* hr = h + (int64_t)r * d;
+  const bool vec = (d & 3) == 0;
   bool stable;
   if (margin) {
     stable = margin[r] > margin_thr;
   } else {
     const float* pr = h_prev + (int64_t)r * d;
     float dd = 0.f, hh = 0.f;
-    for (int c = lane; c < d; c += 64) {
-      const float a = hr[c], b = a - pr[c];
-      dd = fmaf(b, b, dd);
-      hh = fmaf(a, a, hh);
+    if (vec) {
+      for (int c = tid; c < (d >> 2); c += 256) {
+        const floatx4 a = reinterpret_cast<const floatx4*>(hr)[c];
+        const floatx4 b = a - reinterpret_cast<const floatx4*>(pr)[c];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          dd = fmaf(b[q], b[q], dd);
+          hh = fmaf(a[q], a[q], hh);
+        }
+      }
+    } else {
+      for (int c = tid; c < d; c += 256) {
+        const float a = hr[c], b = a - pr[c];
+        dd = fmaf(b, b, dd);
+        hh = fmaf(a, a, hh);
+      }
     }
+    __shared__ float red[2][4];
     dd = wave_sum(dd);
     hh = wave_sum(hh);
+    if ((tid & 63) == 0) {
+      red[0][tid >> 6] = dd;
+      red[1][tid >> 6] = hh;
+    }
+    __syncthreads();
+    dd = red[0][0] + red[0][1] + red[0][2] + red[0][3];
+    hh = red[1][0] + red[1][1] + red[1][2] + red[1][3];
     stable = sqrtf(dd) < tau * sqrtf(hh);
   }
   const int streak = stable ? ri.streak + 1 : 0;
   const bool fin = streak >= patience;
   if (fin) {
     float* dst = h_exit + (int64_t)ri.orig * d;
-    for (int c = lane; c < d; c += 64) dst[c] = hr[c];
+    if (vec) {
+      for (int c = tid; c < (d >> 2); c += 256)
+        reinterpret_cast<floatx4*>(dst)[c] = reinterpret_cast<const floatx4*>(hr)[c];
+    } else {
+      for (int c = tid; c < d; c += 256) dst[c] = hr[c];
+    }
   }
-  if (lane == 0) {
+  if (tid == 0) {
     rows[r].streak = streak;
     if (fin) {
       rows[r].done = 1;
@@ -172,50 +198,39 @@ __global__ __launch_bounds__(256) void ee_probe_kernel(RowInfo* __restrict__ row
   }
 }
 
-// One wave per row: the two largest logits (lane-local pairs merged across the wave).
-__global__ __launch_bounds__(256) void top2_margin_kernel(const float* __restrict__ logits, int n, int V,
-                                                         float* __restrict__ margin) {
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (r >= n) return;
-  const float* lr = logits + (int64_t)r * V;
-  float a = -INFINITY, b = -INFINITY;   // a >= b
-  for (int c = lane; c < V; c += 64) {
-    const float v = lr[c];
-    if (v > a) {
-      b = a;
-      a = v;
-    } else if (v > b) {
-      b = v;
-    }
-  }
+// ---------------------------------------------------------------- greedy token
+// One workgroup per row merges the head GEMM's per-tile partials: the greedy
+// token (largest logit, lowest index on ties) and, when the tiles also kept their
+// runner-up, the top-1 minus top-2 logit margin.
+__global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi,
+                                                            const float* __restrict__ pv2, int tiles, int32_t* out,
+                                                            int32_t* out2, const int32_t* scatter, float* margin) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float bv = -INFINITY, b2 = -INFINITY;
+  int bi = 0x7fffffff;
+  const int64_t base = (int64_t)r * tiles;
+  for (int t = tid; t < tiles; t += 256)
+    best2_merge(bv, bi, b2, pv[base + t], pi[base + t], pv2 ? pv2[base + t] : -INFINITY);
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) {
-    const float a2 = __shfl_xor(a, o, 64), b2 = __shfl_xor(b, o, 64);
-    const float na = fmaxf(a, a2);
-    const float nb = a >= a2 ? fmaxf(b, a2) : fmaxf(b2, a);
-    a = na;
-    b = nb;
+    const float ov = __shfl_xor(bv, o, 64), ov2 = __shfl_xor(b2, o, 64);
+    const int oi = __shfl_xor(bi, o, 64);
+    best2_merge(bv, bi, b2, ov, oi, ov2);
   }
-  if (lane == 0) margin[r] = a - b;
-}
-
-// ---------------------------------------------------------------- greedy token
-__global__ void argmax_reduce_kernel(const float* __restrict__ pv, const int32_t* __restrict__ pi, int n, int tiles,
-                                     int32_t* out, int32_t* out2, const int32_t* scatter) {
-  const int r = blockIdx.x * 256 + threadIdx.x;
-  if (r >= n) return;
-  float bv = -INFINITY;
-  int bi = 0x7fffffff;
-  for (int t = 0; t < tiles; ++t) {
-    const float v = pv[(int64_t)r * tiles + t];
-    const int i = pi[(int64_t)r * tiles + t];
-    if (v > bv || (v == bv && i < bi)) {
-      bv = v;
-      bi = i;
-    }
+  __shared__ float sv[4], sv2[4];
+  __shared__ int si[4];
+  if ((tid & 63) == 0) {
+    sv[tid >> 6] = bv;
+    sv2[tid >> 6] = b2;
+    si[tid >> 6] = bi;
   }
-  if (out) out[r] = bi;
-  if (out2) out2[scatter ? scatter[r] : r] = bi;
+  __syncthreads();
+  if (tid == 0) {
+    for (int w = 1; w < 4; ++w) best2_merge(bv, bi, b2, sv[w], si[w], sv2[w]);
+    if (out) out[r] = bi;
+    if (out2) out2[scatter ? scatter[r] : r] = bi;
+    if (margin) margin[r] = bv - b2;
+  }
 }
 
 __global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restrict__ src, const int32_t* __restrict__ idx,
@@ -380,21 +395,15 @@ hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, const f
                            float tau, float margin_thr, int patience, int d, float* h_exit, int32_t* eff_depth,
                            int32_t* live, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ee_probe_kernel, dim3((n + 3) / 4), dim3(256), 0, s, rows, n, it, h, h_prev, margin, tau,
+  hipLaunchKernelGGL(ee_probe_kernel, dim3(n), dim3(256), 0, s, rows, it, h, h_prev, margin, tau,
                      margin_thr, patience, d, h_exit, eff_depth, live);
   return hipGetLastError();
 }
 
-hipError_t launch_top2_margin(const float* logits, int n, int V, float* margin, hipStream_t s) {
+hipError_t launch_argmax_reduce(const float* pv, const int32_t* pi, const float* pv2, int n, int tiles, int32_t* out,
+                                int32_t* out2, const int32_t* scatter, float* margin, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(top2_margin_kernel, dim3((n + 3) / 4), dim3(256), 0, s, logits, n, V, margin);
-  return hipGetLastError();
-}
-
-hipError_t launch_argmax_reduce(const float* pv, const int32_t* pi, int n, int tiles, int32_t* out, int32_t* out2,
-                                const int32_t* scatter, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3((n + 255) / 256), dim3(256), 0, s, pv, pi, n, tiles, out, out2, scatter);
+  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(n), dim3(256), 0, s, pv, pi, pv2, tiles, out, out2, scatter, margin);
   return hipGetLastError();
 }
 
