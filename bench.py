@@ -85,8 +85,8 @@ def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
-        print("bench.py measures one GPU: this build has no multi-GPU path (lanes would be sharded across "
-              "GPUs with replicated weights; see DESIGN.md). Run with --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: there is no multi-GPU path (lanes would be sharded across "
+              "GPUs with replicated weights). Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch

@@ -8,8 +8,8 @@ Pages cited (titles as printed on each page):
   [CDB]  "Depth-adaptive Inference of Looped Language Models via Continuous Depth
          Batching" (summary page)
 
-What is computed (readings of open points are listed in the design doc's table of
-readings; the short form is repeated where a function depends on one):
+What is computed (where the pages leave a point open, the function that depends
+on it states the reading it takes):
   * pipeline embed -> pre blocks -> shared loop block (stack) x L -> post blocks ->
     head, [VSG] "Where Generic Runtimes Lose On Looped Checkpoints";
   * L is a call argument, never part of the weights, [DYN] "The Core Idea";
@@ -48,6 +48,7 @@ __all__ = [
     "OracleModel", "Lane", "prefill", "decode_step", "forward_batch", "forward_ragged",
     "greedy_argmax", "clamp_depths", "active_lists", "bf16_bits_to_float",
     "EarlyExit", "probe_iteration", "relative_delta", "logit_margin", "decode_step_ee",
+    "append", "fork",
 ]
 
 
@@ -69,7 +70,8 @@ def rope_angles(positions: np.ndarray, head_dim: int, base: float, dt=np.float64
     """cos and sin of p * theta_i, theta_i = base^(-2i/head_dim), i < head_dim/2.
 
     Rotary position embedding with base 10000 (model definition of the workloads);
-    the rotate-half pairing (i, i + head_dim/2) is a reading, see the design doc.
+    the rotate-half pairing (i, i + head_dim/2) is a reading: the pages name RoPE
+    but not its pairing.
     """
     half = head_dim // 2
     i = np.arange(half, dtype=np.float64)
@@ -355,6 +357,63 @@ def decode_step(m: OracleModel, lane: Lane, L_req: int, token: int | None = None
     lane.pending = nxt
     lane.hidden_last = h[0].copy()
     return h[0], logits, nxt, L
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix reuse ([BENCH] section 2, shared-prefix throughput: a prefix's
+# cache is computed once and reused by many requests, across every loop
+# iteration's slot)
+
+
+def append(m: OracleModel, lane: Lane, tokens, L_req: int, want_logits: str = "last"):
+    """Cached forward of several new tokens of one lane.
+
+    The tokens take the next positions of the lane at depth L = min(L_req, ceiling)
+    (monotone clamping as for a decode step); every block application attends to
+    the lane's earlier positions in its own cache slot and, causally, to the new
+    rows.  Returns (hidden [T, d], logits: [V] of the last row, [T, V] or None);
+    the lane's pending token is the greedy token of the last row.
+    """
+    assert L_req >= 1
+    tokens = np.asarray(tokens, dtype=np.int64)
+    assert len(tokens) >= 1
+    L = min(int(L_req), lane.ceiling)
+    p0 = len(lane.tokens)
+    pos = p0 + np.arange(len(tokens))
+    h = m.embed_rows(tokens)
+    for b, key in m.slots(L):
+        pk, pv = lane.kv[key]
+        assert pk.shape[0] == p0, "cache slot misses earlier positions"
+        h, k, v = m.block(b, h, pos, pk, pv)
+        lane.kv[key] = (np.concatenate([pk, k]), np.concatenate([pv, v]))
+    lane.tokens.extend(map(int, tokens))
+    lane.ceiling = L
+    lane.hidden_last = h[-1].copy()
+    logits = None
+    if want_logits == "all":
+        logits = m.logits(h)
+        lane.pending = int(greedy_argmax(logits[-1]))
+    elif want_logits == "last":
+        logits = m.logits(h[-1:])[0]
+        lane.pending = int(greedy_argmax(logits))
+    return h, logits
+
+
+def fork(lane: Lane, prefix_len: int) -> Lane:
+    """A new lane holding the first prefix_len positions of ``lane``.
+
+    Every cache slot keeps those positions (each loop iteration's slot included),
+    the depth ceiling is the source's, and the pending token is the source's when
+    the whole lane is taken (otherwise the next call appends tokens).  The source
+    is left unchanged.
+    """
+    P = int(prefix_len)
+    assert 1 <= P <= len(lane.tokens)
+    kv = {key: (k[:P].copy(), v[:P].copy()) for key, (k, v) in lane.kv.items()}
+    whole = P == len(lane.tokens)
+    return Lane(tokens=list(lane.tokens[:P]), kv=kv, ceiling=lane.ceiling,
+                pending=lane.pending if whole else -1,
+                hidden_last=lane.hidden_last.copy() if whole and lane.hidden_last is not None else None)
 
 
 # ---------------------------------------------------------------------------

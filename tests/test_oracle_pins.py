@@ -489,3 +489,83 @@ def test_ee_streak_resets_on_unstable_probe(monkeypatch):
     b = fresh()
     _, _, _, E = oracle.decode_step_ee(m, b, 8, oracle.EarlyExit(patience=2, min_L=2, tau=0.5))
     assert E == 5   # probes at 2 (stable), 3 (unstable), 4, 5 (stable, stable)
+
+
+# ---------------------------------------------------------------------------
+# shared-prefix reuse: appending to a cache and forking a prefix
+
+
+def _kv_close(a, b, tol=1e-12):
+    assert set(a.kv) == set(b.kv)
+    for key in a.kv:
+        for x, y in zip(a.kv[key], b.kv[key]):
+            assert x.shape == y.shape, key
+            assert np.allclose(x, y, rtol=tol, atol=tol), key
+
+
+@pytest.mark.parametrize("cuts", [[7], [3, 9, 10]])
+def test_append_equals_prefill_of_concatenation(tiny, cuts):
+    """Cached chunks (any split of the prompt) == one uncached prefill of it."""
+    w, m = tiny
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 16, 256)
+    full, h_full, lg_full = oracle.prefill(m, toks, 4, want_logits="all")
+    edges = [0] + cuts + [16]
+    lane, h0, _ = oracle.prefill(m, toks[:edges[1]], 4, want_logits="none")
+    hs = [h0]
+    for a, b in zip(edges[1:-1], edges[2:]):
+        h, lg = oracle.append(m, lane, toks[a:b], 4, want_logits="all")
+        hs.append(h)
+        assert np.allclose(lg, lg_full[a:b], rtol=1e-10, atol=1e-12)
+    assert np.allclose(np.concatenate(hs), h_full, rtol=1e-11, atol=1e-13)
+    _kv_close(lane, full)
+    assert lane.pending == full.pending and lane.tokens == full.tokens and lane.ceiling == 4
+
+
+def test_append_equals_teacher_forced_decode_steps(tiny):
+    """T tokens appended at once == T single-token cached steps (multi-row causal
+    masking against the one-row path), including a clamped depth."""
+    w, m = tiny
+    toks = synth.tokens(0, synth.STREAM_TOKENS, 12, 256)
+    new = synth.tokens(0, 3100, 5, 256)
+    a = oracle.prefill(m, toks, 5)[0]
+    b = oracle.prefill(m, toks, 5)[0]
+    h, lg = oracle.append(m, a, new, 7, want_logits="all")   # requested 7 > ceiling 5 -> 5
+    assert a.ceiling == 5
+    for t, tok in enumerate(new):
+        hb, lb, nb, Lb = oracle.decode_step(m, b, 7, token=int(tok))
+        assert Lb == 5
+        assert np.allclose(h[t], hb, rtol=1e-11, atol=1e-13)
+        assert np.allclose(lg[t], lb, rtol=1e-10, atol=1e-12)
+    _kv_close(a, b)
+    assert a.pending == b.pending
+    h2, _ = oracle.append(m, a, new[:2], 3, want_logits="none")   # lower depth: ceiling drops
+    assert a.ceiling == 3
+    for t in range(2):
+        hb, _, _, Lb = oracle.decode_step(m, b, 3, token=int(new[t]))
+        assert Lb == 3 and np.allclose(h2[t], hb, rtol=1e-11, atol=1e-13)
+
+
+def test_fork_then_append_equals_full_prefill(tiny):
+    """A request built from a forked prefix == the same request prefilled alone
+    (the shared and uncached modes must agree), and the source is left intact."""
+    w, m = tiny
+    prefix = synth.tokens(0, synth.STREAM_TOKENS, 10, 256)
+    src = oracle.prefill(m, prefix, 4)[0]
+    ref_src = oracle.prefill(m, prefix, 4)[0]
+    for P, seed in [(10, 3200), (6, 3201), (1, 3202)]:
+        suffix = synth.tokens(0, seed, 4, 256)
+        child = oracle.fork(src, P)
+        assert child.ceiling == 4 and child.tokens == list(map(int, prefix[:P]))
+        assert child.pending == (src.pending if P == 10 else -1)
+        h, lg = oracle.append(m, child, suffix, 4)
+        want, h_want, lg_want = oracle.prefill(m, np.concatenate([prefix[:P], suffix]), 4)
+        assert np.allclose(h, h_want[P:], rtol=1e-11, atol=1e-13)
+        assert np.allclose(lg, lg_want, rtol=1e-10, atol=1e-12)
+        _kv_close(child, want)
+        assert child.pending == want.pending
+        for _ in range(2):
+            hc, _, nc, _ = oracle.decode_step(m, child, 4)
+            hw, _, nw, _ = oracle.decode_step(m, want, 4)
+            assert np.allclose(hc, hw, rtol=1e-11, atol=1e-13) and nc == nw
+    _kv_close(src, ref_src, tol=0.0)
+    assert src.tokens == ref_src.tokens and src.pending == ref_src.pending
