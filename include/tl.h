@@ -147,6 +147,39 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu_seqlens_host
                      float* out_logits_dev, int32_t* out_next_dev, int32_t* out_active_log_dev,
                      void* stream);
 
+/* Append tokens to prefilled lanes: a cached causal forward of several new
+ * positions per lane (the rest of a prompt after a shared prefix, or any chunk).
+ *   cu_seqlens_host [n_seqs+1], tokens_dev [total]: as in tl_forward; sequence i
+ *      takes the next positions of lanes_host[i] (len .. len + n_i - 1), which
+ *      must fit the lane's capacity.
+ *   per_seq_L_host [n_seqs]: requested depth; effective depth min(request, lane
+ *      ceiling) becomes the new ceiling, as in tl_decode_step.  Every block
+ *      application attends to the lane's earlier positions in its own cache slot
+ *      and, causally, to the new rows.
+ *   out_hidden_dev [total, d], out_logits_dev [n_seqs, V] (last new position),
+ *      out_next_dev [n_seqs] (greedy token of the last position, also the lane's
+ *      pending token), out_eff_L_host [n_seqs]: each may be NULL.
+ * Errors: TL_E_ARG (NULL, empty sequence, lane out of range or repeated, L < 1),
+ * TL_E_STATE (lane never prefilled, capacity exceeded), TL_E_OOM, TL_E_HIP. */
+tl_status tl_append(tl_model* m, int32_t n_seqs, const int32_t* cu_seqlens_host,
+                    const int32_t* tokens_dev, const int32_t* lanes_host,
+                    const int32_t* per_seq_L_host, float* out_hidden_dev, float* out_logits_dev,
+                    int32_t* out_next_dev, int32_t* out_eff_L_host, void* stream);
+
+/* Shared-prefix reuse ("Benchmark Comparison" page, measured benchmarks, section 2:
+ * a prefix's cache is computed once and reused by many requests, in every loop
+ * iteration's slot).  Lane dst (re)starts with the first prefix_len positions of
+ * lane src: every cache slot up to src's depth ceiling is copied on the device
+ * (one strided copy on `stream`), the ceiling is src's, the capacity
+ * prefix_len + max_new_tokens.  When prefix_len equals src's length, dst also
+ * takes src's pending token; otherwise dst must be appended to (tl_append) before
+ * it is decoded.  src is unchanged; dst's previous cache, if any, is released.
+ * Errors: TL_E_ARG (lane out of range, src == dst, prefix_len outside
+ * [1, src length], max_new_tokens < 0), TL_E_STATE (src never prefilled,
+ * prefix_len + max_new_tokens > max_pos, KV arena full), TL_E_HIP. */
+tl_status tl_lane_fork(tl_model* m, int32_t src_lane, int32_t dst_lane, int32_t prefix_len,
+                       int32_t max_new_tokens, void* stream);
+
 /* One cached greedy decode step for n_lanes prefilled lanes.
  *   per_lane_L_host [n_lanes]: requested depth; the effective depth is
  *      min(request, lane ceiling) and becomes the new ceiling, so depth never rises
@@ -159,7 +192,8 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu_seqlens_host
  *   out_eff_L_host [n_lanes] or NULL: effective depth used.
  *   out_active_log_dev: as in tl_forward, over the lanes of this call.
  * Errors: TL_E_ARG (lane out of range, repeated lane, L < 1), TL_E_STATE (lane
- * never prefilled or full), TL_E_HIP. */
+ * never prefilled or full, or in_tokens_dev NULL for a lane holding no pending
+ * token), TL_E_HIP. */
 tl_status tl_decode_step(tl_model* m, int32_t n_lanes, const int32_t* lanes_host,
                          const int32_t* per_lane_L_host, const int32_t* in_tokens_dev,
                          int32_t* out_tokens_dev, float* out_logits_dev, float* out_hidden_dev,

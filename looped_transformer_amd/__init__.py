@@ -73,6 +73,8 @@ def lib():
         "tl_load_weights": [ctypes.POINTER(tl_config), ctypes.POINTER(tl_weights), ALLOC_FN, DEALLOC_FN, _P, _P,
                             ctypes.POINTER(_P)],
         "tl_forward": [_P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P],
+        "tl_append": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+        "tl_lane_fork": [_P, _I, _I, _I, _I, _P],
         "tl_decode_step": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "tl_decode_step_ee": [_P, _I, _P, _P, ctypes.POINTER(tl_early_exit), _P, _P, _P, _P, _P, _P],
         "tl_decode_run": [_P, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P],
@@ -208,6 +210,23 @@ def tl_forward(model, cu_seqlens, tokens, L=1, seq_L=None, lanes=None, max_new_t
     _check(lib().tl_forward(model.handle, len(cu) - 1, _ptr(cu), _ptr(tokens), int(L), _ptr(sl), _ptr(ln),
                             int(max_new_tokens), _ptr(out_hidden), _ptr(out_logits), _ptr(out_next),
                             _ptr(out_active_log), _stream(stream)))
+
+
+def tl_append(model, cu_seqlens, tokens, lanes, per_seq_L, out_hidden=None, out_logits=None, out_next=None,
+              stream=None):
+    """Returns the effective depths (numpy int32)."""
+    cu = _i32(cu_seqlens)
+    ln = _i32(lanes)
+    pl = _i32(per_seq_L)
+    eff = np.zeros(len(ln), np.int32)
+    _check(lib().tl_append(model.handle, len(cu) - 1, _ptr(cu), _ptr(tokens), _ptr(ln), _ptr(pl), _ptr(out_hidden),
+                           _ptr(out_logits), _ptr(out_next), _ptr(eff), _stream(stream)))
+    return eff
+
+
+def tl_lane_fork(model, src_lane: int, dst_lane: int, prefix_len: int, max_new_tokens: int = 0, stream=None):
+    _check(lib().tl_lane_fork(model.handle, int(src_lane), int(dst_lane), int(prefix_len), int(max_new_tokens),
+                              _stream(stream)))
 
 
 def tl_decode_step(model, lanes, per_lane_L, out_tokens, in_tokens=None, out_logits=None, out_hidden=None,

@@ -398,7 +398,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
 // Attention tiles of one iteration: sequences still active, in caller order, each
 // cut into runs of at most attn_tile_rows() consecutive rows.
 void add_tiles(std::vector<AttnTile>& out, const std::vector<int>& seq_len, const std::vector<int>& seq_lane,
-               const std::vector<int>& Ls, int j) {
+               const std::vector<int>& Ls, int j, const std::vector<int>* start = nullptr) {
   const int tr = attn_tile_rows();
   int row = 0;
   for (size_t sq = 0; sq < seq_len.size(); ++sq) {
@@ -407,7 +407,7 @@ void add_tiles(std::vector<AttnTile>& out, const std::vector<int>& seq_len, cons
       AttnTile t{};
       t.row0 = row + p0;
       t.nrows = std::min(tr, seq_len[sq] - p0);
-      t.pos0 = p0;
+      t.pos0 = (start ? (*start)[sq] : 0) + p0;
       t.lane = seq_lane[sq];
       t.iter = j;
       out.push_back(t);
@@ -852,6 +852,7 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
     for (int i = 0; i < n_seqs; ++i) {
       Lane ln;
       ln.live = true;
+      ln.pending = true;
       ln.len = cu[i + 1] - cu[i];
       ln.cap = ln.len + max_new;
       ln.ceiling = Ls[i];
@@ -1018,6 +1019,136 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   return stt;
 }
 
+tl_status tl_append(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32_t* tokens, const int32_t* lanes,
+                    const int32_t* req_L, float* out_hidden, float* out_logits, int32_t* out_next, int32_t* out_eff_L,
+                    void* stream) {
+  g_err.clear();
+  if (!m || !cu || !tokens || !lanes || !req_L) return fail(TL_E_ARG, "NULL argument");
+  const tl_config& c = m->cfg;
+  if (n_seqs < 1) return fail(TL_E_ARG, "n_seqs must be >= 1");
+  if (cu[0] != 0) return fail(TL_E_ARG, "cu_seqlens[0] must be 0");
+  std::vector<char> seen(c.max_lanes, 0);
+  std::vector<int> eff(n_seqs), slen(n_seqs), slane(n_seqs), start(n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    const int l = lanes[i];
+    if (l < 0 || l >= c.max_lanes) return fail(TL_E_ARG, "lane %d out of range [0, %d)", l, c.max_lanes);
+    if (seen[l]) return fail(TL_E_ARG, "lane %d listed twice", l);
+    seen[l] = 1;
+    slen[i] = cu[i + 1] - cu[i];
+    if (slen[i] < 1) return fail(TL_E_ARG, "sequence %d is empty", i);
+    if (req_L[i] < 1) return fail(TL_E_ARG, "requested L %d < 1", req_L[i]);
+    const Lane& ln = m->lanes[l];
+    if (!ln.live) return fail(TL_E_STATE, "lane %d was never prefilled", l);
+    if (ln.len + slen[i] > ln.cap)
+      return fail(TL_E_STATE, "lane %d has room for %d more positions, %d appended", l, ln.cap - ln.len, slen[i]);
+    eff[i] = std::min(req_L[i], ln.ceiling);
+    slane[i] = l;
+    start[i] = ln.len;
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int T = cu[n_seqs];
+  TRY(ensure_ws(m, T, n_seqs, 0, s));
+  std::vector<RowInfo> rows(T);
+  std::vector<int> depth(T);
+  std::vector<int32_t> last(n_seqs), lane_ids(lanes, lanes + n_seqs);
+  for (int i = 0; i < n_seqs; ++i) {
+    for (int p = 0; p < slen[i]; ++p) {
+      RowInfo& r = rows[cu[i] + p];
+      r = RowInfo{};
+      r.orig = cu[i] + p;
+      r.lane = lanes[i];
+      r.pos = start[i] + p;
+      r.depth = eff[i];
+      r.iter = 1;
+      depth[cu[i] + p] = eff[i];
+    }
+    last[i] = cu[i + 1] - 1;
+  }
+  const bool tiled = attn_tiled_supported(m->act, c.head_dim);
+  const std::vector<int> n_act = active_counts(depth);
+  std::vector<std::vector<AttnTile>> tile_lists;
+  if (tiled)
+    for (size_t j = 1; j <= n_act.size(); ++j) {
+      tile_lists.emplace_back();
+      add_tiles(tile_lists.back(), slen, slane, eff, (int)j, &start);
+    }
+  Stage st;
+  std::vector<size_t> o_tiles;
+  for (auto& tlst : tile_lists) o_tiles.push_back(st.add(tlst));
+  const size_t o_rows = st.add(rows), o_last = st.add(last), o_lanes = st.add(lane_ids);
+  TRY(stage_upload(m, st, s));
+  Pass p;
+  p.n = T;
+  p.tokens = tokens;
+  p.rows0 = staged<RowInfo>(m, o_rows);
+  p.n_active = n_act;
+  for (size_t k = 0; k < tile_lists.size(); ++k) {
+    p.tiles.push_back(staged<AttnTile>(m, o_tiles[k]));
+    p.n_tiles.push_back((int)tile_lists[k].size());
+  }
+  p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
+  p.final_h = out_hidden ? out_hidden : m->ws.hX;
+  TRY(run_pass(m, p, s));
+  TRY(run_head(m, p.final_h, staged<int32_t>(m, o_last), n_seqs, out_logits, out_next, staged<int32_t>(m, o_lanes), s));
+  for (int i = 0; i < n_seqs; ++i) {
+    Lane& ln = m->lanes[lanes[i]];
+    ln.len += slen[i];
+    ln.ceiling = eff[i];
+    ln.pending = true;
+    if (out_eff_L) out_eff_L[i] = eff[i];
+  }
+  return TL_OK;
+}
+
+tl_status tl_lane_fork(tl_model* m, int32_t src, int32_t dst, int32_t prefix_len, int32_t max_new, void* stream) {
+  g_err.clear();
+  if (!m) return fail(TL_E_ARG, "NULL model");
+  const tl_config& c = m->cfg;
+  if (src < 0 || src >= c.max_lanes || dst < 0 || dst >= c.max_lanes)
+    return fail(TL_E_ARG, "lane out of range [0, %d)", c.max_lanes);
+  if (src == dst) return fail(TL_E_ARG, "a lane cannot be forked onto itself");
+  const Lane sl = m->lanes[src];
+  if (!sl.live) return fail(TL_E_STATE, "lane %d was never prefilled", src);
+  if (prefix_len < 1 || prefix_len > sl.len)
+    return fail(TL_E_ARG, "prefix_len %d outside [1, %d]", prefix_len, sl.len);
+  if (max_new < 0) return fail(TL_E_ARG, "max_new_tokens < 0");
+  if (prefix_len + max_new > c.max_pos)
+    return fail(TL_E_STATE, "fork needs %d positions > max_pos %d", prefix_len + max_new, c.max_pos);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  tl::KvArena arena = m->arena;
+  if (m->lanes[dst].live) arena.release(m->lanes[dst].off, m->lanes[dst].elems);
+  Lane ln;
+  ln.live = true;
+  ln.len = prefix_len;
+  ln.cap = prefix_len + max_new;
+  ln.ceiling = sl.ceiling;
+  ln.nslots = lane_slots(c, sl.ceiling);   // slots below the ceiling lead the lane's layout
+  ln.elems = lane_elems(m, sl.ceiling, ln.cap);
+  ln.pending = sl.pending && prefix_len == sl.len;
+  if (!arena.alloc(ln.elems, &ln.off))
+    return fail(TL_E_STATE, "KV arena full (lane %d needs %llu elements)", dst, (unsigned long long)ln.elems);
+  std::vector<int64_t> loff = m->h_lane_off;
+  std::vector<int32_t> lcap = m->h_lane_cap;
+  loff[dst] = (int64_t)ln.off;
+  lcap[dst] = ln.cap;
+  Stage st;
+  const size_t o_loff = st.add(loff), o_lcap = st.add(lcap);
+  TRY(stage_upload(m, st, s));
+  // every (slot, K/V, head) block is [cap][head_dim]: copy its first prefix_len rows
+  const size_t row = (size_t)c.head_dim * m->esz;
+  uint8_t* kvb = static_cast<uint8_t*>(m->kv_base);
+  HIPCHK(hipMemcpy2DAsync(kvb + ln.off * m->esz, (size_t)ln.cap * row, kvb + sl.off * m->esz, (size_t)sl.cap * row,
+                          (size_t)prefix_len * row, (size_t)ln.nslots * 2 * c.n_heads, hipMemcpyDeviceToDevice, s));
+  if (ln.pending) HIPCHK(hipMemcpyAsync(m->d_pending + dst, m->d_pending + src, 4, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(m->d_lane_off, staged<int64_t>(m, o_loff), loff.size() * 8, hipMemcpyDeviceToDevice, s));
+  HIPCHK(hipMemcpyAsync(m->d_lane_cap, staged<int32_t>(m, o_lcap), lcap.size() * 4, hipMemcpyDeviceToDevice, s));
+  m->arena = arena;
+  m->lanes[dst] = ln;
+  m->h_lane_off = loff;
+  m->h_lane_cap = lcap;
+  return TL_OK;
+}
+
 tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int32_t* req_L,
                          const int32_t* in_tokens, int32_t* out_tokens, float* out_logits, float* out_hidden,
                          int32_t* out_eff_L, int32_t* out_log, void* stream) {
@@ -1036,6 +1167,7 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
     const Lane& ln = m->lanes[l];
     if (!ln.live) return fail(TL_E_STATE, "lane %d was never prefilled", l);
     if (ln.len >= ln.cap) return fail(TL_E_STATE, "lane %d is full (%d positions)", l, ln.cap);
+    if (!in_tokens && !ln.pending) return fail(TL_E_STATE, "lane %d holds no pending token (append first)", l);
     eff[i] = std::min(req_L[i], ln.ceiling);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1072,6 +1204,7 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
   for (int i = 0; i < n; ++i) {
     Lane& ln = m->lanes[lanes[i]];
     ln.len += 1;
+    ln.pending = true;
     ln.ceiling = eff[i];
     if (out_eff_L) out_eff_L[i] = eff[i];
   }
@@ -1120,6 +1253,7 @@ tl_status tl_decode_step_ee(tl_model* m, int32_t n, const int32_t* lanes, const 
     const Lane& ln = m->lanes[l];
     if (!ln.live) return fail(TL_E_STATE, "lane %d was never prefilled", l);
     if (ln.len >= ln.cap) return fail(TL_E_STATE, "lane %d is full (%d positions)", l, ln.cap);
+    if (!in_tokens && !ln.pending) return fail(TL_E_STATE, "lane %d holds no pending token (append first)", l);
     eff[i] = std::min(req_L[i], ln.ceiling);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1162,6 +1296,7 @@ tl_status tl_decode_step_ee(tl_model* m, int32_t n, const int32_t* lanes, const 
     Lane& ln = m->lanes[lanes[i]];
     const int e = m->ee_eff_host[i];
     ln.len += 1;
+    ln.pending = true;
     ln.ceiling = e;
     if (out_eff_L) out_eff_L[i] = e;
   }
@@ -1250,6 +1385,7 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
     const Lane& ln = m->lanes[l];
     if (!ln.live) return fail(TL_E_STATE, "lane %d was never prefilled", l);
     if (ln.len + n_steps > ln.cap) return fail(TL_E_STATE, "lane %d has room for %d more positions", l, ln.cap - ln.len);
+    if (!ln.pending) return fail(TL_E_STATE, "lane %d holds no pending token (append first)", l);
     for (int t = 0; t < n_steps; ++t)
       if (L_req[(int64_t)i * n_steps + t] < 1) return fail(TL_E_ARG, "requested L < 1 (lane %d step %d)", l, t);
   }

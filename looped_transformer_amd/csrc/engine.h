@@ -32,6 +32,7 @@ struct Lane {
   int32_t ceiling = 0;    // depth bound of the next token
   int32_t nslots = 0;
   uint64_t off = 0, elems = 0;
+  bool pending = false;   // a greedy next token is held on the device
 };
 
 // One matrix in kernel row order: dense [N, K] in the operand dtype, or INT4

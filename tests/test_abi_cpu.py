@@ -39,6 +39,8 @@ def test_null_arguments_rejected(L):
     assert L.tl_decode_step(None, 1, None, None, None, None, None, None, None, None, None) == tl.TL_E_ARG
     assert L.tl_decode_run(None, 1, None, 1, None, None, None, None, None, 1, None) == tl.TL_E_ARG
     assert L.tl_decode_step_ee(None, 1, None, None, None, None, None, None, None, None, None) == tl.TL_E_ARG
+    assert L.tl_append(None, 1, None, None, None, None, None, None, None, None, None) == tl.TL_E_ARG
+    assert L.tl_lane_fork(None, 0, 1, 1, 0, None) == tl.TL_E_ARG
     assert L.tl_lane_release(None, 0) == tl.TL_E_ARG
 
 
