@@ -35,6 +35,7 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-prefix", action="store_true", help="skip the shared-prefix measurement")
     ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one (no graph replay)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -167,6 +168,8 @@ def main():
 
     if not args.no_decode:
         out["decode_L8"] = decode_bench(tl, torch, np, synth, kv_bytes, load_model)
+    if not args.no_prefix:
+        out["shared_prefix"] = prefix_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_cpu_baseline:
         log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -217,6 +220,71 @@ def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
     }
     res["early_exit"] = {k: run(lambda kw=kw: tl.tl_decode_step_ee(model, lanes, Ls, out, **kw))
                          for k, kw in ee.items()}
+    tl.tl_free(model)
+    return res
+
+
+def prefix_bench(tl, torch, np, synth, kv_bytes, load_model):
+    """Requests that share a prompt prefix, on the INT4 model at L = 8: each request
+    is the prefix plus 16 tokens of its own, then 32 greedy tokens (the first from
+    the prompt pass, 31 cached steps).  NO_CACHE prefills every full prompt (one
+    batched pass); SHARED prefills the prefix once, forks it into every request's
+    lane and appends the suffixes (one batched pass).  Wall time of the whole job,
+    best of two runs."""
+    spec = synth.SPECS[2]
+    log("shared prefix: INT4 model")
+    w = synth.make_weights(spec, 0)
+    suffix, new, L = 16, 32, 8
+    cases = [(500, 10), (1024, 10), (1024, 50)]
+    n_max = max(n for _, n in cases)
+    P_max = max(p for p, _ in cases)
+    cap = P_max + suffix + new
+    model = load_model(w, max_lanes=n_max + 1, max_pos=cap, max_L=L,
+                       kv_arena_bytes=kv_bytes(spec, [L] * (n_max + 1), [cap] * (n_max + 1)) * 3 // 2)
+    out_tok = torch.empty(n_max, dtype=torch.int32, device="cuda")
+    res = {"config": "INT4 loop block (2048-wide, vocab 50304), L=8; each request = shared prefix + 16 own tokens, "
+                     "then 32 greedy tokens; wall time of all requests, best of 2"}
+    for P, n in cases:
+        prefix = synth.tokens(0, synth.STREAM_PROMPT_TOKENS, P, spec.vocab)
+        sufs = synth.tokens(0, synth.STREAM_PROMPT_TOKENS + 1, n * suffix, spec.vocab).reshape(n, suffix)
+        full = torch.tensor(np.concatenate([np.concatenate([prefix, sufs[i]]) for i in range(n)]),
+                            dtype=torch.int32, device="cuda")
+        pre = torch.tensor(prefix, dtype=torch.int32, device="cuda")
+        suf = torch.tensor(sufs.reshape(-1), dtype=torch.int32, device="cuda")
+        lanes = np.arange(n, dtype=np.int32)
+        Ls = np.full(n, L, np.int32)
+        out = out_tok[:n]
+
+        def decode():
+            for _ in range(new - 1):
+                tl.tl_decode_step(model, lanes, Ls, out)
+
+        def no_cache():
+            cu = np.arange(0, n * (P + suffix) + 1, P + suffix, dtype=np.int32)
+            tl.tl_forward(model, cu, full, L=L, lanes=lanes, max_new_tokens=new)
+            decode()
+
+        def shared():
+            tl.tl_forward(model, np.array([0, P], np.int32), pre, L=L, lanes=[n_max], max_new_tokens=0)
+            for i in range(n):
+                tl.tl_lane_fork(model, n_max, i, P, max_new_tokens=suffix + new)
+            tl.tl_append(model, np.arange(0, n * suffix + 1, suffix, dtype=np.int32), suf, lanes, Ls)
+            decode()
+
+        row = {}
+        for name, fn in (("no_cache_ms", no_cache), ("shared_ms", shared)):
+            best = None
+            for _ in range(2):
+                torch.cuda.synchronize()
+                t0 = time.perf_counter()
+                fn()
+                torch.cuda.synchronize()
+                el = (time.perf_counter() - t0) * 1e3
+                best = el if best is None else min(best, el)
+            row[name] = round(best, 2)
+        row["speedup"] = round(row["no_cache_ms"] / row["shared_ms"], 2)
+        res["prefix%d_requests%d" % (P, n)] = row
+        log("prefix %d, %d requests: %s" % (P, n, row))
     tl.tl_free(model)
     return res
 
