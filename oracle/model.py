@@ -48,7 +48,7 @@ __all__ = [
     "OracleModel", "Lane", "prefill", "decode_step", "forward_batch", "forward_ragged",
     "greedy_argmax", "clamp_depths", "active_lists", "bf16_bits_to_float",
     "EarlyExit", "probe_iteration", "relative_delta", "logit_margin", "decode_step_ee",
-    "append", "fork",
+    "append", "fork", "truncate", "speculative_decode",
 ]
 
 
@@ -414,6 +414,60 @@ def fork(lane: Lane, prefix_len: int) -> Lane:
     return Lane(tokens=list(lane.tokens[:P]), kv=kv, ceiling=lane.ceiling,
                 pending=lane.pending if whole else -1,
                 hidden_last=lane.hidden_last.copy() if whole and lane.hidden_last is not None else None)
+
+
+# ---------------------------------------------------------------------------
+# self-speculative decoding ([DYN] "Self-Speculative Decoding": draft at a low L,
+# verify at a high L with the same weights; [CLI] "speculate": --draft-loops,
+# --verify-loops, --draft-ahead, greedy at temperature 0)
+
+
+def truncate(lane: Lane, n: int) -> None:
+    """Drop every position from n on, in every cache slot (a rejected draft)."""
+    assert 0 <= n <= len(lane.tokens)
+    lane.tokens = lane.tokens[:n]
+    lane.kv = {key: (k[:n], v[:n]) for key, (k, v) in lane.kv.items()}
+
+
+def speculative_decode(m: OracleModel, lane: Lane, L_draft: int, L_verify: int, draft_ahead: int, n_tokens: int):
+    """n_tokens greedy tokens at depth L_verify, proposed draft_ahead at a time at depth L_draft.
+
+    A round starts from the lane's pending token t at position p (the lane's
+    length).  Draft: draft_ahead cached greedy steps at depth min(L_draft, L) on
+    the lane's own cache, t first, each step's token fed to the next; the lane's
+    ceiling is not lowered.  Verify: the lane is cut back to p and
+    [t, d_1 .. d_k] are appended at depth L = min(L_verify, ceiling) in one cached
+    pass, which rewrites every slot at those positions; g_i is the greedy token
+    after row i.  The drafts are accepted while d_i == g_(i-1); with a accepted
+    (at most the tokens still wanted minus one), the round emits g_0 .. g_a, the
+    lane keeps t, d_1 .. d_a and g_a becomes its pending token.  The emitted
+    sequence is the one greedy decoding at depth L produces.
+    Returns (tokens [n_tokens], accepted drafts per round).
+    """
+    assert draft_ahead >= 0 and n_tokens >= 1
+    Lv = min(int(L_verify), lane.ceiling)
+    Ld = min(int(L_draft), Lv)
+    out, accepted = [], []
+    while len(out) < n_tokens:
+        want = n_tokens - len(out)
+        p, t = len(lane.tokens), lane.pending
+        drafts, tok = [], t
+        for _ in range(draft_ahead):
+            _, _, tok, _ = decode_step(m, lane, Ld, token=tok)
+            lane.ceiling = Lv                      # a draft does not lower the depth bound
+            drafts.append(tok)
+        truncate(lane, p)
+        _, logits = append(m, lane, [t] + drafts, Lv, want_logits="all")
+        g = [int(greedy_argmax(row)) for row in logits]
+        a = 0
+        while a < len(drafts) and drafts[a] == g[a]:
+            a += 1
+        a = min(a, want - 1)
+        truncate(lane, p + a + 1)
+        lane.pending = g[a]
+        out.extend(g[:a + 1])
+        accepted.append(a)
+    return out, accepted
 
 
 # ---------------------------------------------------------------------------

@@ -569,3 +569,70 @@ def test_fork_then_append_equals_full_prefill(tiny):
             assert np.allclose(hc, hw, rtol=1e-11, atol=1e-13) and nc == nw
     _kv_close(src, ref_src, tol=0.0)
     assert src.tokens == ref_src.tokens and src.pending == ref_src.pending
+
+
+# ---------------------------------------------------------------------------
+# self-speculative decoding: the output is greedy decoding at the verify depth
+
+
+def _plain_greedy(m, lane, L, n):
+    out = []
+    for _ in range(n):
+        out.append(oracle.decode_step(m, lane, L)[2])
+    return out
+
+
+@pytest.mark.parametrize("Ld,k", [(2, 4), (4, 3), (6, 1), (1, 5)])
+def test_speculative_equals_greedy_at_verify_depth(tiny, Ld, k):
+    w, m = tiny
+    toks = synth.tokens(0, 3300, 11, 256)
+    a = oracle.prefill(m, toks, 8)[0]
+    b = oracle.prefill(m, toks, 8)[0]
+    got, acc = oracle.speculative_decode(m, a, Ld, 8, k, 17)
+    want = _plain_greedy(m, b, 8, 17)
+    assert got == want
+    assert sum(x + 1 for x in acc) == 17 and all(0 <= x <= k for x in acc)
+    assert a.tokens == b.tokens and a.pending == b.pending and a.ceiling == b.ceiling == 8
+    for key in b.kv:
+        if key[0] == "loop" and key[1] > 8:
+            continue
+        for x, y in zip(a.kv[key], b.kv[key]):
+            assert x.shape == y.shape and np.allclose(x, y, rtol=1e-11, atol=1e-13), key
+
+
+def test_speculative_equal_depths_accepts_every_draft(tiny):
+    w, m = tiny
+    toks = synth.tokens(0, 3301, 9, 256)
+    lane = oracle.prefill(m, toks, 5)[0]
+    got, acc = oracle.speculative_decode(m, lane, 5, 5, 3, 14)
+    assert acc == [3, 3, 3, 1]                    # 4 + 4 + 4 + 2 tokens, the last round capped
+    assert got == _plain_greedy(m, oracle.prefill(m, toks, 5)[0], 5, 14)
+
+
+def test_speculative_without_drafts_is_plain_decode(tiny):
+    w, m = tiny
+    toks = synth.tokens(0, 3302, 7, 256)
+    got, acc = oracle.speculative_decode(m, oracle.prefill(m, toks, 6)[0], 2, 6, 0, 6)
+    assert acc == [0] * 6 and got == _plain_greedy(m, oracle.prefill(m, toks, 6)[0], 6, 6)
+
+
+def test_speculative_wrong_drafts_change_nothing(tiny, monkeypatch):
+    """A planted draft that always proposes a wrong token: nothing is accepted and
+    the output is still greedy decoding at the verify depth."""
+    w, m = tiny
+    toks = synth.tokens(0, 3303, 10, 256)
+    want = _plain_greedy(m, oracle.prefill(m, toks, 7)[0], 7, 9)
+    real = oracle.model.decode_step
+    lane = oracle.prefill(m, toks, 7)[0]
+    seen = {"n": 0}
+
+    def bad(m_, lane_, L, token=None):
+        h, lg, nxt, Le = real(m_, lane_, L, token=token)
+        seen["n"] += 1
+        p = len(lane_.tokens)                      # position of the next token
+        return h, lg, (want[min(p - 10, 8)] + 1) % 256, Le
+
+    monkeypatch.setattr(oracle.model, "decode_step", bad)
+    got, acc = oracle.speculative_decode(m, lane, 3, 7, 2, 9)
+    monkeypatch.undo()
+    assert seen["n"] > 0 and got == want and acc == [0] * 9
