@@ -236,6 +236,33 @@ tl_status tl_decode_step_ee(tl_model* m, int32_t n_lanes, const int32_t* lanes_h
                             float* out_logits_dev, float* out_hidden_dev, int32_t* out_eff_L_host,
                             void* stream);
 
+/* Self-speculative greedy decoding ("Dynamic-L Inference" page, "Self-Speculative
+ * Decoding": draft at a low L, verify at a high L with the same weights; "CLI
+ * Reference" page, "speculate": --draft-loops, --verify-loops, --draft-ahead at
+ * temperature 0).  Produces n_tokens greedy tokens per lane at depth
+ * Lv = min(L_verify, lane ceiling), the same tokens a sequence of tl_decode_step
+ * calls at Lv would give (up to fp32 summation order), in rounds:
+ *   draft: k = min(draft_ahead, tokens still wanted - 1) cached greedy steps at
+ *     depth min(L_draft, Lv) on the lane's own cache, starting from its pending
+ *     token (the ceiling is not lowered);
+ *   verify: [pending, d_1 .. d_k] appended at depth Lv in one cached pass, which
+ *     rewrites every slot at those positions;
+ *   accept: drafts are kept while each equals the verify pass's greedy token
+ *     before it; the round emits those verify tokens plus the one after the last
+ *     kept draft, which becomes the pending token; rejected positions are
+ *     dropped (the lane's length is cut back).
+ * The host waits for the stream once per round to read the accepted counts.
+ *   out_tokens_dev [n_lanes, n_tokens] int32: generated tokens.
+ *   out_accepted_host [n_lanes, n_tokens] or NULL: drafts accepted in each round,
+ *     -1 after the lane's last round.
+ * Lanes need n_tokens + draft_ahead free positions.  Lane ceilings become Lv.
+ * Errors: TL_E_ARG (NULL, lane out of range or repeated, depth < 1, draft_ahead
+ * outside [0, 64], n_tokens < 1), TL_E_STATE (lane never prefilled, no pending
+ * token, too little room), TL_E_OOM, TL_E_HIP. */
+tl_status tl_speculate(tl_model* m, int32_t n_lanes, const int32_t* lanes_host, int32_t L_draft,
+                       int32_t L_verify, int32_t draft_ahead, int32_t n_tokens, int32_t* out_tokens_dev,
+                       int32_t* out_accepted_host, void* stream);
+
 /* n_steps greedy tokens for each of n_lanes prefilled lanes, scheduled one loop
  * iteration at a time across lanes (continuous depth batching: "Continuous Depth
  * Batching" summary page).  A pool holds one in-flight token per lane, each at its

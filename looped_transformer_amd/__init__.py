@@ -75,6 +75,7 @@ def lib():
         "tl_forward": [_P, _I, _P, _P, _I, _P, _P, _I, _P, _P, _P, _P, _P],
         "tl_append": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "tl_lane_fork": [_P, _I, _I, _I, _I, _P],
+        "tl_speculate": [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P],
         "tl_decode_step": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
         "tl_decode_step_ee": [_P, _I, _P, _P, ctypes.POINTER(tl_early_exit), _P, _P, _P, _P, _P, _P],
         "tl_decode_run": [_P, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P],
@@ -227,6 +228,15 @@ def tl_append(model, cu_seqlens, tokens, lanes, per_seq_L, out_hidden=None, out_
 def tl_lane_fork(model, src_lane: int, dst_lane: int, prefix_len: int, max_new_tokens: int = 0, stream=None):
     _check(lib().tl_lane_fork(model.handle, int(src_lane), int(dst_lane), int(prefix_len), int(max_new_tokens),
                               _stream(stream)))
+
+
+def tl_speculate(model, lanes, L_draft, L_verify, draft_ahead, n_tokens, out_tokens, stream=None):
+    """Returns the accepted drafts per round, [n_lanes, n_tokens] int32 (-1 after the last round)."""
+    ln = _i32(lanes)
+    acc = np.zeros((len(ln), int(n_tokens)), np.int32)
+    _check(lib().tl_speculate(model.handle, len(ln), _ptr(ln), int(L_draft), int(L_verify), int(draft_ahead),
+                              int(n_tokens), _ptr(out_tokens), _ptr(acc), _stream(stream)))
+    return acc
 
 
 def tl_decode_step(model, lanes, per_lane_L, out_tokens, in_tokens=None, out_logits=None, out_hidden=None,

@@ -779,6 +779,7 @@ void tl_free(tl_model* m) {
   for (void* p : ps) dev_free(m, p);
   if (m->stage_host) (void)hipHostFree(m->stage_host);
   if (m->ee_eff_host) (void)hipHostFree(m->ee_eff_host);
+  if (m->sp_acc_host) (void)hipHostFree(m->sp_acc_host);
   if (m->stage_done) (void)hipEventDestroy(m->stage_done);
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   delete m;
@@ -1146,6 +1147,185 @@ tl_status tl_lane_fork(tl_model* m, int32_t src, int32_t dst, int32_t prefix_len
   m->lanes[dst] = ln;
   m->h_lane_off = loff;
   m->h_lane_cap = lcap;
+  return TL_OK;
+}
+
+// Buffers of self-speculative rounds for n lanes and k drafts.
+tl_status ensure_spec(tl_model* m, int n, int k, hipStream_t s) {
+  const int64_t need = (int64_t)n * (k + 1);
+  if (need <= m->sp_elems && m->sp_acc_host) return TL_OK;
+  HIPCHK(hipStreamSynchronize(s));
+  dev_free(m, m->sp_draft);
+  dev_free(m, m->sp_in);
+  dev_free(m, m->sp_g);
+  dev_free(m, m->sp_acc);
+  if (m->sp_acc_host) HIPCHK(hipHostFree(m->sp_acc_host));
+  m->sp_acc_host = nullptr;
+  m->sp_elems = 0;
+  const int64_t E = (need + 63) / 64 * 64;
+  m->sp_draft = static_cast<int32_t*>(dev_alloc(m, (size_t)E * 4));
+  m->sp_in = static_cast<int32_t*>(dev_alloc(m, (size_t)E * 4));
+  m->sp_g = static_cast<int32_t*>(dev_alloc(m, (size_t)E * 4));
+  m->sp_acc = static_cast<int32_t*>(dev_alloc(m, (size_t)E * 4));
+  HIPCHK(hipHostMalloc((void**)&m->sp_acc_host, (size_t)E * 4, hipHostMallocDefault));
+  if (!m->sp_draft || !m->sp_in || !m->sp_g || !m->sp_acc) return fail(TL_E_OOM, "speculative buffers");
+  m->sp_elems = E;
+  return TL_OK;
+}
+
+tl_status tl_speculate(tl_model* m, int32_t n, const int32_t* lanes, int32_t L_draft, int32_t L_verify,
+                       int32_t draft_ahead, int32_t n_tokens, int32_t* out_tokens, int32_t* out_accepted,
+                       void* stream) {
+  g_err.clear();
+  if (!m || !lanes || !out_tokens) return fail(TL_E_ARG, "NULL argument");
+  const tl_config& c = m->cfg;
+  if (n < 1) return fail(TL_E_ARG, "n_lanes must be >= 1");
+  if (L_draft < 1 || L_verify < 1) return fail(TL_E_ARG, "depths must be >= 1");
+  if (draft_ahead < 0 || draft_ahead > 64) return fail(TL_E_ARG, "draft_ahead %d outside [0, 64]", draft_ahead);
+  if (n_tokens < 1) return fail(TL_E_ARG, "n_tokens must be >= 1");
+  std::vector<char> seen(c.max_lanes, 0);
+  std::vector<int> Lv(n), Ld(n);
+  for (int i = 0; i < n; ++i) {
+    const int l = lanes[i];
+    if (l < 0 || l >= c.max_lanes) return fail(TL_E_ARG, "lane %d out of range [0, %d)", l, c.max_lanes);
+    if (seen[l]) return fail(TL_E_ARG, "lane %d listed twice", l);
+    seen[l] = 1;
+    const Lane& ln = m->lanes[l];
+    if (!ln.live) return fail(TL_E_STATE, "lane %d was never prefilled", l);
+    if (!ln.pending) return fail(TL_E_STATE, "lane %d holds no pending token (append first)", l);
+    if (ln.len + n_tokens + draft_ahead > ln.cap)
+      return fail(TL_E_STATE, "lane %d needs %d free positions, has %d", l, n_tokens + draft_ahead, ln.cap - ln.len);
+    Lv[i] = std::min(L_verify, ln.ceiling);
+    Ld[i] = std::min(L_draft, Lv[i]);
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int K = draft_ahead;
+  TRY(ensure_ws(m, n * (K + 1), n * (K + 1), 0, s));
+  TRY(ensure_spec(m, n, K, s));
+  if (out_accepted)
+    for (int64_t x = 0; x < (int64_t)n * n_tokens; ++x) out_accepted[x] = -1;
+  const KVParams kvp{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
+  const bool tiled = attn_tiled_supported(m->act, c.head_dim);
+  std::vector<int> emitted(n, 0), rounds(n, 0);
+  for (;;) {
+    // lanes still generating, and this round's draft count
+    std::vector<int> act;
+    int max_want = 0;
+    for (int i = 0; i < n; ++i)
+      if (emitted[i] < n_tokens) {
+        act.push_back(i);
+        max_want = std::max(max_want, n_tokens - emitted[i]);
+      }
+    if (act.empty()) break;
+    const int na = (int)act.size();
+    const int k = std::min(K, max_want - 1);
+    std::vector<int32_t> alanes(na), want(na), emit(na), slot(na);
+    std::vector<int> pos0(na), lv(na), ld(na);
+    for (int a = 0; a < na; ++a) {
+      const int i = act[a];
+      alanes[a] = lanes[i];
+      want[a] = n_tokens - emitted[i];
+      emit[a] = emitted[i];
+      slot[a] = i;
+      pos0[a] = m->lanes[lanes[i]].len;
+      lv[a] = Lv[i];
+      ld[a] = Ld[i];
+    }
+    // descriptors: k draft steps (one row per lane), then the verify pass
+    Stage st;
+    std::vector<size_t> o_drows(k);
+    for (int r = 0; r < k; ++r) {
+      std::vector<RowInfo> rows(na);
+      for (int a = 0; a < na; ++a) {
+        rows[a] = RowInfo{};
+        rows[a].orig = a;
+        rows[a].lane = alanes[a];
+        rows[a].pos = pos0[a] + r;
+        rows[a].depth = ld[a];
+        rows[a].iter = 1;
+      }
+      o_drows[r] = st.add(rows);
+    }
+    const int T = na * (k + 1);
+    std::vector<RowInfo> vrows(T);
+    std::vector<int> vdepth(T), slen(na, k + 1);
+    for (int a = 0; a < na; ++a)
+      for (int q = 0; q <= k; ++q) {
+        RowInfo& r = vrows[a * (k + 1) + q];
+        r = RowInfo{};
+        r.orig = a * (k + 1) + q;
+        r.lane = alanes[a];
+        r.pos = pos0[a] + q;
+        r.depth = lv[a];
+        r.iter = 1;
+        vdepth[a * (k + 1) + q] = lv[a];
+      }
+    const std::vector<int> v_act = active_counts(vdepth);
+    std::vector<std::vector<AttnTile>> tile_lists;
+    if (tiled)
+      for (size_t j = 1; j <= v_act.size(); ++j) {
+        tile_lists.emplace_back();
+        add_tiles(tile_lists.back(), slen, std::vector<int>(alanes.begin(), alanes.end()), lv, (int)j, &pos0);
+      }
+    std::vector<size_t> o_tiles;
+    for (auto& tlst : tile_lists) o_tiles.push_back(st.add(tlst));
+    const size_t o_vrows = st.add(vrows), o_lanes = st.add(alanes), o_want = st.add(want), o_emit = st.add(emit),
+                 o_slot = st.add(slot);
+    TRY(stage_upload(m, st, s));
+    const int32_t* lanes_dev = staged<int32_t>(m, o_lanes);
+    // draft: k cached greedy steps at the draft depth, the ceiling left alone
+    for (int r = 0; r < k; ++r) {
+      const int32_t* toks;
+      if (r == 0) {
+        HIPCHK(launch_gather_i32(m->d_pending, lanes_dev, na, m->ws.tok, s));
+        toks = m->ws.tok;
+      } else {
+        toks = m->sp_draft + (int64_t)(r - 1) * na;
+      }
+      std::vector<int> dd(ld.begin(), ld.end());
+      Pass p;
+      p.n = na;
+      p.tokens = toks;
+      p.rows0 = staged<RowInfo>(m, o_drows[r]);
+      p.n_active = active_counts(dd);
+      p.kv = kvp;
+      p.final_h = m->ws.hX;
+      TRY(run_pass(m, p, s));
+      TRY(run_head(m, p.final_h, nullptr, na, nullptr, m->sp_draft + (int64_t)r * na, nullptr, s));
+    }
+    // verify: [pending, d_1 .. d_k] of every lane in one cached pass at the verify depth
+    HIPCHK(launch_spec_pack(m->d_pending, lanes_dev, m->sp_draft, na, k, m->sp_in, s));
+    {
+      Pass p;
+      p.n = T;
+      p.tokens = m->sp_in;
+      p.rows0 = staged<RowInfo>(m, o_vrows);
+      p.n_active = v_act;
+      for (size_t q = 0; q < tile_lists.size(); ++q) {
+        p.tiles.push_back(staged<AttnTile>(m, o_tiles[q]));
+        p.n_tiles.push_back((int)tile_lists[q].size());
+      }
+      p.kv = kvp;
+      p.final_h = m->ws.hX;
+      TRY(run_pass(m, p, s));
+      TRY(run_head(m, p.final_h, nullptr, T, nullptr, m->sp_g, nullptr, s));
+    }
+    HIPCHK(launch_spec_accept(m->sp_draft, m->sp_g, lanes_dev, staged<int32_t>(m, o_want), staged<int32_t>(m, o_emit),
+                              staged<int32_t>(m, o_slot), na, k, n_tokens, out_tokens, m->d_pending, m->sp_acc, s));
+    HIPCHK(hipMemcpyAsync(m->sp_acc_host, m->sp_acc, (size_t)na * 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(hipStreamSynchronize(s));
+    for (int a = 0; a < na; ++a) {
+      const int i = act[a], acc = m->sp_acc_host[a];
+      if (acc < 0 || acc > k || acc >= want[a]) return fail(TL_E_HIP, "accept count %d out of range", acc);
+      Lane& ln = m->lanes[lanes[i]];
+      ln.len = pos0[a] + acc + 1;
+      ln.ceiling = lv[a];
+      ln.pending = true;
+      if (out_accepted) out_accepted[(int64_t)i * n_tokens + rounds[i]] = acc;
+      emitted[i] += acc + 1;
+      rounds[i] += 1;
+    }
+  }
   return TL_OK;
 }
 

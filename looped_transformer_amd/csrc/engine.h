@@ -126,6 +126,13 @@ struct tl_model {
   float* ee_margin = nullptr;          // [ee_rows]
   int32_t* ee_eff_host = nullptr;      // pinned mirror of ee_eff
   int ee_rows = 0;
+  // self-speculative decoding (allocated on first use)
+  int32_t* sp_draft = nullptr;         // [k, n] drafted tokens, step-major
+  int32_t* sp_in = nullptr;            // [n, k + 1] tokens of the verify pass
+  int32_t* sp_g = nullptr;             // [n, k + 1] greedy token after each verify row
+  int32_t* sp_acc = nullptr;           // [n] accepted drafts of the round
+  int32_t* sp_acc_host = nullptr;      // pinned mirror of sp_acc
+  int64_t sp_elems = 0;                // capacity of the [n, k + 1] buffers
   // kernel-class timing (measurement only)
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;

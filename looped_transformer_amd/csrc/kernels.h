@@ -122,6 +122,16 @@ hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, const f
 // margin != NULL, margin[i] = top-1 minus top-2 logit (a repeated maximum gives 0).
 hipError_t launch_argmax_reduce(const float* pv, const int32_t* pi, const float* pv2, int n, int tiles, int32_t* out,
                                 int32_t* out2, const int32_t* scatter, float* margin, hipStream_t s);
+// Self-speculative round: in[i, 0] = pending[lanes[i]], in[i, c] = draft[c - 1, i]
+// (draft step-major [k, n]); n lanes, k drafts.
+hipError_t launch_spec_pack(const int32_t* pending, const int32_t* lanes, const int32_t* draft, int n, int k,
+                            int32_t* in, hipStream_t s);
+// Accept rule per lane i: a = leading drafts with draft[r, i] == g[i, r], capped at
+// want[i] - 1; out[slot[i] * n_tokens + emitted[i] + c] = g[i, c] for c <= a,
+// pending[lanes[i]] = g[i, a], acc[i] = a.
+hipError_t launch_spec_accept(const int32_t* draft, const int32_t* g, const int32_t* lanes, const int32_t* want,
+                              const int32_t* emitted, const int32_t* slot, int n, int k, int n_tokens,
+                              int32_t* out, int32_t* pending, int32_t* acc, hipStream_t s);
 hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);

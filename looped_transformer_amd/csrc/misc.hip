@@ -233,6 +233,32 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* __restr
   }
 }
 
+// ---------------------------------------------------------------- self-speculative rounds
+__global__ void spec_pack_kernel(const int32_t* __restrict__ pending, const int32_t* __restrict__ lanes,
+                                 const int32_t* __restrict__ draft, int n, int k, int32_t* __restrict__ in) {
+  const int idx = blockIdx.x * 256 + threadIdx.x;
+  if (idx >= n * (k + 1)) return;
+  const int i = idx / (k + 1), c = idx - i * (k + 1);
+  in[idx] = c == 0 ? pending[lanes[i]] : draft[(c - 1) * n + i];
+}
+
+__global__ void spec_accept_kernel(const int32_t* __restrict__ draft, const int32_t* __restrict__ g,
+                                   const int32_t* __restrict__ lanes, const int32_t* __restrict__ want,
+                                   const int32_t* __restrict__ emitted, const int32_t* __restrict__ slot, int n,
+                                   int k, int n_tokens, int32_t* __restrict__ out, int32_t* __restrict__ pending,
+                                   int32_t* __restrict__ acc) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= n) return;
+  const int32_t* gi = g + (int64_t)i * (k + 1);
+  int a = 0;
+  while (a < k && draft[a * n + i] == gi[a]) ++a;
+  a = min(a, want[i] - 1);
+  int32_t* o = out + (int64_t)slot[i] * n_tokens + emitted[i];
+  for (int c = 0; c <= a; ++c) o[c] = gi[c];
+  pending[lanes[i]] = gi[a];
+  acc[i] = a;
+}
+
 __global__ __launch_bounds__(256) void gather_rows_kernel(const float* __restrict__ src, const int32_t* __restrict__ idx,
                                                          int d, float* __restrict__ dst) {
   const int r = blockIdx.x;
@@ -404,6 +430,22 @@ hipError_t launch_argmax_reduce(const float* pv, const int32_t* pi, const float*
                                 int32_t* out2, const int32_t* scatter, float* margin, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(argmax_reduce_kernel, dim3(n), dim3(256), 0, s, pv, pi, pv2, tiles, out, out2, scatter, margin);
+  return hipGetLastError();
+}
+
+hipError_t launch_spec_pack(const int32_t* pending, const int32_t* lanes, const int32_t* draft, int n, int k,
+                            int32_t* in, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(spec_pack_kernel, dim3((n * (k + 1) + 255) / 256), dim3(256), 0, s, pending, lanes, draft, n, k, in);
+  return hipGetLastError();
+}
+
+hipError_t launch_spec_accept(const int32_t* draft, const int32_t* g, const int32_t* lanes, const int32_t* want,
+                              const int32_t* emitted, const int32_t* slot, int n, int k, int n_tokens,
+                              int32_t* out, int32_t* pending, int32_t* acc, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(spec_accept_kernel, dim3((n + 255) / 256), dim3(256), 0, s, draft, g, lanes, want, emitted, slot, n,
+                     k, n_tokens, out, pending, acc);
   return hipGetLastError();
 }
 

@@ -41,6 +41,7 @@ def test_null_arguments_rejected(L):
     assert L.tl_decode_step_ee(None, 1, None, None, None, None, None, None, None, None, None) == tl.TL_E_ARG
     assert L.tl_append(None, 1, None, None, None, None, None, None, None, None, None) == tl.TL_E_ARG
     assert L.tl_lane_fork(None, 0, 1, 1, 0, None) == tl.TL_E_ARG
+    assert L.tl_speculate(None, 1, None, 2, 8, 4, 8, None, None, None) == tl.TL_E_ARG
     assert L.tl_lane_release(None, 0) == tl.TL_E_ARG
 
 
