@@ -36,6 +36,7 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefix", action="store_true", help="skip the shared-prefix measurement")
+    ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative measurement")
     ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one (no graph replay)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -170,6 +171,8 @@ def main():
         out["decode_L8"] = decode_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_prefix:
         out["shared_prefix"] = prefix_bench(tl, torch, np, synth, kv_bytes, load_model)
+    if not args.no_spec:
+        out["speculative_B1"] = spec_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_cpu_baseline:
         log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -285,6 +288,92 @@ def prefix_bench(tl, torch, np, synth, kv_bytes, load_model):
         row["speedup"] = round(row["no_cache_ms"] / row["shared_ms"], 2)
         res["prefix%d_requests%d" % (P, n)] = row
         log("prefix %d, %d requests: %s" % (P, n, row))
+    tl.tl_free(model)
+    return res
+
+
+def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
+    """Batch-1 greedy decode on the INT4 model, 32-token prompt, 64 new tokens:
+    plain steps at L = 8 against self-speculative decoding (drafts at L = 2, 4
+    ahead, verify at L = 8).  Random weights make the acceptance rate meaningless,
+    so the pieces of a round are timed as well: one draft step at L = 2, one
+    5-token verify pass at L = 8, one plain step at L = 8; with a drafts accepted
+    per round a round yields a + 1 tokens, which gives the acceptance at which
+    speculation breaks even."""
+    spec = synth.SPECS[2]
+    log("speculative: INT4 model, batch 1")
+    w = synth.make_weights(spec, 0)
+    plen, new, k = 32, 64, 4
+    cap = plen + new + k + 8
+    model = load_model(w, max_lanes=4, max_pos=cap, max_L=8, kv_arena_bytes=kv_bytes(spec, [8] * 4, [cap] * 4))
+    prompt = torch.tensor(synth.tokens(0, synth.STREAM_PROMPT_TOKENS, plen, spec.vocab), dtype=torch.int32,
+                          device="cuda")
+    cu = np.array([0, plen], np.int32)
+    out1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    outs = torch.empty(1, new, dtype=torch.int32, device="cuda")
+
+    def timed(fn, reps=3):
+        best = None
+        for _ in range(reps):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            fn()
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            best = el if best is None else min(best, el)
+        return best
+
+    def prefill(lane, L):
+        tl.tl_forward(model, cu, prompt, L=L, lanes=[lane], max_new_tokens=cap - plen)
+        torch.cuda.synchronize()
+
+    res = {"config": "INT4 model (2048-wide), batch 1, 32-token prompt, 64 greedy tokens; drafts at L=2, "
+                     "4 ahead, verify at L=8"}
+    acc_log = []
+
+    def plain():
+        prefill(0, 8)
+        for _ in range(new - 1):
+            tl.tl_decode_step(model, [0], [8], out1)
+
+    def specd():
+        prefill(1, 8)
+        acc_log.append(tl.tl_speculate(model, [1], 2, 8, k, new - 1, outs))
+
+    t_plain = timed(plain)
+    t_spec = timed(specd)
+    acc = [int(a) for a in acc_log[-1][0] if a >= 0]
+    res["plain_tok_per_s"] = round((new - 1) / t_plain, 1)
+    res["speculative_tok_per_s"] = round((new - 1) / t_spec, 1)
+    res["rounds"] = len(acc)
+    res["mean_accepted_per_round"] = round(float(np.mean(acc)), 3)
+
+    # pieces of a round (prefill excluded: each piece is timed over 20 repetitions)
+    def rep20(fn):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(20):
+            fn()
+        torch.cuda.synchronize()
+        return (time.perf_counter() - t0) / 20
+
+    prefill(2, 2)
+    t_draft = rep20(lambda: tl.tl_decode_step(model, [2], [2], out1, in_tokens=out1))
+    prefill(2, 8)
+    t_step = rep20(lambda: tl.tl_decode_step(model, [2], [8], out1, in_tokens=out1))
+    five = torch.zeros(k + 1, dtype=torch.int32, device="cuda")
+    prefill(3, 8)
+    t_verify = rep20(lambda: (tl.tl_lane_fork(model, 3, 2, plen, max_new_tokens=k + 1),
+                              tl.tl_append(model, [0, k + 1], five, [2], [8])))
+    res["draft_step_L2_ms"] = round(t_draft * 1e3, 4)
+    res["plain_step_L8_ms"] = round(t_step * 1e3, 4)
+    res["verify_5_tokens_L8_ms"] = round(t_verify * 1e3, 4)
+    round_ms = k * t_draft + t_verify
+    res["break_even_accepted_per_round"] = round(round_ms / t_step - 1, 3)
+    res["tok_per_s_if_all_accepted"] = round((k + 1) / round_ms, 1)
+    res["note"] = ("break-even and all-accepted figures are derived from the timed pieces (a round = 4 draft steps + "
+                   "one verify pass, yielding accepted + 1 tokens); the verify piece includes a fork of the "
+                   "32-token prompt")
     tl.tl_free(model)
     return res
 
