@@ -49,6 +49,7 @@ __all__ = [
     "greedy_argmax", "clamp_depths", "active_lists", "bf16_bits_to_float",
     "EarlyExit", "probe_iteration", "relative_delta", "logit_margin", "decode_step_ee",
     "append", "fork", "truncate", "speculative_decode",
+    "H_MODES", "round_to_operand", "quantize_h", "dequant_h", "h_store", "h_bytes_per_position",
 ]
 
 
@@ -176,6 +177,79 @@ def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
 
 
 # ---------------------------------------------------------------------------
+# iteration-axis KV compression: store-h ([CLI] environment variables
+# TINYLOOP_KV_H_MODE, with TINYLOOP_KV_INT8 / TINYLOOP_KV_INT4; [BENCH] section 9)
+#
+# Instead of K and V, a cache slot keeps the block's pre-QKV norm output x (one
+# row of d values per position); at attention time K and V of every cached
+# position are rebuilt by the block's own QKV projection.  "h" keeps x in the
+# operand type, "h8" / "h4" as symmetric codes in [-127, 127] / [-7, 7] with one
+# fp16 scale per (position, head).
+
+H_MODES = ("kv", "h", "h8", "h4")
+H_LEVELS = {"h8": 127, "h4": 7}
+
+
+def round_to_operand(x: np.ndarray, act: str) -> np.ndarray:
+    """x rounded to the operand type (fp32 / fp16 / bf16 with round-to-nearest-even)."""
+    x32 = np.asarray(x, dtype=np.float32)
+    if act == "f16":
+        return x32.astype(np.float16).astype(np.float64)
+    if act == "bf16":
+        b = x32.view(np.uint32).astype(np.uint64)
+        b = (b + 0x7FFF + ((b >> 16) & 1)) & 0xFFFF0000
+        return b.astype(np.uint32).view(np.float32).astype(np.float64)
+    return x32.astype(np.float64)
+
+
+def quantize_h(x_op: np.ndarray, n_heads: int, levels: int):
+    """Symmetric codes of operand-type rows [T, d], one scale per (row, head).
+
+    s = fp16(max|x| / levels) with the division in fp32; q = clamp(rint(x / s),
+    -levels, levels) with round-half-to-even and the division in fp32; a head whose
+    scale is 0 gets q = 0.  Returns (q int8 [T, d], s float16 [T, H]).
+    """
+    x = np.asarray(x_op, dtype=np.float32)
+    T, d = x.shape
+    xh = x.reshape(T, n_heads, d // n_heads)
+    a = np.abs(xh).max(axis=-1)
+    sc = (a / np.float32(levels)).astype(np.float16)
+    s32 = sc.astype(np.float32)[..., None]
+    with np.errstate(divide="ignore", invalid="ignore"):
+        q = np.where(s32 > 0, np.rint(xh / s32), 0.0)
+    q = np.clip(q, -levels, levels).astype(np.int8)
+    return q.reshape(T, d), sc
+
+
+def dequant_h(q: np.ndarray, sc: np.ndarray) -> np.ndarray:
+    """q * s per head, exact in float64."""
+    T, d = q.shape
+    H = sc.shape[1]
+    return (q.reshape(T, H, d // H).astype(np.float64) * sc.astype(np.float64)[..., None]).reshape(T, d)
+
+
+def h_store(x: np.ndarray, act: str, n_heads: int, mode: str) -> np.ndarray:
+    """The values a store-h slot holds for rows x (what K and V are rebuilt from)."""
+    x_op = round_to_operand(x, act)
+    if mode == "h":
+        return x_op
+    q, sc = quantize_h(x_op, n_heads, H_LEVELS[mode])
+    return dequant_h(q, sc)
+
+
+def h_bytes_per_position(d: int, n_heads: int, mode: str, operand_bytes: int = 2) -> int:
+    """Bytes one position takes in one slot: K and V, x in the operand type, or
+    codes (one byte, or half a byte packed two to a byte) plus fp16 scales."""
+    if mode == "kv":
+        return 2 * d * operand_bytes
+    if mode == "h":
+        return d * operand_bytes
+    if mode == "h8":
+        return d + 2 * n_heads
+    return d // 2 + 2 * n_heads
+
+
+# ---------------------------------------------------------------------------
 # model
 
 
@@ -205,6 +279,7 @@ class OracleModel:
     blocks: list
     w4: dict = field(default_factory=dict)   # (block, name) -> (q int8, s fp16)
     embed_kind: str = "f32"
+    kv_mode: str = "kv"                      # one of H_MODES: what a cache slot keeps
 
     @classmethod
     def from_weights(cls, w, dt=np.float64):
@@ -238,7 +313,9 @@ class OracleModel:
 
         past_k/past_v hold the lane's earlier positions in this block application's
         own cache slot ([CLI] TINYLOOP_KV_H_MODE: per-layer K/V buffers).  Returns the
-        new residual rows and the k, v rows to append to that slot.
+        new residual rows and the k, v rows to append to that slot.  In a store-h
+        mode the slot keeps h_store(x) rows instead (returned as k, with v empty),
+        and K, V of every position are rebuilt from them by this block's wqkv.
         """
         sp, W = self.spec, self.blocks[b]
         H, dh, d = sp.n_heads, sp.head_dim, sp.d_model
@@ -250,9 +327,19 @@ class OracleModel:
         v = qkv[:, 2 * d:].reshape(T, H, dh)
         cos, sin = rope_angles(pos, dh, sp.rope_base, self.dt)
         q = apply_rope(q, cos, sin)
-        k = apply_rope(k, cos, sin)
-        k_all = np.concatenate([past_k, k], axis=0)
-        v_all = np.concatenate([past_v, v], axis=0)
+        if self.kv_mode == "kv":
+            k = apply_rope(k, cos, sin)
+            k_all = np.concatenate([past_k, k], axis=0)
+            v_all = np.concatenate([past_v, v], axis=0)
+        else:
+            k = h_store(x, sp.act_dtype, H, self.kv_mode)          # the rows this slot keeps
+            v = np.zeros((T, 0), dtype=self.dt)
+            x_all = np.concatenate([past_k, k], axis=0)
+            S = x_all.shape[0]
+            kv_all = x_all @ W["wqkv"][d:].T
+            c_all, s_all = rope_angles(np.arange(S), dh, sp.rope_base, self.dt)
+            k_all = apply_rope(kv_all[:, :d].reshape(S, H, dh), c_all, s_all)
+            v_all = kv_all[:, d:].reshape(S, H, dh)
         o = causal_attention(q, k_all, v_all, pos)
         h = h + o @ W["wo"].T
         x2 = rmsnorm(h, W["norm2"], sp.rms_eps)
@@ -266,6 +353,8 @@ class OracleModel:
 
     def empty_kv(self):
         sp = self.spec
+        if self.kv_mode != "kv":
+            return np.zeros((0, sp.d_model), dtype=self.dt), np.zeros((0, 0), dtype=self.dt)
         z = np.zeros((0, sp.n_heads, sp.head_dim), dtype=self.dt)
         return z, z
 

@@ -636,3 +636,91 @@ def test_speculative_wrong_drafts_change_nothing(tiny, monkeypatch):
     got, acc = oracle.speculative_decode(m, lane, 3, 7, 2, 9)
     monkeypatch.undo()
     assert seen["n"] > 0 and got == want and acc == [0] * 9
+
+
+# ---------------------------------------------------------------------------
+# store-h cache modes (iteration-axis KV compression)
+
+
+def test_store_h_bytes_match_the_pages(golden_dir):
+    for row in _read_lines(os.path.join(golden_dir, "store_h_bytes.txt")):
+        mode, d, H, nbytes = row.split()
+        assert oracle.h_bytes_per_position(int(d), int(H), mode) == int(nbytes), mode
+
+
+def test_round_to_operand_against_torch():
+    rng = np.random.default_rng(5)
+    x = np.concatenate([rng.standard_normal(4000) * 10.0 ** rng.integers(-6, 4, 4000),
+                        [0.0, -0.0, 1.0, 65504.0, 1e-8, 3.0e38]])
+    t = torch.from_numpy(x.astype(np.float32))
+    assert np.array_equal(oracle.round_to_operand(x, "bf16"), t.to(torch.bfloat16).to(torch.float64).numpy())
+    small = x[np.abs(x) < 6e4]
+    ts = torch.from_numpy(small.astype(np.float32))
+    assert np.array_equal(oracle.round_to_operand(small, "f16"), ts.to(torch.float16).to(torch.float64).numpy())
+
+
+def test_quantize_h_hand_example_and_bounds():
+    # one row, two heads of 4: head 0 max 2.54 -> s = fp16(0.02) , head 1 all zero
+    x = np.array([[2.54, -1.27, 0.01, 0.03, 0.0, 0.0, 0.0, 0.0]], np.float32)
+    q, s = oracle.quantize_h(x, 2, 127)
+    s0 = np.float32(np.float16(np.float32(2.54) / np.float32(127)))
+    assert s[0, 0] == np.float16(s0) and s[0, 1] == 0
+    assert q[0, :4].tolist() == [int(np.rint(np.float32(v) / s0)) for v in x[0, :4]]
+    assert q[0, 4:].tolist() == [0, 0, 0, 0]
+    # ties go to even: x / s = 2.5 and 3.5 exactly (s a power of two)
+    xt = np.array([[0.625, 0.875, 31.75, -31.75]], np.float32)     # max 31.75 -> s = 0.25
+    qt, st = oracle.quantize_h(xt, 1, 127)
+    assert float(st[0, 0]) == 0.25 and qt[0].tolist() == [2, 4, 127, -127]
+    rng = np.random.default_rng(9)
+    for levels in (127, 7):
+        xr = (rng.standard_normal((64, 96)) * rng.uniform(0.01, 3, (64, 1))).astype(np.float32)
+        q, s = oracle.quantize_h(xr, 3, levels)
+        back = oracle.dequant_h(q, s)
+        s_el = np.repeat(s.astype(np.float64), 32, axis=1)
+        assert np.all(np.abs(back - xr) <= 0.5 * s_el * (1 + 1e-3) + 1e-12)
+        assert np.all(np.abs(q).reshape(64, 3, 32).max(axis=-1) == levels)
+
+
+@pytest.mark.parametrize("mode", ["h", "h8", "h4"])
+def test_store_h_identity_store_equals_kv_mode(tiny, mode, monkeypatch):
+    """With a store that keeps x unchanged, rebuilding K/V from the slot's rows
+    reproduces the K/V cache mode (positions and projection of the rebuild)."""
+    import copy
+    w, m = tiny
+    mh = copy.copy(m)
+    mh.kv_mode = mode
+    monkeypatch.setattr(oracle.model, "h_store", lambda x, act, H, md: np.array(x, dtype=np.float64))
+    toks = synth.tokens(0, 3400, 12, 256)
+    a, ha, la = oracle.prefill(m, toks, 4, want_logits="all")
+    b, hb, lb = oracle.prefill(mh, toks, 4, want_logits="all")
+    assert np.allclose(ha, hb, rtol=1e-11, atol=1e-13) and np.allclose(la, lb, rtol=1e-10, atol=1e-12)
+    for _ in range(3):
+        xa = oracle.decode_step(m, a, 4)
+        xb = oracle.decode_step(mh, b, 4)
+        assert np.allclose(xa[0], xb[0], rtol=1e-11, atol=1e-13) and xa[2] == xb[2]
+
+
+@pytest.mark.parametrize("mode", ["h", "h8", "h4"])
+def test_store_h_cached_equals_uncached(mode):
+    """Compression is per position, so cached decode == a prefill of the extended
+    sequence in the same mode (bf16 model: operand rounding and both code widths)."""
+    import copy
+    spec = synth.ModelSpec("tiny-bf16", 320, 192, 2, 96, 384, 1, 1, 1, "bf16", "bf16")
+    w = synth.make_weights(spec, 4)
+    m = copy.copy(oracle.OracleModel.from_weights(w))
+    m.kv_mode = mode
+    toks = list(synth.tokens(0, 3401, 10, 320))
+    lane, _, _ = oracle.prefill(m, toks, 3)
+    seq = list(toks)
+    for _ in range(3):
+        seq.append(lane.pending)
+        h, logits, _, _ = oracle.decode_step(m, lane, 3)
+        _, h_full, lg_full = oracle.prefill(m, seq, 3, want_logits="last")
+        assert np.allclose(h, h_full[-1], rtol=1e-10, atol=1e-12)
+        assert np.allclose(logits, lg_full, rtol=1e-9, atol=1e-11)
+    # and the compression is visible: the modes differ from each other and from K/V
+    m_kv = oracle.OracleModel.from_weights(w)
+    _, h_kv, _ = oracle.prefill(m_kv, toks, 3)
+    _, h_m, _ = oracle.prefill(m, toks, 3)
+    err = np.linalg.norm(h_m - h_kv) / np.linalg.norm(h_kv)
+    assert 1e-7 < err < {"h": 5e-3, "h8": 2e-2, "h4": 2e-1}[mode], err
