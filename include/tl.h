@@ -80,7 +80,25 @@ typedef struct {
   int32_t max_L;                   /* largest loop count accepted */
   int32_t max_pos;                 /* positions 0 .. max_pos-1 are valid */
   uint64_t kv_arena_bytes;         /* device bytes reserved for lane KV caches (0 = none) */
+  /* What a lane's cache slot keeps per position, one of tl_kv_mode (iteration-axis
+   * KV compression: "CLI Reference" page, environment variables TINYLOOP_KV_H_MODE
+   * with TINYLOOP_KV_INT8 / TINYLOOP_KV_INT4). */
+  int32_t kv_mode;
 } tl_config;
+
+/* TL_KV_KV: K and V in the operand type (2 d elements per position and slot).
+ * TL_KV_H: the block's pre-QKV norm output x in the operand type (d elements).
+ * TL_KV_H8: x as int8 codes, one fp16 scale per (position, head): d + 2 H bytes.
+ * TL_KV_H4: x as packed two's-complement int4 codes (element 2i in the low nibble)
+ *   with one fp16 scale per (position, head): d / 2 + 2 H bytes.
+ * Codes: s = fp16(max|x| / levels) over the head (division in fp32), q =
+ * clamp(rint(x / s), -levels, levels), levels 127 / 7, q = 0 where s = 0.
+ * In the store-h modes each attention rebuilds K and V of every cached position
+ * of the lanes in the pass with the block's own QKV projection, so the cache shrinks
+ * and attention costs a projection over the whole context.  Calls without lanes
+ * (scoring) keep no cache and compute K and V directly; tl_decode_run needs
+ * TL_KV_KV. */
+typedef enum { TL_KV_KV = 0, TL_KV_H = 1, TL_KV_H8 = 2, TL_KV_H4 = 3 } tl_kv_mode;
 
 /* Host weights of one block, canonical layout: linear weights are [out, in]
  * row-major (y = x W^T).  wqkv rows are q (heads 0..H-1, head_dim rows each), then
@@ -327,7 +345,8 @@ tl_status tl_sync_errors(tl_model* m, void* stream);
 #define TL_T_HEAD 10             /* head GEMM and greedy-token reduction */
 #define TL_T_COMPACT 11          /* active-row compaction and row moves */
 #define TL_T_EMBED 12
-#define TL_TIMING_CLASSES 13
+#define TL_T_HREBUILD 13         /* store-h modes: cache write, read-back and K/V projection */
+#define TL_TIMING_CLASSES 14
 tl_status tl_timing_enable(tl_model* m, int32_t on);
 tl_status tl_timing_read(tl_model* m, double* total_ms, int64_t* launches);
 

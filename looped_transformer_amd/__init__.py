@@ -20,6 +20,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tl.h")
 
 TL_OK, TL_E_ARG, TL_E_OOM, TL_E_HIP, TL_E_STATE, TL_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 TL_DT_F32, TL_DT_F16, TL_DT_BF16, TL_DT_W4G128 = 0, 1, 2, 3
+TL_KV_KV, TL_KV_H, TL_KV_H8, TL_KV_H4 = 0, 1, 2, 3
 _STATUS = {0: "TL_OK", -1: "TL_E_ARG", -2: "TL_E_OOM", -3: "TL_E_HIP", -4: "TL_E_STATE", -5: "TL_E_UNSUPPORTED"}
 
 
@@ -36,7 +37,7 @@ class tl_config(ctypes.Structure):
         ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
         ("act_dtype", ctypes.c_int32), ("boundary_dtype", ctypes.c_int32), ("loop_dtype", ctypes.c_int32),
         ("loop_fp16_body", ctypes.c_int32), ("max_lanes", ctypes.c_int32), ("max_L", ctypes.c_int32),
-        ("max_pos", ctypes.c_int32), ("kv_arena_bytes", ctypes.c_uint64)]
+        ("max_pos", ctypes.c_int32), ("kv_arena_bytes", ctypes.c_uint64), ("kv_mode", ctypes.c_int32)]
 
 
 class tl_block_weights(ctypes.Structure):
@@ -298,7 +299,7 @@ def tl_sync_errors(model, stream=None):
 
 TIMING_CLASSES = ("gemm_qkv_loop", "gemm_o_loop", "gemm_gu_loop", "gemm_down_loop", "gemm_qkv_boundary",
                   "gemm_o_boundary", "gemm_gu_boundary", "gemm_down_boundary", "attention", "rmsnorm", "head",
-                  "compact", "embed")
+                  "compact", "embed", "hrebuild")
 
 
 def tl_timing_enable(model, on: bool = True):

@@ -118,6 +118,31 @@ tl_status stage_upload(tl_model* m, const Stage& st, hipStream_t s) {
   return TL_OK;
 }
 
+// The same for the second channel (lists a pass plans after the call's upload).
+tl_status aux_upload(tl_model* m, const Stage& st, hipStream_t s) {
+  const size_t need = std::max<size_t>(st.buf.size(), 256);
+  if (need > m->aux_bytes) {
+    if (m->aux_host) {
+      HIPCHK(hipStreamSynchronize(s));
+      HIPCHK(hipHostFree(m->aux_host));
+      m->aux_host = nullptr;
+      dev_free(m, m->aux_dev);
+      m->aux_dev = nullptr;
+    }
+    size_t cap = std::max<size_t>(need * 2, 1 << 20);
+    HIPCHK(hipHostMalloc(&m->aux_host, cap, hipHostMallocDefault));
+    m->aux_dev = dev_alloc(m, cap);
+    if (!m->aux_dev) return fail(TL_E_OOM, "staging area of %zu bytes", cap);
+    m->aux_bytes = cap;
+  } else {
+    HIPCHK(hipEventSynchronize(m->aux_done));
+  }
+  std::memcpy(m->aux_host, st.buf.data(), st.buf.size());
+  HIPCHK(hipMemcpyAsync(m->aux_dev, m->aux_host, st.buf.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(hipEventRecord(m->aux_done, s));
+  return TL_OK;
+}
+
 // ----------------------------------------------------------------- workspace
 constexpr int64_t kSplitFloats = 8ll << 20;   // 32 MB of split-K partials
 tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStream_t s) {
@@ -238,7 +263,7 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
 // projection's residual update when possible (then ws.x16 holds its output).
 tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, const KVParams& kv, hipStream_t s,
                     const AttnTile* tiles = nullptr, int n_tiles = 0, bool x_ready = false,
-                    const float* next_norm = nullptr) {
+                    const float* next_norm = nullptr, int hgroup = -1) {
   if (n <= 0) return TL_OK;
   const tl_config& c = m->cfg;
   const BlockDev& B = m->blocks[b];
@@ -257,9 +282,27 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   e.H = c.n_heads;
   e.dh = c.head_dim;
   e.skip_done = m->gate_live != nullptr;
+  // store-h: K/V live in a per-pass scratch, rebuilt from the cached x rows of
+  // every position of the pass's lanes (the current rows' x is cached first)
+  const tl::HPass* hpass = (m->hpass && hgroup >= 0) ? m->hpass : nullptr;
+  const KVParams& akv = hpass ? hpass->skv : kv;
+  e.kv = akv;
   TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s)));
-  if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, kv, w.o16, s)));
-  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, kv, w.o16, m->gate_live, s)));
+  if (hpass) {
+    HCacheParams hp = hpass->hp;
+    hp.slot = kv.s0;
+    const RowInfo* rec = hpass->rec[hgroup];
+    const int nrec = hpass->n_rec[hgroup];
+    TIMED(TL_T_HREBUILD, HIPCHK(launch_hcache_write(m->act, w.x16, rows, n, hp, m->gate_live != nullptr, s)));
+    TIMED(TL_T_HREBUILD, HIPCHK(launch_hcache_read(m->act, hp, rec, nrec, m->h_x, s)));
+    GemmEpi r2 = e;
+    r2.q_out = m->h_q;
+    r2.rows = rec;
+    r2.skip_done = false;
+    TIMED(TL_T_HREBUILD, TRY(gemm(m, m->h_x, nrec, B.qkv, r2, s)));
+  }
+  if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, akv, w.o16, s)));
+  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, akv, w.o16, m->gate_live, s)));
   GemmEpi r{};
   r.kind = EPI_RESID;
   r.h = h;
@@ -293,7 +336,89 @@ struct Pass {
   std::vector<int> n_tiles;
   // early exit (decode steps): rule, or NULL
   const tl_early_exit* ee = nullptr;
+  // host copy of rows0 (store-h modes plan the K/V rebuild from it)
+  const std::vector<RowInfo>* rows_host = nullptr;
 };
+
+// Store-h rebuild plan of a pass: every lane's positions 0 .. (last position in
+// the pass), for the pre/post blocks (group 0) and for each loop iteration j (the
+// lanes whose rows run iteration j); scratch K/V of one slot per lane.
+tl_status plan_hpass(tl_model* m, const Pass& p, tl::HPass& hp, hipStream_t s) {
+  const tl_config& c = m->cfg;
+  const int ml = std::max(c.max_lanes, 1), d = c.d_model;
+  std::vector<int> P(ml, 0), depth(ml, 0);
+  for (const RowInfo& r : *p.rows_host) {
+    P[r.lane] = std::max(P[r.lane], r.pos + 1);
+    depth[r.lane] = std::max(depth[r.lane], r.depth);
+  }
+  std::vector<int64_t> soff(ml, 0);
+  std::vector<int32_t> scap(ml, 0);
+  int64_t tot = 0;
+  for (int l = 0; l < ml; ++l)
+    if (P[l] > 0) {
+      soff[l] = tot;
+      scap[l] = P[l];
+      tot += (int64_t)2 * d * P[l];
+    }
+  const int Lmax = (int)p.n_active.size();
+  Stage st;
+  std::vector<size_t> offs;
+  std::vector<int> counts;
+  std::vector<char> prev;
+  int64_t maxR = 1;
+  for (int g = 0; g <= Lmax; ++g) {
+    std::vector<char> in(ml, 0);
+    for (int l = 0; l < ml; ++l) in[l] = P[l] > 0 && (g == 0 || depth[l] >= g);
+    if (g > 0 && in == prev) {   // same lanes as the previous group: same list
+      offs.push_back(offs.back());
+      counts.push_back(counts.back());
+      continue;
+    }
+    std::vector<RowInfo> rec;
+    for (int l = 0; l < ml; ++l)
+      if (in[l])
+        for (int q = 0; q < P[l]; ++q) {
+          RowInfo r{};
+          r.orig = (int)rec.size();
+          r.lane = l;
+          r.pos = q;
+          r.depth = 1;
+          r.iter = 1;
+          rec.push_back(r);
+        }
+    offs.push_back(st.add(rec));
+    counts.push_back((int)rec.size());
+    maxR = std::max<int64_t>(maxR, (int64_t)rec.size());
+    prev = in;
+  }
+  const size_t o_soff = st.add(soff), o_scap = st.add(scap);
+  if (maxR > m->h_rows || tot > m->h_kv_elems) {
+    HIPCHK(hipStreamSynchronize(s));
+    dev_free(m, m->h_x);
+    dev_free(m, m->h_q);
+    dev_free(m, m->h_kv);
+    m->h_rows = std::max(m->h_rows, (maxR + 63) / 64 * 64);
+    m->h_kv_elems = std::max(m->h_kv_elems, tot);
+    m->h_x = dev_alloc(m, (size_t)m->h_rows * d * m->esz);
+    m->h_q = dev_alloc(m, (size_t)m->h_rows * d * m->esz);
+    m->h_kv = dev_alloc(m, (size_t)std::max<int64_t>(m->h_kv_elems, 1) * m->esz);
+    if (!m->h_x || !m->h_q || !m->h_kv) {
+      m->h_rows = m->h_kv_elems = 0;
+      return fail(TL_E_OOM, "store-h rebuild buffers (%lld rows, %lld K/V elements)", (long long)maxR,
+                  (long long)tot);
+    }
+  }
+  TRY(aux_upload(m, st, s));
+  uint8_t* base = static_cast<uint8_t*>(m->aux_dev);
+  hp.hp = HCacheParams{static_cast<uint8_t*>(m->kv_base), m->d_lane_off, m->d_lane_cap, m->esz, m->hrb, 0,
+                       m->kv_mode, c.n_heads, c.head_dim};
+  hp.skv = KVParams{m->h_kv, reinterpret_cast<const int64_t*>(base + o_soff),
+                    reinterpret_cast<const int32_t*>(base + o_scap), c.n_heads, c.head_dim, 0, 0};
+  hp.rec.clear();
+  hp.n_rec = counts;
+  for (size_t o : offs) hp.rec.push_back(reinterpret_cast<const RowInfo*>(base + o));
+  return TL_OK;
+}
 
 tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out, float* logits, int32_t* out_tok,
                    const int32_t* pend_lanes, hipStream_t s, float* margin = nullptr);
@@ -316,6 +441,17 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   auto& w = m->ws;
   const int d = c.d_model;
   const bool tiled = !p.tiles.empty();
+  tl::HPass hps;
+  struct HReset {
+    tl_model* m;
+    ~HReset() { m->hpass = nullptr; }
+  } h_reset{m};
+  const bool hmode = m->kv_mode != TL_KV_KV && !p.scoring;
+  if (hmode) {
+    if (!p.rows_host) return fail(TL_E_STATE, "store-h pass without host rows");
+    TRY(plan_hpass(m, p, hps, s));
+    m->hpass = &hps;
+  }
   TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, w.hA, m->d_err, c.vocab, s)));
   KVParams kv = p.kv;
   kv.s1 = 0;
@@ -328,7 +464,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   for (int b = 0; b < c.n_pre; ++b) {
     kv.s0 = p.scoring ? 0 : b;
     const float* nn = b + 1 < c.n_pre ? m->blocks[b + 1].norm1 : (Lmax > 0 ? loop_first() : nullptr);
-    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn));
+    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn, hmode ? 0 : -1));
     x_ready = nn != nullptr;
   }
   float* h = w.hA;
@@ -359,7 +495,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
       // probe normalises into its own buffer, rows it finishes are only carried)
       const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1 : (leaving ? nullptr : loop_first());
       TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
-                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn));
+                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1));
       x_ready = nn != nullptr;
     }
     if (probe) {
@@ -389,7 +525,8 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   for (int b = 0; b < c.n_post; ++b) {
     kv.s0 = p.scoring ? 0 : c.n_pre + b;
     const float* nn = b + 1 < c.n_post ? m->blocks[c.n_pre + c.n_loop + b + 1].norm1 : nullptr;
-    TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn));
+    TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn,
+                  hmode ? 0 : -1));
     x_ready = nn != nullptr;
   }
   return TL_OK;
@@ -462,6 +599,8 @@ int lane_slots(const tl_config& c, int ceiling) { return c.n_pre + c.n_post + c.
 uint64_t lane_elems(const tl_model* m, int ceiling, int cap) {
   const tl_config& c = m->cfg;
   uint64_t e = (uint64_t)lane_slots(c, ceiling) * 2ull * c.n_heads * (uint64_t)cap * c.head_dim;
+  if (m->kv_mode != TL_KV_KV)   // store-h: rows of hrb bytes, counted in operand elements
+    e = ((uint64_t)lane_slots(c, ceiling) * cap * m->hrb + m->esz - 1) / m->esz;
   return (e + 63) / 64 * 64;
 }
 
@@ -571,6 +710,7 @@ tl_status validate_config(const tl_config* c) {
   }
   if (c->loop_dtype == DT_W4G128 && (c->d_model % 128 || c->ffn % 128))
     return fail(TL_E_UNSUPPORTED, "W4G128 needs d_model and ffn multiples of 128");
+  if (c->kv_mode < TL_KV_KV || c->kv_mode > TL_KV_H4) return fail(TL_E_ARG, "kv_mode %d unknown", c->kv_mode);
   return TL_OK;
 }
 
@@ -648,6 +788,11 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   m->act = cfg->act_dtype;
   m->G = m->act == DT_F32 ? 1 : 16;
   m->esz = dtype_size(m->act);
+  m->kv_mode = cfg->kv_mode;
+  {
+    const int d = cfg->d_model, H = cfg->n_heads;
+    m->hrb = m->kv_mode == TL_KV_H ? d * m->esz : m->kv_mode == TL_KV_H8 ? d + 2 * H : d / 2 + 2 * H;
+  }
   std::vector<void*> temps;
   auto cleanup_fail = [&](tl_status st) {
     std::string msg = g_err;
@@ -763,6 +908,7 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   LHIP(hipMemsetAsync(m->d_pending, 0, ml * 4, s));
   LHIP(hipMemsetAsync(m->d_err, 0, 256, s));
   LHIP(hipEventCreateWithFlags(&m->stage_done, hipEventDisableTiming));
+  LHIP(hipEventCreateWithFlags(&m->aux_done, hipEventDisableTiming));
   LHIP(hipStreamSynchronize(s));
   *out = m;
   return TL_OK;
@@ -781,6 +927,8 @@ void tl_free(tl_model* m) {
   if (m->ee_eff_host) (void)hipHostFree(m->ee_eff_host);
   if (m->sp_acc_host) (void)hipHostFree(m->sp_acc_host);
   if (m->stage_done) (void)hipEventDestroy(m->stage_done);
+  if (m->aux_done) (void)hipEventDestroy(m->aux_done);
+  if (m->aux_host) (void)hipHostFree(m->aux_host);
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   delete m;
 }
@@ -968,6 +1116,7 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   p.n = T;
   p.tokens = tokens;
   p.rows0 = staged<RowInfo>(m, o_rows);
+  p.rows_host = &rows;
   p.n_active = n_act;
   for (size_t k = 0; k < tile_lists.size(); ++k) {
     p.tiles.push_back(staged<AttnTile>(m, o_tiles[k]));
@@ -1082,6 +1231,7 @@ tl_status tl_append(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32_
   p.n = T;
   p.tokens = tokens;
   p.rows0 = staged<RowInfo>(m, o_rows);
+  p.rows_host = &rows;
   p.n_active = n_act;
   for (size_t k = 0; k < tile_lists.size(); ++k) {
     p.tiles.push_back(staged<AttnTile>(m, o_tiles[k]));
@@ -1135,11 +1285,14 @@ tl_status tl_lane_fork(tl_model* m, int32_t src, int32_t dst, int32_t prefix_len
   Stage st;
   const size_t o_loff = st.add(loff), o_lcap = st.add(lcap);
   TRY(stage_upload(m, st, s));
-  // every (slot, K/V, head) block is [cap][head_dim]: copy its first prefix_len rows
-  const size_t row = (size_t)c.head_dim * m->esz;
+  // every (slot, K/V, head) block is [cap][head_dim] (store-h: every slot is [cap]
+  // rows of hrb bytes): copy its first prefix_len rows
+  const bool hm = m->kv_mode != TL_KV_KV;
+  const size_t row = hm ? (size_t)m->hrb : (size_t)c.head_dim * m->esz;
+  const size_t blocks = hm ? (size_t)ln.nslots : (size_t)ln.nslots * 2 * c.n_heads;
   uint8_t* kvb = static_cast<uint8_t*>(m->kv_base);
   HIPCHK(hipMemcpy2DAsync(kvb + ln.off * m->esz, (size_t)ln.cap * row, kvb + sl.off * m->esz, (size_t)sl.cap * row,
-                          (size_t)prefix_len * row, (size_t)ln.nslots * 2 * c.n_heads, hipMemcpyDeviceToDevice, s));
+                          (size_t)prefix_len * row, blocks, hipMemcpyDeviceToDevice, s));
   if (ln.pending) HIPCHK(hipMemcpyAsync(m->d_pending + dst, m->d_pending + src, 4, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipMemcpyAsync(m->d_lane_off, staged<int64_t>(m, o_loff), loff.size() * 8, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipMemcpyAsync(m->d_lane_cap, staged<int32_t>(m, o_lcap), lcap.size() * 4, hipMemcpyDeviceToDevice, s));
@@ -1234,8 +1387,10 @@ tl_status tl_speculate(tl_model* m, int32_t n, const int32_t* lanes, int32_t L_d
     // descriptors: k draft steps (one row per lane), then the verify pass
     Stage st;
     std::vector<size_t> o_drows(k);
+    std::vector<std::vector<RowInfo>> drows_host(k);
     for (int r = 0; r < k; ++r) {
-      std::vector<RowInfo> rows(na);
+      std::vector<RowInfo>& rows = drows_host[r];
+      rows.resize(na);
       for (int a = 0; a < na; ++a) {
         rows[a] = RowInfo{};
         rows[a].orig = a;
@@ -1287,6 +1442,7 @@ tl_status tl_speculate(tl_model* m, int32_t n, const int32_t* lanes, int32_t L_d
       p.n = na;
       p.tokens = toks;
       p.rows0 = staged<RowInfo>(m, o_drows[r]);
+      p.rows_host = &drows_host[r];
       p.n_active = active_counts(dd);
       p.kv = kvp;
       p.final_h = m->ws.hX;
@@ -1300,6 +1456,7 @@ tl_status tl_speculate(tl_model* m, int32_t n, const int32_t* lanes, int32_t L_d
       p.n = T;
       p.tokens = m->sp_in;
       p.rows0 = staged<RowInfo>(m, o_vrows);
+      p.rows_host = &vrows;
       p.n_active = v_act;
       for (size_t q = 0; q < tile_lists.size(); ++q) {
         p.tiles.push_back(staged<AttnTile>(m, o_tiles[q]));
@@ -1375,6 +1532,7 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
   p.n = n;
   p.tokens = toks;
   p.rows0 = staged<RowInfo>(m, o_rows);
+  p.rows_host = &rows;
   p.n_active = active_counts(eff);
   p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
   p.final_h = out_hidden ? out_hidden : m->ws.hX;
@@ -1464,6 +1622,7 @@ tl_status tl_decode_step_ee(tl_model* m, int32_t n, const int32_t* lanes, const 
   p.n = n;
   p.tokens = toks;
   p.rows0 = staged<RowInfo>(m, o_rows);
+  p.rows_host = &rows;
   p.n_active = active_counts(eff);
   p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
   p.final_h = out_hidden ? out_hidden : m->ws.hX;
@@ -1556,6 +1715,7 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
   if (!m || !lanes || !L_req || !out_tokens) return fail(TL_E_ARG, "NULL argument");
   const tl_config& c = m->cfg;
   if (n < 1 || n_steps < 1) return fail(TL_E_ARG, "n_lanes and n_steps must be >= 1");
+  if (m->kv_mode != TL_KV_KV) return fail(TL_E_UNSUPPORTED, "continuous depth decoding needs kv_mode TL_KV_KV");
   std::vector<char> seen(c.max_lanes, 0);
   for (int i = 0; i < n; ++i) {
     const int l = lanes[i];

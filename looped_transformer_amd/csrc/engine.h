@@ -25,6 +25,15 @@ class KvArena {
   std::map<uint64_t, uint64_t> free_;   // offset -> length
 };
 
+// Store-h rebuild of one pass: the cache rows to read and the scratch K/V they are
+// projected into, per group of block applications with the same lanes.
+struct HPass {
+  HCacheParams hp{};                  // slot set per block application
+  KVParams skv{};                     // scratch K/V: one slot per lane of the pass
+  std::vector<const RowInfo*> rec;    // index 0: pre/post blocks; j: loop iteration j
+  std::vector<int> n_rec;
+};
+
 struct Lane {
   bool live = false;
   int32_t len = 0;        // positions written
@@ -84,6 +93,8 @@ struct tl_model {
   int act = DT_F16;
   int G = 16;
   int esz = 2;               // bytes of an activation / KV element
+  int kv_mode = 0;           // tl_kv_mode
+  int hrb = 0;               // store-h: bytes of one position of one slot
   tl_alloc_fn alloc = nullptr;
   tl_dealloc_fn dealloc = nullptr;
   void* user = nullptr;
@@ -114,6 +125,17 @@ struct tl_model {
   size_t stage_bytes = 0;
   hipEvent_t stage_done = nullptr;
   hipStream_t last_stream = nullptr;
+  // second upload channel (store-h rebuild lists, planned inside a pass)
+  void* aux_host = nullptr;
+  void* aux_dev = nullptr;
+  size_t aux_bytes = 0;
+  hipEvent_t aux_done = nullptr;
+  // store-h rebuild buffers: operand x and throw-away q [h_rows, d], scratch K/V
+  void* h_x = nullptr;
+  void* h_q = nullptr;
+  void* h_kv = nullptr;
+  int64_t h_rows = 0, h_kv_elems = 0;
+  const tl::HPass* hpass = nullptr;    // set while a store-h pass runs
   // captured scoring passes; a workspace reallocation invalidates them
   std::vector<tl::GraphEntry> graphs;
   uint64_t graph_clock = 0;

@@ -132,6 +132,26 @@ hipError_t launch_spec_pack(const int32_t* pending, const int32_t* lanes, const 
 hipError_t launch_spec_accept(const int32_t* draft, const int32_t* g, const int32_t* lanes, const int32_t* want,
                               const int32_t* emitted, const int32_t* slot, int n, int k, int n_tokens,
                               int32_t* out, int32_t* pending, int32_t* acc, hipStream_t s);
+// Store-h cache of one block application.  A lane's slot `slot` keeps one row of
+// rb bytes per position at base + lane_off[lane] * unit + (slot * lane_cap[lane] +
+// pos) * rb.  mode 1: x in the operand type (d elements); mode 2: d int8 codes then
+// H fp16 scales; mode 3: d/2 bytes of two's-complement nibbles (element 2i low,
+// 2i+1 high) then H fp16 scales.  Codes: s = fp16(max|x| / levels) over the head's
+// dh values (division in fp32), q = clamp(rint(x / s), -levels, levels), levels 127
+// or 7, q = 0 where s = 0.
+struct HCacheParams {
+  uint8_t* base;
+  const int64_t* lane_off;
+  const int32_t* lane_cap;
+  int32_t unit, rb, slot, mode, H, dh;
+};
+// Write the operand-type rows x [n, d] of rows (lane, pos) into the cache (rows
+// marked done are skipped when skip_done).
+hipError_t launch_hcache_write(int dtype, const void* x, const RowInfo* rows, int n, const HCacheParams& hp,
+                               bool skip_done, hipStream_t s);
+// Read cached rows (lane, pos) back as operand-type x [n, d] (codes times scale).
+hipError_t launch_hcache_read(int dtype, const HCacheParams& hp, const RowInfo* rows, int n, void* out,
+                              hipStream_t s);
 hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);

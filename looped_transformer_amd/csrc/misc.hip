@@ -233,6 +233,86 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* __restr
   }
 }
 
+// ---------------------------------------------------------------- store-h cache
+// One 64-lane workgroup per (row, head); lane i owns elements 2i and 2i + 1 of the
+// head (one packed byte in mode 3).
+__device__ __forceinline__ uint8_t* hcache_row(const HCacheParams& hp, const RowInfo& ri) {
+  return hp.base + hp.lane_off[ri.lane] * hp.unit + ((int64_t)hp.slot * hp.lane_cap[ri.lane] + ri.pos) * hp.rb;
+}
+
+template <class AT>
+__global__ __launch_bounds__(64) void hcache_write_kernel(const AT* __restrict__ x, const RowInfo* __restrict__ rows,
+                                                          HCacheParams hp, int skip_done) {
+  const int r = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+  const RowInfo ri = rows[r];
+  if (skip_done && ri.done) return;
+  const int d = hp.H * hp.dh, e = h * hp.dh + 2 * i;
+  const bool own = 2 * i < hp.dh;
+  uint8_t* row = hcache_row(hp, ri);
+  AT a0{}, a1{};
+  if (own) {
+    a0 = x[(int64_t)r * d + e];
+    a1 = x[(int64_t)r * d + e + 1];
+  }
+  if (hp.mode == 1) {
+    if (own) {
+      reinterpret_cast<AT*>(row)[e] = a0;
+      reinterpret_cast<AT*>(row)[e + 1] = a1;
+    }
+    return;
+  }
+  const float v0 = (float)a0, v1 = (float)a1;
+  const float levels = hp.mode == 2 ? 127.f : 7.f;
+  const float am = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const f16 s16 = (f16)(am / levels);
+  const float sc = (float)s16;
+  int q0 = 0, q1 = 0;
+  if (sc > 0.f) {
+    q0 = (int)fminf(fmaxf(rintf(v0 / sc), -levels), levels);
+    q1 = (int)fminf(fmaxf(rintf(v1 / sc), -levels), levels);
+  }
+  const int cb = hp.mode == 2 ? d : d / 2;
+  if (own) {
+    if (hp.mode == 2) {
+      row[e] = (uint8_t)(int8_t)q0;
+      row[e + 1] = (uint8_t)(int8_t)q1;
+    } else {
+      row[e / 2] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+    }
+  }
+  if (i == 0) *reinterpret_cast<f16*>(row + cb + 2 * h) = s16;
+}
+
+template <class AT>
+__global__ __launch_bounds__(64) void hcache_read_kernel(HCacheParams hp, const RowInfo* __restrict__ rows,
+                                                         AT* __restrict__ out) {
+  const int r = blockIdx.x, h = blockIdx.y, i = threadIdx.x;
+  if (2 * i >= hp.dh) return;
+  const RowInfo ri = rows[r];
+  const int d = hp.H * hp.dh, e = h * hp.dh + 2 * i;
+  const uint8_t* row = hcache_row(hp, ri);
+  AT* o = out + (int64_t)r * d + e;
+  if (hp.mode == 1) {
+    o[0] = reinterpret_cast<const AT*>(row)[e];
+    o[1] = reinterpret_cast<const AT*>(row)[e + 1];
+    return;
+  }
+  int q0, q1, cb;
+  if (hp.mode == 2) {
+    q0 = (int8_t)row[e];
+    q1 = (int8_t)row[e + 1];
+    cb = d;
+  } else {
+    const int b = row[e / 2];
+    q0 = (b & 0x8) ? (b & 0xF) - 16 : (b & 0xF);
+    q1 = (b & 0x80) ? (b >> 4) - 16 : (b >> 4);
+    cb = d / 2;
+  }
+  const float sc = (float)*reinterpret_cast<const f16*>(row + cb + 2 * h);
+  o[0] = from_f32<AT>((float)q0 * sc);
+  o[1] = from_f32<AT>((float)q1 * sc);
+}
+
 // ---------------------------------------------------------------- self-speculative rounds
 __global__ void spec_pack_kernel(const int32_t* __restrict__ pending, const int32_t* __restrict__ lanes,
                                  const int32_t* __restrict__ draft, int n, int k, int32_t* __restrict__ in) {
@@ -430,6 +510,39 @@ hipError_t launch_argmax_reduce(const float* pv, const int32_t* pi, const float*
                                 int32_t* out2, const int32_t* scatter, float* margin, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(argmax_reduce_kernel, dim3(n), dim3(256), 0, s, pv, pi, pv2, tiles, out, out2, scatter, margin);
+  return hipGetLastError();
+}
+
+hipError_t launch_hcache_write(int dtype, const void* x, const RowInfo* rows, int n, const HCacheParams& hp,
+                               bool skip_done, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid(n, hp.H);
+  switch (dtype) {
+    case DT_F32:
+      hipLaunchKernelGGL(hcache_write_kernel<float>, grid, dim3(64), 0, s, (const float*)x, rows, hp, (int)skip_done);
+      break;
+    case DT_F16:
+      hipLaunchKernelGGL(hcache_write_kernel<f16>, grid, dim3(64), 0, s, (const f16*)x, rows, hp, (int)skip_done);
+      break;
+    case DT_BF16:
+      hipLaunchKernelGGL(hcache_write_kernel<bf16>, grid, dim3(64), 0, s, (const bf16*)x, rows, hp, (int)skip_done);
+      break;
+    default:
+      return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_hcache_read(int dtype, const HCacheParams& hp, const RowInfo* rows, int n, void* out,
+                              hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const dim3 grid(n, hp.H);
+  switch (dtype) {
+    case DT_F32: hipLaunchKernelGGL(hcache_read_kernel<float>, grid, dim3(64), 0, s, hp, rows, (float*)out); break;
+    case DT_F16: hipLaunchKernelGGL(hcache_read_kernel<f16>, grid, dim3(64), 0, s, hp, rows, (f16*)out); break;
+    case DT_BF16: hipLaunchKernelGGL(hcache_read_kernel<bf16>, grid, dim3(64), 0, s, hp, rows, (bf16*)out); break;
+    default: return hipErrorInvalidValue;
+  }
   return hipGetLastError();
 }
 

@@ -24,7 +24,7 @@ def ensure_built():
 
 
 def make_config(spec: synth.ModelSpec, max_lanes: int = 0, max_L: int = 32, max_pos: int = 1024,
-                kv_arena_bytes: int = 0) -> tl.tl_config:
+                kv_arena_bytes: int = 0, kv_mode: int = 0) -> tl.tl_config:
     c = tl.tl_config()
     c.vocab, c.d_model, c.n_heads, c.head_dim, c.ffn = spec.vocab, spec.d_model, spec.n_heads, spec.head_dim, spec.ffn
     c.n_pre, c.n_loop, c.n_post = spec.n_pre, spec.n_loop, spec.n_post
@@ -37,6 +37,7 @@ def make_config(spec: synth.ModelSpec, max_lanes: int = 0, max_L: int = 32, max_
     else:
         c.loop_dtype = DT[spec.loop_dtype]
     c.max_lanes, c.max_L, c.max_pos, c.kv_arena_bytes = max_lanes, max_L, max_pos, kv_arena_bytes
+    c.kv_mode = kv_mode
     return c
 
 

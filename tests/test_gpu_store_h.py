@@ -1,0 +1,181 @@
+"""Store-h cache modes on the device against the oracle (iteration-axis KV
+compression: "CLI Reference" page, environment variables TINYLOOP_KV_H_MODE with
+TINYLOOP_KV_INT8 / TINYLOOP_KV_INT4).
+
+A lane's slot keeps the block's pre-QKV norm output x (operand type, int8 or
+packed int4 codes with one fp16 scale per position and head); each attention
+rebuilds K and V of every cached position with the block's QKV projection.  The
+oracle models the same storage.  Codes are decided from the operand-type x in
+fp32 on both sides, but x itself differs between the two by the path's usual
+relative error e (fp32 model ~1e-7, fp16 operands with INT4 weights ~3e-4, bf16
+~3e-3), so an element within e|x| of a rounding boundary takes the neighbouring
+code: with step s (a head's range over 127 or over 7) a fraction ~ 2e|x|/s of
+the codes move by one step and K/V move by about sqrt(2 e |x| s) relative.  The
+bars are three times that estimate: fp16 1e-2 (int8) / 5e-2 (int4), bf16 3e-2 /
+0.15.  On the fp32 model codes almost always agree (1e-7 runs), and a single
+moved code stays below 1e-2, which is its bar: that model is the strict check of
+the code path.  x kept in the operand type takes the usual bars.  Tokens are
+seeded (teacher forcing).
+"""
+import copy
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+from tests.harness import ensure_built, kv_bytes, load_model, rel_l2
+
+torch = pytest.importorskip("torch")
+import looped_transformer_amd as tl  # noqa: E402
+
+pytestmark = pytest.mark.gpu
+
+SPECS = {
+    "tiny-fp32": synth.SPECS[1],
+    "tiny-w4": synth.ModelSpec("tiny-w4", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "w4g128"),
+    "tiny-bf16-stack": synth.ModelSpec("tiny-bf16-stack", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16"),
+}
+MODES = {"h": tl.TL_KV_H, "h8": tl.TL_KV_H8, "h4": tl.TL_KV_H4}
+
+
+def say(*a):
+    print("[gpu-store-h]", *a, flush=True)
+    sys.stdout.flush()
+
+
+CODED_BARS = {"f32": (1e-2, 1e-2), "f16": (1e-2, 5e-2), "bf16": (3e-2, 0.15)}   # (int8, int4)
+
+
+def bar(spec, mode, L):
+    if mode in ("h8", "h4"):
+        return CODED_BARS[spec.act_dtype][mode == "h4"]
+    if spec.act_dtype == "f32":
+        return 1e-4
+    return 1e-2 if L <= 8 else 3e-2
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _built():
+    ensure_built()
+
+
+def _dev(a):
+    return torch.tensor(np.asarray(a, dtype=np.int32), dtype=torch.int32, device="cuda")
+
+
+def _oracle_model(w, mode):
+    m = copy.copy(oracle.OracleModel.from_weights(w))
+    m.kv_mode = mode
+    return m
+
+
+@pytest.mark.parametrize("name", list(SPECS))
+@pytest.mark.parametrize("mode", list(MODES))
+def test_store_h_prefill_append_decode(name, mode):
+    spec = SPECS[name]
+    w = synth.make_weights(spec, 81)
+    m = _oracle_model(w, mode)
+    plens, Ls = [9, 40, 3], [5, 3, 6]
+    prompts = [synth.tokens(81, 9000 + i, n, spec.vocab) for i, n in enumerate(plens)]
+    extra = [synth.tokens(81, 9100 + i, n, spec.vocab) for i, n in enumerate([4, 1, 37])]
+    feed = synth.tokens(81, 9200, 9, spec.vocab).reshape(3, 3)
+    lanes = [2, 0, 5]
+    o_lanes, o_h = [], []
+    for p, L in zip(prompts, Ls):
+        ln, h, _ = oracle.prefill(m, p, L)
+        o_lanes.append(ln)
+        o_h.append(h)
+    caps = [n + 40 for n in plens]
+    model = load_model(w, max_lanes=8, max_pos=128, max_L=16, kv_arena_bytes=kv_bytes(spec, [8] * 3, [90] * 3),
+                       kv_mode=MODES[mode])
+    try:
+        cu = np.concatenate([[0], np.cumsum(plens)]).astype(np.int32)
+        hid = torch.empty(int(cu[-1]), spec.d_model, dtype=torch.float32, device="cuda")
+        tl.tl_forward(model, cu, _dev(np.concatenate(prompts)), seq_L=Ls, lanes=lanes, max_new_tokens=40,
+                      out_hidden=hid)
+        torch.cuda.synchronize()
+        H = hid.cpu().numpy()
+        for i in range(3):
+            r = rel_l2(H[cu[i]:cu[i + 1]], o_h[i])
+            say(name, mode, "prefill lane", lanes[i], "L", Ls[i], "rel %.2e" % r)
+            assert r <= bar(spec, mode, Ls[i]), (i, r)
+        # append (the third sequence spans two 32-row tiles from an unaligned start)
+        cu2 = np.concatenate([[0], np.cumsum([len(e) for e in extra])]).astype(np.int32)
+        hid2 = torch.empty(int(cu2[-1]), spec.d_model, dtype=torch.float32, device="cuda")
+        eff = tl.tl_append(model, cu2, _dev(np.concatenate(extra)), lanes, [8, 2, 6], out_hidden=hid2)
+        torch.cuda.synchronize()
+        H2 = hid2.cpu().numpy()
+        for i, Lr in enumerate([8, 2, 6]):
+            h_o, _ = oracle.append(m, o_lanes[i], extra[i], Lr)
+            assert eff[i] == o_lanes[i].ceiling
+            r = rel_l2(H2[cu2[i]:cu2[i + 1]], h_o)
+            say(name, mode, "append lane", lanes[i], "L", int(eff[i]), "rel %.2e" % r)
+            assert r <= bar(spec, mode, int(eff[i])), (i, r)
+        out = torch.empty(3, dtype=torch.int32, device="cuda")
+        hs = torch.empty(3, spec.d_model, dtype=torch.float32, device="cuda")
+        for t in range(3):
+            e = tl.tl_decode_step(model, lanes, [8, 8, 8], out, in_tokens=_dev(feed[t]), out_hidden=hs)
+            torch.cuda.synchronize()
+            Hd = hs.cpu().numpy()
+            for i in range(3):
+                h_o, _, _, L_o = oracle.decode_step(m, o_lanes[i], 8, token=int(feed[t, i]))
+                assert e[i] == L_o
+                assert rel_l2(Hd[i], h_o) <= bar(spec, mode, L_o), (t, i, rel_l2(Hd[i], h_o))
+    finally:
+        tl.tl_free(model)
+
+
+def test_store_h_fork_append_int8():
+    spec = SPECS["tiny-bf16-stack"]
+    w = synth.make_weights(spec, 83)
+    m = _oracle_model(w, "h8")
+    prefix = synth.tokens(83, 9300, 15, spec.vocab)
+    suffix = synth.tokens(83, 9301, 6, spec.vocab)
+    src = oracle.prefill(m, prefix, 4)[0]
+    child = oracle.fork(src, 11)
+    h_o, lg_o = oracle.append(m, child, suffix, 4)
+    model = load_model(w, max_lanes=4, max_pos=64, max_L=8, kv_arena_bytes=kv_bytes(spec, [4] * 2, [40] * 2),
+                       kv_mode=tl.TL_KV_H8)
+    try:
+        tl.tl_forward(model, np.array([0, 15], np.int32), _dev(prefix), L=4, lanes=[1], max_new_tokens=10)
+        tl.tl_lane_fork(model, 1, 3, 11, max_new_tokens=20)
+        hid = torch.empty(6, spec.d_model, dtype=torch.float32, device="cuda")
+        lg = torch.empty(1, spec.vocab, dtype=torch.float32, device="cuda")
+        tl.tl_append(model, [0, 6], _dev(suffix), [3], [4], out_hidden=hid, out_logits=lg)
+        torch.cuda.synchronize()
+        assert rel_l2(hid.cpu().numpy(), h_o) <= 1e-2 and rel_l2(lg.cpu().numpy()[0], lg_o) <= 1e-2
+    finally:
+        tl.tl_free(model)
+
+
+def test_store_h_lanes_take_less_of_the_arena():
+    """An arena sized for three INT8-h lanes does not hold three K/V lanes (the
+    allocation follows the per-position byte count), and continuous depth
+    decoding is refused in a store-h mode."""
+    spec = SPECS["tiny-w4"]
+    w = synth.make_weights(spec, 85)
+    d, H = spec.d_model, spec.n_heads
+    cap, L = 40, 4
+    slots = spec.n_pre + spec.n_post + spec.n_loop * L
+    per_lane = ((slots * cap * (d + 2 * H) + 1) // 2 + 63) // 64 * 64 * 2    # bytes, as the library rounds
+    arena = 3 * per_lane
+    prompt = synth.tokens(85, 9400, 8, spec.vocab)
+    toks = _dev(np.concatenate([prompt] * 3))
+    cu = np.array([0, 8, 16, 24], np.int32)
+    for mode, ok in ((tl.TL_KV_H8, True), (tl.TL_KV_KV, False)):
+        model = load_model(w, max_lanes=4, max_pos=64, max_L=8, kv_arena_bytes=arena, kv_mode=mode)
+        try:
+            if ok:
+                tl.tl_forward(model, cu, toks, L=L, lanes=[0, 1, 2], max_new_tokens=cap - 8)
+                out = torch.empty(3, 4, dtype=torch.int32, device="cuda")
+                with pytest.raises(tl.TLError) as ei:
+                    tl.tl_decode_run(model, [0, 1, 2], np.full((3, 4), L, np.int32), out)
+                assert ei.value.status == tl.TL_E_UNSUPPORTED
+            else:
+                with pytest.raises(tl.TLError) as ei:
+                    tl.tl_forward(model, cu, toks, L=L, lanes=[0, 1, 2], max_new_tokens=cap - 8)
+                assert ei.value.status == tl.TL_E_STATE
+        finally:
+            tl.tl_free(model)
