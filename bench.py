@@ -37,6 +37,7 @@ def parse():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-prefix", action="store_true", help="skip the shared-prefix measurement")
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative measurement")
+    ap.add_argument("--no-store-h", action="store_true", help="skip the store-h cache-mode measurement")
     ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one (no graph replay)")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -173,6 +174,8 @@ def main():
         out["shared_prefix"] = prefix_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_spec:
         out["speculative_B1"] = spec_bench(tl, torch, np, synth, kv_bytes, load_model)
+    if not args.no_store_h:
+        out["store_h_B1"] = store_h_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_cpu_baseline:
         log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -375,6 +378,41 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
                    "one verify pass, yielding accepted + 1 tokens); the verify piece includes a fork of the "
                    "32-token prompt")
     tl.tl_free(model)
+    return res
+
+
+def store_h_bench(tl, torch, np, synth, kv_bytes, load_model):
+    """Cache modes at batch 1 on the FP16-body model: 512-token prompt, 64 greedy
+    tokens at L = 8 (the first from the prompt pass, 63 cached steps); decode time
+    and the cache bytes one position takes in one slot."""
+    spec = synth.SPECS[3]
+    log("store-h: FP16-body model, batch 1")
+    w = synth.make_weights(spec, 0)
+    plen, new, L = 512, 64, 8
+    d, H = spec.d_model, spec.n_heads
+    prompt = torch.tensor(synth.tokens(0, synth.STREAM_PROMPT_TOKENS, plen, spec.vocab), dtype=torch.int32,
+                          device="cuda")
+    cu = np.array([0, plen], np.int32)
+    out1 = torch.empty(1, dtype=torch.int32, device="cuda")
+    res = {"config": "FP16-body model (2048-wide), batch 1, 512-token prompt, 63 cached greedy steps at L=8"}
+    per_pos = {"kv": 2 * d * 2, "h": d * 2, "h8": d + 2 * H, "h4": d // 2 + 2 * H}
+    for name, mode in (("kv", tl.TL_KV_KV), ("h", tl.TL_KV_H), ("h8", tl.TL_KV_H8), ("h4", tl.TL_KV_H4)):
+        model = load_model(w, max_lanes=1, max_pos=plen + new, max_L=L,
+                           kv_arena_bytes=kv_bytes(spec, [L], [plen + new]), kv_mode=mode)
+        best = None
+        for _ in range(2):
+            tl.tl_forward(model, cu, prompt, L=L, lanes=[0], max_new_tokens=new)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(new - 1):
+                tl.tl_decode_step(model, [0], [L], out1)
+            torch.cuda.synchronize()
+            el = time.perf_counter() - t0
+            best = el if best is None else min(best, el)
+        tl.tl_free(model)
+        res[name] = {"decode_ms": round(best * 1e3, 2), "tok_per_s": round((new - 1) / best, 1),
+                     "bytes_per_position_per_slot": per_pos[name]}
+        log("store-h %s: %s" % (name, res[name]))
     return res
 
 
