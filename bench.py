@@ -185,6 +185,7 @@ def main():
 def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
     """32 lanes, 32-token prompts, greedy cached decode at L = 8 on the FP16-body model;
     the same run with the device-side early-exit rule at three settings."""
+    ds = torch.cuda.Stream()   # repeated decode steps on a stream replay captured graphs
     spec = synth.SPECS[3]
     log("decode: FP16-body model")
     w = synth.make_weights(spec, 0)
@@ -200,7 +201,7 @@ def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
     def run(step):
         times, depth = [], 0
         for rep in range(3):
-            tl.tl_forward(model, cu, toks, L=8, lanes=lanes, max_new_tokens=new)
+            tl.tl_forward(model, cu, toks, L=8, lanes=lanes, max_new_tokens=new, stream=ds)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             tot = 0
@@ -213,7 +214,7 @@ def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
         return {"tok_per_s": round(n * (new - 1) / best, 1), "ms_per_step": round(best / (new - 1) * 1e3, 4),
                 "mean_depth": round(depth, 3)}
 
-    res = run(lambda: tl.tl_decode_step(model, lanes, Ls, out))
+    res = run(lambda: tl.tl_decode_step(model, lanes, Ls, out, stream=ds))
     res["config"] = ("FP16-body loop block, 32 lanes, 32-token prompts, 31 cached greedy steps at L=8 "
                      "(first token comes from the prefill)")
     ee = {
@@ -224,7 +225,7 @@ def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
         # every token finishes at iteration 4: iterations 5..8 run gated kernels only
         "all_finish_at_4": dict(patience=1, min_L=4, tau=1e30),
     }
-    res["early_exit"] = {k: run(lambda kw=kw: tl.tl_decode_step_ee(model, lanes, Ls, out, **kw))
+    res["early_exit"] = {k: run(lambda kw=kw: tl.tl_decode_step_ee(model, lanes, Ls, out, **kw, stream=ds))
                          for k, kw in ee.items()}
     tl.tl_free(model)
     return res
@@ -237,6 +238,7 @@ def prefix_bench(tl, torch, np, synth, kv_bytes, load_model):
     batched pass); SHARED prefills the prefix once, forks it into every request's
     lane and appends the suffixes (one batched pass).  Wall time of the whole job,
     best of two runs."""
+    ds = torch.cuda.Stream()   # repeated decode steps on a stream replay captured graphs
     spec = synth.SPECS[2]
     log("shared prefix: INT4 model")
     w = synth.make_weights(spec, 0)
@@ -263,18 +265,18 @@ def prefix_bench(tl, torch, np, synth, kv_bytes, load_model):
 
         def decode():
             for _ in range(new - 1):
-                tl.tl_decode_step(model, lanes, Ls, out)
+                tl.tl_decode_step(model, lanes, Ls, out, stream=ds)
 
         def no_cache():
             cu = np.arange(0, n * (P + suffix) + 1, P + suffix, dtype=np.int32)
-            tl.tl_forward(model, cu, full, L=L, lanes=lanes, max_new_tokens=new)
+            tl.tl_forward(model, cu, full, L=L, lanes=lanes, max_new_tokens=new, stream=ds)
             decode()
 
         def shared():
-            tl.tl_forward(model, np.array([0, P], np.int32), pre, L=L, lanes=[n_max], max_new_tokens=0)
+            tl.tl_forward(model, np.array([0, P], np.int32), pre, L=L, lanes=[n_max], max_new_tokens=0, stream=ds)
             for i in range(n):
-                tl.tl_lane_fork(model, n_max, i, P, max_new_tokens=suffix + new)
-            tl.tl_append(model, np.arange(0, n * suffix + 1, suffix, dtype=np.int32), suf, lanes, Ls)
+                tl.tl_lane_fork(model, n_max, i, P, max_new_tokens=suffix + new, stream=ds)
+            tl.tl_append(model, np.arange(0, n * suffix + 1, suffix, dtype=np.int32), suf, lanes, Ls, stream=ds)
             decode()
 
         row = {}
@@ -303,6 +305,7 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
     5-token verify pass at L = 8, one plain step at L = 8; with a drafts accepted
     per round a round yields a + 1 tokens, which gives the acceptance at which
     speculation breaks even."""
+    ds = torch.cuda.Stream()   # repeated decode steps on a stream replay captured graphs
     spec = synth.SPECS[2]
     log("speculative: INT4 model, batch 1")
     w = synth.make_weights(spec, 0)
@@ -327,7 +330,7 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
         return best
 
     def prefill(lane, L):
-        tl.tl_forward(model, cu, prompt, L=L, lanes=[lane], max_new_tokens=cap - plen)
+        tl.tl_forward(model, cu, prompt, L=L, lanes=[lane], max_new_tokens=cap - plen, stream=ds)
         torch.cuda.synchronize()
 
     res = {"config": "INT4 model (2048-wide), batch 1, 32-token prompt, 64 greedy tokens; drafts at L=2, "
@@ -337,11 +340,11 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
     def plain():
         prefill(0, 8)
         for _ in range(new - 1):
-            tl.tl_decode_step(model, [0], [8], out1)
+            tl.tl_decode_step(model, [0], [8], out1, stream=ds)
 
     def specd():
         prefill(1, 8)
-        acc_log.append(tl.tl_speculate(model, [1], 2, 8, k, new - 1, outs))
+        acc_log.append(tl.tl_speculate(model, [1], 2, 8, k, new - 1, outs, stream=ds))
 
     t_plain = timed(plain)
     t_spec = timed(specd)
@@ -353,6 +356,7 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
 
     # pieces of a round (prefill excluded: each piece is timed over 20 repetitions)
     def rep20(fn):
+        fn()   # the first call of a shape captures its graph
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for _ in range(20):
@@ -361,13 +365,13 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
         return (time.perf_counter() - t0) / 20
 
     prefill(2, 2)
-    t_draft = rep20(lambda: tl.tl_decode_step(model, [2], [2], out1, in_tokens=out1))
+    t_draft = rep20(lambda: tl.tl_decode_step(model, [2], [2], out1, in_tokens=out1, stream=ds))
     prefill(2, 8)
-    t_step = rep20(lambda: tl.tl_decode_step(model, [2], [8], out1, in_tokens=out1))
+    t_step = rep20(lambda: tl.tl_decode_step(model, [2], [8], out1, in_tokens=out1, stream=ds))
     five = torch.zeros(k + 1, dtype=torch.int32, device="cuda")
     prefill(3, 8)
-    t_verify = rep20(lambda: (tl.tl_lane_fork(model, 3, 2, plen, max_new_tokens=k + 1),
-                              tl.tl_append(model, [0, k + 1], five, [2], [8])))
+    t_verify = rep20(lambda: (tl.tl_lane_fork(model, 3, 2, plen, max_new_tokens=k + 1, stream=ds),
+                              tl.tl_append(model, [0, k + 1], five, [2], [8], stream=ds)))
     res["draft_step_L2_ms"] = round(t_draft * 1e3, 4)
     res["plain_step_L8_ms"] = round(t_step * 1e3, 4)
     res["verify_5_tokens_L8_ms"] = round(t_verify * 1e3, 4)
@@ -385,6 +389,7 @@ def store_h_bench(tl, torch, np, synth, kv_bytes, load_model):
     """Cache modes at batch 1 on the FP16-body model: 512-token prompt, 64 greedy
     tokens at L = 8 (the first from the prompt pass, 63 cached steps); decode time
     and the cache bytes one position takes in one slot."""
+    ds = torch.cuda.Stream()   # repeated decode steps on a stream replay captured graphs
     spec = synth.SPECS[3]
     log("store-h: FP16-body model, batch 1")
     w = synth.make_weights(spec, 0)
@@ -401,11 +406,11 @@ def store_h_bench(tl, torch, np, synth, kv_bytes, load_model):
                            kv_arena_bytes=kv_bytes(spec, [L], [plen + new]), kv_mode=mode)
         best = None
         for _ in range(2):
-            tl.tl_forward(model, cu, prompt, L=L, lanes=[0], max_new_tokens=new)
+            tl.tl_forward(model, cu, prompt, L=L, lanes=[0], max_new_tokens=new, stream=ds)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for _ in range(new - 1):
-                tl.tl_decode_step(model, [0], [L], out1)
+                tl.tl_decode_step(model, [0], [L], out1, stream=ds)
             torch.cuda.synchronize()
             el = time.perf_counter() - t0
             best = el if best is None else min(best, el)
