@@ -318,9 +318,16 @@ tl_status tend(tl_model* m, int cls, hipStream_t s) {
   } while (0)
 
 // ----------------------------------------------------------------- passes
-tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, hipStream_t s) {
+// With norm_h set (only on the few-row INT4 path, see small_w4) the product's
+// input is RMSNorm(norm_h) * norm_g, formed inside the GEMV; x_out receives it.
+tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, hipStream_t s,
+               const float* norm_h = nullptr, const float* norm_g = nullptr, void* x_out = nullptr) {
   GemmArgs g{};
   g.A = A;
+  g.norm_h = norm_h;
+  g.norm_g = norm_g;
+  g.norm_eps = m->cfg.rms_eps;
+  g.x_out = x_out;
   g.M = M;
   g.N = W.N;
   g.K = W.K;
@@ -331,8 +338,31 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
   g.partial_cap = kSplitFloats;
   g.live = m->gate_live;
   e.pair_g = m->G;
+  if (gemv_w4_applies(g, e.kind)) {   // a few rows of an INT4 product: no split-K pass
+    HIPCHK(launch_gemv_w4(g, e, s));
+    if (e.kind == EPI_RESID && e.norm_g)
+      HIPCHK(launch_rmsnorm(m->act, e.h, e.norm_g, nullptr, M, g.N, e.norm_eps, e.norm_out, s));
+    return TL_OK;
+  }
+  if (norm_h) return fail(TL_E_STATE, "normalised input outside the GEMV path");
   HIPCHK(launch_gemm(m->act, g, e, s));
   return TL_OK;
+}
+
+// A block whose four products all take the few-row INT4 GEMV (INT4 loop block,
+// n <= 4 rows): its RMSNorms are formed inside the QKV and gate/up GEMVs.
+bool small_w4(const tl_model* m, const tl::BlockDev& B, int n) {
+  if (m->act != DT_F16) return false;
+  for (const MatDev* W : {&B.qkv, &B.o, &B.gu, &B.down}) {
+    GemmArgs g{};
+    g.M = n;
+    g.N = W->N;
+    g.K = W->K;
+    g.B = W->dense;
+    g.Bw4 = W->dense ? nullptr : W->w4;
+    if (!gemv_w4_applies(g, EPI_RESID)) return false;
+  }
+  return true;
 }
 
 // One pre-norm block on n rows.  x_ready: the caller's previous block already left
@@ -341,13 +371,16 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
 // projection's residual update when possible (then ws.x16 holds its output).
 tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, const KVParams& kv, hipStream_t s,
                     const AttnTile* tiles = nullptr, int n_tiles = 0, bool x_ready = false,
-                    const float* next_norm = nullptr, int hgroup = -1) {
+                    const float* next_norm = nullptr, int hgroup = -1, bool* x_next = nullptr) {
+  if (x_next) *x_next = false;
   if (n <= 0) return TL_OK;
   const tl_config& c = m->cfg;
   const BlockDev& B = m->blocks[b];
   auto& w = m->ws;
   const int tb = B.kind == 1 ? TL_T_GEMM_QKV_LOOP : TL_T_GEMM_QKV_BOUNDARY;
-  if (!x_ready)
+  const bool gv = small_w4(m, B, n);   // norms inside the GEMVs, none fused into the residual products
+  const bool norm_in_qkv = gv && !x_ready;
+  if (!x_ready && !gv)
     TIMED(TL_T_RMSNORM, HIPCHK(launch_rmsnorm(m->act, h, B.norm1, nullptr, n, c.d_model, c.rms_eps, w.x16, s)));
   GemmEpi e{};
   e.kind = EPI_QKV;
@@ -365,7 +398,8 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   const tl::HPass* hpass = (m->hpass && hgroup >= 0) ? m->hpass : nullptr;
   const KVParams& akv = hpass ? hpass->skv : kv;
   e.kv = akv;
-  TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s)));
+  if (norm_in_qkv) TIMED(tb + 0, TRY(gemm(m, nullptr, n, B.qkv, e, s, h, B.norm1, w.x16)));
+  else TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s)));
   if (hpass) {
     HCacheParams hp = hpass->hp;
     hp.slot = kv.s0;
@@ -385,7 +419,7 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   r.kind = EPI_RESID;
   r.h = h;
   r.ldh = c.d_model;
-  r.norm_g = B.norm2;
+  r.norm_g = gv ? nullptr : B.norm2;
   r.norm_out = w.x16;
   r.norm_eps = c.rms_eps;
   TIMED(tb + 1, TRY(gemm(m, w.o16, n, B.o, r, s)));
@@ -393,9 +427,11 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   sw.kind = EPI_SWIGLU;
   sw.u_out = w.u16;
   sw.F = c.ffn;
-  TIMED(tb + 2, TRY(gemm(m, w.x16, n, B.gu, sw, s)));
-  r.norm_g = next_norm;
+  if (gv) TIMED(tb + 2, TRY(gemm(m, nullptr, n, B.gu, sw, s, h, B.norm2)));
+  else TIMED(tb + 2, TRY(gemm(m, w.x16, n, B.gu, sw, s)));
+  r.norm_g = gv ? nullptr : next_norm;
   TIMED(tb + 3, TRY(gemm(m, w.u16, n, B.down, r, s)));
+  if (x_next) *x_next = r.norm_g != nullptr;
   return TL_OK;
 }
 
@@ -542,8 +578,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   for (int b = 0; b < c.n_pre; ++b) {
     kv.s0 = p.scoring ? 0 : b;
     const float* nn = b + 1 < c.n_pre ? m->blocks[b + 1].norm1 : (Lmax > 0 ? loop_first() : nullptr);
-    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn, hmode ? 0 : -1));
-    x_ready = nn != nullptr;
+    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn, hmode ? 0 : -1, &x_ready));
   }
   float* h = w.hA;
   float* hn = w.hB;
@@ -573,8 +608,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
       // probe normalises into its own buffer, rows it finishes are only carried)
       const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1 : (leaving ? nullptr : loop_first());
       TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
-                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1));
-      x_ready = nn != nullptr;
+                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1, &x_ready));
     }
     if (probe) {
       if (by_margin) {
@@ -604,8 +638,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     kv.s0 = p.scoring ? 0 : c.n_pre + b;
     const float* nn = b + 1 < c.n_post ? m->blocks[c.n_pre + c.n_loop + b + 1].norm1 : nullptr;
     TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn,
-                  hmode ? 0 : -1));
-    x_ready = nn != nullptr;
+                  hmode ? 0 : -1, &x_ready));
   }
   return TL_OK;
 }

@@ -38,6 +38,14 @@ struct GemmArgs {
   // device count of rows still running (early exit), or NULL: when it reads 0 the
   // kernels return at once
   const int32_t* live;
+  // GEMV only: with norm_h set, A is the fp32 residual norm_h [M, K] normalised on
+  // the fly, x = h / sqrt(mean(h^2) + norm_eps) * norm_g rounded to the operand
+  // type (the RMSNorm of the producing block, computed by every workgroup); the
+  // x rows are also written to x_out when it is set
+  const float* norm_h;
+  const float* norm_g;
+  float norm_eps;
+  void* x_out;
 };
 
 struct GemmEpi {
@@ -152,6 +160,11 @@ hipError_t launch_hcache_write(int dtype, const void* x, const RowInfo* rows, in
 // Read cached rows (lane, pos) back as operand-type x [n, d] (codes times scale).
 hipError_t launch_hcache_read(int dtype, const HCacheParams& hp, const RowInfo* rows, int n, void* out,
                               hipStream_t s);
+// INT4 GEMV for 1..4 rows (W4G128 weights, QKV / RESID / SWIGLU epilogues; a
+// RESID norm is not fused): no split of K, no partials.  gemv_w4_applies tells
+// whether a product takes this path.
+bool gemv_w4_applies(const GemmArgs& g, int kind);
+hipError_t launch_gemv_w4(const GemmArgs& g, const GemmEpi& e, hipStream_t s);
 hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
