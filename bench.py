@@ -49,14 +49,21 @@ def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
 
+def gemm_source_sha256() -> str:
+    """Hash of the sources the GEMM kernels are compiled from (counters go stale when they change)."""
+    h = hashlib.sha256()
+    for name in ("gemm.hip", "epilogue.h", "device_common.h"):
+        h.update(open(os.path.join(ROOT, "looped_transformer_amd", "csrc", name), "rb").read())
+    return h.hexdigest()
+
+
 def traffic_for(kernel_class: str):
     """HBM bytes per launch from committed rocprofv3 counter runs, if the kernel source is unchanged."""
     path = os.path.join(ROOT, "profiles", "traffic_%s.json" % kernel_class)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    src = open(os.path.join(ROOT, "looped_transformer_amd", "csrc", "gemm.hip"), "rb").read()
-    if rec.get("gemm_source_sha256") != hashlib.sha256(src).hexdigest():
+    if rec.get("gemm_source_sha256") != gemm_source_sha256():
         return None
     return rec.get("bytes_per_launch")
 
