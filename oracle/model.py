@@ -49,7 +49,7 @@ __all__ = [
     "greedy_argmax", "clamp_depths", "active_lists", "bf16_bits_to_float",
     "EarlyExit", "probe_iteration", "relative_delta", "logit_margin", "decode_step_ee",
     "append", "fork", "truncate", "speculative_decode",
-    "H_MODES", "round_to_operand", "quantize_h", "dequant_h", "h_store", "h_bytes_per_position",
+    "H_MODES", "round_to_operand", "quantize_h", "dequant_h", "h_store", "delta_store", "h_bytes_per_position",
 ]
 
 
@@ -186,7 +186,7 @@ def bf16_bits_to_float(bits: np.ndarray) -> np.ndarray:
 # operand type, "h8" / "h4" as symmetric codes in [-127, 127] / [-7, 7] with one
 # fp16 scale per (position, head).
 
-H_MODES = ("kv", "h", "h8", "h4")
+H_MODES = ("kv", "h", "h8", "h4", "d8")
 H_LEVELS = {"h8": 127, "h4": 7}
 
 
@@ -237,6 +237,23 @@ def h_store(x: np.ndarray, act: str, n_heads: int, mode: str) -> np.ndarray:
     return dequant_h(q, sc)
 
 
+def delta_store(x: np.ndarray, prev_hat: np.ndarray, act: str, n_heads: int) -> np.ndarray:
+    """Iteration-axis delta-KV ([BENCH] section 9): a loop layer's slot at
+    iteration j >= 2 codes the difference between its x (operand type) and the
+    previous iteration's reconstruction prev_hat as int8 with one fp16 scale per
+    (row, head); the slot's reconstruction is prev_hat + q * s.  The difference
+    and the sum are taken in fp32, in iteration order (anchor first), so the
+    reconstruction error stays one code step at every depth.
+    """
+    x_op = round_to_operand(x, act).astype(np.float32)
+    p32 = np.asarray(prev_hat, dtype=np.float64).astype(np.float32)
+    q, sc = quantize_h(x_op - p32, n_heads, 127)
+    T, d = q.shape
+    step = (q.reshape(T, n_heads, d // n_heads).astype(np.float32)
+            * sc.astype(np.float32)[..., None]).reshape(T, d)
+    return (p32 + step).astype(np.float64)
+
+
 def h_bytes_per_position(d: int, n_heads: int, mode: str, operand_bytes: int = 2) -> int:
     """Bytes one position takes in one slot: K and V, x in the operand type, or
     codes (one byte, or half a byte packed two to a byte) plus fp16 scales."""
@@ -244,7 +261,7 @@ def h_bytes_per_position(d: int, n_heads: int, mode: str, operand_bytes: int = 2
         return 2 * d * operand_bytes
     if mode == "h":
         return d * operand_bytes
-    if mode == "h8":
+    if mode in ("h8", "d8"):       # d8: a delta slot; its anchor slot takes the "h" size
         return d + 2 * n_heads
     return d // 2 + 2 * n_heads
 
@@ -308,14 +325,18 @@ class OracleModel:
     def embed_rows(self, tokens: np.ndarray) -> np.ndarray:
         return _stored_to_float(self.embed[np.asarray(tokens)], self.embed_kind, self.dt)
 
-    def block(self, b: int, h: np.ndarray, pos: np.ndarray, past_k: np.ndarray, past_v: np.ndarray):
+    def block(self, b: int, h: np.ndarray, pos: np.ndarray, past_k: np.ndarray, past_v: np.ndarray,
+              prev: np.ndarray | None = None):
         """One pre-norm block on rows h at positions pos of ONE lane.
 
         past_k/past_v hold the lane's earlier positions in this block application's
         own cache slot ([CLI] TINYLOOP_KV_H_MODE: per-layer K/V buffers).  Returns the
         new residual rows and the k, v rows to append to that slot.  In a store-h
         mode the slot keeps h_store(x) rows instead (returned as k, with v empty),
-        and K, V of every position are rebuilt from them by this block's wqkv.
+        and K, V of every position are rebuilt from them by this block's wqkv.  In
+        the delta mode ("d8") prev holds the previous iteration's reconstruction of
+        these rows for a loop slot at iteration >= 2 (delta_store), else None (the
+        slot keeps x in the operand type: boundary blocks and the anchor).
         """
         sp, W = self.spec, self.blocks[b]
         H, dh, d = sp.n_heads, sp.head_dim, sp.d_model
@@ -332,7 +353,11 @@ class OracleModel:
             k_all = np.concatenate([past_k, k], axis=0)
             v_all = np.concatenate([past_v, v], axis=0)
         else:
-            k = h_store(x, sp.act_dtype, H, self.kv_mode)          # the rows this slot keeps
+            if self.kv_mode == "d8":
+                k = (delta_store(x, prev, sp.act_dtype, H) if prev is not None
+                     else h_store(x, sp.act_dtype, H, "h"))
+            else:
+                k = h_store(x, sp.act_dtype, H, self.kv_mode)      # the rows this slot keeps
             v = np.zeros((T, 0), dtype=self.dt)
             x_all = np.concatenate([past_k, k], axis=0)
             S = x_all.shape[0]
@@ -357,6 +382,13 @@ class OracleModel:
             return np.zeros((0, sp.d_model), dtype=self.dt), np.zeros((0, 0), dtype=self.dt)
         z = np.zeros((0, sp.n_heads, sp.head_dim), dtype=self.dt)
         return z, z
+
+    def delta_prev(self, kv: dict, key, pos: np.ndarray):
+        """Delta mode: the previous iteration's reconstruction of rows pos for a loop
+        slot at iteration >= 2 (that slot already holds them), else None."""
+        if self.kv_mode != "d8" or key[0] != "loop" or key[1] < 2:
+            return None
+        return kv[("loop", key[1] - 1, key[2])][0][np.asarray(pos)]
 
     def slots(self, L: int):
         """Block applications in pipeline order for depth L: (block index, cache-slot key)."""
@@ -406,7 +438,7 @@ def prefill(m: OracleModel, tokens, L: int, want_logits: str = "last"):
     kv = {}
     for b, key in m.slots(L):
         pk, pv = m.empty_kv()
-        h, k, v = m.block(b, h, pos, pk, pv)
+        h, k, v = m.block(b, h, pos, pk, pv, prev=m.delta_prev(kv, key, pos))
         kv[key] = (k, v)
     lane = Lane(tokens=list(map(int, tokens)), kv=kv, ceiling=L, hidden_last=h[-1].copy())
     logits = None
@@ -437,7 +469,7 @@ def decode_step(m: OracleModel, lane: Lane, L_req: int, token: int | None = None
     for b, key in m.slots(L):
         pk, pv = lane.kv[key]
         assert pk.shape[0] == p, "cache slot misses earlier positions"
-        h, k, v = m.block(b, h, pos, pk, pv)
+        h, k, v = m.block(b, h, pos, pk, pv, prev=m.delta_prev(lane.kv, key, pos))
         lane.kv[key] = (np.concatenate([pk, k]), np.concatenate([pv, v]))
     lane.tokens.append(tok)
     lane.ceiling = L
@@ -473,7 +505,7 @@ def append(m: OracleModel, lane: Lane, tokens, L_req: int, want_logits: str = "l
     for b, key in m.slots(L):
         pk, pv = lane.kv[key]
         assert pk.shape[0] == p0, "cache slot misses earlier positions"
-        h, k, v = m.block(b, h, pos, pk, pv)
+        h, k, v = m.block(b, h, pos, pk, pv, prev=m.delta_prev(lane.kv, key, pos))
         lane.kv[key] = (np.concatenate([pk, k]), np.concatenate([pv, v]))
     lane.tokens.extend(map(int, tokens))
     lane.ceiling = L
@@ -624,7 +656,7 @@ def decode_step_ee(m: OracleModel, lane: Lane, L_req: int, ee: EarlyExit, token:
     def run(b, key, h):
         pk, pv = lane.kv[key]
         assert pk.shape[0] == p, "cache slot misses earlier positions"
-        h, k, v = m.block(b, h, pos, pk, pv)
+        h, k, v = m.block(b, h, pos, pk, pv, prev=m.delta_prev(lane.kv, key, pos))
         lane.kv[key] = (np.concatenate([pk, k]), np.concatenate([pv, v]))
         return h
 
@@ -691,6 +723,7 @@ def forward_batch(m: OracleModel, seqs, Ls, want_logits: str = "last"):
     active row lists per iteration).
     """
     sp = m.spec
+    assert m.kv_mode != "d8", "the delta cache mode chains a lane's slots: use prefill / append / decode_step"
     seqs = [np.asarray(s, dtype=np.int64) for s in seqs]
     lens = [len(s) for s in seqs]
     starts = np.cumsum([0] + lens)
@@ -732,6 +765,7 @@ def forward_ragged(m: OracleModel, tokens, depth_per_pos, want_logits: str = "al
     per-token depths.  Returns (hidden [T, d], logits [T, V] or None).
     """
     sp = m.spec
+    assert m.kv_mode != "d8", "the delta cache mode chains a lane's slots: use prefill / append / decode_step"
     tokens = np.asarray(tokens, dtype=np.int64)
     dep = np.asarray(depth_per_pos)
     assert np.all(np.diff(dep) <= 0) and dep.min() >= 1

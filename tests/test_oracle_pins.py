@@ -724,3 +724,77 @@ def test_store_h_cached_equals_uncached(mode):
     _, h_m, _ = oracle.prefill(m, toks, 3)
     err = np.linalg.norm(h_m - h_kv) / np.linalg.norm(h_kv)
     assert 1e-7 < err < {"h": 5e-3, "h8": 2e-2, "h4": 2e-1}[mode], err
+
+
+# ---------------------------------------------------------------------------
+# delta-KV along the iteration axis
+
+
+def _bf16_model(mode, seed=4):
+    import copy
+    spec = synth.ModelSpec("tiny-bf16", 320, 192, 2, 96, 384, 1, 2, 1, "bf16", "bf16")
+    w = synth.make_weights(spec, seed)
+    m = copy.copy(oracle.OracleModel.from_weights(w))
+    m.kv_mode = mode
+    return w, m
+
+
+def test_delta_exact_differences_equal_store_h(monkeypatch):
+    """With differences kept exactly, the delta chain reproduces the operand-type
+    store-h mode: the anchor, the chaining of each loop layer's slots and the
+    rebuild are right."""
+    w, md = _bf16_model("d8")
+    _, mh = _bf16_model("h")
+    monkeypatch.setattr(oracle.model, "delta_store",
+                        lambda x, prev, act, H: oracle.round_to_operand(x, act))
+    toks = list(synth.tokens(0, 3500, 9, 320))
+    a, ha, _ = oracle.prefill(md, toks, 4)
+    b, hb, _ = oracle.prefill(mh, toks, 4)
+    assert np.array_equal(ha, hb)
+    for _ in range(2):
+        xa, xb = oracle.decode_step(md, a, 4), oracle.decode_step(mh, b, 4)
+        assert np.array_equal(xa[0], xb[0]) and xa[2] == xb[2]
+
+
+def test_delta_reconstruction_within_one_step(monkeypatch):
+    """Each delta slot's reconstruction is within half a code step (plus fp32
+    rounding) of its own x: errors do not add up along the iterations; the first
+    iteration keeps x exactly in the operand type."""
+    w, md = _bf16_model("d8")
+    seen = []
+    real = oracle.model.delta_store
+
+    def rec(x, prev, act, H):
+        out = real(x, prev, act, H)
+        seen.append((oracle.round_to_operand(x, act), np.asarray(prev, np.float64), out, H))
+        return out
+
+    monkeypatch.setattr(oracle.model, "delta_store", rec)
+    toks = list(synth.tokens(0, 3501, 11, 320))
+    oracle.prefill(md, toks, 6)
+    monkeypatch.undo()
+    assert len(seen) == 2 * 5                      # 2 loop layers x iterations 2..6
+    for x_op, prev, out, H in seen:
+        T, d = x_op.shape
+        diff = (x_op.astype(np.float32) - prev.astype(np.float32)).astype(np.float64)
+        step = np.abs(diff).reshape(T, H, d // H).max(axis=-1) / 127.0
+        tol = np.repeat(step, d // H, axis=1) * 0.5 * (1 + 2e-3) + np.abs(x_op) * 2.0 ** -22
+        assert np.all(np.abs(out - x_op) <= tol)
+
+
+def test_delta_cached_equals_uncached():
+    w, md = _bf16_model("d8")
+    toks = list(synth.tokens(0, 3502, 10, 320))
+    lane, _, _ = oracle.prefill(md, toks, 3)
+    seq = list(toks)
+    for _ in range(3):
+        seq.append(lane.pending)
+        h, logits, _, _ = oracle.decode_step(md, lane, 3)
+        _, h_full, lg_full = oracle.prefill(md, seq, 3, want_logits="last")
+        assert np.allclose(h, h_full[-1], rtol=1e-10, atol=1e-12)
+        assert np.allclose(logits, lg_full, rtol=1e-9, atol=1e-11)
+    _, mk = _bf16_model("kv")
+    _, h_kv, _ = oracle.prefill(mk, toks, 3)
+    _, h_d, _ = oracle.prefill(md, toks, 3)
+    err = np.linalg.norm(h_d - h_kv) / np.linalg.norm(h_kv)
+    assert 1e-7 < err < 2e-2, err
