@@ -407,8 +407,11 @@ def store_h_bench(tl, torch, np, synth, kv_bytes, load_model):
     cu = np.array([0, plen], np.int32)
     out1 = torch.empty(1, dtype=torch.int32, device="cuda")
     res = {"config": "FP16-body model (2048-wide), batch 1, 512-token prompt, 63 cached greedy steps at L=8"}
-    per_pos = {"kv": 2 * d * 2, "h": d * 2, "h8": d + 2 * H, "h4": d // 2 + 2 * H}
-    for name, mode in (("kv", tl.TL_KV_KV), ("h", tl.TL_KV_H), ("h8", tl.TL_KV_H8), ("h4", tl.TL_KV_H4)):
+    # bytes of one position in one loop slot (delta: a slot past the first iteration; the
+    # first iteration's anchor slot takes d * 2)
+    per_pos = {"kv": 2 * d * 2, "h": d * 2, "h8": d + 2 * H, "h4": d // 2 + 2 * H, "d8": d + 2 * H}
+    for name, mode in (("kv", tl.TL_KV_KV), ("h", tl.TL_KV_H), ("h8", tl.TL_KV_H8), ("h4", tl.TL_KV_H4),
+                       ("d8", tl.TL_KV_D8)):
         model = load_model(w, max_lanes=1, max_pos=plen + new, max_L=L,
                            kv_arena_bytes=kv_bytes(spec, [L], [plen + new]), kv_mode=mode)
         best = None

@@ -91,6 +91,12 @@ typedef struct {
  * TL_KV_H8: x as int8 codes, one fp16 scale per (position, head): d + 2 H bytes.
  * TL_KV_H4: x as packed two's-complement int4 codes (element 2i in the low nibble)
  *   with one fp16 scale per (position, head): d / 2 + 2 H bytes.
+ * TL_KV_D8: iteration-axis delta-KV ("Benchmark Comparison" page, measured
+ *   benchmarks, section 9): a loop layer's slot at iteration 1 keeps x in the
+ *   operand type (the anchor); at iteration j >= 2 it keeps int8 codes (one fp16
+ *   scale per position and head) of x_j minus the reconstruction of iteration
+ *   j - 1, the reconstruction being the anchor plus the decoded differences,
+ *   summed in fp32 in iteration order.  Pre and post blocks keep x as TL_KV_H.
  * Codes: s = fp16(max|x| / levels) over the head (division in fp32), q =
  * clamp(rint(x / s), -levels, levels), levels 127 / 7, q = 0 where s = 0.
  * In the store-h modes each attention rebuilds K and V of every cached position
@@ -98,7 +104,7 @@ typedef struct {
  * and attention costs a projection over the whole context.  Calls without lanes
  * (scoring) keep no cache and compute K and V directly; tl_decode_run needs
  * TL_KV_KV. */
-typedef enum { TL_KV_KV = 0, TL_KV_H = 1, TL_KV_H8 = 2, TL_KV_H4 = 3 } tl_kv_mode;
+typedef enum { TL_KV_KV = 0, TL_KV_H = 1, TL_KV_H8 = 2, TL_KV_H4 = 3, TL_KV_D8 = 4 } tl_kv_mode;
 
 /* Host weights of one block, canonical layout: linear weights are [out, in]
  * row-major (y = x W^T).  wqkv rows are q (heads 0..H-1, head_dim rows each), then

@@ -20,7 +20,7 @@ HEADER = os.path.join(os.path.dirname(_HERE), "include", "tl.h")
 
 TL_OK, TL_E_ARG, TL_E_OOM, TL_E_HIP, TL_E_STATE, TL_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
 TL_DT_F32, TL_DT_F16, TL_DT_BF16, TL_DT_W4G128 = 0, 1, 2, 3
-TL_KV_KV, TL_KV_H, TL_KV_H8, TL_KV_H4 = 0, 1, 2, 3
+TL_KV_KV, TL_KV_H, TL_KV_H8, TL_KV_H4, TL_KV_D8 = 0, 1, 2, 3, 4
 _STATUS = {0: "TL_OK", -1: "TL_E_ARG", -2: "TL_E_OOM", -3: "TL_E_HIP", -4: "TL_E_STATE", -5: "TL_E_UNSUPPORTED"}
 
 

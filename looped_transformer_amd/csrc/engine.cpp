@@ -525,7 +525,7 @@ tl_status plan_hpass(tl_model* m, const Pass& p, tl::HPass& hp, hipStream_t s) {
   TRY(aux_upload(m, st, s));
   uint8_t* base = static_cast<uint8_t*>(m->aux_dev);
   hp.hp = HCacheParams{static_cast<uint8_t*>(m->kv_base), m->d_lane_off, m->d_lane_cap, m->esz, m->hrb, 0,
-                       m->kv_mode, c.n_heads, c.head_dim};
+                       m->kv_mode, c.n_heads, c.head_dim, c.n_pre + c.n_post, c.n_loop, m->hrbA, m->hrb};
   hp.skv = KVParams{m->h_kv, reinterpret_cast<const int64_t*>(base + o_soff),
                     reinterpret_cast<const int32_t*>(base + o_scap), c.n_heads, c.head_dim, 0, 0};
   hp.rec.clear();
@@ -710,8 +710,15 @@ int lane_slots(const tl_config& c, int ceiling) { return c.n_pre + c.n_post + c.
 uint64_t lane_elems(const tl_model* m, int ceiling, int cap) {
   const tl_config& c = m->cfg;
   uint64_t e = (uint64_t)lane_slots(c, ceiling) * 2ull * c.n_heads * (uint64_t)cap * c.head_dim;
-  if (m->kv_mode != TL_KV_KV)   // store-h: rows of hrb bytes, counted in operand elements
-    e = ((uint64_t)lane_slots(c, ceiling) * cap * m->hrb + m->esz - 1) / m->esz;
+  if (m->kv_mode != TL_KV_KV) {   // store-h: rows of hrb bytes, counted in operand elements
+    const uint64_t ns = lane_slots(c, ceiling);
+    uint64_t bytes = ns * cap * m->hrb;
+    if (m->kv_mode == TL_KV_D8) {   // anchor-format slots first, then the deltas
+      const uint64_t A = std::min<uint64_t>(ns, c.n_pre + c.n_post + c.n_loop);
+      bytes = A * cap * m->hrbA + (ns - A) * cap * m->hrb;
+    }
+    e = (bytes + m->esz - 1) / m->esz;
+  }
   return (e + 63) / 64 * 64;
 }
 
@@ -821,7 +828,7 @@ tl_status validate_config(const tl_config* c) {
   }
   if (c->loop_dtype == DT_W4G128 && (c->d_model % 128 || c->ffn % 128))
     return fail(TL_E_UNSUPPORTED, "W4G128 needs d_model and ffn multiples of 128");
-  if (c->kv_mode < TL_KV_KV || c->kv_mode > TL_KV_H4) return fail(TL_E_ARG, "kv_mode %d unknown", c->kv_mode);
+  if (c->kv_mode < TL_KV_KV || c->kv_mode > TL_KV_D8) return fail(TL_E_ARG, "kv_mode %d unknown", c->kv_mode);
   return TL_OK;
 }
 
@@ -902,7 +909,8 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   m->kv_mode = cfg->kv_mode;
   {
     const int d = cfg->d_model, H = cfg->n_heads;
-    m->hrb = m->kv_mode == TL_KV_H ? d * m->esz : m->kv_mode == TL_KV_H8 ? d + 2 * H : d / 2 + 2 * H;
+    m->hrb = m->kv_mode == TL_KV_H ? d * m->esz : m->kv_mode == TL_KV_H4 ? d / 2 + 2 * H : d + 2 * H;
+    m->hrbA = d * m->esz;   // delta mode: boundary and anchor slots
   }
   std::vector<void*> temps;
   auto cleanup_fail = [&](tl_status st) {
@@ -1388,13 +1396,26 @@ tl_status tl_lane_fork(tl_model* m, int32_t src, int32_t dst, int32_t prefix_len
   const size_t o_loff = st.add(loff), o_lcap = st.add(lcap);
   TRY(stage_upload(m, st, s));
   // every (slot, K/V, head) block is [cap][head_dim] (store-h: every slot is [cap]
-  // rows of hrb bytes): copy its first prefix_len rows
+  // rows of hrb bytes; delta mode: the anchor-format slots, then the delta slots):
+  // copy its first prefix_len rows
   const bool hm = m->kv_mode != TL_KV_KV;
-  const size_t row = hm ? (size_t)m->hrb : (size_t)c.head_dim * m->esz;
-  const size_t blocks = hm ? (size_t)ln.nslots : (size_t)ln.nslots * 2 * c.n_heads;
   uint8_t* kvb = static_cast<uint8_t*>(m->kv_base);
-  HIPCHK(hipMemcpy2DAsync(kvb + ln.off * m->esz, (size_t)ln.cap * row, kvb + sl.off * m->esz, (size_t)sl.cap * row,
-                          (size_t)prefix_len * row, blocks, hipMemcpyDeviceToDevice, s));
+  uint8_t* dstb = kvb + ln.off * m->esz;
+  const uint8_t* srcb = kvb + sl.off * m->esz;
+  auto copy_rows = [&](uint8_t* dp, const uint8_t* sp, size_t row, size_t blocks) -> tl_status {
+    if (blocks)
+      HIPCHK(hipMemcpy2DAsync(dp, (size_t)ln.cap * row, sp, (size_t)sl.cap * row, (size_t)prefix_len * row, blocks,
+                              hipMemcpyDeviceToDevice, s));
+    return TL_OK;
+  };
+  if (m->kv_mode == TL_KV_D8) {
+    const size_t A = std::min<size_t>(ln.nslots, c.n_pre + c.n_post + c.n_loop);
+    TRY(copy_rows(dstb, srcb, m->hrbA, A));
+    TRY(copy_rows(dstb + A * ln.cap * m->hrbA, srcb + A * sl.cap * m->hrbA, m->hrb, ln.nslots - A));
+  } else {
+    TRY(copy_rows(dstb, srcb, hm ? (size_t)m->hrb : (size_t)c.head_dim * m->esz,
+                  hm ? (size_t)ln.nslots : (size_t)ln.nslots * 2 * c.n_heads));
+  }
   if (ln.pending) HIPCHK(hipMemcpyAsync(m->d_pending + dst, m->d_pending + src, 4, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipMemcpyAsync(m->d_lane_off, staged<int64_t>(m, o_loff), loff.size() * 8, hipMemcpyDeviceToDevice, s));
   HIPCHK(hipMemcpyAsync(m->d_lane_cap, staged<int32_t>(m, o_lcap), lcap.size() * 4, hipMemcpyDeviceToDevice, s));

@@ -94,7 +94,8 @@ struct tl_model {
   int G = 16;
   int esz = 2;               // bytes of an activation / KV element
   int kv_mode = 0;           // tl_kv_mode
-  int hrb = 0;               // store-h: bytes of one position of one slot
+  int hrb = 0;               // store-h: bytes of one position of one slot (delta mode: of a delta slot)
+  int hrbA = 0;              // delta mode: of a boundary or anchor slot
   tl_alloc_fn alloc = nullptr;
   tl_dealloc_fn dealloc = nullptr;
   void* user = nullptr;

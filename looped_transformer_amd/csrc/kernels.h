@@ -146,12 +146,17 @@ hipError_t launch_spec_accept(const int32_t* draft, const int32_t* g, const int3
 // H fp16 scales; mode 3: d/2 bytes of two's-complement nibbles (element 2i low,
 // 2i+1 high) then H fp16 scales.  Codes: s = fp16(max|x| / levels) over the head's
 // dh values (division in fp32), q = clamp(rint(x / s), -levels, levels), levels 127
-// or 7, q = 0 where s = 0.
+// or 7, q = 0 where s = 0.  mode 4 (delta along the iterations): the first
+// n_bound + n_loop slots (pre/post blocks, then iteration 1 of each loop layer)
+// keep operand-type rows of rbA bytes, the later slots (iteration j >= 2 of loop
+// layer l is slot n_bound + (j - 1) n_loop + l) int8 codes of x minus the
+// previous iteration's reconstruction plus H fp16 scales, rows of rbD bytes.
 struct HCacheParams {
   uint8_t* base;
   const int64_t* lane_off;
   const int32_t* lane_cap;
   int32_t unit, rb, slot, mode, H, dh;
+  int32_t n_bound, n_loop, rbA, rbD;
 };
 // Write the operand-type rows x [n, d] of rows (lane, pos) into the cache (rows
 // marked done are skipped when skip_done).

@@ -236,8 +236,44 @@ __global__ __launch_bounds__(256) void argmax_reduce_kernel(const float* __restr
 // ---------------------------------------------------------------- store-h cache
 // One 64-lane workgroup per (row, head); lane i owns elements 2i and 2i + 1 of the
 // head (one packed byte in mode 3).
-__device__ __forceinline__ uint8_t* hcache_row(const HCacheParams& hp, const RowInfo& ri) {
-  return hp.base + hp.lane_off[ri.lane] * hp.unit + ((int64_t)hp.slot * hp.lane_cap[ri.lane] + ri.pos) * hp.rb;
+__device__ __forceinline__ uint8_t* hcache_row(const HCacheParams& hp, const RowInfo& ri, int slot) {
+  const int64_t cap = hp.lane_cap[ri.lane];
+  uint8_t* lane = hp.base + hp.lane_off[ri.lane] * hp.unit;
+  if (hp.mode != 4) return lane + ((int64_t)slot * cap + ri.pos) * hp.rb;
+  const int A = hp.n_bound + hp.n_loop;
+  if (slot < A) return lane + ((int64_t)slot * cap + ri.pos) * hp.rbA;
+  return lane + (int64_t)A * cap * hp.rbA + ((int64_t)(slot - A) * cap + ri.pos) * hp.rbD;
+}
+
+// Symmetric codes of one head's values (v0, v1 per lane): the wave's absmax
+// gives s = fp16(max / levels), q = clamp(rint(v / s)).
+__device__ __forceinline__ f16 hcache_codes(float v0, float v1, float levels, int& q0, int& q1) {
+  const float am = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const f16 s16 = (f16)(am / levels);
+  const float sc = (float)s16;
+  q0 = q1 = 0;
+  if (sc > 0.f) {
+    q0 = (int)fminf(fmaxf(rintf(v0 / sc), -levels), levels);
+    q1 = (int)fminf(fmaxf(rintf(v1 / sc), -levels), levels);
+  }
+  return s16;
+}
+
+// Delta mode: reconstruction of elements e, e + 1 of head h at iteration `upto`
+// of loop layer l (anchor, then each decoded difference, in fp32, in order).
+template <class AT>
+__device__ __forceinline__ void hcache_delta_sum(const HCacheParams& hp, const RowInfo& ri, int l, int upto, int e,
+                                                 int h, float& x0, float& x1) {
+  const int d = hp.H * hp.dh;
+  const AT* an = reinterpret_cast<const AT*>(hcache_row(hp, ri, hp.n_bound + l));
+  x0 = (float)an[e];
+  x1 = (float)an[e + 1];
+  for (int i = 2; i <= upto; ++i) {
+    const uint8_t* row = hcache_row(hp, ri, hp.n_bound + (i - 1) * hp.n_loop + l);
+    const float sc = (float)*reinterpret_cast<const f16*>(row + d + 2 * h);
+    x0 += (float)(int8_t)row[e] * sc;
+    x1 += (float)(int8_t)row[e + 1] * sc;
+  }
 }
 
 template <class AT>
@@ -248,36 +284,37 @@ __global__ __launch_bounds__(64) void hcache_write_kernel(const AT* __restrict__
   if (skip_done && ri.done) return;
   const int d = hp.H * hp.dh, e = h * hp.dh + 2 * i;
   const bool own = 2 * i < hp.dh;
-  uint8_t* row = hcache_row(hp, ri);
+  uint8_t* row = hcache_row(hp, ri, hp.slot);
   AT a0{}, a1{};
   if (own) {
     a0 = x[(int64_t)r * d + e];
     a1 = x[(int64_t)r * d + e + 1];
   }
-  if (hp.mode == 1) {
+  const bool plain = hp.mode == 1 || (hp.mode == 4 && hp.slot < hp.n_bound + hp.n_loop);
+  if (plain) {
     if (own) {
       reinterpret_cast<AT*>(row)[e] = a0;
       reinterpret_cast<AT*>(row)[e + 1] = a1;
     }
     return;
   }
-  const float v0 = (float)a0, v1 = (float)a1;
-  const float levels = hp.mode == 2 ? 127.f : 7.f;
-  const float am = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
-  const f16 s16 = (f16)(am / levels);
-  const float sc = (float)s16;
-  int q0 = 0, q1 = 0;
-  if (sc > 0.f) {
-    q0 = (int)fminf(fmaxf(rintf(v0 / sc), -levels), levels);
-    q1 = (int)fminf(fmaxf(rintf(v1 / sc), -levels), levels);
+  float v0 = (float)a0, v1 = (float)a1;
+  if (hp.mode == 4) {   // code the difference to the previous iteration's reconstruction
+    const int t = hp.slot - hp.n_bound, l = t % hp.n_loop, j = t / hp.n_loop + 1;
+    float p0 = 0.f, p1 = 0.f;
+    if (own) hcache_delta_sum<AT>(hp, ri, l, j - 1, e, h, p0, p1);
+    v0 -= p0;
+    v1 -= p1;
   }
-  const int cb = hp.mode == 2 ? d : d / 2;
+  int q0, q1;
+  const f16 s16 = hcache_codes(v0, v1, hp.mode == 3 ? 7.f : 127.f, q0, q1);
+  const int cb = hp.mode == 3 ? d / 2 : d;
   if (own) {
-    if (hp.mode == 2) {
+    if (hp.mode == 3) {
+      row[e / 2] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
+    } else {
       row[e] = (uint8_t)(int8_t)q0;
       row[e + 1] = (uint8_t)(int8_t)q1;
-    } else {
-      row[e / 2] = (uint8_t)((q0 & 0xF) | ((q1 & 0xF) << 4));
     }
   }
   if (i == 0) *reinterpret_cast<f16*>(row + cb + 2 * h) = s16;
@@ -290,11 +327,19 @@ __global__ __launch_bounds__(64) void hcache_read_kernel(HCacheParams hp, const 
   if (2 * i >= hp.dh) return;
   const RowInfo ri = rows[r];
   const int d = hp.H * hp.dh, e = h * hp.dh + 2 * i;
-  const uint8_t* row = hcache_row(hp, ri);
+  const uint8_t* row = hcache_row(hp, ri, hp.slot);
   AT* o = out + (int64_t)r * d + e;
-  if (hp.mode == 1) {
+  if (hp.mode == 1 || (hp.mode == 4 && hp.slot < hp.n_bound + hp.n_loop)) {
     o[0] = reinterpret_cast<const AT*>(row)[e];
     o[1] = reinterpret_cast<const AT*>(row)[e + 1];
+    return;
+  }
+  if (hp.mode == 4) {
+    const int t = hp.slot - hp.n_bound;
+    float x0, x1;
+    hcache_delta_sum<AT>(hp, ri, t % hp.n_loop, t / hp.n_loop + 1, e, h, x0, x1);
+    o[0] = from_f32<AT>(x0);
+    o[1] = from_f32<AT>(x1);
     return;
   }
   int q0, q1, cb;

@@ -1,6 +1,7 @@
-"""Store-h cache modes on the device against the oracle (iteration-axis KV
-compression: "CLI Reference" page, environment variables TINYLOOP_KV_H_MODE with
-TINYLOOP_KV_INT8 / TINYLOOP_KV_INT4).
+"""Store-h cache modes and delta-KV on the device against the oracle
+(iteration-axis KV compression: "CLI Reference" page, environment variables
+TINYLOOP_KV_H_MODE with TINYLOOP_KV_INT8 / TINYLOOP_KV_INT4; "Benchmark
+Comparison" page, measured benchmarks, section 9, delta-KV).
 
 A lane's slot keeps the block's pre-QKV norm output x (operand type, int8 or
 packed int4 codes with one fp16 scale per position and head); each attention
@@ -37,7 +38,7 @@ SPECS = {
     "tiny-w4": synth.ModelSpec("tiny-w4", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "w4g128"),
     "tiny-bf16-stack": synth.ModelSpec("tiny-bf16-stack", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16"),
 }
-MODES = {"h": tl.TL_KV_H, "h8": tl.TL_KV_H8, "h4": tl.TL_KV_H4}
+MODES = {"h": tl.TL_KV_H, "h8": tl.TL_KV_H8, "h4": tl.TL_KV_H4, "d8": tl.TL_KV_D8}
 
 
 def say(*a):
@@ -49,7 +50,7 @@ CODED_BARS = {"f32": (1e-2, 1e-2), "f16": (1e-2, 5e-2), "bf16": (3e-2, 0.15)}   
 
 
 def bar(spec, mode, L):
-    if mode in ("h8", "h4"):
+    if mode in ("h8", "h4", "d8"):    # d8 codes differences with int8 steps: the int8 bars
         return CODED_BARS[spec.act_dtype][mode == "h4"]
     if spec.act_dtype == "f32":
         return 1e-4
@@ -127,17 +128,18 @@ def test_store_h_prefill_append_decode(name, mode):
         tl.tl_free(model)
 
 
-def test_store_h_fork_append_int8():
+@pytest.mark.parametrize("mode", ["h8", "d8"])
+def test_store_h_fork_append_coded(mode):
     spec = SPECS["tiny-bf16-stack"]
     w = synth.make_weights(spec, 83)
-    m = _oracle_model(w, "h8")
+    m = _oracle_model(w, mode)
     prefix = synth.tokens(83, 9300, 15, spec.vocab)
     suffix = synth.tokens(83, 9301, 6, spec.vocab)
     src = oracle.prefill(m, prefix, 4)[0]
     child = oracle.fork(src, 11)
     h_o, lg_o = oracle.append(m, child, suffix, 4)
     model = load_model(w, max_lanes=4, max_pos=64, max_L=8, kv_arena_bytes=kv_bytes(spec, [4] * 2, [40] * 2),
-                       kv_mode=tl.TL_KV_H8)
+                       kv_mode=MODES[mode])
     try:
         tl.tl_forward(model, np.array([0, 15], np.int32), _dev(prefix), L=4, lanes=[1], max_new_tokens=10)
         tl.tl_lane_fork(model, 1, 3, 11, max_new_tokens=20)
