@@ -192,7 +192,7 @@ def main():
 def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
     """32 lanes, 32-token prompts, greedy cached decode at L = 8 on the FP16-body model;
     the same run with the device-side early-exit rule at three settings."""
-    ds = torch.cuda.Stream()   # repeated decode steps on a stream replay captured graphs
+    ds = torch.cuda.Stream()
     spec = synth.SPECS[3]
     log("decode: FP16-body model")
     w = synth.make_weights(spec, 0)
@@ -245,7 +245,7 @@ def prefix_bench(tl, torch, np, synth, kv_bytes, load_model):
     batched pass); SHARED prefills the prefix once, forks it into every request's
     lane and appends the suffixes (one batched pass).  Wall time of the whole job,
     best of two runs."""
-    ds = torch.cuda.Stream()   # repeated decode steps on a stream replay captured graphs
+    ds = torch.cuda.Stream()
     spec = synth.SPECS[2]
     log("shared prefix: INT4 model")
     w = synth.make_weights(spec, 0)
@@ -312,7 +312,7 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
     5-token verify pass at L = 8, one plain step at L = 8; with a drafts accepted
     per round a round yields a + 1 tokens, which gives the acceptance at which
     speculation breaks even."""
-    ds = torch.cuda.Stream()   # repeated decode steps on a stream replay captured graphs
+    ds = torch.cuda.Stream()
     spec = synth.SPECS[2]
     log("speculative: INT4 model, batch 1")
     w = synth.make_weights(spec, 0)
@@ -393,23 +393,30 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
 
 
 def store_h_bench(tl, torch, np, synth, kv_bytes, load_model):
-    """Cache modes at batch 1 on the FP16-body model: 512-token prompt, 64 greedy
-    tokens at L = 8 (the first from the prompt pass, 63 cached steps); decode time
-    and the cache bytes one position takes in one slot."""
-    ds = torch.cuda.Stream()   # repeated decode steps on a stream replay captured graphs
+    """Cache modes at batch 1 on the FP16-body model: 512-token prompt, 64 tokens at
+    L = 8 (the first from the prompt pass, 63 cached steps fed the same seeded
+    tokens in every mode); decode time, the cache bytes one position takes in one
+    slot, and how far the last step's hidden state lies from the K/V mode's."""
     spec = synth.SPECS[3]
     log("store-h: FP16-body model, batch 1")
+    ds = torch.cuda.Stream()
     w = synth.make_weights(spec, 0)
     plen, new, L = 512, 64, 8
     d, H = spec.d_model, spec.n_heads
     prompt = torch.tensor(synth.tokens(0, synth.STREAM_PROMPT_TOKENS, plen, spec.vocab), dtype=torch.int32,
                           device="cuda")
+    feed = torch.tensor(synth.tokens(0, synth.STREAM_PROMPT_TOKENS + 2, new, spec.vocab), dtype=torch.int32,
+                        device="cuda")
     cu = np.array([0, plen], np.int32)
     out1 = torch.empty(1, dtype=torch.int32, device="cuda")
-    res = {"config": "FP16-body model (2048-wide), batch 1, 512-token prompt, 63 cached greedy steps at L=8"}
+    hid = torch.empty(1, d, dtype=torch.float32, device="cuda")
+    res = {"config": "FP16-body model (2048-wide), batch 1, 512-token prompt, 63 cached steps at L=8 on the same "
+                     "seeded tokens; hidden_rel_vs_kv: relative L2 distance of the last step's hidden state from "
+                     "the K/V mode's"}
     # bytes of one position in one loop slot (delta: a slot past the first iteration; the
     # first iteration's anchor slot takes d * 2)
     per_pos = {"kv": 2 * d * 2, "h": d * 2, "h8": d + 2 * H, "h4": d // 2 + 2 * H, "d8": d + 2 * H}
+    ref = None
     for name, mode in (("kv", tl.TL_KV_KV), ("h", tl.TL_KV_H), ("h8", tl.TL_KV_H8), ("h4", tl.TL_KV_H4),
                        ("d8", tl.TL_KV_D8)):
         model = load_model(w, max_lanes=1, max_pos=plen + new, max_L=L,
@@ -419,14 +426,18 @@ def store_h_bench(tl, torch, np, synth, kv_bytes, load_model):
             tl.tl_forward(model, cu, prompt, L=L, lanes=[0], max_new_tokens=new, stream=ds)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
-            for _ in range(new - 1):
-                tl.tl_decode_step(model, [0], [L], out1, stream=ds)
+            for t in range(new - 1):
+                tl.tl_decode_step(model, [0], [L], out1, in_tokens=feed[t:t + 1], out_hidden=hid, stream=ds)
             torch.cuda.synchronize()
             el = time.perf_counter() - t0
             best = el if best is None else min(best, el)
         tl.tl_free(model)
+        last = hid.cpu().numpy()[0].astype(np.float64)
+        if ref is None:
+            ref = last
         res[name] = {"decode_ms": round(best * 1e3, 2), "tok_per_s": round((new - 1) / best, 1),
-                     "bytes_per_position_per_slot": per_pos[name]}
+                     "bytes_per_position_per_slot": per_pos[name],
+                     "hidden_rel_vs_kv": float("%.3g" % (np.linalg.norm(last - ref) / np.linalg.norm(ref)))}
         log("store-h %s: %s" % (name, res[name]))
     return res
 

@@ -3,7 +3,6 @@
 #include "engine.h"
 
 #include <algorithm>
-#include <functional>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -157,68 +156,6 @@ tl_status graph_keep(tl_model* m, tl::GraphEntry& ge, hipStream_t s) {
   }
   m->graphs.push_back(ge);
   return TL_OK;
-}
-
-// Descriptors of a call into a given device buffer (a captured pass's own copy),
-// through the pinned staging area, ordered on the stream.
-tl_status stage_to(tl_model* m, const Stage& st, void* dst, hipStream_t s) {
-  if (st.buf.size() > m->stage_bytes || !m->stage_host) {
-    Stage grow;
-    grow.buf.resize(st.buf.size());
-    TRY(stage_upload(m, grow, s));   // sizes the pinned area
-  }
-  HIPCHK(hipEventSynchronize(m->stage_done));
-  std::memcpy(m->stage_host, st.buf.data(), st.buf.size());
-  HIPCHK(hipMemcpyAsync(dst, m->stage_host, st.buf.size(), hipMemcpyHostToDevice, s));
-  HIPCHK(hipEventRecord(m->stage_done, s));
-  m->last_stream = s;
-  return TL_OK;
-}
-
-// Run a repeated pass as a HIP graph: replay the one stored under key after
-// copying this call's descriptors into its buffer, or capture body (the call's
-// device work, which finds its descriptors through staged()) into a new one.
-// The pass's launch shapes must follow from the key; descriptor contents may vary.
-tl_status graph_run(tl_model* m, const std::vector<int64_t>& key, const Stage& st, hipStream_t s,
-                    const std::function<tl_status()>& body) {
-  for (auto& g : m->graphs)
-    if (g.key == key) {
-      TRY(stage_to(m, st, g.stage, s));
-      g.last_use = ++m->graph_clock;
-      HIPCHK(hipGraphLaunch(g.exec, s));
-      return TL_OK;
-    }
-  tl::GraphEntry ge;
-  ge.stage = dev_alloc(m, std::max<size_t>(st.buf.size(), 256));
-  if (!ge.stage) return fail(TL_E_OOM, "graph descriptors");
-  tl_status stt = stage_to(m, st, ge.stage, s);
-  if (stt != TL_OK) {
-    dev_free(m, ge.stage);
-    return stt;
-  }
-  m->stage_override = ge.stage;
-  hipError_t e1 = hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal);
-  if (e1 != hipSuccess) {
-    m->stage_override = nullptr;
-    dev_free(m, ge.stage);
-    return fail(TL_E_HIP, "stream capture: %s", hipGetErrorString(e1));
-  }
-  stt = body();
-  m->stage_override = nullptr;
-  hipGraph_t graph = nullptr;
-  const hipError_t e2 = hipStreamEndCapture(s, &graph);
-  hipError_t e3 = hipSuccess;
-  if (stt == TL_OK && e2 == hipSuccess) e3 = hipGraphInstantiate(&ge.exec, graph, nullptr, nullptr, 0);
-  if (graph) (void)hipGraphDestroy(graph);
-  if (stt != TL_OK || e2 != hipSuccess || e3 != hipSuccess) {
-    if (ge.exec) (void)hipGraphExecDestroy(ge.exec);
-    dev_free(m, ge.stage);
-    if (stt != TL_OK) return stt;
-    return fail(TL_E_HIP, "graph capture: %s", hipGetErrorString(e2 != hipSuccess ? e2 : e3));
-  }
-  HIPCHK(hipGraphLaunch(ge.exec, s));
-  ge.key = key;
-  return graph_keep(m, ge, s);
 }
 
 // ----------------------------------------------------------------- workspace
@@ -1644,39 +1581,24 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
   }
   Stage st;
   const size_t o_rows = st.add(rows), o_lanes = st.add(lane_ids);
-  const std::vector<int> n_act = active_counts(eff);
-  // the device work of the step; descriptors are read through staged()
-  auto body = [&]() -> tl_status {
-    const int32_t* lanes_dev = staged<int32_t>(m, o_lanes);
-    const int32_t* toks = in_tokens;
-    if (!toks) {
-      HIPCHK(launch_gather_i32(m->d_pending, lanes_dev, n, m->ws.tok, s));
-      toks = m->ws.tok;
-    }
-    Pass p;
-    p.n = n;
-    p.tokens = toks;
-    p.rows0 = staged<RowInfo>(m, o_rows);
-    p.rows_host = &rows;
-    p.n_active = n_act;
-    p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
-    p.final_h = out_hidden ? out_hidden : m->ws.hX;
-    p.log = out_log;
-    TRY(run_pass(m, p, s));
-    return run_head(m, p.final_h, nullptr, n, out_logits, out_tokens, lanes_dev, s);
-  };
-  // a step on a stream is replayed from a captured graph when its shape repeats
-  // (row count, active rows per iteration, buffers): positions and lanes only
-  // change the descriptors, which are copied into the graph's buffer each step
-  if (s != nullptr && !m->timing && !out_log && m->kv_mode == TL_KV_KV) {
-    std::vector<int64_t> key = {-2, n, (int64_t)(intptr_t)in_tokens, (int64_t)(intptr_t)out_tokens,
-                                (int64_t)(intptr_t)out_logits, (int64_t)(intptr_t)out_hidden, (int64_t)(intptr_t)s};
-    key.insert(key.end(), n_act.begin(), n_act.end());
-    TRY(graph_run(m, key, st, s, body));
-  } else {
-    TRY(stage_upload(m, st, s));
-    TRY(body());
+  TRY(stage_upload(m, st, s));
+  const int32_t* lanes_dev = staged<int32_t>(m, o_lanes);
+  const int32_t* toks = in_tokens;
+  if (!toks) {
+    HIPCHK(launch_gather_i32(m->d_pending, lanes_dev, n, m->ws.tok, s));
+    toks = m->ws.tok;
   }
+  Pass p;
+  p.n = n;
+  p.tokens = toks;
+  p.rows0 = staged<RowInfo>(m, o_rows);
+  p.rows_host = &rows;
+  p.n_active = active_counts(eff);
+  p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
+  p.final_h = out_hidden ? out_hidden : m->ws.hX;
+  p.log = out_log;
+  TRY(run_pass(m, p, s));
+  TRY(run_head(m, p.final_h, nullptr, n, out_logits, out_tokens, lanes_dev, s));
   for (int i = 0; i < n; ++i) {
     Lane& ln = m->lanes[lanes[i]];
     ln.len += 1;

@@ -192,54 +192,6 @@ def test_cfg2_forward_full_size():
 
 
 @pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack"])
-def test_decode_graph_replay_matches_eager(name):
-    """Decode steps on a stream replay a captured graph with new positions, lanes
-    and tokens each step; every step equals the same step run eagerly on twin
-    lanes (bitwise), also across a change of the depth profile (a second graph)
-    and back, with eager work and synchronisations between the steps."""
-    spec = TINY[name]
-    w = synth.make_weights(spec, seed=23)
-    plens = [9, 30, 4]
-    prompts = [synth.tokens(23, 6100 + i, n, spec.vocab) for i, n in enumerate(plens)]
-    model = load_model(w, max_lanes=8, max_pos=96, max_L=8,
-                       kv_arena_bytes=kv_bytes(spec, [6] * 6, [60] * 6))
-    try:
-        cu = np.cumsum([0] + plens).astype(np.int32)
-        toks = torch.tensor(np.concatenate(prompts), dtype=torch.int32, device="cuda")
-        eager_lanes, graph_lanes = [0, 1, 2], [5, 3, 7]
-        for lanes in (eager_lanes, graph_lanes):
-            tl.tl_forward(model, cu, toks, L=6, lanes=lanes, max_new_tokens=30, stream=0)
-        torch.cuda.synchronize()
-        side = torch.cuda.Stream()
-        out_e = torch.empty(3, dtype=torch.int32, device="cuda")
-        out_g = torch.empty(3, dtype=torch.int32, device="cuda")
-        hid_e = torch.empty(3, spec.d_model, dtype=torch.float32, device="cuda")
-        hid_g = torch.empty(3, spec.d_model, dtype=torch.float32, device="cuda")
-        feed = synth.tokens(23, 6200, 3 * 12, spec.vocab).reshape(12, 3)
-        depths = [[6, 6, 6]] * 4 + [[6, 4, 6]] * 4 + [[6, 4, 6], [3, 4, 2], [3, 4, 2], [3, 4, 2]]
-        fe_buf = torch.empty(3, dtype=torch.int32, device="cuda")   # one buffer: the graph key holds its address
-        for t in range(12):
-            # teacher-forced steps alternate with free-running ones (pending tokens)
-            fe = None
-            if t % 3:
-                fe_buf.copy_(torch.tensor(feed[t], dtype=torch.int32))
-                fe = fe_buf
-            hid_g.fill_(float("nan"))
-            out_g.fill_(-1)
-            torch.cuda.synchronize()
-            e1 = tl.tl_decode_step(model, eager_lanes, depths[t], out_e, in_tokens=fe, out_hidden=hid_e, stream=0)
-            torch.cuda.synchronize()
-            e2 = tl.tl_decode_step(model, graph_lanes, depths[t], out_g, in_tokens=fe, out_hidden=hid_g,
-                                   stream=side)
-            side.synchronize()
-            assert np.array_equal(e1, e2), t
-            assert torch.equal(out_g, out_e), t
-            assert torch.equal(hid_g, hid_e), t
-    finally:
-        tl.tl_free(model)
-
-
-@pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack"])
 def test_graph_replay_matches_eager(name):
     """Repeated scoring calls on a stream replay a captured graph; every replay,
     with eager work and synchronisations between them, equals the eager pass."""
