@@ -144,6 +144,47 @@ def test_speculate_matches_oracle(name, monkeypatch):
         tl.tl_free(model)
 
 
+@pytest.mark.parametrize("mode", ["h8", "d8"])
+def test_speculate_in_coded_cache_modes(mode, monkeypatch):
+    """Rollbacks in a coded cache mode (the delta chain included): the fp32 model's
+    tokens and per-round acceptance equal the oracle's in the same mode.  A code
+    can move by one step between the two (x differs by fp32 rounding), so the
+    greedy gaps must exceed 1e-2 of the logits' scale."""
+    import copy
+    spec, (Ld, Lv, k), n, n_tok, _ = CASES["tiny-fp32"]
+    modes = {"h8": tl.TL_KV_H8, "d8": tl.TL_KV_D8}
+    w = synth.make_weights(spec, 71)
+    m = copy.copy(oracle.OracleModel.from_weights(w))
+    m.kv_mode = mode
+    chosen = None
+    for seed in range(60):
+        prompts = [synth.tokens(71, 8000 + 100 * seed + i, 6 + 3 * i, spec.vocab) for i in range(n)]
+        lanes, res, plain, gap = _oracle_case(m, spec, prompts, Ld, Lv, k, n_tok, monkeypatch)
+        accs = [a for _, acc in res for a in acc]
+        if gap > 1e-2 and max(accs) == k and any(_rejects(acc, k, n_tok) for _, acc in res):
+            chosen = (seed, prompts, res)
+            break
+    assert chosen is not None, "no seed with well-separated greedy choices"
+    seed, prompts, res = chosen
+    cap = max(len(p) for p in prompts) + n_tok + k + 4
+    model = load_model(w, max_lanes=8, max_pos=64, max_L=16, kv_arena_bytes=kv_bytes(spec, [L_PRE] * n, [cap] * n),
+                       kv_mode=modes[mode])
+    try:
+        cu = np.concatenate([[0], np.cumsum([len(p) for p in prompts])]).astype(np.int32)
+        tl.tl_forward(model, cu, _dev(np.concatenate(prompts)), L=L_PRE, lanes=list(range(n)),
+                      max_new_tokens=cap - max(len(p) for p in prompts))
+        out = torch.empty(n, n_tok, dtype=torch.int32, device="cuda")
+        acc = tl.tl_speculate(model, list(range(n)), Ld, Lv, k, n_tok, out)
+        torch.cuda.synchronize()
+        got = out.cpu().numpy()
+        for i in range(n):
+            say(mode, "seed", seed, "lane", i, "accepted per round", [int(a) for a in acc[i] if a >= 0])
+            assert got[i].tolist() == res[i][0]
+            assert [int(a) for a in acc[i] if a >= 0] == res[i][1]
+    finally:
+        tl.tl_free(model)
+
+
 def test_speculate_errors():
     spec = CASES["tiny-w4"][0]
     w = synth.make_weights(spec, 73)

@@ -181,3 +181,36 @@ def test_store_h_lanes_take_less_of_the_arena():
                 assert ei.value.status == tl.TL_E_STATE
         finally:
             tl.tl_free(model)
+
+
+@pytest.mark.parametrize("mode", ["h8", "d8"])
+@pytest.mark.parametrize("rule", [dict(patience=1, min_L=2, tau=1e30), dict(patience=2, min_L=3, peek_every=2, tau=1e30)])
+def test_store_h_early_exit(mode, rule):
+    """Early exit in a coded cache mode: tokens that finish write no later slots,
+    the others keep building their chain; depths equal the oracle's."""
+    spec = SPECS["tiny-bf16-stack"]
+    w = synth.make_weights(spec, 87)
+    m = _oracle_model(w, mode)
+    prompts = [synth.tokens(87, 9500 + i, 7 + 2 * i, spec.vocab) for i in range(3)]
+    feed = synth.tokens(87, 9600, 9, spec.vocab).reshape(3, 3)
+    reqs = np.array([[6, 4, 8], [5, 6, 3], [8, 8, 2]], np.int32)
+    ee = oracle.EarlyExit(rule["patience"], rule["min_L"], rule["tau"], rule.get("peek_every", 1), 0.0)
+    o_lanes = [oracle.prefill(m, p, 8)[0] for p in prompts]
+    lanes = [1, 4, 2]
+    model = load_model(w, max_lanes=6, max_pos=64, max_L=8, kv_arena_bytes=kv_bytes(spec, [8] * 3, [40] * 3),
+                       kv_mode=MODES[mode])
+    try:
+        cu = np.concatenate([[0], np.cumsum([len(p) for p in prompts])]).astype(np.int32)
+        tl.tl_forward(model, cu, _dev(np.concatenate(prompts)), L=8, lanes=lanes, max_new_tokens=20)
+        out = torch.empty(3, dtype=torch.int32, device="cuda")
+        hs = torch.empty(3, spec.d_model, dtype=torch.float32, device="cuda")
+        for t in range(3):
+            e = tl.tl_decode_step_ee(model, lanes, reqs[t], out, in_tokens=_dev(feed[t]), out_hidden=hs, **rule)
+            torch.cuda.synchronize()
+            H = hs.cpu().numpy()
+            for i in range(3):
+                h_o, _, _, L_o = oracle.decode_step_ee(m, o_lanes[i], int(reqs[t, i]), ee, token=int(feed[t, i]))
+                assert e[i] == L_o, (t, i, e[i], L_o)
+                assert rel_l2(H[i], h_o) <= bar(spec, mode, L_o), (t, i, rel_l2(H[i], h_o))
+    finally:
+        tl.tl_free(model)
