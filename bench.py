@@ -39,6 +39,8 @@ def parse():
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative measurement")
     ap.add_argument("--no-store-h", action="store_true", help="skip the store-h cache-mode measurement")
     ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
+    ap.add_argument("--profile-decode", action="store_true",
+                    help="run batch-1 INT4 decode steps only (32-token prompt, 63 steps at L=8; for rocprofv3)")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one (no graph replay)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the steps, copy 256 MiB once with a plain device copy (counter calibration)")
@@ -105,6 +107,9 @@ def main():
     from tests.harness import ensure_built, kv_bytes, load_model
 
     ensure_built()
+    if args.profile_decode:
+        profile_decode(tl, torch, np, synth, kv_bytes, load_model)
+        return
     spec = synth.SPECS[2]
     log("generating weights")
     w = synth.make_weights(spec, 0)
@@ -187,6 +192,23 @@ def main():
         log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
     print(json.dumps(out), flush=True)
+
+
+def profile_decode(tl, torch, np, synth, kv_bytes, load_model):
+    """Batch-1 greedy decode on the INT4 model (32-token prompt, 63 steps at L = 8),
+    nothing else: the workload of the batch-1 kernel statistics."""
+    spec = synth.SPECS[2]
+    w = synth.make_weights(spec, 0)
+    model = load_model(w, max_lanes=1, max_pos=128, max_L=8, kv_arena_bytes=kv_bytes(spec, [8], [128]))
+    prompt = torch.tensor(synth.tokens(0, synth.STREAM_PROMPT_TOKENS, 32, spec.vocab), dtype=torch.int32,
+                          device="cuda")
+    out = torch.empty(1, dtype=torch.int32, device="cuda")
+    tl.tl_forward(model, np.array([0, 32], np.int32), prompt, L=8, lanes=[0], max_new_tokens=64)
+    for _ in range(63):
+        tl.tl_decode_step(model, [0], [8], out)
+    torch.cuda.synchronize()
+    log("decoded 63 tokens")
+    tl.tl_free(model)
 
 
 def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
