@@ -255,7 +255,7 @@ tl_status tend(tl_model* m, int cls, hipStream_t s) {
   } while (0)
 
 // ----------------------------------------------------------------- passes
-// With norm_h set (only on the few-row INT4 path, see small_w4) the product's
+// With norm_h set (only on the few-row GEMV path, see small_gemv) the product's
 // input is RMSNorm(norm_h) * norm_g, formed inside the GEMV; x_out receives it.
 tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, hipStream_t s,
                const float* norm_h = nullptr, const float* norm_g = nullptr, void* x_out = nullptr) {
@@ -275,8 +275,8 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
   g.partial_cap = kSplitFloats;
   g.live = m->gate_live;
   e.pair_g = m->G;
-  if (gemv_w4_applies(g, e.kind)) {   // a few rows of an INT4 product: no split-K pass
-    HIPCHK(launch_gemv_w4(g, e, s));
+  if (m->act == DT_F16 && gemv_applies(g, e.kind)) {   // a few rows: no split-K pass
+    HIPCHK(launch_gemv(g, e, s));
     if (e.kind == EPI_RESID && e.norm_g)
       HIPCHK(launch_rmsnorm(m->act, e.h, e.norm_g, nullptr, M, g.N, e.norm_eps, e.norm_out, s));
     return TL_OK;
@@ -286,9 +286,10 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
   return TL_OK;
 }
 
-// A block whose four products all take the few-row INT4 GEMV (INT4 loop block,
-// n <= 4 rows): its RMSNorms are formed inside the QKV and gate/up GEMVs.
-bool small_w4(const tl_model* m, const tl::BlockDev& B, int n) {
+// A block whose four products all take the few-row GEMV (fp16 operands, n <= 4
+// rows, INT4 or dense weights): its RMSNorms are formed inside the QKV and
+// gate/up GEMVs.
+bool small_gemv(const tl_model* m, const tl::BlockDev& B, int n) {
   if (m->act != DT_F16) return false;
   for (const MatDev* W : {&B.qkv, &B.o, &B.gu, &B.down}) {
     GemmArgs g{};
@@ -297,7 +298,7 @@ bool small_w4(const tl_model* m, const tl::BlockDev& B, int n) {
     g.K = W->K;
     g.B = W->dense;
     g.Bw4 = W->dense ? nullptr : W->w4;
-    if (!gemv_w4_applies(g, EPI_RESID)) return false;
+    if (!gemv_applies(g, EPI_RESID)) return false;
   }
   return true;
 }
@@ -315,7 +316,7 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   const BlockDev& B = m->blocks[b];
   auto& w = m->ws;
   const int tb = B.kind == 1 ? TL_T_GEMM_QKV_LOOP : TL_T_GEMM_QKV_BOUNDARY;
-  const bool gv = small_w4(m, B, n);   // norms inside the GEMVs, none fused into the residual products
+  const bool gv = small_gemv(m, B, n);   // norms inside the GEMVs, none fused into the residual products
   const bool norm_in_qkv = gv && !x_ready;
   if (!x_ready && !gv)
     TIMED(TL_T_RMSNORM, HIPCHK(launch_rmsnorm(m->act, h, B.norm1, nullptr, n, c.d_model, c.rms_eps, w.x16, s)));

@@ -165,11 +165,11 @@ hipError_t launch_hcache_write(int dtype, const void* x, const RowInfo* rows, in
 // Read cached rows (lane, pos) back as operand-type x [n, d] (codes times scale).
 hipError_t launch_hcache_read(int dtype, const HCacheParams& hp, const RowInfo* rows, int n, void* out,
                               hipStream_t s);
-// INT4 GEMV for 1..4 rows (W4G128 weights, QKV / RESID / SWIGLU epilogues; a
-// RESID norm is not fused): no split of K, no partials.  gemv_w4_applies tells
-// whether a product takes this path.
-bool gemv_w4_applies(const GemmArgs& g, int kind);
-hipError_t launch_gemv_w4(const GemmArgs& g, const GemmEpi& e, hipStream_t s);
+// GEMV for 1..4 rows with fp16 operands (INT4 W4G128 or dense fp16 weights; QKV /
+// RESID / SWIGLU epilogues; a RESID norm is not fused): no split of K, no
+// partials.  gemv_applies tells whether a product takes this path.
+bool gemv_applies(const GemmArgs& g, int kind);
+hipError_t launch_gemv(const GemmArgs& g, const GemmEpi& e, hipStream_t s);
 hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s);
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s);
