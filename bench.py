@@ -41,6 +41,8 @@ def parse():
     ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
     ap.add_argument("--profile-decode", action="store_true",
                     help="run batch-1 INT4 decode steps only (32-token prompt, 63 steps at L=8; for rocprofv3)")
+    ap.add_argument("--profile-decode-fp16", action="store_true",
+                    help="run 32-lane FP16-body decode steps only (32-token prompts, 31 steps at L=8; for rocprofv3)")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one (no graph replay)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the steps, copy 256 MiB once with a plain device copy (counter calibration)")
@@ -109,6 +111,9 @@ def main():
     ensure_built()
     if args.profile_decode:
         profile_decode(tl, torch, np, synth, kv_bytes, load_model)
+        return
+    if args.profile_decode_fp16:
+        profile_decode_fp16(tl, torch, np, synth, kv_bytes, load_model)
         return
     spec = synth.SPECS[2]
     log("generating weights")
@@ -208,6 +213,25 @@ def profile_decode(tl, torch, np, synth, kv_bytes, load_model):
         tl.tl_decode_step(model, [0], [8], out)
     torch.cuda.synchronize()
     log("decoded 63 tokens")
+    tl.tl_free(model)
+
+
+def profile_decode_fp16(tl, torch, np, synth, kv_bytes, load_model):
+    """The decode workload of decode_bench without early exit: FP16-body model, 32
+    lanes, 32-token prompts, 31 greedy steps at L = 8."""
+    spec = synth.SPECS[3]
+    w = synth.make_weights(spec, 0)
+    n, plen, new = 32, 32, 32
+    model = load_model(w, max_lanes=n, max_pos=plen + new, kv_arena_bytes=kv_bytes(spec, [8] * n, [plen + new] * n))
+    toks = torch.tensor(synth.tokens(0, synth.STREAM_PROMPT_TOKENS, n * plen, spec.vocab), dtype=torch.int32,
+                        device="cuda")
+    cu = np.arange(0, n * plen + 1, plen, dtype=np.int32)
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    tl.tl_forward(model, cu, toks, L=8, lanes=list(range(n)), max_new_tokens=new)
+    for _ in range(new - 1):
+        tl.tl_decode_step(model, list(range(n)), [8] * n, out)
+    torch.cuda.synchronize()
+    log("decoded %d steps on %d lanes" % (new - 1, n))
     tl.tl_free(model)
 
 

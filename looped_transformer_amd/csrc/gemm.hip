@@ -714,7 +714,9 @@ constexpr int kCUs = 256;
 // for M <= 128 the kernels are bound by per-workgroup latency, so small tiles
 // (BM 32/64 x BN 64, BK 128, two-stage ring) and a split of K that brings the
 // workgroup count to roughly 320 work best; larger M uses 128 x 128 tiles and
-// splits K only when the tiles cannot cover the 256 CUs.
+// splits K only when the tiles cannot cover the 256 CUs.  Dense weights at
+// <= 32 rows that get no split (gate/up: 176 tiles of 16 stages) keep three
+// stages in flight instead of one: 17.5 -> 12.3 us with the weights in HBM.
 TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
   if (act_dtype == DT_F32) return {64, 64, 1, g.K, 16, 2};
   TileCfg t{};
@@ -742,6 +744,7 @@ TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
       t.splits = (int)((units + per - 1) / per);
     }
   }
+  if (!g.Bw4 && t.bm == 32 && t.bn == 64 && t.splits == 1) t.depth = 4;
   return t;
 }
 
@@ -802,6 +805,9 @@ template <class AT, bool W4>
 hipError_t launch_mfma(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool* norm_done) {
   const TileCfg t = pick_tile(DT_F16, g, e.kind);
   if (t.bn == 64) {
+    if constexpr (!W4) {
+      if (t.bm == 32 && t.depth == 4) return launch_mfma_t<AT, W4, 32, 64, 128, 4>(g, e, t, s, norm_done);
+    }
     if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 64, 128, 2>(g, e, t, s, norm_done);
     return launch_mfma_t<AT, W4, 64, 64, 128, 2>(g, e, t, s, norm_done);
   }
