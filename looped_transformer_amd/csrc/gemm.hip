@@ -311,6 +311,85 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
         if (e.part_val2) e.part_val2[(int64_t)row * e.n_tiles + blockIdx.x] = b2;
       }
     }
+  } else if constexpr (KIND == EPI_QKV) {
+    // The QKV epilogue of epi_pair with its column arithmetic (section, head,
+    // rotary index: integer divisions) done once per column of this lane and its
+    // cache addressing once per row, instead of once per value.
+    constexpr int EJ = TN / 2;
+    const int d = e.d, dh = e.dh, G = e.pair_g, half = dh >> 1;
+    int sect[EJ], head[EJ], cdv[EJ], rn[EJ];
+#pragma unroll
+    for (int jp = 0; jp < EJ; ++jp) {
+      const int c = min(n0 + wn * WTN + 2 * jp * 16 + lc, N - 1);
+      sect[jp] = c / d;
+      const int cc = c - sect[jp] * d;
+      head[jp] = cc / dh;
+      cdv[jp] = cc - head[jp] * dh;
+      const int ci = cdv[jp] / G;
+      rn[jp] = (ci >> 1) * G + (cdv[jp] - ci * G);
+    }
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * WTM + i * 16 + lr + r;
+        if (row >= M) continue;
+        const RowInfo ri = e.rows[row];
+        if (e.skip_done && ri.done) continue;   // finished by early exit: its later cache slots stay unwritten
+        const int64_t cap = e.kv.lane_cap[ri.lane];
+        const int64_t hs = cap * e.kv.dh;                                  // one head of one slot
+        const int slot = e.kv.s0 + e.kv.s1 * ri.iter;
+        const int64_t kbase = e.kv.lane_off[ri.lane] + (int64_t)(slot * 2) * e.kv.H * hs + (int64_t)ri.pos * e.kv.dh;
+        const int64_t vbase = kbase + e.kv.H * hs;
+        AT* const kv = reinterpret_cast<AT*>(e.kv.base);
+#pragma unroll
+        for (int jp = 0; jp < EJ; ++jp) {
+          const int col = n0 + wn * WTN + 2 * jp * 16 + lc;
+          if (col >= N) continue;
+          const float v0 = acc[i][2 * jp][r], v1 = acc[i][2 * jp + 1][r];
+          if (sect[jp] == 2) {
+            AT* vp = kv + vbase + head[jp] * hs;
+            vp[cdv[jp]] = from_f32<AT>(v0);
+            vp[cdv[jp] + G] = from_f32<AT>(v1);
+            continue;
+          }
+          const float cs = e.rope_cos[(int64_t)ri.pos * half + rn[jp]];
+          const float sn = e.rope_sin[(int64_t)ri.pos * half + rn[jp]];
+          const float x1 = v0 * cs - v1 * sn;
+          const float x2 = v1 * cs + v0 * sn;
+          AT* dst = (sect[jp] == 0) ? reinterpret_cast<AT*>(e.q_out) + (int64_t)row * d + head[jp] * dh
+                                    : kv + kbase + head[jp] * hs;
+          dst[rn[jp]] = from_f32<AT>(x1);
+          dst[rn[jp] + half] = from_f32<AT>(x2);
+        }
+      }
+  } else if constexpr (KIND == EPI_SWIGLU) {
+    // epi_pair's SwiGLU with the output column (a division) worked out once per
+    // column of this lane
+    constexpr int EJ = TN / 2;
+    const int G = e.pair_g;
+    int un[EJ];
+#pragma unroll
+    for (int jp = 0; jp < EJ; ++jp) {
+      const int c = min(n0 + wn * WTN + 2 * jp * 16 + lc, N - 1);
+      const int ci = c / G;
+      un[jp] = (ci >> 1) * G + (c - ci * G);
+    }
+    AT* const u = reinterpret_cast<AT*>(e.u_out);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * WTM + i * 16 + lr + r;
+        if (row >= M) continue;
+#pragma unroll
+        for (int jp = 0; jp < EJ; ++jp) {
+          if (n0 + wn * WTN + 2 * jp * 16 + lc >= N) continue;
+          const float v0 = acc[i][2 * jp][r], v1 = acc[i][2 * jp + 1][r];
+          const float sg = v0 / (1.0f + expf(-v0));
+          u[(int64_t)row * e.F + un[jp]] = from_f32<AT>(sg * v1);
+        }
+      }
   } else {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
