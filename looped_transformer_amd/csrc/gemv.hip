@@ -30,7 +30,57 @@ template <int M, int NW>
 __device__ __forceinline__ void gemv_stage_x(const GemmArgs& g, f16* xs) {
   __shared__ float ssw[NW][M];
   const int K = g.K, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  if (g.norm_h) {
+  constexpr int CH = 4;   // residual chunks per thread and row kept in registers
+  if (g.norm_h && K <= CH * NW * 256) {
+    // x = RMSNorm(h) * gain from the fp32 residual: the rows and gains are read
+    // once into registers, the mean of squares is summed per row (per thread in
+    // k order, then a fixed-order workgroup sum), then the rows are normalised
+    floatx4 hv[M][CH], gv[CH];
+#pragma unroll
+    for (int ch = 0; ch < CH; ++ch) {
+      const int c = tid * 4 + ch * NW * 256;
+      if (c < K) {
+        gv[ch] = *reinterpret_cast<const floatx4*>(g.norm_g + c);
+#pragma unroll
+        for (int m = 0; m < M; ++m)
+          hv[m][ch] = *reinterpret_cast<const floatx4*>(g.norm_h + (int64_t)min(m, g.M - 1) * K + c);
+      }
+    }
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float a = 0.f;
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) {
+        if (tid * 4 + ch * NW * 256 < K) {
+          const floatx4 v = hv[m][ch];
+          a = fmaf(v[0], v[0], fmaf(v[1], v[1], fmaf(v[2], v[2], fmaf(v[3], v[3], a))));
+        }
+      }
+      const float sm = wave_sum(a);
+      if (lane == 0) ssw[wave][m] = sm;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int m = 0; m < M; ++m) {
+      float t = 0.f;
+#pragma unroll
+      for (int w = 0; w < NW; ++w) t += ssw[w][m];
+      const float inv = 1.0f / sqrtf(t / (float)K + g.norm_eps);
+      f16* xo = (g.x_out && blockIdx.x == 0 && m < g.M) ? reinterpret_cast<f16*>(g.x_out) + (int64_t)m * K : nullptr;
+#pragma unroll
+      for (int ch = 0; ch < CH; ++ch) {
+        const int c = tid * 4 + ch * NW * 256;
+        if (c < K) {
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const f16 x = (f16)(hv[m][ch][q] * inv * gv[ch][q]);
+            xs[m * K + c + q] = x;
+            if (xo) xo[c + q] = x;
+          }
+        }
+      }
+    }
+  } else if (g.norm_h) {
     // x = RMSNorm(h) * gain, formed here from the fp32 residual: mean of squares
     // per row (fixed-order workgroup sum), then the rows in the operand type
     float ss[M];
