@@ -184,6 +184,12 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __
   constexpr int CH = KB * DH / 8;   // 16-byte chunks of one K (or V) block
   constexpr int CPT = CH / NT;      // per thread
   static_assert(CH % NT == 0, "block split");
+  // V goes to LDS transposed (Vt[dim][key]): thread t < VP loads 8 consecutive keys
+  // of one 8-wide dim chunk and writes each dim as one 16-byte row piece; the
+  // 8-key slot of row r is XOR-ed with (r / 16) mod 8, so that the 16 lanes of a
+  // write phase (dim chunks 0..15) hit distinct banks, and PV's reads undo it.
+  constexpr int VP = (KB / 8) * (DH / 8);
+  static_assert(VP <= NT && KB / 8 == 8, "V staging");
   typedef typename QkMfma<T>::frag qfrag;
   __shared__ __attribute__((aligned(16))) T Ks[KB * LDK];
   __shared__ __attribute__((aligned(16))) f16 Vt[DH * LDV];
@@ -201,14 +207,21 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __
 
   // K/V block k0 -> registers; positions past the end are clamped to the last
   // valid one (their scores are masked, so P = 0 multiplies finite values)
-  u32x4 rk[CPT], rv[CPT];
+  u32x4 rk[CPT], rv[8];
+  const int vkg = tid / (DH / 8), vdc = tid % (DH / 8);   // V: 8-key group, 8-dim chunk
   auto load = [&](int k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + NT * i, key = c / (DH / 8), dc = (c % (DH / 8)) * 8;
       const int kp = min(k0 + key, kend - 1);
       rk[i] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)kp * DH + dc);
-      rv[i] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)kp * DH + dc);
+    }
+    if (tid < VP) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kp = min(k0 + 8 * vkg + i, kend - 1);
+        rv[i] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)kp * DH + 8 * vdc);
+      }
     }
   };
   load(0);
@@ -237,9 +250,16 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __
     for (int i = 0; i < CPT; ++i) {
       const int c = tid + NT * i, key = c / (DH / 8), dc = (c % (DH / 8)) * 8;
       *reinterpret_cast<u32x4*>(&Ks[key * LDK + dc]) = rk[i];
-      const T* ve = reinterpret_cast<const T*>(&rv[i]);
+    }
+    if (tid < VP) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) Vt[(dc + e) * LDV + key] = (f16)(float)ve[e];
+      for (int e = 0; e < 8; ++e) {
+        half8 hv;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) hv[i] = (f16)(float)reinterpret_cast<const T*>(&rv[i])[e];
+        const int r = 8 * vdc + e;
+        *reinterpret_cast<half8*>(&Vt[r * LDV + 8 * (vkg ^ ((r >> 4) & 7))]) = hv;
+      }
     }
     lds_barrier();
     if (k0 + KB < kend) load(k0 + KB);
@@ -310,7 +330,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __
       const half8 a = *reinterpret_cast<const half8*>(&Ps[w][l16 * LDV + kk + 8 * g4]);
 #pragma unroll
       for (int t = 0; t < OT; ++t) {
-        const half8 b = *reinterpret_cast<const half8*>(&Vt[(16 * t + l16) * LDV + kk + 8 * g4]);
+        const half8 b = *reinterpret_cast<const half8*>(&Vt[(16 * t + l16) * LDV + 8 * ((kk / 8 + g4) ^ (t & 7))]);
         o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, o[t], 0, 0, 0);
       }
     }
