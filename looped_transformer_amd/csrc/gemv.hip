@@ -127,7 +127,8 @@ __device__ __forceinline__ void gemv_stage_x(const GemmArgs& g, f16* xs) {
   __syncthreads();
 }
 
-// Wave 0, lanes 0..31 (one output column each): the epilogue for row m.
+// The epilogue for row m, called by threads holding one output column each; for
+// the paired kinds these are lanes 0..31 of wave 0 (a pair lies 16 columns apart).
 template <int KIND>
 __device__ __forceinline__ void gemv_epilogue(const GemmEpi& e, int m, int col, float v) {
   if constexpr (paired(KIND)) {
