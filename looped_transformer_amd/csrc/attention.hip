@@ -23,15 +23,17 @@ template <> struct Row16<float> { typedef floatx4 type; };
 
 // LPK lanes per key (a power of two >= head_dim / elements-per-16-bytes; lanes
 // past the row hold zeros), 64 / LPK keys per load instruction, U loads per lane
-// per block of P = (64 / LPK) * U positions.
-template <class T, int LPK>
+// per block of P = (64 / LPK) * U positions.  UD = 4 cuts blocks to a quarter, for
+// contexts one full block would hold: all four waves then take part.
+template <class T, int LPK, int UD>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, const RowInfo* __restrict__ rows,
                                                        KVParams kv, T* __restrict__ out, int d, float scale,
                                                        const int32_t* live) {
   typedef typename Row16<T>::type R16;
   constexpr int EPL = 16 / (int)sizeof(T);   // elements per lane of a key row
   constexpr int KPI = 64 / LPK;              // keys per load instruction
-  constexpr int U = LPK < 16 ? LPK : 16;
+  constexpr int U = (LPK < 16 ? LPK : 16) / UD;
+  static_assert(U >= 1, "block");
   constexpr int P = KPI * U;                 // positions per block
   const int H = kv.H, dh = kv.dh;
   const int r = blockIdx.x / H, h = blockIdx.x - r * H;
@@ -381,33 +383,38 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
 
 template <class T, int LPK>
 void attn_rows_launch(const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out, const int32_t* live,
-                      hipStream_t s) {
+                      int max_ctx, hipStream_t s) {
   const int d = kv.H * kv.dh;
   const float scale = 1.0f / sqrtf((float)kv.dh);
-  hipLaunchKernelGGL((attn_rows_kernel<T, LPK>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out, d,
-                     scale, live);
+  constexpr int P = (64 / LPK) * (LPK < 16 ? LPK : 16);   // positions of a full block
+  if (max_ctx > 0 && max_ctx <= P)
+    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 4>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+                       d, scale, live);
+  else
+    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 1>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+                       d, scale, live);
 }
 
 template <class T>
 hipError_t attn_rows_dispatch(const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
-                              const int32_t* live, hipStream_t s) {
+                              const int32_t* live, int max_ctx, hipStream_t s) {
   const int chunks = kv.dh * (int)sizeof(T) / 16;   // 16-byte chunks of a row (head_dim is checked at load)
-  if (chunks <= 4) attn_rows_launch<T, 4>(q, rows, n, kv, out, live, s);
-  else if (chunks <= 8) attn_rows_launch<T, 8>(q, rows, n, kv, out, live, s);
-  else if (chunks <= 16) attn_rows_launch<T, 16>(q, rows, n, kv, out, live, s);
-  else if (chunks <= 32) attn_rows_launch<T, 32>(q, rows, n, kv, out, live, s);
+  if (chunks <= 4) attn_rows_launch<T, 4>(q, rows, n, kv, out, live, max_ctx, s);
+  else if (chunks <= 8) attn_rows_launch<T, 8>(q, rows, n, kv, out, live, max_ctx, s);
+  else if (chunks <= 16) attn_rows_launch<T, 16>(q, rows, n, kv, out, live, max_ctx, s);
+  else if (chunks <= 32) attn_rows_launch<T, 32>(q, rows, n, kv, out, live, max_ctx, s);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
-                            const int32_t* live, hipStream_t s) {
+                            const int32_t* live, int max_ctx, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (kv.dh > 128 || (kv.dh * 4) % 16 != 0) return hipErrorInvalidValue;
   switch (dtype) {
-    case DT_F32: return attn_rows_dispatch<float>(q, rows, n, kv, out, live, s);
-    case DT_F16: return attn_rows_dispatch<f16>(q, rows, n, kv, out, live, s);
-    case DT_BF16: return attn_rows_dispatch<bf16>(q, rows, n, kv, out, live, s);
+    case DT_F32: return attn_rows_dispatch<float>(q, rows, n, kv, out, live, max_ctx, s);
+    case DT_F16: return attn_rows_dispatch<f16>(q, rows, n, kv, out, live, max_ctx, s);
+    case DT_BF16: return attn_rows_dispatch<bf16>(q, rows, n, kv, out, live, max_ctx, s);
     default: return hipErrorInvalidValue;
   }
 }

@@ -352,7 +352,7 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
     TIMED(TL_T_HREBUILD, TRY(gemm(m, m->h_x, nrec, B.qkv, r2, s)));
   }
   if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, akv, w.o16, s)));
-  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, akv, w.o16, m->gate_live, s)));
+  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, akv, w.o16, m->gate_live, m->ctx_hint, s)));
   GemmEpi r{};
   r.kind = EPI_RESID;
   r.h = h;
@@ -487,8 +487,14 @@ bool ee_probed(const tl_early_exit* ee, int j, int Lmax) {
 tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   struct GateReset {
     tl_model* m;
-    ~GateReset() { m->gate_live = nullptr; }
+    ~GateReset() {
+      m->gate_live = nullptr;
+      m->ctx_hint = 0;
+    }
   } gate_reset{m};
+  m->ctx_hint = 0;
+  if (p.rows_host)
+    for (const RowInfo& r : *p.rows_host) m->ctx_hint = std::max(m->ctx_hint, r.pos + 1);
   const tl_config& c = m->cfg;
   auto& w = m->ws;
   const int d = c.d_model;

@@ -143,6 +143,7 @@ struct tl_model {
   void* stage_override = nullptr;      // descriptor base while capturing a graph
   // early exit of decode steps (allocated on first use)
   const int32_t* gate_live = nullptr;  // set while the loop of an early-exit step runs
+  int32_t ctx_hint = 0;                // while a pass runs: 1 + the largest position of its rows (0: unknown)
   int32_t* ee_live = nullptr;          // rows still running
   int32_t* ee_eff = nullptr;           // [ee_rows] effective depth by caller order
   float* ee_hprev = nullptr;           // [ee_rows, d] residual before a probed iteration

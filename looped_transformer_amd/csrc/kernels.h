@@ -90,8 +90,10 @@ hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, 
 hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const int32_t* gather, int n,
                           int d, float eps, void* out, hipStream_t s);
 // live: as GemmArgs::live (NULL: always run).  Rows marked done get a zero output.
+// max_ctx: an upper bound on pos + 1 over the rows (0: unknown), which picks
+// the block size.
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv,
-                            void* out, const int32_t* live, hipStream_t s);
+                            void* out, const int32_t* live, int max_ctx, hipStream_t s);
 // A run of up to attn_tile_rows() consecutive rows of one sequence (positions pos0 .. pos0+nrows-1)
 // that attend to positions 0 .. pos0+nrows-1 of their lane's slot.
 struct AttnTile {
