@@ -23,8 +23,9 @@ template <> struct Row16<float> { typedef floatx4 type; };
 
 // LPK lanes per key (a power of two >= head_dim / elements-per-16-bytes; lanes
 // past the row hold zeros), 64 / LPK keys per load instruction, U loads per lane
-// per block of P = (64 / LPK) * U positions.  UD = 4 cuts blocks to a quarter, for
-// contexts one full block would hold: all four waves then take part.
+// per block of P = (64 / LPK) * U positions.  UD = 4 (2) cuts blocks to a quarter
+// (half), for contexts one (two) full blocks would hold: all four waves then take
+// part.
 template <class T, int LPK, int UD>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, const RowInfo* __restrict__ rows,
                                                        KVParams kv, T* __restrict__ out, int d, float scale,
@@ -389,6 +390,9 @@ void attn_rows_launch(const void* q, const RowInfo* rows, int n, const KVParams&
   constexpr int P = (64 / LPK) * (LPK < 16 ? LPK : 16);   // positions of a full block
   if (max_ctx > 0 && max_ctx <= P)
     hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 4>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+                       d, scale, live);
+  else if (max_ctx > 0 && max_ctx <= 2 * P)
+    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 2>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
                        d, scale, live);
   else
     hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 1>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
