@@ -181,20 +181,22 @@ def test_cfg4_L_aware_int4_decode(d2048):
     _check_decode(m, prompts, forced, lane_L, sample, H, T, nxt, plg, steps)
 
 
-@pytest.mark.parametrize("cfg,lane_L", [(2, [8]), (2, [8, 5, 2]), (3, [8, 3]), (3, [8, 8, 3, 6])])
-def test_few_lane_decode_full_size(d2048, cfg, lane_L):
+@pytest.mark.parametrize("cfg,lane_L,plen", [(2, [8], 32), (2, [8, 5, 2], 32), (3, [8, 3], 32), (3, [8, 8, 3, 6], 32),
+                                              (2, [8, 4], 80)])
+def test_few_lane_decode_full_size(d2048, cfg, lane_L, plen):
     """Decode at 1-4 lanes on the 2048-wide INT4 (cfg 2) and FP16-body (cfg 3)
     models: every product of a step takes the few-row GEMVs (INT4 and dense fp16,
     RMSNorms formed inside), at the real K (2048 and 5632, several refills of the
     load rings) and, with lanes of different depth, at 4, 2 and 1 rows within one
     step.  Hidden states are held to the usual bar; too few tokens for a top-1 rate,
     so every greedy token that differs from the oracle must be a near-tie of the
-    oracle's own logits (gap within 5 % of the row rms)."""
+    oracle's own logits (gap within 5 % of the row rms).  Contexts of 33-40 and
+    81-88 positions take the decode attention's quarter- and half-size blocks."""
     spec = synth.SPECS[cfg]
     w = _with_spec(d2048, spec)
     m = oracle.OracleModel.from_weights(w)
     lane_L = np.array(lane_L, np.int32)
-    n, plen, steps = len(lane_L), 32, 8
+    n, steps = len(lane_L), 8
     prompts = synth.tokens(0, 7700 + 10 * cfg + n, n * plen, spec.vocab).reshape(n, plen)
     forced = synth.tokens(0, 7800 + 10 * cfg + n, n * steps, spec.vocab).reshape(n, steps)
     model = load_model(w, max_lanes=n, max_pos=plen + steps, kv_arena_bytes=kv_bytes(spec, lane_L, [plen + steps] * n))
