@@ -531,6 +531,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   int flip = 0;
   int64_t log_off = 0;
   bool moved = true;
+  bool hprev_saved = false;   // ee_hprev already holds the rows entering the next iteration
   if (p.ee) {
     m->gate_live = m->ee_live;
     // the probe marks rows in the loop's row list: keep the caller-order list the
@@ -545,7 +546,11 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     const bool leaving = next < nj;
     const bool probe = ee_probed(p.ee, j, Lmax);
     const bool by_margin = probe && p.ee->logit_margin > 0.f;
-    if (probe && !by_margin) HIPCHK(hipMemcpyAsync(m->ee_hprev, h, (size_t)nj * d * 4, hipMemcpyDeviceToDevice, s));
+    // the hidden rule compares with this iteration's input rows: copied here, unless
+    // the previous iteration's probe left them (same row list) in ee_hprev
+    if (probe && !by_margin && !hprev_saved)
+      HIPCHK(hipMemcpyAsync(m->ee_hprev, h, (size_t)nj * d * 4, hipMemcpyDeviceToDevice, s));
+    const bool save_prev = probe && !by_margin && !leaving && ee_probed(p.ee, j + 1, Lmax);
     for (int l = 0; l < c.n_loop; ++l) {
       kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + (j - 1) * c.n_loop + l;
       // (a probe leaves the next iteration's normalised input alone: the logit
@@ -558,9 +563,11 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
       if (by_margin) {
         TRY(run_head(m, h, nullptr, nj, nullptr, nullptr, nullptr, s, m->ee_margin));
       }
-      HIPCHK(launch_ee_probe(const_cast<RowInfo*>(rows), nj, j, h, m->ee_hprev, by_margin ? m->ee_margin : nullptr,
+      HIPCHK(launch_ee_probe(const_cast<RowInfo*>(rows), nj, j, h, m->ee_hprev, save_prev,
+                             by_margin ? m->ee_margin : nullptr,
                              p.ee->tau, p.ee->logit_margin, p.ee->patience, d, p.final_h, m->ee_eff, m->ee_live, s));
     }
+    hprev_saved = save_prev;
     moved = leaving;
     if (moved) {
       RowInfo* rout = rbuf[flip];

@@ -122,8 +122,10 @@ hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream
 // done are stable when margin[i] > margin_thr (margin != NULL) or when
 // ||h_i - h_prev_i|| / ||h_i|| < tau; streak counts consecutive stable probes and
 // resets otherwise; at streak >= patience the row is marked done, its state goes to
-// h_exit[orig], eff_depth[orig] = it and *live is decremented.
-hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, const float* h_prev,
+// h_exit[orig], eff_depth[orig] = it and *live is decremented.  save_prev (hidden
+// rule): the rows not done then copy h_i into h_prev_i for a probe at the next
+// iteration on the same row list.
+hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, float* h_prev, bool save_prev,
                            const float* margin, float tau, float margin_thr, int patience, int d,
                            float* h_exit, int32_t* eff_depth, int32_t* live, hipStream_t s);
 // Per row i of the head GEMM's tile partials (pv/pi: best value and index of each

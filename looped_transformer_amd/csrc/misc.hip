@@ -131,12 +131,13 @@ __global__ void write_orig_kernel(const RowInfo* rows, int n, int32_t* out) {
 // ---------------------------------------------------------------- early exit
 // One workgroup per row: relative L2 change (or a precomputed logit margin)
 // decides a stable probe; patience consecutive stable probes finish the row, whose
-// state is copied out as its exit state.
+// state is copied out as its exit state.  With save set (hidden rule), the row's h
+// then replaces its h_prev row, ready for a probe at the next iteration.
 __global__ __launch_bounds__(256) void ee_probe_kernel(RowInfo* __restrict__ rows, int it,
-                                                      const float* __restrict__ h, const float* __restrict__ h_prev,
+                                                      const float* __restrict__ h, float* h_prev,
                                                       const float* __restrict__ margin, float tau, float margin_thr,
                                                       int patience, int d, float* __restrict__ h_exit,
-                                                      int32_t* __restrict__ eff_depth, int32_t* live) {
+                                                      int32_t* __restrict__ eff_depth, int32_t* live, int save) {
   const int r = blockIdx.x, tid = threadIdx.x;
   const RowInfo ri = rows[r];
   if (ri.done) return;   // uniform over the workgroup
@@ -172,10 +173,19 @@ __global__ __launch_bounds__(256) void ee_probe_kernel(RowInfo* __restrict__ row
       red[0][tid >> 6] = dd;
       red[1][tid >> 6] = hh;
     }
-    __syncthreads();
+    __syncthreads();   // every read of the h_prev row is done
     dd = red[0][0] + red[0][1] + red[0][2] + red[0][3];
     hh = red[1][0] + red[1][1] + red[1][2] + red[1][3];
     stable = sqrtf(dd) < tau * sqrtf(hh);
+    if (save) {
+      float* sv = h_prev + (int64_t)r * d;
+      if (vec) {
+        for (int c = tid; c < (d >> 2); c += 256)
+          reinterpret_cast<floatx4*>(sv)[c] = reinterpret_cast<const floatx4*>(hr)[c];
+      } else {
+        for (int c = tid; c < d; c += 256) sv[c] = hr[c];
+      }
+    }
   }
   const int streak = stable ? ri.streak + 1 : 0;
   const bool fin = streak >= patience;
@@ -542,12 +552,12 @@ hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream
   return hipGetLastError();
 }
 
-hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, const float* h_prev, const float* margin,
+hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, float* h_prev, bool save_prev, const float* margin,
                            float tau, float margin_thr, int patience, int d, float* h_exit, int32_t* eff_depth,
                            int32_t* live, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(ee_probe_kernel, dim3(n), dim3(256), 0, s, rows, it, h, h_prev, margin, tau,
-                     margin_thr, patience, d, h_exit, eff_depth, live);
+                     margin_thr, patience, d, h_exit, eff_depth, live, (save_prev && !margin) ? 1 : 0);
   return hipGetLastError();
 }
 
