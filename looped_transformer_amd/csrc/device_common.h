@@ -71,6 +71,19 @@ __device__ __forceinline__ half2v w4_pair(uint32_t w, int i) {
   return h - off;
 }
 
+// All four pairs of a word, q[i] = w4_pair(w, i): the low and the high nibble of
+// every byte are split once, then each pair's two nibble bytes are placed under
+// 0x64 exponent bytes by one byte permute (v_perm_b32; selector bytes 0-3 pick
+// from the second operand, 4-7 from the first).
+__device__ __forceinline__ void w4_pairs(uint32_t w, half2v (&q)[4]) {
+  const uint32_t lo = w & 0x0F0F0F0Fu, hi = (w >> 4) & 0x0F0F0F0Fu, e = 0x64646464u;
+  const half2v off = {(f16)1032.0f, (f16)1032.0f};
+  q[0] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(e, lo, 0x04020400u)) - off;   // bits 0-3, 16-19
+  q[1] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(e, hi, 0x04020400u)) - off;   // bits 4-7, 20-23
+  q[2] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(e, lo, 0x04030401u)) - off;   // bits 8-11, 24-27
+  q[3] = __builtin_bit_cast(half2v, __builtin_amdgcn_perm(e, hi, 0x04030401u)) - off;   // bits 12-15, 28-31
+}
+
 // Early-exit gate: true when the pass has no live row left (every row finished).
 // Kernels read it once their first loads are in flight, so its latency overlaps
 // theirs instead of delaying every other argument load; the barrier keeps those

@@ -104,7 +104,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
     for (int i = 0; i < AC; ++i) {
       const int c = tid + 256 * i, r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
       const int gr = m0 + r, gk = k0 + kc;
-      okA |= (gr < M && gk < ke) ? (1u << i) : 0u;
+      if constexpr (!W4) okA |= (gr < M && gk < ke) ? (1u << i) : 0u;   // (INT4: scale 0 instead)
       const int grc = min(gr, M - 1), gkc = min(gk, K - 8);
       ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)grc * K + gkc);
     }
@@ -118,7 +118,6 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
         const int go = c / (BN * 4), rem = c % (BN * 4);
         const int row = (rem >> 7) * 32 + (rem & 31), hb = (rem >> 6) & 1, h = (rem >> 5) & 1;
         const int gn = n0 + row;
-        okB |= (tid + 256 * i < BCH && gn < N && k0 + go * 128 < ke) ? (1u << i) : 0u;
         const int gnc = min(gn, N - 1), gic = min((k0 >> 7) + go, groups - 1);
         rb[i] = *reinterpret_cast<const uint4*>(g.Bw4 + w4_word_offset(gnc, gic * 16 + 8 * hb + h, groups));
       }
@@ -147,10 +146,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
     // keep the masking here: without this the compiler may move it next to the
     // loads and wait for the data as soon as it is requested
     asm volatile("" : "+v"(okA), "+v"(okB));
+    // INT4: no operand is masked.  A group outside the tile or the split (columns
+    // past N, K past the split's end, padded stages) gets scale 0 below, so its
+    // clamped, finite operands add nothing; rows past M are never stored.
 #pragma unroll
     for (int i = 0; i < AC; ++i) {
       const int c = tid + 256 * i, r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-      const uint32_t mk = 0u - ((okA >> i) & 1u);
+      const uint32_t mk = W4 ? ~0u : 0u - ((okA >> i) & 1u);
       *reinterpret_cast<uint4*>(&As[r * LDK + kc]) = uint4{ra[i].x & mk, ra[i].y & mk, ra[i].z & mk, ra[i].w & mk};
     }
     if constexpr (W4) {
@@ -160,19 +162,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
         if (c < BCH) {
           const int go = c / (BN * 4), rem = c % (BN * 4);
           const int row = (rem >> 7) * 32 + (rem & 31), hb = (rem >> 6) & 1, hk = (rem >> 5) & 1;
-          // outside the tile: nibbles 8, i.e. q = 0
-          const uint32_t mk = 0u - ((okB >> i) & 1u), q0 = 0x88888888u & ~mk;
-          const uint32_t ws[4] = {(rb[i].x & mk) | q0, (rb[i].y & mk) | q0, (rb[i].z & mk) | q0, (rb[i].w & mk) | q0};
+          const uint32_t ws[4] = {rb[i].x, rb[i].y, rb[i].z, rb[i].w};
           // word wi: k = 16 (4 hb + wi) + 8 hk + (0..7) of the group
           f16* dst = reinterpret_cast<f16*>(&Bs[row * LDK + go * 128 + 64 * hb + 8 * hk]);
 #pragma unroll
           for (int wi = 0; wi < 4; ++wi) {
             half8 h;
+            half2v t[4];
+            w4_pairs(ws[wi], t);
 #pragma unroll
             for (int p = 0; p < 4; ++p) {
-              const half2v t = w4_pair(ws[wi], p);
-              h[2 * p] = t[0];
-              h[2 * p + 1] = t[1];
+              h[2 * p] = t[p][0];
+              h[2 * p + 1] = t[p][1];
             }
             *reinterpret_cast<half8*>(dst + wi * 16) = h;
           }
@@ -516,11 +517,12 @@ __global__ __launch_bounds__(256) void gemm_skinny_w4_kernel(GemmArgs g, GemmEpi
       for (int cb = 0; cb < WNB; ++cb) {
         const u32x4 q4 = rw[u][cb][j >> 2];
         const uint32_t w = q4[j & 3];
+        half2v t[4];
+        w4_pairs(w, t);
 #pragma unroll
         for (int p = 0; p < 4; ++p) {
-          const half2v t = w4_pair(w, p);
-          b[cb][2 * p] = t[0];
-          b[cb][2 * p + 1] = t[1];
+          b[cb][2 * p] = t[p][0];
+          b[cb][2 * p + 1] = t[p][1];
         }
       }
 #pragma unroll

@@ -190,14 +190,15 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(GemmArgs g, GemmEpi e)
         const uint32_t wd = jj < 4 ? w[j][0][jj] : w[j][1][jj - 4];
         // word jj holds k = 16 jj + 8 hk + 0..7 of the group
         const int k0 = gi * 128 + 16 * jj + 8 * hk;
+        half2v q[4];
+        w4_pairs(wd, q);
 #pragma unroll
         for (int m = 0; m < M; ++m) {
           const half8 xv = *reinterpret_cast<const half8*>(&xs[m * K + k0]);
 #pragma unroll
           for (int p = 0; p < 4; ++p) {
-            const half2v q = w4_pair(wd, p);
             const half2v xp = {xv[2 * p], xv[2 * p + 1]};
-            ga[m] = __builtin_amdgcn_fdot2(q, xp, ga[m], false);
+            ga[m] = __builtin_amdgcn_fdot2(q[p], xp, ga[m], false);
           }
         }
       }
