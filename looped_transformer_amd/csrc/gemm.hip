@@ -826,6 +826,11 @@ TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
     }
   }
   if (!g.Bw4 && t.bm == 32 && t.bn == 64 && t.splits == 1) t.depth = 4;
+  // one unsplit 64 x 64 tile per CU at most (QKV at 128 rows): nothing else on the
+  // CU hides a stage's loads, so keep three stages in flight (171 -> 162 us of QKV
+  // per forward; with two tiles on a CU, or a split that pads the stage count,
+  // two stages measured faster)
+  if (t.bm == 64 && t.bn == 64 && t.splits == 1 && tiles <= kCUs) t.depth = 4;
   return t;
 }
 
@@ -890,6 +895,7 @@ hipError_t launch_mfma(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool*
       if (t.bm == 32 && t.depth == 4) return launch_mfma_t<AT, W4, 32, 64, 128, 4>(g, e, t, s, norm_done);
     }
     if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 64, 128, 2>(g, e, t, s, norm_done);
+    if (t.depth == 4) return launch_mfma_t<AT, W4, 64, 64, 128, 4>(g, e, t, s, norm_done);
     return launch_mfma_t<AT, W4, 64, 64, 128, 2>(g, e, t, s, norm_done);
   }
   if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 128, 128, 2>(g, e, t, s, norm_done);
