@@ -38,6 +38,8 @@ def parse():
     ap.add_argument("--no-prefix", action="store_true", help="skip the shared-prefix measurement")
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative measurement")
     ap.add_argument("--no-store-h", action="store_true", help="skip the store-h cache-mode measurement")
+    ap.add_argument("--no-extra-configs", action="store_true",
+                    help="skip the FP16-body 32 x 128 forward and the L-aware 64-lane INT4 decode")
     ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
     ap.add_argument("--profile-decode", action="store_true",
                     help="run batch-1 INT4 decode steps only (32-token prompt, 63 steps at L=8; for rocprofv3)")
@@ -187,6 +189,10 @@ def main():
 
     if not args.no_decode:
         out["decode_L8"] = decode_bench(tl, torch, np, synth, kv_bytes, load_model)
+    if not args.no_extra_configs:
+        out["forward_fp16_L8"] = forward_fp16_bench(tl, torch, np, synth, load_model,
+                                                    synth.make_weights(synth.SPECS[3], 0))
+        out["decode_lane_aware"] = lane_aware_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_prefix:
         out["shared_prefix"] = prefix_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_spec:
@@ -235,6 +241,101 @@ def profile_decode_fp16(tl, torch, np, synth, kv_bytes, load_model):
     tl.tl_free(model)
 
 
+HBM_PEAK_GBPS = 8000.0
+
+
+def block_weight_bytes(spec, w4):
+    """Bytes of one block's weights: fp16, or W4G128 nibbles plus one fp16 scale per
+    128-wide group."""
+    params = 4 * spec.d_model * spec.d_model + 3 * spec.d_model * spec.ffn
+    return params // 2 + params // 128 * 2 if w4 else 2 * params
+
+
+def decode_step_bytes(spec, loop_w4, lane_L, ctx):
+    """Algorithmic HBM bytes of one cached decode step: the pre/post blocks (fp16), the
+    loop stack once per iteration up to the deepest lane, the head (fp16), and each
+    lane's K/V (fp16) of every slot it attends over ctx positions."""
+    d = spec.d_model
+    weights = ((spec.n_pre + spec.n_post) * block_weight_bytes(spec, False)
+               + int(max(lane_L)) * spec.n_loop * block_weight_bytes(spec, loop_w4) + spec.vocab * d * 2)
+    kv = sum((spec.n_pre + int(L) * spec.n_loop + spec.n_post) * ctx * 2 * d * 2 for L in lane_L)
+    return weights + kv
+
+
+def hbm_rate(nbytes, seconds):
+    gbps = nbytes / seconds / 1e9
+    return {"algorithmic_bytes_per_step": int(nbytes), "achieved_GBps": round(gbps, 1),
+            "peak_GBps": HBM_PEAK_GBPS, "frac": round(gbps / HBM_PEAK_GBPS, 4)}
+
+
+def forward_fp16_bench(tl, torch, np, synth, load_model, w):
+    """Scoring forward of 32 x 128 tokens at L = 8 on the FP16-body model (4096 rows per
+    pass), graph-replayed like the main forward; best of 3 timed runs of 5 calls."""
+    spec = synth.SPECS[3]
+    log("forward: FP16-body model, 32 x 128 tokens, L=8")
+    n, T, L = 32, 128, 8
+    model = load_model(w, max_pos=256)
+    toks = torch.tensor(synth.tokens(0, synth.STREAM_TOKENS, n * T, spec.vocab), dtype=torch.int32, device="cuda")
+    cu = np.arange(0, n * T + 1, T, dtype=np.int32)
+    hid = torch.empty(n * T, spec.d_model, dtype=torch.float32, device="cuda")
+    ds = torch.cuda.Stream()
+    for _ in range(3):
+        tl.tl_forward(model, cu, toks, L=L, out_hidden=hid, stream=ds)
+    torch.cuda.synchronize()
+    best = 1e9
+    for _ in range(3):
+        t0 = time.perf_counter()
+        for _ in range(5):
+            tl.tl_forward(model, cu, toks, L=L, out_hidden=hid, stream=ds)
+        torch.cuda.synchronize()
+        best = min(best, (time.perf_counter() - t0) / 5)
+    tl.tl_free(model)
+    d = spec.d_model
+    per_token_block = 2 * (4 * d * d + 3 * d * spec.ffn)
+    flops = n * T * (spec.n_pre + L * spec.n_loop + spec.n_post) * per_token_block \
+        + n * (spec.n_pre + L * spec.n_loop + spec.n_post) * 4 * (T * T // 2) * d
+    tf = flops / best / 1e12
+    return {"config": "FP16-body loop block (2048-wide), 32 sequences x 128 tokens, L=8, no logits",
+            "ms": round(best * 1e3, 3), "token_iterations_per_s": round(n * T * L / best, 1),
+            "mfma": {"algorithmic_flops": int(flops), "achieved_TFLOPs": round(tf, 1), "peak_TFLOPs": PEAK_F16_TFLOPS,
+                     "frac": round(tf / PEAK_F16_TFLOPS, 4)}}
+
+
+def lane_aware_bench(tl, torch, np, synth, kv_bytes, load_model):
+    """L-aware batched decode on the INT4 model: 64 lanes, per-lane depth drawn from
+    {2, 4, 8, 16, 32}, 32-token prompts, 31 cached greedy steps; best of 2 runs."""
+    ds = torch.cuda.Stream()
+    spec = synth.SPECS[4]
+    log("decode: L-aware lanes, INT4 model")
+    w = synth.make_weights(spec, 0)
+    n, plen, new = 64, 32, 32
+    lane_L = synth.lane_loops(0, n)
+    model = load_model(w, max_lanes=n, max_pos=plen + new, max_L=int(lane_L.max()),
+                       kv_arena_bytes=kv_bytes(spec, lane_L, [plen + new] * n))
+    toks = torch.tensor(synth.tokens(0, synth.STREAM_PROMPT_TOKENS, n * plen, spec.vocab), dtype=torch.int32,
+                        device="cuda")
+    cu = np.arange(0, n * plen + 1, plen, dtype=np.int32)
+    lanes = np.arange(n, dtype=np.int32)
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    best = 1e9
+    for _ in range(2):
+        tl.tl_forward(model, cu, toks, seq_L=lane_L, lanes=lanes, max_new_tokens=new, stream=ds)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(new - 1):
+            tl.tl_decode_step(model, lanes, lane_L, out, stream=ds)
+        torch.cuda.synchronize()
+        best = min(best, time.perf_counter() - t0)
+    tl.tl_free(model)
+    step_s = best / (new - 1)
+    ctx = plen + new / 2
+    return {"config": "INT4 loop block (2048-wide), 64 lanes, per-lane L from {2, 4, 8, 16, 32} (seed 0), "
+                      "32-token prompts, 31 cached greedy steps",
+            "lane_L_sum": int(lane_L.sum()), "ms_per_step": round(step_s * 1e3, 4),
+            "token_iterations_per_s": round(int(lane_L.sum()) / step_s, 1), "tok_per_s": round(n / step_s, 1),
+            "hbm": hbm_rate(decode_step_bytes(spec, True, lane_L, ctx), step_s)}
+
+
 def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
     """32 lanes, 32-token prompts, greedy cached decode at L = 8 on the FP16-body model;
     the same run with the device-side early-exit rule at three settings."""
@@ -270,6 +371,7 @@ def decode_bench(tl, torch, np, synth, kv_bytes, load_model):
     res = run(lambda: tl.tl_decode_step(model, lanes, Ls, out, stream=ds))
     res["config"] = ("FP16-body loop block, 32 lanes, 32-token prompts, 31 cached greedy steps at L=8 "
                      "(first token comes from the prefill)")
+    res["hbm"] = hbm_rate(decode_step_bytes(spec, False, Ls, plen + new / 2), res["ms_per_step"] / 1e3)
     ee = {
         # relative-L2 rule that never fires: the cost of probing every iteration from 2 on
         "hidden_rule_never_fires": dict(patience=1, min_L=2, tau=0.0),
@@ -431,6 +533,9 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
     round_ms = k * t_draft + t_verify
     res["break_even_accepted_per_round"] = round(round_ms / t_step - 1, 3)
     res["tok_per_s_if_all_accepted"] = round((k + 1) / round_ms, 1)
+    # the plain step as an HBM-bound step: weights read once per loop iteration, the
+    # lane's K/V at the mean context of the 64-token run
+    res["plain_step_hbm"] = hbm_rate(decode_step_bytes(spec, True, [8], plen + new / 2), t_step)
     res["note"] = ("break-even and all-accepted figures are derived from the timed pieces (a round = 4 draft steps + "
                    "one verify pass, yielding accepted + 1 tokens); the verify piece includes a fork of the "
                    "32-token prompt")
