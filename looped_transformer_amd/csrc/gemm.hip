@@ -231,9 +231,68 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   // (every prefetch issued unconditionally; padded stages load clamped addresses
   // and are masked to zero), which lets the compiler wait for just the oldest stage.
   const int nst = ((ke - kb + BK - 1) / BK + D - 1) / D * D;
+  // QKV: what the epilogue reads besides the accumulators is requested around
+  // the first stages, so that its latency overlaps the main loop: thread t < BM
+  // takes the cache coordinates of row m0 + t (lane, position, iteration, done,
+  // then the lane's slot offset and capacity), every lane the rotary factors of
+  // its own rows and columns.
+  constexpr int QJ = (KIND == EPI_QKV) ? TN / 2 : 1;
+  constexpr int QM = (KIND == EPI_QKV) ? TM : 1;
+  int qri[4] = {0, 0, 0, 0};
+  int qpos[QM][4] = {};
+  int64_t qcap = 0, qoff = 0;
+  int qsect[QJ] = {}, qhead[QJ] = {}, qcd[QJ] = {}, qrn[QJ] = {};
+  float rcos[QM][4][QJ] = {}, rsin[QM][4][QJ] = {};
+  if constexpr (KIND == EPI_QKV) {
+    if (S == 1) {
+      if (tid < BM) {
+        const RowInfo* ri = e.rows + min(m0 + tid, M - 1);
+        qri[0] = ri->lane;
+        qri[1] = ri->pos;
+        qri[2] = ri->iter;
+        qri[3] = ri->done;
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+          qpos[i][r] = e.rows[min(m0 + wm * WTM + i * 16 + 4 * (lane >> 4) + r, M - 1)].pos;
+    }
+  }
 #pragma unroll
   for (int u = 0; u < D - 1; ++u) gload(ra_[u], rb_[u], rs_[u], okA_[u], okB_[u], kb + u * BK);
   if (gate_closed(g.live)) return;
+  if constexpr (KIND == EPI_QKV) {
+    if (S == 1) {
+      if (tid < BM) {
+        qcap = e.kv.lane_cap[qri[0]];
+        qoff = e.kv.lane_off[qri[0]];
+      }
+      // column arithmetic (section, head, rotary index: integer divisions) once
+      // per column of this lane
+      const int half = e.dh >> 1;
+#pragma unroll
+      for (int jp = 0; jp < QJ; ++jp) {
+        const int c = min(n0 + wn * WTN + 2 * jp * 16 + (lane & 15), N - 1);
+        qsect[jp] = c / e.d;
+        const int cc = c - qsect[jp] * e.d;
+        qhead[jp] = cc / e.dh;
+        qcd[jp] = cc - qhead[jp] * e.dh;
+        const int ci = qcd[jp] / e.pair_g;
+        qrn[jp] = (ci >> 1) * e.pair_g + (qcd[jp] - ci * e.pair_g);
+      }
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r)
+#pragma unroll
+          for (int jp = 0; jp < QJ; ++jp) {
+            const int64_t at = (int64_t)max(qpos[i][r], 0) * half + qrn[jp];
+            rcos[i][r][jp] = e.rope_cos[at];
+            rsin[i][r][jp] = e.rope_sin[at];
+          }
+    }
+  }
   for (int s0 = 0; s0 < nst; s0 += D) {
     static_for<0, D>([&](auto uc) {
       constexpr int u = decltype(uc)::value;
@@ -313,55 +372,45 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       }
     }
   } else if constexpr (KIND == EPI_QKV) {
-    // The QKV epilogue of epi_pair with its column arithmetic (section, head,
-    // rotary index: integer divisions) done once per column of this lane and its
-    // cache addressing once per row, instead of once per value.
-    constexpr int EJ = TN / 2;
-    const int d = e.d, dh = e.dh, G = e.pair_g, half = dh >> 1;
-    int sect[EJ], head[EJ], cdv[EJ], rn[EJ];
-#pragma unroll
-    for (int jp = 0; jp < EJ; ++jp) {
-      const int c = min(n0 + wn * WTN + 2 * jp * 16 + lc, N - 1);
-      sect[jp] = c / d;
-      const int cc = c - sect[jp] * d;
-      head[jp] = cc / dh;
-      cdv[jp] = cc - head[jp] * dh;
-      const int ci = cdv[jp] / G;
-      rn[jp] = (ci >> 1) * G + (cdv[jp] - ci * G);
+    // epi_pair's QKV epilogue with its operands gathered before the main loop
+    // (above); thread t < BM finishes the cache addressing of row m0 + t in LDS.
+    __shared__ int64_t q_kb[BM], q_hs[BM];
+    __shared__ int q_ok[BM];   // 0: row not written (past M, or finished by early exit)
+    if (tid < BM) {
+      const int64_t hs = qcap * e.kv.dh;   // one head of one slot
+      const int slot = e.kv.s0 + e.kv.s1 * qri[2];
+      q_kb[tid] = qoff + (int64_t)(slot * 2) * e.kv.H * hs + (int64_t)qri[1] * e.kv.dh;
+      q_hs[tid] = hs;
+      q_ok[tid] = m0 + tid < M && !(e.skip_done && qri[3]);
     }
+    __syncthreads();
+    const int d = e.d, dh = e.dh, G = e.pair_g, half = dh >> 1;
+    AT* const kv = reinterpret_cast<AT*>(e.kv.base);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
-        const int row = m0 + wm * WTM + i * 16 + lr + r;
-        if (row >= M) continue;
-        const RowInfo ri = e.rows[row];
-        if (e.skip_done && ri.done) continue;   // finished by early exit: its later cache slots stay unwritten
-        const int64_t cap = e.kv.lane_cap[ri.lane];
-        const int64_t hs = cap * e.kv.dh;                                  // one head of one slot
-        const int slot = e.kv.s0 + e.kv.s1 * ri.iter;
-        const int64_t kbase = e.kv.lane_off[ri.lane] + (int64_t)(slot * 2) * e.kv.H * hs + (int64_t)ri.pos * e.kv.dh;
-        const int64_t vbase = kbase + e.kv.H * hs;
-        AT* const kv = reinterpret_cast<AT*>(e.kv.base);
+        const int lrow = wm * WTM + i * 16 + lr + r, row = m0 + lrow;
+        if (!q_ok[lrow]) continue;
+        const int64_t hs = q_hs[lrow], kbase = q_kb[lrow], vbase = kbase + e.kv.H * hs;
 #pragma unroll
-        for (int jp = 0; jp < EJ; ++jp) {
+        for (int jp = 0; jp < QJ; ++jp) {
           const int col = n0 + wn * WTN + 2 * jp * 16 + lc;
           if (col >= N) continue;
           const float v0 = acc[i][2 * jp][r], v1 = acc[i][2 * jp + 1][r];
-          if (sect[jp] == 2) {
-            AT* vp = kv + vbase + head[jp] * hs;
-            vp[cdv[jp]] = from_f32<AT>(v0);
-            vp[cdv[jp] + G] = from_f32<AT>(v1);
+          if (qsect[jp] == 2) {
+            AT* vp = kv + vbase + qhead[jp] * hs;
+            vp[qcd[jp]] = from_f32<AT>(v0);
+            vp[qcd[jp] + G] = from_f32<AT>(v1);
             continue;
           }
-          const float cs = e.rope_cos[(int64_t)ri.pos * half + rn[jp]];
-          const float sn = e.rope_sin[(int64_t)ri.pos * half + rn[jp]];
+          const float cs = rcos[i][r][jp], sn = rsin[i][r][jp];
           const float x1 = v0 * cs - v1 * sn;
           const float x2 = v1 * cs + v0 * sn;
-          AT* dst = (sect[jp] == 0) ? reinterpret_cast<AT*>(e.q_out) + (int64_t)row * d + head[jp] * dh
-                                    : kv + kbase + head[jp] * hs;
-          dst[rn[jp]] = from_f32<AT>(x1);
-          dst[rn[jp] + half] = from_f32<AT>(x2);
+          AT* dst = (qsect[jp] == 0) ? reinterpret_cast<AT*>(e.q_out) + (int64_t)row * d + qhead[jp] * dh
+                                     : kv + kbase + qhead[jp] * hs;
+          dst[qrn[jp]] = from_f32<AT>(x1);
+          dst[qrn[jp] + half] = from_f32<AT>(x2);
         }
       }
   } else if constexpr (KIND == EPI_SWIGLU) {
@@ -791,13 +840,14 @@ struct TileCfg {
 
 constexpr int kCUs = 256;
 
-// Tile and split choice, from a sweep of the 2048-wide model's shapes on MI355X:
+// Tile and split choice, from sweeps of the 2048-wide model's shapes on MI355X:
 // for M <= 128 the kernels are bound by per-workgroup latency, so small tiles
-// (BM 32/64 x BN 64, BK 128, two-stage ring) and a split of K that brings the
-// workgroup count to roughly 320 work best; larger M uses 128 x 128 tiles and
-// splits K only when the tiles cannot cover the 256 CUs.  Dense weights at
-// <= 32 rows that get no split (gate/up: 176 tiles of 16 stages) keep three
-// stages in flight instead of one: 17.5 -> 12.3 us with the weights in HBM.
+// (BM 32/64 x BN 64, BK 128, two-stage ring, refined by the rules at the end) and
+// a split of K that brings the workgroup count to roughly 320 work best; larger
+// M uses 128 x 128 tiles and splits K only when the tiles cannot cover the 256
+// CUs.  Dense weights at <= 32 rows that get no split (gate/up: 176 tiles of 16
+// stages) keep three stages in flight instead of one: 17.5 -> 12.3 us with the
+// weights in HBM.
 TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
   if (act_dtype == DT_F32) return {64, 64, 1, g.K, 16, 2};
   TileCfg t{};
