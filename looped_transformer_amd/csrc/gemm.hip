@@ -231,27 +231,53 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   // (every prefetch issued unconditionally; padded stages load clamped addresses
   // and are masked to zero), which lets the compiler wait for just the oldest stage.
   const int nst = ((ke - kb + BK - 1) / BK + D - 1) / D * D;
-  // QKV: what the epilogue reads besides the accumulators is requested around
-  // the first stages, so that its latency overlaps the main loop: thread t < BM
-  // takes the cache coordinates of row m0 + t (lane, position, iteration, done,
-  // then the lane's slot offset and capacity), every lane the rotary factors of
-  // its own rows and columns.
+  // QKV epilogue operands besides the accumulators: thread t < BM takes the cache
+  // coordinates of row m0 + t (lane, position, iteration, done, then the lane's
+  // slot offset and capacity), every lane the rotary factors of its own rows and
+  // columns.  Small tiles (BM <= 64, BN 64: eight rows and one column pair per
+  // lane) request them around the first stages, so that their latency overlaps
+  // the main loop; larger tiles would hold too many of them in registers across
+  // the loop and gather them after it, in two rounds of loads.
+  constexpr bool QPRE = KIND == EPI_QKV && BM <= 64 && BN == 64;
   constexpr int QJ = (KIND == EPI_QKV) ? TN / 2 : 1;
   constexpr int QM = (KIND == EPI_QKV) ? TM : 1;
   int qri[4] = {0, 0, 0, 0};
-  int qpos[QM][4] = {};
+  int qpos[QPRE ? TM : 1][4] = {};
   int64_t qcap = 0, qoff = 0;
   int qsect[QJ] = {}, qhead[QJ] = {}, qcd[QJ] = {}, qrn[QJ] = {};
   float rcos[QM][4][QJ] = {}, rsin[QM][4][QJ] = {};
-  if constexpr (KIND == EPI_QKV) {
+  auto q_row = [&]() {
+    const RowInfo* ri = e.rows + min(m0 + tid, M - 1);
+    qri[0] = ri->lane;
+    qri[1] = ri->pos;
+    qri[2] = ri->iter;
+    qri[3] = ri->done;
+  };
+  // column arithmetic (section, head, rotary index: integer divisions) once per
+  // column of this lane
+  auto q_cols = [&]() {
+#pragma unroll
+    for (int jp = 0; jp < QJ; ++jp) {
+      const int c = min(n0 + wn * WTN + 2 * jp * 16 + (lane & 15), N - 1);
+      qsect[jp] = c / e.d;
+      const int cc = c - qsect[jp] * e.d;
+      qhead[jp] = cc / e.dh;
+      qcd[jp] = cc - qhead[jp] * e.dh;
+      const int ci = qcd[jp] / e.pair_g;
+      qrn[jp] = (ci >> 1) * e.pair_g + (qcd[jp] - ci * e.pair_g);
+    }
+  };
+  auto q_rope = [&](int i, int r, int pos) {
+#pragma unroll
+    for (int jp = 0; jp < QJ; ++jp) {
+      const int64_t at = (int64_t)max(pos, 0) * (e.dh >> 1) + qrn[jp];
+      rcos[i][r][jp] = e.rope_cos[at];
+      rsin[i][r][jp] = e.rope_sin[at];
+    }
+  };
+  if constexpr (QPRE) {
     if (S == 1) {
-      if (tid < BM) {
-        const RowInfo* ri = e.rows + min(m0 + tid, M - 1);
-        qri[0] = ri->lane;
-        qri[1] = ri->pos;
-        qri[2] = ri->iter;
-        qri[3] = ri->done;
-      }
+      if (tid < BM) q_row();
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -262,35 +288,17 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
 #pragma unroll
   for (int u = 0; u < D - 1; ++u) gload(ra_[u], rb_[u], rs_[u], okA_[u], okB_[u], kb + u * BK);
   if (gate_closed(g.live)) return;
-  if constexpr (KIND == EPI_QKV) {
+  if constexpr (QPRE) {
     if (S == 1) {
       if (tid < BM) {
         qcap = e.kv.lane_cap[qri[0]];
         qoff = e.kv.lane_off[qri[0]];
       }
-      // column arithmetic (section, head, rotary index: integer divisions) once
-      // per column of this lane
-      const int half = e.dh >> 1;
-#pragma unroll
-      for (int jp = 0; jp < QJ; ++jp) {
-        const int c = min(n0 + wn * WTN + 2 * jp * 16 + (lane & 15), N - 1);
-        qsect[jp] = c / e.d;
-        const int cc = c - qsect[jp] * e.d;
-        qhead[jp] = cc / e.dh;
-        qcd[jp] = cc - qhead[jp] * e.dh;
-        const int ci = qcd[jp] / e.pair_g;
-        qrn[jp] = (ci >> 1) * e.pair_g + (qcd[jp] - ci * e.pair_g);
-      }
+      q_cols();
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int r = 0; r < 4; ++r)
-#pragma unroll
-          for (int jp = 0; jp < QJ; ++jp) {
-            const int64_t at = (int64_t)max(qpos[i][r], 0) * half + qrn[jp];
-            rcos[i][r][jp] = e.rope_cos[at];
-            rsin[i][r][jp] = e.rope_sin[at];
-          }
+        for (int r = 0; r < 4; ++r) q_rope(i, r, qpos[i][r]);
     }
   }
   for (int s0 = 0; s0 < nst; s0 += D) {
@@ -372,18 +380,32 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       }
     }
   } else if constexpr (KIND == EPI_QKV) {
-    // epi_pair's QKV epilogue with its operands gathered before the main loop
-    // (above); thread t < BM finishes the cache addressing of row m0 + t in LDS.
+    // epi_pair's QKV epilogue with its operands gathered as described above;
+    // thread t < BM finishes the cache addressing of row m0 + t in LDS.
     __shared__ int64_t q_kb[BM], q_hs[BM];
-    __shared__ int q_ok[BM];   // 0: row not written (past M, or finished by early exit)
+    __shared__ int q_pos[BM];   // -1: row not written (past M, or finished by early exit)
+    if constexpr (!QPRE) {
+      if (tid < BM) {
+        q_row();
+        qcap = e.kv.lane_cap[qri[0]];
+        qoff = e.kv.lane_off[qri[0]];
+      }
+      q_cols();
+    }
     if (tid < BM) {
       const int64_t hs = qcap * e.kv.dh;   // one head of one slot
       const int slot = e.kv.s0 + e.kv.s1 * qri[2];
       q_kb[tid] = qoff + (int64_t)(slot * 2) * e.kv.H * hs + (int64_t)qri[1] * e.kv.dh;
       q_hs[tid] = hs;
-      q_ok[tid] = m0 + tid < M && !(e.skip_done && qri[3]);
+      q_pos[tid] = (m0 + tid < M && !(e.skip_done && qri[3])) ? qri[1] : -1;
     }
     __syncthreads();
+    if constexpr (!QPRE) {
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) q_rope(i, r, q_pos[wm * WTM + i * 16 + lr + r]);
+    }
     const int d = e.d, dh = e.dh, G = e.pair_g, half = dh >> 1;
     AT* const kv = reinterpret_cast<AT*>(e.kv.base);
 #pragma unroll
@@ -391,7 +413,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int lrow = wm * WTM + i * 16 + lr + r, row = m0 + lrow;
-        if (!q_ok[lrow]) continue;
+        if (q_pos[lrow] < 0) continue;
         const int64_t hs = q_hs[lrow], kbase = q_kb[lrow], vbase = kbase + e.kv.H * hs;
 #pragma unroll
         for (int jp = 0; jp < QJ; ++jp) {
@@ -751,6 +773,8 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
     const int row = (int)(idx / per_row);
     const int p = (int)(idx - (int64_t)row * per_row);
     const int c = (p / G) * 2 * G + (p % G);
+    QkvRow qr{};
+    if constexpr (KIND == EPI_QKV) qr = qkv_row(e, row);   // read with the partials
     float v0 = 0.f, v1 = 0.f;
     for (int z = 0; z < S; ++z) {
       const float* pr = g.partial + ((int64_t)z * M + row) * N;
@@ -758,7 +782,8 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
       v1 += pr[c + G];
     }
     if (gate_closed(g.live)) return;
-    epi_pair<AT, KIND>(e, row, c, v0, v1);
+    if constexpr (KIND == EPI_QKV) qkv_put<AT>(e, qkv_prep(e, qr, row, c), v0, v1);
+    else epi_pair<AT, KIND>(e, row, c, v0, v1);
   } else {
     if (idx >= (int64_t)M * N) return;
     const int row = (int)(idx / N);

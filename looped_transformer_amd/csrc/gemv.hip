@@ -129,6 +129,7 @@ __device__ __forceinline__ void gemv_stage_x(const GemmArgs& g, f16* xs) {
 
 // The epilogue for row m, called by threads holding one output column each; for
 // the paired kinds these are lanes 0..31 of wave 0 (a pair lies 16 columns apart).
+// (QKV calls qkv_put instead, with its operands gathered ahead of the product.)
 template <int KIND>
 __device__ __forceinline__ void gemv_epilogue(const GemmEpi& e, int m, int col, float v) {
   if constexpr (paired(KIND)) {
@@ -160,6 +161,17 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(GemmArgs g, GemmEpi e)
   // requested before anything waits
   u32x4 w[D][2];
   uint16_t sc[D];
+  // QKV: the epilogue lanes (wave 0, lanes 0..15: the first columns of the
+  // pairs) read their rows' cache coordinates before the weights are requested
+  constexpr int QR = KIND == EPI_QKV ? M : 1;
+  QkvRow qrow[QR];
+  QkvPrep qp[QR];
+  if constexpr (KIND == EPI_QKV) {
+    if (wave == 0 && lane < 16) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) qrow[m] = qkv_row(e, min(m, g.M - 1));
+    }
+  }
 #pragma unroll
   for (int j = 0; j < D; ++j) {
     const int gi = wave + j * NW;
@@ -174,6 +186,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(GemmArgs g, GemmEpi e)
   }
   if (gate_closed(g.live)) return;   // whole workgroup: no barrier passed yet
   gemv_stage_x<M, NW>(g, xs);
+  if constexpr (KIND == EPI_QKV) {   // slot tables and rotary factors: in flight during the product
+    if (wave == 0 && lane < 16) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) qp[m] = qkv_prep(e, qrow[m], m, col);
+    }
+  }
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
@@ -227,7 +245,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_w4_kernel(GemmArgs g, GemmEpi e)
 #pragma unroll
     for (int w2 = 0; w2 < NW; ++w2) v += red[w2][m][r];
     if (m >= g.M) continue;
-    gemv_epilogue<KIND>(e, m, col, v);
+    if constexpr (KIND == EPI_QKV) {
+      const float v1 = __shfl_down(v, 16, 32);   // column col + 16 of the pair
+      if (r < 16) qkv_put<f16>(e, qp[m], v, v1);
+    } else {
+      gemv_epilogue<KIND>(e, m, col, v);
+    }
   }
 }
 
@@ -249,6 +272,18 @@ __global__ __launch_bounds__(NW * 64) void gemv_f16_kernel(GemmArgs g, GemmEpi e
   const f16* wr = reinterpret_cast<const f16*>(g.B) + (int64_t)row * K + 8 * kl;
   const int nc = K / 64;   // chunks per row
   u32x4 w[U];   // slot j: chunk kp + (j0 + j) KS
+  // QKV (R = 32): the epilogue threads 0..15 handle the column pairs; their rows'
+  // cache coordinates are read first, the rest once the weights are requested
+  constexpr int QR = KIND == EPI_QKV ? M : 1;
+  QkvRow qrow[QR];
+  QkvPrep qp[QR];
+  if constexpr (KIND == EPI_QKV) {
+    static_assert(R == 32, "paired epilogue: a pair lies 16 columns apart");
+    if (tid < 16) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) qrow[m] = qkv_row(e, min(m, g.M - 1));
+    }
+  }
 #pragma unroll
   for (int j = 0; j < U; ++j) {
     const int c = kp + j * KS;
@@ -256,6 +291,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_f16_kernel(GemmArgs g, GemmEpi e
   }
   if (gate_closed(g.live)) return;
   gemv_stage_x<M, NW>(g, xs);
+  if constexpr (KIND == EPI_QKV) {
+    if (tid < 16) {
+#pragma unroll
+      for (int m = 0; m < M; ++m) qp[m] = qkv_prep(e, qrow[m], m, nb * R + tid);
+    }
+  }
   float acc[M];
 #pragma unroll
   for (int m = 0; m < M; ++m) acc[m] = 0.f;
@@ -293,7 +334,12 @@ __global__ __launch_bounds__(NW * 64) void gemv_f16_kernel(GemmArgs g, GemmEpi e
 #pragma unroll
     for (int q = 0; q < KS; ++q) v += red[q][tid][m];
     if (m >= g.M) continue;
-    gemv_epilogue<KIND>(e, m, nb * R + tid, v);
+    if constexpr (KIND == EPI_QKV) {
+      const float v1 = __shfl_down(v, 16, 32);   // column + 16 of the pair
+      if (tid < 16) qkv_put<f16>(e, qp[m], v, v1);
+    } else {
+      gemv_epilogue<KIND>(e, m, nb * R + tid, v);
+    }
   }
 }
 
