@@ -203,8 +203,15 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
   const int slot = kv.s0 + kv.s1 * tile.iter;
-  const int64_t cap = kv.lane_cap[tile.lane];
-  const T* Kg = reinterpret_cast<const T*>(kv.base) + kv.lane_off[tile.lane] + ((int64_t)(slot * 2) * kv.H + h) * cap * DH;
+  int64_t cap, koff;
+  if (tile.cap > 0) {   // carried by the descriptor: one round of dependent loads less
+    cap = tile.cap;
+    koff = tile.koff;
+  } else {
+    cap = kv.lane_cap[tile.lane];
+    koff = kv.lane_off[tile.lane];
+  }
+  const T* Kg = reinterpret_cast<const T*>(kv.base) + koff + ((int64_t)(slot * 2) * kv.H + h) * cap * DH;
   const T* Vg = Kg + (int64_t)kv.H * cap * DH;
   const int kend = tile.pos0 + tile.nrows;
 

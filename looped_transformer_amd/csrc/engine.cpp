@@ -595,9 +595,12 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
 }
 
 // Attention tiles of one iteration: sequences still active, in caller order, each
-// cut into runs of at most attn_tile_rows() consecutive rows.
+// cut into runs of at most attn_tile_rows() consecutive rows.  With lane_off /
+// lane_cap (indexed like seq_lane) the tiles carry the lanes' slot offsets, which
+// must then be the ones of the KVParams the attention runs with.
 void add_tiles(std::vector<AttnTile>& out, const std::vector<int>& seq_len, const std::vector<int>& seq_lane,
-               const std::vector<int>& Ls, int j, const std::vector<int>* start = nullptr) {
+               const std::vector<int>& Ls, int j, const std::vector<int>* start = nullptr,
+               const std::vector<int64_t>* lane_off = nullptr, const std::vector<int32_t>* lane_cap = nullptr) {
   const int tr = attn_tile_rows();
   int row = 0;
   for (size_t sq = 0; sq < seq_len.size(); ++sq) {
@@ -609,6 +612,10 @@ void add_tiles(std::vector<AttnTile>& out, const std::vector<int>& seq_len, cons
       t.pos0 = (start ? (*start)[sq] : 0) + p0;
       t.lane = seq_lane[sq];
       t.iter = j;
+      if (lane_off && lane_cap) {
+        t.cap = (*lane_cap)[t.lane];
+        t.koff = (*lane_off)[t.lane];
+      }
       out.push_back(t);
     }
     row += seq_len[sq];
@@ -1146,7 +1153,9 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   if (tiled)
     for (size_t j = 1; j <= n_act.size(); ++j) {
       tile_lists.emplace_back();
-      add_tiles(tile_lists.back(), slen, slane, Ls, (int)j);
+      // scoring passes attend in the pass's own scratch (soff / scap by sequence)
+      add_tiles(tile_lists.back(), slen, slane, Ls, (int)j, nullptr, lanes ? nullptr : &soff,
+                lanes ? nullptr : &scap);
     }
   Stage st;
   std::vector<size_t> o_tiles;

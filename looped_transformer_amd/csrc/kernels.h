@@ -95,10 +95,14 @@ hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const i
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv,
                             void* out, const int32_t* live, int max_ctx, hipStream_t s);
 // A run of up to attn_tile_rows() consecutive rows of one sequence (positions pos0 .. pos0+nrows-1)
-// that attend to positions 0 .. pos0+nrows-1 of their lane's slot.
+// that attend to positions 0 .. pos0+nrows-1 of their lane's slot.  cap > 0: the lane's slot-0
+// offset (koff) and capacity are carried here, so the kernel need not read the lane tables;
+// cap == 0: read them from the KVParams tables.
 struct AttnTile {
-  int32_t row0, nrows, pos0, lane, iter, p0, p1, p2;
+  int32_t row0, nrows, pos0, lane, iter, cap;
+  int64_t koff;
 };
+static_assert(sizeof(AttnTile) == 32, "descriptor layout");
 // Tiled causal attention (MFMA) for prefill / scoring passes; 16-bit types and
 // head_dim in {64, 96, 128} only (attn_tiled_supported).  A tile holds at most
 // attn_tile_rows() consecutive rows.
