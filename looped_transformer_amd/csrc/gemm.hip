@@ -806,9 +806,17 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
   float* hr = e.h + (int64_t)row * e.ldh;
   const floatx4* P = reinterpret_cast<const floatx4*>(g.partial);
   const int64_t zs = (int64_t)M * N / 4, rs = (int64_t)row * N / 4;
-  floatx4 acc[VPT];
+  floatx4 acc[VPT], hv0[VPT], gv[VPT];
 #pragma unroll
   for (int u = 0; u < VPT; ++u) acc[u] = floatx4{0.f, 0.f, 0.f, 0.f};
+  // the residual row and the norm gain are requested with the partials: one round
+  // of loads before the sums instead of three
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int c4 = min((int)threadIdx.x + 256 * u, N / 4 - 1);
+    hv0[u] = *reinterpret_cast<const floatx4*>(hr + 4 * c4);
+    gv[u] = *reinterpret_cast<const floatx4*>(e.norm_g + 4 * c4);
+  }
   if constexpr (SN > 0) {
     floatx4 p[SN][VPT];
 #pragma unroll
@@ -835,7 +843,7 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
   for (int u = 0; u < VPT; ++u) {
     const int c4 = (int)threadIdx.x + 256 * u;
     if (c4 * 4 < N) {
-      const floatx4 hv = *reinterpret_cast<const floatx4*>(hr + 4 * c4) + acc[u];
+      const floatx4 hv = hv0[u] + acc[u];
       *reinterpret_cast<floatx4*>(hr + 4 * c4) = hv;
       acc[u] = hv;
       ss = fmaf(hv[0], hv[0], fmaf(hv[1], hv[1], fmaf(hv[2], hv[2], fmaf(hv[3], hv[3], ss))));
@@ -852,7 +860,7 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
   for (int u = 0; u < VPT; ++u) {
     const int c4 = (int)threadIdx.x + 256 * u;
     if (c4 * 4 < N) {
-      const floatx4 gg = *reinterpret_cast<const floatx4*>(e.norm_g + 4 * c4);
+      const floatx4 gg = gv[u];
 #pragma unroll
       for (int q = 0; q < 4; ++q) o[4 * c4 + q] = from_f32<AT>(acc[u][q] * inv * gg[q]);
     }
