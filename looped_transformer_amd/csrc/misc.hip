@@ -22,34 +22,75 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E, con
 }
 
 // ---------------------------------------------------------------- RMSNorm
-// x = h / sqrt(mean(h^2) + eps) * g, one wave per row; fp32 statistics.
+// x = h / sqrt(mean(h^2) + eps) * g, one wave per row; fp32 statistics.  With
+// VPT > 0 (d <= 256 VPT) a lane keeps its VPT groups of 4 values and gains in
+// registers: the row and the gain are requested in one round, and each group
+// leaves in one 8- or 16-byte store.  VPT = 0 serves any d (multiple of 4),
+// reading the row twice.
 template <class T>
+__device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
+  if constexpr (sizeof(T) == 4) {
+    *reinterpret_cast<float4*>(p) = make_float4(a, b, c, d);
+  } else {
+    const T t[4] = {from_f32<T>(a), from_f32<T>(b), from_f32<T>(c), from_f32<T>(d)};
+    uint2 u;
+    __builtin_memcpy(&u, t, sizeof(u));
+    *reinterpret_cast<uint2*>(p) = u;
+  }
+}
+
+template <class T, int VPT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, const float* __restrict__ g,
                                                      const int32_t* __restrict__ gather, int n, int d, float eps,
                                                      T* __restrict__ out) {
   const int lane = threadIdx.x & 63;
   const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (r >= n) return;
-  const int src = gather ? gather[r] : r;
-  const float* hr = h + (int64_t)src * d;
-  float ss = 0.f;
-  for (int i = lane * 4; i < d; i += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(hr + i);
-    ss = fmaf(v.x, v.x, ss);
-    ss = fmaf(v.y, v.y, ss);
-    ss = fmaf(v.z, v.z, ss);
-    ss = fmaf(v.w, v.w, ss);
-  }
-  ss = wave_sum(ss);
-  const float inv = 1.0f / sqrtf(ss / (float)d + eps);
   T* o = out + (int64_t)r * d;
-  for (int i = lane * 4; i < d; i += 256) {
-    const float4 v = *reinterpret_cast<const float4*>(hr + i);
-    const float4 gg = *reinterpret_cast<const float4*>(g + i);
-    o[i] = from_f32<T>(v.x * inv * gg.x);
-    o[i + 1] = from_f32<T>(v.y * inv * gg.y);
-    o[i + 2] = from_f32<T>(v.z * inv * gg.z);
-    o[i + 3] = from_f32<T>(v.w * inv * gg.w);
+  if constexpr (VPT > 0) {
+    float4 gg[VPT], v[VPT];
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) gg[u] = *reinterpret_cast<const float4*>(g + min(lane * 4 + 256 * u, d - 4));
+    const int src = gather ? gather[r] : r;
+    const float* hr = h + (int64_t)src * d;
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) v[u] = *reinterpret_cast<const float4*>(hr + min(lane * 4 + 256 * u, d - 4));
+    float ss = 0.f;
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      if (lane * 4 + 256 * u < d) {
+        ss = fmaf(v[u].x, v[u].x, ss);
+        ss = fmaf(v[u].y, v[u].y, ss);
+        ss = fmaf(v[u].z, v[u].z, ss);
+        ss = fmaf(v[u].w, v[u].w, ss);
+      }
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int u = 0; u < VPT; ++u) {
+      const int i = lane * 4 + 256 * u;
+      if (i < d)
+        store4(o + i, v[u].x * inv * gg[u].x, v[u].y * inv * gg[u].y, v[u].z * inv * gg[u].z, v[u].w * inv * gg[u].w);
+    }
+  } else {
+    const int src = gather ? gather[r] : r;
+    const float* hr = h + (int64_t)src * d;
+    float ss = 0.f;
+    for (int i = lane * 4; i < d; i += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(hr + i);
+      ss = fmaf(v.x, v.x, ss);
+      ss = fmaf(v.y, v.y, ss);
+      ss = fmaf(v.z, v.z, ss);
+      ss = fmaf(v.w, v.w, ss);
+    }
+    ss = wave_sum(ss);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int i = lane * 4; i < d; i += 256) {
+      const float4 v = *reinterpret_cast<const float4*>(hr + i);
+      const float4 gg = *reinterpret_cast<const float4*>(g + i);
+      store4(o + i, v.x * inv * gg.x, v.y * inv * gg.y, v.z * inv * gg.z, v.w * inv * gg.w);
+    }
   }
 }
 
@@ -522,13 +563,27 @@ hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, 
 hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const int32_t* gather, int n, int d, float eps,
                           void* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
+  if (d < 4 || (d % 4) != 0) return hipErrorInvalidValue;
   dim3 grid((n + 3) / 4);
+  const int vpt = d <= 256 ? 1 : d <= 512 ? 2 : d <= 1024 ? 4 : d <= 2048 ? 8 : 0;
+#define TL_RMS(T, V)                                                                                          \
+  hipLaunchKernelGGL((rmsnorm_kernel<T, V>), grid, dim3(256), 0, s, h, g, gather, n, d, eps, (T*)out)
+#define TL_RMS_T(T)                      \
+  switch (vpt) {                         \
+    case 1: TL_RMS(T, 1); break;         \
+    case 2: TL_RMS(T, 2); break;         \
+    case 4: TL_RMS(T, 4); break;         \
+    case 8: TL_RMS(T, 8); break;         \
+    default: TL_RMS(T, 0); break;        \
+  }
   switch (out_dtype) {
-    case DT_F32: hipLaunchKernelGGL(rmsnorm_kernel<float>, grid, dim3(256), 0, s, h, g, gather, n, d, eps, (float*)out); break;
-    case DT_F16: hipLaunchKernelGGL(rmsnorm_kernel<f16>, grid, dim3(256), 0, s, h, g, gather, n, d, eps, (f16*)out); break;
-    case DT_BF16: hipLaunchKernelGGL(rmsnorm_kernel<bf16>, grid, dim3(256), 0, s, h, g, gather, n, d, eps, (bf16*)out); break;
+    case DT_F32: TL_RMS_T(float) break;
+    case DT_F16: TL_RMS_T(f16) break;
+    case DT_BF16: TL_RMS_T(bf16) break;
     default: return hipErrorInvalidValue;
   }
+#undef TL_RMS_T
+#undef TL_RMS
   return hipGetLastError();
 }
 
