@@ -510,7 +510,11 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     TRY(plan_hpass(m, p, hps, s));
     m->hpass = &hps;
   }
-  TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, w.hA, m->d_err, c.vocab, s)));
+  // the first pre block's norm is formed with the gather (x_ready)
+  bool x_ready = false;
+  TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, w.hA, m->d_err, c.vocab, s,
+                                        c.n_pre > 0 ? m->blocks[0].norm1 : nullptr, c.rms_eps, m->act, w.x16,
+                                        &x_ready)));
   KVParams kv = p.kv;
   kv.s1 = 0;
   const AttnTile* t0 = tiled ? p.tiles[0] : nullptr;
@@ -518,7 +522,6 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   const int Lmax = (int)p.n_active.size();
   // norm gain of the first block after pre block b / loop layer l on the same rows
   auto loop_first = [&]() { return m->blocks[c.n_pre].norm1; };
-  bool x_ready = false;
   for (int b = 0; b < c.n_pre; ++b) {
     kv.s0 = p.scoring ? 0 : b;
     const float* nn = b + 1 < c.n_pre ? m->blocks[b + 1].norm1 : (Lmax > 0 ? loop_first() : nullptr);

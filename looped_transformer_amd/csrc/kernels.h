@@ -85,8 +85,11 @@ struct GemmEpi {
 int gemm_head_tiles(int act_dtype, int M, int N);
 hipError_t launch_gemm(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s);
 
+// With norm_g, x and x_done set (and d a multiple of 4 up to 8192), the gather also
+// writes x = RMSNorm(h) * norm_g in x_dtype and sets *x_done.
 hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, int d, float* h,
-                        int32_t* err_flag, int vocab, hipStream_t s);
+                        int32_t* err_flag, int vocab, hipStream_t s, const float* norm_g = nullptr, float eps = 0.f,
+                        int x_dtype = 0, void* x = nullptr, bool* x_done = nullptr);
 hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const int32_t* gather, int n,
                           int d, float eps, void* out, hipStream_t s);
 // live: as GemmArgs::live (NULL: always run).  Rows marked done get a zero output.

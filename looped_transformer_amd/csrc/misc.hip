@@ -94,6 +94,61 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ 
   }
 }
 
+// Embedding gather fused with the first block's RMSNorm: one workgroup per row
+// keeps its 4 VPT-wide groups (d <= 1024 VPT) in registers, writes h and then
+// x = h / sqrt(mean(h^2) + eps) * g (fp32 statistics, a fixed-order workgroup sum)
+// in the operand type, saving the norm kernel's launch and its read of h.
+template <class T>
+__device__ __forceinline__ float4 load4(const T* p) {
+  if constexpr (sizeof(T) == 4) {
+    return *reinterpret_cast<const float4*>(p);
+  } else {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    T t[4];
+    __builtin_memcpy(t, &u, sizeof(u));
+    return make_float4((float)t[0], (float)t[1], (float)t[2], (float)t[3]);
+  }
+}
+
+template <class T, class X, int VPT>
+__global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ E, const int32_t* __restrict__ tokens,
+                                                        int d, float* __restrict__ h, int32_t* err, int vocab,
+                                                        const float* __restrict__ g, float eps, X* __restrict__ x) {
+  const int r = blockIdx.x, tid = threadIdx.x;
+  float4 gg[VPT], v[VPT];
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) gg[u] = *reinterpret_cast<const float4*>(g + min(4 * (tid + 256 * u), d - 4));
+  int tok = tokens[r];
+  if (tok < 0 || tok >= vocab) {
+    if (tid == 0 && err) atomicOr(err, 1);
+    tok = 0;
+  }
+  const T* src = E + (int64_t)tok * d;
+  float* dst = h + (int64_t)r * d;
+  float ss = 0.f;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int i = 4 * (tid + 256 * u);
+    v[u] = load4(src + min(i, d - 4));
+    if (i < d) {
+      *reinterpret_cast<float4*>(dst + i) = v[u];
+      ss = fmaf(v[u].x, v[u].x, fmaf(v[u].y, v[u].y, fmaf(v[u].z, v[u].z, fmaf(v[u].w, v[u].w, ss))));
+    }
+  }
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((tid & 63) == 0) red[tid >> 6] = ss;
+  __syncthreads();
+  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+  X* xo = x + (int64_t)r * d;
+#pragma unroll
+  for (int u = 0; u < VPT; ++u) {
+    const int i = 4 * (tid + 256 * u);
+    if (i < d)
+      store4(xo + i, v[u].x * inv * gg[u].x, v[u].y * inv * gg[u].y, v[u].z * inv * gg[u].z, v[u].w * inv * gg[u].w);
+  }
+}
+
 // ---------------------------------------------------------------- compaction
 // Stable filter in one workgroup: chunks of 1024 rows, wave ballots + prefix.
 __global__ __launch_bounds__(1024) void compact_kernel(const RowInfo* __restrict__ in, int n, int it,
@@ -548,9 +603,47 @@ __global__ __launch_bounds__(256) void w4_export_kernel(const uint32_t* __restri
 
 }  // namespace
 
+template <class T>
+hipError_t embed_norm_x(const T* E, const int32_t* tokens, int n, int d, float* h, int32_t* err, int vocab,
+                        const float* g, float eps, int x_dtype, void* x, hipStream_t s) {
+  const int vpt = (d + 1023) / 1024;
+#define TL_EN(X, V)                                                                                        \
+  hipLaunchKernelGGL((embed_norm_kernel<T, X, V>), dim3(n), dim3(256), 0, s, E, tokens, d, h, err, vocab, g, eps, \
+                     (X*)x)
+#define TL_EN_X(X)                 \
+  switch (vpt) {                   \
+    case 1: TL_EN(X, 1); break;    \
+    case 2: TL_EN(X, 2); break;    \
+    case 3:                        \
+    case 4: TL_EN(X, 4); break;    \
+    default: TL_EN(X, 8); break;   \
+  }
+  switch (x_dtype) {
+    case DT_F32: TL_EN_X(float) break;
+    case DT_F16: TL_EN_X(f16) break;
+    case DT_BF16: TL_EN_X(bf16) break;
+    default: return hipErrorInvalidValue;
+  }
+#undef TL_EN_X
+#undef TL_EN
+  return hipGetLastError();
+}
+
 hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, int d, float* h, int32_t* err,
-                        int vocab, hipStream_t s) {
+                        int vocab, hipStream_t s, const float* norm_g, float eps, int x_dtype, void* x, bool* x_done) {
+  if (x_done) *x_done = false;
   if (n <= 0) return hipSuccess;
+  if (norm_g && x && x_done && d >= 4 && (d % 4) == 0 && d <= 8192) {
+    hipError_t err2 = hipErrorInvalidValue;
+    switch (dtype) {
+      case DT_F32: err2 = embed_norm_x<float>((const float*)E, tokens, n, d, h, err, vocab, norm_g, eps, x_dtype, x, s); break;
+      case DT_F16: err2 = embed_norm_x<f16>((const f16*)E, tokens, n, d, h, err, vocab, norm_g, eps, x_dtype, x, s); break;
+      case DT_BF16: err2 = embed_norm_x<bf16>((const bf16*)E, tokens, n, d, h, err, vocab, norm_g, eps, x_dtype, x, s); break;
+      default: break;
+    }
+    if (err2 == hipSuccess) *x_done = true;
+    return err2;
+  }
   switch (dtype) {
     case DT_F32: hipLaunchKernelGGL(embed_kernel<float>, dim3(n), dim3(256), 0, s, (const float*)E, tokens, d, h, err, vocab); break;
     case DT_F16: hipLaunchKernelGGL(embed_kernel<f16>, dim3(n), dim3(256), 0, s, (const f16*)E, tokens, d, h, err, vocab); break;
