@@ -14,6 +14,10 @@
  *   - stream is a hipStream_t (NULL = the null stream).  Calls enqueue device work
  *     on it and return without waiting; device outputs are valid once the stream
  *     has reached that point.  Host outputs are written before the call returns.
+ *     Calls of one model may use different streams: a call on a stream other than
+ *     the previous call's first makes its stream wait for the work the previous
+ *     call enqueued (the model's staging area and workspaces are shared), so the
+ *     previous call's stream must not have been destroyed.
  *   - On any status other than TL_OK nothing has been enqueued and the model and
  *     its lanes are unchanged (validation happens before any device work), except
  *     TL_E_HIP, which reports a failed HIP call; tl_last_error() gives the reason.

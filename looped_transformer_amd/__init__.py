@@ -195,7 +195,9 @@ def tl_load_weights(cfg: tl_config, embed, head, final_norm, blocks, stream=None
         arr[i] = tl_block_weights(**fields)
     head_ptr = keep[0].ctypes.data if head is embed else keep[1].ctypes.data
     w = tl_weights(keep[0].ctypes.data, head_ptr, keep[2].ctypes.data, arr)
-    alloc = TorchAllocator() if allocator == "torch" else None
+    # "torch": torch's caching allocator; None: hipMalloc; or an object with
+    # alloc_cb / free_cb (e.g. a TorchAllocator subclass)
+    alloc = TorchAllocator() if isinstance(allocator, str) and allocator == "torch" else allocator
     out = _P()
     st = lib().tl_load_weights(ctypes.byref(cfg), ctypes.byref(w),
                                alloc.alloc_cb if alloc else ALLOC_FN(0), alloc.free_cb if alloc else DEALLOC_FN(0),

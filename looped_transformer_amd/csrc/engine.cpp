@@ -92,21 +92,40 @@ void drop_graphs(tl_model* m) {
   m->graphs.clear();
 }
 
+// The staging area, the workspaces and the lane tables are shared by every call.
+// Before a call enqueues work on a stream other than the previous call's, that
+// stream waits for everything the previous call enqueued (which may still read
+// them).  The previous call's stream must still exist.
+tl_status stream_handover(tl_model* m, hipStream_t s) {
+  if (m->has_last_stream && m->last_stream != s) {
+    HIPCHK(hipEventRecord(m->handover, m->last_stream));
+    HIPCHK(hipStreamWaitEvent(s, m->handover, 0));
+  }
+  m->last_stream = s;
+  m->has_last_stream = true;
+  return TL_OK;
+}
+
 tl_status stage_upload(tl_model* m, const Stage& st, hipStream_t s) {
+  TRY(stream_handover(m, s));
   const size_t need = std::max<size_t>(st.buf.size(), 256);
   if (need > m->stage_bytes) {
     if (m->stage_host) {
       HIPCHK(hipStreamSynchronize(s));
-      if (m->last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
       HIPCHK(hipHostFree(m->stage_host));
       m->stage_host = nullptr;
       dev_free(m, m->stage_dev);
       m->stage_dev = nullptr;
+      m->stage_bytes = 0;
     }
     size_t cap = std::max<size_t>(need * 2, 1 << 20);
     HIPCHK(hipHostMalloc(&m->stage_host, cap, hipHostMallocDefault));
     m->stage_dev = dev_alloc(m, cap);
-    if (!m->stage_dev) return fail(TL_E_OOM, "staging area of %zu bytes", cap);
+    if (!m->stage_dev) {
+      (void)hipHostFree(m->stage_host);
+      m->stage_host = nullptr;
+      return fail(TL_E_OOM, "staging area of %zu bytes", cap);
+    }
     m->stage_bytes = cap;
   } else {
     HIPCHK(hipEventSynchronize(m->stage_done));
@@ -114,7 +133,6 @@ tl_status stage_upload(tl_model* m, const Stage& st, hipStream_t s) {
   std::memcpy(m->stage_host, st.buf.data(), st.buf.size());
   HIPCHK(hipMemcpyAsync(m->stage_dev, m->stage_host, st.buf.size(), hipMemcpyHostToDevice, s));
   HIPCHK(hipEventRecord(m->stage_done, s));
-  m->last_stream = s;
   return TL_OK;
 }
 
@@ -128,11 +146,16 @@ tl_status aux_upload(tl_model* m, const Stage& st, hipStream_t s) {
       m->aux_host = nullptr;
       dev_free(m, m->aux_dev);
       m->aux_dev = nullptr;
+      m->aux_bytes = 0;
     }
     size_t cap = std::max<size_t>(need * 2, 1 << 20);
     HIPCHK(hipHostMalloc(&m->aux_host, cap, hipHostMallocDefault));
     m->aux_dev = dev_alloc(m, cap);
-    if (!m->aux_dev) return fail(TL_E_OOM, "staging area of %zu bytes", cap);
+    if (!m->aux_dev) {
+      (void)hipHostFree(m->aux_host);
+      m->aux_host = nullptr;
+      return fail(TL_E_OOM, "staging area of %zu bytes", cap);
+    }
     m->aux_bytes = cap;
   } else {
     HIPCHK(hipEventSynchronize(m->aux_done));
@@ -168,7 +191,7 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
   const int O = std::max(w.outs, (outs + 63) / 64 * 64);
   const int64_t KS = std::max(w.kv_scratch_elems, kv_scratch);
   HIPCHK(hipStreamSynchronize(s));
-  if (m->last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
+  if (m->has_last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
   drop_graphs(m);
   void* olds[] = {w.hA, w.hB, w.hX, w.hE, w.x16, w.q16, w.o16, w.u16, w.xh, w.rowsA, w.rowsB,
                   w.dest, w.count, w.tok, w.tok2, w.part_v, w.part_i, w.part_v2, w.kv_scratch, w.splitk};
@@ -989,6 +1012,7 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   LHIP(hipMemsetAsync(m->d_err, 0, 256, s));
   LHIP(hipEventCreateWithFlags(&m->stage_done, hipEventDisableTiming));
   LHIP(hipEventCreateWithFlags(&m->aux_done, hipEventDisableTiming));
+  LHIP(hipEventCreateWithFlags(&m->handover, hipEventDisableTiming));
   LHIP(hipStreamSynchronize(s));
   *out = m;
   return TL_OK;
@@ -1008,6 +1032,7 @@ void tl_free(tl_model* m) {
   if (m->sp_acc_host) (void)hipHostFree(m->sp_acc_host);
   if (m->stage_done) (void)hipEventDestroy(m->stage_done);
   if (m->aux_done) (void)hipEventDestroy(m->aux_done);
+  if (m->handover) (void)hipEventDestroy(m->handover);
   if (m->aux_host) (void)hipHostFree(m->aux_host);
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
   delete m;
@@ -1036,6 +1061,7 @@ tl_status tl_sync_errors(tl_model* m, void* stream) {
   if (!m) return fail(TL_E_ARG, "NULL model");
   hipStream_t s = static_cast<hipStream_t>(stream);
   int32_t flag = 0;
+  TRY(stream_handover(m, s));
   HIPCHK(hipStreamSynchronize(s));
   HIPCHK(hipMemcpy(&flag, m->d_err, 4, hipMemcpyDeviceToHost));
   if (flag) {
@@ -1100,6 +1126,7 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   const bool graphable = !lanes && s != nullptr && !m->timing;
   std::vector<int64_t> key;
   if (graphable) {
+    TRY(stream_handover(m, s));
     key = {n_seqs, (int64_t)(intptr_t)tokens, (int64_t)(intptr_t)out_hidden, (int64_t)(intptr_t)out_logits,
            (int64_t)(intptr_t)out_next, (int64_t)(intptr_t)out_log, (int64_t)(intptr_t)s};
     for (int i = 0; i <= n_seqs; ++i) key.push_back(cu[i]);

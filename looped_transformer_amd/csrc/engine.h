@@ -125,7 +125,11 @@ struct tl_model {
   void* stage_dev = nullptr;
   size_t stage_bytes = 0;
   hipEvent_t stage_done = nullptr;
+  // stream of the previous call (valid once has_last_stream); a call on another
+  // stream first waits for it through `handover`
   hipStream_t last_stream = nullptr;
+  bool has_last_stream = false;
+  hipEvent_t handover = nullptr;
   // second upload channel (store-h rebuild lists, planned inside a pass)
   void* aux_host = nullptr;
   void* aux_dev = nullptr;

@@ -1,6 +1,7 @@
-"""Test and benchmark helpers: map synthetic model specs onto the C ABI structs.
+"""Test and benchmark helpers: map synthetic model specs onto the C ABI structs,
+and compare device outputs with the oracle's.
 
-Marshalling only; no model arithmetic happens here.
+Marshalling and comparison only; no model arithmetic happens here.
 """
 from __future__ import annotations
 
@@ -60,3 +61,25 @@ def rel_l2(a, b) -> float:
     a = np.asarray(a, dtype=np.float64)
     b = np.asarray(b, dtype=np.float64)
     return float(np.linalg.norm(a - b) / np.linalg.norm(b))
+
+
+def row_rel_max(a, b) -> float:
+    """Largest per-row relative L2 error over the rows of [rows, d] arrays."""
+    a = np.asarray(a, dtype=np.float64).reshape(-1, np.shape(b)[-1])
+    b = np.asarray(b, dtype=np.float64).reshape(-1, np.shape(b)[-1])
+    return float(np.max(np.linalg.norm(a - b, axis=1) / np.linalg.norm(b, axis=1)))
+
+
+def near_tie_gaps(got_tokens, ref_logits) -> list:
+    """For each token where the device's greedy choice differs from the oracle's,
+    the oracle's own logit gap between its best token and the device's token, in
+    units of the row's rms logit.  An empty list means every token agreed."""
+    lg = np.asarray(ref_logits, dtype=np.float64).reshape(len(got_tokens), -1)
+    got = np.asarray(got_tokens, dtype=np.int64)
+    import oracle
+    top = oracle.greedy_argmax(lg)
+    gaps = []
+    for t in np.nonzero(top != got)[0]:
+        row = lg[t]
+        gaps.append(float((row[top[t]] - row[got[t]]) / np.sqrt(np.mean(row * row))))
+    return gaps

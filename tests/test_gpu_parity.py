@@ -12,7 +12,7 @@ import pytest
 
 import oracle
 import synth
-from tests.harness import ensure_built, kv_bytes, load_model, rel_l2
+from tests.harness import ensure_built, kv_bytes, load_model, near_tie_gaps, rel_l2, row_rel_max
 
 torch = pytest.importorskip("torch")
 import looped_transformer_amd as tl  # noqa: E402
@@ -88,11 +88,69 @@ def test_tiny_forward_parity(name):
     off = 0
     for i, s in enumerate(seqs):
         r = rel_l2(hid[off:off + len(s)], ref_h[off:off + len(s)])
-        say(name, "seq", i, "L", Ls[i], "rel", r)
+        rm = row_rel_max(hid[off:off + len(s)], ref_h[off:off + len(s)])
+        say(name, "seq", i, "L", Ls[i], "rel %.2e row max %.2e" % (r, rm))
         assert r <= hidden_bar(spec, Ls[i]), (i, r)
+        assert rm <= hidden_bar(spec, Ls[i]), (i, rm)
         off += len(s)
     assert rel_l2(lg, ref_lg) <= (1e-4 if spec.boundary_dtype == "f32" else 1e-2)
-    assert np.array_equal(nxt, oracle.greedy_argmax(ref_lg)) or np.mean(nxt == oracle.greedy_argmax(ref_lg)) >= 0.75
+    if spec.boundary_dtype == "f32":
+        assert np.array_equal(nxt, oracle.greedy_argmax(ref_lg))
+    else:
+        # 16-bit operands: a token may differ only where the oracle's own best two
+        # logits nearly tie (within 5 % of the row's rms logit)
+        gaps = near_tie_gaps(nxt, ref_lg)
+        say(name, "differing greedy tokens, gaps x rms:", gaps)
+        assert all(g <= 0.05 for g in gaps), gaps
+
+
+@pytest.mark.parametrize("name", ["tiny-f32", "tiny-f16", "tiny-bf16-stack"])
+def test_greedy_ties_take_lowest_index(name):
+    """Head rows 37, 40 and 200 are one vector v, every other row is zero, so the
+    logits of those three tokens are equal bit for bit and the rest are exactly 0.
+    v points along the prefill's last normalised hidden state, so the three tie at
+    the maximum there and the greedy token must be 37 (the tie spans head tiles).
+    The decode step's logits tie either at 37 (positive) or among the zero rows
+    (lowest index 0)."""
+    spec = TINY[name]
+    w = synth.make_weights(spec, seed=11)
+    m = oracle.OracleModel.from_weights(w)
+    toks = synth.tokens(11, 7000, 10, spec.vocab)
+    _, ref_h, _ = oracle.prefill(m, toks, 2, want_logits="none")
+    x = oracle.rmsnorm(ref_h[-1:], m.final_norm, spec.rms_eps)[0]
+    v = (0.05 * x / np.linalg.norm(x)).astype(np.float32)
+    head = np.zeros((spec.vocab, spec.d_model), np.float32)
+    for r in (37, 40, 200):
+        head[r] = v
+    if spec.boundary_dtype == "f16":
+        head = head.astype(np.float16)
+    elif spec.boundary_dtype == "bf16":
+        head = synth.f32_to_bf16_bits(head)
+    w.head = head
+    model = load_model(w, max_lanes=1, max_pos=64, max_L=4, kv_arena_bytes=kv_bytes(spec, [2], [16]))
+    try:
+        dt = torch.tensor(toks, dtype=torch.int32, device="cuda")
+        lg = torch.empty(1, spec.vocab, dtype=torch.float32, device="cuda")
+        nxt = torch.empty(1, dtype=torch.int32, device="cuda")
+        tl.tl_forward(model, np.array([0, 10], np.int32), dt, L=2, lanes=[0], max_new_tokens=4, out_logits=lg,
+                      out_next=nxt)
+        torch.cuda.synchronize()
+        row = lg.cpu().numpy()[0]
+        say(name, "tied logit %.4e, next %d" % (row[37], int(nxt.cpu()[0])))
+        assert row[37] == row[40] == row[200] and row[37] > 0
+        assert np.count_nonzero(row) == 3
+        assert int(nxt.cpu()[0]) == 37
+        out = torch.empty(1, dtype=torch.int32, device="cuda")
+        tl.tl_decode_step(model, [0], [2], out, in_tokens=torch.tensor([5], dtype=torch.int32, device="cuda"),
+                          out_logits=lg)
+        torch.cuda.synchronize()
+        row = lg.cpu().numpy()[0]
+        assert row[37] == row[40] == row[200]
+        want = 37 if row[37] > 0 else 0
+        say(name, "decode tied logit %.4e, next %d" % (row[37], int(out.cpu()[0])))
+        assert int(out.cpu()[0]) == want
+    finally:
+        tl.tl_free(model)
 
 
 def test_w4_export_bit_exact():
