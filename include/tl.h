@@ -227,6 +227,29 @@ tl_status tl_decode_step(tl_model* m, int32_t n_lanes, const int32_t* lanes_host
                          int32_t* out_tokens_dev, float* out_logits_dev, float* out_hidden_dev,
                          int32_t* out_eff_L_host, int32_t* out_active_log_dev, void* stream);
 
+/* tl_decode_step for callers that cannot allocate memory: code under HIP graph
+ * capture, tight serving loops, hosts that forbid allocation during a request.
+ * The call allocates nothing (no hipMalloc / hipFree / pinned host memory / any
+ * allocating library routine): its workspace (activations, split-K partials, head
+ * partials, row descriptors) lives in one device array the library holds on every
+ * device it runs on, 64 MiB (TL_NOALLOC_SCRATCH_BYTES) per device, kept until the
+ * process ends; the row descriptors go through the pinned host area the model
+ * allocated at load.  Results are those of tl_decode_step on the same lanes
+ * (the same kernels and split choices), bit for bit.
+ *   The array is shared by every call on a device and keeps the last call's
+ *   contents (nothing in it is assumed zero): calls that overlap on one device,
+ *   from any model or thread, race; serialise them (one stream, or events).
+ * Arguments and lane semantics as tl_decode_step (no active-row log).
+ * Errors: as tl_decode_step; TL_E_ARG when n_lanes rows need more scratch than
+ * TL_NOALLOC_SCRATCH_BYTES (the message gives the bytes; e.g. a 2048-wide model
+ * fits about 450 rows, a 5280-wide one about 200); TL_E_UNSUPPORTED for the store-h
+ * cache modes (their K/V rebuild buffers are allocated). */
+#define TL_NOALLOC_SCRATCH_BYTES (64ull << 20)
+tl_status tl_decode_step_noalloc(tl_model* m, int32_t n_lanes, const int32_t* lanes_host,
+                                 const int32_t* per_lane_L_host, const int32_t* in_tokens_dev,
+                                 int32_t* out_tokens_dev, float* out_logits_dev, float* out_hidden_dev,
+                                 int32_t* out_eff_L_host, void* stream);
+
 /* Early-exit rule of a decode call ("CLI Reference" page, "generate": the
  * --early-exit-patience, --early-exit-min-L, --early-exit-tau,
  * --early-exit-peek-every and --early-exit-logit-margin options).  A token is

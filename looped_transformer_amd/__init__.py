@@ -78,6 +78,7 @@ def lib():
         "tl_lane_fork": [_P, _I, _I, _I, _I, _P],
         "tl_speculate": [_P, _I, _P, _I, _I, _I, _I, _P, _P, _P],
         "tl_decode_step": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P, _P],
+        "tl_decode_step_noalloc": [_P, _I, _P, _P, _P, _P, _P, _P, _P, _P],
         "tl_decode_step_ee": [_P, _I, _P, _P, ctypes.POINTER(tl_early_exit), _P, _P, _P, _P, _P, _P],
         "tl_decode_run": [_P, _I, _P, _I, _P, _P, _P, _P, _P, _I, _P],
         "tl_export_w4": [_P, _I, _I, _P, _P],
@@ -251,6 +252,19 @@ def tl_decode_step(model, lanes, per_lane_L, out_tokens, in_tokens=None, out_log
     _check(lib().tl_decode_step(model.handle, len(ln), _ptr(ln), _ptr(pl), _ptr(in_tokens), _ptr(out_tokens),
                                 _ptr(out_logits), _ptr(out_hidden), _ptr(eff), _ptr(out_active_log),
                                 _stream(stream)))
+    return eff
+
+
+def tl_decode_step_noalloc(model, lanes, per_lane_L, out_tokens, in_tokens=None, out_logits=None, out_hidden=None,
+                           stream=None):
+    """tl_decode_step on the library's per-device scratch (no allocation);
+    returns the effective depths."""
+    ln = _i32(lanes)
+    pl = _i32(per_lane_L)
+    eff = np.zeros(len(ln), np.int32)
+    _check(lib().tl_decode_step_noalloc(model.handle, len(ln), _ptr(ln), _ptr(pl), _ptr(in_tokens),
+                                        _ptr(out_tokens), _ptr(out_logits), _ptr(out_hidden), _ptr(eff),
+                                        _stream(stream)))
     return eff
 
 

@@ -66,6 +66,7 @@ void dev_free(tl_model* m, void* p) {
 }
 
 // ----------------------------------------------------------------- staging
+constexpr size_t kStageInitBytes = 1 << 20;
 // Host data of one call is assembled here and copied in one transfer to a device
 // area; device pointers are offsets into that area.
 struct Stage {
@@ -891,6 +892,7 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   m->G = m->act == DT_F32 ? 1 : 16;
   m->esz = dtype_size(m->act);
   m->kv_mode = cfg->kv_mode;
+  m->device = dev;
   {
     const int d = cfg->d_model, H = cfg->n_heads;
     m->hrb = m->kv_mode == TL_KV_H ? d * m->esz : m->kv_mode == TL_KV_H4 ? d / 2 + 2 * H : d + 2 * H;
@@ -1013,6 +1015,14 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   LHIP(hipEventCreateWithFlags(&m->stage_done, hipEventDisableTiming));
   LHIP(hipEventCreateWithFlags(&m->aux_done, hipEventDisableTiming));
   LHIP(hipEventCreateWithFlags(&m->handover, hipEventDisableTiming));
+  // a first staging area (later calls grow it when they need more), so that a
+  // decode step of the entry point that allocates nothing finds it
+  LHIP(hipHostMalloc(&m->stage_host, kStageInitBytes, hipHostMallocDefault));
+  m->stage_dev = dev_alloc(m, kStageInitBytes);
+  if (!m->stage_dev) return cleanup_fail(fail(TL_E_OOM, "staging area"));
+  m->stage_bytes = kStageInitBytes;
+  // device address of the scratch array of tl_decode_step_noalloc on this device
+  LHIP(noalloc_scratch_init(dev));
   LHIP(hipStreamSynchronize(s));
   *out = m;
   return TL_OK;
@@ -1599,15 +1609,14 @@ tl_status tl_speculate(tl_model* m, int32_t n, const int32_t* lanes, int32_t L_d
   return TL_OK;
 }
 
-tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int32_t* req_L,
-                         const int32_t* in_tokens, int32_t* out_tokens, float* out_logits, float* out_hidden,
-                         int32_t* out_eff_L, int32_t* out_log, void* stream) {
-  g_err.clear();
-  if (!m || !lanes || !req_L || !out_tokens) return fail(TL_E_ARG, "NULL argument");
+// Validation shared by the decode-step entry points: lanes in range, distinct,
+// prefilled, not full, holding a pending token unless one is fed; eff receives
+// the clamped depths.
+tl_status decode_check(tl_model* m, int32_t n, const int32_t* lanes, const int32_t* req_L, const int32_t* in_tokens,
+                       std::vector<int>& eff) {
   const tl_config& c = m->cfg;
-  if (n < 1) return fail(TL_E_ARG, "n_lanes must be >= 1");
   std::vector<char> seen(c.max_lanes, 0);
-  std::vector<int> eff(n);
+  eff.assign(n, 0);
   for (int i = 0; i < n; ++i) {
     const int l = lanes[i];
     if (l < 0 || l >= c.max_lanes) return fail(TL_E_ARG, "lane %d out of range [0, %d)", l, c.max_lanes);
@@ -1620,21 +1629,32 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
     if (!in_tokens && !ln.pending) return fail(TL_E_STATE, "lane %d holds no pending token (append first)", l);
     eff[i] = std::min(req_L[i], ln.ceiling);
   }
-  hipStream_t s = static_cast<hipStream_t>(stream);
-  TRY(ensure_ws(m, n, n, 0, s));
-  std::vector<RowInfo> rows(n);
+  return TL_OK;
+}
+
+// Row descriptors of a decode step (staged as [rows, lane ids]).
+void decode_stage(const tl_model* m, int n, const int32_t* lanes, const std::vector<int>& eff,
+                  std::vector<RowInfo>& rows, Stage& st, size_t* o_rows, size_t* o_lanes) {
+  rows.assign(n, RowInfo{});
   std::vector<int32_t> lane_ids(lanes, lanes + n);
   for (int i = 0; i < n; ++i) {
-    rows[i] = RowInfo{};
     rows[i].orig = i;
     rows[i].lane = lanes[i];
     rows[i].pos = m->lanes[lanes[i]].len;
     rows[i].depth = eff[i];
     rows[i].iter = 1;
   }
-  Stage st;
-  const size_t o_rows = st.add(rows), o_lanes = st.add(lane_ids);
-  TRY(stage_upload(m, st, s));
+  *o_rows = st.add(rows);
+  *o_lanes = st.add(lane_ids);
+}
+
+// The pass and head of a decode step whose descriptors are staged and whose
+// workspace is m->ws; then the lanes advance.
+tl_status decode_run_step(tl_model* m, int n, const int32_t* lanes, const std::vector<int>& eff,
+                          const std::vector<RowInfo>& rows, size_t o_rows, size_t o_lanes, const int32_t* in_tokens,
+                          int32_t* out_tokens, float* out_logits, float* out_hidden, int32_t* out_eff_L,
+                          int32_t* out_log, hipStream_t s) {
+  const tl_config& c = m->cfg;
   const int32_t* lanes_dev = staged<int32_t>(m, o_lanes);
   const int32_t* toks = in_tokens;
   if (!toks) {
@@ -1660,6 +1680,128 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
     if (out_eff_L) out_eff_L[i] = eff[i];
   }
   return TL_OK;
+}
+
+tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int32_t* req_L,
+                         const int32_t* in_tokens, int32_t* out_tokens, float* out_logits, float* out_hidden,
+                         int32_t* out_eff_L, int32_t* out_log, void* stream) {
+  g_err.clear();
+  if (!m || !lanes || !req_L || !out_tokens) return fail(TL_E_ARG, "NULL argument");
+  if (n < 1) return fail(TL_E_ARG, "n_lanes must be >= 1");
+  std::vector<int> eff;
+  TRY(decode_check(m, n, lanes, req_L, in_tokens, eff));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(ensure_ws(m, n, n, 0, s));
+  std::vector<RowInfo> rows;
+  Stage st;
+  size_t o_rows = 0, o_lanes = 0;
+  decode_stage(m, n, lanes, eff, rows, st, &o_rows, &o_lanes);
+  TRY(stage_upload(m, st, s));
+  return decode_run_step(m, n, lanes, eff, rows, o_rows, o_lanes, in_tokens, out_tokens, out_logits, out_hidden,
+                         out_eff_L, out_log, s);
+}
+
+// Layout of tl_decode_step_noalloc's scratch for n rows: the workspace of a decode
+// step (as ensure_ws lays it out for n rows, with room for the split-K partials
+// the products of at most n rows can take: at most 16 splits, never more than the
+// kSplitFloats every path is capped at) followed by the staged descriptors.
+// Returns the bytes used; with base set, points w's buffers into it and the
+// staging area *stage to its place.
+size_t noalloc_layout(const tl_model* m, int n, size_t stage_bytes, uint8_t* base, tl::Workspace* w, void** stage) {
+  const tl_config& c = m->cfg;
+  const size_t R = (size_t)(n + 63) / 64 * 64;
+  const size_t d = c.d_model, F = c.ffn;
+  const int tiles = (c.vocab + 63) / 64;
+  const size_t nmax = std::max({3 * d, 2 * F, d});
+  const size_t split_floats = std::min<size_t>((size_t)kSplitFloats, 16 * (size_t)n * nmax);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    void* p = base ? base + off : nullptr;
+    off += (bytes + 255) & ~(size_t)255;
+    return p;
+  };
+  tl::Workspace x{};
+  x.hA = static_cast<float*>(take(R * d * 4));
+  x.hB = static_cast<float*>(take(R * d * 4));
+  x.hX = static_cast<float*>(take(R * d * 4));
+  x.hE = static_cast<float*>(take(R * d * 4));
+  x.x16 = take(R * d * m->esz);
+  x.q16 = take(R * d * m->esz);
+  x.o16 = take(R * d * m->esz);
+  x.u16 = take(R * F * m->esz);
+  x.xh = take(R * d * m->esz);
+  x.rowsA = static_cast<RowInfo*>(take(R * sizeof(RowInfo)));
+  x.rowsB = static_cast<RowInfo*>(take(R * sizeof(RowInfo)));
+  x.dest = static_cast<int32_t*>(take(R * 4));
+  x.count = static_cast<int32_t*>(take(256));
+  x.tok = static_cast<int32_t*>(take(R * 4));
+  x.tok2 = static_cast<int32_t*>(take(R * 4));
+  x.part_v = static_cast<float*>(take(R * tiles * 4));
+  x.part_i = static_cast<int32_t*>(take(R * tiles * 4));
+  x.part_v2 = static_cast<float*>(take(R * tiles * 4));
+  x.splitk = static_cast<float*>(take(split_floats * 4));
+  x.kv_scratch = nullptr;
+  x.kv_scratch_elems = 0;
+  x.rows = (int)R;
+  x.outs = (int)R;
+  x.part_tiles = tiles;
+  void* st = take(stage_bytes);
+  if (w) *w = x;
+  if (stage) *stage = st;
+  return off;
+}
+
+tl_status tl_decode_step_noalloc(tl_model* m, int32_t n, const int32_t* lanes, const int32_t* req_L,
+                                 const int32_t* in_tokens, int32_t* out_tokens, float* out_logits,
+                                 float* out_hidden, int32_t* out_eff_L, void* stream) {
+  g_err.clear();
+  if (!m || !lanes || !req_L || !out_tokens) return fail(TL_E_ARG, "NULL argument");
+  if (n < 1) return fail(TL_E_ARG, "n_lanes must be >= 1");
+  if (m->kv_mode != TL_KV_KV)
+    return fail(TL_E_UNSUPPORTED, "the store-h cache modes allocate rebuild buffers; use tl_decode_step");
+  const size_t stage_need = ((size_t)n * sizeof(RowInfo) + 255) / 256 * 256 + (size_t)n * 4 + 256;
+  const size_t need = noalloc_layout(m, n, stage_need, nullptr, nullptr, nullptr);
+  if (need > kNoAllocScratchBytes)
+    return fail(TL_E_ARG, "%d lanes need %zu bytes of scratch, more than the %zu the library holds per device", n,
+                need, (size_t)kNoAllocScratchBytes);
+  std::vector<int> eff;
+  TRY(decode_check(m, n, lanes, req_L, in_tokens, eff));
+  uint8_t* base = static_cast<uint8_t*>(noalloc_scratch(m->device));
+  if (!base) return fail(TL_E_STATE, "no scratch on device %d", m->device);
+  tl::Workspace w{};
+  void* stage_area = nullptr;
+  noalloc_layout(m, n, stage_need, base, &w, &stage_area);
+  std::vector<RowInfo> rows;
+  Stage st;
+  size_t o_rows = 0, o_lanes = 0;
+  decode_stage(m, n, lanes, eff, rows, st, &o_rows, &o_lanes);
+  if (st.buf.size() > stage_need || st.buf.size() > m->stage_bytes || !m->stage_host)
+    return fail(TL_E_STATE, "descriptors of %zu bytes do not fit the staging area", st.buf.size());
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  TRY(stream_handover(m, s));
+  // descriptors: the model's pinned host area (allocated at load) -> the scratch
+  HIPCHK(hipEventSynchronize(m->stage_done));
+  std::memcpy(m->stage_host, st.buf.data(), st.buf.size());
+  HIPCHK(hipMemcpyAsync(stage_area, m->stage_host, st.buf.size(), hipMemcpyHostToDevice, s));
+  HIPCHK(hipEventRecord(m->stage_done, s));
+  // run on the scratch: the model's own workspace, staging pointer and timing are
+  // put back on every return
+  struct Restore {
+    tl_model* m;
+    tl::Workspace ws;
+    void* ov;
+    bool timing;
+    ~Restore() {
+      m->ws = ws;
+      m->stage_override = ov;
+      m->timing = timing;
+    }
+  } restore{m, m->ws, m->stage_override, m->timing};
+  m->ws = w;
+  m->stage_override = stage_area;
+  m->timing = false;   // timing records events it may first have to create
+  return decode_run_step(m, n, lanes, eff, rows, o_rows, o_lanes, in_tokens, out_tokens, out_logits, out_hidden,
+                         out_eff_L, nullptr, s);
 }
 
 // Early-exit buffers for n rows.

@@ -90,6 +90,7 @@ struct Workspace {
 
 struct tl_model {
   tl_config cfg{};
+  int device = 0;            // HIP device the model was loaded on
   int act = DT_F16;
   int G = 16;
   int esz = 2;               // bytes of an activation / KV element

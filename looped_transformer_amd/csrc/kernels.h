@@ -200,3 +200,10 @@ hipError_t launch_w4_to_f16(const uint32_t* words, const uint16_t* scales, int N
 // Canonical export: q[perm[n], k], s[perm[n], g] from kernel row n.
 hipError_t launch_w4_export(const uint32_t* words, const uint16_t* scales, const int32_t* perm, int N, int K,
                             int8_t* q, uint16_t* s_out, hipStream_t s);
+
+// Scratch of tl_decode_step_noalloc: a device array of this many bytes per device.
+// noalloc_scratch_init (device current) looks up its address once per device;
+// noalloc_scratch returns it (NULL before the lookup).
+constexpr size_t kNoAllocScratchBytes = 64ull << 20;
+hipError_t noalloc_scratch_init(int device);
+void* noalloc_scratch(int device);
