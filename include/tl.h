@@ -72,8 +72,13 @@ typedef struct {
   int32_t act_dtype;               /* GEMM operands, activations and KV cache: F32, F16 or BF16 */
   /* Storage type of the weights the caller passes.  Each must equal act_dtype,
    * except BF16 weights with F16 operands (converted once at load, exact for
-   * |w| >= 2^-14; the embedding table is read in its stored type) and W4G128
-   * loop blocks with F16 operands. */
+   * |w| >= 2^-14; the embedding table is read in its stored type), W4G128 loop
+   * blocks with F16 operands, and F16 / BF16 weights (all of them) with F32
+   * activations: the weights are kept as fp16 (bf16 converted as above), and each
+   * product runs on fp16 matrix cores with every fp32 operand x split into
+   * x_hi = fp16(x) and x_lo = fp16(x - x_hi), two passes per weight fragment
+   * (about 22 significant bits of x); activations, attention and the KV cache are
+   * fp32 (K/V cache mode only). */
   int32_t boundary_dtype;          /* embed, head, pre and post blocks: F32, F16 or BF16 */
   int32_t loop_dtype;              /* loop blocks: F32, F16, BF16 or W4G128 */
   /* W4G128 only: 1 = dequantise the loop block once at load to fp16(q * s) and run
@@ -88,6 +93,14 @@ typedef struct {
    * KV compression: "CLI Reference" page, environment variables TINYLOOP_KV_H_MODE
    * with TINYLOOP_KV_INT8 / TINYLOOP_KV_INT4). */
   int32_t kv_mode;
+  /* 1: every row's results are independent of which other rows share its passes
+   * (bit for bit): the split of each product's K is chosen from its N and K only,
+   * one GEMM kernel family runs at every batch size (no few-row GEMVs), decode
+   * attention uses one block size for every context, and every RMSNorm sums its
+   * squares in one order.  Then continuous-depth decoding (tl_decode_run) equals
+   * step-by-step decoding and a mixed batch equals each lane alone exactly.
+   * 0: kernels and splits are picked per pass size (faster at small batches). */
+  int32_t batch_invariant;
 } tl_config;
 
 /* TL_KV_KV: K and V in the operand type (2 d elements per position and slot).
@@ -326,8 +339,9 @@ tl_status tl_speculate(tl_model* m, int32_t n_lanes, const int32_t* lanes_host, 
  * so the host plans every tick before enqueuing any work.
  *   L_req_host [n_lanes, n_steps]: requested depth of each new token; clamped
  *      exactly as in tl_decode_step.  The results equal n_steps calls of
- *      tl_decode_step with these requests (up to fp32 summation order: batches of
- *      different sizes may split K differently); only the order of work differs.
+ *      tl_decode_step with these requests (bit for bit with batch_invariant set;
+ *      otherwise up to fp32 summation order, as batches of different sizes may
+ *      split K differently); only the order of work differs.
  *   in_tokens_dev [n_lanes, n_steps] int32 or NULL: token fed at each step (NULL:
  *      the lane's pending greedy token, i.e. free-running greedy decoding).
  *   out_tokens_dev [n_lanes, n_steps] int32: greedy token of each step.

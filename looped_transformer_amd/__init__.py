@@ -37,7 +37,8 @@ class tl_config(ctypes.Structure):
         ("rms_eps", ctypes.c_float), ("rope_base", ctypes.c_float),
         ("act_dtype", ctypes.c_int32), ("boundary_dtype", ctypes.c_int32), ("loop_dtype", ctypes.c_int32),
         ("loop_fp16_body", ctypes.c_int32), ("max_lanes", ctypes.c_int32), ("max_L", ctypes.c_int32),
-        ("max_pos", ctypes.c_int32), ("kv_arena_bytes", ctypes.c_uint64), ("kv_mode", ctypes.c_int32)]
+        ("max_pos", ctypes.c_int32), ("kv_arena_bytes", ctypes.c_uint64), ("kv_mode", ctypes.c_int32),
+        ("batch_invariant", ctypes.c_int32)]
 
 
 class tl_block_weights(ctypes.Structure):

@@ -356,12 +356,243 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __
   }
 }
 
+// The same tiling for fp32 Q / K / V on fp16 MFMA: every fp32 operand x is split
+// into x_hi = fp16(x) and x_lo = fp16(x - x_hi) on its way into registers or LDS
+// (about 22 significant bits), and each product takes the three terms that carry
+// them: S = Qh Kh^T + Qh Kl^T + Ql Kh^T, O += Ph Vh + Ph Vl + Pl Vh (the lo * lo
+// term is below fp32 rounding).  Softmax statistics stay fp32.
+template <int DH>
+__global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_split_kernel(const float* __restrict__ q,
+                                                                           const AttnTile* __restrict__ tiles,
+                                                                           KVParams kv, float* __restrict__ out, int d,
+                                                                           float scale) {
+  constexpr int NW = kAttnWaves, NT = 64 * NW;
+  constexpr int KB = 64;
+  constexpr int LDK = DH + 8;
+  constexpr int LDV = KB + 8;
+  constexpr int KS = DH / 32;
+  constexpr int OT = DH / 16;
+  constexpr int CH = KB * DH / 4;   // 16-byte chunks (4 floats) of one K block
+  constexpr int CPT = CH / NT;      // per thread
+  static_assert(CH % NT == 0, "block split");
+  // V: thread t < VP holds 8 consecutive keys of one 8-wide dim chunk (16 words)
+  // and writes each dim as one 16-byte piece of the transposed row (hi and lo),
+  // the 8-key slot XOR-ed with (row / 16) mod 8 as in attn_tiled_kernel
+  constexpr int VP = (KB / 8) * (DH / 8);
+  static_assert(VP <= NT && KB / 8 == 8, "V staging");
+  __shared__ __attribute__((aligned(16))) f16 Kh[KB * LDK];
+  __shared__ __attribute__((aligned(16))) f16 Kl[KB * LDK];
+  __shared__ __attribute__((aligned(16))) f16 Vth[DH * LDV];
+  __shared__ __attribute__((aligned(16))) f16 Vtl[DH * LDV];
+  __shared__ __attribute__((aligned(16))) f16 Ph[NW][16 * LDV];
+  __shared__ __attribute__((aligned(16))) f16 Pl[NW][16 * LDV];
+
+  const AttnTile tile = tiles[blockIdx.x];
+  const int h = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int g4 = lane >> 4, l16 = lane & 15;
+  const int slot = kv.s0 + kv.s1 * tile.iter;
+  int64_t cap, koff;
+  if (tile.cap > 0) {
+    cap = tile.cap;
+    koff = tile.koff;
+  } else {
+    cap = kv.lane_cap[tile.lane];
+    koff = kv.lane_off[tile.lane];
+  }
+  const float* Kg = reinterpret_cast<const float*>(kv.base) + koff + ((int64_t)(slot * 2) * kv.H + h) * cap * DH;
+  const float* Vg = Kg + (int64_t)kv.H * cap * DH;
+  const int kend = tile.pos0 + tile.nrows;
+
+  auto split8 = [](const float* x, half8& hi, half8& lo) __attribute__((always_inline)) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const f16 xh = (f16)x[e];
+      hi[e] = xh;
+      lo[e] = (f16)(x[e] - (float)xh);
+    }
+  };
+
+  u32x4 rk[CPT], rv[8][2];
+  const int vkg = tid / (DH / 8), vdc = tid % (DH / 8);
+  auto load = [&](int k0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + NT * i, key = c / (DH / 4), dc = (c % (DH / 4)) * 4;
+      const int kp = min(k0 + key, kend - 1);
+      rk[i] = *reinterpret_cast<const u32x4*>(Kg + (int64_t)kp * DH + dc);
+    }
+    if (tid < VP) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const int kp = min(k0 + 8 * vkg + i, kend - 1);
+        rv[i][0] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)kp * DH + 8 * vdc);
+        rv[i][1] = *reinterpret_cast<const u32x4*>(Vg + (int64_t)kp * DH + 8 * vdc + 4);
+      }
+    }
+  };
+  load(0);
+
+  const int qr = 16 * w + l16;
+  half8 qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int qrc = min(qr, tile.nrows - 1);
+    const float* qp = q + (int64_t)(tile.row0 + qrc) * d + h * DH + ks * 32 + 8 * g4;
+    float x[8];
+    const floatx4 a = *reinterpret_cast<const floatx4*>(qp), b = *reinterpret_cast<const floatx4*>(qp + 4);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = a[e];
+      x[4 + e] = b[e];
+    }
+    split8(x, qh[ks], ql[ks]);
+  }
+  floatx4 o[OT];
+#pragma unroll
+  for (int t = 0; t < OT; ++t) o[t] = floatx4{0.f, 0.f, 0.f, 0.f};
+  float mrow[4], lrow[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    mrow[r] = -INFINITY;
+    lrow[r] = 0.f;
+  }
+  const int qpos0 = tile.pos0 + 16 * w + 4 * g4;
+
+  for (int k0 = 0; k0 < kend; k0 += KB) {
+    lds_barrier();
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + NT * i, key = c / (DH / 4), dc = (c % (DH / 4)) * 4;
+      const floatx4 v = __builtin_bit_cast(floatx4, rk[i]);
+      half2v hi0, hi1, lo0, lo1;
+#pragma unroll
+      for (int e = 0; e < 2; ++e) {
+        const f16 a = (f16)v[e], b = (f16)v[2 + e];
+        hi0[e] = a;
+        hi1[e] = b;
+        lo0[e] = (f16)(v[e] - (float)a);
+        lo1[e] = (f16)(v[2 + e] - (float)b);
+      }
+      *reinterpret_cast<half2v*>(&Kh[key * LDK + dc]) = hi0;
+      *reinterpret_cast<half2v*>(&Kh[key * LDK + dc + 2]) = hi1;
+      *reinterpret_cast<half2v*>(&Kl[key * LDK + dc]) = lo0;
+      *reinterpret_cast<half2v*>(&Kl[key * LDK + dc + 2]) = lo1;
+    }
+    if (tid < VP) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        float x[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) x[i] = __builtin_bit_cast(floatx4, rv[i][e >> 2])[e & 3];
+        half8 hv, lv;
+        split8(x, hv, lv);
+        const int r = 8 * vdc + e;
+        const int at = r * LDV + 8 * (vkg ^ ((r >> 4) & 7));
+        *reinterpret_cast<half8*>(&Vth[at]) = hv;
+        *reinterpret_cast<half8*>(&Vtl[at]) = lv;
+      }
+    }
+    lds_barrier();
+    if (k0 + KB < kend) load(k0 + KB);
+    asm volatile("" ::: "memory");
+
+    floatx4 sacc[4];
+#pragma unroll
+    for (int n = 0; n < 4; ++n) {
+      sacc[n] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int at = (16 * n + l16) * LDK + ks * 32 + 8 * g4;
+        const half8 bh = *reinterpret_cast<const half8*>(&Kh[at]);
+        const half8 bl = *reinterpret_cast<const half8*>(&Kl[at]);
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], bh, sacc[n], 0, 0, 0);
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(qh[ks], bl, sacc[n], 0, 0, 0);
+        sacc[n] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ql[ks], bh, sacc[n], 0, 0, 0);
+      }
+    }
+    float mx[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) mx[r] = -INFINITY;
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int kp = k0 + 16 * n + l16;
+        float v = sacc[n][r] * scale;
+        if (kp > qpos0 + r || kp >= kend) v = -INFINITY;
+        sacc[n][r] = v;
+        mx[r] = fmaxf(mx[r], v);
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) mx[r] = fmaxf(mx[r], __shfl_xor(mx[r], off, 64));
+    }
+    float corr[4], rs[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const float mn = fmaxf(mrow[r], mx[r]);
+      corr[r] = mn == -INFINITY ? 1.f : expf(mrow[r] - mn);
+      mrow[r] = mn;
+      rs[r] = 0.f;
+    }
+#pragma unroll
+    for (int n = 0; n < 4; ++n)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float p = sacc[n][r] == -INFINITY ? 0.f : expf(sacc[n][r] - mrow[r]);
+        rs[r] += p;
+        const f16 ph = (f16)p;
+        Ph[w][(4 * g4 + r) * LDV + 16 * n + l16] = ph;
+        Pl[w][(4 * g4 + r) * LDV + 16 * n + l16] = (f16)(p - (float)ph);
+      }
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) rs[r] += __shfl_xor(rs[r], off, 64);
+      lrow[r] = lrow[r] * corr[r] + rs[r];
+    }
+#pragma unroll
+    for (int t = 0; t < OT; ++t)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) o[t][r] *= corr[r];
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront", "local");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront", "local");
+#pragma unroll
+    for (int kk = 0; kk < KB; kk += 32) {
+      const half8 ah = *reinterpret_cast<const half8*>(&Ph[w][l16 * LDV + kk + 8 * g4]);
+      const half8 al = *reinterpret_cast<const half8*>(&Pl[w][l16 * LDV + kk + 8 * g4]);
+#pragma unroll
+      for (int t = 0; t < OT; ++t) {
+        const int at = (16 * t + l16) * LDV + 8 * ((kk / 8 + g4) ^ (t & 7));
+        const half8 bh = *reinterpret_cast<const half8*>(&Vth[at]);
+        const half8 bl = *reinterpret_cast<const half8*>(&Vtl[at]);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bh, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(ah, bl, o[t], 0, 0, 0);
+        o[t] = __builtin_amdgcn_mfma_f32_16x16x32_f16(al, bh, o[t], 0, 0, 0);
+      }
+    }
+  }
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int rl = 16 * w + 4 * g4 + r;
+    if (rl >= tile.nrows) continue;
+    const float inv = 1.0f / lrow[r];
+    float* op = out + (int64_t)(tile.row0 + rl) * d + h * DH + l16;
+#pragma unroll
+    for (int t = 0; t < OT; ++t) op[16 * t] = o[t][r] * inv;
+  }
+}
+
 }  // namespace
 
 int attn_tile_rows() { return kAttnTileRows; }
 
 bool attn_tiled_supported(int dtype, int head_dim) {
-  return (dtype == DT_F16 || dtype == DT_BF16) && (head_dim == 64 || head_dim == 96 || head_dim == 128);
+  return (dtype == DT_F16 || dtype == DT_BF16 || dtype == DT_F32) &&
+         (head_dim == 64 || head_dim == 96 || head_dim == 128);
 }
 
 hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tiles, int n_tiles, const KVParams& kv,
@@ -384,6 +615,17 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
     TL_ATTN_CASE(bf16, 64)
     TL_ATTN_CASE(bf16, 96)
     TL_ATTN_CASE(bf16, 128)
+  } else if (dtype == DT_F32) {
+#define TL_ATTN_SPLIT(DHV)                                                                                     \
+  if (kv.dh == DHV) {                                                                                          \
+    hipLaunchKernelGGL((attn_tiled_split_kernel<DHV>), grid, dim3(kAttnWaves * 64), 0, s, (const float*)q, tiles, kv, \
+                       (float*)out, d, scale);                                                                 \
+    return hipGetLastError();                                                                                  \
+  }
+    TL_ATTN_SPLIT(64)
+    TL_ATTN_SPLIT(96)
+    TL_ATTN_SPLIT(128)
+#undef TL_ATTN_SPLIT
   }
 #undef TL_ATTN_CASE
   return hipErrorInvalidValue;

@@ -15,7 +15,15 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 #include "kernels.h"
 
 template <class T> __device__ __forceinline__ float to_f32(T x) { return (float)x; }
-template <class T> __device__ __forceinline__ T from_f32(float x) { return (T)x; }  // RNE
+// fp32 -> T with round-to-nearest-even of the fp32 value.  For 16-bit T the value
+// is first pinned in a register: otherwise the compiler may fold the conversion
+// into the multiply-add that produced x (a mixed-precision FMA that rounds the
+// exact result once, straight to 16 bits), and whether it does depends on the
+// surrounding code, so one value could round differently in two kernels.
+template <class T> __device__ __forceinline__ T from_f32(float x) {
+  if constexpr (sizeof(T) == 2) asm volatile("" : "+v"(x));
+  return (T)x;
+}
 
 // Workgroup barrier that orders LDS accesses only.  __syncthreads() also waits
 // for every outstanding global load of the thread, which would drain the
@@ -32,6 +40,26 @@ __device__ __forceinline__ float wave_sum(float v) {
   for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o, 64);
   return v;
 }
+// RMSNorm statistics shared by every kernel that normalises a row (the norm
+// kernel, the embedding gather, the split-K residual reduction), so that a row
+// gets the same bits whichever of them normalises it: a workgroup of 256 threads
+// per row, thread t holding the groups of four columns 4 (t + 256 u), its sum of
+// squares accumulated group after group (last element of a group first), then the
+// wave sums, then waves 0..3 in order.
+__device__ __forceinline__ float sumsq4(float x, float y, float z, float w, float ss) {
+  return fmaf(x, x, fmaf(y, y, fmaf(z, z, fmaf(w, w, ss))));
+}
+__device__ __forceinline__ float row_sum256(float ss) {
+  __shared__ float red[4];
+  ss = wave_sum(ss);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
+  __syncthreads();
+  return red[0] + red[1] + red[2] + red[3];
+}
+__device__ __forceinline__ float rms_inv(float sumsq, int d, float eps) {
+  return 1.0f / sqrtf(sumsq / (float)d + eps);
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o, 64));

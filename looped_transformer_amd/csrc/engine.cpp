@@ -298,15 +298,16 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
   g.partial = m->ws.splitk;
   g.partial_cap = kSplitFloats;
   g.live = m->gate_live;
+  g.invariant = m->invariant;
   e.pair_g = m->G;
-  if (m->act == DT_F16 && gemv_applies(g, e.kind)) {   // a few rows: no split-K pass
+  if (m->act == DT_F16 && !m->invariant && gemv_applies(g, e.kind)) {   // a few rows: no split-K pass
     HIPCHK(launch_gemv(g, e, s));
     if (e.kind == EPI_RESID && e.norm_g)
       HIPCHK(launch_rmsnorm(m->act, e.h, e.norm_g, nullptr, M, g.N, e.norm_eps, e.norm_out, s));
     return TL_OK;
   }
   if (norm_h) return fail(TL_E_STATE, "normalised input outside the GEMV path");
-  HIPCHK(launch_gemm(m->act, g, e, s));
+  HIPCHK(launch_gemm(m->gdt, g, e, s));
   return TL_OK;
 }
 
@@ -314,7 +315,7 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
 // rows, INT4 or dense weights): its RMSNorms are formed inside the QKV and
 // gate/up GEMVs.
 bool small_gemv(const tl_model* m, const tl::BlockDev& B, int n) {
-  if (m->act != DT_F16) return false;
+  if (m->act != DT_F16 || m->invariant) return false;
   for (const MatDev* W : {&B.qkv, &B.o, &B.gu, &B.down}) {
     GemmArgs g{};
     g.M = n;
@@ -376,7 +377,8 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
     TIMED(TL_T_HREBUILD, TRY(gemm(m, m->h_x, nrec, B.qkv, r2, s)));
   }
   if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, akv, w.o16, s)));
-  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, akv, w.o16, m->gate_live, m->ctx_hint, s)));
+  else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, akv, w.o16, m->gate_live,
+                                                     m->invariant ? 0 : m->ctx_hint, s)));
   GemmEpi r{};
   r.kind = EPI_RESID;
   r.h = h;
@@ -658,13 +660,14 @@ tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out
   auto& w = m->ws;
   TRY(tbegin(m, s));
   HIPCHK(launch_rmsnorm(m->act, h, m->final_norm, gather, n_out, c.d_model, c.rms_eps, w.xh, s));
-  const int tiles = gemm_head_tiles(m->act, n_out, c.vocab);
+  const int tiles = gemm_head_tiles(m->gdt, n_out, c.vocab);
   GemmArgs g{};
   g.A = w.xh;
   g.M = n_out;
   g.N = c.vocab;
   g.K = c.d_model;
   g.B = m->head;
+  g.invariant = m->invariant;
   GemmEpi e{};
   e.kind = EPI_HEAD;
   e.logits = logits;
@@ -673,7 +676,7 @@ tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out
   e.part_idx = w.part_i;
   e.n_tiles = tiles;
   e.part_val2 = margin ? w.part_v2 : nullptr;
-  HIPCHK(launch_gemm(m->act, g, e, s));
+  HIPCHK(launch_gemm(m->gdt, g, e, s));
   if (out_tok || pend_lanes || margin)
     HIPCHK(launch_argmax_reduce(w.part_v, w.part_i, e.part_val2, n_out, tiles, out_tok,
                                 pend_lanes ? m->d_pending : nullptr, pend_lanes, margin, s));
@@ -748,7 +751,8 @@ tl_status prepare_matrix(tl_model* m, MatDev& md, const void* src0, const void* 
                          bool w4, bool fp16_body, const int32_t* perm_dev, hipStream_t s,
                          std::vector<void*>& temps) {
   // dtype: storage type given by the caller; dense matrices end in the operand type
-  // (m->act), converting bf16 -> fp16 on the way when the two differ.
+  // (m->act; fp16 with fp32 activations), converting bf16 -> fp16 on the way when
+  // the two differ.
   md.N = N;
   md.K = K;
   md.perm = const_cast<int32_t*>(perm_dev);
@@ -775,11 +779,11 @@ tl_status prepare_matrix(tl_model* m, MatDev& md, const void* src0, const void* 
     }
     return TL_OK;
   }
-  const size_t bytes = (size_t)N * K * m->esz;
+  const size_t bytes = (size_t)N * K * (m->wide ? 2 : m->esz);
   md.dense = dev_alloc(m, bytes);
   if (!md.dense) return fail(TL_E_OOM, "dense weights");
   m->weight_bytes += bytes;
-  if (dtype == DT_BF16 && m->act == DT_F16)
+  if (dtype == DT_BF16 && (m->act == DT_F16 || m->wide))
     HIPCHK(launch_permute_bf16_to_f16(static_cast<const uint16_t*>(canon), perm_dev, N, K,
                                       static_cast<uint16_t*>(md.dense), s));
   else if (perm_dev) HIPCHK(launch_permute_rows(in_esz, canon, perm_dev, N, K, md.dense, s));
@@ -795,18 +799,24 @@ tl_status validate_config(const tl_config* c) {
   if (c->max_L < 1 || c->max_pos < 1 || c->max_lanes < 0) return fail(TL_E_ARG, "max_L / max_pos / max_lanes");
   if (c->act_dtype < DT_F32 || c->act_dtype > DT_BF16) return fail(TL_E_UNSUPPORTED, "act_dtype");
   // weights are stored in the operand type, or as bf16 with fp16 operands (converted
-  // at load), or (loop blocks) as W4G128 with fp16 operands
+  // at load), or (loop blocks) as W4G128 with fp16 operands; with fp32 activations
+  // either every weight is fp32 or every weight is 16-bit (fp16 / bf16, run as
+  // fp16 with the fp32 operands split into two fp16 halves)
+  const bool wide = c->act_dtype == DT_F32 && c->boundary_dtype != DT_F32;
   auto storable = [&](int dt) {
+    if (wide) return dt == DT_F16 || dt == DT_BF16;
     return dt == c->act_dtype || (dt == DT_BF16 && c->act_dtype == DT_F16);
   };
   if (!storable(c->boundary_dtype)) return fail(TL_E_UNSUPPORTED, "boundary dtype incompatible with act dtype");
   if (!storable(c->loop_dtype) && !(c->loop_dtype == DT_W4G128 && c->act_dtype == DT_F16))
-    return fail(TL_E_UNSUPPORTED, "loop dtype must match act dtype (bf16 storage allowed with F16 operands), "
-                                  "or W4G128 with F16 operands");
+    return fail(TL_E_UNSUPPORTED, "loop dtype must match act dtype (bf16 storage allowed with F16 operands; "
+                                  "F16 / BF16 weights with F32 activations), or W4G128 with F16 operands");
+  if (wide && c->kv_mode != TL_KV_KV)
+    return fail(TL_E_UNSUPPORTED, "fp32 activations with 16-bit weights keep K/V (kv_mode TL_KV_KV)");
   if (c->loop_fp16_body && c->loop_dtype != DT_W4G128) return fail(TL_E_ARG, "loop_fp16_body needs W4G128");
   if (c->head_dim % 2 || c->head_dim > 128) return fail(TL_E_UNSUPPORTED, "head_dim must be even and <= 128");
   if (c->d_model % 8 || c->ffn % 8) return fail(TL_E_UNSUPPORTED, "d_model and ffn must be multiples of 8");
-  if (c->act_dtype == DT_F32) {
+  if (c->act_dtype == DT_F32 && !wide) {
     if (c->head_dim % 4) return fail(TL_E_UNSUPPORTED, "fp32 head_dim must be a multiple of 4");
   } else {
     if (c->head_dim % 32 || c->ffn % 16) return fail(TL_E_UNSUPPORTED, "16-bit: head_dim % 32, ffn % 16");
@@ -814,6 +824,7 @@ tl_status validate_config(const tl_config* c) {
   if (c->loop_dtype == DT_W4G128 && (c->d_model % 128 || c->ffn % 128))
     return fail(TL_E_UNSUPPORTED, "W4G128 needs d_model and ffn multiples of 128");
   if (c->kv_mode < TL_KV_KV || c->kv_mode > TL_KV_D8) return fail(TL_E_ARG, "kv_mode %d unknown", c->kv_mode);
+  if (c->batch_invariant != 0 && c->batch_invariant != 1) return fail(TL_E_ARG, "batch_invariant must be 0 or 1");
   return TL_OK;
 }
 
@@ -889,7 +900,10 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   m->dealloc = dealloc;
   m->user = alloc_user;
   m->act = cfg->act_dtype;
-  m->G = m->act == DT_F32 ? 1 : 16;
+  m->wide = m->act == DT_F32 && cfg->boundary_dtype != DT_F32;   // validated: all weights 16-bit
+  m->gdt = m->wide ? DT_F32X16 : m->act;
+  m->invariant = cfg->batch_invariant ? 1 : 0;
+  m->G = (m->act == DT_F32 && !m->wide) ? 1 : 16;
   m->esz = dtype_size(m->act);
   m->kv_mode = cfg->kv_mode;
   m->device = dev;
@@ -922,14 +936,14 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   const int64_t d = c.d_model, F = c.ffn, V = c.vocab;
   const int besz = dtype_size(c.boundary_dtype);
   LTRY(upload_bytes(m, &m->embed, w->embed, (size_t)V * d * besz, s));
-  if (c.boundary_dtype != m->act) {
-    // head in the operand type (bf16 storage -> fp16); the embedding gather reads
-    // the stored type directly
+  if (c.boundary_dtype == DT_BF16 && (m->act == DT_F16 || m->wide)) {
+    // head in the GEMM's weight type (bf16 storage -> fp16); the embedding gather
+    // reads the stored type directly
     void* hs = nullptr;
     LTRY(upload_bytes(m, &hs, w->head, (size_t)V * d * besz, s));
-    m->head = dev_alloc(m, (size_t)V * d * m->esz);
+    m->head = dev_alloc(m, (size_t)V * d * 2);
     if (!m->head) return cleanup_fail(fail(TL_E_OOM, "head"));
-    m->weight_bytes += (size_t)V * d * m->esz - (size_t)V * d * besz;
+    m->weight_bytes += (size_t)V * d * 2 - (size_t)V * d * besz;
     LHIP(launch_permute_bf16_to_f16(static_cast<const uint16_t*>(hs), nullptr, (int)V, (int)d,
                                     static_cast<uint16_t*>(m->head), s));
     LHIP(hipStreamSynchronize(s));

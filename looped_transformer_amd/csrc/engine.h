@@ -92,6 +92,9 @@ struct tl_model {
   tl_config cfg{};
   int device = 0;            // HIP device the model was loaded on
   int act = DT_F16;
+  int gdt = DT_F16;          // GEMM dispatch type: act, or DT_F32X16 (fp32 activations, fp16 weights)
+  bool wide = false;         // fp32 activations with 16-bit weights (stored as fp16)
+  int32_t invariant = 0;     // tl_config.batch_invariant
   int G = 16;
   int esz = 2;               // bytes of an activation / KV element
   int kv_mode = 0;           // tl_kv_mode

@@ -6,6 +6,12 @@
 
 namespace {
 
+// The rotary pair (x1, x2) = (v0 cos - v1 sin, v1 cos + v0 sin) with its fused
+// multiply-adds written out, so that every kernel that rotates a pair rounds it
+// the same way.
+__device__ __forceinline__ float rot_x1(float v0, float v1, float cs, float sn) { return fmaf(v0, cs, -(v1 * sn)); }
+__device__ __forceinline__ float rot_x2(float v0, float v1, float cs, float sn) { return fmaf(v1, cs, v0 * sn); }
+
 template <class AT, int KIND>
 __device__ __forceinline__ void epi_pair(const GemmEpi& e, int r, int c, float v0, float v1) {
   if constexpr (KIND == EPI_QKV) {
@@ -27,8 +33,8 @@ __device__ __forceinline__ void epi_pair(const GemmEpi& e, int r, int c, float v
     const int n0 = (ci >> 1) * G + (cd - ci * G);
     const float cs = e.rope_cos[(int64_t)ri.pos * half + n0];
     const float sn = e.rope_sin[(int64_t)ri.pos * half + n0];
-    const float x1 = v0 * cs - v1 * sn;
-    const float x2 = v1 * cs + v0 * sn;
+    const float x1 = rot_x1(v0, v1, cs, sn);
+    const float x2 = rot_x2(v0, v1, cs, sn);
     AT* dst = (sect == 0) ? reinterpret_cast<AT*>(e.q_out) + (int64_t)r * d + head * dh
                           : kv_ptr<AT>(e.kv, ri, 0, head, ri.pos);
     dst[n0] = from_f32<AT>(x1);
@@ -104,8 +110,8 @@ __device__ __forceinline__ void qkv_put(const GemmEpi& e, const QkvPrep& p, floa
     vp[e.pair_g] = from_f32<AT>(v1);
     return;
   }
-  const float x1 = v0 * p.cs - v1 * p.sn;
-  const float x2 = v1 * p.cs + v0 * p.sn;
+  const float x1 = rot_x1(v0, v1, p.cs, p.sn);
+  const float x2 = rot_x2(v0, v1, p.cs, p.sn);
   AT* dst = (p.sect == 0 ? reinterpret_cast<AT*>(e.q_out) : reinterpret_cast<AT*>(e.kv.base)) + p.off;
   dst[0] = from_f32<AT>(x1);
   dst[e.dh >> 1] = from_f32<AT>(x2);

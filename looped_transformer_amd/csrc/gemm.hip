@@ -53,8 +53,18 @@ template <> struct Mfma<bf16> {
 // 16x16x32 MFMAs per 32-wide k step.  INT4 stages cover whole 128-wide groups; each group's MFMA sum
 // is scaled when the group ends.  With several splits each workgroup stores an
 // fp32 partial tile and splitk_epilogue_kernel finishes the tile.
-template <class AT, bool W4, int BM, int BN, int BK, int D, int KIND>
+//
+// XT is the activation type (A in memory, epilogue outputs).  XT = AT: A goes to
+// the MFMA as it is.  XT = float with AT = f16 (fp32 activations, fp16 weights):
+// each fp32 operand x is split on its way into LDS into x_hi = fp16(x) and
+// x_lo = fp16(x - x_hi) (x_hi + x_lo carries about 22 significant bits), and every
+// k step runs both halves against the same weight fragment, acc += x_hi w then
+// acc += x_lo w, so the product has close to fp32 accuracy on fp16 MFMA.
+template <class AT, class XT, bool W4, int BM, int BN, int BK, int D, int KIND>
 __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e, int kchunk) {
+  constexpr bool SPLIT = std::is_same<XT, float>::value;
+  static_assert(!SPLIT || (std::is_same<AT, f16>::value && !W4), "split operands: fp16 MFMA, dense weights");
+  constexpr int AW = SPLIT ? 2 : 1;   // 16-byte words of one 8-element A chunk
   constexpr int LDK = BK + 8;   // padded LDS row, elements
   constexpr int WTM = BM / 2, WTN = BN / 2;
   constexpr int TM = WTM / 16, TN = WTN / 16;
@@ -68,6 +78,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   typedef typename Mfma<AT>::frag frag;
 
   __shared__ __attribute__((aligned(16))) AT As[BM * LDK];
+  __shared__ __attribute__((aligned(16))) AT As2[SPLIT ? BM * LDK : 8];   // x_lo of split operands
   __shared__ __attribute__((aligned(16))) AT Bs[BN * LDK];
   __shared__ float Ss[W4 ? GPS : 1][W4 ? BN : 1];
 
@@ -77,7 +88,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   const int M = g.M, N = g.N, K = g.K;
   const int S = gridDim.z, z = blockIdx.z;
   const int kb = z * kchunk, ke = min(K, kb + kchunk);
-  const AT* A = reinterpret_cast<const AT*>(g.A);
+  const XT* A = reinterpret_cast<const XT*>(g.A);
   const int groups = K >> 7;
 
   floatx4 acc[TM][TN];
@@ -93,10 +104,10 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   // Register ring.  Every load is issued unconditionally from an address clamped
   // into the operand (branch-free code lets the compiler wait for exactly the
   // oldest stage); chunks outside the tile are zeroed when they go to LDS.
-  uint4 ra_[D][AC], rb_[D][BC];
+  uint4 ra_[D][AC * AW], rb_[D][BC];
   uint16_t rs_[D][W4 ? GPS : 1];
   uint32_t okA_[D], okB_[D];
-  auto gload = [&](uint4 (&ra)[AC], uint4 (&rb)[BC], uint16_t (&rs)[W4 ? GPS : 1], uint32_t& okA, uint32_t& okB,
+  auto gload = [&](uint4 (&ra)[AC * AW], uint4 (&rb)[BC], uint16_t (&rs)[W4 ? GPS : 1], uint32_t& okA, uint32_t& okB,
                    int k0) {
     okA = 0;
     okB = 0;
@@ -106,7 +117,9 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       const int gr = m0 + r, gk = k0 + kc;
       if constexpr (!W4) okA |= (gr < M && gk < ke) ? (1u << i) : 0u;   // (INT4: scale 0 instead)
       const int grc = min(gr, M - 1), gkc = min(gk, K - 8);
-      ra[i] = *reinterpret_cast<const uint4*>(A + (int64_t)grc * K + gkc);
+      const XT* src = A + (int64_t)grc * K + gkc;
+#pragma unroll
+      for (int w = 0; w < AW; ++w) ra[i * AW + w] = *reinterpret_cast<const uint4*>(src + w * (16 / sizeof(XT)));
     }
     if constexpr (W4) {
       // chunk c: group go of the stage, 32-row block of the tile, half hb of the
@@ -141,8 +154,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       }
     }
   };
-  auto lstore = [&](const uint4 (&ra)[AC], const uint4 (&rb)[BC], const uint16_t (&rs)[W4 ? GPS : 1], uint32_t okA,
-                    uint32_t okB) {
+  auto lstore = [&](const uint4 (&ra)[AC * AW], const uint4 (&rb)[BC], const uint16_t (&rs)[W4 ? GPS : 1],
+                    uint32_t okA, uint32_t okB) {
     // keep the masking here: without this the compiler may move it next to the
     // loads and wait for the data as soon as it is requested
     asm volatile("" : "+v"(okA), "+v"(okB));
@@ -153,7 +166,25 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
     for (int i = 0; i < AC; ++i) {
       const int c = tid + 256 * i, r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
       const uint32_t mk = W4 ? ~0u : 0u - ((okA >> i) & 1u);
-      *reinterpret_cast<uint4*>(&As[r * LDK + kc]) = uint4{ra[i].x & mk, ra[i].y & mk, ra[i].z & mk, ra[i].w & mk};
+      if constexpr (SPLIT) {
+        half8 hi, lo;
+#pragma unroll
+        for (int w = 0; w < 2; ++w) {
+          const uint4 q = ra[i * 2 + w];
+          const uint32_t u[4] = {q.x & mk, q.y & mk, q.z & mk, q.w & mk};
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float x = __builtin_bit_cast(float, u[e2]);
+            const f16 xh = (f16)x;
+            hi[4 * w + e2] = xh;
+            lo[4 * w + e2] = (f16)(x - (float)xh);
+          }
+        }
+        *reinterpret_cast<half8*>(&As[r * LDK + kc]) = hi;
+        *reinterpret_cast<half8*>(&As2[r * LDK + kc]) = lo;
+      } else {
+        *reinterpret_cast<uint4*>(&As[r * LDK + kc]) = uint4{ra[i].x & mk, ra[i].y & mk, ra[i].z & mk, ra[i].w & mk};
+      }
     }
     if constexpr (W4) {
 #pragma unroll
@@ -198,18 +229,27 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   auto compute = [&]() {
 #pragma unroll
     for (int kk = 0; kk < BK; kk += 32) {
-      frag a[TM], b[TN];
+      frag a[TM], b[TN], a2[SPLIT ? TM : 1];
       const int lrow = lane & 15, lk = kk + 8 * (lane >> 4);
 #pragma unroll
       for (int i = 0; i < TM; ++i) a[i] = *reinterpret_cast<const frag*>(&As[(wm * WTM + i * 16 + lrow) * LDK + lk]);
+      if constexpr (SPLIT) {
+#pragma unroll
+        for (int i = 0; i < TM; ++i)
+          a2[i] = *reinterpret_cast<const frag*>(&As2[(wm * WTM + i * 16 + lrow) * LDK + lk]);
+      }
 #pragma unroll
       for (int j = 0; j < TN; ++j) b[j] = *reinterpret_cast<const frag*>(&Bs[(wn * WTN + j * 16 + lrow) * LDK + lk]);
 #pragma unroll
       for (int i = 0; i < TM; ++i)
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
-          if constexpr (W4) tmp[i][j] = Mfma<AT>::run(a[i], b[j], tmp[i][j]);
-          else acc[i][j] = Mfma<AT>::run(a[i], b[j], acc[i][j]);
+          if constexpr (W4) {
+            tmp[i][j] = Mfma<AT>::run(a[i], b[j], tmp[i][j]);
+          } else {
+            acc[i][j] = Mfma<AT>::run(a[i], b[j], acc[i][j]);
+            if constexpr (SPLIT) acc[i][j] = Mfma<AT>::run(a2[i], b[j], acc[i][j]);
+          }
         }
       if constexpr (W4) {
         if ((kk & 127) == 96) {   // end of a 128-wide group: apply its scale
@@ -407,7 +447,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
         for (int r = 0; r < 4; ++r) q_rope(i, r, q_pos[wm * WTM + i * 16 + lr + r]);
     }
     const int d = e.d, dh = e.dh, G = e.pair_g, half = dh >> 1;
-    AT* const kv = reinterpret_cast<AT*>(e.kv.base);
+    XT* const kv = reinterpret_cast<XT*>(e.kv.base);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -421,18 +461,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
           if (col >= N) continue;
           const float v0 = acc[i][2 * jp][r], v1 = acc[i][2 * jp + 1][r];
           if (qsect[jp] == 2) {
-            AT* vp = kv + vbase + qhead[jp] * hs;
-            vp[qcd[jp]] = from_f32<AT>(v0);
-            vp[qcd[jp] + G] = from_f32<AT>(v1);
+            XT* vp = kv + vbase + qhead[jp] * hs;
+            vp[qcd[jp]] = from_f32<XT>(v0);
+            vp[qcd[jp] + G] = from_f32<XT>(v1);
             continue;
           }
           const float cs = rcos[i][r][jp], sn = rsin[i][r][jp];
-          const float x1 = v0 * cs - v1 * sn;
-          const float x2 = v1 * cs + v0 * sn;
-          AT* dst = (qsect[jp] == 0) ? reinterpret_cast<AT*>(e.q_out) + (int64_t)row * d + qhead[jp] * dh
+          const float x1 = rot_x1(v0, v1, cs, sn);
+          const float x2 = rot_x2(v0, v1, cs, sn);
+          XT* dst = (qsect[jp] == 0) ? reinterpret_cast<XT*>(e.q_out) + (int64_t)row * d + qhead[jp] * dh
                                      : kv + kbase + qhead[jp] * hs;
-          dst[qrn[jp]] = from_f32<AT>(x1);
-          dst[qrn[jp] + half] = from_f32<AT>(x2);
+          dst[qrn[jp]] = from_f32<XT>(x1);
+          dst[qrn[jp] + half] = from_f32<XT>(x2);
         }
       }
   } else if constexpr (KIND == EPI_SWIGLU) {
@@ -447,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       const int ci = c / G;
       un[jp] = (ci >> 1) * G + (c - ci * G);
     }
-    AT* const u = reinterpret_cast<AT*>(e.u_out);
+    XT* const u = reinterpret_cast<XT*>(e.u_out);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -459,7 +499,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
           if (n0 + wn * WTN + 2 * jp * 16 + lc >= N) continue;
           const float v0 = acc[i][2 * jp][r], v1 = acc[i][2 * jp + 1][r];
           const float sg = v0 / (1.0f + expf(-v0));
-          u[(int64_t)row * e.F + un[jp]] = from_f32<AT>(sg * v1);
+          u[(int64_t)row * e.F + un[jp]] = from_f32<XT>(sg * v1);
         }
       }
   } else {
@@ -473,7 +513,7 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
 #pragma unroll
           for (int j = 0; j < TN; j += 2) {
             const int col = n0 + wn * WTN + j * 16 + lc;
-            if (col < N) epi_pair<AT, KIND>(e, row, col, acc[i][j][r], acc[i][j + 1][r]);
+            if (col < N) epi_pair<XT, KIND>(e, row, col, acc[i][j][r], acc[i][j + 1][r]);
           }
         } else {
 #pragma unroll
@@ -846,15 +886,10 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
       const floatx4 hv = hv0[u] + acc[u];
       *reinterpret_cast<floatx4*>(hr + 4 * c4) = hv;
       acc[u] = hv;
-      ss = fmaf(hv[0], hv[0], fmaf(hv[1], hv[1], fmaf(hv[2], hv[2], fmaf(hv[3], hv[3], ss))));
+      ss = sumsq4(hv[0], hv[1], hv[2], hv[3], ss);
     }
   }
-  __shared__ float red[4];
-  ss = wave_sum(ss);
-  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
-  __syncthreads();
-  const float tot = red[0] + red[1] + red[2] + red[3];
-  const float inv = 1.0f / sqrtf(tot / (float)N + e.norm_eps);
+  const float inv = rms_inv(row_sum256(ss), N, e.norm_eps);
   AT* o = reinterpret_cast<AT*>(e.norm_out) + (int64_t)row * N;
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -872,6 +907,9 @@ struct TileCfg {
 };
 
 constexpr int kCUs = 256;
+// rows the split of K is sized for when it must not depend on M (a decode-sized
+// product)
+constexpr int kInvariantRows = 64;
 
 // Tile and split choice, from sweeps of the 2048-wide model's shapes on MI355X:
 // for M <= 128 the kernels are bound by per-workgroup latency, so small tiles
@@ -880,28 +918,38 @@ constexpr int kCUs = 256;
 // M uses 128 x 128 tiles and splits K only when the tiles cannot cover the 256
 // CUs.  Dense weights at <= 32 rows that get no split (gate/up: 176 tiles of 16
 // stages) keep three stages in flight instead of one: 17.5 -> 12.3 us with the
-// weights in HBM.
+// weights in HBM.  Every tile accumulates k in the same order (32-wide steps, in
+// order, within a split), so only the split changes the arithmetic; with
+// g.invariant the split is the one kInvariantRows rows would get.
 TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
   if (act_dtype == DT_F32) return {64, 64, 1, g.K, 16, 2};
   TileCfg t{};
   t.depth = 2;
   t.splits = 1;
   t.kchunk = g.K;
-  if (g.M <= 128 && kind != EPI_HEAD) {
-    t.bm = g.M <= 32 ? 32 : 64;
-    t.bn = 64;
-    t.bk = 128;
-  } else {
-    t.bm = g.M <= 32 ? 32 : ((g.M <= 64 || g.Bw4) ? 64 : 128);   // INT4 128 x 128 would spill
-    t.bn = 128;
-    t.bk = g.Bw4 ? 128 : 64;
-  }
+  auto shape = [&](int M, int* bm, int* bn, int* bk) {
+    if (M <= 128 && kind != EPI_HEAD) {
+      *bm = M <= 32 ? 32 : 64;
+      *bn = 64;
+      *bk = 128;
+    } else {
+      *bm = M <= 32 ? 32 : ((M <= 64 || g.Bw4) ? 64 : 128);   // INT4 128 x 128 would spill
+      *bn = 128;
+      *bk = g.Bw4 ? 128 : 64;
+    }
+  };
+  shape(g.M, &t.bm, &t.bn, &t.bk);
+  const int Ms = g.invariant ? kInvariantRows : g.M;
+  int sbm = t.bm, sbn = t.bn, sbk = t.bk;
+  shape(Ms, &sbm, &sbn, &sbk);
   const int64_t tiles = (int64_t)((g.M + t.bm - 1) / t.bm) * ((g.N + t.bn - 1) / t.bn);
+  const int64_t stiles = (int64_t)((Ms + sbm - 1) / sbm) * ((g.N + sbn - 1) / sbn);
   const int64_t units = g.K / 128;   // splits cut K at 128-wide group boundaries
-  const int64_t target = g.M <= 128 ? 320 : 2 * kCUs;
-  if (kind != EPI_HEAD && g.partial && (g.N % 32) == 0 && (g.K % 128) == 0 && tiles < target && units >= 4) {
-    int64_t want = std::min<int64_t>(std::min<int64_t>(target / tiles, units / 2), 8);
-    while (want > 1 && want * g.M * g.N > g.partial_cap) --want;
+  const int64_t target = Ms <= 128 ? 320 : 2 * kCUs;
+  if (kind != EPI_HEAD && g.partial && (g.N % 32) == 0 && (g.K % 128) == 0 && stiles < target && units >= 4) {
+    int64_t want = std::min<int64_t>(std::min<int64_t>(target / stiles, units / 2), 8);
+    if (!g.invariant)
+      while (want > 1 && want * g.M * g.N > g.partial_cap) --want;
     if (want > 1) {
       const int64_t per = (units + want - 1) / want;
       t.kchunk = (int)(per * 128);
@@ -927,8 +975,9 @@ TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
 
 // Finish a split-K product: the residual GEMM with a following RMSNorm sums the
 // splits in one kernel per row and normalises (fused, *norm_done = true); the
-// others sum per element and run their epilogue.
-template <class AT>
+// others sum per element and run their epilogue.  XT: the activation type of the
+// outputs.
+template <class XT>
 hipError_t finish_splits(const GemmArgs& g, const GemmEpi& e, int splits, hipStream_t s, bool* norm_done) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
@@ -936,13 +985,13 @@ hipError_t finish_splits(const GemmArgs& g, const GemmEpi& e, int splits, hipStr
   if (e.kind == EPI_RESID && e.norm_g && (g.N % 4) == 0 && (e.ldh % 4) == 0 && vpt <= 6) {
 #define TL_RN(VPT_)                                                                                                \
   switch (splits) {                                                                                               \
-    case 2: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 2>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 3: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 3>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 4: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 4>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 5: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 5>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 6: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 6>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 8: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 8>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    default: hipLaunchKernelGGL((splitk_resid_norm_kernel<AT, VPT_, 0>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 2: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 2>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 3: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 3>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 4: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 4>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 5: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 5>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 6: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 6>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 8: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 8>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    default: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 0>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
   }
     if (vpt <= 2) { TL_RN(2) }
     else { TL_RN(6) }
@@ -954,48 +1003,49 @@ hipError_t finish_splits(const GemmArgs& g, const GemmEpi& e, int splits, hipStr
   const int64_t items = (int64_t)g.M * (pr ? g.N / 2 : g.N);
   dim3 rg((unsigned)((items + 255) / 256));
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_QKV>), rg, dim3(256), 0, s, g, e, splits); break;
-    case EPI_RESID: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_RESID>), rg, dim3(256), 0, s, g, e, splits); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_SWIGLU>), rg, dim3(256), 0, s, g, e, splits); break;
-    case EPI_STORE: hipLaunchKernelGGL((splitk_epilogue_kernel<AT, EPI_STORE>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_QKV: hipLaunchKernelGGL((splitk_epilogue_kernel<XT, EPI_QKV>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_RESID: hipLaunchKernelGGL((splitk_epilogue_kernel<XT, EPI_RESID>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((splitk_epilogue_kernel<XT, EPI_SWIGLU>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_STORE: hipLaunchKernelGGL((splitk_epilogue_kernel<XT, EPI_STORE>), rg, dim3(256), 0, s, g, e, splits); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
 
-template <class AT, bool W4, int BM, int BN, int BK, int D>
+template <class AT, class XT, bool W4, int BM, int BN, int BK, int D>
 hipError_t launch_mfma_t(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, hipStream_t s, bool* norm_done) {
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, t.splits);
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_HEAD: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_HEAD>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, W4, BM, BN, BK, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_QKV: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_HEAD: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_HEAD>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
     default: return hipErrorInvalidValue;
   }
-  if (t.splits > 1) return finish_splits<AT>(g, e, t.splits, s, norm_done);
+  if (t.splits > 1) return finish_splits<XT>(g, e, t.splits, s, norm_done);
   return hipGetLastError();
 }
 
-template <class AT, bool W4>
-hipError_t launch_mfma(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool* norm_done) {
-  const TileCfg t = pick_tile(DT_F16, g, e.kind);
+template <class AT, class XT, bool W4>
+hipError_t launch_mfma(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, hipStream_t s, bool* norm_done) {
   if (t.bn == 64) {
     if constexpr (!W4) {
-      if (t.bm == 32 && t.depth == 4) return launch_mfma_t<AT, W4, 32, 64, 128, 4>(g, e, t, s, norm_done);
+      if (t.bm == 32 && t.depth == 4) return launch_mfma_t<AT, XT, W4, 32, 64, 128, 4>(g, e, t, s, norm_done);
     }
-    if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 64, 128, 2>(g, e, t, s, norm_done);
+    if (t.bm == 32) return launch_mfma_t<AT, XT, W4, 32, 64, 128, 2>(g, e, t, s, norm_done);
     if constexpr (W4) {
-      if (t.bk == 256) return launch_mfma_t<AT, W4, 64, 64, 256, 2>(g, e, t, s, norm_done);
+      if (t.bk == 256) return launch_mfma_t<AT, XT, W4, 64, 64, 256, 2>(g, e, t, s, norm_done);
     }
-    if (t.depth == 4) return launch_mfma_t<AT, W4, 64, 64, 128, 4>(g, e, t, s, norm_done);
-    return launch_mfma_t<AT, W4, 64, 64, 128, 2>(g, e, t, s, norm_done);
+    if constexpr (!std::is_same<XT, float>::value) {   // (split operands: four stages would spill)
+      if (t.depth == 4) return launch_mfma_t<AT, XT, W4, 64, 64, 128, 4>(g, e, t, s, norm_done);
+    }
+    return launch_mfma_t<AT, XT, W4, 64, 64, 128, 2>(g, e, t, s, norm_done);
   }
-  if (t.bm == 32) return launch_mfma_t<AT, W4, 32, 128, 128, 2>(g, e, t, s, norm_done);
-  if (t.bm == 64) return launch_mfma_t<AT, W4, 64, 128, 128, 2>(g, e, t, s, norm_done);
+  if (t.bm == 32) return launch_mfma_t<AT, XT, W4, 32, 128, 128, 2>(g, e, t, s, norm_done);
+  if (t.bm == 64) return launch_mfma_t<AT, XT, W4, 64, 128, 128, 2>(g, e, t, s, norm_done);
   if constexpr (W4) return hipErrorInvalidValue;
-  else return launch_mfma_t<AT, W4, 128, 128, 64, 2>(g, e, t, s, norm_done);
+  else return launch_mfma_t<AT, XT, W4, 128, 128, 64, 2>(g, e, t, s, norm_done);
 }
 
 // ---- small-M INT4 path
@@ -1010,7 +1060,7 @@ struct SkinnyCfg {
 // and N >= 8192 the LDS-tiled kernel measured faster and is kept.
 SkinnyCfg pick_skinny(const GemmArgs& g, int kind) {
   SkinnyCfg t{0, 1, 1, 0, 2};
-  if (!g.Bw4 || g.M > 64 || kind == EPI_HEAD || (g.K % 128) != 0 || (g.N % 32) != 0) return t;
+  if (!g.Bw4 || g.invariant || g.M > 64 || kind == EPI_HEAD || (g.K % 128) != 0 || (g.N % 32) != 0) return t;
   if (g.M > 32 && g.N >= 8192) return t;
   const int bm = g.M <= 32 ? 32 : 64;
   const int units = g.K / 128;
@@ -1076,14 +1126,57 @@ int gemm_head_tiles(int act_dtype, int M, int N) {
 static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s,
                                    bool* norm_done);
 
+namespace {
+int act_bytes(int act_dtype) { return (act_dtype == DT_F32 || act_dtype == DT_F32X16) ? 4 : 2; }
+
+// Rows [r0, r0 + M) of a product: A, the epilogue's row-indexed outputs and row
+// descriptors offset to that range.
+void row_range(int act_dtype, const GemmArgs& g, const GemmEpi& e, int r0, int M, GemmArgs* gc, GemmEpi* ec) {
+  const int64_t esz = act_bytes(act_dtype);
+  *gc = g;
+  *ec = e;
+  gc->M = M;
+  gc->A = static_cast<const uint8_t*>(g.A) + (int64_t)r0 * g.K * esz;
+  if (e.rows) ec->rows = e.rows + r0;
+  if (e.q_out) ec->q_out = static_cast<uint8_t*>(e.q_out) + (int64_t)r0 * e.d * esz;
+  if (e.h) ec->h = e.h + (int64_t)r0 * e.ldh;
+  if (e.norm_out) ec->norm_out = static_cast<uint8_t*>(e.norm_out) + (int64_t)r0 * g.N * esz;
+  if (e.u_out) ec->u_out = static_cast<uint8_t*>(e.u_out) + (int64_t)r0 * e.F * esz;
+  if (e.out) ec->out = e.out + (int64_t)r0 * e.ldo;
+  if (e.logits) ec->logits = e.logits + (int64_t)r0 * e.ldl;
+  if (e.part_val) ec->part_val = e.part_val + (int64_t)r0 * e.n_tiles;
+  if (e.part_idx) ec->part_idx = e.part_idx + (int64_t)r0 * e.n_tiles;
+  if (e.part_val2) ec->part_val2 = e.part_val2 + (int64_t)r0 * e.n_tiles;
+}
+}  // namespace
+
 // Residual GEMM with a following RMSNorm: fused into the split-K reduction when K
 // is split, else the epilogue adds into h and a separate RMSNorm kernel runs.
+// With g.invariant a product whose split partials would exceed g.partial_cap runs
+// as several launches over consecutive row ranges (same split, same arithmetic).
 hipError_t launch_gemm(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
+  if (g.invariant && act_dtype != DT_F32) {
+    const TileCfg t = pick_tile(act_dtype, g, e.kind);
+    const int64_t per_row = (int64_t)t.splits * g.N;
+    if (t.splits > 1 && per_row * g.M > g.partial_cap) {
+      const int rows = (int)std::max<int64_t>(1, g.partial_cap / per_row);
+      if (rows < 1 || per_row > g.partial_cap) return hipErrorInvalidValue;
+      for (int r0 = 0; r0 < g.M; r0 += rows) {
+        GemmArgs gc;
+        GemmEpi ec;
+        row_range(act_dtype, g, e, r0, std::min(rows, g.M - r0), &gc, &ec);
+        const hipError_t err = launch_gemm(act_dtype, gc, ec, s);
+        if (err != hipSuccess) return err;
+      }
+      return hipSuccess;
+    }
+  }
   bool norm_done = false;
   hipError_t err = launch_gemm_core(act_dtype, g, e, s, &norm_done);
   if (err != hipSuccess || e.kind != EPI_RESID || !e.norm_g || norm_done) return err;
-  return launch_rmsnorm(act_dtype, e.h, e.norm_g, nullptr, g.M, g.N, e.norm_eps, e.norm_out, s);
+  const int xdt = act_dtype == DT_F32X16 ? DT_F32 : act_dtype;
+  return launch_rmsnorm(xdt, e.h, e.norm_g, nullptr, g.M, g.N, e.norm_eps, e.norm_out, s);
 }
 
 static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s,
@@ -1100,19 +1193,24 @@ static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmE
     }
     return hipGetLastError();
   }
+  const TileCfg t = pick_tile(act_dtype, g, e.kind);
   if (act_dtype == DT_F16) {
     if (g.Bw4) {
       if (e.pair_g == 16) {
-        const SkinnyCfg t = pick_skinny(g, e.kind);
-        if (t.bm) return launch_skinny(g, e, t, s, norm_done);
+        const SkinnyCfg k = pick_skinny(g, e.kind);
+        if (k.bm) return launch_skinny(g, e, k, s, norm_done);
       }
-      return launch_mfma<f16, true>(g, e, s, norm_done);
+      return launch_mfma<f16, f16, true>(g, e, t, s, norm_done);
     }
-    return launch_mfma<f16, false>(g, e, s, norm_done);
+    return launch_mfma<f16, f16, false>(g, e, t, s, norm_done);
   }
   if (act_dtype == DT_BF16) {
     if (g.Bw4) return hipErrorInvalidValue;
-    return launch_mfma<bf16, false>(g, e, s, norm_done);
+    return launch_mfma<bf16, bf16, false>(g, e, t, s, norm_done);
+  }
+  if (act_dtype == DT_F32X16) {
+    if (g.Bw4) return hipErrorInvalidValue;
+    return launch_mfma<f16, float, false>(g, e, t, s, norm_done);
   }
   return hipErrorInvalidValue;
 }

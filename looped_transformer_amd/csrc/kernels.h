@@ -5,6 +5,10 @@
 #include <stdint.h>
 
 enum DType : int32_t { DT_F32 = 0, DT_F16 = 1, DT_BF16 = 2, DT_W4G128 = 3 };
+// GEMM dispatch type of fp32 activations with fp16 weights: each product runs on
+// fp16 MFMA with the fp32 operand split into two fp16 halves (gemm.hip).  Outputs,
+// norms, attention and the KV cache are fp32 (DT_F32) in that mode.
+constexpr int32_t DT_F32X16 = 16;
 
 // One activation row of a pass.  orig: index of the row in the caller's order;
 // lane: KV lane table entry; pos: absolute position; depth: loop iterations the
@@ -38,6 +42,11 @@ struct GemmArgs {
   // device count of rows still running (early exit), or NULL: when it reads 0 the
   // kernels return at once
   const int32_t* live;
+  // nonzero: the split of K depends on (N, K) only, never on M (rows are cut into
+  // chunks when the partials of one launch would not fit partial_cap), and only
+  // the LDS-tiled MFMA kernel runs, so a row's result does not depend on the
+  // other rows of the product
+  int32_t invariant;
   // GEMV only: with norm_h set, A is the fp32 residual norm_h [M, K] normalised on
   // the fly, x = h / sqrt(mean(h^2) + norm_eps) * norm_g rounded to the operand
   // type (the RMSNorm of the producing block, computed by every workgroup); the

@@ -22,11 +22,11 @@ __global__ __launch_bounds__(256) void embed_kernel(const T* __restrict__ E, con
 }
 
 // ---------------------------------------------------------------- RMSNorm
-// x = h / sqrt(mean(h^2) + eps) * g, one wave per row; fp32 statistics.  With
-// VPT > 0 (d <= 256 VPT) a lane keeps its VPT groups of 4 values and gains in
-// registers: the row and the gain are requested in one round, and each group
-// leaves in one 8- or 16-byte store.  VPT = 0 serves any d (multiple of 4),
-// reading the row twice.
+// x = h / sqrt(mean(h^2) + eps) * g with fp32 statistics: one workgroup per row,
+// the shared arithmetic of sumsq4 / row_sum256 / rms_inv.  With VPT > 0 (d <=
+// 1024 VPT) a thread keeps its VPT groups of 4 values and gains in registers: the
+// row and the gain are requested in one round, and each group leaves in one 8- or
+// 16-byte store.  VPT = 0 serves any d (multiple of 4), reading the row twice.
 template <class T>
 __device__ __forceinline__ void store4(T* p, float a, float b, float c, float d) {
   if constexpr (sizeof(T) == 4) {
@@ -43,50 +43,38 @@ template <class T, int VPT>
 __global__ __launch_bounds__(256) void rmsnorm_kernel(const float* __restrict__ h, const float* __restrict__ g,
                                                      const int32_t* __restrict__ gather, int n, int d, float eps,
                                                      T* __restrict__ out) {
-  const int lane = threadIdx.x & 63;
-  const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (r >= n) return;
+  const int tid = threadIdx.x;
+  const int r = blockIdx.x;
   T* o = out + (int64_t)r * d;
+  const int src = gather ? gather[r] : r;
+  const float* hr = h + (int64_t)src * d;
   if constexpr (VPT > 0) {
     float4 gg[VPT], v[VPT];
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) gg[u] = *reinterpret_cast<const float4*>(g + min(lane * 4 + 256 * u, d - 4));
-    const int src = gather ? gather[r] : r;
-    const float* hr = h + (int64_t)src * d;
-#pragma unroll
-    for (int u = 0; u < VPT; ++u) v[u] = *reinterpret_cast<const float4*>(hr + min(lane * 4 + 256 * u, d - 4));
+    for (int u = 0; u < VPT; ++u) {
+      const int i = min(4 * (tid + 256 * u), d - 4);
+      gg[u] = *reinterpret_cast<const float4*>(g + i);
+      v[u] = *reinterpret_cast<const float4*>(hr + i);
+    }
     float ss = 0.f;
 #pragma unroll
-    for (int u = 0; u < VPT; ++u) {
-      if (lane * 4 + 256 * u < d) {
-        ss = fmaf(v[u].x, v[u].x, ss);
-        ss = fmaf(v[u].y, v[u].y, ss);
-        ss = fmaf(v[u].z, v[u].z, ss);
-        ss = fmaf(v[u].w, v[u].w, ss);
-      }
-    }
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int u = 0; u < VPT; ++u)
+      if (4 * (tid + 256 * u) < d) ss = sumsq4(v[u].x, v[u].y, v[u].z, v[u].w, ss);
+    const float inv = rms_inv(row_sum256(ss), d, eps);
 #pragma unroll
     for (int u = 0; u < VPT; ++u) {
-      const int i = lane * 4 + 256 * u;
+      const int i = 4 * (tid + 256 * u);
       if (i < d)
         store4(o + i, v[u].x * inv * gg[u].x, v[u].y * inv * gg[u].y, v[u].z * inv * gg[u].z, v[u].w * inv * gg[u].w);
     }
   } else {
-    const int src = gather ? gather[r] : r;
-    const float* hr = h + (int64_t)src * d;
     float ss = 0.f;
-    for (int i = lane * 4; i < d; i += 256) {
+    for (int i = 4 * tid; i < d; i += 1024) {
       const float4 v = *reinterpret_cast<const float4*>(hr + i);
-      ss = fmaf(v.x, v.x, ss);
-      ss = fmaf(v.y, v.y, ss);
-      ss = fmaf(v.z, v.z, ss);
-      ss = fmaf(v.w, v.w, ss);
+      ss = sumsq4(v.x, v.y, v.z, v.w, ss);
     }
-    ss = wave_sum(ss);
-    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
-    for (int i = lane * 4; i < d; i += 256) {
+    const float inv = rms_inv(row_sum256(ss), d, eps);
+    for (int i = 4 * tid; i < d; i += 1024) {
       const float4 v = *reinterpret_cast<const float4*>(hr + i);
       const float4 gg = *reinterpret_cast<const float4*>(g + i);
       store4(o + i, v.x * inv * gg.x, v.y * inv * gg.y, v.z * inv * gg.z, v.w * inv * gg.w);
@@ -132,14 +120,10 @@ __global__ __launch_bounds__(256) void embed_norm_kernel(const T* __restrict__ E
     v[u] = load4(src + min(i, d - 4));
     if (i < d) {
       *reinterpret_cast<float4*>(dst + i) = v[u];
-      ss = fmaf(v[u].x, v[u].x, fmaf(v[u].y, v[u].y, fmaf(v[u].z, v[u].z, fmaf(v[u].w, v[u].w, ss))));
+      ss = sumsq4(v[u].x, v[u].y, v[u].z, v[u].w, ss);
     }
   }
-  __shared__ float red[4];
-  ss = wave_sum(ss);
-  if ((tid & 63) == 0) red[tid >> 6] = ss;
-  __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)d + eps);
+  const float inv = rms_inv(row_sum256(ss), d, eps);
   X* xo = x + (int64_t)r * d;
 #pragma unroll
   for (int u = 0; u < VPT; ++u) {
@@ -657,8 +641,8 @@ hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const i
                           void* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (d < 4 || (d % 4) != 0) return hipErrorInvalidValue;
-  dim3 grid((n + 3) / 4);
-  const int vpt = d <= 256 ? 1 : d <= 512 ? 2 : d <= 1024 ? 4 : d <= 2048 ? 8 : 0;
+  dim3 grid(n);
+  const int vpt = d <= 1024 ? 1 : d <= 2048 ? 2 : d <= 4096 ? 4 : d <= 8192 ? 8 : 0;
 #define TL_RMS(T, V)                                                                                          \
   hipLaunchKernelGGL((rmsnorm_kernel<T, V>), grid, dim3(256), 0, s, h, g, gather, n, d, eps, (T*)out)
 #define TL_RMS_T(T)                      \

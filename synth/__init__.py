@@ -162,7 +162,7 @@ SPECS = {
     2: ModelSpec("d2048-int4loop", 50304, 2048, 16, 128, 5632, 1, 1, 0, "f16", "w4g128"),
     3: ModelSpec("d2048-fp16body", 50304, 2048, 16, 128, 5632, 1, 1, 0, "f16", "f16body"),
     4: ModelSpec("d2048-int4loop", 50304, 2048, 16, 128, 5632, 1, 1, 0, "f16", "w4g128"),
-    5: ModelSpec("d5280-bf16-stack4", 65536, 5280, 55, 96, 17920, 2, 4, 2, "bf16", "bf16", act="f16"),
+    5: ModelSpec("d5280-bf16-stack4", 65536, 5280, 55, 96, 17920, 2, 4, 2, "bf16", "bf16", act="f32"),
 }
 
 

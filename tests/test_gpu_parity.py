@@ -28,6 +28,9 @@ TINY = {
     # INT4, 16 K groups in the down projection: at decode sizes its K is split 16
     # ways, more than the fused residual + norm reduction loads at once
     "tiny-w4-wide": synth.ModelSpec("tiny-w4-wide", 256, 256, 4, 64, 2048, 1, 1, 0, "f16", "w4g128"),
+    # bf16 weights with fp32 activations and K/V: products on fp16 MFMA with the
+    # fp32 operands split into two fp16 halves
+    "tiny-wide": synth.ModelSpec("tiny-wide", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16", act="f32"),
 }
 
 
@@ -37,7 +40,7 @@ def say(*a):
 
 
 def hidden_bar(spec, L):
-    if spec.boundary_dtype == "f32":
+    if spec.act_dtype == "f32":
         return 1e-4
     return 1e-2 if L <= 8 else 3e-2
 
@@ -93,8 +96,8 @@ def test_tiny_forward_parity(name):
         assert r <= hidden_bar(spec, Ls[i]), (i, r)
         assert rm <= hidden_bar(spec, Ls[i]), (i, rm)
         off += len(s)
-    assert rel_l2(lg, ref_lg) <= (1e-4 if spec.boundary_dtype == "f32" else 1e-2)
-    if spec.boundary_dtype == "f32":
+    assert rel_l2(lg, ref_lg) <= (1e-4 if spec.act_dtype == "f32" else 1e-2)
+    if spec.act_dtype == "f32":
         assert np.array_equal(nxt, oracle.greedy_argmax(ref_lg))
     else:
         # 16-bit operands: a token may differ only where the oracle's own best two
@@ -197,7 +200,7 @@ def test_cfg1_forward_and_greedy_decode():
         tl.tl_free(model)
 
 
-@pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack", "tiny-w4-wide"])
+@pytest.mark.parametrize("name", ["tiny-w4", "tiny-bf16-stack", "tiny-w4-wide", "tiny-wide"])
 def test_tiny_decode_mixed_and_monotone_depth(name):
     """Lanes at different depths, per-token requests clamped to never rise."""
     spec = TINY[name]
