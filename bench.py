@@ -5,8 +5,12 @@ Step: one forward scoring pass of the 2048-wide model with an INT4 shared loop
 block (vocab 50304, 16 heads x 128, SwiGLU 5632, 1 pre block, 1 x 128 tokens,
 L = 8, no logits) with inputs resident in HBM.  Reported value: token-loop
 iterations per second (128 tokens x 8 iterations per step); ms_per_step is the
-milliseconds per seq-128 L = 8 forward.  Secondary field: greedy cached decode
-tok/s at L = 8 on the FP16-body model (32 lanes, 32-token prompts).
+milliseconds per seq-128 L = 8 forward.  Secondary fields: greedy cached decode
+tok/s at L = 8 on the FP16-body model (32 lanes, 32-token prompts), the FP16-body
+32 x 128 forward at L = 2, 8 and 32, L-aware INT4 decode (64 lanes), the
+Infinity-Cache residency control, shared-prefix reuse, self-speculative and
+store-h decoding, the 5280-wide continuous-depth workload (prefill, continuous
+depth and lockstep decode), and the CPU oracle timed on the host.
 
 Prints one JSON line.  Synthetic seeded weights and token ids (no checkpoint).
 """
@@ -39,7 +43,8 @@ def parse():
     ap.add_argument("--no-spec", action="store_true", help="skip the self-speculative measurement")
     ap.add_argument("--no-store-h", action="store_true", help="skip the store-h cache-mode measurement")
     ap.add_argument("--no-extra-configs", action="store_true",
-                    help="skip the FP16-body 32 x 128 forward and the L-aware 64-lane INT4 decode")
+                    help="skip the FP16-body 32 x 128 forwards, the L-aware 64-lane INT4 decode and the MALL control")
+    ap.add_argument("--no-cfg5", action="store_true", help="skip the 5280-wide continuous-depth workload")
     ap.add_argument("--profile-only", action="store_true", help="run the timed steps only (for rocprofv3)")
     ap.add_argument("--profile-decode", action="store_true",
                     help="run batch-1 INT4 decode steps only (32-token prompt, 63 steps at L=8; for rocprofv3)")
@@ -74,11 +79,24 @@ def traffic_for(kernel_class: str):
     return rec.get("bytes_per_launch")
 
 
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def cpu_baseline(seconds: float):
+    """The fp64 numpy oracle on the host: the same cfg-2 forward (1 x 128 tokens,
+    L = 8), with every BLAS thread for about `seconds`, then one forward on one
+    thread."""
     import numpy as np
     import oracle
     import synth
-    from threadpoolctl import threadpool_info
+    from threadpoolctl import threadpool_info, threadpool_limits
     spec = synth.SPECS[2]
     w = synth.make_weights(spec, 0)
     m = oracle.OracleModel.from_weights(w)
@@ -91,10 +109,17 @@ def cpu_baseline(seconds: float):
         if el >= seconds or runs >= 50:
             break
     threads = max([p.get("num_threads", 1) for p in threadpool_info() if p.get("user_api") == "blas"] or [1])
+    with threadpool_limits(limits=1):
+        t1 = time.perf_counter()
+        oracle.prefill(m, toks, 8, want_logits="none")
+        el1 = time.perf_counter() - t1
     return {"value": round(1024 * runs / el, 1), "unit": "token-loop iterations/s", "cores": int(threads),
             "kind": "oracle",
             "sample": "%d full forwards of the same workload (1x128 tokens, L=8) by the fp64 numpy oracle, %.1f s"
-                      % (runs, el)}
+                      % (runs, el),
+            "nproc": os.cpu_count(), "cpu_model": cpu_model(),
+            "one_thread": {"value": round(1024 / el1, 1), "unit": "token-loop iterations/s", "cores": 1,
+                           "sample": "one forward of the same workload on one BLAS thread, %.1f s" % el1}}
 
 
 def main():
@@ -190,15 +215,21 @@ def main():
     if not args.no_decode:
         out["decode_L8"] = decode_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_extra_configs:
-        out["forward_fp16_L8"] = forward_fp16_bench(tl, torch, np, synth, load_model,
-                                                    synth.make_weights(synth.SPECS[3], 0))
+        w3 = synth.make_weights(synth.SPECS[3], 0)
+        for L in (2, 8, 32):
+            out["forward_fp16_L%d" % L] = forward_fp16_bench(tl, torch, np, synth, load_model, w3, L)
+        del w3
         out["decode_lane_aware"] = lane_aware_bench(tl, torch, np, synth, kv_bytes, load_model)
+        out["mall_control"] = mall_bench(tl, torch, np, synth, load_model)
     if not args.no_prefix:
         out["shared_prefix"] = prefix_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_spec:
         out["speculative_B1"] = spec_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_store_h:
         out["store_h_B1"] = store_h_bench(tl, torch, np, synth, kv_bytes, load_model)
+    if not args.no_cfg5:
+        torch.cuda.empty_cache()
+        out["cfg5_continuous_depth"] = cfg5_bench(tl, torch, np, synth, kv_bytes, load_model)
     if not args.no_cpu_baseline:
         log("cpu baseline")
         out["cpu_baseline"] = cpu_baseline(args.cpu_seconds)
@@ -268,12 +299,12 @@ def hbm_rate(nbytes, seconds):
             "peak_GBps": HBM_PEAK_GBPS, "frac": round(gbps / HBM_PEAK_GBPS, 4)}
 
 
-def forward_fp16_bench(tl, torch, np, synth, load_model, w):
-    """Scoring forward of 32 x 128 tokens at L = 8 on the FP16-body model (4096 rows per
-    pass), graph-replayed like the main forward; best of 3 timed runs of 5 calls."""
+def forward_fp16_bench(tl, torch, np, synth, load_model, w, L):
+    """Scoring forward of 32 x 128 tokens at depth L on the FP16-body model (4096 rows
+    per pass), graph-replayed like the main forward; best of 3 timed runs of 5 calls."""
     spec = synth.SPECS[3]
-    log("forward: FP16-body model, 32 x 128 tokens, L=8")
-    n, T, L = 32, 128, 8
+    log("forward: FP16-body model, 32 x 128 tokens, L=%d" % L)
+    n, T = 32, 128
     model = load_model(w, max_pos=256)
     toks = torch.tensor(synth.tokens(0, synth.STREAM_TOKENS, n * T, spec.vocab), dtype=torch.int32, device="cuda")
     cu = np.arange(0, n * T + 1, T, dtype=np.int32)
@@ -295,7 +326,7 @@ def forward_fp16_bench(tl, torch, np, synth, load_model, w):
     flops = n * T * (spec.n_pre + L * spec.n_loop + spec.n_post) * per_token_block \
         + n * (spec.n_pre + L * spec.n_loop + spec.n_post) * 4 * (T * T // 2) * d
     tf = flops / best / 1e12
-    return {"config": "FP16-body loop block (2048-wide), 32 sequences x 128 tokens, L=8, no logits",
+    return {"config": "FP16-body loop block (2048-wide), 32 sequences x 128 tokens, L=%d, no logits" % L,
             "ms": round(best * 1e3, 3), "token_iterations_per_s": round(n * T * L / best, 1),
             "mfma": {"algorithmic_flops": int(flops), "achieved_TFLOPs": round(tf, 1), "peak_TFLOPs": PEAK_F16_TFLOPS,
                      "frac": round(tf / PEAK_F16_TFLOPS, 4)}}
@@ -541,6 +572,123 @@ def spec_bench(tl, torch, np, synth, kv_bytes, load_model):
                    "32-token prompt")
     tl.tl_free(model)
     return res
+
+
+def mall_bench(tl, torch, np, synth, load_model):
+    """The pages' L2-residency control ("Benchmark Comparison" page, measured
+    benchmarks, section 6: one loop iteration with its weights warm in cache vs
+    flushed) moved to the 256 MB Infinity Cache: one-iteration forwards (1 x 128
+    tokens, L = 1) of the INT4 model, repeated (the loop block's 26.5 MB stay
+    resident) or each after streaming 512 MB through the memory system; kernel-
+    class event timing of the loop block's products."""
+    spec = synth.SPECS[2]
+    log("MALL control: INT4 model, L=1 forwards, warm vs flushed")
+    w = synth.make_weights(spec, 0)
+    model = load_model(w, max_pos=256)
+    toks = torch.tensor(synth.tokens(0, synth.STREAM_TOKENS, 128, spec.vocab), dtype=torch.int32, device="cuda")
+    cu = np.array([0, 128], np.int32)
+    hid = torch.empty(128, spec.d_model, dtype=torch.float32, device="cuda")
+    src = torch.ones(64 << 20, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    loop_cls = ("gemm_qkv_loop", "gemm_o_loop", "gemm_gu_loop", "gemm_down_loop")
+    res = {"config": "INT4 model (2048-wide), 1 x 128 tokens, L=1 (one loop iteration per call); flushed = "
+                     "256 MiB copied (512 MiB streamed) before each call; per-launch microseconds of the loop "
+                     "block's four products (event-timed) and of the whole call",
+           "loop_block_bytes": block_weight_bytes(spec, True)}
+    reps = 30
+    for name, flush in (("warm", False), ("flushed", True)):
+        for _ in range(3):
+            tl.tl_forward(model, cu, toks, L=1, out_hidden=hid, stream=0)
+        torch.cuda.synchronize()
+        tl.tl_timing_enable(model, True)
+        call_ms = []
+        for _ in range(reps):
+            if flush:
+                dst.copy_(src)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            tl.tl_forward(model, cu, toks, L=1, out_hidden=hid, stream=0)
+            torch.cuda.synchronize()
+            call_ms.append((time.perf_counter() - t0) * 1e3)
+        cls = tl.tl_timing_read(model)
+        tl.tl_timing_enable(model, False)
+        row = {k: round(cls[k][0] / cls[k][1] * 1e3, 2) for k in loop_cls if cls[k][1]}
+        row["loop_block_us"] = round(sum(cls[k][0] for k in loop_cls) / reps * 1e3, 2)
+        row["call_ms_median"] = round(float(np.median(call_ms)), 4)
+        res[name] = row
+        log("MALL %s: %s" % (name, row))
+    res["flushed_over_warm_loop_block"] = round(res["flushed"]["loop_block_us"] / res["warm"]["loop_block_us"], 3)
+    tl.tl_free(model)
+    return res
+
+
+def cfg5_bench(tl, torch, np, synth, kv_bytes, load_model):
+    """Continuous-depth decode on the 5280-wide bf16 model (2 pre blocks, a 4-layer
+    loop stack, 2 post blocks): 256 sequences, prompts uniform in [32, 512], 64 new
+    tokens each (the first from the prefill, 63 cached), per-token depth
+    min(32, 1 + Poisson(7)) clamped to never rise.  fp32 activations and K/V on
+    split-fp16 matrix cores, batch-invariant kernels.  Times the prefill, the
+    continuous-depth decode (tl_decode_run, boundary queue of 64 lanes) and the
+    same decode in lockstep (one tl_decode_step per token, iteration-level
+    compaction); both give the same tokens bit for bit."""
+    spec = synth.SPECS[5]
+    log("cfg 5: 5280-wide model, 256 sequences")
+    n, new = 256, 64
+    w = synth.make_weights(spec, 0)
+    plens = synth.prompt_lengths(0, n)
+    prompts = [synth.tokens(0, 3000 + i, int(p), spec.vocab) for i, p in enumerate(plens)]
+    draws = synth.token_loop_draws(0, n, new)
+    L1 = draws[:, 0].copy()
+    model = load_model(w, max_lanes=n, max_pos=512 + new, max_L=32,
+                       kv_arena_bytes=kv_bytes(spec, L1, plens + new - 1), batch_invariant=1)
+    del w
+    toks = torch.tensor(np.concatenate(prompts), dtype=torch.int32, device="cuda")
+    cu = np.concatenate([[0], np.cumsum(plens)]).astype(np.int32)
+    lanes = np.arange(n, dtype=np.int32)
+    T = int(cu[-1])
+    ds = torch.cuda.Stream()
+
+    def prefill():
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        tl.tl_forward(model, cu, toks, seq_L=L1, lanes=lanes, max_new_tokens=new - 1, stream=ds)
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0
+
+    t_pre = prefill()
+    out_run = torch.empty(n, new - 1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    eff = tl.tl_decode_run(model, lanes, draws[:, 1:], out_run, boundary_min=64, stream=ds)
+    torch.cuda.synchronize()
+    t_cdb = time.perf_counter() - t0
+    prefill()
+    out = torch.empty(n, dtype=torch.int32, device="cuda")
+    step_tok = torch.empty(n, new - 1, dtype=torch.int32, device="cuda")
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for t in range(new - 1):
+        tl.tl_decode_step(model, lanes, draws[:, 1 + t], out, stream=ds)
+        with torch.cuda.stream(ds):   # ordered after the step that wrote out
+            step_tok[:, t].copy_(out)
+    torch.cuda.synchronize()
+    t_lock = time.perf_counter() - t0
+    same = bool(torch.equal(step_tok, out_run))
+    tl.tl_free(model)
+    iters = int(eff.sum())
+    pre_iters = int(np.sum(plens * L1))
+    return {"config": "5280-wide bf16 model (2 pre + 4-layer loop stack + 2 post, 55x96 heads, SwiGLU 17920, "
+                      "vocab 65536), 256 sequences, prompts uniform in [32, 512] (%d rows), 64 new tokens, per-token "
+                      "L = min(32, 1 + Poisson(7)) clamped monotone; fp32 activations, split-fp16 MFMA, "
+                      "batch-invariant" % T,
+            "prefill_s": round(t_pre, 3), "prefill_token_iterations_per_s": round(pre_iters / t_pre, 1),
+            "decode_token_iterations": iters,
+            "continuous_depth": {"s": round(t_cdb, 3), "tok_per_s": round(n * (new - 1) / t_cdb, 1),
+                                 "token_iterations_per_s": round(iters / t_cdb, 1)},
+            "lockstep": {"s": round(t_lock, 3), "tok_per_s": round(n * (new - 1) / t_lock, 1),
+                         "token_iterations_per_s": round(iters / t_lock, 1)},
+            "lockstep_over_continuous": round(t_lock / t_cdb, 3),
+            "same_tokens": same}
 
 
 def store_h_bench(tl, torch, np, synth, kv_bytes, load_model):
