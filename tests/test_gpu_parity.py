@@ -28,6 +28,9 @@ TINY = {
     # INT4, 16 K groups in the down projection: at decode sizes its K is split 16
     # ways, more than the fused residual + norm reduction loads at once
     "tiny-w4-wide": synth.ModelSpec("tiny-w4-wide", 256, 256, 4, 64, 2048, 1, 1, 0, "f16", "w4g128"),
+    # INT4 with SwiGLU 4096: at 65..128 rows gate/up (N = 8192) and down (K = 4096)
+    # take the row-tiled INT4 kernel (down with K split 4 ways)
+    "mid-w4-ffn4096": synth.ModelSpec("mid-w4-ffn4096", 256, 256, 4, 64, 4096, 1, 1, 0, "f16", "w4g128"),
     # bf16 weights with fp32 activations and K/V: products on fp16 MFMA with the
     # fp32 operands split into two fp16 halves
     "tiny-wide": synth.ModelSpec("tiny-wide", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16", act="f32"),
