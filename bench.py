@@ -50,6 +50,8 @@ def parse():
                     help="run batch-1 INT4 decode steps only (32-token prompt, 63 steps at L=8; for rocprofv3)")
     ap.add_argument("--profile-decode-fp16", action="store_true",
                     help="run 32-lane FP16-body decode steps only (32-token prompts, 31 steps at L=8; for rocprofv3)")
+    ap.add_argument("--profile-lane-aware", action="store_true",
+                    help="run the 64-lane L-aware INT4 decode steps only (for rocprofv3)")
     ap.add_argument("--eager", action="store_true", help="launch kernels one by one (no graph replay)")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="after the steps, copy 256 MiB once with a plain device copy (counter calibration)")
@@ -138,6 +140,9 @@ def main():
     ensure_built()
     if args.profile_decode:
         profile_decode(tl, torch, np, synth, kv_bytes, load_model)
+        return
+    if args.profile_lane_aware:
+        lane_aware_bench(tl, torch, np, synth, kv_bytes, load_model)
         return
     if args.profile_decode_fp16:
         profile_decode_fp16(tl, torch, np, synth, kv_bytes, load_model)

@@ -714,149 +714,23 @@ __global__ __launch_bounds__(256) void gemm_skinny_w4_kernel(GemmArgs g, GemmEpi
     }
 }
 
-// INT4 GEMM for passes of 65..128 rows (a 128-token forward, prefill chunks):
-// the small-M kernel's structure with the rows cut into BM = 64 tiles.
-//  * A (BM x 128 GPS fp16 per stage of GPS groups) goes global -> registers ->
-//    LDS once per workgroup, 16-byte chunks XOR-swizzled by (row mod 16) within
-//    each group's 16 chunks;
-//  * the four waves are arranged WM x (4 / WM): a wave owns BM / WM rows and one
-//    32-column block, whose INT4 fragments it loads straight from global memory in
-//    MFMA order (two coalesced 1 KB loads per group) and expands in registers;
-//  * 32x32x16 MFMAs form each group's sum in a fresh accumulator, multiplied by
-//    the column's fp32 scale and added.
-// A sweep at 128 rows of the 2048-wide model's products (per-launch event timing,
-// a dependent kernel before each launch) measured gate/up (N = 11264) at 18.5 us
-// with WM = 1, one group per stage and no split, against 23.1 us for the LDS-tiled
-// kernel, and the down projection (K = 5632) at 17.3 us with WM = 2, two groups per
-// stage and K split 4 ways (reduction included) against 20.7 us; QKV and O came
-// out even and stay on the tiled kernel.
-template <int WM, int GPS, int D, int KIND>
-__global__ __launch_bounds__(256, 2) void gemm_w4_rows_kernel(GemmArgs g, GemmEpi e, int kchunk) {
-  constexpr int BM = 64;
-  constexpr int WN = 4 / WM;
-  constexpr int RB = BM / WM / 32;       // 32-row blocks per wave
-  constexpr int BN = WN * 32;
-  constexpr int KC = GPS * 16;           // 16-byte chunks of one A row per stage
-  constexpr int AC = BM * KC / 256;      // per thread
-  static_assert(WM * WN == 4 && RB >= 1 && D >= 2 && AC >= 1, "tile");
-  __shared__ u32x4 As[2][BM * KC];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave / WN, wn = wave % WN;
-  const int m0 = blockIdx.y * BM, wn0 = blockIdx.x * BN + wn * 32, wr0 = wm * (BM / WM);
-  const int M = g.M, N = g.N, K = g.K, groups = K >> 7;
-  const int S = gridDim.z, z = blockIdx.z;
-  const int kb = z * kchunk, ke = min(K, kb + kchunk);
-  const int g0 = kb >> 7, gend = ke >> 7;
-  const int nreal = (gend - g0 + GPS - 1) / GPS;   // stages
-  const int nst = (nreal + D - 1) / D * D;
-  const f16* A = reinterpret_cast<const f16*>(g.A);
-
-  floatx16 acc[RB];
-#pragma unroll
-  for (int i = 0; i < RB; ++i)
-#pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
-
-  // register ring; every address is clamped into its operand (stages or groups
-  // past the split's end are given scale 0)
-  u32x4 ra[D][AC];
-  u32x4 rw[D][GPS][2];
-  uint16_t rs[D][GPS];
-  auto gload = [&](auto uc, int st) __attribute__((always_inline)) {
-    constexpr int u = decltype(uc)::value;
-    const int sc = min(st, nreal - 1);
-#pragma unroll
-    for (int i = 0; i < AC; ++i) {
-      const int c = tid + 256 * i, r = c / KC, ch = c % KC;
-      const int gr = min(m0 + r, M - 1);
-      const int gk = min((g0 + sc * GPS) * 128 + ch * 8, K - 8);
-      ra[u][i] = *reinterpret_cast<const u32x4*>(A + (int64_t)gr * K + gk);
-    }
-    const int nb = min(wn0 >> 5, (N >> 5) - 1);
-#pragma unroll
-    for (int go = 0; go < GPS; ++go) {
-      const int gi = min(g0 + sc * GPS + go, groups - 1);
-      const uint32_t* wp = g.Bw4 + ((int64_t)nb * groups + gi) * 512 + lane * 4;
-      rw[u][go][0] = *reinterpret_cast<const u32x4*>(wp);
-      rw[u][go][1] = *reinterpret_cast<const u32x4*>(wp + 256);
-      rs[u][go] = g.Bs[(int64_t)gi * N + min(wn0 + (lane & 31), N - 1)];
-    }
-  };
-  auto slot = [](int r, int ch) { return r * KC + ((ch & ~15) | ((ch & 15) ^ (r & 15))); };
-  auto lstore = [&](auto uc, int buf) __attribute__((always_inline)) {
-    constexpr int u = decltype(uc)::value;
-#pragma unroll
-    for (int i = 0; i < AC; ++i) {
-      const int c = tid + 256 * i;
-      As[buf][slot(c / KC, c % KC)] = ra[u][i];
-    }
-  };
-  auto compute = [&](auto uc, int buf, int st) __attribute__((always_inline)) {
-    constexpr int u = decltype(uc)::value;
-#pragma unroll
-    for (int go = 0; go < GPS; ++go) {
-      const bool valid = st < nreal && g0 + st * GPS + go < gend;
-      floatx16 tmp[RB];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        half8 a[RB];
-#pragma unroll
-        for (int i = 0; i < RB; ++i)
-          a[i] = __builtin_bit_cast(half8, As[buf][slot(wr0 + 32 * i + (lane & 31), go * 16 + 2 * j + (lane >> 5))]);
-        half8 b;
-        half2v t[4];
-        w4_pairs(rw[u][go][j >> 2][j & 3], t);
-#pragma unroll
-        for (int p = 0; p < 4; ++p) {
-          b[2 * p] = t[p][0];
-          b[2 * p + 1] = t[p][1];
-        }
-#pragma unroll
-        for (int i = 0; i < RB; ++i) {
-          if (j == 0) {
-            floatx16 zero;
-#pragma unroll
-            for (int r = 0; r < 16; ++r) zero[r] = 0.f;
-            tmp[i] = mfma32(a[i], b, zero);
-          } else {
-            tmp[i] = mfma32(a[i], b, tmp[i]);
-          }
-        }
-      }
-      const float sc = valid ? (float)__builtin_bit_cast(f16, rs[u][go]) : 0.f;
-#pragma unroll
-      for (int i = 0; i < RB; ++i) acc[i] += sc * tmp[i];
-    }
-  };
-
-  static_for<0, D - 1>([&](auto uc) __attribute__((always_inline)) { gload(uc, decltype(uc)::value); });
-  if (gate_closed(g.live)) return;
-  for (int s0 = 0; s0 < nst; s0 += D) {
-    static_for<0, D>([&](auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value;
-      const int st = s0 + u;
-      lstore(uc, st & 1);
-      lds_barrier();
-      gload(std::integral_constant<int, (u + D - 1) % D>{}, st + D - 1);
-      // keep the prefetch ahead of this stage's MFMAs
-      asm volatile("" ::: "memory");
-      __builtin_amdgcn_sched_barrier(0);
-      compute(uc, st & 1, st);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-  }
-
-  // C layout of a 32x32 tile: lane holds column (lane & 31), rows
-  // 8 (r / 4) + 4 (lane / 32) + (r mod 4) for r = 0 .. 15
+// Output of a wave that holds RB 32 x 32 tiles (rows r0 + 32 i, columns c0 ..
+// c0 + 31) of a row-tiled INT4 product: split partials, or the epilogue.  C layout
+// of a 32x32 tile: lane holds column (lane & 31), rows 8 (r / 4) + 4 (lane / 32) +
+// (r mod 4) for r = 0 .. 15.
+template <int RB, int KIND>
+__device__ __forceinline__ void rows_store(const GemmArgs& g, const GemmEpi& e, const floatx16 (&acc)[RB], int r0,
+                                           int c0, int lane) {
+  const int M = g.M, N = g.N, S = gridDim.z;
   const int lc = lane & 31, lh = lane >> 5;
-  const int col = wn0 + lc;
+  const int col = c0 + lc;
   if (S > 1) {
-    float* part = g.partial + (int64_t)z * M * N;
+    float* part = g.partial + (int64_t)blockIdx.z * M * N;
 #pragma unroll
     for (int i = 0; i < RB; ++i)
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wr0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+        const int row = r0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
         if (row < M && col < N) part[(int64_t)row * N + col] = acc[i][r];
       }
     return;
@@ -865,7 +739,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_rows_kernel(GemmArgs g, GemmEp
   for (int i = 0; i < RB; ++i)
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
-      const int row = m0 + wr0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
+      const int row = r0 + 32 * i + 8 * (r >> 2) + 4 * lh + (r & 3);
       const float v = acc[i][r];
       if constexpr (paired(KIND)) {
         // pair (c, c + 16) of a 32-column block: the partner sits 16 lanes away
@@ -875,6 +749,229 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_rows_kernel(GemmArgs g, GemmEp
         if (row < M && col < N) epi_one<KIND>(e, row, col, v);
       }
     }
+}
+
+// One 128-wide group of a row-tiled INT4 product on a wave: RB A fragments per k
+// step from the LDS stage (16-byte chunks XOR-swizzled by row within the group's 16),
+// the wave's 32-column INT4 fragments (two 16-byte words per lane, in MFMA order)
+// expanded in registers, 32x32x16 MFMAs into a fresh group sum that is scaled by the
+// column's fp32 group scale and added.  After k step j the callback issues piece j of
+// the next stage's loads, so that they leave one at a time between the MFMAs: issued
+// together ahead of the MFMAs, the wave's in-order issue held its MFMAs until the
+// memory pipeline had taken every load (gate/up at 128 rows: 18.9 -> 17.9 us per
+// launch with four waves).
+template <int RB, int KC, class Issue>
+__device__ __forceinline__ void rows_group(floatx16 (&acc)[RB], const u32x4* As, int r0, int ch0, int lane,
+                                           const u32x4 (&w)[2], float sc, Issue&& issue) {
+  floatx16 tmp[RB];
+  static_for<0, 8>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value;
+    half8 a[RB];
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      const int r = r0 + 32 * i + (lane & 31), ch = ch0 + 2 * j + (lane >> 5);
+      a[i] = __builtin_bit_cast(half8, As[r * KC + ((ch & ~15) | ((ch & 15) ^ (r & 15)))]);
+    }
+    half8 b;
+    half2v t[4];
+    w4_pairs(w[j >> 2][j & 3], t);
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      b[2 * p] = t[p][0];
+      b[2 * p + 1] = t[p][1];
+    }
+#pragma unroll
+    for (int i = 0; i < RB; ++i) {
+      if constexpr (j == 0) {
+        floatx16 zero;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) zero[r] = 0.f;
+        tmp[i] = mfma32(a[i], b, zero);
+      } else {
+        tmp[i] = mfma32(a[i], b, tmp[i]);
+      }
+    }
+    issue(jc);
+  });
+#pragma unroll
+  for (int i = 0; i < RB; ++i) acc[i] += sc * tmp[i];
+}
+
+// INT4 GEMM for passes of 65..128 rows (a 128-token forward, prefill chunks): the
+// small-M kernel's structure with the rows cut into BM = 64 tiles.
+//  * A (64 x 128 fp16 per stage) goes global -> registers -> LDS once per workgroup;
+//  * the four waves are arranged WM x (4 / WM): a wave owns 64 / WM rows and one
+//    32-column block, whose INT4 fragments it loads straight from global memory
+//    (two coalesced 1 KB loads per group) and expands in registers (rows_group);
+//  * a two-stage register ring, the next stage's loads issued between this stage's
+//    MFMAs.
+// At 128 rows of the 2048-wide model (per-launch event timing, a dependent kernel
+// before each launch) the down projection (K = 5632, WM = 2, K split 4 ways,
+// reduction included) took 17.1 us against 20.7 us on the LDS-tiled kernel.
+template <int WM, int KIND>
+__global__ __launch_bounds__(256, 2) void gemm_w4_rows_kernel(GemmArgs g, GemmEpi e, int kchunk) {
+  constexpr int BM = 64, KC = 16, AC = BM * KC / 256;
+  constexpr int WN = 4 / WM;
+  constexpr int RB = BM / WM / 32;
+  static_assert(WM * WN == 4 && RB >= 1, "tile");
+  __shared__ u32x4 As[2][BM * KC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / WN, wn = wave % WN;
+  const int m0 = blockIdx.y * BM, wn0 = blockIdx.x * (WN * 32) + wn * 32, wr0 = wm * (BM / WM);
+  const int M = g.M, N = g.N, K = g.K, groups = K >> 7;
+  const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
+  const int g0 = kb >> 7, nreal = (ke >> 7) - g0;
+  const int nst = (nreal + 1) & ~1;
+  const int nb = min(wn0 >> 5, (N >> 5) - 1);
+  const f16* A = reinterpret_cast<const f16*>(g.A);
+
+  floatx16 acc[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  // two-stage register ring; every address is clamped into its operand (stages past
+  // the split's end are given scale 0)
+  u32x4 ra[2][AC];
+  u32x4 rw[2][2];
+  uint16_t rs[2];
+  // piece p of stage st's loads into ring slot u: the A chunks, then the two INT4
+  // words, then the scale
+  auto piece = [&](auto uc, auto pc, int st) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value, p = decltype(pc)::value;
+    const int gi = min(g0 + min(st, nreal - 1), groups - 1);
+    if constexpr (p < AC) {
+      const int c = tid + 256 * p, r = c / KC, ch = c % KC;
+      ra[u][p] = *reinterpret_cast<const u32x4*>(A + (int64_t)min(m0 + r, M - 1) * K + gi * 128 + ch * 8);
+    } else if constexpr (p == AC) {
+      rw[u][0] = *reinterpret_cast<const u32x4*>(g.Bw4 + ((int64_t)nb * groups + gi) * 512 + lane * 4);
+    } else if constexpr (p == AC + 1) {
+      rw[u][1] = *reinterpret_cast<const u32x4*>(g.Bw4 + ((int64_t)nb * groups + gi) * 512 + 256 + lane * 4);
+    } else if constexpr (p == AC + 2) {
+      rs[u] = g.Bs[(int64_t)gi * N + min(wn0 + (lane & 31), N - 1)];
+    }
+  };
+  auto lstore = [&](auto uc, int buf) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int c = tid + 256 * i, r = c / KC, ch = c % KC;
+      As[buf][r * KC + (ch ^ (r & 15))] = ra[u][i];
+    }
+  };
+
+  static_for<0, AC + 3>([&](auto pc) __attribute__((always_inline)) { piece(std::integral_constant<int, 0>{}, pc, 0); });
+  if (gate_closed(g.live)) return;
+  for (int s0 = 0; s0 < nst; s0 += 2) {
+    static_for<0, 2>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      const int st = s0 + u;
+      lstore(uc, st & 1);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      const float sc = st < nreal ? (float)__builtin_bit_cast(f16, rs[u]) : 0.f;
+      rows_group<RB, KC>(acc, As[st & 1], wr0, 0, lane, rw[u], sc, [&](auto jc) __attribute__((always_inline)) {
+        piece(std::integral_constant<int, 1 - u>{}, jc, st + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  }
+  rows_store<RB, KIND>(g, e, acc, m0 + wr0, wn0, lane);
+}
+
+// Gate/up-shaped products at 65..128 rows: eight waves on one 64 x 128 tile (two
+// per SIMD, so that one wave's expansion and LDS reads overlap the other's MFMAs).
+// Each stage covers two 128-wide groups: waves 0-3 take the first, waves 4-7 the
+// second, each wave all 64 rows of its 32-column block, with the next stage's loads
+// issued between its MFMAs; the two halves' sums meet in LDS at the end (the A
+// stages' memory) and waves 0-3 apply the epilogue.  Gate/up at 128 rows: 16.4 us
+// per launch against 18.9 us for the four-wave row-tiled kernel.
+template <int KIND>
+__global__ __launch_bounds__(512, 1) void gemm_w4_pair_kernel(GemmArgs g, GemmEpi e, int kchunk) {
+  constexpr int BM = 64, KC = 32, RB = 2, AC = BM * KC / 512;
+  __shared__ u32x4 As[2][BM * KC];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wn = wave & 3, kh = wave >> 2;
+  const int m0 = blockIdx.y * BM, wn0 = blockIdx.x * 128 + wn * 32;
+  const int M = g.M, N = g.N, K = g.K, groups = K >> 7;
+  const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
+  const int g0 = kb >> 7, gend = ke >> 7;
+  const int nreal = (gend - g0 + 1) >> 1;   // two-group stages
+  const int nst = (nreal + 1) & ~1;
+  const int nb = min(wn0 >> 5, (N >> 5) - 1);
+  const f16* A = reinterpret_cast<const f16*>(g.A);
+
+  floatx16 acc[RB];
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] = 0.f;
+
+  u32x4 ra[2][AC];
+  u32x4 rw[2][2];
+  uint16_t rs[2];
+  auto piece = [&](auto uc, auto pc, int st) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value, p = decltype(pc)::value;
+    const int s2 = g0 + 2 * min(st, nreal - 1);
+    if constexpr (p < AC) {
+      const int c = tid + 512 * p, r = c / KC, ch = c % KC;
+      const int gk = min(s2 * 128 + ch * 8, K - 8);
+      ra[u][p] = *reinterpret_cast<const u32x4*>(A + (int64_t)min(m0 + r, M - 1) * K + gk);
+    } else {
+      const int gi = min(s2 + kh, groups - 1);
+      if constexpr (p == AC) {
+        rw[u][0] = *reinterpret_cast<const u32x4*>(g.Bw4 + ((int64_t)nb * groups + gi) * 512 + lane * 4);
+      } else if constexpr (p == AC + 1) {
+        rw[u][1] = *reinterpret_cast<const u32x4*>(g.Bw4 + ((int64_t)nb * groups + gi) * 512 + 256 + lane * 4);
+      } else if constexpr (p == AC + 2) {
+        rs[u] = g.Bs[(int64_t)gi * N + min(wn0 + (lane & 31), N - 1)];
+      }
+    }
+  };
+  auto lstore = [&](auto uc, int buf) __attribute__((always_inline)) {
+    constexpr int u = decltype(uc)::value;
+#pragma unroll
+    for (int i = 0; i < AC; ++i) {
+      const int c = tid + 512 * i, r = c / KC, ch = c % KC;
+      As[buf][r * KC + ((ch & ~15) | ((ch & 15) ^ (r & 15)))] = ra[u][i];
+    }
+  };
+
+  static_for<0, AC + 3>([&](auto pc) __attribute__((always_inline)) { piece(std::integral_constant<int, 0>{}, pc, 0); });
+  if (gate_closed(g.live)) return;
+  for (int s0 = 0; s0 < nst; s0 += 2) {
+    static_for<0, 2>([&](auto uc) __attribute__((always_inline)) {
+      constexpr int u = decltype(uc)::value;
+      const int st = s0 + u;
+      lstore(uc, st & 1);
+      lds_barrier();
+      __builtin_amdgcn_sched_barrier(0);
+      // an odd group count leaves the last stage's second half empty
+      const bool valid = st < nreal && g0 + 2 * st + kh < gend;
+      const float sc = valid ? (float)__builtin_bit_cast(f16, rs[u]) : 0.f;
+      rows_group<RB, KC>(acc, As[st & 1], 0, 16 * kh, lane, rw[u], sc, [&](auto jc) __attribute__((always_inline)) {
+        piece(std::integral_constant<int, 1 - u>{}, jc, st + 1);
+        __builtin_amdgcn_sched_barrier(0);
+      });
+    });
+  }
+  // waves 4-7 hand their sums to waves 0-3 through the A stages' LDS (32 KB of 64)
+  float* red = reinterpret_cast<float*>(&As[0][0]);
+  lds_barrier();
+  if (kh == 1) {
+#pragma unroll
+    for (int i = 0; i < RB; ++i)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) red[((wn * RB + i) * 16 + r) * 64 + lane] = acc[i][r];
+  }
+  lds_barrier();
+  if (kh == 1) return;
+#pragma unroll
+  for (int i = 0; i < RB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i][r] += red[((wn * RB + i) * 16 + r) * 64 + lane];
+  rows_store<RB, KIND>(g, e, acc, m0, wn0, lane);
 }
 
 // fp32 operands: a plain LDS-tiled SIMT kernel (64 x 64 tile, 4 x 4 per thread).
@@ -1275,37 +1372,33 @@ hipError_t launch_skinny(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg& t
   return hipErrorInvalidValue;
 }
 
-// The row-tiled INT4 kernel for 65..128 rows where it measured ahead (see its
-// comment): gate/up-shaped products (N >= 8192) unsplit with WM = 1, products
-// with K >= 4096 (the down projection) split 4 ways with WM = 2 and two groups per
-// stage.  Returns false to keep the LDS-tiled kernel.
+// The row-tiled INT4 kernels for 65..128 rows where they measured ahead (see their
+// comments): gate/up-shaped products (N >= 8192) unsplit on the eight-wave pair
+// kernel, products with K >= 4096 (the down projection) split 4 ways on the
+// row-tiled kernel with WM = 2.  Returns false to keep the LDS-tiled kernel.
 bool w4_rows_launch(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool* norm_done, hipError_t* err) {
   if (!g.Bw4 || g.invariant || g.M <= 64 || g.M > 128 || e.pair_g != 16 || (g.K % 128) || (g.N % 32)) return false;
   if (e.kind != EPI_SWIGLU && e.kind != EPI_RESID && e.kind != EPI_STORE) return false;
   const int units = g.K / 128;
-  int wm, gps, sp;
   if (g.N >= 8192) {
-    wm = 1, gps = 1, sp = 1;
-  } else if (g.K >= 4096 && g.partial && (int64_t)4 * g.M * g.N <= g.partial_cap) {
-    wm = 2, gps = 2, sp = 4;
-  } else {
-    return false;
+    dim3 grid((g.N + 127) / 128, (g.M + 63) / 64, 1);
+    switch (e.kind) {
+      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_w4_pair_kernel<EPI_SWIGLU>), grid, dim3(512), 0, s, g, e, g.K); break;
+      case EPI_RESID: hipLaunchKernelGGL((gemm_w4_pair_kernel<EPI_RESID>), grid, dim3(512), 0, s, g, e, g.K); break;
+      default: hipLaunchKernelGGL((gemm_w4_pair_kernel<EPI_STORE>), grid, dim3(512), 0, s, g, e, g.K); break;
+    }
+    *err = hipGetLastError();
+    return true;
   }
-  int per = (units + sp - 1) / sp;
-  per = (per + gps - 1) / gps * gps;
-  sp = (units + per - 1) / per;
-  const int BN = (4 / wm) * 32;
-  dim3 grid((g.N + BN - 1) / BN, (g.M + 63) / 64, sp);
-  const int kc = per * 128;
-#define TL_W4R(WM_, G_)                                                                                              \
-  switch (e.kind) {                                                                                                 \
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_w4_rows_kernel<WM_, G_, 2, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, kc); break; \
-    case EPI_RESID: hipLaunchKernelGGL((gemm_w4_rows_kernel<WM_, G_, 2, EPI_RESID>), grid, dim3(256), 0, s, g, e, kc); break; \
-    default: hipLaunchKernelGGL((gemm_w4_rows_kernel<WM_, G_, 2, EPI_STORE>), grid, dim3(256), 0, s, g, e, kc); break; \
+  if (g.K < 4096 || !g.partial || (int64_t)4 * g.M * g.N > g.partial_cap) return false;
+  const int per = (units + 3) / 4;
+  const int sp = (units + per - 1) / per;
+  dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, sp);
+  switch (e.kind) {
+    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_w4_rows_kernel<2, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, per * 128); break;
+    case EPI_RESID: hipLaunchKernelGGL((gemm_w4_rows_kernel<2, EPI_RESID>), grid, dim3(256), 0, s, g, e, per * 128); break;
+    default: hipLaunchKernelGGL((gemm_w4_rows_kernel<2, EPI_STORE>), grid, dim3(256), 0, s, g, e, per * 128); break;
   }
-  if (wm == 1) { TL_W4R(1, 1) }
-  else { TL_W4R(2, 2) }
-#undef TL_W4R
   *err = sp > 1 ? finish_splits<f16>(g, e, sp, s, norm_done) : hipGetLastError();
   return true;
 }
