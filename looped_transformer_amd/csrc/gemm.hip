@@ -107,12 +107,18 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
   uint4 ra_[D][AC * AW], rb_[D][BC];
   uint16_t rs_[D][W4 ? GPS : 1];
   uint32_t okA_[D], okB_[D];
-  auto gload = [&](uint4 (&ra)[AC * AW], uint4 (&rb)[BC], uint16_t (&rs)[W4 ? GPS : 1], uint32_t& okA, uint32_t& okB,
-                   int k0) {
-    okA = 0;
-    okB = 0;
-#pragma unroll
-    for (int i = 0; i < AC; ++i) {
+  // The loads of one stage in pieces: piece p < AC is A chunk p, then the B chunks,
+  // then (INT4) the group scales.  Piece 0 clears the stage's in-tile masks.
+  constexpr int NPIECE = AC + BC + (W4 ? 1 : 0);
+  auto gpiece = [&](auto pc, uint4 (&ra)[AC * AW], uint4 (&rb)[BC], uint16_t (&rs)[W4 ? GPS : 1], uint32_t& okA,
+                    uint32_t& okB, int k0) __attribute__((always_inline)) {
+    constexpr int p = decltype(pc)::value;
+    if constexpr (p == 0) {
+      okA = 0;
+      okB = 0;
+    }
+    if constexpr (p < AC) {
+      constexpr int i = p;
       const int c = tid + 256 * i, r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
       const int gr = m0 + r, gk = k0 + kc;
       if constexpr (!W4) okA |= (gr < M && gk < ke) ? (1u << i) : 0u;   // (INT4: scale 0 instead)
@@ -120,20 +126,27 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       const XT* src = A + (int64_t)grc * K + gkc;
 #pragma unroll
       for (int w = 0; w < AW; ++w) ra[i * AW + w] = *reinterpret_cast<const uint4*>(src + w * (16 / sizeof(XT)));
-    }
-    if constexpr (W4) {
-      // chunk c: group go of the stage, 32-row block of the tile, half hb of the
-      // 2 KB fragment block, lane (row mod 32, k half h): 64 consecutive chunks are
-      // one contiguous 1 KB half (four words: k steps 4 hb .. 4 hb + 3)
-#pragma unroll
-      for (int i = 0; i < BC; ++i) {
+    } else if constexpr (p < AC + BC) {
+      constexpr int i = p - AC;
+      if constexpr (W4) {
+        // chunk c: group go of the stage, 32-row block of the tile, half hb of the
+        // 2 KB fragment block, lane (row mod 32, k half h): 64 consecutive chunks are
+        // one contiguous 1 KB half (four words: k steps 4 hb .. 4 hb + 3)
         const int c = min(tid + 256 * i, BCH - 1);
         const int go = c / (BN * 4), rem = c % (BN * 4);
         const int row = (rem >> 7) * 32 + (rem & 31), hb = (rem >> 6) & 1, h = (rem >> 5) & 1;
         const int gn = n0 + row;
         const int gnc = min(gn, N - 1), gic = min((k0 >> 7) + go, groups - 1);
         rb[i] = *reinterpret_cast<const uint4*>(g.Bw4 + w4_word_offset(gnc, gic * 16 + 8 * hb + h, groups));
+      } else {
+        const AT* B = reinterpret_cast<const AT*>(g.B);
+        const int c = min(tid + 256 * i, BCH - 1), r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
+        const int gn = n0 + r, gk = k0 + kc;
+        okB |= (tid + 256 * i < BCH && gn < N && gk < ke) ? (1u << i) : 0u;
+        const int gnc = min(gn, N - 1), gkc = min(gk, K - 8);
+        rb[i] = *reinterpret_cast<const uint4*>(B + (int64_t)gnc * K + gkc);
       }
+    } else if constexpr (W4 && p == AC + BC) {
 #pragma unroll
       for (int go = 0; go < GPS; ++go) {
         const int gn = n0 + (tid < BN ? tid : 0);
@@ -142,17 +155,11 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
         rs[go] = g.Bs[(int64_t)gic * N + gnc];
         okB |= ok ? (1u << (16 + go)) : 0u;
       }
-    } else {
-      const AT* B = reinterpret_cast<const AT*>(g.B);
-#pragma unroll
-      for (int i = 0; i < BC; ++i) {
-        const int c = min(tid + 256 * i, BCH - 1), r = c / (BK / 8), kc = (c % (BK / 8)) * 8;
-        const int gn = n0 + r, gk = k0 + kc;
-        okB |= (tid + 256 * i < BCH && gn < N && gk < ke) ? (1u << i) : 0u;
-        const int gnc = min(gn, N - 1), gkc = min(gk, K - 8);
-        rb[i] = *reinterpret_cast<const uint4*>(B + (int64_t)gnc * K + gkc);
-      }
     }
+  };
+  auto gload = [&](uint4 (&ra)[AC * AW], uint4 (&rb)[BC], uint16_t (&rs)[W4 ? GPS : 1], uint32_t& okA, uint32_t& okB,
+                   int k0) __attribute__((always_inline)) {
+    static_for<0, NPIECE>([&](auto pc) __attribute__((always_inline)) { gpiece(pc, ra, rb, rs, okA, okB, k0); });
   };
   auto lstore = [&](const uint4 (&ra)[AC * AW], const uint4 (&rb)[BC], const uint16_t (&rs)[W4 ? GPS : 1],
                     uint32_t okA, uint32_t okB) {
@@ -226,9 +233,13 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
     }
   };
 
-  auto compute = [&]() {
-#pragma unroll
-    for (int kk = 0; kk < BK; kk += 32) {
+  // One stage's MFMAs; after k step ks the callback may issue a share of the next
+  // stage's load pieces, so that they leave between the MFMAs (issued together ahead
+  // of them, the wave's in-order issue holds its MFMAs until the memory pipeline has
+  // taken every load).
+  auto compute = [&](auto&& issue) __attribute__((always_inline)) {
+    static_for<0, BK / 32>([&](auto kc) __attribute__((always_inline)) {
+      constexpr int kk = decltype(kc)::value * 32;
       frag a[TM], b[TN], a2[SPLIT ? TM : 1];
       const int lrow = lane & 15, lk = kk + 8 * (lane >> 4);
 #pragma unroll
@@ -264,7 +275,8 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
           }
         }
       }
-    }
+      issue(kc);
+    });
   };
 
   // Stage count padded to a multiple of D so that the loop body is straight-line
@@ -347,8 +359,23 @@ __global__ __launch_bounds__(256, 2) void gemm_mfma_kernel(GemmArgs g, GemmEpi e
       constexpr int nx = (u + D - 1) % D;
       lstore(ra_[u], rb_[u], rs_[u], okA_[u], okB_[u]);
       lds_barrier();
-      gload(ra_[nx], rb_[nx], rs_[nx], okA_[nx], okB_[nx], kb + (s0 + u + D - 1) * BK);
-      compute();
+      const int k0n = kb + (s0 + u + D - 1) * BK;
+      if constexpr (BM >= 128) {
+        // large tiles: the next stage's loads between this stage's MFMAs (FP16-body
+        // forward of 32 x 128 tokens at L = 8: 5.61 -> 5.47 ms); the 32- and 64-row
+        // tiles measured no better or slightly worse this way
+        compute([&](auto kc) __attribute__((always_inline)) {
+          constexpr int KS = BK / 32, PPS = (NPIECE + KS - 1) / KS, ks = decltype(kc)::value;
+          static_for<ks * PPS, (ks + 1) * PPS < NPIECE ? (ks + 1) * PPS : NPIECE>(
+              [&](auto pc) __attribute__((always_inline)) {
+                gpiece(pc, ra_[nx], rb_[nx], rs_[nx], okA_[nx], okB_[nx], k0n);
+              });
+          __builtin_amdgcn_sched_barrier(0);
+        });
+      } else {
+        gload(ra_[nx], rb_[nx], rs_[nx], okA_[nx], okB_[nx], k0n);
+        compute([](auto) {});
+      }
       lds_barrier();
     });
   }
@@ -1059,6 +1086,12 @@ __global__ __launch_bounds__(256) void gemm_f32_kernel(GemmArgs g, GemmEpi e) {
   }
 }
 
+// Split-K reductions with a run-time split count request the partials of
+// kSplitBatch splits at a time (indices clamped, the extra ones not added), so that
+// their loads overlap instead of following one another; the sum is still taken in
+// split order.
+constexpr int kSplitBatch = 4;
+
 // Sum of the split-K partials in split order, then the epilogue.  Paired
 // epilogues get one thread per (row, pair): columns c and c + G with c in an even
 // G-chunk; the others one thread per (row, column).
@@ -1076,10 +1109,20 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
     QkvRow qr{};
     if constexpr (KIND == EPI_QKV) qr = qkv_row(e, row);   // read with the partials
     float v0 = 0.f, v1 = 0.f;
-    for (int z = 0; z < S; ++z) {
-      const float* pr = g.partial + ((int64_t)z * M + row) * N;
-      v0 += pr[c];
-      v1 += pr[c + G];
+    for (int z0 = 0; z0 < S; z0 += kSplitBatch) {
+      float a0[kSplitBatch], a1[kSplitBatch];
+#pragma unroll
+      for (int q = 0; q < kSplitBatch; ++q) {
+        const float* pr = g.partial + ((int64_t)min(z0 + q, S - 1) * M + row) * N;
+        a0[q] = pr[c];
+        a1[q] = pr[c + G];
+      }
+#pragma unroll
+      for (int q = 0; q < kSplitBatch; ++q)
+        if (z0 + q < S) {
+          v0 += a0[q];
+          v1 += a1[q];
+        }
     }
     if (gate_closed(g.live)) return;
     if constexpr (KIND == EPI_QKV) qkv_put<AT>(e, qkv_prep(e, qr, row, c), v0, v1);
@@ -1089,7 +1132,14 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
     const int row = (int)(idx / N);
     const int c = (int)(idx - (int64_t)row * N);
     float v = 0.f;
-    for (int z = 0; z < S; ++z) v += g.partial[((int64_t)z * M + row) * N + c];
+    for (int z0 = 0; z0 < S; z0 += kSplitBatch) {
+      float a[kSplitBatch];
+#pragma unroll
+      for (int q = 0; q < kSplitBatch; ++q) a[q] = g.partial[((int64_t)min(z0 + q, S - 1) * M + row) * N + c];
+#pragma unroll
+      for (int q = 0; q < kSplitBatch; ++q)
+        if (z0 + q < S) v += a[q];
+    }
     if (gate_closed(g.live)) return;
     epi_one<KIND>(e, row, c, v);
   }
@@ -1099,7 +1149,8 @@ __global__ __launch_bounds__(256) void splitk_epilogue_kernel(GemmArgs g, GemmEp
 // adds the splits in order onto the fp32 residual, then normalises the new row
 // (fp32 statistics) into the next GEMM's operand type.  Each thread owns VPT
 // groups of 4 consecutive columns (16-byte loads); with SN > 0 the SN splits are
-// all requested before any is used, with SN == 0 a loop adds any number.
+// all requested before any is used, with SN == 0 a loop adds any number,
+// kSplitBatch at a time.
 template <class AT, int VPT, int SN>
 __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, GemmEpi e, int S) {
   const int row = blockIdx.x, N = g.N, M = g.M;
@@ -1132,11 +1183,19 @@ __global__ __launch_bounds__(256) void splitk_resid_norm_kernel(GemmArgs g, Gemm
       }
   } else {
     if (gate_closed(g.live)) return;
-    for (int z = 0; z < S; ++z)
+    for (int z0 = 0; z0 < S; z0 += kSplitBatch) {
+      floatx4 p[kSplitBatch][VPT];
 #pragma unroll
-      for (int u = 0; u < VPT; ++u) {
-        acc[u] += P[z * zs + rs + min((int)threadIdx.x + 256 * u, N / 4 - 1)];
-      }
+      for (int q = 0; q < kSplitBatch; ++q)
+#pragma unroll
+        for (int u = 0; u < VPT; ++u) p[q][u] = P[min(z0 + q, S - 1) * zs + rs + min((int)threadIdx.x + 256 * u, N / 4 - 1)];
+#pragma unroll
+      for (int q = 0; q < kSplitBatch; ++q)
+        if (z0 + q < S) {
+#pragma unroll
+          for (int u = 0; u < VPT; ++u) acc[u] += p[q][u];
+        }
+    }
   }
   float ss = 0.f;
 #pragma unroll
