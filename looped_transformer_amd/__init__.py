@@ -15,7 +15,9 @@ import re
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libtl.so")
+# TL_LIBRARY names another build of the same library (the host-sanitizer build
+# libtl_asan.so); by default the in-tree libtl.so
+LIB_PATH = os.environ.get("TL_LIBRARY") or os.path.join(_HERE, "libtl.so")
 HEADER = os.path.join(os.path.dirname(_HERE), "include", "tl.h")
 
 TL_OK, TL_E_ARG, TL_E_OOM, TL_E_HIP, TL_E_STATE, TL_E_UNSUPPORTED = 0, -1, -2, -3, -4, -5
@@ -69,7 +71,7 @@ def lib():
     if _lib is not None:
         return _lib
     if not os.path.exists(LIB_PATH):
-        raise RuntimeError("libtl.so is not built (run __graft_entry__.build()); there is no fallback path")
+        raise RuntimeError("%s is not built (run __graft_entry__.build()); there is no fallback path" % LIB_PATH)
     L = ctypes.CDLL(LIB_PATH)
     sig = {
         "tl_load_weights": [ctypes.POINTER(tl_config), ctypes.POINTER(tl_weights), ALLOC_FN, DEALLOC_FN, _P, _P,
