@@ -23,6 +23,11 @@
  *     TL_E_HIP, which reports a failed HIP call; tl_last_error() gives the reason.
  *   - A model is used by one host thread at a time.
  *   - There are no silent fallbacks: an unsupported shape or dtype is an error.
+ *   - Environment variable TL_LOG_LEVEL (read once; stderr only; the pages' CLI
+ *     has a log-level variable of the same range, "CLI Reference" page,
+ *     Environment Variables): 0 or unset silent, 1 prints the reason of every
+ *     failing call, 2 also one line per load and per forward or decode call;
+ *     any other value counts as 1.  It never changes what a call computes.
  */
 #ifndef TL_H
 #define TL_H

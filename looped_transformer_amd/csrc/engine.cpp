@@ -6,6 +6,7 @@
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <numeric>
 
@@ -17,6 +18,30 @@ namespace {
 
 thread_local std::string g_err;
 
+// TL_LOG_LEVEL (read once, stderr only): 0 or unset silent, 1 every failing call's
+// reason, 2 also one line per load and per call; any other value counts as 1.
+// Logging never changes what a call computes.
+int log_level() {
+  static const int level = [] {
+    const char* s = std::getenv("TL_LOG_LEVEL");
+    if (!s || !*s) return 0;
+    char* end = nullptr;
+    const long v = std::strtol(s, &end, 10);
+    return (*end || v < 0 || v > 2) ? 1 : (int)v;
+  }();
+  return level;
+}
+
+void tl_log(int level, const char* fmt, ...) {
+  if (log_level() < level) return;
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  std::fprintf(stderr, "[tl] %s\n", buf);
+}
+
 tl_status fail(tl_status st, const char* fmt, ...) {
   char buf[512];
   va_list ap;
@@ -24,6 +49,7 @@ tl_status fail(tl_status st, const char* fmt, ...) {
   vsnprintf(buf, sizeof buf, fmt, ap);
   va_end(ap);
   g_err = buf;
+  if (log_level() >= 1) std::fprintf(stderr, "[tl] error %d: %s\n", (int)st, buf);
   return st;
 }
 
@@ -1039,6 +1065,11 @@ tl_status tl_load_weights(const tl_config* cfg, const tl_weights* w, tl_alloc_fn
   LHIP(noalloc_scratch_init(dev));
   LHIP(hipStreamSynchronize(s));
   *out = m;
+  tl_log(2, "loaded: d_model %d, %d heads x %d, ffn %d, vocab %d, blocks %d pre + %d loop + %d post, act %d, "
+            "loop weights %d, kv mode %d, device %d, weights %.1f MB, kv arena %.1f MB",
+         m->cfg.d_model, m->cfg.n_heads, m->cfg.head_dim, m->cfg.ffn, m->cfg.vocab, m->cfg.n_pre, m->cfg.n_loop,
+         m->cfg.n_post, m->cfg.act_dtype, m->cfg.loop_dtype, m->cfg.kv_mode, m->device, m->weight_bytes / 1e6,
+         m->kv_bytes / 1e6);
   return TL_OK;
 #undef LTRY
 #undef LHIP
@@ -1102,6 +1133,8 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   if (!m || !cu || !tokens) return fail(TL_E_ARG, "NULL argument");
   const tl_config& c = m->cfg;
   if (n_seqs < 1) return fail(TL_E_ARG, "n_seqs must be >= 1");
+  tl_log(2, "tl_forward: %d sequences, L %d%s, %s", n_seqs, L, seq_L ? " (per sequence)" : "",
+         lanes ? "into lanes" : "scoring");
   if (cu[0] != 0) return fail(TL_E_ARG, "cu_seqlens[0] must be 0");
   std::vector<int> Ls(n_seqs);
   for (int i = 0; i < n_seqs; ++i) {
@@ -1702,6 +1735,7 @@ tl_status tl_decode_step(tl_model* m, int32_t n, const int32_t* lanes, const int
   g_err.clear();
   if (!m || !lanes || !req_L || !out_tokens) return fail(TL_E_ARG, "NULL argument");
   if (n < 1) return fail(TL_E_ARG, "n_lanes must be >= 1");
+  tl_log(2, "tl_decode_step: %d lanes", n);
   std::vector<int> eff;
   TRY(decode_check(m, n, lanes, req_L, in_tokens, eff));
   hipStream_t s = static_cast<hipStream_t>(stream);
@@ -1984,6 +2018,7 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
   if (!m || !lanes || !L_req || !out_tokens) return fail(TL_E_ARG, "NULL argument");
   const tl_config& c = m->cfg;
   if (n < 1 || n_steps < 1) return fail(TL_E_ARG, "n_lanes and n_steps must be >= 1");
+  tl_log(2, "tl_decode_run: %d lanes x %d steps, boundary queue %d", n, n_steps, boundary_min);
   if (m->kv_mode != TL_KV_KV) return fail(TL_E_UNSUPPORTED, "continuous depth decoding needs kv_mode TL_KV_KV");
   std::vector<char> seen(c.max_lanes, 0);
   for (int i = 0; i < n; ++i) {

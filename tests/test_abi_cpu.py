@@ -81,3 +81,29 @@ def test_w4_constraints(L):
     cfg = make_config(synth.SPECS[5])
     cfg.loop_fp16_body = 1                    # body cache only for INT4 loops
     assert _load(L, cfg, w) == tl.TL_E_ARG
+
+
+_LOG_PROBE = """
+import looped_transformer_amd as tl
+L = tl.lib()
+assert L.tl_forward(None, 1, None, None, 1, None, None, 0, None, None, None, None, None) == tl.TL_E_ARG
+"""
+
+
+@pytest.mark.parametrize("level,printed", [(None, False), ("0", False), ("1", True), ("2", True), ("7", True),
+                                           ("x", True)])
+def test_log_level(L, level, printed):
+    """TL_LOG_LEVEL: errors reach stderr from level 1 (out-of-range values count as 1),
+    nothing is printed when unset or 0."""
+    import os
+    import subprocess
+    import sys
+    env = dict(os.environ)
+    env.pop("TL_LOG_LEVEL", None)
+    if level is not None:
+        env["TL_LOG_LEVEL"] = level
+    root = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+    r = subprocess.run([sys.executable, "-c", _LOG_PROBE], cwd=root, env=env, capture_output=True, text=True,
+                       timeout=120)
+    assert r.returncode == 0, r.stderr
+    assert ("[tl] error -1: NULL argument" in r.stderr) == printed, r.stderr
