@@ -782,7 +782,9 @@ __device__ __forceinline__ void rows_store(const GemmArgs& g, const GemmEpi& e, 
 // step from the LDS stage (16-byte chunks XOR-swizzled by row within the group's 16),
 // the wave's 32-column INT4 fragments (two 16-byte words per lane, in MFMA order)
 // expanded in registers, 32x32x16 MFMAs into a fresh group sum that is scaled by the
-// column's fp32 group scale and added.  After k step j the callback issues piece j of
+// column's fp32 group scale and added.  The next k step's fragments are read and
+// expanded before this step's MFMAs, so the MFMAs do not wait on their own LDS
+// reads (gate/up at 128 rows: 20.4 -> 20.0 us per launch in the forward).  After k step j the callback issues piece j of
 // the next stage's loads, so that they leave one at a time between the MFMAs: issued
 // together ahead of the MFMAs, the wave's in-order issue held its MFMAs until the
 // memory pipeline had taken every load (gate/up at 128 rows: 18.9 -> 17.9 us per
@@ -791,15 +793,14 @@ template <int RB, int KC, class Issue>
 __device__ __forceinline__ void rows_group(floatx16 (&acc)[RB], const u32x4* As, int r0, int ch0, int lane,
                                            const u32x4 (&w)[2], float sc, Issue&& issue) {
   floatx16 tmp[RB];
-  static_for<0, 8>([&](auto jc) __attribute__((always_inline)) {
-    constexpr int j = decltype(jc)::value;
-    half8 a[RB];
+  auto rd = [&](int j, half8 (&a)[RB]) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       const int r = r0 + 32 * i + (lane & 31), ch = ch0 + 2 * j + (lane >> 5);
       a[i] = __builtin_bit_cast(half8, As[r * KC + ((ch & ~15) | ((ch & 15) ^ (r & 15)))]);
     }
-    half8 b;
+  };
+  auto ex = [&](int j, half8& b) __attribute__((always_inline)) {
     half2v t[4];
     w4_pairs(w[j >> 2][j & 3], t);
 #pragma unroll
@@ -807,15 +808,25 @@ __device__ __forceinline__ void rows_group(floatx16 (&acc)[RB], const u32x4* As,
       b[2 * p] = t[p][0];
       b[2 * p + 1] = t[p][1];
     }
+  };
+  half8 a[2][RB], b[2];
+  rd(0, a[0]);
+  ex(0, b[0]);
+  static_for<0, 8>([&](auto jc) __attribute__((always_inline)) {
+    constexpr int j = decltype(jc)::value, c = j & 1;
+    if constexpr (j < 7) {
+      rd(j + 1, a[1 - c]);
+      ex(j + 1, b[1 - c]);
+    }
 #pragma unroll
     for (int i = 0; i < RB; ++i) {
       if constexpr (j == 0) {
         floatx16 zero;
 #pragma unroll
         for (int r = 0; r < 16; ++r) zero[r] = 0.f;
-        tmp[i] = mfma32(a[i], b, zero);
+        tmp[i] = mfma32(a[c][i], b[c], zero);
       } else {
-        tmp[i] = mfma32(a[i], b, tmp[i]);
+        tmp[i] = mfma32(a[c][i], b[c], tmp[i]);
       }
     }
     issue(jc);
