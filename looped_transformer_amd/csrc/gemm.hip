@@ -1384,21 +1384,24 @@ struct SkinnyCfg {
 };
 
 // Tile and split choice for the small-M INT4 kernel, fitted to a sweep of the
-// 2048-wide model's shapes at 32 and 64 rows on MI355X: two 32-column blocks per
-// wave when one-block tiles would number 32..63 (else one), K split so that
-// about 192 workgroups run, a third ring stage for K >= 4096.  For 33..64 rows
-// and N >= 8192 the LDS-tiled kernel measured faster and is kept.
+// 2048-wide model's decode shapes at 13..64 rows on MI355X (per-launch event
+// timing, the split reduction and the norm included): 32-row tiles at every row
+// count (64-row tiles re-read less of A but ran 0.5-4.5 us slower per product),
+// two 32-column blocks per wave when one-block tiles would number 32..63 (else
+// one), K split so that about 192 workgroups run but at most 8 ways (the down
+// projection at 11 splits with a third ring stage: 13.5-17.7 us; at 8 splits and
+// two stages: 11.4-13.3 us).  Gate/up at 33..64 rows: 12.7-13.3 us unsplit here
+// against 15.0-15.3 us on the LDS-tiled kernel.
 SkinnyCfg pick_skinny(const GemmArgs& g, int kind) {
   SkinnyCfg t{0, 1, 1, 0, 2};
   if (!g.Bw4 || g.invariant || g.M > 64 || kind == EPI_HEAD || (g.K % 128) != 0 || (g.N % 32) != 0) return t;
-  if (g.M > 32 && g.N >= 8192) return t;
-  const int bm = g.M <= 32 ? 32 : 64;
+  const int bm = 32;
   const int units = g.K / 128;
   const int64_t rows = (g.M + bm - 1) / bm;
   const int64_t tiles1 = (int64_t)((g.N + 127) / 128) * rows;
   const int wnb = (tiles1 >= 32 && tiles1 < 64) ? 2 : 1;
   const int64_t tiles = (int64_t)((g.N + 128 * wnb - 1) / (128 * wnb)) * rows;
-  int sp = (int)std::min<int64_t>(16, std::max<int64_t>(1, (192 + tiles / 2) / tiles));
+  int sp = (int)std::min<int64_t>(8, std::max<int64_t>(1, (192 + tiles / 2) / tiles));
   sp = std::min(sp, units);
   int per = (units + sp - 1) / sp;
   sp = (units + per - 1) / per;
@@ -1410,7 +1413,7 @@ SkinnyCfg pick_skinny(const GemmArgs& g, int kind) {
   t.wnb = wnb;
   t.splits = sp;
   t.kchunk = per * 128;
-  t.depth = g.K >= 4096 ? 3 : 2;
+  t.depth = 2;
   return t;
 }
 
@@ -1432,13 +1435,11 @@ hipError_t launch_skinny_t(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg&
 template <int D>
 hipError_t launch_skinny_d(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg& t, hipStream_t s, bool* norm_done) {
   if (t.bm == 32) return t.wnb == 1 ? launch_skinny_t<32, 1, D>(g, e, t, s, norm_done) : launch_skinny_t<32, 2, D>(g, e, t, s, norm_done);
-  if (t.bm == 64) return t.wnb == 1 ? launch_skinny_t<64, 1, D>(g, e, t, s, norm_done) : launch_skinny_t<64, 2, D>(g, e, t, s, norm_done);
   return hipErrorInvalidValue;
 }
 
 hipError_t launch_skinny(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg& t, hipStream_t s, bool* norm_done) {
   if (t.depth == 2) return launch_skinny_d<2>(g, e, t, s, norm_done);
-  if (t.depth == 3) return launch_skinny_d<3>(g, e, t, s, norm_done);
   return hipErrorInvalidValue;
 }
 
