@@ -13,6 +13,7 @@
 // data exchange until the final merge.  Online softmax in fp32.  The tiled kernel
 // below serves prefill runs of consecutive rows.
 #include "device_common.h"
+#include "epilogue.h"
 
 namespace {
 
@@ -26,10 +27,16 @@ template <> struct Row16<float> { typedef floatx4 type; };
 // per block of P = (64 / LPK) * U positions.  UD = 4 (2) cuts blocks to a quarter
 // (half), for contexts one (two) full blocks would hold: all four waves then take
 // part.
+//
+// With qp.part set the workgroup first finishes its row's q, k and v from the QKV
+// product's split-K partials (QkvParts): the arithmetic of the split-K QKV epilogue
+// (sums in split order, the same rotation and roundings), k and v stored into the
+// cache at the row's position, q kept in LDS; one kernel fewer per block on a
+// decode pass.
 template <class T, int LPK, int UD>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, const RowInfo* __restrict__ rows,
                                                        KVParams kv, T* __restrict__ out, int d, float scale,
-                                                       const int32_t* live) {
+                                                       const int32_t* live, QkvParts qp) {
   typedef typename Row16<T>::type R16;
   constexpr int EPL = 16 / (int)sizeof(T);   // elements per lane of a key row
   constexpr int KPI = 64 / LPK;              // keys per load instruction
@@ -56,7 +63,56 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   const T* Kp = kv_ptr<T>(kv, ri, 0, h, 0);
   const T* Vp = kv_ptr<T>(kv, ri, 1, h, 0);
   float qv[EPL];
-  {
+  if (qp.part) {
+    // thread t < 3 dh/2: section t / (dh/2) (q, k, v), pair p of the head: kernel
+    // columns cd = (p / G) 2G + p mod G and cd + G; after the rotation the pair's
+    // values go to p and p + dh/2 (q, k), V keeps kernel order
+    __shared__ float qs[128];
+    const int half = dh >> 1, G = qp.G;
+    if (tid < 3 * half) {
+      const int sec = tid / half, p = tid - sec * half;
+      const int cd = (p / G) * 2 * G + p % G;
+      const int64_t c = (int64_t)sec * d + h * dh + cd;
+      float v0 = 0.f, v1 = 0.f;
+      for (int z0 = 0; z0 < qp.S; z0 += 4) {
+        float a0[4], a1[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float* pr = qp.part + ((int64_t)min(z0 + u, qp.S - 1) * qp.M + r) * qp.N + c;
+          a0[u] = pr[0];
+          a1[u] = pr[G];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+          if (z0 + u < qp.S) {
+            v0 += a0[u];
+            v1 += a1[u];
+          }
+      }
+      if (sec == 2) {
+        T* vp = kv_ptr<T>(kv, ri, 1, h, ri.pos);
+        vp[cd] = from_f32<T>(v0);
+        vp[cd + G] = from_f32<T>(v1);
+      } else {
+        const float cs = qp.rope_cos[(int64_t)ri.pos * half + p];
+        const float sn = qp.rope_sin[(int64_t)ri.pos * half + p];
+        const T x1 = from_f32<T>(rot_x1(v0, v1, cs, sn));
+        const T x2 = from_f32<T>(rot_x2(v0, v1, cs, sn));
+        if (sec == 0) {
+          qs[p] = (float)x1;
+          qs[p + half] = (float)x2;
+        } else {
+          T* kp = kv_ptr<T>(kv, ri, 0, h, ri.pos);
+          kp[p] = x1;
+          kp[p + half] = x2;
+        }
+      }
+    }
+    // this position's K/V stored (workgroup-visible) and q in LDS
+    __syncthreads();
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] = kin ? qs[k * EPL + e] * scale : 0.f;
+  } else {
     R16 x{};
     if (kin) x = *reinterpret_cast<const R16*>(q + (int64_t)r * d + h * dh + k * EPL);
 #pragma unroll
@@ -633,41 +689,50 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
 
 template <class T, int LPK>
 void attn_rows_launch(const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out, const int32_t* live,
-                      int max_ctx, hipStream_t s) {
+                      int max_ctx, hipStream_t s, const QkvParts& qp) {
   const int d = kv.H * kv.dh;
   const float scale = 1.0f / sqrtf((float)kv.dh);
   constexpr int P = (64 / LPK) * (LPK < 16 ? LPK : 16);   // positions of a full block
   if (max_ctx > 0 && max_ctx <= P)
     hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 4>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
-                       d, scale, live);
+                       d, scale, live, qp);
   else if (max_ctx > 0 && max_ctx <= 2 * P)
     hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 2>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
-                       d, scale, live);
+                       d, scale, live, qp);
   else
     hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 1>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
-                       d, scale, live);
+                       d, scale, live, qp);
 }
 
 template <class T>
 hipError_t attn_rows_dispatch(const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
-                              const int32_t* live, int max_ctx, hipStream_t s) {
+                              const int32_t* live, int max_ctx, hipStream_t s, const QkvParts& qp) {
   const int chunks = kv.dh * (int)sizeof(T) / 16;   // 16-byte chunks of a row (head_dim is checked at load)
-  if (chunks <= 4) attn_rows_launch<T, 4>(q, rows, n, kv, out, live, max_ctx, s);
-  else if (chunks <= 8) attn_rows_launch<T, 8>(q, rows, n, kv, out, live, max_ctx, s);
-  else if (chunks <= 16) attn_rows_launch<T, 16>(q, rows, n, kv, out, live, max_ctx, s);
-  else if (chunks <= 32) attn_rows_launch<T, 32>(q, rows, n, kv, out, live, max_ctx, s);
+  if (chunks <= 4) attn_rows_launch<T, 4>(q, rows, n, kv, out, live, max_ctx, s, qp);
+  else if (chunks <= 8) attn_rows_launch<T, 8>(q, rows, n, kv, out, live, max_ctx, s, qp);
+  else if (chunks <= 16) attn_rows_launch<T, 16>(q, rows, n, kv, out, live, max_ctx, s, qp);
+  else if (chunks <= 32) attn_rows_launch<T, 32>(q, rows, n, kv, out, live, max_ctx, s, qp);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
-                            const int32_t* live, int max_ctx, hipStream_t s) {
+                            const int32_t* live, int max_ctx, hipStream_t s, const QkvParts* qp) {
   if (n <= 0) return hipSuccess;
   if (kv.dh > 128 || (kv.dh * 4) % 16 != 0) return hipErrorInvalidValue;
+  QkvParts p{};
+  if (qp && qp->part) {
+    // the prologue's threads cover 3 dh/2 pairs, pairs stay inside a head, and the
+    // partials hold n rows of the 3 d columns
+    if (3 * (kv.dh / 2) > 256 || qp->G <= 0 || kv.dh % (2 * qp->G) != 0 || qp->S < 1 || qp->M != n ||
+        qp->N != 3 * kv.H * kv.dh || !qp->rope_cos || !qp->rope_sin)
+      return hipErrorInvalidValue;
+    p = *qp;
+  }
   switch (dtype) {
-    case DT_F32: return attn_rows_dispatch<float>(q, rows, n, kv, out, live, max_ctx, s);
-    case DT_F16: return attn_rows_dispatch<f16>(q, rows, n, kv, out, live, max_ctx, s);
-    case DT_BF16: return attn_rows_dispatch<bf16>(q, rows, n, kv, out, live, max_ctx, s);
+    case DT_F32: return attn_rows_dispatch<float>(q, rows, n, kv, out, live, max_ctx, s, p);
+    case DT_F16: return attn_rows_dispatch<f16>(q, rows, n, kv, out, live, max_ctx, s, p);
+    case DT_BF16: return attn_rows_dispatch<bf16>(q, rows, n, kv, out, live, max_ctx, s, p);
     default: return hipErrorInvalidValue;
   }
 }

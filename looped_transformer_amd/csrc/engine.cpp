@@ -308,7 +308,9 @@ tl_status tend(tl_model* m, int cls, hipStream_t s) {
 // With norm_h set (only on the few-row GEMV path, see small_gemv) the product's
 // input is RMSNorm(norm_h) * norm_g, formed inside the GEMV; x_out receives it.
 tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, hipStream_t s,
-               const float* norm_h = nullptr, const float* norm_g = nullptr, void* x_out = nullptr) {
+               const float* norm_h = nullptr, const float* norm_g = nullptr, void* x_out = nullptr,
+               int32_t* defer_split = nullptr) {
+  if (defer_split) *defer_split = 0;
   GemmArgs g{};
   g.A = A;
   g.norm_h = norm_h;
@@ -333,6 +335,7 @@ tl_status gemm(tl_model* m, const void* A, int M, const MatDev& W, GemmEpi& e, h
     return TL_OK;
   }
   if (norm_h) return fail(TL_E_STATE, "normalised input outside the GEMV path");
+  g.defer_split = defer_split;
   HIPCHK(launch_gemm(m->gdt, g, e, s));
   return TL_OK;
 }
@@ -358,9 +361,12 @@ bool small_gemv(const tl_model* m, const tl::BlockDev& B, int n) {
 // this block's normalised input in ws.x16.  next_norm: gain of the norm that
 // follows on the same rows (the next block's first norm), fused into the down
 // projection's residual update when possible (then ws.x16 holds its output).
+// one_row_per_lane: no lane has two rows in the pass (decode steps), so a split QKV
+// product can be finished inside the decode attention (QkvParts).
 tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, const KVParams& kv, hipStream_t s,
                     const AttnTile* tiles = nullptr, int n_tiles = 0, bool x_ready = false,
-                    const float* next_norm = nullptr, int hgroup = -1, bool* x_next = nullptr) {
+                    const float* next_norm = nullptr, int hgroup = -1, bool* x_next = nullptr,
+                    bool one_row_per_lane = false) {
   if (x_next) *x_next = false;
   if (n <= 0) return TL_OK;
   const tl_config& c = m->cfg;
@@ -387,8 +393,13 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   const tl::HPass* hpass = (m->hpass && hgroup >= 0) ? m->hpass : nullptr;
   const KVParams& akv = hpass ? hpass->skv : kv;
   e.kv = akv;
+  // a decode pass's split QKV product is finished by the attention
+  int32_t qkv_splits = 0;
+  int32_t* defer = (one_row_per_lane && !tiles && !hpass) ? &qkv_splits : nullptr;
   if (norm_in_qkv) TIMED(tb + 0, TRY(gemm(m, nullptr, n, B.qkv, e, s, h, B.norm1, w.x16)));
-  else TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s)));
+  else TIMED(tb + 0, TRY(gemm(m, w.x16, n, B.qkv, e, s, nullptr, nullptr, nullptr, defer)));
+  QkvParts qp{};
+  if (qkv_splits > 0) qp = QkvParts{m->ws.splitk, qkv_splits, n, B.qkv.N, m->G, m->rope_cos, m->rope_sin};
   if (hpass) {
     HCacheParams hp = hpass->hp;
     hp.slot = kv.s0;
@@ -404,7 +415,7 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   }
   if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, akv, w.o16, s)));
   else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, akv, w.o16, m->gate_live,
-                                                     m->invariant ? 0 : m->ctx_hint, s)));
+                                                     m->invariant ? 0 : m->ctx_hint, s, &qp)));
   GemmEpi r{};
   r.kind = EPI_RESID;
   r.h = h;
@@ -442,6 +453,8 @@ struct Pass {
   const tl_early_exit* ee = nullptr;
   // host copy of rows0 (store-h modes plan the K/V rebuild from it)
   const std::vector<RowInfo>* rows_host = nullptr;
+  // decode steps: every lane has one row
+  bool one_row_per_lane = false;
 };
 
 // Store-h rebuild plan of a pass: every lane's positions 0 .. (last position in
@@ -577,7 +590,8 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   for (int b = 0; b < c.n_pre; ++b) {
     kv.s0 = p.scoring ? 0 : b;
     const float* nn = b + 1 < c.n_pre ? m->blocks[b + 1].norm1 : (Lmax > 0 ? loop_first() : nullptr);
-    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn, hmode ? 0 : -1, &x_ready));
+    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn, hmode ? 0 : -1, &x_ready,
+                  p.one_row_per_lane));
   }
   float* h = w.hA;
   float* hn = w.hB;
@@ -612,7 +626,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
       // probe normalises into its own buffer, rows it finishes are only carried)
       const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1 : (leaving ? nullptr : loop_first());
       TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
-                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1, &x_ready));
+                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1, &x_ready, p.one_row_per_lane));
     }
     if (probe) {
       if (by_margin) {
@@ -644,7 +658,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     kv.s0 = p.scoring ? 0 : c.n_pre + b;
     const float* nn = b + 1 < c.n_post ? m->blocks[c.n_pre + c.n_loop + b + 1].norm1 : nullptr;
     TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn,
-                  hmode ? 0 : -1, &x_ready));
+                  hmode ? 0 : -1, &x_ready, p.one_row_per_lane));
   }
   return TL_OK;
 }
@@ -1613,6 +1627,7 @@ tl_status tl_speculate(tl_model* m, int32_t n, const int32_t* lanes, int32_t L_d
       p.tokens = toks;
       p.rows0 = staged<RowInfo>(m, o_drows[r]);
       p.rows_host = &drows_host[r];
+      p.one_row_per_lane = true;
       p.n_active = active_counts(dd);
       p.kv = kvp;
       p.final_h = m->ws.hX;
@@ -1717,6 +1732,7 @@ tl_status decode_run_step(tl_model* m, int n, const int32_t* lanes, const std::v
   p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
   p.final_h = out_hidden ? out_hidden : m->ws.hX;
   p.log = out_log;
+  p.one_row_per_lane = true;
   TRY(run_pass(m, p, s));
   TRY(run_head(m, p.final_h, nullptr, n, out_logits, out_tokens, lanes_dev, s));
   for (int i = 0; i < n; ++i) {
@@ -1930,6 +1946,7 @@ tl_status tl_decode_step_ee(tl_model* m, int32_t n, const int32_t* lanes, const 
   p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
   p.final_h = out_hidden ? out_hidden : m->ws.hX;
   p.ee = ee;
+  p.one_row_per_lane = true;
   TRY(run_pass(m, p, s));
   TRY(run_head(m, p.final_h, nullptr, n, out_logits, out_tokens, lanes_dev, s));
   HIPCHK(hipMemcpyAsync(m->ee_eff_host, m->ee_eff, (size_t)n * 4, hipMemcpyDeviceToHost, s));
@@ -2139,7 +2156,8 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
       kv.s1 = 0;
       for (int b = 0; b < c.n_post; ++b) {
         kv.s0 = c.n_pre + b;
-        TRY(run_block(m, c.n_pre + c.n_loop + b, w.hE, xr, tk.n_exit, kv, s));
+        TRY(run_block(m, c.n_pre + c.n_loop + b, w.hE, xr, tk.n_exit, kv, s, nullptr, 0, false, nullptr, -1,
+                      nullptr, true));
       }
       TRY(run_head(m, w.hE, nullptr, tk.n_exit, nullptr, w.tok2, staged<int32_t>(m, tk.o_xlanes), s));
       HIPCHK(launch_scatter_i32(w.tok2, staged<int32_t>(m, tk.o_xout), tk.n_exit, out_tokens, s));
@@ -2154,7 +2172,7 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
       kv.s1 = 0;
       for (int b = 0; b < c.n_pre; ++b) {
         kv.s0 = b;
-        TRY(run_block(m, b, hin, er, tk.n_enter, kv, s));
+        TRY(run_block(m, b, hin, er, tk.n_enter, kv, s, nullptr, 0, false, nullptr, -1, nullptr, true));
       }
       HIPCHK(hipMemcpyAsync(rcur + npool, er, sizeof(RowInfo) * tk.n_enter, hipMemcpyDeviceToDevice, s));
       npool += tk.n_enter;
@@ -2163,7 +2181,7 @@ tl_status tl_decode_run(tl_model* m, int32_t n, const int32_t* lanes, int32_t n_
       for (int l = 0; l < c.n_loop; ++l) {
         kv.s0 = c.n_pre + c.n_post + l - c.n_loop;
         kv.s1 = c.n_loop;
-        TRY(run_block(m, c.n_pre + l, hcur, rcur, npool, kv, s));
+        TRY(run_block(m, c.n_pre + l, hcur, rcur, npool, kv, s, nullptr, 0, false, nullptr, -1, nullptr, true));
       }
       TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rcur, npool, 0, rnxt, w.dest, w.count, nullptr, nullptr, s));
                           HIPCHK(launch_move_rows(hcur, w.dest, rcur, npool, d, hnxt, w.hX, s)));

@@ -1311,6 +1311,10 @@ template <class XT>
 hipError_t finish_splits(const GemmArgs& g, const GemmEpi& e, int splits, hipStream_t s, bool* norm_done) {
   hipError_t err = hipGetLastError();
   if (err != hipSuccess) return err;
+  if (e.kind == EPI_QKV && g.defer_split) {   // the decode attention finishes the partials
+    *g.defer_split = splits;
+    return hipSuccess;
+  }
   const int vpt = (g.N / 4 + 255) / 256;
   if (e.kind == EPI_RESID && e.norm_g && (g.N % 4) == 0 && (e.ldh % 4) == 0 && vpt <= 6) {
 #define TL_RN(VPT_)                                                                                                \
@@ -1517,6 +1521,7 @@ void row_range(int act_dtype, const GemmArgs& g, const GemmEpi& e, int r0, int M
 // With g.invariant a product whose split partials would exceed g.partial_cap runs
 // as several launches over consecutive row ranges (same split, same arithmetic).
 hipError_t launch_gemm(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
+  if (g.defer_split) *g.defer_split = 0;
   if (g.M <= 0 || g.N <= 0) return hipSuccess;
   if (g.invariant && act_dtype != DT_F32) {
     const TileCfg t = pick_tile(act_dtype, g, e.kind);
@@ -1528,6 +1533,7 @@ hipError_t launch_gemm(int act_dtype, const GemmArgs& g, const GemmEpi& e, hipSt
         GemmArgs gc;
         GemmEpi ec;
         row_range(act_dtype, g, e, r0, std::min(rows, g.M - r0), &gc, &ec);
+        gc.defer_split = nullptr;   // each row range's partials reuse the buffer: finished here
         const hipError_t err = launch_gemm(act_dtype, gc, ec, s);
         if (err != hipSuccess) return err;
       }

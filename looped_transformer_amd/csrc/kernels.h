@@ -55,6 +55,10 @@ struct GemmArgs {
   const float* norm_g;
   float norm_eps;
   void* x_out;
+  // host pointer, or NULL: when set, a QKV product that is split over K leaves its
+  // partials in `partial` unfinished and stores the split count here (0 when the
+  // product was finished); the decode attention then finishes them (QkvParts)
+  int32_t* defer_split;
 };
 
 struct GemmEpi {
@@ -101,11 +105,24 @@ hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, 
                         int x_dtype = 0, void* x = nullptr, bool* x_done = nullptr);
 hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const int32_t* gather, int n,
                           int d, float eps, void* out, hipStream_t s);
+// The split-K partials of a pass's QKV product left unfinished (GemmArgs::defer_split),
+// for the decode attention to finish: each (row, head) workgroup sums its q, k and v
+// columns in split order, rotates q and k as the QKV epilogue does, stores k and v
+// into the row's cache slot and keeps q.  Only for passes with one row per lane
+// (another row's workgroup would read this row's K/V while it is written).
+struct QkvParts {
+  const float* part;       // [S][M][N] fp32, kernel column order; NULL: q is finished in q
+  int32_t S, M, N;         // splits, rows of the pass, columns (3 d)
+  int32_t G;               // pair granularity: pair (c, c + G) within each 2G-column chunk
+  const float* rope_cos;   // [max_pos, dh/2]
+  const float* rope_sin;
+};
 // live: as GemmArgs::live (NULL: always run).  Rows marked done get a zero output.
 // max_ctx: an upper bound on pos + 1 over the rows (0: unknown), which picks
-// the block size.
+// the block size.  qp: see QkvParts (NULL or qp->part NULL: q from `q`).
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv,
-                            void* out, const int32_t* live, int max_ctx, hipStream_t s);
+                            void* out, const int32_t* live, int max_ctx, hipStream_t s,
+                            const QkvParts* qp = nullptr);
 // A run of up to attn_tile_rows() consecutive rows of one sequence (positions pos0 .. pos0+nrows-1)
 // that attend to positions 0 .. pos0+nrows-1 of their lane's slot.  cap > 0: the lane's slot-0
 // offset (koff) and capacity are carried here, so the kernel need not read the lane tables;
