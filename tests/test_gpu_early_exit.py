@@ -24,6 +24,9 @@ pytestmark = pytest.mark.gpu
 SPECS = {
     "tiny-w4": synth.ModelSpec("tiny-w4", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "w4g128"),
     "tiny-bf16-stack": synth.ModelSpec("tiny-bf16-stack", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16"),
+    # wide enough (K = 512: four 128-wide groups) that five lanes' QKV products are
+    # split over K and finished inside the decode attention, also on exiting rows
+    "mid-w4": synth.ModelSpec("mid-w4", 256, 512, 8, 64, 1024, 1, 1, 0, "f16", "w4g128"),
 }
 N_LANES, PLEN, STEPS, L0 = 5, 10, 6, 8
 
