@@ -48,6 +48,23 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
   const int g = lane / LPK, k = lane % LPK;   // key in the instruction, 16-byte chunk of the row
   const bool kin = k * EPL < dh;
+  // fused QKV finish: thread t < 3 dh/2 takes section t / (dh/2) (q, k, v) and pair
+  // p of the head, kernel columns cd = (p / G) 2G + p mod G and cd + G; the first
+  // eight splits' partials are requested before the row descriptor arrives
+  const int half = dh >> 1;
+  const bool fz = qp.part != nullptr && tid < 3 * half;
+  const int sec = tid / half, pq = tid - sec * half;
+  const int cd = qp.G > 0 ? (pq / qp.G) * 2 * qp.G + pq % qp.G : 0;
+  const int64_t pc = (int64_t)sec * d + h * dh + cd;
+  float a0[8], a1[8];
+  if (fz) {
+#pragma unroll
+    for (int u = 0; u < 8; ++u) {
+      const float* pr = qp.part + ((int64_t)min(u, qp.S - 1) * qp.M + r) * qp.N + pc;
+      a0[u] = pr[0];
+      a1[u] = pr[qp.G];
+    }
+  }
   const RowInfo ri = rows[r];
   if (gate_closed(live)) return;
   T* op = out + (int64_t)r * d + h * dh;
@@ -64,30 +81,22 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   const T* Vp = kv_ptr<T>(kv, ri, 1, h, 0);
   float qv[EPL];
   if (qp.part) {
-    // thread t < 3 dh/2: section t / (dh/2) (q, k, v), pair p of the head: kernel
-    // columns cd = (p / G) 2G + p mod G and cd + G; after the rotation the pair's
-    // values go to p and p + dh/2 (q, k), V keeps kernel order
+    // after the rotation the pair's values go to p and p + dh/2 (q, k); V keeps
+    // kernel order
     __shared__ float qs[128];
-    const int half = dh >> 1, G = qp.G;
-    if (tid < 3 * half) {
-      const int sec = tid / half, p = tid - sec * half;
-      const int cd = (p / G) * 2 * G + p % G;
-      const int64_t c = (int64_t)sec * d + h * dh + cd;
-      float v0 = 0.f, v1 = 0.f;
-      for (int z0 = 0; z0 < qp.S; z0 += 4) {
-        float a0[4], a1[4];
+    const int G = qp.G, p = pq;
+    if (fz) {
+      float v0 = 0.f, v1 = 0.f;   // split order, as the split-K QKV epilogue adds them
 #pragma unroll
-        for (int u = 0; u < 4; ++u) {
-          const float* pr = qp.part + ((int64_t)min(z0 + u, qp.S - 1) * qp.M + r) * qp.N + c;
-          a0[u] = pr[0];
-          a1[u] = pr[G];
+      for (int u = 0; u < 8; ++u)
+        if (u < qp.S) {
+          v0 += a0[u];
+          v1 += a1[u];
         }
-#pragma unroll
-        for (int u = 0; u < 4; ++u)
-          if (z0 + u < qp.S) {
-            v0 += a0[u];
-            v1 += a1[u];
-          }
+      for (int z = 8; z < qp.S; ++z) {
+        const float* pr = qp.part + ((int64_t)z * qp.M + r) * qp.N + pc;
+        v0 += pr[0];
+        v1 += pr[G];
       }
       if (sec == 2) {
         T* vp = kv_ptr<T>(kv, ri, 1, h, ri.pos);
