@@ -65,6 +65,9 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
       a1[u] = pr[qp.G];
     }
   }
+  // a finished q is likewise requested with the descriptor
+  R16 qx{};
+  if (!qp.part && kin) qx = *reinterpret_cast<const R16*>(q + (int64_t)r * d + h * dh + k * EPL);
   const RowInfo ri = rows[r];
   if (gate_closed(live)) return;
   T* op = out + (int64_t)r * d + h * dh;
@@ -122,10 +125,8 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[e] = kin ? qs[k * EPL + e] * scale : 0.f;
   } else {
-    R16 x{};
-    if (kin) x = *reinterpret_cast<const R16*>(q + (int64_t)r * d + h * dh + k * EPL);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[e] = (float)x[e] * scale;
+    for (int e = 0; e < EPL; ++e) qv[e] = (float)qx[e] * scale;
   }
   const int npos = ri.pos + 1;
   const int nblk = (npos + P - 1) / P;
