@@ -240,10 +240,29 @@ template <> struct QkMfma<bf16> {
 constexpr int kAttnTileRows = 32;
 constexpr int kAttnWaves = kAttnTileRows / 16;
 
+// The tile of this workgroup: from the closed form when the list has one, else
+// loaded from the list.
+__device__ __forceinline__ AttnTile attn_tile(const AttnTile* __restrict__ tiles, const AttnGrid& ug) {
+  if (ug.on) {
+    const int b = blockIdx.x, sq = b / ug.tps, p0 = (b - sq * ug.tps) * kAttnTileRows;
+    AttnTile t;
+    t.row0 = sq * ug.T + p0;
+    t.nrows = min(kAttnTileRows, ug.T - p0);
+    t.pos0 = p0;
+    t.lane = 0;
+    t.iter = ug.iter;
+    t.cap = ug.cap;
+    t.koff = ug.koff0 + (int64_t)sq * ug.kstride;
+    return t;
+  }
+  return tiles[blockIdx.x];
+}
+
 template <class T, int DH>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __restrict__ q,
                                                                      const AttnTile* __restrict__ tiles, KVParams kv,
-                                                                     T* __restrict__ out, int d, float scale) {
+                                                                     T* __restrict__ out, int d, float scale,
+                                                                     AttnGrid ug) {
   constexpr int NW = kAttnWaves, NT = 64 * NW;
   constexpr int KB = 64;
   constexpr int LDK = DH + 8;
@@ -264,7 +283,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_kernel(const T* __
   __shared__ __attribute__((aligned(16))) f16 Vt[DH * LDV];
   __shared__ __attribute__((aligned(16))) f16 Ps[NW][16 * LDV];
 
-  const AttnTile tile = tiles[blockIdx.x];
+  const AttnTile tile = attn_tile(tiles, ug);
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -431,7 +450,7 @@ template <int DH>
 __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_split_kernel(const float* __restrict__ q,
                                                                            const AttnTile* __restrict__ tiles,
                                                                            KVParams kv, float* __restrict__ out, int d,
-                                                                           float scale) {
+                                                                           float scale, AttnGrid ug) {
   constexpr int NW = kAttnWaves, NT = 64 * NW;
   constexpr int KB = 64;
   constexpr int LDK = DH + 8;
@@ -453,7 +472,7 @@ __global__ __launch_bounds__(kAttnWaves * 64) void attn_tiled_split_kernel(const
   __shared__ __attribute__((aligned(16))) f16 Ph[NW][16 * LDV];
   __shared__ __attribute__((aligned(16))) f16 Pl[NW][16 * LDV];
 
-  const AttnTile tile = tiles[blockIdx.x];
+  const AttnTile tile = attn_tile(tiles, ug);
   const int h = blockIdx.y;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int g4 = lane >> 4, l16 = lane & 15;
@@ -662,15 +681,22 @@ bool attn_tiled_supported(int dtype, int head_dim) {
 }
 
 hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tiles, int n_tiles, const KVParams& kv,
-                                  void* out, hipStream_t s) {
+                                  void* out, hipStream_t s, const AttnGrid* grid) {
   if (n_tiles <= 0) return hipSuccess;
+  AttnGrid ug{};
+  if (grid && grid->on) {
+    if (grid->T < 1 || grid->cap < grid->T || grid->tps != (grid->T + kAttnTileRows - 1) / kAttnTileRows ||
+        n_tiles % grid->tps != 0)
+      return hipErrorInvalidValue;
+    ug = *grid;
+  }
   const int d = kv.H * kv.dh;
   const float scale = 1.0f / sqrtf((float)kv.dh);
-  dim3 grid(n_tiles, kv.H);
+  dim3 grd(n_tiles, kv.H);
 #define TL_ATTN_CASE(T, DHV)                                                                                   \
   if (kv.dh == DHV) {                                                                                          \
-    hipLaunchKernelGGL((attn_tiled_kernel<T, DHV>), grid, dim3(kAttnWaves * 64), 0, s, (const T*)q, tiles, kv, (T*)out, d, \
-                       scale);                                                                                 \
+    hipLaunchKernelGGL((attn_tiled_kernel<T, DHV>), grd, dim3(kAttnWaves * 64), 0, s, (const T*)q, tiles, kv, (T*)out, d, \
+                       scale, ug);                                                                             \
     return hipGetLastError();                                                                                  \
   }
   if (dtype == DT_F16) {
@@ -684,8 +710,8 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
   } else if (dtype == DT_F32) {
 #define TL_ATTN_SPLIT(DHV)                                                                                     \
   if (kv.dh == DHV) {                                                                                          \
-    hipLaunchKernelGGL((attn_tiled_split_kernel<DHV>), grid, dim3(kAttnWaves * 64), 0, s, (const float*)q, tiles, kv, \
-                       (float*)out, d, scale);                                                                 \
+    hipLaunchKernelGGL((attn_tiled_split_kernel<DHV>), grd, dim3(kAttnWaves * 64), 0, s, (const float*)q, tiles, kv, \
+                       (float*)out, d, scale, ug);                                                             \
     return hipGetLastError();                                                                                  \
   }
     TL_ATTN_SPLIT(64)

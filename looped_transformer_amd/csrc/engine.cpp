@@ -366,7 +366,7 @@ bool small_gemv(const tl_model* m, const tl::BlockDev& B, int n) {
 tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, const KVParams& kv, hipStream_t s,
                     const AttnTile* tiles = nullptr, int n_tiles = 0, bool x_ready = false,
                     const float* next_norm = nullptr, int hgroup = -1, bool* x_next = nullptr,
-                    bool one_row_per_lane = false) {
+                    bool one_row_per_lane = false, const AttnGrid* grid = nullptr) {
   if (x_next) *x_next = false;
   if (n <= 0) return TL_OK;
   const tl_config& c = m->cfg;
@@ -413,7 +413,7 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
     r2.skip_done = false;
     TIMED(TL_T_HREBUILD, TRY(gemm(m, m->h_x, nrec, B.qkv, r2, s)));
   }
-  if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, akv, w.o16, s)));
+  if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, akv, w.o16, s, grid)));
   else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, akv, w.o16, m->gate_live,
                                                      m->invariant ? 0 : m->ctx_hint, s, &qp)));
   GemmEpi r{};
@@ -449,6 +449,7 @@ struct Pass {
   // iteration 1's list covers every row in caller order (pre and post blocks too)
   std::vector<const AttnTile*> tiles;
   std::vector<int> n_tiles;
+  std::vector<AttnGrid> grids;       // closed form of each list (on = 0: none)
   // early exit (decode steps): rule, or NULL
   const tl_early_exit* ee = nullptr;
   // host copy of rows0 (store-h modes plan the K/V rebuild from it)
@@ -584,6 +585,9 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   kv.s1 = 0;
   const AttnTile* t0 = tiled ? p.tiles[0] : nullptr;
   const int nt0 = tiled ? p.n_tiles[0] : 0;
+  auto grid_of = [&](int k) -> const AttnGrid* {
+    return (tiled && k < (int)p.grids.size()) ? &p.grids[k] : nullptr;
+  };
   const int Lmax = (int)p.n_active.size();
   // norm gain of the first block after pre block b / loop layer l on the same rows
   auto loop_first = [&]() { return m->blocks[c.n_pre].norm1; };
@@ -591,7 +595,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     kv.s0 = p.scoring ? 0 : b;
     const float* nn = b + 1 < c.n_pre ? m->blocks[b + 1].norm1 : (Lmax > 0 ? loop_first() : nullptr);
     TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn, hmode ? 0 : -1, &x_ready,
-                  p.one_row_per_lane));
+                  p.one_row_per_lane, grid_of(0)));
   }
   float* h = w.hA;
   float* hn = w.hB;
@@ -626,7 +630,8 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
       // probe normalises into its own buffer, rows it finishes are only carried)
       const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1 : (leaving ? nullptr : loop_first());
       TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
-                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1, &x_ready, p.one_row_per_lane));
+                    tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1, &x_ready, p.one_row_per_lane,
+                    grid_of(j - 1)));
     }
     if (probe) {
       if (by_margin) {
@@ -658,7 +663,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     kv.s0 = p.scoring ? 0 : c.n_pre + b;
     const float* nn = b + 1 < c.n_post ? m->blocks[c.n_pre + c.n_loop + b + 1].norm1 : nullptr;
     TRY(run_block(m, c.n_pre + c.n_loop + b, p.final_h, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn,
-                  hmode ? 0 : -1, &x_ready, p.one_row_per_lane));
+                  hmode ? 0 : -1, &x_ready, p.one_row_per_lane, grid_of(0)));
   }
   return TL_OK;
 }
@@ -689,6 +694,34 @@ void add_tiles(std::vector<AttnTile>& out, const std::vector<int>& seq_len, cons
     }
     row += seq_len[sq];
   }
+}
+
+// The closed form of a tile list (AttnGrid) when it has one: equal-length
+// sequences cut into consecutive tiles, capacities carried (cap > 0) and slot
+// offsets in arithmetic progression; else on = 0.
+AttnGrid tile_grid(const std::vector<AttnTile>& t) {
+  AttnGrid g{};
+  if (t.empty() || t[0].cap <= 0 || t[0].row0 != 0 || t[0].pos0 != 0) return g;
+  const int tr = attn_tile_rows();
+  int tps = 0;
+  while (tps < (int)t.size() && t[tps].koff == t[0].koff) ++tps;
+  const int T = t[tps - 1].pos0 + t[tps - 1].nrows;
+  if (tps != (T + tr - 1) / tr || t.size() % tps != 0) return g;
+  g.T = T;
+  g.tps = tps;
+  g.iter = t[0].iter;
+  g.cap = t[0].cap;
+  g.koff0 = t[0].koff;
+  g.kstride = t.size() > (size_t)tps ? t[tps].koff - t[0].koff : 0;
+  for (size_t b = 0; b < t.size(); ++b) {
+    const int sq = (int)b / tps, p0 = ((int)b % tps) * tr;
+    const AttnTile& x = t[b];
+    if (x.row0 != sq * T + p0 || x.nrows != std::min(tr, T - p0) || x.pos0 != p0 || x.iter != g.iter ||
+        x.cap != g.cap || x.koff != g.koff0 + (int64_t)sq * g.kstride)
+      return AttnGrid{};
+  }
+  g.on = 1;
+  return g;
 }
 
 // Final norm on the selected rows, head GEMM, greedy token (lowest index on ties)
@@ -1301,6 +1334,7 @@ tl_status tl_forward(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32
   for (size_t k = 0; k < tile_lists.size(); ++k) {
     p.tiles.push_back(staged<AttnTile>(m, o_tiles[k]));
     p.n_tiles.push_back((int)tile_lists[k].size());
+    p.grids.push_back(tile_grid(tile_lists[k]));
   }
   p.kv.H = c.n_heads;
   p.kv.dh = c.head_dim;
@@ -1407,6 +1441,7 @@ tl_status tl_append(tl_model* m, int32_t n_seqs, const int32_t* cu, const int32_
   for (size_t k = 0; k < tile_lists.size(); ++k) {
     p.tiles.push_back(staged<AttnTile>(m, o_tiles[k]));
     p.n_tiles.push_back((int)tile_lists[k].size());
+    p.grids.push_back(tile_grid(tile_lists[k]));
   }
   p.kv = KVParams{m->kv_base, m->d_lane_off, m->d_lane_cap, c.n_heads, c.head_dim, 0, 0};
   p.final_h = out_hidden ? out_hidden : m->ws.hX;
@@ -1646,6 +1681,7 @@ tl_status tl_speculate(tl_model* m, int32_t n, const int32_t* lanes, int32_t L_d
       for (size_t q = 0; q < tile_lists.size(); ++q) {
         p.tiles.push_back(staged<AttnTile>(m, o_tiles[q]));
         p.n_tiles.push_back((int)tile_lists[q].size());
+        p.grids.push_back(tile_grid(tile_lists[q]));
       }
       p.kv = kvp;
       p.final_h = m->ws.hX;

@@ -137,8 +137,16 @@ static_assert(sizeof(AttnTile) == 32, "descriptor layout");
 // attn_tile_rows() consecutive rows.
 bool attn_tiled_supported(int dtype, int head_dim);
 int attn_tile_rows();
+// A tile list of regular shape, given in closed form so that the kernel need not
+// load its descriptor: tile b is sequence sq = b / tps, rows p0 = (b mod tps) *
+// attn_tile_rows() of it, row0 = sq * T + p0, nrows = min(rows, T - p0), pos0 = p0,
+// iteration iter, capacity cap > 0 and slot-0 offset koff0 + sq * kstride.
+struct AttnGrid {
+  int32_t on, T, tps, iter, cap, pad;
+  int64_t koff0, kstride;
+};
 hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tiles, int n_tiles, const KVParams& kv,
-                                  void* out, hipStream_t s);
+                                  void* out, hipStream_t s, const AttnGrid* grid = nullptr);
 // Stable filter of the active rows after iteration it (it = 0: each row's own
 // iter): rows with depth > it stay (their iter becomes it + 1), the others leave.
 // dest[i] = new index or -1.  count_out[0] = number kept.  If log_out is non-NULL
