@@ -31,6 +31,15 @@ __device__ __forceinline__ void static_for(F&& f) {
   }
 }
 
+// The loads of k step J of a stage's eight: pieces PPS J .. PPS (J + 1) - 1 of NP,
+// and every piece left at the last step.
+template <int PPS, int NP, int J, class P>
+__device__ __forceinline__ void issue_pieces(P&& piece) {
+  constexpr int b = PPS * J < NP ? PPS * J : NP;
+  constexpr int e = J == 7 ? NP : (PPS * (J + 1) < NP ? PPS * (J + 1) : NP);
+  static_for<b, e>(piece);
+}
+
 template <class AT> struct Mfma;
 template <> struct Mfma<f16> {
   typedef half8 frag;
@@ -859,7 +868,7 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_rows_kernel(GemmArgs g, GemmEp
   const int M = g.M, N = g.N, K = g.K, groups = K >> 7;
   const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
   const int g0 = kb >> 7, nreal = (ke >> 7) - g0;
-  const int nst = (nreal + 1) & ~1;
+  const int nst = (nreal + 3) & ~3;
   const int nb = min(wn0 >> 5, (N >> 5) - 1);
   const f16* A = reinterpret_cast<const f16*>(g.A);
 
@@ -901,16 +910,18 @@ __global__ __launch_bounds__(256, 2) void gemm_w4_rows_kernel(GemmArgs g, GemmEp
 
   static_for<0, AC + 3>([&](auto pc) __attribute__((always_inline)) { piece(std::integral_constant<int, 0>{}, pc, 0); });
   if (gate_closed(g.live)) return;
-  for (int s0 = 0; s0 < nst; s0 += 2) {
-    static_for<0, 2>([&](auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value;
-      const int st = s0 + u;
-      lstore(uc, st & 1);
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+    static_for<0, 4>([&](auto sc4) __attribute__((always_inline)) {
+      constexpr int u = decltype(sc4)::value & 1;
+      const int st = s0 + decltype(sc4)::value;
+      lstore(std::integral_constant<int, u>{}, st & 1);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       const float sc = st < nreal ? (float)__builtin_bit_cast(f16, rs[u]) : 0.f;
       rows_group<RB, KC>(acc, As[st & 1], wr0, 0, lane, rw[u], sc, [&](auto jc) __attribute__((always_inline)) {
-        piece(std::integral_constant<int, 1 - u>{}, jc, st + 1);
+        issue_pieces<2, AC + 3, decltype(jc)::value>([&](auto pc) __attribute__((always_inline)) {
+          piece(std::integral_constant<int, 1 - u>{}, pc, st + 1);
+        });
         __builtin_amdgcn_sched_barrier(0);
       });
     });
@@ -936,7 +947,7 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_pair_kernel(GemmArgs g, GemmEp
   const int kb = blockIdx.z * kchunk, ke = min(K, kb + kchunk);
   const int g0 = kb >> 7, gend = ke >> 7;
   const int nreal = (gend - g0 + 1) >> 1;   // two-group stages
-  const int nst = (nreal + 1) & ~1;
+  const int nst = (nreal + 3) & ~3;
   const int nb = min(wn0 >> 5, (N >> 5) - 1);
   const f16* A = reinterpret_cast<const f16*>(g.A);
 
@@ -978,18 +989,20 @@ __global__ __launch_bounds__(512, 1) void gemm_w4_pair_kernel(GemmArgs g, GemmEp
 
   static_for<0, AC + 3>([&](auto pc) __attribute__((always_inline)) { piece(std::integral_constant<int, 0>{}, pc, 0); });
   if (gate_closed(g.live)) return;
-  for (int s0 = 0; s0 < nst; s0 += 2) {
-    static_for<0, 2>([&](auto uc) __attribute__((always_inline)) {
-      constexpr int u = decltype(uc)::value;
-      const int st = s0 + u;
-      lstore(uc, st & 1);
+  for (int s0 = 0; s0 < nst; s0 += 4) {
+    static_for<0, 4>([&](auto sc4) __attribute__((always_inline)) {
+      constexpr int u = decltype(sc4)::value & 1;
+      const int st = s0 + decltype(sc4)::value;
+      lstore(std::integral_constant<int, u>{}, st & 1);
       lds_barrier();
       __builtin_amdgcn_sched_barrier(0);
       // an odd group count leaves the last stage's second half empty
       const bool valid = st < nreal && g0 + 2 * st + kh < gend;
       const float sc = valid ? (float)__builtin_bit_cast(f16, rs[u]) : 0.f;
       rows_group<RB, KC>(acc, As[st & 1], 0, 16 * kh, lane, rw[u], sc, [&](auto jc) __attribute__((always_inline)) {
-        piece(std::integral_constant<int, 1 - u>{}, jc, st + 1);
+        issue_pieces<2, AC + 3, decltype(jc)::value>([&](auto pc) __attribute__((always_inline)) {
+          piece(std::integral_constant<int, 1 - u>{}, pc, st + 1);
+        });
         __builtin_amdgcn_sched_barrier(0);
       });
     });
@@ -1287,11 +1300,13 @@ TileCfg pick_tile(int act_dtype, const GemmArgs& g, int kind) {
     }
   }
   if (!g.Bw4 && t.bm == 32 && t.bn == 64 && t.splits == 1) t.depth = 4;
-  // one unsplit 64 x 64 tile per CU at most (QKV at 128 rows): nothing else on the
-  // CU hides a stage's loads, so keep three stages in flight (171 -> 162 us of QKV
-  // per forward; with two tiles on a CU, or a split that pads the stage count,
-  // two stages measured faster)
-  if (t.bm == 64 && t.bn == 64 && t.splits == 1 && tiles <= kCUs) t.depth = 4;
+  // one unsplit INT4 64 x 64 tile per CU at most (QKV at 128 rows): nothing else on
+  // the CU hides a stage's loads, so keep three stages in flight (171 -> 162 us of
+  // QKV per forward; with two tiles on a CU, or a split that pads the stage count,
+  // two stages measured faster).  The 16-bit tile of the same shape is faster with
+  // two stages (QKV 6144 x 2048 at 96 / 128 rows: 17.9 / 17.5 us with three stages
+  // in flight, 16.4 / 16.0 us with one).
+  if (g.Bw4 && t.bm == 64 && t.bn == 64 && t.splits == 1 && tiles <= kCUs) t.depth = 4;
   // INT4 64 x 64 tiles whose K range (split) is whole 256-wide stages: two groups
   // per stage, half the stages (with the two-stage ring: four stages of this size
   // spill).  Per forward at 128 rows: QKV 162 -> 152 us, gate/up 180 -> 170 us,
