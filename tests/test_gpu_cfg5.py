@@ -62,22 +62,39 @@ def _sample(plens, L1):
     return pick
 
 
-def _oracle_lanes(w, lanes, prompts, forced, plens, L1, eff):
-    """Oracle hidden states and logits of the sampled lanes (host thread)."""
-    t0 = time.time()
-    m = oracle.OracleModel.from_weights(w)
-    say("oracle model in %.1f s" % (time.time() - t0))
-    out = {}
-    for i in lanes:
+class _OracleRunner:
+    """Oracle hidden states and logits of the sampled lanes, computed lane by lane
+    on a host thread (it needs only host-known inputs: the depths follow from the
+    draws), so the host works while the device does."""
+
+    def __init__(self, w, lanes, prompts, forced, plens, L1, eff):
+        self.args = (w, prompts, forced, plens, L1, eff)
+        self.pool = cf.ThreadPoolExecutor(1)
+        self.model = self.pool.submit(self._model, w)
+        self.futs = {i: self.pool.submit(self._lane, i) for i in lanes}
+
+    @staticmethod
+    def _model(w):
+        t0 = time.time()
+        m = oracle.OracleModel.from_weights(w)
+        say("oracle model in %.1f s" % (time.time() - t0))
+        return m
+
+    def _lane(self, i):
+        _, prompts, forced, plens, L1, eff = self.args
+        m = self.model.result()
         deps = np.concatenate([np.full(plens[i], L1[i]), eff[i]])
         seq = np.concatenate([prompts[i], forced[i]])
         t0 = time.time()
-        out[i] = oracle.forward_ragged(m, seq, deps, want_logits="all")
+        out = oracle.forward_ragged(m, seq, deps, want_logits="all")
         say("oracle lane", i, "prompt", int(plens[i]), "L1", int(L1[i]), "in %.1f s" % (time.time() - t0))
-    return out
+        return out
 
 
-def test_cfg5_continuous_depth_decode():
+@pytest.fixture(scope="module")
+def cfg5_run():
+    """Prefill of the 256 lanes, continuous-depth decode, then the same lanes again
+    in lockstep on the device; the oracle's lanes start on the host first."""
     ensure_built()
     spec = synth.SPECS[5]
     n, new = 256, 64
@@ -92,14 +109,13 @@ def test_cfg5_continuous_depth_decode():
     eff_host = np.stack([oracle.clamp_depths(draws[i, 1:], int(L1[i])) for i in range(n)])
     sample = _sample(plens, L1)
     say("oracle sample:", sample)
-    # the oracle needs only host-known inputs (depths follow from the draws), so it
-    # runs while the device works
-    pool = cf.ThreadPoolExecutor(1)
-    fut = pool.submit(_oracle_lanes, w, sample, prompts, forced, plens, L1, eff_host)
+    runner = _OracleRunner(w, sample, prompts, forced, plens, L1, eff_host)
     caps = plens + new - 1
     model = load_model(w, max_lanes=n, max_pos=512 + new, max_L=32, kv_arena_bytes=kv_bytes(spec, L1, caps),
                        batch_invariant=1)
     say("loaded; memory (weights, kv, workspace) =", tl.tl_memory_info(model))
+    res = {"sample": sample, "plens": plens, "L1": L1, "eff_host": eff_host, "oracle": runner,
+           "lockstep_first_diff": None, "agree": {}, "gaps": {}}
     try:
         toks = torch.tensor(np.concatenate(prompts), dtype=torch.int32, device="cuda")
         cu = np.concatenate([[0], np.cumsum(plens)]).astype(np.int32)
@@ -120,11 +136,11 @@ def test_cfg5_continuous_depth_decode():
         tl.tl_sync_errors(model)
         t_cdb = time.time() - t0
         say("continuous-depth decode of %d x %d tokens in %.2f s" % (n, new - 1, t_cdb))
-        assert np.array_equal(eff, eff_host)
-        H_pre = {i: hid[cu[i]:cu[i + 1]].cpu().numpy() for i in sample}
+        res["eff"] = eff
+        res["H_pre"] = {i: hid[cu[i]:cu[i + 1]].cpu().numpy() for i in sample}
         H_run = run_h.cpu().numpy()
         T_run = run_tok.cpu().numpy()
-        T_pre = nxt.cpu().numpy()
+        res["H_run"], res["T_run"], res["T_pre"] = H_run, T_run, nxt.cpu().numpy()
         # lockstep: the same lanes prefilled again, then one tl_decode_step per token
         tl.tl_forward(model, cu, toks, seq_L=L1, lanes=lanes, max_new_tokens=new - 1)
         torch.cuda.synchronize()
@@ -134,37 +150,66 @@ def test_cfg5_continuous_depth_decode():
         dt_copy = 0.0
         for t in range(new - 1):
             e2 = tl.tl_decode_step(model, lanes, draws[:, 1 + t], out, in_tokens=feed[:, t].contiguous(), out_hidden=hs)
-            assert np.array_equal(e2, eff[:, t])
             torch.cuda.synchronize()
             t1 = time.time()
-            assert np.array_equal(out.cpu().numpy(), T_run[:, t]), t
-            assert np.array_equal(hs.cpu().numpy(), H_run[:, t]), t
+            same = (np.array_equal(e2, eff[:, t]) and np.array_equal(out.cpu().numpy(), T_run[:, t])
+                    and np.array_equal(hs.cpu().numpy(), H_run[:, t]))
             dt_copy += time.time() - t1
-        say("lockstep decode %.2f s vs continuous-depth %.2f s; equal bit for bit"
-            % (time.time() - t0 - dt_copy, t_cdb))
+            if not same:
+                res["lockstep_first_diff"] = t
+                break
+        say("lockstep decode %.2f s vs continuous-depth %.2f s" % (time.time() - t0 - dt_copy, t_cdb))
     finally:
         tl.tl_free(model)
-    ref = fut.result()
-    pool.shutdown()
-    agree, total, gaps = 0, 0, []
-    for i in sample:
-        h_ref, lg_ref = ref[i]
-        P = int(plens[i])
-        r_pre, rm_pre = rel_l2(H_pre[i], h_ref[:P]), row_rel_max(H_pre[i], h_ref[:P])
-        r_dec, rm_dec = rel_l2(H_run[i], h_ref[P:]), row_rel_max(H_run[i], h_ref[P:])
-        say("lane", i, "prompt", P, "L1", int(L1[i]), "prefill rel %.2e (row max %.2e) decode rel %.2e (row max %.2e)"
+    yield res
+    runner.pool.shutdown(cancel_futures=True)
+
+
+# the oracle's lanes are checked in three groups so that no single test waits on
+# more than about a minute of host work: the 13 shortest prompts, the two longest
+# (511 and 512 tokens, contexts up to 575), and the lane of the deepest first token
+# (or, when that lane is already among them, the next-shortest)
+GROUPS = {"short": slice(0, 13), "long": slice(13, 15), "deepest": slice(15, 16)}
+
+
+@pytest.mark.timeout(300)
+def test_cfg5_continuous_depth_equals_lockstep(cfg5_run):
+    r = cfg5_run
+    assert np.array_equal(r["eff"], r["eff_host"]), "effective depths differ from the monotone clamp"
+    assert r["lockstep_first_diff"] is None, "lockstep differs from continuous depth at token %s" % (
+        r["lockstep_first_diff"],)
+
+
+@pytest.mark.timeout(300)
+@pytest.mark.parametrize("group", list(GROUPS))
+def test_cfg5_oracle_lanes(cfg5_run, group):
+    r = cfg5_run
+    for i in r["sample"][GROUPS[group]]:
+        h_ref, lg_ref = r["oracle"].futs[i].result()
+        P, L1 = int(r["plens"][i]), int(r["L1"][i])
+        H_pre, H_run = r["H_pre"][i], r["H_run"][i]
+        r_pre, rm_pre = rel_l2(H_pre, h_ref[:P]), row_rel_max(H_pre, h_ref[:P])
+        r_dec, rm_dec = rel_l2(H_run, h_ref[P:]), row_rel_max(H_run, h_ref[P:])
+        say("lane", i, "prompt", P, "L1", L1, "prefill rel %.2e (row max %.2e) decode rel %.2e (row max %.2e)"
             % (r_pre, rm_pre, r_dec, rm_dec))
-        assert r_pre <= bar(int(L1[i])) and rm_pre <= bar(int(L1[i]))
-        assert r_dec <= bar(int(L1[i])) and rm_dec <= bar(int(L1[i]))
-        lg = lg_ref[P - 1:]
-        got = np.concatenate([[T_pre[i]], T_run[i]])
-        g = near_tie_gaps(got, lg)
-        gaps += g
-        agree += len(got) - len(g)
-        total += len(got)
+        assert r_pre <= bar(L1) and rm_pre <= bar(L1)
+        assert r_dec <= bar(L1) and rm_dec <= bar(L1)
+        got = np.concatenate([[r["T_pre"][i]], r["T_run"][i]])
+        g = near_tie_gaps(got, lg_ref[P - 1:])
+        r["gaps"][i] = g
+        r["agree"][i] = (len(got) - len(g), len(got))
+        # a token may differ only at a near-tie of the oracle's own logits
+        assert all(x <= 0.05 for x in g), (i, g)
+
+
+def test_cfg5_top1_agreement(cfg5_run):
+    """At least 99 % of the sampled lanes' greedy tokens agree with the oracle's
+    (the benchmark spec's bar), over at least 1000 tokens."""
+    r = cfg5_run
+    assert sorted(r["agree"]) == sorted(r["sample"]), "some oracle lanes were not checked"
+    agree = sum(a for a, _ in r["agree"].values())
+    total = sum(t for _, t in r["agree"].values())
+    gaps = [g for v in r["gaps"].values() for g in v]
     say("top-1 agreement", agree, "/", total, "gaps of the differing tokens (x rms):", ["%.4f" % g for g in gaps])
-    # a token may differ only at a near-tie of the oracle's own logits, and at
-    # least 99 % of the greedy tokens must agree (the benchmark spec's bar)
-    assert all(g <= 0.05 for g in gaps)
     assert total >= 1000
     assert agree >= 0.99 * total

@@ -61,6 +61,7 @@ def test_abi_checks_under_sanitizers():
 
 
 @pytest.mark.gpu
+@pytest.mark.timeout(900)
 def test_device_paths_under_sanitizers():
     """Load, scoring forwards and their graph replay, cached decode with early exit
     and in every cache mode, lane forks and appends, speculative rounds, the
