@@ -1464,8 +1464,12 @@ hipError_t launch_skinny(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg& t
 
 // The row-tiled INT4 kernels for 65..128 rows where they measured ahead (see their
 // comments): gate/up-shaped products (N >= 8192) unsplit on the eight-wave pair
-// kernel, products with K >= 4096 (the down projection) split 4 ways on the
-// row-tiled kernel with WM = 2.  Returns false to keep the LDS-tiled kernel.
+// kernel; products with K >= 4096 (the down projection) and residual products with
+// N <= 4096 (the O projection at 128 rows: 12.4 -> 11.6 us per launch with its
+// reduction, forward 0.598 -> 0.587 ms) split 4 ways on the row-tiled kernel with
+// WM = 2.  The QKV product stays on the LDS-tiled kernel, whose epilogue gathers
+// its operands during the K loop (on the row-tiled kernel: 16.5 -> 23 us per
+// launch).  Returns false to keep the LDS-tiled kernel.
 bool w4_rows_launch(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool* norm_done, hipError_t* err) {
   if (!g.Bw4 || g.invariant || g.M <= 64 || g.M > 128 || e.pair_g != 16 || (g.K % 128) || (g.N % 32)) return false;
   if (e.kind != EPI_SWIGLU && e.kind != EPI_RESID && e.kind != EPI_STORE) return false;
@@ -1480,7 +1484,8 @@ bool w4_rows_launch(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool* no
     *err = hipGetLastError();
     return true;
   }
-  if (g.K < 4096 || !g.partial || (int64_t)4 * g.M * g.N > g.partial_cap) return false;
+  if ((g.K < 4096 && !(e.kind == EPI_RESID && g.N <= 4096)) || !g.partial || (int64_t)4 * g.M * g.N > g.partial_cap)
+    return false;
   const int per = (units + 3) / 4;
   const int sp = (units + per - 1) / per;
   dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, sp);
