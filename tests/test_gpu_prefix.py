@@ -26,6 +26,7 @@ SPECS = {
     "tiny-fp32": synth.SPECS[1],
     "tiny-w4": synth.ModelSpec("tiny-w4", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "w4g128"),
     "tiny-bf16-stack": synth.ModelSpec("tiny-bf16-stack", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16"),
+    "mid-w4": synth.ModelSpec("mid-w4", 256, 512, 8, 64, 1024, 1, 1, 0, "f16", "w4g128"),
 }
 L0, PLEN, CAP_NEW = 6, 13, 64
 

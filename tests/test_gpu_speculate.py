@@ -30,6 +30,8 @@ CASES = {
     "tiny-w4": (synth.ModelSpec("tiny-w4", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "w4g128"), (6, 8, 3), 3, 10, 5e-3),
     "tiny-bf16-stack": (synth.ModelSpec("tiny-bf16-stack", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16"),
                         (6, 8, 2), 1, 6, 3e-2),
+    # the MFMA and split-K paths at a 512-wide INT4 model (8 heads x 64)
+    "mid-w4": (synth.ModelSpec("mid-w4", 256, 512, 8, 64, 1024, 1, 1, 0, "f16", "w4g128"), (6, 8, 3), 2, 8, 5e-3),
 }
 L_PRE = 8
 

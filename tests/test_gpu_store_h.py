@@ -37,6 +37,7 @@ SPECS = {
     "tiny-fp32": synth.SPECS[1],
     "tiny-w4": synth.ModelSpec("tiny-w4", 256, 128, 4, 32, 256, 1, 1, 0, "f16", "w4g128"),
     "tiny-bf16-stack": synth.ModelSpec("tiny-bf16-stack", 320, 192, 2, 96, 384, 2, 2, 1, "bf16", "bf16"),
+    "mid-w4": synth.ModelSpec("mid-w4", 256, 512, 8, 64, 1024, 1, 1, 0, "f16", "w4g128"),
 }
 MODES = {"h": tl.TL_KV_H, "h8": tl.TL_KV_H8, "h4": tl.TL_KV_H4, "d8": tl.TL_KV_D8}
 
