@@ -576,9 +576,17 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     TRY(plan_hpass(m, p, hps, s));
     m->hpass = &hps;
   }
+  const int Lmax = (int)p.n_active.size();
+  // every row runs the same number of loop iterations (no early exit): no row moves
+  // before the last iteration, where all leave at once, so the pass works in
+  // p.final_h from the start and that last compaction (which would only copy every
+  // row there, in caller order) is skipped
+  bool in_final = !p.ee && p.final_h && Lmax > 0;
+  for (int j = 0; j < Lmax && in_final; ++j) in_final = p.n_active[j] == p.n;
+  float* const h0 = in_final ? p.final_h : w.hA;
   // the first pre block's norm is formed with the gather (x_ready)
   bool x_ready = false;
-  TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, w.hA, m->d_err, c.vocab, s,
+  TIMED(TL_T_EMBED, HIPCHK(launch_embed(c.boundary_dtype, m->embed, p.tokens, p.n, d, h0, m->d_err, c.vocab, s,
                                         c.n_pre > 0 ? m->blocks[0].norm1 : nullptr, c.rms_eps, m->act, w.x16,
                                         &x_ready)));
   KVParams kv = p.kv;
@@ -588,16 +596,15 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
   auto grid_of = [&](int k) -> const AttnGrid* {
     return (tiled && k < (int)p.grids.size()) ? &p.grids[k] : nullptr;
   };
-  const int Lmax = (int)p.n_active.size();
   // norm gain of the first block after pre block b / loop layer l on the same rows
   auto loop_first = [&]() { return m->blocks[c.n_pre].norm1; };
   for (int b = 0; b < c.n_pre; ++b) {
     kv.s0 = p.scoring ? 0 : b;
     const float* nn = b + 1 < c.n_pre ? m->blocks[b + 1].norm1 : (Lmax > 0 ? loop_first() : nullptr);
-    TRY(run_block(m, b, w.hA, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn, hmode ? 0 : -1, &x_ready,
+    TRY(run_block(m, b, h0, p.rows0, p.n, kv, s, t0, nt0, x_ready, nn, hmode ? 0 : -1, &x_ready,
                   p.one_row_per_lane, grid_of(0)));
   }
-  float* h = w.hA;
+  float* h = h0;
   float* hn = w.hB;
   const RowInfo* rows = p.rows0;
   RowInfo* rbuf[2] = {w.rowsA, w.rowsB};
@@ -643,7 +650,9 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     }
     hprev_saved = save_prev;
     moved = leaving;
-    if (moved) {
+    if (moved && in_final && next == 0) {
+      moved = false;   // every row is in p.final_h already, in caller order
+    } else if (moved) {
       RowInfo* rout = rbuf[flip];
       int32_t* logn = p.log ? p.log + log_off + nj : nullptr;
       TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rows, nj, j, rout, w.dest, w.count, logn, p.ee ? m->ee_live : nullptr, s));
