@@ -456,6 +456,12 @@ struct Pass {
   const std::vector<RowInfo>* rows_host = nullptr;
   // decode steps: every lane has one row
   bool one_row_per_lane = false;
+  // gain of the final norm, for a pass whose every row is followed by the head: when
+  // all rows leave the loop together and no post block follows, the last residual
+  // product forms RMSNorm(h) * head_norm into ws.x16 (the same bits the head's own
+  // norm would give) and run_pass sets head_norm_done
+  const float* head_norm = nullptr;
+  bool head_norm_done = false;
 };
 
 // Store-h rebuild plan of a pass: every lane's positions 0 .. (last position in
@@ -538,8 +544,10 @@ tl_status plan_hpass(tl_model* m, const Pass& p, tl::HPass& hp, hipStream_t s) {
   return TL_OK;
 }
 
+// xnorm: the rows already normalised by the final norm (operand type), or NULL to
+// normalise h (gathered) here.
 tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out, float* logits, int32_t* out_tok,
-                   const int32_t* pend_lanes, hipStream_t s, float* margin = nullptr);
+                   const int32_t* pend_lanes, hipStream_t s, float* margin = nullptr, const void* xnorm = nullptr);
 
 // Iteration j is probed by the early-exit rule (never the last one: it could not
 // shorten the loop).
@@ -635,7 +643,9 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
       kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + (j - 1) * c.n_loop + l;
       // (a probe leaves the next iteration's normalised input alone: the logit
       // probe normalises into its own buffer, rows it finishes are only carried)
-      const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1 : (leaving ? nullptr : loop_first());
+      const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1
+                                         : (!leaving ? loop_first()
+                                                     : (in_final && next == 0 && c.n_post == 0 ? p.head_norm : nullptr));
       TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
                     tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1, &x_ready, p.one_row_per_lane,
                     grid_of(j - 1)));
@@ -667,6 +677,7 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     log_off += nj;
   }
   m->gate_live = nullptr;
+  p.head_norm_done = in_final && c.n_post == 0 && p.head_norm && x_ready;
   x_ready = false;
   for (int b = 0; b < c.n_post; ++b) {
     kv.s0 = p.scoring ? 0 : c.n_pre + b;
@@ -736,15 +747,15 @@ AttnGrid tile_grid(const std::vector<AttnTile>& t) {
 // Final norm on the selected rows, head GEMM, greedy token (lowest index on ties)
 // and, with margin != NULL, the top-1 minus top-2 logit margin of each row.
 tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out, float* logits, int32_t* out_tok,
-                   const int32_t* pend_lanes, hipStream_t s, float* margin) {
+                   const int32_t* pend_lanes, hipStream_t s, float* margin, const void* xnorm) {
   if (n_out <= 0) return TL_OK;
   const tl_config& c = m->cfg;
   auto& w = m->ws;
   TRY(tbegin(m, s));
-  HIPCHK(launch_rmsnorm(m->act, h, m->final_norm, gather, n_out, c.d_model, c.rms_eps, w.xh, s));
+  if (!xnorm) HIPCHK(launch_rmsnorm(m->act, h, m->final_norm, gather, n_out, c.d_model, c.rms_eps, w.xh, s));
   const int tiles = gemm_head_tiles(m->gdt, n_out, c.vocab);
   GemmArgs g{};
-  g.A = w.xh;
+  g.A = xnorm ? xnorm : w.xh;
   g.M = n_out;
   g.N = c.vocab;
   g.K = c.d_model;
@@ -1778,8 +1789,10 @@ tl_status decode_run_step(tl_model* m, int n, const int32_t* lanes, const std::v
   p.final_h = out_hidden ? out_hidden : m->ws.hX;
   p.log = out_log;
   p.one_row_per_lane = true;
+  p.head_norm = m->final_norm;
   TRY(run_pass(m, p, s));
-  TRY(run_head(m, p.final_h, nullptr, n, out_logits, out_tokens, lanes_dev, s));
+  TRY(run_head(m, p.final_h, nullptr, n, out_logits, out_tokens, lanes_dev, s, nullptr,
+               p.head_norm_done ? m->ws.x16 : nullptr));
   for (int i = 0; i < n; ++i) {
     Lane& ln = m->lanes[lanes[i]];
     ln.len += 1;
