@@ -220,7 +220,7 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
   HIPCHK(hipStreamSynchronize(s));
   if (m->has_last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
   drop_graphs(m);
-  void* olds[] = {w.hA, w.hB, w.hX, w.hE, w.x16, w.q16, w.o16, w.u16, w.xh, w.rowsA, w.rowsB,
+  void* olds[] = {w.hA, w.hB, w.hX, w.hE, w.x16, w.x16b, w.q16, w.o16, w.u16, w.xh, w.rowsA, w.rowsB,
                   w.dest, w.count, w.tok, w.tok2, w.part_v, w.part_i, w.part_v2, w.kv_scratch, w.splitk};
   for (void* p : olds) dev_free(m, p);
   w = tl::Workspace{};
@@ -230,7 +230,8 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
   struct Req { void** p; size_t bytes; } reqs[] = {
       {(void**)&w.hA, (size_t)R * d * 4},           {(void**)&w.hB, (size_t)R * d * 4},
       {(void**)&w.hX, (size_t)R * d * 4},           {(void**)&w.hE, (size_t)R * d * 4},
-      {&w.x16, (size_t)R * d * m->esz},             {&w.q16, (size_t)R * d * m->esz},
+      {&w.x16, (size_t)R * d * m->esz},             {&w.x16b, (size_t)R * d * m->esz},
+      {&w.q16, (size_t)R * d * m->esz},
       {&w.o16, (size_t)R * d * m->esz},             {&w.u16, (size_t)R * F * m->esz},
       {&w.xh, (size_t)std::max(O, 1) * d * m->esz}, {(void**)&w.rowsA, (size_t)R * sizeof(RowInfo)},
       {(void**)&w.rowsB, (size_t)R * sizeof(RowInfo)}, {(void**)&w.dest, (size_t)R * 4},
@@ -639,13 +640,18 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     if (probe && !by_margin && !hprev_saved)
       HIPCHK(hipMemcpyAsync(m->ee_hprev, h, (size_t)nj * d * 4, hipMemcpyDeviceToDevice, s));
     const bool save_prev = probe && !by_margin && !leaving && ee_probed(p.ee, j + 1, Lmax);
+    // the compaction after this iteration as one kernel (no early exit, few rows)
+    const bool fused_move = !p.ee && nj <= kCompactMoveRows;
     for (int l = 0; l < c.n_loop; ++l) {
       kv.s0 = p.scoring ? 0 : c.n_pre + c.n_post + (j - 1) * c.n_loop + l;
       // (a probe leaves the next iteration's normalised input alone: the logit
       // probe normalises into its own buffer, rows it finishes are only carried)
+      // rows that stay after a compaction get their next norm here too when the
+      // compaction can move the normalised rows along (fused_move)
       const float* nn = l + 1 < c.n_loop ? m->blocks[c.n_pre + l + 1].norm1
-                                         : (!leaving ? loop_first()
-                                                     : (in_final && next == 0 && c.n_post == 0 ? p.head_norm : nullptr));
+                        : !leaving        ? loop_first()
+                        : (in_final && next == 0 && c.n_post == 0) ? p.head_norm
+                        : (next > 0 && fused_move) ? loop_first() : nullptr;
       TRY(run_block(m, c.n_pre + l, h, rows, nj, kv, s, tiled ? p.tiles[j - 1] : nullptr,
                     tiled ? p.n_tiles[j - 1] : 0, x_ready, nn, hmode ? j : -1, &x_ready, p.one_row_per_lane,
                     grid_of(j - 1)));
@@ -665,8 +671,17 @@ tl_status run_pass(tl_model* m, Pass& p, hipStream_t s) {
     } else if (moved) {
       RowInfo* rout = rbuf[flip];
       int32_t* logn = p.log ? p.log + log_off + nj : nullptr;
-      TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rows, nj, j, rout, w.dest, w.count, logn, p.ee ? m->ee_live : nullptr, s));
-                          HIPCHK(launch_move_rows(h, w.dest, rows, nj, d, hn, p.final_h, s)));
+      if (fused_move) {
+        // the next iteration's normalised rows (if the last product formed them)
+        // move with the rows they belong to
+        TIMED(TL_T_COMPACT, HIPCHK(launch_compact_move(rows, nj, j, rout, w.count, logn, h, d, hn, p.final_h,
+                                                       x_ready ? w.x16 : nullptr, w.x16b, d * m->esz, s)));
+        if (x_ready) std::swap(w.x16, w.x16b);
+      } else {
+        TIMED(TL_T_COMPACT, HIPCHK(launch_compact(rows, nj, j, rout, w.dest, w.count, logn, p.ee ? m->ee_live : nullptr, s));
+                            HIPCHK(launch_move_rows(h, w.dest, rows, nj, d, hn, p.final_h, s)));
+        x_ready = false;   // rows moved, their normalised rows did not
+      }
       rows = rout;
       flip ^= 1;
       std::swap(h, hn);
@@ -1848,6 +1863,7 @@ size_t noalloc_layout(const tl_model* m, int n, size_t stage_bytes, uint8_t* bas
   x.hX = static_cast<float*>(take(R * d * 4));
   x.hE = static_cast<float*>(take(R * d * 4));
   x.x16 = take(R * d * m->esz);
+  x.x16b = take(R * d * m->esz);
   x.q16 = take(R * d * m->esz);
   x.o16 = take(R * d * m->esz);
   x.u16 = take(R * F * m->esz);

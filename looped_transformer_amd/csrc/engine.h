@@ -76,6 +76,7 @@ struct Workspace {
   int64_t kv_scratch_elems = 0;
   float *hA = nullptr, *hB = nullptr, *hX = nullptr, *hE = nullptr;
   void *x16 = nullptr, *q16 = nullptr, *o16 = nullptr, *u16 = nullptr, *xh = nullptr;
+  void* x16b = nullptr;             // x16's partner: normalised rows moved by a compaction
   RowInfo *rowsA = nullptr, *rowsB = nullptr;
   int32_t *dest = nullptr, *count = nullptr, *tok = nullptr, *tok2 = nullptr;
   float* part_v = nullptr;

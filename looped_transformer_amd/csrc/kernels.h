@@ -159,6 +159,15 @@ hipError_t launch_compact(const RowInfo* rows_in, int n, int it, RowInfo* rows_o
 hipError_t launch_move_rows(const float* h, const int32_t* dest, const RowInfo* rows, int n, int d,
                             float* h_next, float* h_exit, hipStream_t s);
 hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream_t s);
+// launch_compact followed by launch_move_rows in one kernel, for at most
+// kCompactMoveRows rows none of which is marked done: kept rows to rows_out /
+// h_next (and, with x set, their rows of xrow_bytes bytes from x to x_next), leaving
+// rows to h_exit[orig]; count_out[0] = rows kept.  No dest array.
+constexpr int kCompactMoveRows = 1024;
+hipError_t launch_compact_move(const RowInfo* rows_in, int n, int it, RowInfo* rows_out, int32_t* count_out,
+                               int32_t* log_out, const float* h, int d, float* h_next, float* h_exit, const void* x,
+                               void* x_next, int xrow_bytes, hipStream_t s);
+
 // Early-exit probe after loop iteration it on n rows (one workgroup per row): rows not
 // done are stable when margin[i] > margin_thr (margin != NULL) or when
 // ||h_i - h_prev_i|| / ||h_i|| < tau; streak counts consecutive stable probes and

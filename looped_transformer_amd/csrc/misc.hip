@@ -203,6 +203,52 @@ __global__ __launch_bounds__(256) void move_rows_kernel(const float* __restrict_
   for (int c = threadIdx.x * 4; c < d; c += 1024) *reinterpret_cast<float4*>(dst + c) = *reinterpret_cast<const float4*>(src + c);
 }
 
+// Compaction and row move in one kernel, for passes of at most kCompactMoveRows
+// rows without early exit.  Workgroup i counts the rows before i that stay (every
+// workgroup reads the row list), so row i's destination needs no separate
+// compaction kernel.  A kept row goes to rows_out / h_next at that index (and its
+// operand-type normalised row of x to x_next, when x is set); a leaving row goes
+// to h_exit at its caller index.  The last workgroup writes the kept count.
+__global__ __launch_bounds__(256) void compact_move_kernel(const RowInfo* __restrict__ in, int n, int it,
+                                                          RowInfo* __restrict__ out, int32_t* count_out,
+                                                          int32_t* log_out, const float* __restrict__ h, int d,
+                                                          float* __restrict__ h_next, float* __restrict__ h_exit,
+                                                          const uint8_t* __restrict__ x, uint8_t* __restrict__ x_next,
+                                                          int xrow_bytes) {
+  __shared__ int wcnt[4];
+  const int i = blockIdx.x, tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  RowInfo ri = in[i];
+  int c = 0;
+  for (int k = tid; k < i; k += 256) {
+    const RowInfo rk = in[k];
+    c += rk.depth > (it > 0 ? it : rk.iter) ? 1 : 0;
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) c += __shfl_xor(c, o, 64);
+  if (lane == 0) wcnt[w] = c;
+  __syncthreads();
+  const int before = wcnt[0] + wcnt[1] + wcnt[2] + wcnt[3];
+  if (it > 0) ri.iter = it;
+  const bool keep = ri.depth > ri.iter;
+  if (tid == 0) {
+    if (keep) {
+      RowInfo ro = ri;
+      ro.iter += 1;
+      out[before] = ro;
+      if (log_out) log_out[before] = ri.orig;
+    }
+    if (i == n - 1 && count_out) *count_out = before + (keep ? 1 : 0);
+  }
+  float* dst = keep ? h_next + (int64_t)before * d : h_exit + (int64_t)ri.orig * d;
+  const float* src = h + (int64_t)i * d;
+  for (int c4 = tid * 4; c4 < d; c4 += 1024) *reinterpret_cast<float4*>(dst + c4) = *reinterpret_cast<const float4*>(src + c4);
+  if (keep && x) {
+    const uint8_t* xs = x + (int64_t)i * xrow_bytes;
+    uint8_t* xd = x_next + (int64_t)before * xrow_bytes;
+    for (int b = tid * 16; b < xrow_bytes; b += 4096) *reinterpret_cast<uint4*>(xd + b) = *reinterpret_cast<const uint4*>(xs + b);
+  }
+}
+
 __global__ void write_orig_kernel(const RowInfo* rows, int n, int32_t* out) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) out[i] = rows[i].orig;
@@ -668,6 +714,16 @@ hipError_t launch_compact(const RowInfo* rows_in, int n, int it, RowInfo* rows_o
                           int32_t* log_out, int32_t* running_out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, rows_in, n, it, rows_out, dest, count_out, log_out, running_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_compact_move(const RowInfo* rows_in, int n, int it, RowInfo* rows_out, int32_t* count_out,
+                               int32_t* log_out, const float* h, int d, float* h_next, float* h_exit, const void* x,
+                               void* x_next, int xrow_bytes, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n > kCompactMoveRows || (d % 4) || (x && (xrow_bytes % 16))) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(compact_move_kernel, dim3(n), dim3(256), 0, s, rows_in, n, it, rows_out, count_out, log_out, h, d,
+                     h_next, h_exit, static_cast<const uint8_t*>(x), static_cast<uint8_t*>(x_next), xrow_bytes);
   return hipGetLastError();
 }
 
