@@ -110,57 +110,62 @@ def cfg5_run():
     sample = _sample(plens, L1)
     say("oracle sample:", sample)
     runner = _OracleRunner(w, sample, prompts, forced, plens, L1, eff_host)
-    caps = plens + new - 1
-    model = load_model(w, max_lanes=n, max_pos=512 + new, max_L=32, kv_arena_bytes=kv_bytes(spec, L1, caps),
-                       batch_invariant=1)
-    say("loaded; memory (weights, kv, workspace) =", tl.tl_memory_info(model))
-    res = {"sample": sample, "plens": plens, "L1": L1, "eff_host": eff_host, "oracle": runner,
-           "lockstep_first_diff": None, "agree": {}, "gaps": {}}
+    # a failure on the device stops the oracle thread too (queued lanes are dropped)
     try:
-        toks = torch.tensor(np.concatenate(prompts), dtype=torch.int32, device="cuda")
-        cu = np.concatenate([[0], np.cumsum(plens)]).astype(np.int32)
-        T = int(cu[-1])
-        lanes = np.arange(n, dtype=np.int32)
-        hid = torch.empty(T, spec.d_model, dtype=torch.float32, device="cuda")
-        nxt = torch.empty(n, dtype=torch.int32, device="cuda")
-        t0 = time.time()
-        tl.tl_forward(model, cu, toks, seq_L=L1, lanes=lanes, max_new_tokens=new - 1, out_hidden=hid, out_next=nxt)
-        torch.cuda.synchronize()
-        say("prefill of %d rows in %.2f s" % (T, time.time() - t0))
-        run_tok = torch.empty(n, new - 1, dtype=torch.int32, device="cuda")
-        run_h = torch.empty(n, new - 1, spec.d_model, dtype=torch.float32, device="cuda")
-        feed = torch.tensor(forced, dtype=torch.int32, device="cuda")
-        t0 = time.time()
-        eff = tl.tl_decode_run(model, lanes, draws[:, 1:], run_tok, in_tokens=feed, out_hidden=run_h, boundary_min=64)
-        torch.cuda.synchronize()
-        tl.tl_sync_errors(model)
-        t_cdb = time.time() - t0
-        say("continuous-depth decode of %d x %d tokens in %.2f s" % (n, new - 1, t_cdb))
-        res["eff"] = eff
-        res["H_pre"] = {i: hid[cu[i]:cu[i + 1]].cpu().numpy() for i in sample}
-        H_run = run_h.cpu().numpy()
-        T_run = run_tok.cpu().numpy()
-        res["H_run"], res["T_run"], res["T_pre"] = H_run, T_run, nxt.cpu().numpy()
-        # lockstep: the same lanes prefilled again, then one tl_decode_step per token
-        tl.tl_forward(model, cu, toks, seq_L=L1, lanes=lanes, max_new_tokens=new - 1)
-        torch.cuda.synchronize()
-        out = torch.empty(n, dtype=torch.int32, device="cuda")
-        hs = torch.empty(n, spec.d_model, dtype=torch.float32, device="cuda")
-        t0 = time.time()
-        dt_copy = 0.0
-        for t in range(new - 1):
-            e2 = tl.tl_decode_step(model, lanes, draws[:, 1 + t], out, in_tokens=feed[:, t].contiguous(), out_hidden=hs)
+        caps = plens + new - 1
+        model = load_model(w, max_lanes=n, max_pos=512 + new, max_L=32, kv_arena_bytes=kv_bytes(spec, L1, caps),
+                           batch_invariant=1)
+        say("loaded; memory (weights, kv, workspace) =", tl.tl_memory_info(model))
+        res = {"sample": sample, "plens": plens, "L1": L1, "eff_host": eff_host, "oracle": runner,
+               "lockstep_first_diff": None, "agree": {}, "gaps": {}}
+        try:
+            toks = torch.tensor(np.concatenate(prompts), dtype=torch.int32, device="cuda")
+            cu = np.concatenate([[0], np.cumsum(plens)]).astype(np.int32)
+            T = int(cu[-1])
+            lanes = np.arange(n, dtype=np.int32)
+            hid = torch.empty(T, spec.d_model, dtype=torch.float32, device="cuda")
+            nxt = torch.empty(n, dtype=torch.int32, device="cuda")
+            t0 = time.time()
+            tl.tl_forward(model, cu, toks, seq_L=L1, lanes=lanes, max_new_tokens=new - 1, out_hidden=hid, out_next=nxt)
             torch.cuda.synchronize()
-            t1 = time.time()
-            same = (np.array_equal(e2, eff[:, t]) and np.array_equal(out.cpu().numpy(), T_run[:, t])
-                    and np.array_equal(hs.cpu().numpy(), H_run[:, t]))
-            dt_copy += time.time() - t1
-            if not same:
-                res["lockstep_first_diff"] = t
-                break
-        say("lockstep decode %.2f s vs continuous-depth %.2f s" % (time.time() - t0 - dt_copy, t_cdb))
-    finally:
-        tl.tl_free(model)
+            say("prefill of %d rows in %.2f s" % (T, time.time() - t0))
+            run_tok = torch.empty(n, new - 1, dtype=torch.int32, device="cuda")
+            run_h = torch.empty(n, new - 1, spec.d_model, dtype=torch.float32, device="cuda")
+            feed = torch.tensor(forced, dtype=torch.int32, device="cuda")
+            t0 = time.time()
+            eff = tl.tl_decode_run(model, lanes, draws[:, 1:], run_tok, in_tokens=feed, out_hidden=run_h, boundary_min=64)
+            torch.cuda.synchronize()
+            tl.tl_sync_errors(model)
+            t_cdb = time.time() - t0
+            say("continuous-depth decode of %d x %d tokens in %.2f s" % (n, new - 1, t_cdb))
+            res["eff"] = eff
+            res["H_pre"] = {i: hid[cu[i]:cu[i + 1]].cpu().numpy() for i in sample}
+            H_run = run_h.cpu().numpy()
+            T_run = run_tok.cpu().numpy()
+            res["H_run"], res["T_run"], res["T_pre"] = H_run, T_run, nxt.cpu().numpy()
+            # lockstep: the same lanes prefilled again, then one tl_decode_step per token
+            tl.tl_forward(model, cu, toks, seq_L=L1, lanes=lanes, max_new_tokens=new - 1)
+            torch.cuda.synchronize()
+            out = torch.empty(n, dtype=torch.int32, device="cuda")
+            hs = torch.empty(n, spec.d_model, dtype=torch.float32, device="cuda")
+            t0 = time.time()
+            dt_copy = 0.0
+            for t in range(new - 1):
+                e2 = tl.tl_decode_step(model, lanes, draws[:, 1 + t], out, in_tokens=feed[:, t].contiguous(), out_hidden=hs)
+                torch.cuda.synchronize()
+                t1 = time.time()
+                same = (np.array_equal(e2, eff[:, t]) and np.array_equal(out.cpu().numpy(), T_run[:, t])
+                        and np.array_equal(hs.cpu().numpy(), H_run[:, t]))
+                dt_copy += time.time() - t1
+                if not same:
+                    res["lockstep_first_diff"] = t
+                    break
+            say("lockstep decode %.2f s vs continuous-depth %.2f s" % (time.time() - t0 - dt_copy, t_cdb))
+        finally:
+            tl.tl_free(model)
+    except BaseException:
+        runner.pool.shutdown(wait=False, cancel_futures=True)
+        raise
     yield res
     runner.pool.shutdown(cancel_futures=True)
 
