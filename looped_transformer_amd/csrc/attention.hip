@@ -15,6 +15,8 @@
 #include "device_common.h"
 #include "epilogue.h"
 
+#include <algorithm>
+
 namespace {
 
 template <class T> struct Row16;   // 16 bytes of a K/V row
@@ -33,10 +35,17 @@ template <> struct Row16<float> { typedef floatx4 type; };
 // (sums in split order, the same rotation and roundings), k and v stored into the
 // cache at the row's position, q kept in LDS; one kernel fewer per block on a
 // decode pass.
+//
+// Position split (nsplit > 1, grid y): workgroup (row, head, y) attends to the
+// y-th run of a row's position blocks and leaves its unnormalised (max, sum,
+// output) in part[((row H + head) nsplit + y)][dh + 2]; attn_merge_kernel then
+// combines the runs in order.  Every split forms q; only the split holding the
+// row's own position stores its k and v.
 template <class T, int LPK, int UD>
 __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q, const RowInfo* __restrict__ rows,
                                                        KVParams kv, T* __restrict__ out, int d, float scale,
-                                                       const int32_t* live, QkvParts qp) {
+                                                       const int32_t* live, QkvParts qp, int nsplit,
+                                                       float* __restrict__ part) {
   typedef typename Row16<T>::type R16;
   constexpr int EPL = 16 / (int)sizeof(T);   // elements per lane of a key row
   constexpr int KPI = 64 / LPK;              // keys per load instruction
@@ -72,7 +81,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   if (gate_closed(live)) return;
   T* op = out + (int64_t)r * d + h * dh;
   if (ri.done) {   // finished by early exit: carried only, its state no longer matters
-    if (tid < 64 && kin) {
+    if (blockIdx.y == 0 && tid < 64 && kin) {
       R16 z;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) z[e] = from_f32<T>(0.f);
@@ -82,6 +91,12 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   }
   const T* Kp = kv_ptr<T>(kv, ri, 0, h, 0);
   const T* Vp = kv_ptr<T>(kv, ri, 1, h, 0);
+  const int npos = ri.pos + 1;
+  const int nblk = (npos + P - 1) / P;
+  // this split's run of position blocks [b0, b1)
+  const int bs = (nblk + nsplit - 1) / nsplit;
+  const int b0 = min(nblk, (int)blockIdx.y * bs), b1 = min(nblk, b0 + bs);
+  const bool own_pos = b0 < b1 && b1 == nblk;   // the run holding the row's own position
   float qv[EPL];
   if (qp.part) {
     // after the rotation the pair's values go to p and p + dh/2 (q, k); V keeps
@@ -102,9 +117,11 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
         v1 += pr[G];
       }
       if (sec == 2) {
-        T* vp = kv_ptr<T>(kv, ri, 1, h, ri.pos);
-        vp[cd] = from_f32<T>(v0);
-        vp[cd + G] = from_f32<T>(v1);
+        if (own_pos) {
+          T* vp = kv_ptr<T>(kv, ri, 1, h, ri.pos);
+          vp[cd] = from_f32<T>(v0);
+          vp[cd + G] = from_f32<T>(v1);
+        }
       } else {
         const float cs = qp.rope_cos[(int64_t)ri.pos * half + p];
         const float sn = qp.rope_sin[(int64_t)ri.pos * half + p];
@@ -113,7 +130,7 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
         if (sec == 0) {
           qs[p] = (float)x1;
           qs[p + half] = (float)x2;
-        } else {
+        } else if (own_pos) {
           T* kp = kv_ptr<T>(kv, ri, 0, h, ri.pos);
           kp[p] = x1;
           kp[p + half] = x2;
@@ -128,12 +145,10 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
 #pragma unroll
     for (int e = 0; e < EPL; ++e) qv[e] = (float)qx[e] * scale;
   }
-  const int npos = ri.pos + 1;
-  const int nblk = (npos + P - 1) / P;
   float m = -INFINITY, l = 0.f, o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  for (int b = wv; b < nblk; b += 4) {
+  for (int b = b0 + wv; b < b1; b += 4) {
     const int t0 = b * P;
     R16 kr[U], vr[U];
 #pragma unroll
@@ -193,7 +208,29 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
   }
   __syncthreads();
   if (wv == 0 && g == 0 && kin) {
-    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));   // wave 0 always saw position 0
+    // wave 0 saw the run's first block: M = -inf only for an empty run of a split
+    const float M = fmaxf(fmaxf(wm[0], wm[1]), fmaxf(wm[2], wm[3]));
+    if (nsplit > 1) {
+      float* pp = part + ((int64_t)blockIdx.x * nsplit + blockIdx.y) * (dh + 2);
+      float f[4], L = 0.f;
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        f[w] = M == -INFINITY ? 0.f : expf(wm[w] - M);
+        L += wl[w] * f[w];
+      }
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) {
+        float acc = 0.f;
+#pragma unroll
+        for (int w = 0; w < 4; ++w) acc += wo[w][k * EPL + e] * f[w];
+        pp[2 + k * EPL + e] = acc;
+      }
+      if (k == 0) {
+        pp[0] = M;
+        pp[1] = L;
+      }
+      return;
+    }
     float f[4], L = 0.f;
 #pragma unroll
     for (int w = 0; w < 4; ++w) {
@@ -211,6 +248,31 @@ __global__ __launch_bounds__(256) void attn_rows_kernel(const T* __restrict__ q,
     }
     *reinterpret_cast<R16*>(op + k * EPL) = res;
   }
+}
+
+// The position-split runs of attn_rows_kernel combined, one workgroup per (row,
+// head), thread t < dh taking output dimension t: with M the largest run maximum,
+// out = sum_y O_y e^(m_y - M) / sum_y l_y e^(m_y - M), runs added in order (empty
+// runs, m = -inf, skipped).  Rows marked done keep the zero output already written.
+template <class T>
+__global__ __launch_bounds__(128) void attn_merge_kernel(const float* __restrict__ part, int nsplit, int H, int dh,
+                                                        const RowInfo* __restrict__ rows, T* __restrict__ out, int d,
+                                                        const int32_t* live) {
+  const int rh = blockIdx.x, r = rh / H, h = rh - r * H, t = threadIdx.x;
+  const RowInfo ri = rows[r];
+  if (gate_closed(live) || ri.done) return;
+  const float* pp = part + (int64_t)rh * nsplit * (dh + 2);
+  float M = -INFINITY;
+  for (int y = 0; y < nsplit; ++y) M = fmaxf(M, pp[y * (dh + 2)]);
+  float L = 0.f, acc = 0.f;
+  for (int y = 0; y < nsplit; ++y) {
+    const float my = pp[y * (dh + 2)];
+    if (my == -INFINITY) continue;
+    const float f = expf(my - M);
+    L += pp[y * (dh + 2) + 1] * f;
+    if (t < dh) acc += pp[y * (dh + 2) + 2 + t] * f;
+  }
+  if (t < dh) out[(int64_t)r * d + h * dh + t] = from_f32<T>(acc * (1.0f / L));
 }
 
 // ----------------------------------------------------------------------------
@@ -723,37 +785,53 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
   return hipErrorInvalidValue;
 }
 
+// Few (row, head) workgroups and long contexts: the positions are split over up to
+// kAttnMaxSplit workgroups per (row, head), as many as keep the launch within
+// kAttnSplitWGs workgroups, and merged by attn_merge_kernel.  max_ctx = 0 (unknown,
+// or batch-invariant passes) never splits.
+constexpr int kAttnSplitWGs = 256;
+constexpr int kAttnMaxSplit = 16;
+
 template <class T, int LPK>
 void attn_rows_launch(const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out, const int32_t* live,
-                      int max_ctx, hipStream_t s, const QkvParts& qp) {
+                      int max_ctx, hipStream_t s, const QkvParts& qp, float* part) {
   const int d = kv.H * kv.dh;
   const float scale = 1.0f / sqrtf((float)kv.dh);
   constexpr int P = (64 / LPK) * (LPK < 16 ? LPK : 16);   // positions of a full block
-  if (max_ctx > 0 && max_ctx <= P)
-    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 4>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
-                       d, scale, live, qp);
-  else if (max_ctx > 0 && max_ctx <= 2 * P)
-    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 2>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
-                       d, scale, live, qp);
+  const int wgs = n * kv.H;
+  int ns = 1;
+  if (part && max_ctx > 4 * P && wgs < kAttnSplitWGs)
+    ns = std::min(std::min(kAttnSplitWGs / wgs, (max_ctx + P - 1) / P), kAttnMaxSplit);
+  const int ctx = (max_ctx + ns - 1) / ns;   // positions per run, at most
+  const dim3 grid(wgs, ns);
+  if (max_ctx > 0 && ctx <= P)
+    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 4>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+                       d, scale, live, qp, ns, part);
+  else if (max_ctx > 0 && ctx <= 2 * P)
+    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 2>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+                       d, scale, live, qp, ns, part);
   else
-    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 1>), dim3(n * kv.H), dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
-                       d, scale, live, qp);
+    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 1>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+                       d, scale, live, qp, ns, part);
+  if (ns > 1)
+    hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(wgs), dim3(128), 0, s, (const float*)part, ns, kv.H, kv.dh, rows,
+                       (T*)out, d, live);
 }
 
 template <class T>
 hipError_t attn_rows_dispatch(const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
-                              const int32_t* live, int max_ctx, hipStream_t s, const QkvParts& qp) {
+                              const int32_t* live, int max_ctx, hipStream_t s, const QkvParts& qp, float* part) {
   const int chunks = kv.dh * (int)sizeof(T) / 16;   // 16-byte chunks of a row (head_dim is checked at load)
-  if (chunks <= 4) attn_rows_launch<T, 4>(q, rows, n, kv, out, live, max_ctx, s, qp);
-  else if (chunks <= 8) attn_rows_launch<T, 8>(q, rows, n, kv, out, live, max_ctx, s, qp);
-  else if (chunks <= 16) attn_rows_launch<T, 16>(q, rows, n, kv, out, live, max_ctx, s, qp);
-  else if (chunks <= 32) attn_rows_launch<T, 32>(q, rows, n, kv, out, live, max_ctx, s, qp);
+  if (chunks <= 4) attn_rows_launch<T, 4>(q, rows, n, kv, out, live, max_ctx, s, qp, part);
+  else if (chunks <= 8) attn_rows_launch<T, 8>(q, rows, n, kv, out, live, max_ctx, s, qp, part);
+  else if (chunks <= 16) attn_rows_launch<T, 16>(q, rows, n, kv, out, live, max_ctx, s, qp, part);
+  else if (chunks <= 32) attn_rows_launch<T, 32>(q, rows, n, kv, out, live, max_ctx, s, qp, part);
   else return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv, void* out,
-                            const int32_t* live, int max_ctx, hipStream_t s, const QkvParts* qp) {
+                            const int32_t* live, int max_ctx, hipStream_t s, const QkvParts* qp, float* part) {
   if (n <= 0) return hipSuccess;
   if (kv.dh > 128 || (kv.dh * 4) % 16 != 0) return hipErrorInvalidValue;
   QkvParts p{};
@@ -766,9 +844,9 @@ hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n
     p = *qp;
   }
   switch (dtype) {
-    case DT_F32: return attn_rows_dispatch<float>(q, rows, n, kv, out, live, max_ctx, s, p);
-    case DT_F16: return attn_rows_dispatch<f16>(q, rows, n, kv, out, live, max_ctx, s, p);
-    case DT_BF16: return attn_rows_dispatch<bf16>(q, rows, n, kv, out, live, max_ctx, s, p);
+    case DT_F32: return attn_rows_dispatch<float>(q, rows, n, kv, out, live, max_ctx, s, p, part);
+    case DT_F16: return attn_rows_dispatch<f16>(q, rows, n, kv, out, live, max_ctx, s, p, part);
+    case DT_BF16: return attn_rows_dispatch<bf16>(q, rows, n, kv, out, live, max_ctx, s, p, part);
     default: return hipErrorInvalidValue;
   }
 }

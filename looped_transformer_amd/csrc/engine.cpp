@@ -221,7 +221,7 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
   if (m->has_last_stream && m->last_stream != s) HIPCHK(hipStreamSynchronize(m->last_stream));
   drop_graphs(m);
   void* olds[] = {w.hA, w.hB, w.hX, w.hE, w.x16, w.x16b, w.q16, w.o16, w.u16, w.xh, w.rowsA, w.rowsB,
-                  w.dest, w.count, w.tok, w.tok2, w.part_v, w.part_i, w.part_v2, w.kv_scratch, w.splitk};
+                  w.dest, w.count, w.tok, w.tok2, w.part_v, w.part_i, w.part_v2, w.kv_scratch, w.splitk, w.attn_part};
   for (void* p : olds) dev_free(m, p);
   w = tl::Workspace{};
   m->ws_bytes = 0;
@@ -242,6 +242,7 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
       {(void**)&w.part_v2, (size_t)std::max(O, 1) * tiles * 4},
       {&w.kv_scratch, (size_t)std::max<int64_t>(KS, 1) * m->esz},
       {(void**)&w.splitk, (size_t)kSplitFloats * 4},
+      {(void**)&w.attn_part, (size_t)kAttnPartFloats * 4},
   };
   for (auto& r : reqs) {
     *r.p = dev_alloc(m, r.bytes);
@@ -416,7 +417,7 @@ tl_status run_block(tl_model* m, int b, float* h, const RowInfo* rows, int n, co
   }
   if (tiles) TIMED(TL_T_ATTENTION, HIPCHK(launch_attention_tiled(m->act, w.q16, tiles, n_tiles, akv, w.o16, s, grid)));
   else TIMED(TL_T_ATTENTION, HIPCHK(launch_attention(m->act, w.q16, rows, n, akv, w.o16, m->gate_live,
-                                                     m->invariant ? 0 : m->ctx_hint, s, &qp)));
+                                                     m->invariant ? 0 : m->ctx_hint, s, &qp, w.attn_part)));
   GemmEpi r{};
   r.kind = EPI_RESID;
   r.h = h;
@@ -1878,6 +1879,7 @@ size_t noalloc_layout(const tl_model* m, int n, size_t stage_bytes, uint8_t* bas
   x.part_i = static_cast<int32_t*>(take(R * tiles * 4));
   x.part_v2 = static_cast<float*>(take(R * tiles * 4));
   x.splitk = static_cast<float*>(take(split_floats * 4));
+  x.attn_part = static_cast<float*>(take((size_t)kAttnPartFloats * 4));
   x.kv_scratch = nullptr;
   x.kv_scratch_elems = 0;
   x.rows = (int)R;

@@ -85,6 +85,7 @@ struct Workspace {
   void* kv_scratch = nullptr;
   int part_tiles = 0;
   float* splitk = nullptr;          // split-K partial tiles
+  float* attn_part = nullptr;       // kAttnPartFloats: decode attention split over positions
 };
 
 }  // namespace tl

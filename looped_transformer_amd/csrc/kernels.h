@@ -120,9 +120,12 @@ struct QkvParts {
 // live: as GemmArgs::live (NULL: always run).  Rows marked done get a zero output.
 // max_ctx: an upper bound on pos + 1 over the rows (0: unknown), which picks
 // the block size.  qp: see QkvParts (NULL or qp->part NULL: q from `q`).
+// part: kAttnPartFloats floats of scratch for splitting long contexts over several
+// workgroups per (row, head) when there are few of them (NULL: never split).
+constexpr int kAttnPartFloats = 256 * (128 + 2);
 hipError_t launch_attention(int dtype, const void* q, const RowInfo* rows, int n, const KVParams& kv,
                             void* out, const int32_t* live, int max_ctx, hipStream_t s,
-                            const QkvParts* qp = nullptr);
+                            const QkvParts* qp = nullptr, float* part = nullptr);
 // A run of up to attn_tile_rows() consecutive rows of one sequence (positions pos0 .. pos0+nrows-1)
 // that attend to positions 0 .. pos0+nrows-1 of their lane's slot.  cap > 0: the lane's slot-0
 // offset (koff) and capacity are carried here, so the kernel need not read the lane tables;
