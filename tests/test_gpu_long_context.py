@@ -158,3 +158,32 @@ def test_long_prefix_fork_append_decode(weights):
             _check_tokens(out.cpu().numpy(), np.stack([x[1] for x in refs]), "decode step %d" % t)
     finally:
         tl.tl_free(model)
+
+
+def test_long_prompt_batch1_decode(weights):
+    """One lane after a 520-token prompt: with only 16 (row, head) workgroups the
+    decode attention splits each row's positions over nine of them per head
+    (quarter-size blocks), and a merge kernel combines the runs."""
+    w, m = weights
+    P, L = PLENS[0], LS[0]
+    prompt = synth.tokens(7, 7400, P, SPEC.vocab)
+    feed = synth.tokens(7, 7500, 4, SPEC.vocab)
+    model = load_model(w, max_lanes=1, max_pos=640, max_L=8, kv_arena_bytes=kv_bytes(SPEC, [L], [P + NEW]))
+    try:
+        tl.tl_forward(model, np.array([0, P], dtype=np.int32), _dev(prompt), seq_L=[L], lanes=[0],
+                      max_new_tokens=NEW)
+        torch.cuda.synchronize()
+        ln, _, _ = oracle.prefill(m, prompt, L)
+        out = torch.empty(1, dtype=torch.int32, device="cuda")
+        hs = torch.empty(1, SPEC.d_model, dtype=torch.float32, device="cuda")
+        lg = torch.empty(1, SPEC.vocab, dtype=torch.float32, device="cuda")
+        for t in range(4):
+            tl.tl_decode_step(model, [0], [L], out, in_tokens=_dev(feed[t:t + 1]), out_logits=lg, out_hidden=hs)
+            torch.cuda.synchronize()
+            h_o, l_o, _, _ = oracle.decode_step(m, ln, L, token=int(feed[t]))
+            r, rl = rel_l2(hs.cpu().numpy()[0], h_o), rel_l2(lg.cpu().numpy()[0], l_o)
+            say("batch-1 step", t, "ctx", P + t + 1, "hidden %.2e logits %.2e" % (r, rl))
+            assert r <= 1e-2 and rl <= 1e-2, (t, r, rl)
+            _check_tokens(out.cpu().numpy(), l_o[None, :], "batch-1 step %d" % t)
+    finally:
+        tl.tl_free(model)
