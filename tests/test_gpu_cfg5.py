@@ -209,7 +209,7 @@ def test_cfg5_oracle_lanes(cfg5_run, group):
 
 def test_cfg5_top1_agreement(cfg5_run):
     """At least 99 % of the sampled lanes' greedy tokens agree with the oracle's
-    (the benchmark spec's bar), over at least 1000 tokens."""
+    over at least 1000 tokens: the bar for the greedy token stream."""
     r = cfg5_run
     assert sorted(r["agree"]) == sorted(r["sample"]), "some oracle lanes were not checked"
     agree = sum(a for a, _ in r["agree"].values())
