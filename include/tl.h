@@ -401,6 +401,18 @@ tl_status tl_sync_errors(tl_model* m, void* stream);
 #define TL_TIMING_CLASSES 14
 tl_status tl_timing_enable(tl_model* m, int32_t on);
 tl_status tl_timing_read(tl_model* m, double* total_ms, int64_t* launches);
+/* Measurement: the kernels' own durations behind the same classes.  While timing
+ * is on, every launch of a product kernel (the QKV, O, gate/up, down and head
+ * products, and their split-K reduction kernels) hands the runtime a further
+ * event pair that the runtime stamps with that kernel's start and end, so these
+ * sums leave out the dispatch and event overhead held in tl_timing_read's
+ * figures.  Writes, per class (arrays of TL_TIMING_CLASSES), the summed kernel
+ * milliseconds and the number of kernels, and resets the sums.  Classes whose
+ * kernels are not products (attention, rmsnorm, compact, embed) read 0.
+ * Errors: TL_E_ARG (NULL pointer), TL_E_HIP (a recorded event failed, or some
+ * product launches went untimed because no event could be created; the sums
+ * then miss them). */
+tl_status tl_timing_read_kernels(tl_model* m, double* kernel_ms, int64_t* kernels);
 
 /* Waits for the model's own device work, frees everything the model holds. */
 void tl_free(tl_model* m);

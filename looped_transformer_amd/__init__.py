@@ -90,6 +90,7 @@ def lib():
         "tl_sync_errors": [_P, _P],
         "tl_timing_enable": [_P, _I],
         "tl_timing_read": [_P, _P, _P],
+        "tl_timing_read_kernels": [_P, _P, _P],
     }
     for name, args in sig.items():
         f = getattr(L, name)
@@ -330,6 +331,15 @@ def tl_timing_read(model):
     ms = np.zeros(len(TIMING_CLASSES), np.float64)
     n = np.zeros(len(TIMING_CLASSES), np.int64)
     _check(lib().tl_timing_read(model.handle, _ptr(ms), _ptr(n)))
+    return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(TIMING_CLASSES)}
+
+
+def tl_timing_read_kernels(model):
+    """{class name: (summed kernel ms, kernels)} since the last read: the product
+    kernels' own durations, stamped by the runtime."""
+    ms = np.zeros(len(TIMING_CLASSES), np.float64)
+    n = np.zeros(len(TIMING_CLASSES), np.int64)
+    _check(lib().tl_timing_read_kernels(model.handle, _ptr(ms), _ptr(n)))
     return {k: (float(ms[i]), int(n[i])) for i, k in enumerate(TIMING_CLASSES)}
 
 

@@ -264,30 +264,57 @@ tl_status ensure_ws(tl_model* m, int rows, int outs, int64_t kv_scratch, hipStre
 tl_status flush_timing(tl_model* m) {
   if (m->ev_used == 0) return TL_OK;
   HIPCHK(hipEventSynchronize(m->ev_pool[m->ev_used - 1]));
-  for (size_t i = 0; i < m->ev_class.size(); ++i) {
+  for (const TimedSpan& sp : m->ev_spans) {
     float ms = 0.f;
-    HIPCHK(hipEventElapsedTime(&ms, m->ev_pool[2 * i], m->ev_pool[2 * i + 1]));
-    m->t_ms[m->ev_class[i]] += ms;
-    m->t_n[m->ev_class[i]] += 1;
+    HIPCHK(hipEventElapsedTime(&ms, m->ev_pool[sp.ev], m->ev_pool[sp.ev + 1]));
+    m->t_ms[sp.cls] += ms;
+    m->t_n[sp.cls] += 1;
+    for (size_t k = sp.k0; k < sp.k1; k += 2) {
+      HIPCHK(hipEventElapsedTime(&ms, m->kev_pool[k], m->kev_pool[k + 1]));
+      m->tk_ms[sp.cls] += ms;
+      m->tk_n[sp.cls] += 1;
+    }
   }
   m->ev_used = 0;
-  m->ev_class.clear();
+  m->kev_used = 0;
+  m->ev_spans.clear();
   return TL_OK;
 }
 
-tl_status tbegin(tl_model* m, hipStream_t s) {
-  if (!m->timing) return TL_OK;
-  if (m->ev_used + 2 > m->ev_pool.size()) {
-    if (m->ev_pool.size() >= 16384) {
-      TRY(flush_timing(m));
-    } else {
-      for (int i = 0; i < 512; ++i) {
-        hipEvent_t e;
-        HIPCHK(hipEventCreate(&e));
-        m->ev_pool.push_back(e);
+}  // namespace
+
+bool ModelKernelTimer::take(hipEvent_t* start, hipEvent_t* stop) {
+  if (m->kev_used + 2 > m->kev_pool.size()) {
+    for (int i = 0; i < 256; ++i) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) {
+        m->kev_short = true;
+        return false;
       }
+      m->kev_pool.push_back(e);
     }
   }
+  *start = m->kev_pool[m->kev_used++];
+  *stop = m->kev_pool[m->kev_used++];
+  return true;
+}
+
+namespace {
+
+tl_status tbegin(tl_model* m, hipStream_t s) {
+  if (!m->timing) return TL_OK;
+  // no span is open here: a full pool is emptied by reading what it holds
+  if ((m->ev_used + 2 > m->ev_pool.size() && m->ev_pool.size() >= 16384) || m->kev_used >= 16384)
+    TRY(flush_timing(m));
+  if (m->ev_used + 2 > m->ev_pool.size()) {
+    for (int i = 0; i < 512; ++i) {
+      hipEvent_t e;
+      HIPCHK(hipEventCreate(&e));
+      m->ev_pool.push_back(e);
+    }
+  }
+  m->span_ev = m->ev_used;
+  m->span_k = m->kev_used;
   HIPCHK(hipEventRecord(m->ev_pool[m->ev_used++], s));
   return TL_OK;
 }
@@ -295,15 +322,35 @@ tl_status tbegin(tl_model* m, hipStream_t s) {
 tl_status tend(tl_model* m, int cls, hipStream_t s) {
   if (!m->timing) return TL_OK;
   HIPCHK(hipEventRecord(m->ev_pool[m->ev_used++], s));
-  m->ev_class.push_back(cls);
+  m->ev_spans.push_back(TimedSpan{cls, m->span_ev, m->span_k, m->kev_used});
   return TL_OK;
 }
 
-#define TIMED(cls, stmt)      \
-  do {                        \
-    TRY(tbegin(m, s));        \
-    stmt;                     \
-    TRY(tend(m, (cls), s));   \
+// Installs the model's kernel timer on this thread for the launches of one timed
+// group, and takes it down however the group ends.
+struct TimerScope {
+  explicit TimerScope(tl_model* m) : on(m->timing) {
+    if (on) {
+      m->ktimer.m = m;
+      set_kernel_timer(&m->ktimer);
+    }
+  }
+  ~TimerScope() {
+    if (on) set_kernel_timer(nullptr);
+  }
+  TimerScope(const TimerScope&) = delete;
+  TimerScope& operator=(const TimerScope&) = delete;
+  bool on;
+};
+
+#define TIMED(cls, stmt)            \
+  do {                              \
+    TRY(tbegin(m, s));              \
+    {                               \
+      TimerScope tl_ts_(m);         \
+      stmt;                         \
+    }                               \
+    TRY(tend(m, (cls), s));         \
   } while (0)
 
 // ----------------------------------------------------------------- passes
@@ -785,7 +832,10 @@ tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out
   e.part_idx = w.part_i;
   e.n_tiles = tiles;
   e.part_val2 = margin ? w.part_v2 : nullptr;
-  HIPCHK(launch_gemm(m->gdt, g, e, s));
+  {
+    TimerScope ts(m);
+    HIPCHK(launch_gemm(m->gdt, g, e, s));
+  }
   if (out_tok || pend_lanes || margin)
     HIPCHK(launch_argmax_reduce(w.part_v, w.part_i, e.part_val2, n_out, tiles, out_tok,
                                 pend_lanes ? m->d_pending : nullptr, pend_lanes, margin, s));
@@ -1173,6 +1223,7 @@ void tl_free(tl_model* m) {
   if (m->handover) (void)hipEventDestroy(m->handover);
   if (m->aux_host) (void)hipHostFree(m->aux_host);
   for (hipEvent_t e : m->ev_pool) (void)hipEventDestroy(e);
+  for (hipEvent_t e : m->kev_pool) (void)hipEventDestroy(e);
   delete m;
 }
 
@@ -2090,6 +2141,22 @@ tl_status tl_timing_read(tl_model* m, double* total_ms, int64_t* launches) {
     m->t_ms[i] = 0.0;
     m->t_n[i] = 0;
   }
+  return TL_OK;
+}
+
+tl_status tl_timing_read_kernels(tl_model* m, double* kernel_ms, int64_t* kernels) {
+  g_err.clear();
+  if (!m || !kernel_ms || !kernels) return fail(TL_E_ARG, "NULL argument");
+  TRY(flush_timing(m));
+  for (int i = 0; i < TL_TIMING_CLASSES; ++i) {
+    kernel_ms[i] = m->tk_ms[i];
+    kernels[i] = m->tk_n[i];
+    m->tk_ms[i] = 0.0;
+    m->tk_n[i] = 0;
+  }
+  const bool short_ = m->kev_short;
+  m->kev_short = false;
+  if (short_) return fail(TL_E_HIP, "some product launches went untimed: no event could be created");
   return TL_OK;
 }
 

@@ -90,6 +90,19 @@ struct Workspace {
 
 }  // namespace tl
 
+// A timed launch group: its class, its (start, stop) pair in ev_pool at ev, and
+// the kernel-stamped pairs its product launches took, kev_pool[k0, k1).
+struct TimedSpan {
+  int cls;
+  size_t ev, k0, k1;
+};
+
+struct tl_model;
+struct ModelKernelTimer final : KernelTimer {
+  tl_model* m = nullptr;
+  bool take(hipEvent_t* start, hipEvent_t* stop) override;
+};
+
 struct tl_model {
   tl_config cfg{};
   int device = 0;            // HIP device the model was loaded on
@@ -171,7 +184,14 @@ struct tl_model {
   bool timing = false;
   std::vector<hipEvent_t> ev_pool;
   size_t ev_used = 0;
-  std::vector<int> ev_class;           // class of each recorded (start, stop) pair
+  std::vector<TimedSpan> ev_spans;     // one per timed launch group, in record order
+  std::vector<hipEvent_t> kev_pool;    // (start, stop) pairs the product launches stamp
+  size_t kev_used = 0;
+  size_t span_ev = 0, span_k = 0;      // where the open span's events start
+  bool kev_short = false;              // a product launch went untimed (no pair to give)
+  ModelKernelTimer ktimer;
   double t_ms[TL_TIMING_CLASSES] = {};
   int64_t t_n[TL_TIMING_CLASSES] = {};
+  double tk_ms[TL_TIMING_CLASSES] = {};
+  int64_t tk_n[TL_TIMING_CLASSES] = {};
 };

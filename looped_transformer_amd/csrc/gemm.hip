@@ -16,6 +16,7 @@
 //   STORE  : fp32 store.
 #include "device_common.h"
 #include "epilogue.h"
+#include "launch.h"
 
 #include <algorithm>
 #include <type_traits>
@@ -1334,13 +1335,13 @@ hipError_t finish_splits(const GemmArgs& g, const GemmEpi& e, int splits, hipStr
   if (e.kind == EPI_RESID && e.norm_g && (g.N % 4) == 0 && (e.ldh % 4) == 0 && vpt <= 6) {
 #define TL_RN(VPT_)                                                                                                \
   switch (splits) {                                                                                               \
-    case 2: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 2>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 3: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 3>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 4: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 4>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 5: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 5>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 6: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 6>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    case 8: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 8>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
-    default: hipLaunchKernelGGL((splitk_resid_norm_kernel<XT, VPT_, 0>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 2: TL_LAUNCH((splitk_resid_norm_kernel<XT, VPT_, 2>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 3: TL_LAUNCH((splitk_resid_norm_kernel<XT, VPT_, 3>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 4: TL_LAUNCH((splitk_resid_norm_kernel<XT, VPT_, 4>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 5: TL_LAUNCH((splitk_resid_norm_kernel<XT, VPT_, 5>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 6: TL_LAUNCH((splitk_resid_norm_kernel<XT, VPT_, 6>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    case 8: TL_LAUNCH((splitk_resid_norm_kernel<XT, VPT_, 8>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
+    default: TL_LAUNCH((splitk_resid_norm_kernel<XT, VPT_, 0>), dim3(g.M), dim3(256), 0, s, g, e, splits); break; \
   }
     if (vpt <= 2) { TL_RN(2) }
     else { TL_RN(6) }
@@ -1352,10 +1353,10 @@ hipError_t finish_splits(const GemmArgs& g, const GemmEpi& e, int splits, hipStr
   const int64_t items = (int64_t)g.M * (pr ? g.N / 2 : g.N);
   dim3 rg((unsigned)((items + 255) / 256));
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((splitk_epilogue_kernel<XT, EPI_QKV>), rg, dim3(256), 0, s, g, e, splits); break;
-    case EPI_RESID: hipLaunchKernelGGL((splitk_epilogue_kernel<XT, EPI_RESID>), rg, dim3(256), 0, s, g, e, splits); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((splitk_epilogue_kernel<XT, EPI_SWIGLU>), rg, dim3(256), 0, s, g, e, splits); break;
-    case EPI_STORE: hipLaunchKernelGGL((splitk_epilogue_kernel<XT, EPI_STORE>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_QKV: TL_LAUNCH((splitk_epilogue_kernel<XT, EPI_QKV>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_RESID: TL_LAUNCH((splitk_epilogue_kernel<XT, EPI_RESID>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_SWIGLU: TL_LAUNCH((splitk_epilogue_kernel<XT, EPI_SWIGLU>), rg, dim3(256), 0, s, g, e, splits); break;
+    case EPI_STORE: TL_LAUNCH((splitk_epilogue_kernel<XT, EPI_STORE>), rg, dim3(256), 0, s, g, e, splits); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -1365,11 +1366,11 @@ template <class AT, class XT, bool W4, int BM, int BN, int BK, int D>
 hipError_t launch_mfma_t(const GemmArgs& g, const GemmEpi& e, const TileCfg& t, hipStream_t s, bool* norm_done) {
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, t.splits);
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_HEAD: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_HEAD>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_STORE: hipLaunchKernelGGL((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_QKV: TL_LAUNCH((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_RESID: TL_LAUNCH((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_SWIGLU: TL_LAUNCH((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_HEAD: TL_LAUNCH((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_HEAD>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_STORE: TL_LAUNCH((gemm_mfma_kernel<AT, XT, W4, BM, BN, BK, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
     default: return hipErrorInvalidValue;
   }
   if (t.splits > 1) return finish_splits<XT>(g, e, t.splits, s, norm_done);
@@ -1441,10 +1442,10 @@ hipError_t launch_skinny_t(const GemmArgs& g, const GemmEpi& e, const SkinnyCfg&
   constexpr int BN = 4 * 32 * WNB;
   dim3 grid((g.N + BN - 1) / BN, (g.M + BM - 1) / BM, t.splits);
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((gemm_skinny_w4_kernel<BM, WNB, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_skinny_w4_kernel<BM, WNB, D, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_skinny_w4_kernel<BM, WNB, D, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
-    case EPI_STORE: hipLaunchKernelGGL((gemm_skinny_w4_kernel<BM, WNB, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_QKV: TL_LAUNCH((gemm_skinny_w4_kernel<BM, WNB, D, EPI_QKV>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_RESID: TL_LAUNCH((gemm_skinny_w4_kernel<BM, WNB, D, EPI_RESID>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_SWIGLU: TL_LAUNCH((gemm_skinny_w4_kernel<BM, WNB, D, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
+    case EPI_STORE: TL_LAUNCH((gemm_skinny_w4_kernel<BM, WNB, D, EPI_STORE>), grid, dim3(256), 0, s, g, e, t.kchunk); break;
     default: return hipErrorInvalidValue;
   }
   if (t.splits > 1) return finish_splits<f16>(g, e, t.splits, s, norm_done);
@@ -1477,9 +1478,9 @@ bool w4_rows_launch(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool* no
   if (g.N >= 8192) {
     dim3 grid((g.N + 127) / 128, (g.M + 63) / 64, 1);
     switch (e.kind) {
-      case EPI_SWIGLU: hipLaunchKernelGGL((gemm_w4_pair_kernel<EPI_SWIGLU>), grid, dim3(512), 0, s, g, e, g.K); break;
-      case EPI_RESID: hipLaunchKernelGGL((gemm_w4_pair_kernel<EPI_RESID>), grid, dim3(512), 0, s, g, e, g.K); break;
-      default: hipLaunchKernelGGL((gemm_w4_pair_kernel<EPI_STORE>), grid, dim3(512), 0, s, g, e, g.K); break;
+      case EPI_SWIGLU: TL_LAUNCH((gemm_w4_pair_kernel<EPI_SWIGLU>), grid, dim3(512), 0, s, g, e, g.K); break;
+      case EPI_RESID: TL_LAUNCH((gemm_w4_pair_kernel<EPI_RESID>), grid, dim3(512), 0, s, g, e, g.K); break;
+      default: TL_LAUNCH((gemm_w4_pair_kernel<EPI_STORE>), grid, dim3(512), 0, s, g, e, g.K); break;
     }
     *err = hipGetLastError();
     return true;
@@ -1490,15 +1491,22 @@ bool w4_rows_launch(const GemmArgs& g, const GemmEpi& e, hipStream_t s, bool* no
   const int sp = (units + per - 1) / per;
   dim3 grid((g.N + 63) / 64, (g.M + 63) / 64, sp);
   switch (e.kind) {
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_w4_rows_kernel<2, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, per * 128); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemm_w4_rows_kernel<2, EPI_RESID>), grid, dim3(256), 0, s, g, e, per * 128); break;
-    default: hipLaunchKernelGGL((gemm_w4_rows_kernel<2, EPI_STORE>), grid, dim3(256), 0, s, g, e, per * 128); break;
+    case EPI_SWIGLU: TL_LAUNCH((gemm_w4_rows_kernel<2, EPI_SWIGLU>), grid, dim3(256), 0, s, g, e, per * 128); break;
+    case EPI_RESID: TL_LAUNCH((gemm_w4_rows_kernel<2, EPI_RESID>), grid, dim3(256), 0, s, g, e, per * 128); break;
+    default: TL_LAUNCH((gemm_w4_rows_kernel<2, EPI_STORE>), grid, dim3(256), 0, s, g, e, per * 128); break;
   }
   *err = sp > 1 ? finish_splits<f16>(g, e, sp, s, norm_done) : hipGetLastError();
   return true;
 }
 
 }  // namespace
+
+namespace {
+thread_local KernelTimer* t_kernel_timer = nullptr;
+}  // namespace
+
+void set_kernel_timer(KernelTimer* t) { t_kernel_timer = t; }
+KernelTimer* kernel_timer() { return t_kernel_timer; }
 
 int gemm_head_tiles(int act_dtype, int M, int N) {
   GemmArgs g{};
@@ -1572,11 +1580,11 @@ static hipError_t launch_gemm_core(int act_dtype, const GemmArgs& g, const GemmE
   if (act_dtype == DT_F32) {
     dim3 grid((g.N + 63) / 64, (g.M + 63) / 64);
     switch (e.kind) {
-      case EPI_QKV: hipLaunchKernelGGL(gemm_f32_kernel<EPI_QKV>, grid, dim3(256), 0, s, g, e); break;
-      case EPI_RESID: hipLaunchKernelGGL(gemm_f32_kernel<EPI_RESID>, grid, dim3(256), 0, s, g, e); break;
-      case EPI_SWIGLU: hipLaunchKernelGGL(gemm_f32_kernel<EPI_SWIGLU>, grid, dim3(256), 0, s, g, e); break;
-      case EPI_HEAD: hipLaunchKernelGGL(gemm_f32_kernel<EPI_HEAD>, grid, dim3(256), 0, s, g, e); break;
-      case EPI_STORE: hipLaunchKernelGGL(gemm_f32_kernel<EPI_STORE>, grid, dim3(256), 0, s, g, e); break;
+      case EPI_QKV: TL_LAUNCH(gemm_f32_kernel<EPI_QKV>, grid, dim3(256), 0, s, g, e); break;
+      case EPI_RESID: TL_LAUNCH(gemm_f32_kernel<EPI_RESID>, grid, dim3(256), 0, s, g, e); break;
+      case EPI_SWIGLU: TL_LAUNCH(gemm_f32_kernel<EPI_SWIGLU>, grid, dim3(256), 0, s, g, e); break;
+      case EPI_HEAD: TL_LAUNCH(gemm_f32_kernel<EPI_HEAD>, grid, dim3(256), 0, s, g, e); break;
+      case EPI_STORE: TL_LAUNCH(gemm_f32_kernel<EPI_STORE>, grid, dim3(256), 0, s, g, e); break;
       default: return hipErrorInvalidValue;
     }
     return hipGetLastError();

@@ -17,6 +17,7 @@
 // as it is staged (the RMSNorm then needs no kernel of its own at these sizes).
 #include "device_common.h"
 #include "epilogue.h"
+#include "launch.h"
 
 namespace {
 
@@ -349,9 +350,9 @@ hipError_t gemv_f16_launch(const GemmArgs& g, const GemmEpi& e, hipStream_t s) {
   // paired epilogues: 32 rows per workgroup, two waves per row group; residual:
   // 8 rows per workgroup, four waves per row group (four times the workgroups)
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((gemv_f16_kernel<M, 8, 2, EPI_QKV>), dim3(g.N / 32), dim3(512), lds, s, g, e); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemv_f16_kernel<M, 8, 2, EPI_SWIGLU>), dim3(g.N / 32), dim3(512), lds, s, g, e); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemv_f16_kernel<M, 4, 4, EPI_RESID>), dim3(g.N / 8), dim3(256), lds, s, g, e); break;
+    case EPI_QKV: TL_LAUNCH((gemv_f16_kernel<M, 8, 2, EPI_QKV>), dim3(g.N / 32), dim3(512), lds, s, g, e); break;
+    case EPI_SWIGLU: TL_LAUNCH((gemv_f16_kernel<M, 8, 2, EPI_SWIGLU>), dim3(g.N / 32), dim3(512), lds, s, g, e); break;
+    case EPI_RESID: TL_LAUNCH((gemv_f16_kernel<M, 4, 4, EPI_RESID>), dim3(g.N / 8), dim3(256), lds, s, g, e); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -362,9 +363,9 @@ hipError_t gemv_launch_kind(const GemmArgs& g, const GemmEpi& e, hipStream_t s) 
   const dim3 grid(g.N / 32);
   const size_t lds = (size_t)M * g.K * sizeof(f16);
   switch (e.kind) {
-    case EPI_QKV: hipLaunchKernelGGL((gemv_w4_kernel<M, NW, EPI_QKV>), grid, dim3(NW * 64), lds, s, g, e); break;
-    case EPI_RESID: hipLaunchKernelGGL((gemv_w4_kernel<M, NW, EPI_RESID>), grid, dim3(NW * 64), lds, s, g, e); break;
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemv_w4_kernel<M, NW, EPI_SWIGLU>), grid, dim3(NW * 64), lds, s, g, e); break;
+    case EPI_QKV: TL_LAUNCH((gemv_w4_kernel<M, NW, EPI_QKV>), grid, dim3(NW * 64), lds, s, g, e); break;
+    case EPI_RESID: TL_LAUNCH((gemv_w4_kernel<M, NW, EPI_RESID>), grid, dim3(NW * 64), lds, s, g, e); break;
+    case EPI_SWIGLU: TL_LAUNCH((gemv_w4_kernel<M, NW, EPI_SWIGLU>), grid, dim3(NW * 64), lds, s, g, e); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();

@@ -253,3 +253,19 @@ hipError_t launch_w4_export(const uint32_t* words, const uint16_t* scales, const
 constexpr size_t kNoAllocScratchBytes = 64ull << 20;
 hipError_t noalloc_scratch_init(int device);
 void* noalloc_scratch(int device);
+
+// Kernel-duration timing of the product launchers (measurement only).  While a
+// timer is installed on the calling thread, each launch in gemm.hip and gemv.hip
+// takes a fresh (start, stop) event pair from it and has the runtime stamp the
+// kernel's own start and end into the pair (hipExtLaunchKernel), so that the
+// pair's elapsed time excludes the dispatch and event-packet overhead that a
+// pair recorded around the launch holds.  take returns false when it has no
+// pair to give; the launch then goes ahead untimed.
+struct KernelTimer {
+  virtual bool take(hipEvent_t* start, hipEvent_t* stop) = 0;
+
+ protected:
+  ~KernelTimer() = default;
+};
+void set_kernel_timer(KernelTimer* t);   // per thread; nullptr: plain launches
+KernelTimer* kernel_timer();
