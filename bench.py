@@ -185,8 +185,8 @@ def main():
 
     # per-kernel-class HIP-event timing over a second timed region of the same steps,
     # eager launches on the forward's stream: a pair recorded around each launch
-    # group (dispatch and event overhead included), and for the products a pair the
-    # runtime stamps with each kernel's own start and end
+    # group (dispatch and event overhead included), and for every kernel a pair the
+    # runtime stamps with the kernel's own start and end (used below)
     tl.tl_timing_enable(model, True)
     for _ in range(args.steps):
         step()
@@ -208,7 +208,7 @@ def main():
                 "timing": "kernel start/end stamped by the runtime (hipExtLaunchKernel event pairs)",
                 "event_pair_us": round(tot_ms / n * 1e3, 2),
                 "algorithmic_flops_per_launch": flops[dom]}
-    breakdown = {k: round(v[0] / args.steps * 1e3, 2) for k, v in cls.items() if v[1]}
+    breakdown = {k: round(v[0] / args.steps * 1e3, 2) for k, v in kcls.items() if v[1]}
     tl.tl_free(model)
     del model
 

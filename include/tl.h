@@ -402,13 +402,12 @@ tl_status tl_sync_errors(tl_model* m, void* stream);
 tl_status tl_timing_enable(tl_model* m, int32_t on);
 tl_status tl_timing_read(tl_model* m, double* total_ms, int64_t* launches);
 /* Measurement: the kernels' own durations behind the same classes.  While timing
- * is on, every launch of a product kernel (the QKV, O, gate/up, down and head
- * products, and their split-K reduction kernels) hands the runtime a further
+ * is on, every kernel launched inside a timed class hands the runtime a further
  * event pair that the runtime stamps with that kernel's start and end, so these
  * sums leave out the dispatch and event overhead held in tl_timing_read's
- * figures.  Writes, per class (arrays of TL_TIMING_CLASSES), the summed kernel
- * milliseconds and the number of kernels, and resets the sums.  Classes whose
- * kernels are not products (attention, rmsnorm, compact, embed) read 0.
+ * figures (which the stamping itself raises).  Writes, per class (arrays of
+ * TL_TIMING_CLASSES), the summed kernel milliseconds and the number of kernels,
+ * and resets the sums.
  * Errors: TL_E_ARG (NULL pointer), TL_E_HIP (a recorded event failed, or some
  * product launches went untimed because no event could be created; the sums
  * then miss them). */

@@ -14,6 +14,7 @@
 // below serves prefill runs of consecutive rows.
 #include "device_common.h"
 #include "epilogue.h"
+#include "launch.h"
 
 #include <algorithm>
 
@@ -757,7 +758,7 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
   dim3 grd(n_tiles, kv.H);
 #define TL_ATTN_CASE(T, DHV)                                                                                   \
   if (kv.dh == DHV) {                                                                                          \
-    hipLaunchKernelGGL((attn_tiled_kernel<T, DHV>), grd, dim3(kAttnWaves * 64), 0, s, (const T*)q, tiles, kv, (T*)out, d, \
+    TL_LAUNCH((attn_tiled_kernel<T, DHV>), grd, dim3(kAttnWaves * 64), 0, s, (const T*)q, tiles, kv, (T*)out, d, \
                        scale, ug);                                                                             \
     return hipGetLastError();                                                                                  \
   }
@@ -772,7 +773,7 @@ hipError_t launch_attention_tiled(int dtype, const void* q, const AttnTile* tile
   } else if (dtype == DT_F32) {
 #define TL_ATTN_SPLIT(DHV)                                                                                     \
   if (kv.dh == DHV) {                                                                                          \
-    hipLaunchKernelGGL((attn_tiled_split_kernel<DHV>), grd, dim3(kAttnWaves * 64), 0, s, (const float*)q, tiles, kv, \
+    TL_LAUNCH((attn_tiled_split_kernel<DHV>), grd, dim3(kAttnWaves * 64), 0, s, (const float*)q, tiles, kv, \
                        (float*)out, d, scale, ug);                                                             \
     return hipGetLastError();                                                                                  \
   }
@@ -805,16 +806,16 @@ void attn_rows_launch(const void* q, const RowInfo* rows, int n, const KVParams&
   const int ctx = (max_ctx + ns - 1) / ns;   // positions per run, at most
   const dim3 grid(wgs, ns);
   if (max_ctx > 0 && ctx <= P)
-    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 4>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+    TL_LAUNCH((attn_rows_kernel<T, LPK, 4>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
                        d, scale, live, qp, ns, part);
   else if (max_ctx > 0 && ctx <= 2 * P)
-    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 2>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+    TL_LAUNCH((attn_rows_kernel<T, LPK, 2>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
                        d, scale, live, qp, ns, part);
   else
-    hipLaunchKernelGGL((attn_rows_kernel<T, LPK, 1>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
+    TL_LAUNCH((attn_rows_kernel<T, LPK, 1>), grid, dim3(256), 0, s, (const T*)q, rows, kv, (T*)out,
                        d, scale, live, qp, ns, part);
   if (ns > 1)
-    hipLaunchKernelGGL((attn_merge_kernel<T>), dim3(wgs), dim3(128), 0, s, (const float*)part, ns, kv.H, kv.dh, rows,
+    TL_LAUNCH((attn_merge_kernel<T>), dim3(wgs), dim3(128), 0, s, (const float*)part, ns, kv.H, kv.dh, rows,
                        (T*)out, d, live);
 }
 

@@ -815,6 +815,7 @@ tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out
   const tl_config& c = m->cfg;
   auto& w = m->ws;
   TRY(tbegin(m, s));
+  TimerScope ts(m);
   if (!xnorm) HIPCHK(launch_rmsnorm(m->act, h, m->final_norm, gather, n_out, c.d_model, c.rms_eps, w.xh, s));
   const int tiles = gemm_head_tiles(m->gdt, n_out, c.vocab);
   GemmArgs g{};
@@ -832,10 +833,7 @@ tl_status run_head(tl_model* m, const float* h, const int32_t* gather, int n_out
   e.part_idx = w.part_i;
   e.n_tiles = tiles;
   e.part_val2 = margin ? w.part_v2 : nullptr;
-  {
-    TimerScope ts(m);
-    HIPCHK(launch_gemm(m->gdt, g, e, s));
-  }
+  HIPCHK(launch_gemm(m->gdt, g, e, s));
   if (out_tok || pend_lanes || margin)
     HIPCHK(launch_argmax_reduce(w.part_v, w.part_i, e.part_val2, n_out, tiles, out_tok,
                                 pend_lanes ? m->d_pending : nullptr, pend_lanes, margin, s));

@@ -254,9 +254,8 @@ constexpr size_t kNoAllocScratchBytes = 64ull << 20;
 hipError_t noalloc_scratch_init(int device);
 void* noalloc_scratch(int device);
 
-// Kernel-duration timing of the product launchers (measurement only).  While a
-// timer is installed on the calling thread, each launch in gemm.hip and gemv.hip
-// takes a fresh (start, stop) event pair from it and has the runtime stamp the
+// Kernel-duration timing (measurement only).  While a timer is installed on the
+// calling thread, each launch of the library's kernels takes a fresh (start, stop) event pair from it and has the runtime stamp the
 // kernel's own start and end into the pair (hipExtLaunchKernel), so that the
 // pair's elapsed time excludes the dispatch and event-packet overhead that a
 // pair recorded around the launch holds.  take returns false when it has no

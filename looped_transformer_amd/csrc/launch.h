@@ -1,4 +1,4 @@
-// Launch macro of the product kernels: a plain launch, or with a kernel timer
+// Launch macro of the library's kernels: a plain launch, or with a kernel timer
 // installed on this thread (kernels.h), a launch whose event pair the runtime
 // stamps with the kernel's own start and end.
 #pragma once

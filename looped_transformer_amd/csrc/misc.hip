@@ -3,6 +3,7 @@
 // load-time kernels (INT4 quantisation into the kernel layout, FP16-body
 // dequantisation, canonical export, row permutation).
 #include "device_common.h"
+#include "launch.h"
 
 namespace {
 
@@ -638,7 +639,7 @@ hipError_t embed_norm_x(const T* E, const int32_t* tokens, int n, int d, float* 
                         const float* g, float eps, int x_dtype, void* x, hipStream_t s) {
   const int vpt = (d + 1023) / 1024;
 #define TL_EN(X, V)                                                                                        \
-  hipLaunchKernelGGL((embed_norm_kernel<T, X, V>), dim3(n), dim3(256), 0, s, E, tokens, d, h, err, vocab, g, eps, \
+  TL_LAUNCH((embed_norm_kernel<T, X, V>), dim3(n), dim3(256), 0, s, E, tokens, d, h, err, vocab, g, eps, \
                      (X*)x)
 #define TL_EN_X(X)                 \
   switch (vpt) {                   \
@@ -675,9 +676,9 @@ hipError_t launch_embed(int dtype, const void* E, const int32_t* tokens, int n, 
     return err2;
   }
   switch (dtype) {
-    case DT_F32: hipLaunchKernelGGL(embed_kernel<float>, dim3(n), dim3(256), 0, s, (const float*)E, tokens, d, h, err, vocab); break;
-    case DT_F16: hipLaunchKernelGGL(embed_kernel<f16>, dim3(n), dim3(256), 0, s, (const f16*)E, tokens, d, h, err, vocab); break;
-    case DT_BF16: hipLaunchKernelGGL(embed_kernel<bf16>, dim3(n), dim3(256), 0, s, (const bf16*)E, tokens, d, h, err, vocab); break;
+    case DT_F32: TL_LAUNCH(embed_kernel<float>, dim3(n), dim3(256), 0, s, (const float*)E, tokens, d, h, err, vocab); break;
+    case DT_F16: TL_LAUNCH(embed_kernel<f16>, dim3(n), dim3(256), 0, s, (const f16*)E, tokens, d, h, err, vocab); break;
+    case DT_BF16: TL_LAUNCH(embed_kernel<bf16>, dim3(n), dim3(256), 0, s, (const bf16*)E, tokens, d, h, err, vocab); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -690,7 +691,7 @@ hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const i
   dim3 grid(n);
   const int vpt = d <= 1024 ? 1 : d <= 2048 ? 2 : d <= 4096 ? 4 : d <= 8192 ? 8 : 0;
 #define TL_RMS(T, V)                                                                                          \
-  hipLaunchKernelGGL((rmsnorm_kernel<T, V>), grid, dim3(256), 0, s, h, g, gather, n, d, eps, (T*)out)
+  TL_LAUNCH((rmsnorm_kernel<T, V>), grid, dim3(256), 0, s, h, g, gather, n, d, eps, (T*)out)
 #define TL_RMS_T(T)                      \
   switch (vpt) {                         \
     case 1: TL_RMS(T, 1); break;         \
@@ -713,7 +714,7 @@ hipError_t launch_rmsnorm(int out_dtype, const float* h, const float* g, const i
 hipError_t launch_compact(const RowInfo* rows_in, int n, int it, RowInfo* rows_out, int32_t* dest, int32_t* count_out,
                           int32_t* log_out, int32_t* running_out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(compact_kernel, dim3(1), dim3(1024), 0, s, rows_in, n, it, rows_out, dest, count_out, log_out, running_out);
+  TL_LAUNCH(compact_kernel, dim3(1), dim3(1024), 0, s, rows_in, n, it, rows_out, dest, count_out, log_out, running_out);
   return hipGetLastError();
 }
 
@@ -722,7 +723,7 @@ hipError_t launch_compact_move(const RowInfo* rows_in, int n, int it, RowInfo* r
                                void* x_next, int xrow_bytes, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   if (n > kCompactMoveRows || (d % 4) || (x && (xrow_bytes % 16))) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(compact_move_kernel, dim3(n), dim3(256), 0, s, rows_in, n, it, rows_out, count_out, log_out, h, d,
+  TL_LAUNCH(compact_move_kernel, dim3(n), dim3(256), 0, s, rows_in, n, it, rows_out, count_out, log_out, h, d,
                      h_next, h_exit, static_cast<const uint8_t*>(x), static_cast<uint8_t*>(x_next), xrow_bytes);
   return hipGetLastError();
 }
@@ -730,13 +731,13 @@ hipError_t launch_compact_move(const RowInfo* rows_in, int n, int it, RowInfo* r
 hipError_t launch_move_rows(const float* h, const int32_t* dest, const RowInfo* rows, int n, int d, float* h_next,
                             float* h_exit, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(move_rows_kernel, dim3(n), dim3(256), 0, s, h, dest, rows, d, h_next, h_exit);
+  TL_LAUNCH(move_rows_kernel, dim3(n), dim3(256), 0, s, h, dest, rows, d, h_next, h_exit);
   return hipGetLastError();
 }
 
 hipError_t launch_write_orig(const RowInfo* rows, int n, int32_t* out, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(write_orig_kernel, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, out);
+  TL_LAUNCH(write_orig_kernel, dim3((n + 255) / 256), dim3(256), 0, s, rows, n, out);
   return hipGetLastError();
 }
 
@@ -744,7 +745,7 @@ hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, float* 
                            float tau, float margin_thr, int patience, int d, float* h_exit, int32_t* eff_depth,
                            int32_t* live, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(ee_probe_kernel, dim3(n), dim3(256), 0, s, rows, it, h, h_prev, margin, tau,
+  TL_LAUNCH(ee_probe_kernel, dim3(n), dim3(256), 0, s, rows, it, h, h_prev, margin, tau,
                      margin_thr, patience, d, h_exit, eff_depth, live, (save_prev && !margin) ? 1 : 0);
   return hipGetLastError();
 }
@@ -752,7 +753,7 @@ hipError_t launch_ee_probe(RowInfo* rows, int n, int it, const float* h, float* 
 hipError_t launch_argmax_reduce(const float* pv, const int32_t* pi, const float* pv2, int n, int tiles, int32_t* out,
                                 int32_t* out2, const int32_t* scatter, float* margin, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_reduce_kernel, dim3(n), dim3(256), 0, s, pv, pi, pv2, tiles, out, out2, scatter, margin);
+  TL_LAUNCH(argmax_reduce_kernel, dim3(n), dim3(256), 0, s, pv, pi, pv2, tiles, out, out2, scatter, margin);
   return hipGetLastError();
 }
 
@@ -762,13 +763,13 @@ hipError_t launch_hcache_write(int dtype, const void* x, const RowInfo* rows, in
   const dim3 grid(n, hp.H);
   switch (dtype) {
     case DT_F32:
-      hipLaunchKernelGGL(hcache_write_kernel<float>, grid, dim3(64), 0, s, (const float*)x, rows, hp, (int)skip_done);
+      TL_LAUNCH(hcache_write_kernel<float>, grid, dim3(64), 0, s, (const float*)x, rows, hp, (int)skip_done);
       break;
     case DT_F16:
-      hipLaunchKernelGGL(hcache_write_kernel<f16>, grid, dim3(64), 0, s, (const f16*)x, rows, hp, (int)skip_done);
+      TL_LAUNCH(hcache_write_kernel<f16>, grid, dim3(64), 0, s, (const f16*)x, rows, hp, (int)skip_done);
       break;
     case DT_BF16:
-      hipLaunchKernelGGL(hcache_write_kernel<bf16>, grid, dim3(64), 0, s, (const bf16*)x, rows, hp, (int)skip_done);
+      TL_LAUNCH(hcache_write_kernel<bf16>, grid, dim3(64), 0, s, (const bf16*)x, rows, hp, (int)skip_done);
       break;
     default:
       return hipErrorInvalidValue;
@@ -781,9 +782,9 @@ hipError_t launch_hcache_read(int dtype, const HCacheParams& hp, const RowInfo* 
   if (n <= 0) return hipSuccess;
   const dim3 grid(n, hp.H);
   switch (dtype) {
-    case DT_F32: hipLaunchKernelGGL(hcache_read_kernel<float>, grid, dim3(64), 0, s, hp, rows, (float*)out); break;
-    case DT_F16: hipLaunchKernelGGL(hcache_read_kernel<f16>, grid, dim3(64), 0, s, hp, rows, (f16*)out); break;
-    case DT_BF16: hipLaunchKernelGGL(hcache_read_kernel<bf16>, grid, dim3(64), 0, s, hp, rows, (bf16*)out); break;
+    case DT_F32: TL_LAUNCH(hcache_read_kernel<float>, grid, dim3(64), 0, s, hp, rows, (float*)out); break;
+    case DT_F16: TL_LAUNCH(hcache_read_kernel<f16>, grid, dim3(64), 0, s, hp, rows, (f16*)out); break;
+    case DT_BF16: TL_LAUNCH(hcache_read_kernel<bf16>, grid, dim3(64), 0, s, hp, rows, (bf16*)out); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -792,7 +793,7 @@ hipError_t launch_hcache_read(int dtype, const HCacheParams& hp, const RowInfo* 
 hipError_t launch_spec_pack(const int32_t* pending, const int32_t* lanes, const int32_t* draft, int n, int k,
                             int32_t* in, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(spec_pack_kernel, dim3((n * (k + 1) + 255) / 256), dim3(256), 0, s, pending, lanes, draft, n, k, in);
+  TL_LAUNCH(spec_pack_kernel, dim3((n * (k + 1) + 255) / 256), dim3(256), 0, s, pending, lanes, draft, n, k, in);
   return hipGetLastError();
 }
 
@@ -800,38 +801,38 @@ hipError_t launch_spec_accept(const int32_t* draft, const int32_t* g, const int3
                               const int32_t* emitted, const int32_t* slot, int n, int k, int n_tokens,
                               int32_t* out, int32_t* pending, int32_t* acc, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(spec_accept_kernel, dim3((n + 255) / 256), dim3(256), 0, s, draft, g, lanes, want, emitted, slot, n,
+  TL_LAUNCH(spec_accept_kernel, dim3((n + 255) / 256), dim3(256), 0, s, draft, g, lanes, want, emitted, slot, n,
                      k, n_tokens, out, pending, acc);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_rows_kernel, dim3(n), dim3(256), 0, s, src, idx, d, dst);
+  TL_LAUNCH(gather_rows_kernel, dim3(n), dim3(256), 0, s, src, idx, d, dst);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter_rows(const float* src, const int32_t* idx, int n, int d, float* dst, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_rows_kernel, dim3(n), dim3(256), 0, s, src, idx, d, dst);
+  TL_LAUNCH(scatter_rows_kernel, dim3(n), dim3(256), 0, s, src, idx, d, dst);
   return hipGetLastError();
 }
 
 hipError_t launch_fill_i32(int32_t* p, int32_t v, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, v, n);
+  TL_LAUNCH(fill_i32_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, p, v, n);
   return hipGetLastError();
 }
 
 hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
+  TL_LAUNCH(gather_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
   return hipGetLastError();
 }
 
 hipError_t launch_scatter_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(scatter_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
+  TL_LAUNCH(scatter_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
   return hipGetLastError();
 }
 
@@ -839,33 +840,33 @@ hipError_t launch_permute_rows(int elem_bytes, const void* src, const int32_t* p
                                hipStream_t s) {
   if ((int64_t)K * elem_bytes % 4 != 0) return hipErrorInvalidValue;
   const int wpr = (int)((int64_t)K * elem_bytes / 4);
-  hipLaunchKernelGGL(permute_rows_kernel, dim3(N), dim3(256), 0, s, (const uint32_t*)src, perm, wpr, (uint32_t*)dst);
+  TL_LAUNCH(permute_rows_kernel, dim3(N), dim3(256), 0, s, (const uint32_t*)src, perm, wpr, (uint32_t*)dst);
   return hipGetLastError();
 }
 
 hipError_t launch_permute_bf16_to_f16(const uint16_t* src, const int32_t* perm, int N, int K, uint16_t* dst,
                                       hipStream_t s) {
-  hipLaunchKernelGGL(permute_bf16_to_f16_kernel, dim3(N), dim3(256), 0, s, src, perm, K, dst);
+  TL_LAUNCH(permute_bf16_to_f16_kernel, dim3(N), dim3(256), 0, s, src, perm, K, dst);
   return hipGetLastError();
 }
 
 hipError_t launch_quant_w4(const float* w, const int32_t* perm, int N, int K, uint32_t* words, uint16_t* scales,
                            hipStream_t s) {
   const int64_t items = (int64_t)N * (K / 128);
-  hipLaunchKernelGGL(quant_w4_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, w, perm, N, K, words, scales);
+  TL_LAUNCH(quant_w4_kernel, dim3((unsigned)((items + 3) / 4)), dim3(256), 0, s, w, perm, N, K, words, scales);
   return hipGetLastError();
 }
 
 hipError_t launch_w4_to_f16(const uint32_t* words, const uint16_t* scales, int N, int K, uint16_t* out, hipStream_t s) {
   const int64_t tot = (int64_t)N * K;
-  hipLaunchKernelGGL(w4_to_f16_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, words, scales, N, K, out);
+  TL_LAUNCH(w4_to_f16_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, words, scales, N, K, out);
   return hipGetLastError();
 }
 
 hipError_t launch_w4_export(const uint32_t* words, const uint16_t* scales, const int32_t* perm, int N, int K, int8_t* q,
                             uint16_t* s_out, hipStream_t s) {
   const int64_t tot = (int64_t)N * K;
-  hipLaunchKernelGGL(w4_export_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, words, scales, perm, N, K,
+  TL_LAUNCH(w4_export_kernel, dim3((unsigned)((tot + 255) / 256)), dim3(256), 0, s, words, scales, perm, N, K,
                      q, s_out);
   return hipGetLastError();
 }
