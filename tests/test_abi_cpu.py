@@ -44,6 +44,9 @@ def test_null_arguments_rejected(L):
     assert L.tl_lane_fork(None, 0, 1, 1, 0, None) == tl.TL_E_ARG
     assert L.tl_speculate(None, 1, None, 2, 8, 4, 8, None, None, None) == tl.TL_E_ARG
     assert L.tl_lane_release(None, 0) == tl.TL_E_ARG
+    assert L.tl_timing_enable(None, 1) == tl.TL_E_ARG
+    assert L.tl_timing_read(None, None, None) == tl.TL_E_ARG
+    assert L.tl_timing_read_kernels(None, None, None) == tl.TL_E_ARG
 
 
 def _weights_struct():
