@@ -289,3 +289,69 @@ def test_graph_replay_matches_eager(name):
             torch.cuda.synchronize()
     finally:
         tl.tl_free(model)
+
+
+@pytest.mark.parametrize("name", ["tiny-f32", "tiny-w4"])
+def test_degenerate_sizes_and_forward_errors(name):
+    """One-token prompts at depth 1 and at the model's max_L, next to a prompt
+    whose new tokens fill max_pos exactly, against the oracle; then calls that
+    break tl_forward's rules (an empty sequence, depth 0 or above max_L, a
+    cu_seqlens not starting at 0, a prompt that leaves too few positions for its
+    new tokens) fail before any device work, and one cached step per lane still
+    matches the oracle."""
+    spec = TINY[name]
+    say("degenerate sizes", name)
+    w = synth.make_weights(spec, seed=6)
+    m = oracle.OracleModel.from_weights(w)
+    MAXP, MAXL, NEW = 64, 16, 8
+    seqs = [synth.tokens(6, 600, 1, spec.vocab), synth.tokens(6, 601, 1, spec.vocab),
+            synth.tokens(6, 602, MAXP - NEW, spec.vocab)]
+    Ls = [1, MAXL, 3]
+    model = load_model(w, max_lanes=4, max_pos=MAXP, max_L=MAXL,
+                       kv_arena_bytes=kv_bytes(spec, Ls, [len(s) + NEW for s in seqs]))
+    try:
+        hid, lg, nxt, log, depth = gpu_forward(model, spec, seqs, Ls, lanes=[0, 1, 2], max_new=NEW)
+        check_log(log, depth)
+        ref_h, ref_lg, _ = oracle.forward_batch(m, seqs, Ls)
+        off = 0
+        for i, s in enumerate(seqs):
+            r = rel_l2(hid[off:off + len(s)], ref_h[off:off + len(s)])
+            say(name, "prompt", len(s), "L", Ls[i], "hidden rel %.2e" % r)
+            assert r <= hidden_bar(spec, Ls[i]), (i, r)
+            off += len(s)
+        assert rel_l2(lg, ref_lg) <= (1e-4 if spec.act_dtype == "f32" else 1e-2)
+        gaps = near_tie_gaps(nxt, ref_lg)
+        assert (not gaps) if spec.act_dtype == "f32" else all(g <= 0.05 for g in gaps), gaps
+
+        one = torch.tensor(seqs[0], dtype=torch.int32, device="cuda")
+        longer = torch.tensor(synth.tokens(6, 604, MAXP - NEW + 1, spec.vocab), dtype=torch.int32, device="cuda")
+        bad = [(dict(cu_seqlens=[0, 0], tokens=one, L=1), tl.TL_E_ARG),            # empty sequence
+               (dict(cu_seqlens=[0, 1], tokens=one, L=0), tl.TL_E_ARG),            # depth 0
+               (dict(cu_seqlens=[0, 1], tokens=one, L=MAXL + 1), tl.TL_E_ARG),     # above max_L
+               (dict(cu_seqlens=[1, 2], tokens=one, L=1), tl.TL_E_ARG),            # cu_seqlens[0] != 0
+               (dict(cu_seqlens=[0, MAXP - NEW + 1], tokens=longer, L=1, lanes=[3], max_new_tokens=NEW),
+                tl.TL_E_STATE)]                                                     # 65 positions > 64
+        for kw, want in bad:
+            with pytest.raises(tl.TLError) as ei:
+                tl.tl_forward(model, **kw)
+            say(name, "rejected:", ei.value)
+            assert ei.value.status == want, (kw, ei.value)
+
+        feed = synth.tokens(6, 603, 3, spec.vocab)
+        out = torch.empty(3, dtype=torch.int32, device="cuda")
+        hs = torch.empty(3, spec.d_model, dtype=torch.float32, device="cuda")
+        lgd = torch.empty(3, spec.vocab, dtype=torch.float32, device="cuda")
+        eff = tl.tl_decode_step(model, [0, 1, 2], Ls, out,
+                                in_tokens=torch.tensor(feed, dtype=torch.int32, device="cuda"),
+                                out_logits=lgd, out_hidden=hs)
+        torch.cuda.synchronize()
+        Hd, LGd = hs.cpu().numpy(), lgd.cpu().numpy()
+        for i, (s, L) in enumerate(zip(seqs, Ls)):
+            lane, _, _ = oracle.prefill(m, s, L)
+            h_o, l_o, _, L_o = oracle.decode_step(m, lane, L, token=int(feed[i]))
+            r, rl = rel_l2(Hd[i], h_o), rel_l2(LGd[i], l_o)
+            say(name, "step lane", i, "ctx", len(s) + 1, "L", L, "hidden %.2e logits %.2e" % (r, rl))
+            assert eff[i] == L_o
+            assert r <= hidden_bar(spec, L) and rl <= (1e-4 if spec.act_dtype == "f32" else 1e-2), (i, r, rl)
+    finally:
+        tl.tl_free(model)
